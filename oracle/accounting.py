@@ -1,0 +1,85 @@
+"""Bytes and FLOPs per decoded token, in closed form (TEST INFRASTRUCTURE and bench reporting).
+
+The HBM-roofline accounting is the pages' own: interactivity bound = aggregate HBM
+bandwidth / active bytes per token (TileRT article, "Ultra-High Interactivity on
+NVIDIA GPUs? TileRT on InferenceX": the 64 TB/s / 21 GB worked example in the
+introduction and the 38.4 TB/s / 42 GB example in "But What Exactly is TileRT?"),
+and weight bytes = parameters x bits per weight / 8 (Vera Rubin article, section
+"Lookup Table Weight Decompression in Rubin SM107 Tensor Core", MXFP4 4.25 and LUT
+3.125 bits per weight). SwiGLU costs 2*d*m + 2*d*m + 2*m*d = 6*d*m FLOPs per token
+(Kimi K3 article, LatentMoE section).
+
+Algorithmic bytes of one decode layer-token (this project's definition): every stored
+byte of the weights it reads (linear weights, FP8 block scales, norm gains, router
+bias; only the selected and shared experts), the KV rows attention reads (all p+1 rows
+for dense attention; the selected rows plus every index key for sparse attention),
+the appended cache row, and the bf16 input and output vectors.
+"""
+from __future__ import annotations
+
+import math
+
+from synth.configs import LayerShape
+
+
+def tokens_per_s_user(bandwidth_bytes_per_s: float, bytes_per_token: float) -> float:
+    return bandwidth_bytes_per_s / bytes_per_token
+
+
+def weight_bytes(n_params: float, bits_per_weight: float) -> float:
+    return n_params * bits_per_weight / 8.0
+
+
+def swiglu_flops(d: int, m: int) -> int:
+    return 2 * d * m + 2 * d * m + 2 * m * d
+
+
+def _mat_bytes(out_dim: int, in_dim: int, fmt: str) -> int:
+    if fmt == "fp8":
+        return out_dim * in_dim + 4 * math.ceil(out_dim / 128) * math.ceil(in_dim / 128)
+    return 2 * out_dim * in_dim
+
+
+def layer_weight_bytes(s: LayerShape) -> dict:
+    """Storage bytes by group for one layer-token (selected + shared experts only)."""
+    f = s.wfmt
+    H = s.hidden
+    g = {}
+    if s.attn == "gqa":
+        g["attn"] = (_mat_bytes(s.n_heads * s.head_dim, H, f) + 2 * _mat_bytes(s.n_kv_heads * s.head_dim, H, f)
+                     + _mat_bytes(H, s.o_dim, f))
+    else:
+        g["attn"] = (_mat_bytes(s.q_lora, H, f) + _mat_bytes(s.n_heads * (s.nope_dim + s.rope_dim), s.q_lora, f)
+                     + _mat_bytes(s.kv_lora + s.rope_dim, H, f) + _mat_bytes(s.n_heads * s.nope_dim, s.kv_lora, f)
+                     + _mat_bytes(s.n_heads * s.v_dim, s.kv_lora, f) + _mat_bytes(H, s.o_dim, f))
+        if s.index_topk:
+            g["indexer"] = (_mat_bytes(s.index_heads * s.index_dim, s.q_lora, f) + _mat_bytes(s.index_heads, H, "bf16")
+                            + _mat_bytes(s.index_dim, H, f))
+    n_active = 1 if s.ffn == "dense" else s.top_k + s.n_shared
+    g["experts"] = n_active * (2 * _mat_bytes(s.inter, H, f) + _mat_bytes(H, s.inter, f))
+    if s.ffn == "moe":
+        g["router"] = 2 * s.n_experts * H + (4 * s.n_experts if s.router == "sigmoid_bias" else 0)
+    g["norms"] = 4 * (2 * H + ((s.q_lora + s.kv_lora) if s.attn == "mla" else 0))
+    return g
+
+
+def layer_kv_bytes(s: LayerShape, pos: int) -> dict:
+    T = pos + 1
+    if s.attn == "gqa":
+        row = 2 * s.n_kv_heads * s.head_dim * 2          # K and V, bf16
+        return {"kv_read": T * row, "kv_write": row}
+    row = 2 * s.latent_dim
+    if s.index_topk:
+        n_sel = min(s.index_topk, T)
+        return {"kv_read": n_sel * row + T * (s.index_dim + 4), "kv_write": row + s.index_dim + 4}
+    return {"kv_read": T * row, "kv_write": row}
+
+
+def layer_bytes(s: LayerShape, pos: int) -> int:
+    """Algorithmic bytes of one decode layer-token at position ``pos``."""
+    return (sum(layer_weight_bytes(s).values()) + sum(layer_kv_bytes(s, pos).values())
+            + 2 * 2 * s.hidden)
+
+
+def head_bytes(hidden: int, vocab: int, fmt: str = "fp8") -> int:
+    return _mat_bytes(vocab, hidden, fmt) + 4 * hidden + 2 * hidden   # head, final gain, embedding row

@@ -1,0 +1,288 @@
+"""Plain fp64 CPU oracle of one batch-1 decode layer.
+
+TEST INFRASTRUCTURE: only tests/, __graft_entry__.smoke() and bench.py's CPU
+baseline use it; the HIP library shares no code with it and never calls it.
+
+What is computed, and where the pages describe it:
+
+* The layer order RMSNorm -> projections (GEMM/GEMV) -> (sparse) attention ->
+  output projection + residual follows the description of an attention layer's
+  workers in the TileRT article ("Ultra-High Interactivity on NVIDIA GPUs? TileRT on
+  InferenceX", section "But What Exactly is TileRT?"), and the decode step reading a
+  growing KV cache follows its section "PD Disaggregated Engine with vLLM and TileRT".
+* Absorbed MLA is named in the Kimi K3 article's section on Kimi Linear ("absorption
+  trick"); this oracle computes MLA *non-absorbed* (per-head keys and values
+  materialised), so the absorbed GPU form is checked against the plain definition.
+* Top-k with a "biased router score" cutoff follows the Quantile Balancing section
+  of the Kimi K3 article; the bias steers selection only and the gates use the
+  unbiased sigmoid scores.
+* SwiGLU experts with three matrix products per expert follow the LatentMoE
+  derivation in the Kimi K3 article ("Up projection / Gate projection / Down
+  projection"); the shared expert next to the routed ones follows the vLLM Kimi K3
+  backend article, section "Four changes drive the gains" (sharded MoE routing).
+* The indexer that scores every cached token and keeps the top 2048 follows the
+  "Sparse Indexer worker" of the TileRT article (section "But What Exactly is
+  TileRT?") and the DeepSeek sparse attention mentioned in the Kimi K3 article.
+
+The pages fix none of the formulas below; each reading taken where they are silent
+is listed in the module-level table ``READINGS``.
+
+Storage rounding that is part of the method (and therefore done here too): the
+appended cache row is stored as bf16 (the indexer key as FP8 + scale), and the
+layer output is a bf16 vector. Everything else is fp64.
+
+Indexer decision path: the selection is an integer result decided by floating point,
+so the values that feed it are taken at the precision the kernel stores them in:
+``a`` and ``c_q`` as fp32, ``q_I`` as bf16, head weights ``w`` and the new key as fp32,
+key codes as FP8; the score is then evaluated in fp64 in one fixed order with plain
+multiplies and adds.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Optional
+
+import numpy as np
+
+from . import numerics as nx
+
+READINGS = {
+    "cache_len": "a cache of N tokens holds positions 0..N-1; the decode token is written at p=N and attends over N+1 rows",
+    "rope": "interleaved pairs (2i, 2i+1), theta_i = base^(-2i/d_rot), base 10000; GQA rotates whole heads, MLA only the 64 rope dims",
+    "eps_gamma": "eps = 1e-6 everywhere; gains gamma = 1 + 0.02 N(0,1)",
+    "gqa_groups": "q head h uses kv head floor(h * n_kv / n_q) (contiguous groups)",
+    "mla_dims": "qk_nope 128, rope 64, v 128, scale 1/sqrt(192); RMSNorm on c_q and c_kv",
+    "sparse_shapes": "sparse workload: hidden 4096, 32 heads, MLA 512+64 latent, q_lora 1536, bf16 weights, 64-expert MoE top-8 softmax, inter 1536, 1 shared",
+    "indexer": "q_I = bf16(W_qI c_q) [8x64], w = W_w a [8], k_I = W_kI a [64] -> FP8 with scale amax/448; "
+               "score_t = sum_h w_h * max(0, s_t * sum_i q_I[h,i] dec(code_t[i])), fp64, i then h ascending, no FMA; "
+               "the current token is a candidate; top-2048 by (score desc, index asc)",
+    "router": "softmax router: logits r = W_r b, top-8 by (r desc, idx asc), gates = softmax(r[sel]); "
+              "sigmoid router: s = sigmoid(r), top-8 by (s + bias desc, idx asc), gates = s[sel]/sum(s[sel])",
+    "shared_expert": "shared expert has the routed width and gate weight 1; no routed scaling factor",
+    "fp8": "OCP E4M3FN, fp32 scale per 128x128 block of [out, in] (edge blocks their own), weight-only",
+    "ties": "every top-k breaks ties to the lower index",
+    "output": "the layer output is stored as bf16; multi-layer stacks pass bf16 hidden states",
+}
+
+
+class Counted:
+    """Wraps a weight source and counts the storage bytes of every distinct tensor read."""
+
+    def __init__(self, src):
+        self.src = src
+        self.bytes = 0
+        self._seen = set()
+
+    def _count(self, key, n):
+        if key not in self._seen:
+            self._seen.add(key)
+            self.bytes += n
+
+    def matrix(self, name, expert=0):
+        m = self.src.matrix(name, expert)
+        if m["fmt"] == "fp8":
+            self._count((name, expert), m["codes"].size + 4 * m["scales"].size)
+        else:
+            self._count((name, expert), 2 * m["bits"].size)
+        return m
+
+    def norm(self, name):
+        g = self.src.norm(name)
+        self._count(("norm", name), 4 * g.size)
+        return g
+
+    def router_bias(self):
+        b = self.src.router_bias()
+        self._count(("router_bias",), 4 * b.size)
+        return b
+
+
+def weight_f64(m: Dict) -> np.ndarray:
+    if m["fmt"] == "fp8":
+        return nx.dequant_fp8_block(m["codes"], m["scales"])
+    return nx.bf16_to_f64(m["bits"])
+
+
+def _linear(W, name, v, expert=0):
+    return weight_f64(W.matrix(name, expert)) @ v
+
+
+# ---------------------------------------------------------------------------
+# attention families
+# ---------------------------------------------------------------------------
+def gqa_attention(s, W, cache, a, pos, rec):
+    """MHA/GQA: q,k,v projections, RoPE, cache append, softmax attention, concat heads."""
+    hd, nh, nkv = s.head_dim, s.n_heads, s.n_kv_heads
+    q = _linear(W, "wq", a).reshape(nh, hd)
+    k = _linear(W, "wk", a).reshape(nkv, hd)
+    v = _linear(W, "wv", a).reshape(nkv, hd)
+    q = nx.rope(q, pos, s.rope_base)
+    k = nx.rope(k, pos, s.rope_base)
+    k_st = nx.round_to_bf16(k)
+    v_st = nx.round_to_bf16(v)
+    rec["q"], rec["k_new"], rec["v_new"] = q, k_st, v_st
+    K = np.concatenate([nx.bf16_to_f64(cache["k"][:, :pos, :]), k_st[:, None, :]], axis=1)
+    V = np.concatenate([nx.bf16_to_f64(cache["v"][:, :pos, :]), v_st[:, None, :]], axis=1)
+    rec["kv_bytes_read"] = 2 * K.size * 2
+    rec["kv_bytes_written"] = 2 * (k_st.size + v_st.size)
+    o = np.empty((nh, hd))
+    for h in range(nh):
+        g = (h * nkv) // nh
+        sc = K[g] @ q[h] / math.sqrt(hd)
+        p = nx.softmax(sc)
+        o[h] = p @ V[g]
+    rec["o"] = o
+    return _linear(W, "wo", o.reshape(-1))
+
+
+def indexer_select(s, W, cache, a, pos, rec):
+    """Score every cached token (and the new one) and keep the top index_topk positions.
+
+    The inputs of the score are formed from fp32 ``a`` and fp32 ``c_q`` (recomputed from
+    fp32 ``a``), at the precision the kernel holds them in; see the module docstring.
+    """
+    a32 = nx.round_to_f32(a)
+    cq32 = nx.round_to_f32(nx.rmsnorm(_linear(W, "w_dq", a32), W.norm("q_norm"), s.eps))
+    q_i = nx.round_to_bf16(_linear(W, "w_qi", cq32)).reshape(s.index_heads, s.index_dim)
+    w = nx.round_to_f32(_linear(W, "w_w", a32))
+    k_i = nx.round_to_f32(_linear(W, "w_ki", a32))
+    # FP8 quantisation of the new key: fp32 scale amax/448, fp32 quotient, RNE, saturate
+    k32 = k_i.astype(np.float32)
+    amax = np.float32(np.max(np.abs(k32)))
+    sig = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+    quo = np.clip(k32 / sig, np.float32(-448.0), np.float32(448.0))
+    code_new = nx.e4m3_encode_f32(quo)
+    rec["q_i"], rec["w_idx"], rec["k_i"] = q_i, w, k_i
+    rec["index_code_new"], rec["index_scale_new"] = code_new, sig
+    codes = np.concatenate([cache["index_codes"][:pos], code_new[None, :]], axis=0)
+    scales = np.concatenate([np.asarray(cache["index_scales"][:pos], np.float32), [sig]]).astype(np.float64)
+    dec = nx.E4M3[codes]                         # [T, 64], exact
+    T = codes.shape[0]
+    score = np.zeros(T)
+    for h in range(s.index_heads):
+        d = np.zeros(T)
+        for i in range(s.index_dim):
+            d = d + q_i[h, i] * dec[:, i]        # separate multiply and add, i ascending
+        r = scales * d
+        r = np.maximum(r, 0.0)
+        score = score + w[h] * r
+    rec["index_score"] = score
+    rec["index_bytes_read"] = T * (s.index_dim + 4)
+    k = min(s.index_topk, T)
+    sel = np.sort(nx.topk_desc(score, k))
+    rec["index_sel"] = sel
+    return sel
+
+
+def mla_attention(s, W, cache, a, pos, rec):
+    """MLA, computed without absorption: per-head keys/values are materialised from c_kv."""
+    nh, nope, rd, vd, L = s.n_heads, s.nope_dim, s.rope_dim, s.v_dim, s.kv_lora
+    c_q = nx.rmsnorm(_linear(W, "w_dq", a), W.norm("q_norm"), s.eps)
+    qf = _linear(W, "w_uq", c_q).reshape(nh, nope + rd)
+    q_nope = qf[:, :nope]
+    q_rope = nx.rope(qf[:, nope:], pos, s.rope_base)
+    kv = _linear(W, "w_dkv", a)
+    c_kv = nx.rmsnorm(kv[:L], W.norm("kv_norm"), s.eps)
+    k_rope = nx.rope(kv[L:], pos, s.rope_base)
+    row = nx.round_to_bf16(np.concatenate([c_kv, k_rope]))
+    rec["c_q"], rec["q_nope"], rec["q_rope"], rec["latent_new"] = c_q, q_nope, q_rope, row
+    C = np.concatenate([nx.bf16_to_f64(cache["latent"][:pos]), row[None, :]], axis=0)   # [T, L+rd]
+    T = C.shape[0]
+    rows = np.arange(T)
+    if s.index_topk:
+        rows = indexer_select(s, W, cache, a, pos, rec)
+    Cs = C[rows]
+    rec["kv_bytes_read"] = Cs.size * 2
+    rec["kv_bytes_written"] = row.size * 2 + (s.index_dim + 4 if s.index_topk else 0)
+    W_uk = weight_f64(W.matrix("w_uk")).reshape(nh, nope, L)
+    W_uv = weight_f64(W.matrix("w_uv")).reshape(nh, vd, L)
+    ckv, kr = Cs[:, :L], Cs[:, L:]
+    scale = 1.0 / math.sqrt(nope + rd)
+    o = np.empty((nh, vd))
+    for h in range(nh):
+        k_nope = ckv @ W_uk[h].T                 # [T, nope]   key of head h
+        v_h = ckv @ W_uv[h].T                    # [T, vd]     value of head h
+        sc = (k_nope @ q_nope[h] + kr @ q_rope[h]) * scale
+        p = nx.softmax(sc)
+        o[h] = p @ v_h
+    rec["o"] = o
+    return _linear(W, "wo", o.reshape(-1))
+
+
+# ---------------------------------------------------------------------------
+# FFN
+# ---------------------------------------------------------------------------
+def expert(W, e, b):
+    g = _linear(W, "w_gate", b, e)
+    u = _linear(W, "w_up", b, e)
+    return _linear(W, "w_down", nx.silu(g) * u, e)
+
+
+def route(s, W, b, rec):
+    r = nx.bf16_to_f64(W.matrix("router")["bits"]) @ b
+    rec["router_logits"] = r
+    if s.router == "softmax":
+        sel = nx.topk_desc(r, s.top_k)
+        gates = nx.softmax(r[sel])
+    else:
+        sc = nx.sigmoid(r)
+        bias = np.asarray(W.router_bias(), np.float64)
+        sel = nx.topk_desc(sc + bias, s.top_k)
+        gates = sc[sel] / np.sum(sc[sel])
+    rec["router_sel"], rec["gates"] = sel, gates
+    return sel, gates
+
+
+def ffn(s, W, b, rec):
+    if s.ffn == "dense":
+        return expert(W, 0, b)
+    sel, gates = route(s, W, b, rec)
+    f = np.zeros(s.hidden)
+    for e, g in zip(sel, gates):
+        f = f + g * expert(W, int(e), b)
+    for j in range(s.n_shared):
+        f = f + expert(W, s.n_experts + j, b)
+    return f
+
+
+# ---------------------------------------------------------------------------
+def decode_layer(s, W, cache, x_bits: np.ndarray, pos: int, record: Optional[dict] = None) -> dict:
+    """Decode one token at position ``pos`` through one layer.
+
+    ``W``: weight source (``matrix(name, expert)``, ``norm(name)``, ``router_bias()``).
+    ``cache``: host arrays holding at least positions 0..pos-1 (bf16 bits; FP8 codes +
+    fp32 scales for index keys). ``x_bits``: bf16 [hidden]. Returns a dict with ``out``
+    (fp64 values of the bf16 output), ``out_bits`` and the intermediates.
+    """
+    rec = {} if record is None else record
+    CW = Counted(W)
+    h = nx.bf16_to_f64(x_bits)
+    a = nx.rmsnorm(h, CW.norm("attn_norm"), s.eps)
+    rec["a"] = a
+    if s.attn == "gqa":
+        y = gqa_attention(s, CW, cache, a, pos, rec)
+    else:
+        y = mla_attention(s, CW, cache, a, pos, rec)
+    h2 = h + y
+    b = nx.rmsnorm(h2, CW.norm("ffn_norm"), s.eps)
+    rec["y"], rec["h2"], rec["b"] = y, h2, b
+    f = ffn(s, CW, b, rec)
+    out = h2 + f
+    rec["f"] = f
+    rec["out_f64"] = out
+    rec["out"] = nx.round_to_bf16(out)
+    rec["out_bits"] = nx.bf16_bits_of(rec["out"])
+    rec["weight_bytes"] = CW.bytes
+    return rec
+
+
+def append_to_cache(s, cache, rec, pos):
+    """Write the rows the step appended into a host cache (mutates ``cache``)."""
+    if s.attn == "gqa":
+        cache["k"][:, pos, :] = nx.bf16_bits_of(rec["k_new"])
+        cache["v"][:, pos, :] = nx.bf16_bits_of(rec["v_new"])
+    else:
+        cache["latent"][pos] = nx.bf16_bits_of(rec["latent_new"])
+        if s.index_topk:
+            cache["index_codes"][pos] = rec["index_code_new"]
+            cache["index_scales"][pos] = rec["index_scale_new"]

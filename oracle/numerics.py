@@ -1,0 +1,149 @@
+"""Scalar building blocks of the CPU oracle (fp64 NumPy).
+
+TEST INFRASTRUCTURE. Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` may import this package. It shares no code with the
+HIP library and the library never calls it.
+
+Every routine here is pinned by ``tests/test_oracle_pins.py`` against a library
+routine (torch's bfloat16 / float8_e4m3fn casts), a closed form or brute force.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# --- storage formats --------------------------------------------------------
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> exact fp64 values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """fp64 -> nearest bf16 value (ties to even), returned as fp64. Finite normal range only.
+
+    One rounding straight from fp64 (no detour through fp32, which would round twice).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                   # x = m * 2**e, 0.5 <= |m| < 1
+    q = np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)   # 8 significant bits
+    return np.where(x == 0, x, q)
+
+
+def bf16_bits_of(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns of values that are already exactly bf16."""
+    return (np.asarray(x, dtype=np.float64).astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def round_to_f32(x: np.ndarray) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def e4m3_decode_table() -> np.ndarray:
+    """All 256 OCP E4M3FN codes -> fp64 value (NaN for S.1111.111).
+
+    Normal: (-1)^s * 2^(E-7) * (1 + M/8) for E >= 1; subnormal: (-1)^s * 2^-6 * M/8.
+    """
+    t = np.empty(256, dtype=np.float64)
+    for c in range(256):
+        s = -1.0 if c & 0x80 else 1.0
+        e = (c >> 3) & 0xF
+        m = c & 0x7
+        if e == 0xF and m == 0x7:
+            t[c] = np.nan
+        elif e == 0:
+            t[c] = s * 2.0 ** -6 * (m / 8.0)
+        else:
+            t[c] = s * 2.0 ** (e - 7) * (1.0 + m / 8.0)
+    return t
+
+
+E4M3 = e4m3_decode_table()
+
+
+def dequant_fp8_block(codes: np.ndarray, scales: np.ndarray, block: int = 128) -> np.ndarray:
+    """W[n, k] = dec(Q[n, k]) * S[n // 128, k // 128] in fp64."""
+    n, k = codes.shape
+    s = np.repeat(np.repeat(np.asarray(scales, np.float64), block, 0), block, 1)[:n, :k]
+    return E4M3[codes] * s
+
+
+def e4m3_encode_f32(q: np.ndarray) -> np.ndarray:
+    """fp32 values in [-448, 448] -> E4M3FN codes, round to nearest, ties to even mantissa.
+
+    Works from the binary exponent: for |q| >= 2^-6 the spacing is 2^(floor(log2|q|) - 3),
+    below it the subnormal spacing 2^-9; rint() rounds half to even, which on this grid is
+    the even code.  A value that rounds up into the next binade is still on the grid.
+    """
+    q = np.asarray(q, dtype=np.float32).astype(np.float64)
+    a = np.minimum(np.abs(q), 448.0)
+    _, e = np.frexp(a)                  # a in [2^(e-1), 2^e)
+    exp = np.maximum(e - 1, -6)
+    step = np.ldexp(1.0, exp - 3)
+    r = np.rint(a / step) * step        # exact: power-of-two scaling
+    r = np.minimum(r, 448.0)
+    # encode r
+    _, e2 = np.frexp(r)
+    E = np.where(r >= 2.0 ** -6, e2 - 1 + 7, 0)
+    M = np.where(E > 0, np.rint((r / np.ldexp(1.0, e2 - 1) - 1.0) * 8.0), np.rint(r / 2.0 ** -9))
+    code = (E.astype(np.int64) << 3) | M.astype(np.int64)
+    code = code | (np.signbit(q).astype(np.int64) << 7)
+    return code.astype(np.uint8)
+
+
+# --- layer math ---------------------------------------------------------------
+def rms_inverse(h: np.ndarray, eps: float) -> float:
+    """1 / sqrt(mean(h^2) + eps), all in fp64."""
+    h = np.asarray(h, dtype=np.float64)
+    ss = float(np.sum(h * h))
+    return 1.0 / np.sqrt(ss / h.shape[-1] + eps)
+
+
+def rmsnorm(h: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """(h * r) * gamma with r = 1/sqrt(mean(h^2)+eps)."""
+    r = rms_inverse(h, eps)
+    return (np.asarray(h, np.float64) * r) * np.asarray(gamma, np.float64)
+
+
+def rope_angles(pos: int, dim: int, base: float) -> np.ndarray:
+    """theta_i * pos for the dim/2 interleaved pairs, theta_i = base^(-2i/dim)."""
+    i = np.arange(dim // 2, dtype=np.float64)
+    return pos * base ** (-2.0 * i / dim)
+
+
+def rope(x: np.ndarray, pos: int, base: float) -> np.ndarray:
+    """Rotate interleaved pairs (x[2i], x[2i+1]) of the last axis by angle pos * theta_i."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    ang = rope_angles(pos, d, base)
+    c, s = np.cos(ang), np.sin(ang)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+def softmax(s: np.ndarray) -> np.ndarray:
+    s = np.asarray(s, dtype=np.float64)
+    m = np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    z = np.asarray(z, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def topk_desc(score: np.ndarray, k: int) -> np.ndarray:
+    """Indices of the k largest scores, ties to the lower index, in selection order."""
+    score = np.asarray(score, dtype=np.float64)
+    idx = np.arange(score.shape[0])
+    order = np.lexsort((idx, -score))
+    return order[:k]
