@@ -1,0 +1,224 @@
+/*
+ * pld.h — C ABI of the persistent batch-1 decode library (libpld.so, MI355X / gfx950).
+ *
+ * One decode step of one MoE transformer layer runs as ONE launch of a persistent
+ * cooperative kernel: every workgroup stays resident, and the stages (RMSNorm,
+ * projections, attention, output projection + residual, router top-k, experts) are
+ * chained by device-side counters instead of kernel boundaries. This is the
+ * "persistent Engine Kernel" of the TileRT article (InferenceX, "Ultra-High
+ * Interactivity on NVIDIA GPUs? TileRT on InferenceX", section "But What Exactly is
+ * TileRT?": the host launches once and execution stays on the GPU; stages overlap at
+ * tile granularity; intermediates move through on-chip memory and L2), rebuilt for
+ * gfx950 with HIP. The calls follow that article's decode problem: batch 1, one
+ * in-flight request per decode engine, a KV cache prefilled elsewhere and handed over
+ * (section "PD Disaggregated Engine with vLLM and TileRT"); input preparation,
+ * sampling policy and KV-cache management stay with the caller, as in the vLLM Kimi K3
+ * backend article ("A narrow deployment lane"), which also routes unsupported
+ * configurations elsewhere — here they are rejected with PLD_E_UNSUPPORTED.
+ *
+ * Conventions for every call:
+ *  - All tensors are caller-owned DEVICE memory (e.g. allocated by torch). The library
+ *    keeps non-owning pointers; it never allocates, frees or reallocates device memory.
+ *  - Pointers must be 16-byte aligned; reduction dimensions must be multiples of the
+ *    16-byte load width (8 bf16 or 16 FP8 elements).
+ *  - Linear weights are row-major [out, in] ("rows" are outputs). bf16 weights are raw
+ *    bf16 bit patterns. FP8 weights are OCP E4M3FN bytes with one fp32 scale per
+ *    128x128 block: scales[ceil(out/128)][ceil(in/128)], W[n,k] = dec(Q[n,k]) *
+ *    scales[n/128][k/128] (edge blocks have their own scale).
+ *  - Expert weights are stacked per slot: w_gate/w_up [n_experts+n_shared][inter][hidden],
+ *    w_down [n_experts+n_shared][hidden][inter]; shared experts come after the routed
+ *    ones. FP8 expert scales are stacked the same way.
+ *  - Norm gains and router bias are fp32.
+ *  - Errors: every call returns a pld_status. Argument errors are returned
+ *    synchronously before anything is enqueued. Device-side failures (the watchdog of a
+ *    bounded wait) are reported by decode_poll_status after the stream has completed,
+ *    and leave the handle in PLD_E_STATE until decode_reset. No C++ exception crosses
+ *    the ABI.
+ *  - Threading: one handle = one sequence, used from one host thread and one stream at
+ *    a time. Launches on one handle must be stream-ordered.
+ */
+#ifndef PLD_H
+#define PLD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PLD_ABI_VERSION 1
+
+typedef enum pld_status {
+  PLD_OK = 0,
+  PLD_E_INVALID = -1,        /* null or misaligned pointer, bad size, bad index */
+  PLD_E_UNSUPPORTED = -2,    /* configuration outside the supported set (no fallback) */
+  PLD_E_CAPACITY = -3,       /* pos + n_query > max_seq, or workspace too small */
+  PLD_E_HIP = -4,            /* a HIP runtime call failed */
+  PLD_E_DEVICE_TIMEOUT = -5, /* a device wait passed its deadline; see pld_device_status */
+  PLD_E_STATE = -6           /* handle needs decode_reset after a device failure */
+} pld_status;
+
+enum { PLD_ATTN_GQA = 0, PLD_ATTN_MLA = 1 };
+enum { PLD_WFMT_BF16 = 0, PLD_WFMT_FP8_BLOCK128 = 1 };
+enum { PLD_FFN_DENSE = 0, PLD_FFN_MOE = 1 };
+enum { PLD_ROUTER_SOFTMAX_TOPK = 0, PLD_ROUTER_SIGMOID_BIAS = 1 };
+
+/* Layer shape. GQA fields are used when attn_kind == PLD_ATTN_GQA (MHA is
+ * n_kv_heads == n_heads); MLA fields when attn_kind == PLD_ATTN_MLA; index_* when
+ * index_topk > 0 (MLA only). */
+typedef struct pld_config {
+  int32_t attn_kind;
+  int32_t wfmt;
+  int32_t hidden;
+  int32_t n_heads;
+  int32_t n_kv_heads, head_dim;                          /* GQA */
+  int32_t q_lora, kv_lora, rope_dim, nope_dim, v_dim;    /* MLA */
+  int32_t index_heads, index_dim, index_topk;            /* sparse indexer */
+  int32_t ffn_kind;
+  int32_t inter;                                         /* dense width or per-expert width */
+  int32_t n_experts, top_k, n_shared;
+  int32_t router_kind;
+  int32_t max_seq;                                       /* cache capacity in rows */
+  double eps;                                            /* RMSNorm epsilon */
+  double rope_base;                                      /* RoPE base (interleaved pairs) */
+  int32_t vocab;                                         /* LM head rows; 0 = no head */
+  int32_t reserved[5];
+} pld_config;
+
+typedef struct pld_matrix {
+  const void* data;    /* bf16 bits or E4M3FN bytes, [out, in] row-major */
+  const float* scales; /* FP8 only: [ceil(out/128)][ceil(in/128)]; NULL for bf16 */
+} pld_matrix;
+
+typedef struct pld_layer_weights {
+  const float* attn_norm;   /* [hidden] */
+  const float* ffn_norm;    /* [hidden] */
+  const float* q_norm;      /* MLA: [q_lora] */
+  const float* kv_norm;     /* MLA: [kv_lora] */
+  pld_matrix wq, wk, wv;    /* GQA: [n_heads*hd, H], [n_kv*hd, H], [n_kv*hd, H] */
+  pld_matrix w_dq;          /* MLA: [q_lora, H] */
+  pld_matrix w_uq;          /* MLA: [n_heads*(nope+rope), q_lora]; per head nope rows then rope rows */
+  pld_matrix w_dkv;         /* MLA: [kv_lora+rope, H]; latent rows then rope rows */
+  pld_matrix w_uk;          /* MLA: [n_heads*nope, kv_lora] */
+  pld_matrix w_uv;          /* MLA: [n_heads*v_dim, kv_lora] */
+  pld_matrix w_qi;          /* indexer: [index_heads*index_dim, q_lora] */
+  pld_matrix w_w;           /* indexer head weights: [index_heads, H], always bf16 */
+  pld_matrix w_ki;          /* indexer key: [index_dim, H] */
+  pld_matrix wo;            /* [H, n_heads*hd] (GQA) or [H, n_heads*v_dim] (MLA) */
+  const void* router;       /* MoE: bf16 [n_experts, H] */
+  const float* router_bias; /* sigmoid router: [n_experts] */
+  pld_matrix w_gate, w_up;  /* [slots][inter][H] (dense FFN: slots = 1) */
+  pld_matrix w_down;        /* [slots][H][inter] */
+} pld_layer_weights;
+
+/* KV cache of one layer (caller-owned, device). Rows 0..pos-1 must hold the prefilled
+ * history; decode writes row pos. */
+typedef struct pld_kv_cache {
+  void* k;              /* GQA: bf16 [n_kv_heads][max_seq][head_dim] */
+  void* v;              /* GQA: bf16 [n_kv_heads][max_seq][head_dim] */
+  void* latent;         /* MLA: bf16 [max_seq][kv_lora + rope_dim] (c_kv then k_rope) */
+  void* index_codes;    /* indexer: E4M3FN [max_seq][index_dim] */
+  float* index_scales;  /* indexer: fp32 [max_seq] */
+} pld_kv_cache;
+
+/* LM head of a layer stack (only with vocab > 0). */
+typedef struct pld_head_weights {
+  const void* embed;        /* bf16 [vocab][hidden] */
+  const float* final_norm;  /* [hidden] */
+  pld_matrix head;          /* [vocab, hidden], FP8 block-scaled or bf16 (same wfmt as the layers) */
+} pld_head_weights;
+
+/* Device status read back by decode_poll_status. code 0 = ok. */
+typedef struct pld_device_status {
+  int32_t code;       /* 0 ok, PLD_E_DEVICE_TIMEOUT when a wait expired */
+  int32_t stage;      /* stage id whose wait expired */
+  int32_t layer;      /* layer index (within the launch's stack) */
+  int32_t token;      /* token index within the launch */
+  int32_t wg;         /* workgroup that detected it */
+  int32_t reserved[3];
+} pld_device_status;
+
+typedef struct pld_persistent_args {
+  int32_t start_pos;          /* cache position of the first token */
+  int32_t n_tokens;           /* tokens to decode in this launch (greedy loop when a head is present) */
+  int32_t n_query;            /* 1; >1 = multi-position verify (head required) */
+  int32_t in_token;           /* >= 0: first input is embed[in_token]; < 0: use in_hidden */
+  const void* in_hidden;      /* bf16 [hidden] first input when in_token < 0 */
+  const int32_t* draft_tokens;/* verify: device int32 [n_query-1] */
+  void* out_hidden;           /* bf16 [hidden]: output of the last layer for the last position */
+  float* out_logits;          /* fp32 [n_tokens or n_query][vocab], or NULL */
+  int32_t* out_tokens;        /* int32 [n_tokens or n_query] greedy tokens, or NULL */
+  int32_t* out_accepted;      /* verify: int32 [1] accepted draft count, or NULL */
+  int32_t reserved[4];
+} pld_persistent_args;
+
+typedef struct pld_handle pld_handle;
+
+/* Bytes of device workspace decode_layer_init needs for this shape and stack depth
+ * (counters, intermediates, attention partials, RoPE table, layer descriptors).
+ * Returns 0 for an invalid or unsupported configuration. */
+size_t pld_workspace_bytes(const pld_config* cfg, int32_t n_layers);
+
+/* Validate the configuration and pointers, build the static per-workgroup schedule
+ * (the ahead-of-time scheduling of the TileRT article, section "Why Is TileRT
+ * Development Slow?", done here at init), upload the RoPE table and layer
+ * descriptors into `workspace`, zero the counters, and check that the persistent grid
+ * can be co-resident. Synchronous. Nothing is allocated on the device.
+ *   cfg:       layer shape (copied)
+ *   n_layers:  number of layers in `w` and `kv` (>= 1)
+ *   w, kv:     host arrays of n_layers descriptors of device pointers (copied)
+ *   head:      NULL, or LM head weights when cfg->vocab > 0
+ *   workspace: device buffer of at least pld_workspace_bytes(cfg, n_layers) bytes,
+ *              owned by the caller, used exclusively by this handle until destroy
+ *   out:       receives the handle (host memory owned by the library)
+ * Errors: PLD_E_INVALID, PLD_E_UNSUPPORTED, PLD_E_CAPACITY, PLD_E_HIP. */
+pld_status decode_layer_init(const pld_config* cfg, int32_t n_layers, const pld_layer_weights* w,
+                             const pld_kv_cache* kv, const pld_head_weights* head, void* workspace,
+                             size_t ws_bytes, pld_handle** out);
+
+/* Decode one token through layer `layer` in one launch: RMSNorm -> projections ->
+ * RoPE + cache append at row `pos` -> attention over rows 0..pos -> output projection +
+ * residual -> RMSNorm -> router top-k -> routed + shared SwiGLU experts -> residual.
+ * x_in, x_out: device bf16 [hidden] (may alias). Asynchronous on `stream`.
+ * Errors: PLD_E_INVALID (bad layer/pointers), PLD_E_CAPACITY (pos >= max_seq),
+ * PLD_E_STATE, PLD_E_HIP. */
+pld_status decode_step(pld_handle* h, int32_t layer, const void* x_in, int32_t pos, void* x_out,
+                       void* stream);
+
+/* One launch for a whole decode run: for each of a->n_tokens tokens (or the n_query
+ * verify positions), every layer of the stack in order, then (with a head) final
+ * RMSNorm -> LM head -> greedy argmax (lowest id on ties) -> embedding of the chosen
+ * token as the next input. Asynchronous on `stream`.
+ * Errors: PLD_E_INVALID, PLD_E_UNSUPPORTED (verify without head), PLD_E_CAPACITY,
+ * PLD_E_STATE, PLD_E_HIP. */
+pld_status decode_layers_persistent(pld_handle* h, const pld_persistent_args* a, void* stream);
+
+/* Copy the device status word into *out (synchronises the handle's last stream).
+ * Returns PLD_OK, or PLD_E_DEVICE_TIMEOUT if the last launch's watchdog fired. */
+pld_status decode_poll_status(pld_handle* h, pld_device_status* out);
+
+/* Re-zero counters and status so the handle can be used again (synchronous). */
+pld_status decode_reset(pld_handle* h);
+
+/* Free the host-side handle. Device memory stays with the caller. NULL is ignored. */
+void decode_layer_destroy(pld_handle* h);
+
+/* Static description of a status code. */
+const char* pld_status_string(pld_status s);
+
+/* Device pointer and size in bytes of a named intermediate in the workspace, as left by
+ * the last completed launch (for tests): "a", "q", "o", "h2", "b", "logits" (fp64),
+ * "sel" (int32), "gates" (fp32), "m", "x". Returns PLD_E_INVALID for an unknown name. */
+pld_status pld_debug_buffer(pld_handle* h, const char* name, void** ptr, size_t* bytes);
+
+/* Launch geometry actually used: number of workgroups and threads per workgroup. */
+pld_status pld_launch_shape(pld_handle* h, int32_t* n_wg, int32_t* block);
+
+/* Set the watchdog budget of every bounded device wait, in microseconds (default 2e6). */
+pld_status pld_set_watchdog_us(pld_handle* h, int64_t us);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PLD_H */

@@ -1,0 +1,243 @@
+"""Python binding of libpld.so, the persistent batch-1 decode library for MI355X.
+
+Argument marshalling only: every step of the decode path runs in the HIP kernels of
+libpld.so (C ABI in include/pld.h). torch is used for device memory and streams. There
+is no fallback: if the library is missing, using it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional, Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpld.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pld.h")
+
+PLD_OK, PLD_E_INVALID, PLD_E_UNSUPPORTED, PLD_E_CAPACITY, PLD_E_HIP, PLD_E_DEVICE_TIMEOUT, PLD_E_STATE = 0, -1, -2, -3, -4, -5, -6
+PLD_ATTN_GQA, PLD_ATTN_MLA = 0, 1
+PLD_WFMT_BF16, PLD_WFMT_FP8_BLOCK128 = 0, 1
+PLD_FFN_DENSE, PLD_FFN_MOE = 0, 1
+PLD_ROUTER_SOFTMAX_TOPK, PLD_ROUTER_SIGMOID_BIAS = 0, 1
+
+# every entry point include/pld.h declares
+EXPORTS = (
+    "pld_workspace_bytes", "decode_layer_init", "decode_step", "decode_layers_persistent", "decode_poll_status",
+    "decode_reset", "decode_layer_destroy", "pld_status_string", "pld_debug_buffer", "pld_launch_shape",
+    "pld_set_watchdog_us",
+)
+
+i32, vp, f64 = ctypes.c_int32, ctypes.c_void_p, ctypes.c_double
+
+
+class PldConfig(ctypes.Structure):
+    _fields_ = [(n, i32) for n in (
+        "attn_kind", "wfmt", "hidden", "n_heads", "n_kv_heads", "head_dim", "q_lora", "kv_lora", "rope_dim",
+        "nope_dim", "v_dim", "index_heads", "index_dim", "index_topk", "ffn_kind", "inter", "n_experts", "top_k",
+        "n_shared", "router_kind", "max_seq")] + [("eps", f64), ("rope_base", f64), ("vocab", i32),
+                                                   ("reserved", i32 * 5)]
+
+
+class PldMatrix(ctypes.Structure):
+    _fields_ = [("data", vp), ("scales", vp)]
+
+
+class PldLayerWeights(ctypes.Structure):
+    _fields_ = [("attn_norm", vp), ("ffn_norm", vp), ("q_norm", vp), ("kv_norm", vp)] + \
+               [(n, PldMatrix) for n in ("wq", "wk", "wv", "w_dq", "w_uq", "w_dkv", "w_uk", "w_uv", "w_qi", "w_w",
+                                         "w_ki", "wo")] + \
+               [("router", vp), ("router_bias", vp)] + [(n, PldMatrix) for n in ("w_gate", "w_up", "w_down")]
+
+
+class PldKvCache(ctypes.Structure):
+    _fields_ = [("k", vp), ("v", vp), ("latent", vp), ("index_codes", vp), ("index_scales", vp)]
+
+
+class PldHeadWeights(ctypes.Structure):
+    _fields_ = [("embed", vp), ("final_norm", vp), ("head", PldMatrix)]
+
+
+class PldDeviceStatus(ctypes.Structure):
+    _fields_ = [("code", i32), ("stage", i32), ("layer", i32), ("token", i32), ("wg", i32), ("reserved", i32 * 3)]
+
+
+class PldPersistentArgs(ctypes.Structure):
+    _fields_ = [("start_pos", i32), ("n_tokens", i32), ("n_query", i32), ("in_token", i32), ("in_hidden", vp),
+                ("draft_tokens", vp), ("out_hidden", vp), ("out_logits", vp), ("out_tokens", vp),
+                ("out_accepted", vp), ("reserved", i32 * 4)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libpld.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run python -m persistent_latency_bound_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        L.pld_workspace_bytes.argtypes = [ctypes.POINTER(PldConfig), i32]
+        L.pld_workspace_bytes.restype = ctypes.c_size_t
+        L.decode_layer_init.argtypes = [ctypes.POINTER(PldConfig), i32, ctypes.POINTER(PldLayerWeights),
+                                        ctypes.POINTER(PldKvCache), ctypes.POINTER(PldHeadWeights), vp,
+                                        ctypes.c_size_t, ctypes.POINTER(vp)]
+        L.decode_step.argtypes = [vp, i32, vp, i32, vp, vp]
+        L.decode_layers_persistent.argtypes = [vp, ctypes.POINTER(PldPersistentArgs), vp]
+        L.decode_poll_status.argtypes = [vp, ctypes.POINTER(PldDeviceStatus)]
+        L.decode_reset.argtypes = [vp]
+        L.decode_layer_destroy.argtypes = [vp]
+        L.decode_layer_destroy.restype = None
+        L.pld_status_string.argtypes = [i32]
+        L.pld_status_string.restype = ctypes.c_char_p
+        L.pld_debug_buffer.argtypes = [vp, ctypes.c_char_p, ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_size_t)]
+        L.pld_launch_shape.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+        L.pld_set_watchdog_us.argtypes = [vp, ctypes.c_int64]
+        for f in ("decode_layer_init", "decode_step", "decode_layers_persistent", "decode_poll_status",
+                  "decode_reset", "pld_debug_buffer", "pld_launch_shape", "pld_set_watchdog_us"):
+            getattr(L, f).restype = i32
+        _lib = L
+    return _lib
+
+
+class PldError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        msg = lib().pld_status_string(code).decode()
+        super().__init__(f"{what}: {msg} ({code})")
+
+
+def check(code: int, what: str):
+    if code != PLD_OK:
+        raise PldError(code, what)
+
+
+def config_from_shape(s, vocab: int = 0) -> PldConfig:
+    """pld_config of a synth.configs.LayerShape."""
+    c = PldConfig()
+    c.attn_kind = PLD_ATTN_GQA if s.attn == "gqa" else PLD_ATTN_MLA
+    c.wfmt = PLD_WFMT_FP8_BLOCK128 if s.wfmt == "fp8" else PLD_WFMT_BF16
+    c.hidden, c.n_heads, c.n_kv_heads, c.head_dim = s.hidden, s.n_heads, s.n_kv_heads, s.head_dim
+    c.q_lora, c.kv_lora, c.rope_dim, c.nope_dim, c.v_dim = s.q_lora, s.kv_lora, s.rope_dim, s.nope_dim, s.v_dim
+    c.index_heads, c.index_dim, c.index_topk = s.index_heads, s.index_dim, s.index_topk
+    c.ffn_kind = PLD_FFN_MOE if s.ffn == "moe" else PLD_FFN_DENSE
+    c.inter, c.n_experts, c.top_k, c.n_shared = s.inter, s.n_experts, s.top_k, s.n_shared
+    c.router_kind = PLD_ROUTER_SIGMOID_BIAS if s.router == "sigmoid_bias" else PLD_ROUTER_SOFTMAX_TOPK
+    c.max_seq, c.eps, c.rope_base, c.vocab = s.max_seq, s.eps, s.rope_base, vocab
+    return c
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _mat(m) -> PldMatrix:
+    x = PldMatrix()
+    if m is not None:
+        x.data = m["data"].data_ptr()
+        x.scales = _ptr(m.get("scales"))
+    return x
+
+
+def layer_struct(W: dict) -> PldLayerWeights:
+    """pld_layer_weights from a dict of device tensors (as made by synth.device.layer_weights)."""
+    L = PldLayerWeights()
+    for n in ("attn_norm", "ffn_norm", "q_norm", "kv_norm", "router_bias"):
+        if n in W:
+            setattr(L, n, W[n].data_ptr())
+    for n in ("wq", "wk", "wv", "w_dq", "w_uq", "w_dkv", "w_uk", "w_uv", "w_qi", "w_w", "w_ki", "wo", "w_gate",
+              "w_up", "w_down"):
+        if n in W:
+            setattr(L, n, _mat(W[n]))
+    if "router" in W:
+        L.router = W["router"]["data"].data_ptr()
+    return L
+
+
+def cache_struct(C: dict) -> PldKvCache:
+    K = PldKvCache()
+    for n in ("k", "v", "latent", "index_codes", "index_scales"):
+        if n in C:
+            setattr(K, n, C[n].data_ptr())
+    return K
+
+
+class Decoder:
+    """One decode handle over a stack of layers (weights and caches are caller-owned torch tensors)."""
+
+    def __init__(self, shape, layers: Sequence[dict], caches: Sequence[dict], head: Optional[dict] = None,
+                 vocab: int = 0):
+        import torch
+
+        self.shape = shape
+        self.cfg = config_from_shape(shape, vocab)
+        n = len(layers)
+        self._keep = (list(layers), list(caches), head)   # keep the tensors alive
+        ws = lib().pld_workspace_bytes(ctypes.byref(self.cfg), n)
+        if ws == 0:
+            raise PldError(PLD_E_UNSUPPORTED, "pld_workspace_bytes")
+        self.workspace = torch.zeros(ws, dtype=torch.uint8, device="cuda")
+        arr_w = (PldLayerWeights * n)(*[layer_struct(W) for W in layers])
+        arr_c = (PldKvCache * n)(*[cache_struct(C) for C in caches])
+        hp = None
+        if head is not None:
+            h = PldHeadWeights()
+            h.embed = head["embed"].data_ptr()
+            h.final_norm = head["final_norm"].data_ptr()
+            h.head = _mat(head["head"])
+            hp = ctypes.byref(h)
+        self.handle = vp()
+        check(lib().decode_layer_init(ctypes.byref(self.cfg), n, arr_w, arr_c, hp, self.workspace.data_ptr(), ws,
+                                      ctypes.byref(self.handle)), "decode_layer_init")
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.decode_layer_destroy(h)
+            self.handle = None
+
+    @staticmethod
+    def _stream():
+        import torch
+        return vp(torch.cuda.current_stream().cuda_stream)
+
+    def step(self, layer: int, x_in, pos: int, x_out):
+        check(lib().decode_step(self.handle, layer, x_in.data_ptr(), pos, x_out.data_ptr(), self._stream()),
+              "decode_step")
+
+    def persistent(self, start_pos: int, in_hidden=None, out_hidden=None, n_tokens: int = 1, n_query: int = 1,
+                   in_token: int = -1, draft_tokens=None, out_logits=None, out_tokens=None, out_accepted=None):
+        a = PldPersistentArgs()
+        a.start_pos, a.n_tokens, a.n_query, a.in_token = start_pos, n_tokens, n_query, in_token
+        a.in_hidden, a.out_hidden = _ptr(in_hidden), _ptr(out_hidden)
+        a.draft_tokens, a.out_logits = _ptr(draft_tokens), _ptr(out_logits)
+        a.out_tokens, a.out_accepted = _ptr(out_tokens), _ptr(out_accepted)
+        check(lib().decode_layers_persistent(self.handle, ctypes.byref(a), self._stream()), "decode_layers_persistent")
+
+    def status(self) -> PldDeviceStatus:
+        st = PldDeviceStatus()
+        rc = lib().decode_poll_status(self.handle, ctypes.byref(st))
+        if rc not in (PLD_OK, PLD_E_DEVICE_TIMEOUT):
+            check(rc, "decode_poll_status")
+        return st
+
+    def reset(self):
+        check(lib().decode_reset(self.handle), "decode_reset")
+
+    def set_watchdog_us(self, us: int):
+        check(lib().pld_set_watchdog_us(self.handle, int(us)), "pld_set_watchdog_us")
+
+    def launch_shape(self):
+        n, b = i32(), i32()
+        check(lib().pld_launch_shape(self.handle, ctypes.byref(n), ctypes.byref(b)), "pld_launch_shape")
+        return n.value, b.value
+
+    def debug(self, name: str, dtype=None):
+        """Copy of an intermediate left in the workspace by the last launch (after a sync)."""
+        import torch
+        p, nb = vp(), ctypes.c_size_t()
+        check(lib().pld_debug_buffer(self.handle, name.encode(), ctypes.byref(p), ctypes.byref(nb)), "pld_debug_buffer")
+        off = p.value - self.workspace.data_ptr()
+        raw = self.workspace[off: off + nb.value].clone()
+        dt = dtype or {"logits": torch.float64, "sel": torch.int32, "x": torch.int32}.get(name, torch.float32)
+        return raw.view(dt)

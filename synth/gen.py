@@ -32,6 +32,8 @@ host and device agree bit for bit):
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 from .configs import LayerShape, ModelShape
@@ -87,11 +89,30 @@ def normal_f32(seed: int, tid: int, index: np.ndarray) -> np.ndarray:
     return s.astype(np.float32) * INV_SIGMA
 
 
-def scaled_normal(seed, tid, index, std, mean=None) -> np.ndarray:
+def _scaled_normal_1(seed, tid, index, std, mean):
     v = normal_f32(seed, tid, index) * np.float32(std)
     if mean is not None:
         v = v + np.float32(mean)
     return v
+
+
+_POOL = None
+
+
+def scaled_normal(seed, tid, index, std, mean=None) -> np.ndarray:
+    """std * N(0,1) (+ mean) at the given element indices (large requests run in threads)."""
+    index = np.asarray(index, dtype=U64)
+    n = index.size
+    if n < (1 << 21):
+        return _scaled_normal_1(seed, tid, index, std, mean)
+    global _POOL
+    if _POOL is None:
+        from concurrent.futures import ThreadPoolExecutor
+        _POOL = ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1))
+    flat = index.reshape(-1)
+    parts = np.array_split(np.arange(n), 16)
+    outs = list(_POOL.map(lambda ix: _scaled_normal_1(seed, tid, flat[ix], std, mean), parts))
+    return np.concatenate(outs).reshape(index.shape)
 
 
 def f32_to_bf16_bits(v: np.ndarray) -> np.ndarray:
