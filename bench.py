@@ -1,0 +1,241 @@
+"""Benchmark of the persistent batch-1 decode layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers R] [--no-cpu-baseline]
+
+Workload: the single MoE decode layer, batch 1, bf16 — hidden 4096, GQA 32 q / 8 kv heads x
+128, 8192-token KV cache, router over 64 experts (top-8, softmax renormalised), expert
+SwiGLU width 1536 plus one shared expert; weights N(0, 0.02), router N(0, 0.1). A step
+decodes one token through a stack of R independent seeded copies of that layer in ONE
+launch of the persistent kernel (decode_layers_persistent). R copies keep the weights
+cold: R x 458 MB is far larger than the 256 MB Infinity Cache, so the bytes come from
+HBM. Each step gets its own seeded input vector (all resident before timing), so the
+routed experts change from step to step. The cache position stays at 8192 (the step
+rewrites the same row), so every step does the same work.
+
+Prints ONE JSON line: value = microseconds per layer (lower is better), plus the HBM
+roofline of the kernel (algorithmic bytes per launch / measured launch time) and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
+WORKLOAD = "gqa_moe_bf16_decode_layer"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gqa_moe_bf16.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "persistent_latency_bound_amd", "csrc", f)
+                  for f in ("pld_kernel.hip", "pld_device.hpp")]
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_per_launch(layers: int):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    t = json.load(open(TRAFFIC_FILE))
+    if t.get("kernel_sha") != kernel_sha() or t.get("layers_per_launch") != layers:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(shape, pos: int, budget_s: float = 20.0) -> dict:
+    """The CPU oracle (unchanged) on a bounded sample: whole layer-tokens of the same workload."""
+    import numpy as np
+    from oracle import layer as OL
+    from synth import gen
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from gpu_common import host_cache
+
+    W = gen.LayerWeights(shape, 0, 0, cache_size=256)
+    cache = host_cache(shape)
+    x = gen.input_hidden(shape, 0, 0)
+    OL.decode_layer(shape, W, cache, x, pos)          # generates and caches the weights it touches
+    n, t0 = 0, time.perf_counter()
+    while True:
+        OL.decode_layer(shape, W, cache, x, pos)
+        n += 1
+        if time.perf_counter() - t0 > budget_s / 2 or n >= 8:
+            break
+    dt = (time.perf_counter() - t0) / n
+    cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"value": round(dt * 1e6, 1), "unit": "us/layer", "cores": cores, "kind": "oracle",
+            "sample": f"{n} layer-token(s) of the same layer at position {pos} after one warm-up call that "
+                      f"generates the weights; fp64 NumPy, BLAS and generator threads = {cores}"}
+
+
+STAMPS = ["start", "x_ready", "qkv_done", "att_ready", "att_done", "o_ready", "wo_done", "h2_ready",
+          "router_ready", "ffn_done", "m_ready", "down_done"]
+
+
+def write_trace_summary(dec, shape, pos, x, out, R, path):
+    """One extra (untimed) launch with the device trace on; per-stage wait and work times."""
+    import numpy as np
+    import torch
+    nwg, _ = dec.launch_shape()
+    buf = torch.zeros(R * nwg * 32, dtype=torch.int64, device="cuda")
+    dec.set_trace(buf)
+    dec.persistent(start_pos=pos, in_hidden=x, out_hidden=out)
+    torch.cuda.synchronize()
+    dec.set_trace(None)
+    t = buf.cpu().numpy().reshape(R, nwg, 32)[:, :, :len(STAMPS)].astype(np.float64)
+    tick_us = 1e-2   # wall_clock64 runs at 100 MHz on MI355X (hipDeviceAttributeWallClockRate = 100000 kHz)
+    rel = (t - t[:, :, :1].min(axis=1, keepdims=True)) * tick_us
+    seg = {}
+    names = list(zip(STAMPS[:-1], STAMPS[1:]))
+    for i, (a_, b_) in enumerate(names):
+        d = (t[:, :, i + 1] - t[:, :, i]) * tick_us
+        seg[f"{a_}->{b_}"] = {"median_us": round(float(np.median(d)), 2), "max_us": round(float(d.max()), 2)}
+    full = buf.cpu().numpy().reshape(R, nwg, 32).astype(np.float64)
+    att = {}
+    for name, i0, i1 in (("att_ready->q_loaded", 3, 12), ("q_loaded->softmax", 12, 13), ("softmax->partial_stored", 13, 14),
+                         ("partial_stored->att_done", 14, 4), ("x_ready->qkv_gemv", 1, 21), ("qkv_gemv->qkv_done", 21, 2),
+                         ("h2_ready->shared_gemv", 7, 22), ("shared_gemv->router_ready", 22, 8),
+                         ("router_ready->topk", 8, 16), ("topk->m_stored", 16, 18),
+                         ("m_stored->ffn_done", 18, 9), ("m_ready->down_gemv", 10, 19), ("down_gemv->out_stored", 19, 20),
+                         ("out_stored->down_done", 20, 11)):
+        d = (full[:, :, i1] - full[:, :, i0]) * tick_us
+        att[name] = {"median_us": round(float(np.median(d)), 2), "max_us": round(float(d.max()), 2)}
+    merged = full[:, :, 15] > 0
+    if merged.any():
+        d = (full[:, :, 15] - full[:, :, 14])[merged] * tick_us
+        att["partial_stored->merged (mergers only)"] = {"median_us": round(float(np.median(d)), 2), "max_us": round(float(d.max()), 2)}
+    seg["attention_detail"] = att
+    layer_us = [(t[l, :, -1].max() - t[l, :, 0].min()) * tick_us for l in range(R)]
+    summary = {"layers": R, "nwg": nwg, "segments": seg,
+               "layer_critical_path_us": [round(float(v), 2) for v in layer_us],
+               "stamp_median_us_from_layer_start": {n: round(float(np.median(rel[:, :, i])), 2) for i, n in enumerate(STAMPS)}}
+    with open(path, "w") as f:
+        json.dump(summary, f, indent=1)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace", default=None, help="write a per-stage device-trace summary (JSON) to this path")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="first run one plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is not built.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import persistent_latency_bound_amd as pld
+    from oracle import accounting
+    from synth import configs, device as sdev
+
+    if args.calib_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    shape = configs.C2
+    pos = shape.cache_len
+    R = args.layers
+    Ws = [sdev.layer_weights(shape, 0, l) for l in range(R)]
+    Cs = [sdev.kv_cache(shape, 0, l) for l in range(R)]
+    n_in = args.steps + args.warmup
+    xs = [sdev.input_hidden(shape, 0, i) for i in range(n_in)]
+    out = torch.zeros(shape.hidden, dtype=torch.int16, device="cuda")
+    dec = pld.Decoder(shape, Ws, Cs)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        dec.persistent(start_pos=pos, in_hidden=xs[i], out_hidden=out)
+    torch.cuda.synchronize()
+    st = dec.status()
+    if st.code != 0:
+        raise SystemExit(f"device status {st.code} at stage {st.stage}")
+
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        dec.persistent(start_pos=pos, in_hidden=xs[args.warmup + i], out_hidden=out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1)
+    st = dec.status()
+    if st.code != 0:
+        raise SystemExit(f"device status {st.code} at stage {st.stage}")
+    ms_per_step = ms / args.steps
+    us_per_layer = ms_per_step * 1e3 / R
+
+    # single-launch decode_step (one layer per launch, launch cost included)
+    x1 = xs[0]
+    for _ in range(5):
+        dec.step(0, x1, pos, out)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    n1 = 50
+    for i in range(n1):
+        dec.step(i % R, x1, pos, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    single_us = e0.elapsed_time(e1) * 1e3 / n1
+
+    if args.trace:
+        write_trace_summary(dec, shape, pos, xs[0], out, R, args.trace)
+
+    bytes_layer = accounting.layer_bytes(shape, pos)
+    bytes_launch = bytes_layer * R
+    achieved = bytes_launch / (ms_per_step * 1e-3) / 1e9
+    traffic = traffic_per_launch(R)
+    line = {
+        "metric": "batch-1 decode us/layer (achieved HBM TB/s vs peak, implied tokens/s/user)",
+        "value": round(us_per_layer, 3),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD, "hidden": shape.hidden, "heads": f"{shape.n_heads}q/{shape.n_kv_heads}kv x {shape.head_dim}",
+                   "kv_cache_tokens": pos, "experts": f"{shape.n_experts} top-{shape.top_k} + {shape.n_shared} shared",
+                   "expert_inter": shape.inter, "layers_per_launch": R, "tokens_per_step": 1, "batch": 1},
+        "achieved_TBps": round(achieved / 1e3, 3),
+        "frac_of_peak": round(achieved / PEAK_HBM_GBPS, 4),
+        "implied_tokens_per_s_user_24_layers": round(1e6 / (us_per_layer * 24), 1),
+        "single_launch_us_per_layer": round(single_us, 3),
+        "launches_per_token": round(1.0 / R, 4),
+        "algorithmic_bytes_per_layer": bytes_layer,
+        "wall_s_timed_region": round(wall, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": None if traffic is None else round(traffic / (ms_per_step * 1e-3) / 1e9, 1)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(shape, pos)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -208,12 +208,24 @@ void decode_layer_destroy(pld_handle* h);
 const char* pld_status_string(pld_status s);
 
 /* Device pointer and size in bytes of a named intermediate in the workspace, as left by
- * the last completed launch (for tests): "a", "q", "o", "h2", "b", "logits" (fp64),
+ * the last completed launch (for tests): "a", "q", "o", "h2", "b", "logits" (fp64 pairs
+ * (logit, selection key) per expert),
  * "sel" (int32), "gates" (fp32), "m", "x". Returns PLD_E_INVALID for an unknown name. */
 pld_status pld_debug_buffer(pld_handle* h, const char* name, void** ptr, size_t* bytes);
 
 /* Launch geometry actually used: number of workgroups and threads per workgroup. */
 pld_status pld_launch_shape(pld_handle* h, int32_t* n_wg, int32_t* block);
+
+/* Device trace for profiling inside one launch: while set, every later launch writes,
+ * for each (step, workgroup) of its first bytes/(n_wg*16*8) steps (a step is one layer of
+ * one token), 16 uint64 wall-clock stamps (hipDeviceAttributeWallClockRate ticks) at
+ * fixed points of the step: 0 start, 1 input ready, 2 q/k/v published, 3 attention inputs
+ * ready, 4 attention done, 5 attention output ready, 6 residual h2 published, 7 h2 ready,
+ * 8 router top-k ready, 9 expert activations published, 10 expert activations ready,
+ * 11 layer output published (unused slots are left untouched). buffer: device memory of
+ * `bytes` bytes, 8-aligned, owned by the caller; NULL turns tracing off. Returns
+ * PLD_E_CAPACITY if the buffer cannot hold one step. */
+pld_status pld_set_trace(pld_handle* h, void* buffer, size_t bytes);
 
 /* Set the watchdog budget of every bounded device wait, in microseconds (default 2e6). */
 pld_status pld_set_watchdog_us(pld_handle* h, int64_t us);

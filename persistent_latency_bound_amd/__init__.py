@@ -24,7 +24,7 @@ PLD_ROUTER_SOFTMAX_TOPK, PLD_ROUTER_SIGMOID_BIAS = 0, 1
 EXPORTS = (
     "pld_workspace_bytes", "decode_layer_init", "decode_step", "decode_layers_persistent", "decode_poll_status",
     "decode_reset", "decode_layer_destroy", "pld_status_string", "pld_debug_buffer", "pld_launch_shape",
-    "pld_set_watchdog_us",
+    "pld_set_watchdog_us", "pld_set_trace",
 )
 
 i32, vp, f64 = ctypes.c_int32, ctypes.c_void_p, ctypes.c_double
@@ -93,8 +93,9 @@ def lib():
         L.pld_debug_buffer.argtypes = [vp, ctypes.c_char_p, ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_size_t)]
         L.pld_launch_shape.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.pld_set_watchdog_us.argtypes = [vp, ctypes.c_int64]
+        L.pld_set_trace.argtypes = [vp, vp, ctypes.c_size_t]
         for f in ("decode_layer_init", "decode_step", "decode_layers_persistent", "decode_poll_status",
-                  "decode_reset", "pld_debug_buffer", "pld_launch_shape", "pld_set_watchdog_us"):
+                  "decode_reset", "pld_debug_buffer", "pld_launch_shape", "pld_set_watchdog_us", "pld_set_trace"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -227,6 +228,14 @@ class Decoder:
     def set_watchdog_us(self, us: int):
         check(lib().pld_set_watchdog_us(self.handle, int(us)), "pld_set_watchdog_us")
 
+    def set_trace(self, buf):
+        """Record per-stage wall-clock stamps into `buf` (int64 device tensor) on later launches; None stops."""
+        if buf is None:
+            check(lib().pld_set_trace(self.handle, None, 0), "pld_set_trace")
+        else:
+            check(lib().pld_set_trace(self.handle, buf.data_ptr(), buf.numel() * buf.element_size()), "pld_set_trace")
+        self._trace = buf
+
     def launch_shape(self):
         n, b = i32(), i32()
         check(lib().pld_launch_shape(self.handle, ctypes.byref(n), ctypes.byref(b)), "pld_launch_shape")
@@ -239,5 +248,5 @@ class Decoder:
         check(lib().pld_debug_buffer(self.handle, name.encode(), ctypes.byref(p), ctypes.byref(nb)), "pld_debug_buffer")
         off = p.value - self.workspace.data_ptr()
         raw = self.workspace[off: off + nb.value].clone()
-        dt = dtype or {"logits": torch.float64, "sel": torch.int32, "x": torch.int32}.get(name, torch.float32)
+        dt = dtype or {"logits": torch.float64, "sel": torch.int32, "x": torch.int16}.get(name, torch.float32)
         return raw.view(dt)

@@ -73,6 +73,12 @@ __device__ __forceinline__ double ld_f64(const double* p) {
   return __longlong_as_double((long long)__hip_atomic_load(gp(reinterpret_cast<uint64_t*>(const_cast<double*>(p))),
                                                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
+__device__ __forceinline__ uint64_t ld_u64(const uint64_t* p) {
+  return __hip_atomic_load(gp(const_cast<uint64_t*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ uint32_t atomic_add_u32(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -100,6 +106,27 @@ __device__ __forceinline__ T wave_max(T v) {
   for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
   return v;
 }
+// Sum over groups of N consecutive lanes (N = 8, 16, 32 or 64) with DPP lane moves, which
+// run in the vector ALU (a __shfl_xor compiles to an LDS permute). The group sum is valid
+// in the group's LAST lane (for N = 8 and 16 in every lane of the group).
+template <int CTRL, int ROW_MASK, bool BOUND>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, BOUND));
+}
+template <int N>
+__device__ __forceinline__ float dpp_sum(float v) {
+  static_assert(N == 8 || N == 16 || N == 32 || N == 64, "group size");
+  v += dpp_mov<0xB1, 0xf, false>(v);    // quad_perm [1,0,3,2]
+  v += dpp_mov<0x4E, 0xf, false>(v);    // quad_perm [2,3,0,1]
+  v += dpp_mov<0x141, 0xf, false>(v);   // row_half_mirror: sums of 8
+  if constexpr (N >= 16) v += dpp_mov<0x140, 0xf, false>(v);   // row_mirror: sums of 16 (each row)
+  // row_bcast15: lane 15 of row r is added into row r+1 (only rows 1 and 3 are written)
+  if constexpr (N >= 32) v += dpp_mov<0x142, 0xa, true>(v);
+  // row_bcast31: lane 31 is added into rows 2 and 3
+  if constexpr (N >= 64) v += dpp_mov<0x143, 0xc, true>(v);
+  return v;
+}
+
 // Block-wide sum in a fixed order (wave sums, then wave 0..7 in order). All threads get the result.
 template <typename T>
 __device__ __forceinline__ T block_sum(T v, T* red) {
@@ -157,116 +184,164 @@ struct DMat {
   int rows, cols, sbk; // sbk = ceil(cols/128)
 };
 
+// Copies n 32-bit words of cross-workgroup data (written with write-through stores by
+// other workgroups) into LDS. Each thread issues PER independent 8-byte agent-scope
+// loads before using any of them, so the copy costs about one device-coherence-point
+// latency per PER*BLOCK*2 words instead of one per word. n must be even, src 8-aligned.
+template <int PER = 8>
+__device__ __forceinline__ void coh_copy_to_lds(uint32_t* dst, const uint32_t* src, int n) {
+  const uint64_t* s = reinterpret_cast<const uint64_t*>(src);
+  const int n2 = n >> 1;
+  for (int base = 0; base < n2; base += BLOCK * PER) {
+    uint64_t v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; j++) {
+      const int i = base + j * BLOCK + threadIdx.x;
+      v[j] = i < n2 ? ld_u64(s + i) : 0ull;
+    }
+#pragma unroll
+    for (int j = 0; j < PER; j++) {
+      const int i = base + j * BLOCK + threadIdx.x;
+      if (i < n2) {
+        dst[2 * i] = (uint32_t)v[j];
+        dst[2 * i + 1] = (uint32_t)(v[j] >> 32);
+      }
+    }
+  }
+}
+
 // Output handling of a GEMV: out[r - r0] = v (store) or out[r - r0] += alpha * v.
 enum OutMode { OUT_STORE = 0, OUT_ACCUM = 1 };
 
 // Lane layout per reduction length K (elements) and weight format, fixed at compile time:
-// LPR lanes per row, CPL 16-byte chunks per lane and row, U rows in flight per wave.
+// LPR lanes per row, CPL 16-byte chunks per lane and row, U rows in flight per wave
+// (U*CPL ~ 24 loads of 16 bytes per lane: ~190 KB in flight per 512-thread workgroup).
 template <bool FP8, int K>
 struct GemvLayout {
   static constexpr int EPC = FP8 ? 16 : 8;
   static constexpr int CHUNKS = K / EPC;
   static constexpr int LPR = CHUNKS >= 64 ? 64 : CHUNKS;
   static constexpr int CPL = CHUNKS / LPR;
-  static constexpr int U = CPL >= 4 ? 2 : (CPL >= 2 ? 4 : 8);
+  static constexpr int U0 = 24 / CPL;
+  static constexpr int U = U0 < 1 ? 1 : (U0 > 12 ? 12 : U0);
   static_assert(K % EPC == 0 && CHUNKS % LPR == 0 && (LPR == 16 || LPR == 32 || LPR == 64), "unsupported K");
 };
 
-// Streams rows [r0, r1) of a [rows, K] weight matrix against an fp32 activation vector
-// in LDS.
+// A GEMV task is a list of row segments streamed as one pipeline: segment s holds n
+// consecutive rows starting at w (row stride K elements), FP8 scales s (row-block
+// stride ceil(K/128)) with row offset srow, reads the activation at act + act_off, and
+// scales its row results by alpha (OUT_ACCUM). Results land in out[] in list order.
+struct RowSeg {
+  const uint8_t* w;
+  const float* s;
+  int n;
+  int srow;      // row index of w's first row inside its scale grid (FP8)
+  int act_off;
+  float alpha;
+};
+constexpr int MAX_SEGS = 12;
+
+// Streams the rows of a segment list against fp32 activation vectors in LDS.
 //  * LPR lanes share one row (64/LPR rows per wave pass); each lane reads CPL 16-byte
 //    chunks per row, chunk j of lane l covering elements [(j*LPR + l) * EPC, +EPC);
-//  * a wave keeps U rows of loads in flight (U*CPL 16-byte loads per lane);
+//  * a wave keeps U rows of loads in flight; the pipeline runs through all segments;
 //  * the first U rows are issued BEFORE `pre()` runs -- pre is where the caller waits
 //    for its dependency and stages the activation into LDS -- so the wait overlaps with
 //    the first weight bytes arriving; only static weights are loaded ahead of a wait;
 //  * partial sums are reduced across the LPR lanes and the row's first lane writes the
-//    result into `out` (LDS) per OutMode.
-// Returns false if pre() reported an abort.
-template <bool FP8, int K, typename ACC, typename Pre>
-__device__ __forceinline__ bool gemv(const uint8_t* __restrict__ W, const float* __restrict__ S, int r0, int r1,
-                                     const float* act, ACC* out, int mode, float alpha, Pre&& pre) {
+//    result into out[i] (LDS) per OutMode.
+// `segs` lives in LDS. Returns false if pre() reported an abort.
+template <bool FP8, int K, typename Pre>
+__device__ __forceinline__ bool gemv_list(const RowSeg* segs, int nseg, const float* act, float* out, int mode,
+                                          Pre&& pre) {
   using LY = GemvLayout<FP8, K>;
   constexpr int EPC = LY::EPC, LPR = LY::LPR, CPL = LY::CPL, U = LY::U;
   constexpr int RPW = 64 / LPR;
   constexpr int SBK = (K + 127) / 128;
-  // activations stay in registers when they fit beside the in-flight loads, else they
-  // are re-read from LDS per chunk (ds_read_b128, 2-4 LDS bytes per weight byte)
-  constexpr bool AREG = CPL * EPC <= 32;
+  constexpr size_t RS = (size_t)K * (FP8 ? 1 : 2);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane % LPR, rsub = lane / LPR;
-  const int nrows = r1 - r0;
+  int nrows = 0;
+  for (int s = 0; s < nseg; s++) nrows += segs[s].n;
   const int groups = (nrows + RPW - 1) / RPW;
   const int iters = (groups + NWAVES - 1) / NWAVES;
-  constexpr size_t RS = (size_t)K * (FP8 ? 1 : 2);
+  constexpr int STEP = NWAVES * RPW;   // list rows between consecutive rows of one lane
   uint4 buf[U][CPL];
   float sc[FP8 ? U : 1][FP8 ? CPL : 1];
-  // rows past r1 re-read the last valid row (results discarded): no predicated loads
-  auto issue = [&](int it, int u) {
-    const int r = min(r0 + (it * NWAVES + wave) * RPW + rsub, r1 - 1);
-    const uint8_t* p = W + (size_t)r * RS + (size_t)li * 16;
+  // Per-lane cursor over the segment list: (segment, row in segment). Rows advance by
+  // STEP; crossing into the next segment costs one LDS read of its length. Rows past the
+  // end of the list clamp to the last row (their results are discarded).
+  struct Cursor {
+    int seg, r;
+  };
+  auto advance = [&](Cursor& c, int by) {
+    c.r += by;
+    int n = segs[c.seg].n;
+    while (c.r >= n && c.seg < nseg - 1) {
+      c.r -= n;
+      c.seg++;
+      n = segs[c.seg].n;
+    }
+  };
+  auto clamp_row = [&](const Cursor& c) { return c.seg == nseg - 1 ? min(c.r, segs[c.seg].n - 1) : c.r; };
+  Cursor ci{0, -STEP}, cc{0, -STEP};   // issue cursor runs U rows ahead of the compute cursor
+  const int first = wave * RPW + rsub;
+  auto issue = [&](int u) {
+    const RowSeg& S = segs[ci.seg];
+    const int r = clamp_row(ci);
+    const uint8_t* p = S.w + (size_t)r * RS + (size_t)li * 16;
 #pragma unroll
     for (int j = 0; j < CPL; j++) buf[u][j] = ld_stream16(p + (size_t)j * LPR * 16);
     if constexpr (FP8) {
-      const PLD_GLOBAL float* sr = gp(S) + (size_t)(r >> 7) * SBK;
+      const PLD_GLOBAL float* sr = gp(S.s) + (size_t)((S.srow + r) >> 7) * SBK;
 #pragma unroll
       for (int j = 0; j < CPL; j++) sc[u][j] = sr[((j * LPR + li) * 16) >> 7];
     }
   };
   if (nrows > 0) {
+    ci.r = 0;
+    advance(ci, first);
+    cc = ci;
 #pragma unroll
-    for (int u = 0; u < U; u++) issue(u, u);
+    for (int u = 0; u < U; u++) {
+      issue(u);
+      if (u + 1 < U) advance(ci, STEP);
+    }
   }
   if (!pre()) return false;
   if (nrows <= 0) return true;
-  float av[AREG ? CPL : 1][AREG ? EPC : 1];
-  if constexpr (AREG) {
-#pragma unroll
-    for (int j = 0; j < CPL; j++) {
-      const float4* ap = reinterpret_cast<const float4*>(act + (j * LPR + li) * EPC);
-#pragma unroll
-      for (int q = 0; q < EPC / 4; q++) {
-        const float4 t = ap[q];
-        av[j][4 * q] = t.x; av[j][4 * q + 1] = t.y; av[j][4 * q + 2] = t.z; av[j][4 * q + 3] = t.w;
-      }
-    }
-  }
 #pragma unroll 1
   for (int it = 0; it < iters; it += U) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int cur = it + u;
-      ACC acc = 0;
+      const int i = cur * STEP + first;
+      const RowSeg& S = segs[cc.seg];
+      const float* a = act + S.act_off;
+      const float alpha = S.alpha;
+      const int oi = i;
+      float acc = 0.f;
 #pragma unroll
       for (int j = 0; j < CPL; j++) {
-        float atmp[EPC];
-        const float* aj;
-        if constexpr (AREG) {
-          aj = av[j];
-        } else {
-          const float4* ap = reinterpret_cast<const float4*>(act + (j * LPR + li) * EPC);
+        float at[EPC];
+        const float4* ap = reinterpret_cast<const float4*>(a + (j * LPR + li) * EPC);
 #pragma unroll
-          for (int q = 0; q < EPC / 4; q++) {
-            const float4 t = ap[q];
-            atmp[4 * q] = t.x; atmp[4 * q + 1] = t.y; atmp[4 * q + 2] = t.z; atmp[4 * q + 3] = t.w;
-          }
-          aj = atmp;
+        for (int q = 0; q < EPC / 4; q++) {
+          const float4 t = ap[q];
+          at[4 * q] = t.x; at[4 * q + 1] = t.y; at[4 * q + 2] = t.z; at[4 * q + 3] = t.w;
         }
-        if constexpr (FP8) {
-          acc += (ACC)(sc[u][j] * dot16_fp8(buf[u][j], aj));
-        } else if constexpr (sizeof(ACC) == 8) {
-          acc += dot8_bf16_f64(buf[u][j], aj);
-        } else {
-          acc += dot8_bf16(buf[u][j], aj);
-        }
+        if constexpr (FP8) acc += sc[u][j] * dot16_fp8(buf[u][j], at);
+        else acc += dot8_bf16(buf[u][j], at);
       }
-      if (cur + U < iters) issue(cur + U, u);
-#pragma unroll
-      for (int off = LPR / 2; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-      const int r = r0 + (cur * NWAVES + wave) * RPW + rsub;
-      if (li == 0 && cur < iters && r < r1) {
-        if (mode == OUT_STORE) out[r - r0] = acc;
-        else out[r - r0] += (ACC)alpha * acc;
+      if (cur + U < iters) {
+        advance(ci, STEP);
+        issue(u);
+      }
+      advance(cc, STEP);
+      acc = dpp_sum<LPR>(acc);
+      if (li == LPR - 1 && cur < iters && oi < nrows) {
+        if (mode == OUT_STORE) out[oi] = acc;
+        else out[oi] += alpha * acc;
       }
     }
   }

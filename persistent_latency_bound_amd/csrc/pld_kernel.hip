@@ -42,6 +42,13 @@ namespace pld {
 // ------------------------------------------------------------------ shared structs
 enum Stage { S_QKV = 0, S_H2 = 1, S_RT = 2, S_M = 3, S_OUT = 4, NSTG = 8 };
 enum { ST_CODE = 0, ST_STAGE = 1, ST_LAYER = 2, ST_TOKEN = 3, ST_WG = 4, ST_ABORT = 8 };
+// device trace: wall-clock stamps per (step, workgroup)
+enum TraceSlot {
+  TR_START = 0, TR_X_READY, TR_QKV_DONE, TR_ATT_READY, TR_ATT_DONE, TR_O_READY, TR_WO_DONE, TR_H2_READY,
+  TR_RT_READY, TR_FFN_DONE, TR_M_READY, TR_DOWN_DONE, TR_ATT_Q = 12, TR_ATT_SOFTMAX = 13, TR_ATT_PARTIAL = 14,
+  TR_ATT_MERGED = 15, TR_TOPK = 16, TR_ROUTED_GEMV = 17, TR_M_STORED = 18, TR_DOWN_GEMV = 19, TR_DOWN_EPI = 20,
+  TR_QKV_GEMV = 21, TR_SHARED_GEMV = 22, TR_SLOTS = 32
+};
 
 struct KCfg {
   int attn, wfmt, H, nh, nkv, hd, q_lora, kv_lora, rope, nope, vdim, ih, idim, itopk;
@@ -51,7 +58,7 @@ struct KCfg {
   int G;       // q heads per kv head
   int cpg;     // attention chunks per kv head = workgroups per kv head
   int chmax;   // max tokens in one attention chunk
-  int act_floats, outb_floats;
+  int act_floats, stage_words, outb_floats;
   int nwg;
 };
 
@@ -81,6 +88,8 @@ struct KArgs {
   const uint16_t* in_hidden;
   uint16_t* out_hidden;
   long long budget;
+  uint64_t* trace;     // [trace_steps][nwg][TR_SLOTS] or null
+  int trace_steps;
 };
 
 // ------------------------------------------------------------------ device context
@@ -144,114 +153,98 @@ __device__ __forceinline__ bool wait_all(Ctx& cx, int stage, uint32_t k1, int n_
   return spin_until(cx, cx.ctr_glob + stage * CTR_STRIDE, k1 * groups, stage);
 }
 
-// Hidden-state source: the caller's bf16 input, or the in-launch buffer of bf16 words.
-struct XSrc {
-  const uint16_t* p16;
-  const uint32_t* p32;
-  __device__ __forceinline__ float operator()(int i) const {
-    return p32 ? __uint_as_float(ld_u32(p32 + i) << 16) : bf16_to_f32(gp(p16)[i]);
-  }
-};
-
-// act[i] = fp32((x_i * r) * g_i), r = 1/sqrt(sum(x^2)/n + eps), statistics in fp64.
-template <typename LoadX>
-__device__ __forceinline__ void rmsnorm_to_lds(LoadX ldx, const float* __restrict__ gamma, int n, double eps, float* act, double* red) {
-  double ss = 0.0;
-  for (int i = threadIdx.x; i < n; i += BLOCK) {
-    const float v = ldx(i);
-    act[i] = v;
-    ss += (double)v * (double)v;
-  }
-  ss = block_sum(ss, red);
-  const double r = 1.0 / sqrt(ss / (double)n + eps);
-  for (int i = threadIdx.x; i < n; i += BLOCK) act[i] = (float)(((double)act[i] * r) * (double)gp(gamma)[i]);
-  __syncthreads();
-}
-
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// ------------------------------------------------------------------ top-k (one wave)
-// Selects k of n fp64 scores (desc, lowest index on ties); writes indices in selection order.
-__device__ void wave_topk(const double* score, int n, int k, int* sel_out) {
-  const int lane = threadIdx.x & 63;
-  constexpr int PER = 8;   // up to 512 candidates
-  double v[PER];
-  int id[PER];
-#pragma unroll
-  for (int i = 0; i < PER; i++) {
-    const int e = lane + 64 * i;
-    v[i] = e < n ? score[e] : -INFINITY;
-    id[i] = e < n ? e : 0x7fffffff;
-  }
-  for (int s = 0; s < k; s++) {
-    double bv = -INFINITY;
-    int bi = 0x7fffffff;
-#pragma unroll
-    for (int i = 0; i < PER; i++)
-      if (v[i] > bv || (v[i] == bv && id[i] < bi)) { bv = v[i]; bi = id[i]; }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double ov = __shfl_xor(bv, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    if (lane == 0) sel_out[s] = bi;
-#pragma unroll
-    for (int i = 0; i < PER; i++)
-      if (id[i] == bi) { v[i] = -INFINITY; id[i] = 0x7fffffff; }
-  }
+// In-place RMSNorm of act[0..n): act = fp32((act * r) * gamma), r = 1/sqrt(sum(act^2)/n + eps)
+// with the statistics in fp64 (bf16 and fp32 squares are exact in fp64).
+__device__ __forceinline__ void rmsnorm_inplace(float* act, const float* __restrict__ gamma, int n, double eps,
+                                                double* red) {
+  double ss = 0.0;
+  for (int i = threadIdx.x; i < n; i += BLOCK) ss += (double)act[i] * (double)act[i];
+  ss = block_sum(ss, red);
+  const double r = 1.0 / sqrt(ss / (double)n + eps);
+  const PLD_GLOBAL float* g = gp(gamma);
+  for (int i = threadIdx.x; i < n; i += BLOCK) act[i] = (float)(((double)act[i] * r) * (double)g[i]);
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------ LDS layout
 struct Lds {
-  float* act;   // [act_floats]
-  float* outb;  // [outb_floats]
-  float* outc;  // [outb_floats]
-  double* red;  // [16]
-  int* isel;    // [32]
-  float* fgate; // [32]
-  int* flag;    // [8]
+  float* act;        // [act_floats]   activation vector / attention scratch / merge staging
+  uint32_t* stage;   // [stage_words]  raw bf16-pair words of the incoming hidden state
+  float* outb;       // [outb_floats]  GEMV row results
+  float* outc;       // [outb_floats]
+  float* xres;       // [outb_floats]  this workgroup's rows of the layer input (for the residual)
+  double* red;       // [16]
+  int* isel;         // [32]
+  float* fgate;      // [32]
+  int* flag;         // [8]
+  RowSeg* segs;      // [MAX_SEGS] GEMV segment list of the current stage
 };
 __device__ __forceinline__ Lds carve(float* base, const KCfg& c) {
   Lds L;
   L.act = base;
-  L.outb = base + c.act_floats;
+  L.stage = reinterpret_cast<uint32_t*>(base + c.act_floats);
+  L.outb = reinterpret_cast<float*>(L.stage + c.stage_words);
   L.outc = L.outb + c.outb_floats;
-  L.red = reinterpret_cast<double*>(L.outc + c.outb_floats);
+  L.xres = L.outc + c.outb_floats;
+  L.red = reinterpret_cast<double*>(L.xres + c.outb_floats);
   L.isel = reinterpret_cast<int*>(L.red + 16);
   L.fgate = reinterpret_cast<float*>(L.isel + 32);
   L.flag = reinterpret_cast<int*>(L.fgate + 32);
+  L.segs = reinterpret_cast<RowSeg*>(L.flag + 8);
   return L;
 }
-__host__ __device__ inline size_t lds_bytes_for(int act_floats, int outb_floats) {
-  return (size_t)4 * (act_floats + 2 * outb_floats) + 8 * 16 + 4 * 32 + 4 * 32 + 4 * 8;
+__host__ __device__ inline size_t lds_bytes_for(int act_floats, int stage_words, int outb_floats) {
+  return (size_t)4 * (act_floats + stage_words + 3 * outb_floats) + 8 * 16 + 4 * 32 + 4 * 32 + 4 * 8 +
+         sizeof(RowSeg) * MAX_SEGS;
 }
+
+// Publishes a segment list to the workgroup (the previous list must be out of use).
+__device__ __forceinline__ void seg_begin() { __syncthreads(); }
+__device__ __forceinline__ void seg_set(Lds& L, int i, const uint8_t* w, const float* sc, int n, int srow, int act_off,
+                                        float alpha) {
+  if (threadIdx.x == 0) {
+    RowSeg& S = L.segs[i];
+    S.w = w; S.s = sc; S.n = n; S.srow = srow; S.act_off = act_off; S.alpha = alpha;
+  }
+}
+__device__ __forceinline__ void seg_end() { __syncthreads(); }
 
 // ------------------------------------------------------------------ compiled layer shapes
 // One kernel is compiled per supported layer shape, so every reduction length, head
 // size and expert width is a compile-time constant: each GEMV call site gets exactly one
 // lane layout, and the whole step inlines into the kernel (no device calls on the hot
 // path). Row counts that vary at run time (experts, top-k, cache length) stay runtime.
-template <int H_, int NH_, int NKV_, int HD_, int INTER_, bool FP8_, bool MOE_>
+// ATT_NB = K row passes and ATT_NV V tokens per wave held in registers per attention batch.
+template <int H_, int NH_, int NKV_, int HD_, int INTER_, bool FP8_, bool MOE_, int ATT_NB_, int ATT_NV_>
 struct GqaShape {
-  static constexpr int H = H_, NH = NH_, NKV = NKV_, HD = HD_, INTER = INTER_;
+  static constexpr int H = H_, NH = NH_, NKV = NKV_, HD = HD_, INTER = INTER_, ATT_NB = ATT_NB_, ATT_NV = ATT_NV_;
   static constexpr int G = NH / NKV, ODIM = NH * HD;
   static constexpr bool FP8 = FP8_, MOE = MOE_;
+  static_assert(H % 2 == 0 && ODIM % 2 == 0, "hidden sizes must be even");
 };
 
 // Per-(token, layer) state of one workgroup.
 struct Step {
   const DLayer* Ly;
-  XSrc xs;
-  uint32_t k1;   // step number + 1 (counter epoch)
-  bool first;    // first step of the launch: input comes from the caller
+  const uint16_t* in_hidden;   // caller's bf16 input for the first step of the launch, else null
+  uint32_t k1;                 // step number + 1 (counter epoch)
+  bool first;                  // first step of the launch
   int pos;
+  int idx;                     // step index within the launch (trace row)
 };
 
-template <bool FP8, int K, typename Pre>
-__device__ __forceinline__ bool mv(const DMat& M, size_t boff, size_t soff, int r0, int r1, const float* act,
-                                   float* out, int mode, float alpha, Pre&& pre) {
-  return gemv<FP8, K, float>(M.w + boff, FP8 ? M.s + soff : nullptr, r0, r1, act, out, mode, alpha, pre);
+__device__ __forceinline__ void stamp(const KArgs& a, const Ctx& cx, const Step& st, int slot) {
+  if (a.trace && st.idx < a.trace_steps && threadIdx.x == 0)
+    gp(a.trace)[((size_t)st.idx * cx.nwg + cx.w) * TR_SLOTS + slot] = wall_clock64();
+}
+
+// Rows [r0, r1) of an H-row stage for this workgroup, split in pairs (the hidden state
+// moves between workgroups as packed bf16 pairs).
+__device__ __forceinline__ void hrows(int H, int nwg, int w, int* r0, int* r1) {
+  *r0 = 2 * split_at(H / 2, nwg, w);
+  *r1 = 2 * split_at(H / 2, nwg, w + 1);
 }
 
 // ------------------------------------------------------------------ stage: RMSNorm + QKV + RoPE + cache append
@@ -264,48 +257,69 @@ __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Ste
   constexpr int qR = SH::NH * HD, kR = SH::NKV * HD, R = qR + 2 * kR;
   constexpr int P = R / 2;
   const int r0 = 2 * split_at(P, nwg, w), r1 = 2 * split_at(P, nwg, w + 1);
+  int h0, h1;
+  hrows(SH::H, nwg, w, &h0, &h1);
   bool pending = true;   // the input wait + RMSNorm has not run yet
   auto pre_x = [&]() -> bool {
     if (!pending) return true;
     pending = false;
     if (!st.first && !wait_all(cx, S_OUT, st.k1 - 1, nwg)) return false;
-    rmsnorm_to_lds(st.xs, Ly.attn_norm, SH::H, c.eps, L.act, L.red);
+    stamp(a, cx, st, TR_X_READY);
+    // stage the bf16 pairs of x, keep this workgroup's residual rows, expand to fp32
+    if (st.first) {
+      const PLD_GLOBAL uint32_t* src = gp(reinterpret_cast<const uint32_t*>(st.in_hidden));
+      for (int i = threadIdx.x; i < SH::H / 2; i += BLOCK) L.stage[i] = src[i];
+    } else {
+      coh_copy_to_lds(L.stage, wsp<uint32_t>(a, a.off.xbuf), SH::H / 2);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < SH::H / 2; i += BLOCK) {
+      const uint32_t v = L.stage[i];
+      L.act[2 * i] = bf_lo(v);
+      L.act[2 * i + 1] = bf_hi(v);
+    }
+    __syncthreads();
+    for (int r = h0 + threadIdx.x; r < h1; r += BLOCK) L.xres[r - h0] = L.act[r];
+    rmsnorm_inplace(L.act, Ly.attn_norm, SH::H, c.eps, L.red);
     if (w == 0)
       for (int i = threadIdx.x; i < SH::H; i += BLOCK) st_f32(wsp<float>(a, a.off.a_dbg) + i, L.act[i]);
     return true;
   };
   {
-    const int lo = max(r0, 0), hi = min(r1, qR);
-    if (lo < hi && !mv<SH::FP8, SH::H>(Ly.wq, 0, 0, lo, hi, L.act, L.outb + (lo - r0), OUT_STORE, 1.f, pre_x)) return false;
+    // one pipelined pass over this workgroup's rows of [W_q; W_k; W_v]
+    const DMat* mats[3] = {&Ly.wq, &Ly.wk, &Ly.wv};
+    const int seg0[4] = {0, qR, qR + kR, R};
+    constexpr size_t RB = (size_t)SH::H * (SH::FP8 ? 1 : 2);
+    seg_begin();
+    int ns = 0;
+#pragma unroll
+    for (int m = 0; m < 3; m++) {
+      const int lo = max(r0, seg0[m]), hi = min(r1, seg0[m + 1]);
+      if (lo < hi) {
+        seg_set(L, ns, mats[m]->w + (size_t)(lo - seg0[m]) * RB, mats[m]->s, hi - lo, lo - seg0[m], 0, 1.f);
+        ns++;
+      }
+    }
+    seg_end();
+    if (!gemv_list<SH::FP8, SH::H>(L.segs, ns, L.act, L.outb, OUT_STORE, pre_x)) return false;
   }
-  {
-    const int lo = max(r0, qR), hi = min(r1, qR + kR);
-    if (lo < hi && !mv<SH::FP8, SH::H>(Ly.wk, 0, 0, lo - qR, hi - qR, L.act, L.outb + (lo - r0), OUT_STORE, 1.f, pre_x))
-      return false;
-  }
-  {
-    const int lo = max(r0, qR + kR), hi = min(r1, R);
-    if (lo < hi &&
-        !mv<SH::FP8, SH::H>(Ly.wv, 0, 0, lo - qR - kR, hi - qR - kR, L.act, L.outb + (lo - r0), OUT_STORE, 1.f, pre_x))
-      return false;
-  }
+  stamp(a, cx, st, TR_QKV_GEMV);
   if (!pre_x()) return false;
   __syncthreads();
-  const float* rope = wsp<float>(a, a.off.rope) + (size_t)pos * HD;   // (cos, sin) pairs, HD/2 per position
+  const PLD_GLOBAL float* rope = gp(wsp<float>(a, a.off.rope)) + (size_t)pos * HD;   // (cos, sin) pairs
   float* qw = wsp<float>(a, a.off.q);
   for (int p = r0 / 2 + threadIdx.x; p < r1 / 2; p += BLOCK) {
     const int r = 2 * p;
     float v0 = L.outb[r - r0], v1 = L.outb[r + 1 - r0];
     if (r < qR + kR) {
       const int d = (r < qR ? r : r - qR) % HD;
-      const float cs = gp(rope)[d], sn = gp(rope)[d + 1];
+      const float cs = rope[d], sn = rope[d + 1];
       const float x0 = v0 * cs - v1 * sn, x1 = v0 * sn + v1 * cs;
       v0 = x0;
       v1 = x1;
     }
     if (r < qR) {
-      st_f32(qw + r, v0);
-      st_f32(qw + r + 1, v1);
+      st_u64(reinterpret_cast<uint64_t*>(qw + r), (uint64_t)__float_as_uint(v0) | ((uint64_t)__float_as_uint(v1) << 32));
     } else {
       const bool isk = r < qR + kR;
       const int rr = isk ? r - qR : r - qR - kR;
@@ -315,6 +329,7 @@ __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Ste
     }
   }
   arrive(cx, S_QKV, st.k1, nwg);
+  stamp(a, cx, st, TR_QKV_DONE);
   return true;
 }
 
@@ -322,72 +337,105 @@ __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Ste
 // One workgroup = one (kv head g, token chunk) pair. Scores for the G query heads of
 // the group, chunk-local softmax, P.V, then a partial (m, l, acc[HD]) per head. The
 // group's last arriver merges the partials into o.
+//  * scores: 16-byte K loads, HD/8 lanes per token row, ATT_NB row passes held in
+//    registers; the per-token dot is reduced with DPP moves inside each 16-lane row;
+//  * P.V: each wave owns a contiguous token range and each lane HD/64 dims, so the sum
+//    over tokens needs no lane exchange, only one cross-wave pass through LDS;
+//  * the static history rows of the first batch (K and V) are issued before the wait
+//    for this step's q/k/v; rows written in this launch are read coherently after it.
 template <class SH>
 __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Step& st, Lds& L) {
   const KCfg& c = a.c;
   const DLayer Ly = *gp(st.Ly);
   const uint32_t k1 = st.k1;
-  constexpr int HD = SH::HD, G = SH::G;
-  constexpr int LPT = HD / 8;      // lanes per token row (16 bytes each)
-  constexpr int TPW = 64 / LPT;    // tokens per wave pass
+  constexpr int HD = SH::HD, G = SH::G, NB = SH::ATT_NB, NV = SH::ATT_NV;
+  constexpr int LPT = HD / 8;          // lanes per token row in the score pass (16 bytes each)
+  constexpr int TPW = 64 / LPT;        // tokens per wave pass
+  constexpr int PASS = NWAVES * TPW;   // tokens per workgroup pass
+  constexpr int DPL = HD / 64;         // dims per lane in the P.V pass
+  static_assert(DPL == 1 || DPL == 2, "head dim 64 or 128");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int dl = lane % LPT, tl = lane / LPT;
   const int cpg = c.cpg;
   const int g = cx.w / cpg, ch = cx.w % cpg;
   const int T = st.pos + 1;
   const int t0 = split_at(T, cpg, ch), t1 = split_at(T, cpg, ch + 1), n = t1 - t0;
-  const uint16_t* kbase = Ly.kc + (size_t)g * c.max_seq * HD;
-  const uint16_t* vbase = Ly.vc + (size_t)g * c.max_seq * HD;
-  const int fresh = a.pos0;   // rows >= fresh were written inside this launch
-
-  auto load_row = [&](const uint16_t* base, int t) -> uint4 {
-    const uint16_t* p = base + (size_t)t * HD + dl * 8;
-    if (t >= fresh) {
-      const uint32_t* q = reinterpret_cast<const uint32_t*>(p);
-      return make_uint4(ld_u32(q), ld_u32(q + 1), ld_u32(q + 2), ld_u32(q + 3));
-    }
-    return ld_g16(p);
+  const int tw = (n + NWAVES - 1) / NWAVES;             // P.V tokens per wave
+  const int pv0 = min(n, wave * tw), pv1 = min(n, pv0 + tw);
+  const uint16_t* kbase = Ly.kc + (size_t)g * c.max_seq * HD + dl * 8;
+  const uint16_t* vbase = Ly.vc + (size_t)g * c.max_seq * HD + lane * DPL;
+  const int fresh = a.pos0;   // rows >= fresh were written inside this launch: coherent loads only
+  auto tok = [&](int tb0, int b) { return tb0 + b * PASS + wave * TPW + tl; };
+  auto k_static = [&](int t) -> uint4 {
+    return (t < n && t0 + t < fresh) ? ld_g16(kbase + (size_t)(t0 + t) * HD) : make_uint4(0u, 0u, 0u, 0u);
   };
-
-  // static history rows are issued before the wait for this step's q/k/v
-  uint4 kpre = make_uint4(0u, 0u, 0u, 0u);
-  {
-    const int t = wave * TPW + tl;
-    if (t < n && t0 + t < fresh) kpre = ld_g16(kbase + (size_t)(t0 + t) * HD + dl * 8);
-  }
+  auto k_fresh = [&](int t) -> uint4 {
+    const uint64_t* q = reinterpret_cast<const uint64_t*>(kbase + (size_t)(t0 + t) * HD);
+    const uint64_t x = ld_u64(q), y = ld_u64(q + 1);
+    return make_uint4((uint32_t)x, (uint32_t)(x >> 32), (uint32_t)y, (uint32_t)(y >> 32));
+  };
+  // V element(s) of this lane for token t (DPL bf16 values packed in a word)
+  auto v_static = [&](int t) -> uint32_t {
+    if (t >= pv1 || t0 + t >= fresh) return 0u;
+    const uint16_t* p = vbase + (size_t)(t0 + t) * HD;
+    if constexpr (DPL == 2) return *(const PLD_GLOBAL uint32_t*)(p);
+    else return (uint32_t)(*(const PLD_GLOBAL uint16_t*)(p));
+  };
+  auto v_fresh = [&](int t) -> uint32_t {
+    const uint16_t* p = vbase + (size_t)(t0 + t) * HD;
+    if constexpr (DPL == 2) return ld_u32(reinterpret_cast<const uint32_t*>(p));
+    else {
+      const uint32_t w2 = ld_u32(reinterpret_cast<const uint32_t*>(p - (lane & 1)));
+      return (lane & 1) ? (w2 >> 16) : (w2 & 0xffffu);
+    }
+  };
+  uint4 kb[NB];
+  uint32_t vb[NV];
+#pragma unroll
+  for (int b = 0; b < NB; b++) kb[b] = k_static(tok(0, b));
+#pragma unroll
+  for (int b = 0; b < NV; b++) vb[b] = v_static(pv0 + b);
   if (!wait_all(cx, S_QKV, k1, cx.nwg)) return false;
+  stamp(a, cx, st, TR_ATT_READY);
 
-  const float* qg = wsp<float>(a, a.off.q) + (size_t)g * G * HD;
+  const uint64_t* qg = reinterpret_cast<const uint64_t*>(wsp<float>(a, a.off.q) + (size_t)g * G * HD + dl * 8);
   const float scale = 1.0f / sqrtf((float)HD);
   float qr[G][8];
 #pragma unroll
   for (int h = 0; h < G; h++)
 #pragma unroll
-    for (int j = 0; j < 8; j++) qr[h][j] = ld_f32(qg + h * HD + dl * 8 + j) * scale;
-
+    for (int j = 0; j < 4; j++) {
+      const uint64_t v = ld_u64(qg + h * HD / 2 + j);
+      qr[h][2 * j] = __uint_as_float((uint32_t)v) * scale;
+      qr[h][2 * j + 1] = __uint_as_float((uint32_t)(v >> 32)) * scale;
+    }
+  stamp(a, cx, st, TR_ATT_Q);
   float* sc = L.act;                               // [G][chmax]
   float* red2 = L.act + G * c.chmax;               // [NWAVES][G][HD]
   float* ml = red2 + NWAVES * G * HD;              // [2G]
-  for (int tb = 0; tb < n; tb += NWAVES * TPW) {
-    const int t = tb + wave * TPW + tl;
-    float s[G];
+  // ---- pass 1: scores
+  for (int tb0 = 0; tb0 < n; tb0 += NB * PASS) {
 #pragma unroll
-    for (int h = 0; h < G; h++) s[h] = 0.f;
-    if (t < n) {
-      const uint4 kv = (tb == 0 && t0 + t < fresh) ? kpre : load_row(kbase, t0 + t);
-      float kf[8] = {bf_lo(kv.x), bf_hi(kv.x), bf_lo(kv.y), bf_hi(kv.y), bf_lo(kv.z), bf_hi(kv.z), bf_lo(kv.w), bf_hi(kv.w)};
-#pragma unroll
-      for (int h = 0; h < G; h++)
-#pragma unroll
-        for (int j = 0; j < 8; j++) s[h] = fmaf(qr[h][j], kf[j], s[h]);
+    for (int b = 0; b < NB; b++) {
+      const int t = tok(tb0, b);
+      if (tb0 > 0) kb[b] = k_static(t);
+      if (t < n && t0 + t >= fresh) kb[b] = k_fresh(t);
     }
 #pragma unroll
-    for (int h = 0; h < G; h++)
+    for (int b = 0; b < NB; b++) {
+      const int t = tok(tb0, b);
+      const uint4 kv = kb[b];
+      const float kf[8] = {bf_lo(kv.x), bf_hi(kv.x), bf_lo(kv.y), bf_hi(kv.y),
+                           bf_lo(kv.z), bf_hi(kv.z), bf_lo(kv.w), bf_hi(kv.w)};
 #pragma unroll
-      for (int off = LPT / 2; off >= 1; off >>= 1) s[h] += __shfl_xor(s[h], off, 64);
-    if (dl == 0 && t < n)
+      for (int h = 0; h < G; h++) {
+        float sh = 0.f;
 #pragma unroll
-      for (int h = 0; h < G; h++) sc[h * c.chmax + t] = s[h];
+        for (int j = 0; j < 8; j++) sh = fmaf(qr[h][j], kf[j], sh);
+        sh = dpp_sum<LPT>(sh);
+        if (dl == LPT - 1 && t < n) sc[h * c.chmax + t] = sh;
+      }
+    }
   }
   __syncthreads();
   for (int h = wave; h < G; h += NWAVES) {
@@ -404,80 +452,86 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
     if (lane == 0) { ml[2 * h] = m; ml[2 * h + 1] = l; }
   }
   __syncthreads();
-  float acc[G][8];
+  stamp(a, cx, st, TR_ATT_SOFTMAX);
+  // ---- pass 2: P.V over this wave's token range, DPL dims per lane
+  float acc[G][DPL];
 #pragma unroll
   for (int h = 0; h < G; h++)
 #pragma unroll
-    for (int j = 0; j < 8; j++) acc[h][j] = 0.f;
-  for (int tb = 0; tb < n; tb += NWAVES * TPW) {
-    const int t = tb + wave * TPW + tl;
-    if (t < n) {
-      const uint4 vv = load_row(vbase, t0 + t);
-      float vf[8] = {bf_lo(vv.x), bf_hi(vv.x), bf_lo(vv.y), bf_hi(vv.y), bf_lo(vv.z), bf_hi(vv.z), bf_lo(vv.w), bf_hi(vv.w)};
+    for (int e = 0; e < DPL; e++) acc[h][e] = 0.f;
+  for (int tb = pv0; tb < pv1; tb += NV) {
 #pragma unroll
-      for (int h = 0; h < G; h++) {
-        const float p = sc[h * c.chmax + t];
+    for (int b = 0; b < NV; b++) {
+      const int t = tb + b;
+      if (tb > pv0) vb[b] = v_static(t);
+      if (t < pv1 && t0 + t >= fresh) vb[b] = v_fresh(t);
+    }
 #pragma unroll
-        for (int j = 0; j < 8; j++) acc[h][j] = fmaf(p, vf[j], acc[h][j]);
+    for (int b = 0; b < NV; b++) {
+      const int t = tb + b;
+      if (t < pv1) {
+        const float v0 = bf_lo(vb[b]);
+        const float v1 = DPL == 2 ? bf_hi(vb[b]) : 0.f;
+#pragma unroll
+        for (int h = 0; h < G; h++) {
+          const float p = sc[h * c.chmax + t];
+          acc[h][0] = fmaf(p, v0, acc[h][0]);
+          if constexpr (DPL == 2) acc[h][1] = fmaf(p, v1, acc[h][1]);
+        }
       }
     }
   }
 #pragma unroll
   for (int h = 0; h < G; h++)
 #pragma unroll
-    for (int j = 0; j < 8; j++)
-#pragma unroll
-      for (int off = LPT; off < 64; off <<= 1) acc[h][j] += __shfl_xor(acc[h][j], off, 64);
-  if (tl == 0)
-#pragma unroll
-    for (int h = 0; h < G; h++)
-#pragma unroll
-      for (int j = 0; j < 8; j++) red2[(wave * G + h) * HD + dl * 8 + j] = acc[h][j];
+    for (int e = 0; e < DPL; e++) red2[(wave * G + h) * HD + lane * DPL + e] = acc[h][e];
   __syncthreads();
+  // partial of head h for this chunk: [m, l, acc[0..HD)] at ((g*G + h)*cpg + ch)*(HD+2)
   float* part = wsp<float>(a, a.off.part);
-  for (int i = threadIdx.x; i < G * HD; i += BLOCK) {
-    float s = 0.f;
+  for (int i = threadIdx.x; i < G * HD / 2; i += BLOCK) {
+    const int h = (2 * i) / HD, d = (2 * i) % HD;
+    float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-    for (int wv = 0; wv < NWAVES; wv++) s += red2[wv * G * HD + i];
-    const int h = i / HD, d = i % HD;
-    st_f32(part + ((size_t)(g * G + h) * cpg + ch) * (HD + 2) + 2 + d, s);
+    for (int wv = 0; wv < NWAVES; wv++) {
+      s0 += red2[(wv * G + h) * HD + d];
+      s1 += red2[(wv * G + h) * HD + d + 1];
+    }
+    st_u64(reinterpret_cast<uint64_t*>(part + ((size_t)(g * G + h) * cpg + ch) * (HD + 2) + 2 + d),
+           (uint64_t)__float_as_uint(s0) | ((uint64_t)__float_as_uint(s1) << 32));
   }
   if (threadIdx.x < G) {
     const int h = threadIdx.x;
-    float* pp = part + ((size_t)(g * G + h) * cpg + ch) * (HD + 2);
-    st_f32(pp, ml[2 * h]);
-    st_f32(pp + 1, ml[2 * h + 1]);
+    st_u64(reinterpret_cast<uint64_t*>(part + ((size_t)(g * G + h) * cpg + ch) * (HD + 2)),
+           (uint64_t)__float_as_uint(ml[2 * h]) | ((uint64_t)__float_as_uint(ml[2 * h + 1]) << 32));
   }
-  // last arriver of the group merges
+  // last arriver of the group merges (all partials of the group are one contiguous block)
   vm_wait();
   __syncthreads();
+  stamp(a, cx, st, TR_ATT_PARTIAL);
   if (threadIdx.x == 0) {
     const uint32_t old = atomic_add_u32(cx.ctr_grp + g * CTR_STRIDE, 1u);
     L.flag[0] = (old + 1u == k1 * (uint32_t)cpg);
   }
   __syncthreads();
   if (L.flag[0]) {
-    float* mlc = L.act;  // [G][cpg][2]
-    for (int i = threadIdx.x; i < G * cpg; i += BLOCK) {
-      const int h = i / cpg, cc = i % cpg;
-      const float* pp = part + ((size_t)(g * G + h) * cpg + cc) * (HD + 2);
-      mlc[2 * i] = ld_f32(pp);
-      mlc[2 * i + 1] = ld_f32(pp + 1);
-    }
+    float* pl = L.act;   // [G][cpg][HD+2]
+    coh_copy_to_lds<24>(reinterpret_cast<uint32_t*>(pl),
+                        reinterpret_cast<const uint32_t*>(part + (size_t)g * G * cpg * (HD + 2)), G * cpg * (HD + 2));
     __syncthreads();
     float* obuf = wsp<float>(a, a.off.o);
     for (int i = threadIdx.x; i < G * HD; i += BLOCK) {
       const int h = i / HD, d = i % HD;
+      const float* ph = pl + (size_t)h * cpg * (HD + 2);
       float M = -INFINITY;
       for (int cc = 0; cc < cpg; cc++)
-        if (mlc[2 * (h * cpg + cc) + 1] > 0.f) M = fmaxf(M, mlc[2 * (h * cpg + cc)]);
+        if (ph[cc * (HD + 2) + 1] > 0.f) M = fmaxf(M, ph[cc * (HD + 2)]);
       float Ls = 0.f, o = 0.f;
       for (int cc = 0; cc < cpg; cc++) {
-        const float l = mlc[2 * (h * cpg + cc) + 1];
+        const float l = ph[cc * (HD + 2) + 1];
         if (l > 0.f) {
-          const float f = __expf(mlc[2 * (h * cpg + cc)] - M);
+          const float f = __expf(ph[cc * (HD + 2)] - M);
           Ls += f * l;
-          o += f * ld_f32(part + ((size_t)(g * G + h) * cpg + cc) * (HD + 2) + 2 + d);
+          o += f * ph[cc * (HD + 2) + 2 + d];
         }
       }
       st_f32(obuf + (size_t)(g * G + h) * HD + d, o / Ls);
@@ -485,43 +539,69 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
     vm_wait();
     __syncthreads();
     if (threadIdx.x == 0) atomic_add_u32(cx.ctr_att, 1u);
+    stamp(a, cx, st, TR_ATT_MERGED);
   }
+  stamp(a, cx, st, TR_ATT_DONE);
   return true;
 }
 
 // ------------------------------------------------------------------ stage: output projection + residual
 template <class SH>
 __device__ __forceinline__ bool stage_wo(Ctx& cx, const KArgs& a, const Step& st, Lds& L) {
-  const int r0 = split_at(SH::H, cx.nwg, cx.w), r1 = split_at(SH::H, cx.nwg, cx.w + 1);
+  int r0, r1;
+  hrows(SH::H, cx.nwg, cx.w, &r0, &r1);
   auto pre_o = [&]() -> bool {
     if (!spin_until(cx, cx.ctr_att, st.k1 * (uint32_t)SH::NKV, 10)) return false;
-    const float* o = wsp<float>(a, a.off.o);
-    for (int i = threadIdx.x; i < SH::ODIM; i += BLOCK) L.act[i] = ld_f32(o + i);
+    stamp(a, cx, st, TR_O_READY);
+    coh_copy_to_lds(reinterpret_cast<uint32_t*>(L.act), wsp<uint32_t>(a, a.off.o), SH::ODIM);
     __syncthreads();
     return true;
   };
-  if (!mv<SH::FP8, SH::ODIM>(st.Ly->wo, 0, 0, r0, r1, L.act, L.outb, OUT_STORE, 1.f, pre_o)) return false;
+  {
+    const DMat wo = gp(st.Ly)->wo;
+    seg_begin();
+    seg_set(L, 0, wo.w + (size_t)r0 * SH::ODIM * (SH::FP8 ? 1 : 2), wo.s, r1 - r0, r0, 0, 1.f);
+    seg_end();
+    if (!gemv_list<SH::FP8, SH::ODIM>(L.segs, r1 > r0 ? 1 : 0, L.act, L.outb, OUT_STORE, pre_o)) return false;
+  }
   __syncthreads();
   float* h2 = wsp<float>(a, a.off.h2);
-  for (int r = r0 + threadIdx.x; r < r1; r += BLOCK) st_f32(h2 + r, st.xs(r) + L.outb[r - r0]);
+  for (int r = r0 + 2 * threadIdx.x; r < r1; r += 2 * BLOCK)
+    st_u64(reinterpret_cast<uint64_t*>(h2 + r), (uint64_t)__float_as_uint(L.xres[r - r0] + L.outb[r - r0]) |
+                                                    ((uint64_t)__float_as_uint(L.xres[r + 1 - r0] + L.outb[r + 1 - r0]) << 32));
   arrive(cx, S_H2, st.k1, cx.nwg);
+  stamp(a, cx, st, TR_WO_DONE);
   return true;
 }
 
 // ------------------------------------------------------------------ stage: FFN gate/up (+ router)
-// m[slot][j] = silu(gate_j . b) * (up_j . b) for rows [j0, j1) of one expert
+// Gate/up rows of several (expert, slot, row range) pieces as one GEMV list, then
+// m[slot][j] = silu(gate_j . b) * (up_j . b). Each piece contributes a gate segment and
+// an up segment; results come back in list order.
+struct GuPiece { int expert, slot, j0, j1; };
 template <class SH, typename Pre>
-__device__ __forceinline__ bool gate_up(const KArgs& a, const Step& st, Lds& L, int expert, int slot, int j0, int j1,
-                                        Pre&& pre) {
+__device__ __forceinline__ bool gate_up_list(const KArgs& a, const Step& st, Lds& L, const GuPiece* pc, int np, Pre&& pre) {
   const DLayer Ly = *gp(st.Ly);
-  const size_t bo = (size_t)expert * Ly.gu_slot_bytes, so = (size_t)expert * Ly.gu_slot_scales;
-  if (!mv<SH::FP8, SH::H>(Ly.w_gate, bo, so, j0, j1, L.act, L.outb, OUT_STORE, 1.f, pre)) return false;
-  if (!mv<SH::FP8, SH::H>(Ly.w_up, bo, so, j0, j1, L.act, L.outc, OUT_STORE, 1.f, NoPre{})) return false;
+  constexpr size_t RB = (size_t)SH::H * (SH::FP8 ? 1 : 2);
+  seg_begin();
+  for (int p = 0; p < np; p++) {
+    const size_t bo = (size_t)pc[p].expert * Ly.gu_slot_bytes + (size_t)pc[p].j0 * RB;
+    const float* sg = SH::FP8 ? Ly.w_gate.s + (size_t)pc[p].expert * Ly.gu_slot_scales : nullptr;
+    const float* su = SH::FP8 ? Ly.w_up.s + (size_t)pc[p].expert * Ly.gu_slot_scales : nullptr;
+    seg_set(L, 2 * p, Ly.w_gate.w + bo, sg, pc[p].j1 - pc[p].j0, pc[p].j0, 0, 1.f);
+    seg_set(L, 2 * p + 1, Ly.w_up.w + bo, su, pc[p].j1 - pc[p].j0, pc[p].j0, 0, 1.f);
+  }
+  seg_end();
+  if (!gemv_list<SH::FP8, SH::H>(L.segs, 2 * np, L.act, L.outb, OUT_STORE, pre)) return false;
   __syncthreads();
   float* mbuf = wsp<float>(a, a.off.m);
-  for (int j = j0 + threadIdx.x; j < j1; j += BLOCK)
-    st_f32(mbuf + (size_t)slot * SH::INTER + j, silu_f(L.outb[j - j0]) * L.outc[j - j0]);
-  __syncthreads();
+  int base = 0;
+  for (int p = 0; p < np; p++) {
+    const int n = pc[p].j1 - pc[p].j0;
+    for (int j = threadIdx.x; j < n; j += BLOCK)
+      st_f32(mbuf + (size_t)pc[p].slot * SH::INTER + pc[p].j0 + j, silu_f(L.outb[base + j]) * L.outb[base + n + j]);
+    base += 2 * n;
+  }
   return true;
 }
 
@@ -536,17 +616,27 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
     if (!pending) return true;
     pending = false;
     if (!wait_all(cx, S_H2, st.k1, nwg)) return false;
-    const float* h2 = wsp<float>(a, a.off.h2);
-    rmsnorm_to_lds([&](int i) { return ld_f32(h2 + i); }, Ly.ffn_norm, SH::H, c.eps, L.act, L.red);
+    stamp(a, cx, st, TR_H2_READY);
+    coh_copy_to_lds(reinterpret_cast<uint32_t*>(L.act), wsp<uint32_t>(a, a.off.h2), SH::H);
+    __syncthreads();
+    rmsnorm_inplace(L.act, Ly.ffn_norm, SH::H, c.eps, L.red);
     if (w == 0)
       for (int i = threadIdx.x; i < SH::H; i += BLOCK) st_f32(wsp<float>(a, a.off.b_dbg) + i, L.act[i]);
     if constexpr (SH::MOE) {
       if (w < c.E) {
+        // logit of expert w (fp64 accumulation) and its selection key: the logit itself
+        // (softmax router) or sigmoid(logit) + bias (biased-score router)
         const uint16_t* rrow = Ly.router + (size_t)w * SH::H;
         double s = 0.0;
         for (int q = threadIdx.x; q < SH::H / 8; q += BLOCK) s += dot8_bf16_f64(ld_g16(rrow + q * 8), L.act + q * 8);
         s = block_sum(s, L.red);
-        if (threadIdx.x == 0) st_f64(wsp<double>(a, a.off.logits) + w, s);
+        if (threadIdx.x == 0) {
+          const double key = c.router == PLD_ROUTER_SIGMOID_BIAS
+                                 ? (1.0 / (1.0 + exp(-s))) + (double)gp(Ly.router_bias)[w] : s;
+          double* lk = wsp<double>(a, a.off.logits) + 2 * w;
+          st_u64(reinterpret_cast<uint64_t*>(lk), (uint64_t)__double_as_longlong(s));
+          st_u64(reinterpret_cast<uint64_t*>(lk + 1), (uint64_t)__double_as_longlong(key));
+        }
       }
       arrive(cx, S_RT, st.k1, c.E);
     }
@@ -554,54 +644,67 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
   };
   const int j0 = split_at(SH::INTER, nwg, w), j1 = split_at(SH::INTER, nwg, w + 1);
   if constexpr (!SH::MOE) {
-    if (!gate_up<SH>(a, st, L, 0, 0, j0, j1, pre_b)) return false;
+    const GuPiece pc[1] = {{0, 0, j0, j1}};
+    if (!gate_up_list<SH>(a, st, L, pc, j1 > j0 ? 1 : 0, pre_b)) return false;
   } else {
     // shared experts first: they do not depend on the router
-    for (int sj = 0; sj < c.nshared; sj++)
-      if (!gate_up<SH>(a, st, L, c.E + sj, c.topk + sj, j0, j1, pre_b)) return false;
+    GuPiece pc[2];
+    int np = 0;
+    for (int sj = 0; sj < c.nshared && j1 > j0; sj++) pc[np++] = {c.E + sj, c.topk + sj, j0, j1};
+    if (!gate_up_list<SH>(a, st, L, pc, np, pre_b)) return false;
     if (!pre_b()) return false;
+    stamp(a, cx, st, TR_SHARED_GEMV);
     // router top-k (every workgroup computes the same selection)
     if (!wait_all(cx, S_RT, st.k1, c.E)) return false;
-    double* lg = reinterpret_cast<double*>(L.outc);   // E doubles (outc is free here)
-    const double* logits = wsp<double>(a, a.off.logits);
-    for (int x = threadIdx.x; x < c.E; x += BLOCK) {
-      const double r = ld_f64(logits + x);
-      lg[x] = (c.router == PLD_ROUTER_SIGMOID_BIAS) ? (1.0 / (1.0 + exp(-r))) + (double)gp(Ly.router_bias)[x] : r;
+    stamp(a, cx, st, TR_RT_READY);
+    // top-k by rank: expert e is selected at position rank(e) = #{j : key_j > key_e or
+    // (key_j == key_e and j < e)} when that rank is < topk (lowest index wins ties)
+    double* lk = reinterpret_cast<double*>(L.outb);   // [E][2] (logit, key); outb is free here
+    coh_copy_to_lds(reinterpret_cast<uint32_t*>(lk), wsp<uint32_t>(a, a.off.logits), 4 * c.E);
+    __syncthreads();
+    const bool sig = c.router == PLD_ROUTER_SIGMOID_BIAS;
+    for (int e = threadIdx.x; e < c.E; e += BLOCK) {
+      const double ke = lk[2 * e + 1];
+      int rank = 0;
+      for (int j = 0; j < c.E; j++) {
+        const double kj = lk[2 * j + 1];
+        rank += (kj > ke) || (kj == ke && j < e);
+      }
+      if (rank < c.topk) L.isel[rank] = e;
     }
     __syncthreads();
-    if (threadIdx.x < 64) {
-      wave_topk(lg, c.E, c.topk, L.isel);
-      if (threadIdx.x == 0) {
-        double gsum = 0.0, tmp[32];
-        if (c.router == PLD_ROUTER_SIGMOID_BIAS) {
-          for (int s = 0; s < c.topk; s++) {
-            tmp[s] = 1.0 / (1.0 + exp(-ld_f64(logits + L.isel[s])));
-            gsum += tmp[s];
-          }
-        } else {
-          const double mx = ld_f64(logits + L.isel[0]);
-          for (int s = 0; s < c.topk; s++) {
-            tmp[s] = exp(ld_f64(logits + L.isel[s]) - mx);
-            gsum += tmp[s];
-          }
-        }
-        for (int s = 0; s < c.topk; s++) L.fgate[s] = (float)(tmp[s] / gsum);
-      }
+    stamp(a, cx, st, TR_TOPK);
+    // gates: softmax over the selected logits, or sigmoid scores normalised over the selection
+    double* num = reinterpret_cast<double*>(L.outc);
+    if (threadIdx.x < c.topk) {
+      const double r = lk[2 * L.isel[threadIdx.x]];
+      num[threadIdx.x] = sig ? 1.0 / (1.0 + exp(-r)) : exp(r - lk[2 * L.isel[0]]);
+    }
+    __syncthreads();
+    if (threadIdx.x < c.topk) {
+      double gsum = 0.0;
+      for (int j = 0; j < c.topk; j++) gsum += num[j];
+      L.fgate[threadIdx.x] = (float)(num[threadIdx.x] / gsum);
     }
     __syncthreads();
     if (w == 0 && threadIdx.x < c.topk) {
       st_u32(reinterpret_cast<uint32_t*>(wsp<int>(a, a.off.sel)) + threadIdx.x, (uint32_t)L.isel[threadIdx.x]);
       st_f32(wsp<float>(a, a.off.gates) + threadIdx.x, L.fgate[threadIdx.x]);
     }
-    // routed experts: this workgroup's share of the topk*inter (slot, row) pairs
+    // routed experts: this workgroup's share of the topk*inter (slot, row) pairs, one list
     const int tot = c.topk * SH::INTER;
     const int i0 = split_at(tot, nwg, w), i1 = split_at(tot, nwg, w + 1);
-    for (int s = i0 / SH::INTER; s < c.topk && s * SH::INTER < i1; s++) {
+    GuPiece rp[MAX_SEGS / 2];
+    int nr = 0;
+    for (int s = i0 / SH::INTER; s < c.topk && s * SH::INTER < i1 && nr < MAX_SEGS / 2; s++) {
       const int lo = max(i0, s * SH::INTER) - s * SH::INTER, hi = min(i1, (s + 1) * SH::INTER) - s * SH::INTER;
-      if (lo < hi && !gate_up<SH>(a, st, L, L.isel[s], s, lo, hi, NoPre{})) return false;
+      if (lo < hi) rp[nr++] = {L.isel[s], s, lo, hi};
     }
+    if (!gate_up_list<SH>(a, st, L, rp, nr, NoPre{})) return false;
   }
+  stamp(a, cx, st, TR_M_STORED);
   arrive(cx, S_M, st.k1, nwg);
+  stamp(a, cx, st, TR_FFN_DONE);
   return true;
 }
 
@@ -610,35 +713,57 @@ template <class SH>
 __device__ __forceinline__ bool stage_down(Ctx& cx, const KArgs& a, const Step& st, Lds& L, uint16_t* out_hidden) {
   const KCfg& c = a.c;
   const DLayer Ly = *gp(st.Ly);
-  const int r0 = split_at(SH::H, cx.nwg, cx.w), r1 = split_at(SH::H, cx.nwg, cx.w + 1);
+  int r0, r1;
+  hrows(SH::H, cx.nwg, cx.w, &r0, &r1);
   bool pending = true;
   auto pre_m = [&]() -> bool {
     if (!pending) return true;
     pending = false;
     if (!wait_all(cx, S_M, st.k1, cx.nwg)) return false;
-    const float* mbuf = wsp<float>(a, a.off.m);
-    for (int i = threadIdx.x; i < c.slots * SH::INTER; i += BLOCK) L.act[i] = ld_f32(mbuf + i);
-    for (int r = threadIdx.x; r < r1 - r0; r += BLOCK) L.outb[r] = 0.f;
+    stamp(a, cx, st, TR_M_READY);
+    coh_copy_to_lds(reinterpret_cast<uint32_t*>(L.act), wsp<uint32_t>(a, a.off.m), c.slots * SH::INTER);
     __syncthreads();
     return true;
   };
-  for (int s = 0; s < c.slots; s++) {
-    const int expert = !SH::MOE ? 0 : (s < c.topk ? L.isel[s] : c.E + (s - c.topk));
-    const float gate = (!SH::MOE || s >= c.topk) ? 1.0f : L.fgate[s];
-    const size_t bo = (size_t)expert * Ly.dn_slot_bytes, so = (size_t)expert * Ly.dn_slot_scales;
-    if (!mv<SH::FP8, SH::INTER>(Ly.w_down, bo, so, r0, r1, L.act + (size_t)s * SH::INTER, L.outb, OUT_ACCUM, gate, pre_m))
-      return false;
+  {
+    // all slots' rows [r0, r1) as one list; slot s reads activation m_s
+    constexpr size_t RB = (size_t)SH::INTER * (SH::FP8 ? 1 : 2);
+    seg_begin();
+    for (int s = 0; s < c.slots; s++) {
+      const int expert = !SH::MOE ? 0 : (s < c.topk ? L.isel[s] : c.E + (s - c.topk));
+      const size_t bo = (size_t)expert * Ly.dn_slot_bytes + (size_t)r0 * RB;
+      const float* sd = SH::FP8 ? Ly.w_down.s + (size_t)expert * Ly.dn_slot_scales : nullptr;
+      seg_set(L, s, Ly.w_down.w + bo, sd, r1 - r0, r0, s * SH::INTER, 1.f);
+    }
+    seg_end();
+    if (!gemv_list<SH::FP8, SH::INTER>(L.segs, r1 > r0 ? c.slots : 0, L.act, L.outb, OUT_STORE, pre_m)) return false;
   }
+  stamp(a, cx, st, TR_DOWN_GEMV);
   if (!pre_m()) return false;
   __syncthreads();
-  const float* h2 = wsp<float>(a, a.off.h2);
-  uint32_t* xb = wsp<uint32_t>(a, a.off.xbuf);
-  for (int r = r0 + threadIdx.x; r < r1; r += BLOCK) {
-    const uint32_t bits = f32_to_bf16(ld_f32(h2 + r) + L.outb[r - r0]);
-    st_u32(xb + r, bits);
-    if (out_hidden) gp(out_hidden)[r] = (uint16_t)bits;
+  // f_r = sum_s gate_s * down_s[r] (fixed slot order)
+  {
+    const int nr = r1 - r0;
+    for (int r = threadIdx.x; r < nr; r += BLOCK) {
+      float f = 0.f;
+      for (int s = 0; s < c.slots; s++) f += ((!SH::MOE || s >= c.topk) ? 1.0f : L.fgate[s]) * L.outb[s * nr + r];
+      L.outc[r] = f;
+    }
   }
+  __syncthreads();
+  // out = h2 + f, rounded to bf16; h2 rows are this workgroup's own (same pair split)
+  const uint64_t* h2 = reinterpret_cast<const uint64_t*>(wsp<float>(a, a.off.h2));
+  uint32_t* xb = wsp<uint32_t>(a, a.off.xbuf);
+  for (int r = r0 + 2 * threadIdx.x; r < r1; r += 2 * BLOCK) {
+    const uint64_t hv = ld_u64(h2 + r / 2);
+    const uint32_t lo = f32_to_bf16(__uint_as_float((uint32_t)hv) + L.outc[r - r0]);
+    const uint32_t hi = f32_to_bf16(__uint_as_float((uint32_t)(hv >> 32)) + L.outc[r + 1 - r0]);
+    st_u32(xb + r / 2, lo | (hi << 16));
+    if (out_hidden) gp(reinterpret_cast<uint32_t*>(out_hidden))[r / 2] = lo | (hi << 16);
+  }
+  stamp(a, cx, st, TR_DOWN_EPI);
   arrive(cx, S_OUT, st.k1, cx.nwg);
+  stamp(a, cx, st, TR_DOWN_DONE);
   return true;
 }
 
@@ -662,12 +787,13 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_gqa(KArgs a) {
       cx.token = t;
       Step st;
       st.Ly = layers + a.layer0 + li;
-      st.k1 = a.step0 + (uint32_t)(t * a.n_layers + li) + 1u;
+      st.idx = t * a.n_layers + li;
+      st.k1 = a.step0 + (uint32_t)st.idx + 1u;
       st.first = (t == 0 && li == 0);
+      st.in_hidden = st.first ? a.in_hidden : nullptr;
       st.pos = a.pos0 + t;
-      st.xs.p16 = st.first ? a.in_hidden : nullptr;
-      st.xs.p32 = st.first ? nullptr : wsp<uint32_t>(a, a.off.xbuf);
       const bool last = (t == a.n_tokens - 1) && (li == a.n_layers - 1);
+      stamp(a, cx, st, TR_START);
       if (!stage_qkv_gqa<SH>(cx, a, st, L)) return;
       if (!attention_gqa<SH>(cx, a, st, L)) return;
       if (!stage_wo<SH>(cx, a, st, L)) return;
@@ -681,8 +807,8 @@ typedef void (*KernelFn)(KArgs);
 
 // The compiled shapes: the tiny dense MHA layer (hidden 256, 4x64 heads, FFN 1024) and
 // the GQA MoE layer (hidden 4096, 32 q / 8 kv heads x 128, 64 experts of width 1536).
-using ShapeTinyDense = GqaShape<256, 4, 4, 64, 1024, false, false>;
-using ShapeGqaMoe = GqaShape<4096, 32, 8, 128, 1536, false, true>;
+using ShapeTinyDense = GqaShape<256, 4, 4, 64, 1024, false, false, 1, 2>;
+using ShapeGqaMoe = GqaShape<4096, 32, 8, 128, 1536, false, true, 9, 33>;
 
 template <class SH>
 static bool matches(const pld_config* c) {
@@ -718,6 +844,8 @@ struct pld_handle {
   hipStream_t last_stream;
   KernelFn fn;
   int device;
+  uint64_t* trace;
+  int trace_steps;
 };
 
 namespace {
@@ -756,6 +884,7 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
     if (c->router_kind != PLD_ROUTER_SOFTMAX_TOPK && c->router_kind != PLD_ROUTER_SIGMOID_BIAS) return PLD_E_UNSUPPORTED;
     if (c->hidden % 8) return PLD_E_UNSUPPORTED;
     k->slots = c->top_k + c->n_shared;
+    if (k->slots > MAX_SEGS) return PLD_E_UNSUPPORTED;
   } else {
     return PLD_E_UNSUPPORTED;
   }
@@ -767,13 +896,15 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
     k->cpg = nwg / c->n_kv_heads;
     k->chmax = (c->max_seq + k->cpg - 1) / k->cpg + 1;
     const int R = (c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
-    int act = std::max({c->hidden, c->n_heads * c->head_dim, k->slots * c->inter, 2 * c->n_experts,
-                        k->G * k->chmax + NWAVES * k->G * c->head_dim + 2 * k->G, 2 * k->G * k->cpg});
+    int act = std::max({c->hidden, c->n_heads * c->head_dim, k->slots * c->inter,
+                        k->G * k->chmax + NWAVES * k->G * c->head_dim + 2 * k->G,
+                        k->G * k->cpg * (c->head_dim + 2)});
     k->act_floats = (int)al(act, 64);
-    int outb = std::max({R / nwg + 4, c->hidden / nwg + 2, (k->slots * c->inter) / nwg + 2, c->inter / nwg + 2,
-                         2 * c->n_experts + 2});
+    k->stage_words = (int)al(c->hidden / 2 + 2, 64);
+    int outb = std::max({R / nwg + 4, k->slots * (c->hidden / nwg + 4), 2 * ((k->slots * c->inter) / nwg + 2),
+                         2 * (c->inter / nwg + 2) * std::max(1, c->n_shared), 4 * c->n_experts + 4});
     k->outb_floats = (int)al(outb, 64);
-    if (lds_bytes_for(k->act_floats, k->outb_floats) > 160 * 1024) return PLD_E_UNSUPPORTED;
+    if (lds_bytes_for(k->act_floats, k->stage_words, k->outb_floats) > 160 * 1024) return PLD_E_UNSUPPORTED;
   } else {
     return PLD_E_UNSUPPORTED;   // MLA path: not built yet
   }
@@ -794,7 +925,7 @@ WsOff layout(const KCfg& k, int n_layers) {
   o.part = p; p += al((size_t)k.nh * k.cpg * (k.hd + 2) * 4);
   o.o = p; p += al((size_t)std::max(k.nh * k.hd, 1) * 4);
   o.h2 = p; p += al((size_t)k.H * 4);
-  o.logits = p; p += al((size_t)std::max(k.E, 1) * 8);
+  o.logits = p; p += al((size_t)std::max(k.E, 1) * 16);
   o.sel = p; p += al(64 * 4);
   o.gates = p; p += al(64 * 4);
   o.m = p; p += al((size_t)k.slots * k.inter * 4);
@@ -908,11 +1039,13 @@ pld_status decode_layer_init(const pld_config* cfg, int32_t n_layers, const pld_
   h->n_layers = n_layers;
   h->ws = (uint8_t*)workspace;
   h->ws_bytes = ws_bytes;
-  h->lds_bytes = lds_bytes_for(k.act_floats, k.outb_floats);
+  h->lds_bytes = lds_bytes_for(k.act_floats, k.stage_words, k.outb_floats);
   h->steps = 0;
   h->bad = false;
   h->device = dev;
   h->last_stream = nullptr;
+  h->trace = nullptr;
+  h->trace_steps = 0;
   const char* coop = getenv("PLD_COOPERATIVE");
   h->coop = coop && atoi(coop) != 0;
   h->fn = pick_kernel(cfg);
@@ -963,6 +1096,8 @@ static pld_status launch(pld_handle* h, int layer0, int n_layers, int n_tokens, 
   a.in_hidden = (const uint16_t*)in_hidden;
   a.out_hidden = (uint16_t*)out_hidden;
   a.budget = h->budget;
+  a.trace = h->trace;
+  a.trace_steps = h->trace_steps;
   hipError_t e;
   if (h->coop) {
     void* args[] = {&a};
@@ -1035,11 +1170,11 @@ pld_status pld_debug_buffer(pld_handle* h, const char* name, void** ptr, size_t*
       {"o", h->off.o, (size_t)k.nh * k.hd * 4},
       {"h2", h->off.h2, (size_t)k.H * 4},
       {"b", h->off.b_dbg, (size_t)k.H * 4},
-      {"logits", h->off.logits, (size_t)k.E * 8},
+      {"logits", h->off.logits, (size_t)k.E * 16},
       {"sel", h->off.sel, (size_t)k.topk * 4},
       {"gates", h->off.gates, (size_t)k.topk * 4},
       {"m", h->off.m, (size_t)k.slots * k.inter * 4},
-      {"x", h->off.xbuf, (size_t)k.H * 4},
+      {"x", h->off.xbuf, (size_t)k.H * 2},
   };
   for (auto& e : tab)
     if (!strcmp(e.n, name)) {
@@ -1054,6 +1189,20 @@ pld_status pld_launch_shape(pld_handle* h, int32_t* n_wg, int32_t* block) {
   if (!h || !n_wg || !block) return PLD_E_INVALID;
   *n_wg = h->kc.nwg;
   *block = BLOCK;
+  return PLD_OK;
+}
+
+pld_status pld_set_trace(pld_handle* h, void* buffer, size_t bytes) {
+  if (!h) return PLD_E_INVALID;
+  const size_t row = (size_t)h->kc.nwg * TR_SLOTS * sizeof(uint64_t);
+  if (!buffer || bytes < row) {
+    h->trace = nullptr;
+    h->trace_steps = 0;
+    return buffer ? PLD_E_CAPACITY : PLD_OK;
+  }
+  if (((uintptr_t)buffer & 7u) != 0) return PLD_E_INVALID;
+  h->trace = (uint64_t*)buffer;
+  h->trace_steps = (int)std::min(bytes / row, (size_t)1 << 20);
   return PLD_OK;
 }
 
