@@ -215,14 +215,14 @@ enum OutMode { OUT_STORE = 0, OUT_ACCUM = 1 };
 
 // Lane layout per reduction length K (elements) and weight format, fixed at compile time:
 // LPR lanes per row, CPL 16-byte chunks per lane and row, U rows in flight per wave
-// (U*CPL ~ 24 loads of 16 bytes per lane: ~190 KB in flight per 512-thread workgroup).
-template <bool FP8, int K>
+// (U*CPL ~ INFL loads of 16 bytes per lane: INFL * 8 KB in flight per 512-thread workgroup).
+template <bool FP8, int K, int INFL>
 struct GemvLayout {
   static constexpr int EPC = FP8 ? 16 : 8;
   static constexpr int CHUNKS = K / EPC;
   static constexpr int LPR = CHUNKS >= 64 ? 64 : CHUNKS;
   static constexpr int CPL = CHUNKS / LPR;
-  static constexpr int U0 = 24 / CPL;
+  static constexpr int U0 = INFL / CPL;
   static constexpr int U = U0 < 1 ? 1 : (U0 > 12 ? 12 : U0);
   static_assert(K % EPC == 0 && CHUNKS % LPR == 0 && (LPR == 16 || LPR == 32 || LPR == 64), "unsupported K");
 };
@@ -251,10 +251,10 @@ constexpr int MAX_SEGS = 12;
 //  * partial sums are reduced across the LPR lanes and the row's first lane writes the
 //    result into out[i] (LDS) per OutMode.
 // `segs` lives in LDS. Returns false if pre() reported an abort.
-template <bool FP8, int K, typename Pre>
+template <bool FP8, int K, int INFL, typename Pre>
 __device__ __forceinline__ bool gemv_list(const RowSeg* segs, int nseg, const float* act, float* out, int mode,
                                           Pre&& pre) {
-  using LY = GemvLayout<FP8, K>;
+  using LY = GemvLayout<FP8, K, INFL>;
   constexpr int EPC = LY::EPC, LPR = LY::LPR, CPL = LY::CPL, U = LY::U;
   constexpr int RPW = 64 / LPR;
   constexpr int SBK = (K + 127) / 128;

@@ -40,14 +40,15 @@
 namespace pld {
 
 // ------------------------------------------------------------------ shared structs
-enum Stage { S_QKV = 0, S_H2 = 1, S_RT = 2, S_M = 3, S_OUT = 4, NSTG = 8 };
+enum Stage { S_QKV = 0, S_H2 = 1, S_RT = 2, S_M = 3, S_OUT = 4, S_ATT = 5, NSTG = 8 };
 enum { ST_CODE = 0, ST_STAGE = 1, ST_LAYER = 2, ST_TOKEN = 3, ST_WG = 4, ST_ABORT = 8 };
 // device trace: wall-clock stamps per (step, workgroup)
 enum TraceSlot {
   TR_START = 0, TR_X_READY, TR_QKV_DONE, TR_ATT_READY, TR_ATT_DONE, TR_O_READY, TR_WO_DONE, TR_H2_READY,
   TR_RT_READY, TR_FFN_DONE, TR_M_READY, TR_DOWN_DONE, TR_ATT_Q = 12, TR_ATT_SOFTMAX = 13, TR_ATT_PARTIAL = 14,
   TR_ATT_MERGED = 15, TR_TOPK = 16, TR_ROUTED_GEMV = 17, TR_M_STORED = 18, TR_DOWN_GEMV = 19, TR_DOWN_EPI = 20,
-  TR_QKV_GEMV = 21, TR_SHARED_GEMV = 22, TR_SLOTS = 32
+  TR_QKV_GEMV = 21, TR_SHARED_GEMV = 22, TR_X_COPIED = 23, TR_X_NORMED = 24, TR_MERGE_FLAG = 25,
+  TR_MERGE_COPIED = 26, TR_RT_LOGIT = 27, TR_O_COPIED = 28, TR_M_COPIED = 29, TR_ATT_SCORES = 30, TR_SLOTS = 32
 };
 
 struct KCfg {
@@ -168,6 +169,62 @@ __device__ __forceinline__ void rmsnorm_inplace(float* act, const float* __restr
   __syncthreads();
 }
 
+// This thread's elements i = threadIdx.x + k*BLOCK of a length-N fp32 vector, held in
+// registers. Small static vectors (norm weights) are loaded this way BEFORE a stage's
+// weight prefetch is issued, so they sit at the front of the wave's in-order load queue
+// instead of behind ~tens of KB of weight loads.
+template <int N>
+struct RegVec {
+  static constexpr int K = (N + BLOCK - 1) / BLOCK;
+  float v[K];
+  __device__ __forceinline__ void load(const float* p) {
+    const PLD_GLOBAL float* g = gp(p);
+#pragma unroll
+    for (int k = 0; k < K; k++) {
+      const int i = threadIdx.x + k * BLOCK;
+      v[k] = i < N ? g[i] : 0.f;
+    }
+  }
+};
+// rmsnorm_inplace with the weights in registers (same arithmetic, same summation order)
+template <int N>
+__device__ __forceinline__ void rmsnorm_reg(float* act, const RegVec<N>& gam, double eps, double* red) {
+  double ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < RegVec<N>::K; k++) {
+    const int i = threadIdx.x + k * BLOCK;
+    if (i < N) ss += (double)act[i] * (double)act[i];
+  }
+  ss = block_sum(ss, red);
+  const double r = 1.0 / sqrt(ss / (double)N + eps);
+#pragma unroll
+  for (int k = 0; k < RegVec<N>::K; k++) {
+    const int i = threadIdx.x + k * BLOCK;
+    if (i < N) act[i] = (float)(((double)act[i] * r) * (double)gam.v[k]);
+  }
+  __syncthreads();
+}
+
+// Weight loads in flight per lane for each GEMV stage (16-byte loads). Deep prefetch
+// keeps HBM busy, but every load queued ahead of a latency-critical access (a counter
+// poll, an activation copy) delays it: the queue drains at the lane's share of HBM
+// bandwidth. The depths below were chosen by measurement.
+#ifndef PLD_IF_QKV
+#define PLD_IF_QKV 8
+#endif
+#ifndef PLD_IF_WO
+#define PLD_IF_WO 8
+#endif
+#ifndef PLD_IF_SHARED
+#define PLD_IF_SHARED 8
+#endif
+#ifndef PLD_IF_ROUTED
+#define PLD_IF_ROUTED 8
+#endif
+#ifndef PLD_IF_DOWN
+#define PLD_IF_DOWN 8
+#endif
+
 // ------------------------------------------------------------------ LDS layout
 struct Lds {
   float* act;        // [act_floats]   activation vector / attention scratch / merge staging
@@ -259,6 +316,8 @@ __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Ste
   const int r0 = 2 * split_at(P, nwg, w), r1 = 2 * split_at(P, nwg, w + 1);
   int h0, h1;
   hrows(SH::H, nwg, w, &h0, &h1);
+  RegVec<SH::H> gam;
+  gam.load(Ly.attn_norm);
   bool pending = true;   // the input wait + RMSNorm has not run yet
   auto pre_x = [&]() -> bool {
     if (!pending) return true;
@@ -273,6 +332,7 @@ __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Ste
       coh_copy_to_lds(L.stage, wsp<uint32_t>(a, a.off.xbuf), SH::H / 2);
     }
     __syncthreads();
+    stamp(a, cx, st, TR_X_COPIED);
     for (int i = threadIdx.x; i < SH::H / 2; i += BLOCK) {
       const uint32_t v = L.stage[i];
       L.act[2 * i] = bf_lo(v);
@@ -280,7 +340,8 @@ __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Ste
     }
     __syncthreads();
     for (int r = h0 + threadIdx.x; r < h1; r += BLOCK) L.xres[r - h0] = L.act[r];
-    rmsnorm_inplace(L.act, Ly.attn_norm, SH::H, c.eps, L.red);
+    rmsnorm_reg<SH::H>(L.act, gam, c.eps, L.red);
+    stamp(a, cx, st, TR_X_NORMED);
     if (w == 0)
       for (int i = threadIdx.x; i < SH::H; i += BLOCK) st_f32(wsp<float>(a, a.off.a_dbg) + i, L.act[i]);
     return true;
@@ -301,7 +362,7 @@ __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Ste
       }
     }
     seg_end();
-    if (!gemv_list<SH::FP8, SH::H>(L.segs, ns, L.act, L.outb, OUT_STORE, pre_x)) return false;
+    if (!gemv_list<SH::FP8, SH::H, PLD_IF_QKV>(L.segs, ns, L.act, L.outb, OUT_STORE, pre_x)) return false;
   }
   stamp(a, cx, st, TR_QKV_GEMV);
   if (!pre_x()) return false;
@@ -358,6 +419,7 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
   const int dl = lane % LPT, tl = lane / LPT;
   const int cpg = c.cpg;
   const int g = cx.w / cpg, ch = cx.w % cpg;
+  if (g < SH::NKV) {   // workgroups past the last group only take part in the final arrive
   const int T = st.pos + 1;
   const int t0 = split_at(T, cpg, ch), t1 = split_at(T, cpg, ch + 1), n = t1 - t0;
   const int tw = (n + NWAVES - 1) / NWAVES;             // P.V tokens per wave
@@ -437,6 +499,7 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
       }
     }
   }
+  stamp(a, cx, st, TR_ATT_SCORES);
   __syncthreads();
   for (int h = wave; h < G; h += NWAVES) {
     float m = -INFINITY;
@@ -504,43 +567,55 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
     st_u64(reinterpret_cast<uint64_t*>(part + ((size_t)(g * G + h) * cpg + ch) * (HD + 2)),
            (uint64_t)__float_as_uint(ml[2 * h]) | ((uint64_t)__float_as_uint(ml[2 * h + 1]) << 32));
   }
-  // last arriver of the group merges (all partials of the group are one contiguous block)
+  // Distributed merge: once all cpg partials of the group are stored, workgroup ch of
+  // the group merges dims [d0, d1) of the group's G*HD outputs (flash-decoding rescale:
+  // o = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c over the chunks with l_c > 0).
   vm_wait();
   __syncthreads();
   stamp(a, cx, st, TR_ATT_PARTIAL);
-  if (threadIdx.x == 0) {
-    const uint32_t old = atomic_add_u32(cx.ctr_grp + g * CTR_STRIDE, 1u);
-    L.flag[0] = (old + 1u == k1 * (uint32_t)cpg);
-  }
-  __syncthreads();
-  if (L.flag[0]) {
-    float* pl = L.act;   // [G][cpg][HD+2]
-    coh_copy_to_lds<24>(reinterpret_cast<uint32_t*>(pl),
-                        reinterpret_cast<const uint32_t*>(part + (size_t)g * G * cpg * (HD + 2)), G * cpg * (HD + 2));
+  if (threadIdx.x == 0) atomic_add_u32(cx.ctr_grp + g * CTR_STRIDE, 1u);
+  if (!spin_until(cx, cx.ctr_grp + g * CTR_STRIDE, k1 * (uint32_t)cpg, 9)) return false;
+  stamp(a, cx, st, TR_MERGE_FLAG);
+  {
+    const int d0 = split_at(G * HD, cpg, ch), d1 = split_at(G * HD, cpg, ch + 1), nd = d1 - d0;
+    const float* pg = part + (size_t)g * G * cpg * (HD + 2);
+    float* mls = L.act;              // [cpg][2] (m, l) of the head of dim d0 .. (two heads at most)
+    float* accs = L.act + 4 * cpg;   // [cpg][nd]
+    const int h0 = d0 / HD, hlast = (d1 - 1) / HD;
+    for (int i = threadIdx.x; i < cpg * nd; i += BLOCK) {
+      const int cc = i / nd, j = i % nd, d = d0 + j;
+      accs[i] = ld_f32(pg + ((size_t)(d / HD) * cpg + cc) * (HD + 2) + 2 + d % HD);
+    }
+    for (int i = threadIdx.x; i < cpg * (hlast - h0 + 1); i += BLOCK) {
+      const int hh = i / cpg, cc = i % cpg;
+      const uint64_t v = ld_u64(reinterpret_cast<const uint64_t*>(pg + ((size_t)(h0 + hh) * cpg + cc) * (HD + 2)));
+      mls[2 * i] = __uint_as_float((uint32_t)v);
+      mls[2 * i + 1] = __uint_as_float((uint32_t)(v >> 32));
+    }
     __syncthreads();
-    float* obuf = wsp<float>(a, a.off.o);
-    for (int i = threadIdx.x; i < G * HD; i += BLOCK) {
-      const int h = i / HD, d = i % HD;
-      const float* ph = pl + (size_t)h * cpg * (HD + 2);
+    stamp(a, cx, st, TR_MERGE_COPIED);
+    float* obuf = wsp<float>(a, a.off.o) + (size_t)g * G * HD;
+    for (int j = threadIdx.x; j < nd; j += BLOCK) {
+      const int d = d0 + j;
+      const float* ml2 = mls + 2 * cpg * (d / HD - h0);
       float M = -INFINITY;
       for (int cc = 0; cc < cpg; cc++)
-        if (ph[cc * (HD + 2) + 1] > 0.f) M = fmaxf(M, ph[cc * (HD + 2)]);
+        if (ml2[2 * cc + 1] > 0.f) M = fmaxf(M, ml2[2 * cc]);
       float Ls = 0.f, o = 0.f;
       for (int cc = 0; cc < cpg; cc++) {
-        const float l = ph[cc * (HD + 2) + 1];
+        const float l = ml2[2 * cc + 1];
         if (l > 0.f) {
-          const float f = __expf(ph[cc * (HD + 2)] - M);
+          const float f = __expf(ml2[2 * cc] - M);
           Ls += f * l;
-          o += f * ph[cc * (HD + 2) + 2 + d];
+          o += f * accs[cc * nd + j];
         }
       }
-      st_f32(obuf + (size_t)(g * G + h) * HD + d, o / Ls);
+      st_f32(obuf + d, o / Ls);
     }
-    vm_wait();
-    __syncthreads();
-    if (threadIdx.x == 0) atomic_add_u32(cx.ctr_att, 1u);
-    stamp(a, cx, st, TR_ATT_MERGED);
   }
+  }   // grouped workgroups
+  arrive(cx, S_ATT, k1, cx.nwg);
+  stamp(a, cx, st, TR_ATT_MERGED);
   stamp(a, cx, st, TR_ATT_DONE);
   return true;
 }
@@ -551,10 +626,11 @@ __device__ __forceinline__ bool stage_wo(Ctx& cx, const KArgs& a, const Step& st
   int r0, r1;
   hrows(SH::H, cx.nwg, cx.w, &r0, &r1);
   auto pre_o = [&]() -> bool {
-    if (!spin_until(cx, cx.ctr_att, st.k1 * (uint32_t)SH::NKV, 10)) return false;
+    if (!wait_all(cx, S_ATT, st.k1, cx.nwg)) return false;
     stamp(a, cx, st, TR_O_READY);
     coh_copy_to_lds(reinterpret_cast<uint32_t*>(L.act), wsp<uint32_t>(a, a.off.o), SH::ODIM);
     __syncthreads();
+    stamp(a, cx, st, TR_O_COPIED);
     return true;
   };
   {
@@ -562,7 +638,7 @@ __device__ __forceinline__ bool stage_wo(Ctx& cx, const KArgs& a, const Step& st
     seg_begin();
     seg_set(L, 0, wo.w + (size_t)r0 * SH::ODIM * (SH::FP8 ? 1 : 2), wo.s, r1 - r0, r0, 0, 1.f);
     seg_end();
-    if (!gemv_list<SH::FP8, SH::ODIM>(L.segs, r1 > r0 ? 1 : 0, L.act, L.outb, OUT_STORE, pre_o)) return false;
+    if (!gemv_list<SH::FP8, SH::ODIM, PLD_IF_WO>(L.segs, r1 > r0 ? 1 : 0, L.act, L.outb, OUT_STORE, pre_o)) return false;
   }
   __syncthreads();
   float* h2 = wsp<float>(a, a.off.h2);
@@ -579,7 +655,7 @@ __device__ __forceinline__ bool stage_wo(Ctx& cx, const KArgs& a, const Step& st
 // m[slot][j] = silu(gate_j . b) * (up_j . b). Each piece contributes a gate segment and
 // an up segment; results come back in list order.
 struct GuPiece { int expert, slot, j0, j1; };
-template <class SH, typename Pre>
+template <class SH, int INFL, typename Pre>
 __device__ __forceinline__ bool gate_up_list(const KArgs& a, const Step& st, Lds& L, const GuPiece* pc, int np, Pre&& pre) {
   const DLayer Ly = *gp(st.Ly);
   constexpr size_t RB = (size_t)SH::H * (SH::FP8 ? 1 : 2);
@@ -592,7 +668,7 @@ __device__ __forceinline__ bool gate_up_list(const KArgs& a, const Step& st, Lds
     seg_set(L, 2 * p + 1, Ly.w_up.w + bo, su, pc[p].j1 - pc[p].j0, pc[p].j0, 0, 1.f);
   }
   seg_end();
-  if (!gemv_list<SH::FP8, SH::H>(L.segs, 2 * np, L.act, L.outb, OUT_STORE, pre)) return false;
+  if (!gemv_list<SH::FP8, SH::H, INFL>(L.segs, 2 * np, L.act, L.outb, OUT_STORE, pre)) return false;
   __syncthreads();
   float* mbuf = wsp<float>(a, a.off.m);
   int base = 0;
@@ -610,6 +686,21 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
   const KCfg& c = a.c;
   const DLayer Ly = *gp(st.Ly);
   const int w = cx.w, nwg = cx.nwg;
+  RegVec<SH::H> gam;
+  gam.load(Ly.ffn_norm);
+  // router workgroups: their router row, loaded ahead of the expert weights
+  constexpr int RCH = SH::H / 8, RPT = (RCH + BLOCK - 1) / BLOCK;
+  uint4 rrow[SH::MOE ? RPT : 1];
+  if constexpr (SH::MOE) {
+    if (w < c.E) {
+      const uint16_t* rp0 = Ly.router + (size_t)w * SH::H;
+#pragma unroll
+      for (int k = 0; k < RPT; k++) {
+        const int q = threadIdx.x + k * BLOCK;
+        rrow[k] = q < RCH ? ld_g16(rp0 + q * 8) : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  }
   bool pending = true;
   // wait for h2, RMSNorm it into LDS; router workgroups compute their logit (fp64)
   auto pre_b = [&]() -> bool {
@@ -619,16 +710,19 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
     stamp(a, cx, st, TR_H2_READY);
     coh_copy_to_lds(reinterpret_cast<uint32_t*>(L.act), wsp<uint32_t>(a, a.off.h2), SH::H);
     __syncthreads();
-    rmsnorm_inplace(L.act, Ly.ffn_norm, SH::H, c.eps, L.red);
+    rmsnorm_reg<SH::H>(L.act, gam, c.eps, L.red);
     if (w == 0)
       for (int i = threadIdx.x; i < SH::H; i += BLOCK) st_f32(wsp<float>(a, a.off.b_dbg) + i, L.act[i]);
     if constexpr (SH::MOE) {
       if (w < c.E) {
         // logit of expert w (fp64 accumulation) and its selection key: the logit itself
         // (softmax router) or sigmoid(logit) + bias (biased-score router)
-        const uint16_t* rrow = Ly.router + (size_t)w * SH::H;
         double s = 0.0;
-        for (int q = threadIdx.x; q < SH::H / 8; q += BLOCK) s += dot8_bf16_f64(ld_g16(rrow + q * 8), L.act + q * 8);
+#pragma unroll
+        for (int k = 0; k < RPT; k++) {
+          const int q = threadIdx.x + k * BLOCK;
+          if (q < RCH) s += dot8_bf16_f64(rrow[k], L.act + q * 8);
+        }
         s = block_sum(s, L.red);
         if (threadIdx.x == 0) {
           const double key = c.router == PLD_ROUTER_SIGMOID_BIAS
@@ -637,6 +731,7 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
           st_u64(reinterpret_cast<uint64_t*>(lk), (uint64_t)__double_as_longlong(s));
           st_u64(reinterpret_cast<uint64_t*>(lk + 1), (uint64_t)__double_as_longlong(key));
         }
+        stamp(a, cx, st, TR_RT_LOGIT);
       }
       arrive(cx, S_RT, st.k1, c.E);
     }
@@ -645,13 +740,13 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
   const int j0 = split_at(SH::INTER, nwg, w), j1 = split_at(SH::INTER, nwg, w + 1);
   if constexpr (!SH::MOE) {
     const GuPiece pc[1] = {{0, 0, j0, j1}};
-    if (!gate_up_list<SH>(a, st, L, pc, j1 > j0 ? 1 : 0, pre_b)) return false;
+    if (!gate_up_list<SH, PLD_IF_SHARED>(a, st, L, pc, j1 > j0 ? 1 : 0, pre_b)) return false;
   } else {
     // shared experts first: they do not depend on the router
     GuPiece pc[2];
     int np = 0;
     for (int sj = 0; sj < c.nshared && j1 > j0; sj++) pc[np++] = {c.E + sj, c.topk + sj, j0, j1};
-    if (!gate_up_list<SH>(a, st, L, pc, np, pre_b)) return false;
+    if (!gate_up_list<SH, PLD_IF_SHARED>(a, st, L, pc, np, pre_b)) return false;
     if (!pre_b()) return false;
     stamp(a, cx, st, TR_SHARED_GEMV);
     // router top-k (every workgroup computes the same selection)
@@ -700,7 +795,7 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
       const int lo = max(i0, s * SH::INTER) - s * SH::INTER, hi = min(i1, (s + 1) * SH::INTER) - s * SH::INTER;
       if (lo < hi) rp[nr++] = {L.isel[s], s, lo, hi};
     }
-    if (!gate_up_list<SH>(a, st, L, rp, nr, NoPre{})) return false;
+    if (!gate_up_list<SH, PLD_IF_ROUTED>(a, st, L, rp, nr, NoPre{})) return false;
   }
   stamp(a, cx, st, TR_M_STORED);
   arrive(cx, S_M, st.k1, nwg);
@@ -723,6 +818,7 @@ __device__ __forceinline__ bool stage_down(Ctx& cx, const KArgs& a, const Step& 
     stamp(a, cx, st, TR_M_READY);
     coh_copy_to_lds(reinterpret_cast<uint32_t*>(L.act), wsp<uint32_t>(a, a.off.m), c.slots * SH::INTER);
     __syncthreads();
+    stamp(a, cx, st, TR_M_COPIED);
     return true;
   };
   {
@@ -736,7 +832,8 @@ __device__ __forceinline__ bool stage_down(Ctx& cx, const KArgs& a, const Step& 
       seg_set(L, s, Ly.w_down.w + bo, sd, r1 - r0, r0, s * SH::INTER, 1.f);
     }
     seg_end();
-    if (!gemv_list<SH::FP8, SH::INTER>(L.segs, r1 > r0 ? c.slots : 0, L.act, L.outb, OUT_STORE, pre_m)) return false;
+    if (!gemv_list<SH::FP8, SH::INTER, PLD_IF_DOWN>(L.segs, r1 > r0 ? c.slots : 0, L.act, L.outb, OUT_STORE, pre_m))
+      return false;
   }
   stamp(a, cx, st, TR_DOWN_GEMV);
   if (!pre_m()) return false;
