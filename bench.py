@@ -101,24 +101,18 @@ def write_trace_summary(dec, shape, pos, x, out, R, path):
         seg[f"{a_}->{b_}"] = {"median_us": round(float(np.median(d)), 2), "max_us": round(float(d.max()), 2)}
     full = buf.cpu().numpy().reshape(R, nwg, 32).astype(np.float64)
     att = {}
-    for name, i0, i1 in (("att_ready->q_loaded", 3, 12), ("q_loaded->softmax", 12, 13), ("softmax->partial_stored", 13, 14),
-                         ("partial_stored->att_done", 14, 4), ("x_ready->qkv_gemv", 1, 21), ("qkv_gemv->qkv_done", 21, 2),
+    for name, i0, i1 in (("att_ready->q_regs", 3, 12), ("q_regs->scores", 12, 30), ("scores->softmax", 30, 13),
+                         ("softmax->pv", 13, 23), ("pv->drained", 23, 28), ("drained->partial_stored", 28, 14),
+                         ("partial_stored->merge_start", 14, 25), ("merge_start->merge_fetched", 25, 26),
+                         ("merge_fetched->merged", 26, 15),
+                         ("x_ready->x_normed", 1, 24), ("x_normed->qkv_gemv", 24, 21), ("qkv_gemv->qkv_done", 21, 2),
+                         ("o_ready->wo_done", 5, 6),
                          ("h2_ready->shared_gemv", 7, 22), ("shared_gemv->router_ready", 22, 8),
                          ("router_ready->topk", 8, 16), ("topk->m_stored", 16, 18),
-                         ("m_stored->ffn_done", 18, 9), ("m_ready->down_gemv", 10, 19), ("down_gemv->out_stored", 19, 20),
-                         ("out_stored->down_done", 20, 11),
-                         ("x_ready->x_copied", 1, 23), ("x_copied->x_normed", 23, 24), ("x_normed->qkv_gemv", 24, 21),
-                         ("o_ready->o_copied", 5, 28), ("o_copied->wo_done", 28, 6),
-                         ("m_ready->m_copied", 10, 29), ("m_copied->down_gemv", 29, 19),
-                         ("q_loaded->scores", 12, 30), ("scores->softmax", 30, 13)):
+                         ("m_ready->down_gemv", 10, 19), ("down_gemv->epilogue", 19, 20), ("epilogue->down_done", 20, 11)):
         d = (full[:, :, i1] - full[:, :, i0]) * tick_us
         att[name] = {"median_us": round(float(np.median(d)), 2), "max_us": round(float(d.max()), 2)}
-    merged = full[:, :, 15] > 0
-    if merged.any():
-        d = (full[:, :, 15] - full[:, :, 14])[merged] * tick_us
-        att["partial_stored->merged (mergers only)"] = {"median_us": round(float(np.median(d)), 2), "max_us": round(float(d.max()), 2)}
-    for name, i0, i1, sel in (("partial_stored->merge_flag (mergers)", 14, 25, 25), ("merge_flag->merge_copied", 25, 26, 25),
-                              ("merge_copied->merged", 26, 15, 25), ("h2_ready->router_logit (router wgs)", 7, 27, 27),
+    for name, i0, i1, sel in (("h2_ready->router_logit (router wgs)", 7, 27, 27),
                               ("router_logit->router_ready (router wgs)", 27, 8, 27)):
         msk = full[:, :, sel] > 0
         if msk.any():

@@ -4,7 +4,8 @@
  * One decode step of one MoE transformer layer runs as ONE launch of a persistent
  * cooperative kernel: every workgroup stays resident, and the stages (RMSNorm,
  * projections, attention, output projection + residual, router top-k, experts) are
- * chained by device-side counters instead of kernel boundaries. This is the
+ * chained by device-side data dependencies (epoch-tagged activation words that the
+ * consumers poll) instead of kernel boundaries. This is the
  * "persistent Engine Kernel" of the TileRT article (InferenceX, "Ultra-High
  * Interactivity on NVIDIA GPUs? TileRT on InferenceX", section "But What Exactly is
  * TileRT?": the host launches once and execution stays on the GPU; stages overlap at
@@ -132,7 +133,9 @@ typedef struct pld_head_weights {
 /* Device status read back by decode_poll_status. code 0 = ok. */
 typedef struct pld_device_status {
   int32_t code;       /* 0 ok, PLD_E_DEVICE_TIMEOUT when a wait expired */
-  int32_t stage;      /* stage id whose wait expired */
+  int32_t stage;      /* what the expired wait was for: 0 layer input x, 1 q, 2 new k/v row,
+                         3 attention partials, 4 attention output o, 5 h2, 6 router logits,
+                         7 expert activations m */
   int32_t layer;      /* layer index (within the launch's stack) */
   int32_t token;      /* token index within the launch */
   int32_t wg;         /* workgroup that detected it */
@@ -156,14 +159,14 @@ typedef struct pld_persistent_args {
 typedef struct pld_handle pld_handle;
 
 /* Bytes of device workspace decode_layer_init needs for this shape and stack depth
- * (counters, intermediates, attention partials, RoPE table, layer descriptors).
+ * (status, handoff buffers, attention partials, RoPE table, layer descriptors).
  * Returns 0 for an invalid or unsupported configuration. */
 size_t pld_workspace_bytes(const pld_config* cfg, int32_t n_layers);
 
 /* Validate the configuration and pointers, build the static per-workgroup schedule
  * (the ahead-of-time scheduling of the TileRT article, section "Why Is TileRT
  * Development Slow?", done here at init), upload the RoPE table and layer
- * descriptors into `workspace`, zero the counters, and check that the persistent grid
+ * descriptors into `workspace`, zero the handoff buffers, and check that the persistent grid
  * can be co-resident. Synchronous. Nothing is allocated on the device.
  *   cfg:       layer shape (copied)
  *   n_layers:  number of layers in `w` and `kv` (>= 1)
@@ -198,7 +201,8 @@ pld_status decode_layers_persistent(pld_handle* h, const pld_persistent_args* a,
  * Returns PLD_OK, or PLD_E_DEVICE_TIMEOUT if the last launch's watchdog fired. */
 pld_status decode_poll_status(pld_handle* h, pld_device_status* out);
 
-/* Re-zero counters and status so the handle can be used again (synchronous). */
+/* Clear the status and the inter-workgroup handoff buffers so the handle can be used
+ * again (synchronous). The step epoch keeps counting across resets. */
 pld_status decode_reset(pld_handle* h);
 
 /* Free the host-side handle. Device memory stays with the caller. NULL is ignored. */
@@ -208,9 +212,11 @@ void decode_layer_destroy(pld_handle* h);
 const char* pld_status_string(pld_status s);
 
 /* Device pointer and size in bytes of a named intermediate in the workspace, as left by
- * the last completed launch (for tests): "a", "q", "o", "h2", "b", "logits" (fp64 pairs
- * (logit, selection key) per expert),
- * "sel" (int32), "gates" (fp32), "m", "x". Returns PLD_E_INVALID for an unknown name. */
+ * the last completed launch (for tests). Plain arrays: "a", "b" (fp32 [hidden]), "sel"
+ * (int32 [top_k]), "gates" (fp32 [top_k]). LL arrays of 8-byte words whose low 32 bits
+ * are the payload and high 32 bits the step epoch: "q", "o", "h2", "m" (fp32 payloads),
+ * "x" (bf16 pairs), "logits" (4 words per expert: logit and selection key as fp64,
+ * low then high halves). Returns PLD_E_INVALID for an unknown name. */
 pld_status pld_debug_buffer(pld_handle* h, const char* name, void** ptr, size_t* bytes);
 
 /* Launch geometry actually used: number of workgroups and threads per workgroup. */

@@ -67,6 +67,9 @@ class PldPersistentArgs(ctypes.Structure):
                 ("out_accepted", vp), ("reserved", i32 * 4)]
 
 
+# intermediates kept as LL words (32-bit payload, 32-bit epoch) in the workspace
+LL_BUFFERS = ("q", "o", "h2", "logits", "m", "x")
+
 _lib = None
 
 
@@ -248,5 +251,7 @@ class Decoder:
         check(lib().pld_debug_buffer(self.handle, name.encode(), ctypes.byref(p), ctypes.byref(nb)), "pld_debug_buffer")
         off = p.value - self.workspace.data_ptr()
         raw = self.workspace[off: off + nb.value].clone()
+        if name in LL_BUFFERS:   # 8-byte LL words: keep the 32-bit payloads (low halves)
+            raw = raw.view(torch.int32)[0::2].contiguous().view(torch.uint8)
         dt = dtype or {"logits": torch.float64, "sel": torch.int32, "x": torch.int16}.get(name, torch.float32)
         return raw.view(dt)

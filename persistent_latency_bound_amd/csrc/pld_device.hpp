@@ -6,14 +6,16 @@
 //    device coherence point, and read back with agent-scope relaxed atomic loads.
 //    No L2 write-back or invalidate is needed per stage; weights use ordinary
 //    (non-temporal) loads because they are never written.
-//  * A producer workgroup waits for its own stores (s_waitcnt vmcnt(0) in every
-//    wave), passes a workgroup barrier, and one thread bumps a per-XCD counter; the
-//    last arriver of each XCD group bumps the stage's global counter. Consumers poll
-//    the global counter. A grid-wide dependency costs about 2.8 us this way, versus
-//    ~10 us for one flat counter with release/acquire fences.
-//  * Only static weights may be loaded before a wait; activations are always read
-//    after it. This is the ordering rule the vLLM Kimi K3 backend article reports
-//    from its kernel audit (section "Agent-written kernels face evidence gates").
+//  * Activations move as LL words: each 8-byte store holds a 32-bit payload and the
+//    step's epoch, so the consumer polls the data itself. A handoff then costs about
+//    one store plus one load round trip; a counter barrier (drain the stores, count
+//    per XCD, count globally, poll) cost four to five, i.e. ~10 us per stage boundary
+//    while HBM is busy, because every round trip queues behind the weight stream.
+//  * Only static weights may be loaded before an activation is read. This is the
+//    ordering rule the vLLM Kimi K3 backend article reports from its kernel audit
+//    (section "Agent-written kernels face evidence gates").
+//  * A wave's loads return in order, so a latency-critical load waits for every weight
+//    load the wave issued before it: prefetch depth is kept to what HBM needs.
 //  * Every wait is bounded by a wall-clock deadline; on expiry the workgroup records
 //    a status word, raises a global abort flag and leaves, and so do all others.
 #pragma once
@@ -43,6 +45,15 @@ template <typename T>
 __device__ __forceinline__ PLD_GLOBAL T* gp(T* p) { return (PLD_GLOBAL T*)(p); }
 template <typename T>
 __device__ __forceinline__ const PLD_GLOBAL T* gp(const T* p) { return (const PLD_GLOBAL T*)(p); }
+
+// tid_opaque() as a value the compiler cannot treat as loop-invariant: per-lane addresses
+// computed from it inside a helper are then not hoisted out of the layer loop, where they
+// would stay live (and spill) across every stage.
+__device__ __forceinline__ int tid_opaque() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
 
 // 16-byte streaming load of static weights (non-temporal hint: read once per step)
 __device__ __forceinline__ uint4 ld_stream16(const void* p) {
@@ -78,6 +89,17 @@ __device__ __forceinline__ uint64_t ld_u64(const uint64_t* p) {
 }
 __device__ __forceinline__ void st_u64(uint64_t* p, uint64_t v) {
   __hip_atomic_store(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The same loads/stores addressed as uniform base + 32-bit byte offset: the compiler can
+// use the scalar-base + 32-bit vector-offset form, so no 64-bit per-lane address has to
+// stay live across the layer loop.
+__device__ __forceinline__ uint64_t ld_u64_off(const void* base, uint32_t byte_off) {
+  const PLD_GLOBAL char* b = gp(reinterpret_cast<const char*>(base));
+  return __hip_atomic_load((PLD_GLOBAL uint64_t*)(b + byte_off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_u64_off(void* base, uint32_t byte_off, uint64_t v) {
+  PLD_GLOBAL char* b = gp(reinterpret_cast<char*>(base));
+  __hip_atomic_store((PLD_GLOBAL uint64_t*)(b + byte_off), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t atomic_add_u32(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -131,7 +153,7 @@ __device__ __forceinline__ float dpp_sum(float v) {
 template <typename T>
 __device__ __forceinline__ T block_sum(T v, T* red) {
   v = wave_sum(v);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tid_opaque() & 63, wave = tid_opaque() >> 6;
   __syncthreads();
   if (lane == 0) red[wave] = v;
   __syncthreads();
@@ -196,12 +218,12 @@ __device__ __forceinline__ void coh_copy_to_lds(uint32_t* dst, const uint32_t* s
     uint64_t v[PER];
 #pragma unroll
     for (int j = 0; j < PER; j++) {
-      const int i = base + j * BLOCK + threadIdx.x;
+      const int i = base + j * BLOCK + tid_opaque();
       v[j] = i < n2 ? ld_u64(s + i) : 0ull;
     }
 #pragma unroll
     for (int j = 0; j < PER; j++) {
-      const int i = base + j * BLOCK + threadIdx.x;
+      const int i = base + j * BLOCK + tid_opaque();
       if (i < n2) {
         dst[2 * i] = (uint32_t)v[j];
         dst[2 * i + 1] = (uint32_t)(v[j] >> 32);
@@ -259,7 +281,7 @@ __device__ __forceinline__ bool gemv_list(const RowSeg* segs, int nseg, const fl
   constexpr int RPW = 64 / LPR;
   constexpr int SBK = (K + 127) / 128;
   constexpr size_t RS = (size_t)K * (FP8 ? 1 : 2);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = tid_opaque() & 63, wave = tid_opaque() >> 6;
   const int li = lane % LPR, rsub = lane / LPR;
   int nrows = 0;
   for (int s = 0; s < nseg; s++) nrows += segs[s].n;

@@ -40,15 +40,16 @@
 namespace pld {
 
 // ------------------------------------------------------------------ shared structs
-enum Stage { S_QKV = 0, S_H2 = 1, S_RT = 2, S_M = 3, S_OUT = 4, S_ATT = 5, NSTG = 8 };
+// Watchdog wait ids (pld_device_status.stage): which LL activation a workgroup waited for.
+enum WaitId { W_X = 0, W_QKV = 1, W_KV = 2, W_PART = 3, W_O = 4, W_H2 = 5, W_RT = 6, W_M = 7 };
 enum { ST_CODE = 0, ST_STAGE = 1, ST_LAYER = 2, ST_TOKEN = 3, ST_WG = 4, ST_ABORT = 8 };
 // device trace: wall-clock stamps per (step, workgroup)
 enum TraceSlot {
   TR_START = 0, TR_X_READY, TR_QKV_DONE, TR_ATT_READY, TR_ATT_DONE, TR_O_READY, TR_WO_DONE, TR_H2_READY,
   TR_RT_READY, TR_FFN_DONE, TR_M_READY, TR_DOWN_DONE, TR_ATT_Q = 12, TR_ATT_SOFTMAX = 13, TR_ATT_PARTIAL = 14,
   TR_ATT_MERGED = 15, TR_TOPK = 16, TR_ROUTED_GEMV = 17, TR_M_STORED = 18, TR_DOWN_GEMV = 19, TR_DOWN_EPI = 20,
-  TR_QKV_GEMV = 21, TR_SHARED_GEMV = 22, TR_X_COPIED = 23, TR_X_NORMED = 24, TR_MERGE_FLAG = 25,
-  TR_MERGE_COPIED = 26, TR_RT_LOGIT = 27, TR_O_COPIED = 28, TR_M_COPIED = 29, TR_ATT_SCORES = 30, TR_SLOTS = 32
+  TR_QKV_GEMV = 21, TR_SHARED_GEMV = 22, TR_ATT_PV = 23, TR_X_NORMED = 24, TR_MERGE_START = 25,
+  TR_MERGE_COPIED = 26, TR_RT_LOGIT = 27, TR_ATT_DRAINED = 28, TR_ATT_SCORES = 30, TR_SLOTS = 32
 };
 
 struct KCfg {
@@ -75,9 +76,10 @@ struct DLayer {
   float* iscales;
 };
 
+// Workspace layout. The LL buffers (8-byte words: payload | epoch << 32) follow the
+// status words; both are zeroed at init and by decode_reset.
 struct WsOff {
-  size_t ctr_xcd, ctr_glob, ctr_grp, ctr_att, status, xbuf, q, part, o, h2, logits, sel, gates, m, a_dbg,
-      b_dbg, rope, layers, total;
+  size_t status, x, q, kv, part, o, h2, logits, m, ll_end, sel, gates, a_dbg, b_dbg, rope, layers, total;
 };
 
 struct KArgs {
@@ -97,7 +99,7 @@ struct KArgs {
 struct Ctx {
   long long budget;   // watchdog budget of one wait, in wall-clock ticks
   int w, nwg;
-  uint32_t *ctr_xcd, *ctr_glob, *ctr_grp, *ctr_att, *status;
+  uint32_t* status;
   int layer, token;
 };
 
@@ -107,11 +109,11 @@ __device__ __forceinline__ T* wsp(const KArgs& a, size_t off) {
 }
 
 // Cold path: record the first expired wait and raise the abort flag.
-__device__ __noinline__ void raise_timeout(uint32_t* status, int stage, int layer, int token, int w) {
+__device__ __noinline__ void raise_timeout(uint32_t* status, int wait_id, int layer, int token, int w) {
   uint32_t expected = 0;
   if (__hip_atomic_compare_exchange_strong(gp(status + ST_CODE), &expected, (uint32_t)(int32_t)PLD_E_DEVICE_TIMEOUT,
                                            __ATOMIC_RELAXED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-    st_u32(status + ST_STAGE, (uint32_t)stage);
+    st_u32(status + ST_STAGE, (uint32_t)wait_id);
     st_u32(status + ST_LAYER, (uint32_t)layer);
     st_u32(status + ST_TOKEN, (uint32_t)token);
     st_u32(status + ST_WG, (uint32_t)w);
@@ -119,60 +121,102 @@ __device__ __noinline__ void raise_timeout(uint32_t* status, int stage, int laye
   st_u32(status + ST_ABORT, 1u);
 }
 
-// Thread 0 spins (bounded) until *ctr reaches target; every thread gets the verdict.
-__device__ __forceinline__ bool spin_until(Ctx& cx, const uint32_t* ctr, uint32_t target, int stage) {
+// ------------------------------------------------------------------ LL handoff
+// Every activation that crosses workgroups travels as LL words: one 8-byte atomic store
+// carries a 32-bit payload in its low half and the epoch (step number + 1) in its high
+// half, so a consumer that reads a word with the expected epoch has the payload too.
+// There are no counters, no store drains and no atomics on the critical path: the
+// producer stores and moves on; the consumer loads the words it needs and re-reads only
+// those not yet published. Each LL buffer is written once per step, and every buffer's
+// next write happens only after all its readers have moved past it (each consumer set
+// depends on all producers of the following stage), so one buffer per activation is
+// enough and a word can only hold the current epoch or an older one.
+__device__ __forceinline__ uint64_t ll_word(uint32_t v, uint32_t ep) { return ((uint64_t)ep << 32) | v; }
+__device__ __forceinline__ void ll_put(uint64_t* p, uint32_t v, uint32_t ep) { st_u64(p, ll_word(v, ep)); }
+__device__ __forceinline__ void ll_put_f32(uint64_t* p, float v, uint32_t ep) { ll_put(p, __float_as_uint(v), ep); }
+
+struct IdxLinear {
+  __device__ __forceinline__ int operator()(int i) const { return i; }
+};
+
+// Reads the LL words src[idx(i)], i in [0, n), of epoch ep into dst[i] (LDS). PER loads
+// per thread are issued together; words that are not yet published are re-read in a
+// bounded loop (watchdog wait id wid). Every thread of the block must call; returns
+// false (in every thread) on expiry or when another workgroup raised the abort flag.
+template <int PER, typename Idx = IdxLinear>
+__device__ __forceinline__ bool ll_fetch(Ctx& cx, uint32_t* dst, const uint64_t* src, int n, uint32_t ep, int wid,
+                                         Idx idx = Idx{}) {
   int failed = 0;
-  if (threadIdx.x == 0 && (int)(ld_u32(ctr) - target) < 0) {
-    const long long deadline = wall_clock64() + cx.budget;
-    int n = 0;
-    while ((int)(ld_u32(ctr) - target) < 0) {
-      if ((++n & 15) == 0) {
-        if (ld_u32(cx.status + ST_ABORT)) { failed = 1; break; }
-        if (wall_clock64() > deadline) { raise_timeout(cx.status, stage, cx.layer, cx.token, cx.w); failed = 1; break; }
+  const int tid = tid_opaque();
+  for (int base = 0; base < n; base += BLOCK * PER) {
+    uint64_t v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; j++) {
+      const int i = base + j * BLOCK + tid;
+      v[j] = i < n ? ld_u64_off(src, (uint32_t)idx(i) * 8u) : ll_word(0u, ep);
+    }
+    uint32_t pend = 0;
+#pragma unroll
+    for (int j = 0; j < PER; j++) pend |= (uint32_t)((uint32_t)(v[j] >> 32) != ep) << j;
+    if (pend && !failed) {
+      const long long deadline = wall_clock64() + cx.budget;
+      int it = 0;
+      while (pend) {
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int j = 0; j < PER; j++)
+          if (pend >> j & 1u) v[j] = ld_u64_off(src, (uint32_t)idx(base + j * BLOCK + tid) * 8u);
+#pragma unroll
+        for (int j = 0; j < PER; j++)
+          if ((uint32_t)(v[j] >> 32) == ep) pend &= ~(1u << j);
+        if ((++it & 15) == 0 && pend) {
+          if (ld_u32(cx.status + ST_ABORT)) { failed = 1; break; }
+          if (wall_clock64() > deadline) { raise_timeout(cx.status, wid, cx.layer, cx.token, cx.w); failed = 1; break; }
+        }
       }
-      __builtin_amdgcn_s_sleep(1);
+    }
+#pragma unroll
+    for (int j = 0; j < PER; j++) {
+      const int i = base + j * BLOCK + tid;
+      if (i < n) dst[i] = (uint32_t)v[j];
     }
   }
   return !__syncthreads_or(failed);
 }
-
-// Publish: every wave waits for its write-through stores, then one thread counts this
-// workgroup in its XCD group; the group's last arriver counts the group globally.
-// Participants are workgroups [0, n_part).
-__device__ __forceinline__ void arrive(Ctx& cx, int stage, uint32_t k1, int n_part) {
-  vm_wait();
-  __syncthreads();
-  if (threadIdx.x == 0 && cx.w < n_part) {
-    const int x = cx.w & (NXCD - 1);
-    const uint32_t per = (uint32_t)((n_part - x + NXCD - 1) / NXCD);
-    const uint32_t old = atomic_add_u32(cx.ctr_xcd + (stage * NXCD + x) * CTR_STRIDE, 1u);
-    if (old + 1u == k1 * per) atomic_add_u32(cx.ctr_glob + stage * CTR_STRIDE, 1u);
-  }
-}
-__device__ __forceinline__ bool wait_all(Ctx& cx, int stage, uint32_t k1, int n_part) {
-  const uint32_t groups = (uint32_t)min(NXCD, n_part);
-  return spin_until(cx, cx.ctr_glob + stage * CTR_STRIDE, k1 * groups, stage);
-}
+constexpr int per_for(int n) { return n <= BLOCK ? 1 : (n + BLOCK - 1) / BLOCK > 16 ? 16 : (n + BLOCK - 1) / BLOCK; }
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// In-place RMSNorm of act[0..n): act = fp32((act * r) * gamma), r = 1/sqrt(sum(act^2)/n + eps)
-// with the statistics in fp64 (bf16 and fp32 squares are exact in fp64).
-__device__ __forceinline__ void rmsnorm_inplace(float* act, const float* __restrict__ gamma, int n, double eps,
-                                                double* red) {
-  double ss = 0.0;
-  for (int i = threadIdx.x; i < n; i += BLOCK) ss += (double)act[i] * (double)act[i];
-  ss = block_sum(ss, red);
-  const double r = 1.0 / sqrt(ss / (double)n + eps);
-  const PLD_GLOBAL float* g = gp(gamma);
-  for (int i = threadIdx.x; i < n; i += BLOCK) act[i] = (float)(((double)act[i] * r) * (double)g[i]);
-  __syncthreads();
+// e^x in fp64 for the router (a handful of threads per step): x = k ln2 + r with ln2
+// split into a head with trailing zero bits and a tail (k ln2_hi is exact), |r| <= ln2/2,
+// e^r by its Taylor series to degree 13 in Horner form (truncation < 1e-17 relative),
+// then scaled by 2^k. The constants are read from LDS (dk, written at kernel start):
+// literal fp64 constants would be hoisted out of the layer loop into registers that
+// stay live, and spill, across every stage.
+constexpr int EXP_TERMS = 13;
+__device__ __forceinline__ void exp_f64_init(double* dk) {
+  if (tid_opaque() == 0) {
+    dk[0] = 1.4426950408889634;         // 1/ln2
+    dk[1] = 6.93147180369123816490e-01; // ln2 head
+    dk[2] = 1.90821492927058770002e-10; // ln2 tail
+    for (int n = 1; n <= EXP_TERMS; n++) dk[2 + n] = 1.0 / (double)n;
+  }
+}
+__device__ __forceinline__ double exp_f64(double x, const double* dk) {
+  if (x > 709.0) return INFINITY;
+  if (x < -745.0) return 0.0;
+  const double k = rint(x * dk[0]);
+  double r = fma(-k, dk[1], x);
+  r = fma(-k, dk[2], r);
+  double p = 1.0;
+  for (int n = EXP_TERMS; n >= 1; n--) p = fma(p, r * dk[2 + n], 1.0);
+  return ldexp(p, (int)k);
 }
 
-// This thread's elements i = threadIdx.x + k*BLOCK of a length-N fp32 vector, held in
+// This thread's elements i = tid_opaque() + k*BLOCK of a length-N fp32 vector, held in
 // registers. Small static vectors (norm weights) are loaded this way BEFORE a stage's
 // weight prefetch is issued, so they sit at the front of the wave's in-order load queue
-// instead of behind ~tens of KB of weight loads.
+// instead of behind the weight loads.
 template <int N>
 struct RegVec {
   static constexpr int K = (N + BLOCK - 1) / BLOCK;
@@ -181,34 +225,35 @@ struct RegVec {
     const PLD_GLOBAL float* g = gp(p);
 #pragma unroll
     for (int k = 0; k < K; k++) {
-      const int i = threadIdx.x + k * BLOCK;
+      const int i = tid_opaque() + k * BLOCK;
       v[k] = i < N ? g[i] : 0.f;
     }
   }
 };
-// rmsnorm_inplace with the weights in registers (same arithmetic, same summation order)
+// In-place RMSNorm of act[0..N): act = fp32((act * r) * gamma), r = 1/sqrt(sum(act^2)/N + eps),
+// statistics in fp64 (bf16 and fp32 squares are exact in fp64); gamma in registers.
 template <int N>
 __device__ __forceinline__ void rmsnorm_reg(float* act, const RegVec<N>& gam, double eps, double* red) {
   double ss = 0.0;
 #pragma unroll
   for (int k = 0; k < RegVec<N>::K; k++) {
-    const int i = threadIdx.x + k * BLOCK;
+    const int i = tid_opaque() + k * BLOCK;
     if (i < N) ss += (double)act[i] * (double)act[i];
   }
   ss = block_sum(ss, red);
   const double r = 1.0 / sqrt(ss / (double)N + eps);
 #pragma unroll
   for (int k = 0; k < RegVec<N>::K; k++) {
-    const int i = threadIdx.x + k * BLOCK;
+    const int i = tid_opaque() + k * BLOCK;
     if (i < N) act[i] = (float)(((double)act[i] * r) * (double)gam.v[k]);
   }
   __syncthreads();
 }
 
 // Weight loads in flight per lane for each GEMV stage (16-byte loads). Deep prefetch
-// keeps HBM busy, but every load queued ahead of a latency-critical access (a counter
-// poll, an activation copy) delays it: the queue drains at the lane's share of HBM
-// bandwidth. The depths below were chosen by measurement.
+// keeps HBM busy, but every load queued ahead of a latency-critical access in the same
+// wave (an LL read of an activation) delays it, because a wave's loads return in order
+// and the queue drains at the lane's share of HBM bandwidth. Chosen by measurement.
 #ifndef PLD_IF_QKV
 #define PLD_IF_QKV 8
 #endif
@@ -231,12 +276,14 @@ struct Lds {
   uint32_t* stage;   // [stage_words]  raw bf16-pair words of the incoming hidden state
   float* outb;       // [outb_floats]  GEMV row results
   float* outc;       // [outb_floats]
-  float* xres;       // [outb_floats]  this workgroup's rows of the layer input (for the residual)
+  float* xres;       // [outb_floats]  this workgroup's rows of the layer input (residual of W_o)
+  float* h2res;      // [outb_floats]  this workgroup's rows of h2 (residual of the FFN)
   double* red;       // [16]
   int* isel;         // [32]
   float* fgate;      // [32]
-  int* flag;         // [8]
   RowSeg* segs;      // [MAX_SEGS] GEMV segment list of the current stage
+  uint64_t* tr;      // [TR_SLOTS] trace stamps of the current step (flushed at its end)
+  double* dk;        // [16] fp64 constants of exp_f64 (kept in LDS, see there)
 };
 __device__ __forceinline__ Lds carve(float* base, const KCfg& c) {
   Lds L;
@@ -245,23 +292,25 @@ __device__ __forceinline__ Lds carve(float* base, const KCfg& c) {
   L.outb = reinterpret_cast<float*>(L.stage + c.stage_words);
   L.outc = L.outb + c.outb_floats;
   L.xres = L.outc + c.outb_floats;
-  L.red = reinterpret_cast<double*>(L.xres + c.outb_floats);
+  L.h2res = L.xres + c.outb_floats;
+  L.red = reinterpret_cast<double*>(L.h2res + c.outb_floats);
   L.isel = reinterpret_cast<int*>(L.red + 16);
   L.fgate = reinterpret_cast<float*>(L.isel + 32);
-  L.flag = reinterpret_cast<int*>(L.fgate + 32);
-  L.segs = reinterpret_cast<RowSeg*>(L.flag + 8);
+  L.segs = reinterpret_cast<RowSeg*>(L.fgate + 32);
+  L.tr = reinterpret_cast<uint64_t*>(L.segs + MAX_SEGS);
+  L.dk = reinterpret_cast<double*>(L.tr + TR_SLOTS);
   return L;
 }
 __host__ __device__ inline size_t lds_bytes_for(int act_floats, int stage_words, int outb_floats) {
-  return (size_t)4 * (act_floats + stage_words + 3 * outb_floats) + 8 * 16 + 4 * 32 + 4 * 32 + 4 * 8 +
-         sizeof(RowSeg) * MAX_SEGS;
+  return (size_t)4 * (act_floats + stage_words + 4 * outb_floats) + 8 * 16 + 4 * 32 + 4 * 32 +
+         sizeof(RowSeg) * MAX_SEGS + 8 * TR_SLOTS + 8 * 16;
 }
 
 // Publishes a segment list to the workgroup (the previous list must be out of use).
 __device__ __forceinline__ void seg_begin() { __syncthreads(); }
 __device__ __forceinline__ void seg_set(Lds& L, int i, const uint8_t* w, const float* sc, int n, int srow, int act_off,
                                         float alpha) {
-  if (threadIdx.x == 0) {
+  if (tid_opaque() == 0) {
     RowSeg& S = L.segs[i];
     S.w = w; S.s = sc; S.n = n; S.srow = srow; S.act_off = act_off; S.alpha = alpha;
   }
@@ -286,15 +335,27 @@ struct GqaShape {
 struct Step {
   const DLayer* Ly;
   const uint16_t* in_hidden;   // caller's bf16 input for the first step of the launch, else null
-  uint32_t k1;                 // step number + 1 (counter epoch)
+  uint32_t k1;                 // step number + 1 (LL epoch of this step)
   bool first;                  // first step of the launch
   int pos;
   int idx;                     // step index within the launch (trace row)
+  uint64_t* tr;                // LDS stamps of this step (thread 0)
 };
 
+// Device trace: thread 0 keeps the step's stamps in LDS (a global store here would be
+// waited for by the next in-order load wait of wave 0 and distort what it measures);
+// trace_flush writes them out once per step.
 __device__ __forceinline__ void stamp(const KArgs& a, const Ctx& cx, const Step& st, int slot) {
-  if (a.trace && st.idx < a.trace_steps && threadIdx.x == 0)
-    gp(a.trace)[((size_t)st.idx * cx.nwg + cx.w) * TR_SLOTS + slot] = wall_clock64();
+  if (a.trace && st.idx < a.trace_steps && tid_opaque() == 0) st.tr[slot] = wall_clock64();
+}
+__device__ __forceinline__ void trace_flush(const KArgs& a, const Ctx& cx, const Step& st) {
+  if (a.trace && st.idx < a.trace_steps && tid_opaque() == 0) {
+    PLD_GLOBAL uint64_t* dst = gp(a.trace) + ((size_t)st.idx * cx.nwg + cx.w) * TR_SLOTS;
+    for (int i = 0; i < TR_SLOTS; i++) {
+      dst[i] = st.tr[i];
+      st.tr[i] = 0;
+    }
+  }
 }
 
 // Rows [r0, r1) of an H-row stage for this workgroup, split in pairs (the hidden state
@@ -311,6 +372,7 @@ __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Ste
   const DLayer Ly = *gp(st.Ly);
   constexpr int HD = SH::HD;
   const int w = cx.w, nwg = cx.nwg, pos = st.pos;
+  const uint32_t k1 = st.k1;
   constexpr int qR = SH::NH * HD, kR = SH::NKV * HD, R = qR + 2 * kR;
   constexpr int P = R / 2;
   const int r0 = 2 * split_at(P, nwg, w), r1 = 2 * split_at(P, nwg, w + 1);
@@ -318,32 +380,31 @@ __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Ste
   hrows(SH::H, nwg, w, &h0, &h1);
   RegVec<SH::H> gam;
   gam.load(Ly.attn_norm);
-  bool pending = true;   // the input wait + RMSNorm has not run yet
+  bool pending = true;   // the input read + RMSNorm has not run yet
   auto pre_x = [&]() -> bool {
     if (!pending) return true;
     pending = false;
-    if (!st.first && !wait_all(cx, S_OUT, st.k1 - 1, nwg)) return false;
-    stamp(a, cx, st, TR_X_READY);
-    // stage the bf16 pairs of x, keep this workgroup's residual rows, expand to fp32
+    // the layer input: the caller's bf16 vector (first step of the launch) or the previous
+    // step's output, LL words of bf16 pairs published with the previous step's epoch
     if (st.first) {
       const PLD_GLOBAL uint32_t* src = gp(reinterpret_cast<const uint32_t*>(st.in_hidden));
-      for (int i = threadIdx.x; i < SH::H / 2; i += BLOCK) L.stage[i] = src[i];
-    } else {
-      coh_copy_to_lds(L.stage, wsp<uint32_t>(a, a.off.xbuf), SH::H / 2);
+      for (int i = tid_opaque(); i < SH::H / 2; i += BLOCK) L.stage[i] = src[i];
+      __syncthreads();
+    } else if (!ll_fetch<per_for(SH::H / 2)>(cx, L.stage, wsp<uint64_t>(a, a.off.x), SH::H / 2, k1 - 1u, W_X)) {
+      return false;
     }
-    __syncthreads();
-    stamp(a, cx, st, TR_X_COPIED);
-    for (int i = threadIdx.x; i < SH::H / 2; i += BLOCK) {
+    stamp(a, cx, st, TR_X_READY);
+    for (int i = tid_opaque(); i < SH::H / 2; i += BLOCK) {
       const uint32_t v = L.stage[i];
       L.act[2 * i] = bf_lo(v);
       L.act[2 * i + 1] = bf_hi(v);
     }
     __syncthreads();
-    for (int r = h0 + threadIdx.x; r < h1; r += BLOCK) L.xres[r - h0] = L.act[r];
+    for (int r = h0 + tid_opaque(); r < h1; r += BLOCK) L.xres[r - h0] = L.act[r];
     rmsnorm_reg<SH::H>(L.act, gam, c.eps, L.red);
     stamp(a, cx, st, TR_X_NORMED);
     if (w == 0)
-      for (int i = threadIdx.x; i < SH::H; i += BLOCK) st_f32(wsp<float>(a, a.off.a_dbg) + i, L.act[i]);
+      for (int i = tid_opaque(); i < SH::H; i += BLOCK) st_f32(wsp<float>(a, a.off.a_dbg) + i, L.act[i]);
     return true;
   };
   {
@@ -367,9 +428,12 @@ __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Ste
   stamp(a, cx, st, TR_QKV_GEMV);
   if (!pre_x()) return false;
   __syncthreads();
+  // RoPE on q and k; q -> LL (fp32); k, v -> cache row (bf16) and LL (bf16 pairs) for
+  // this step's attention
   const PLD_GLOBAL float* rope = gp(wsp<float>(a, a.off.rope)) + (size_t)pos * HD;   // (cos, sin) pairs
-  float* qw = wsp<float>(a, a.off.q);
-  for (int p = r0 / 2 + threadIdx.x; p < r1 / 2; p += BLOCK) {
+  uint64_t* qll = wsp<uint64_t>(a, a.off.q);
+  uint64_t* kvll = wsp<uint64_t>(a, a.off.kv);   // [k: NKV*HD/2 | v: NKV*HD/2] bf16-pair words
+  for (int p = r0 / 2 + tid_opaque(); p < r1 / 2; p += BLOCK) {
     const int r = 2 * p;
     float v0 = L.outb[r - r0], v1 = L.outb[r + 1 - r0];
     if (r < qR + kR) {
@@ -380,30 +444,33 @@ __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Ste
       v1 = x1;
     }
     if (r < qR) {
-      st_u64(reinterpret_cast<uint64_t*>(qw + r), (uint64_t)__float_as_uint(v0) | ((uint64_t)__float_as_uint(v1) << 32));
+      ll_put_f32(qll + r, v0, k1);
+      ll_put_f32(qll + r + 1, v1, k1);
     } else {
       const bool isk = r < qR + kR;
       const int rr = isk ? r - qR : r - qR - kR;
       const int head = rr / HD, d = rr % HD;
+      const uint32_t pair = f32_to_bf16(v0) | (f32_to_bf16(v1) << 16);
       uint16_t* dst = (isk ? Ly.kc : Ly.vc) + ((size_t)head * c.max_seq + pos) * HD + d;
-      st_u32(reinterpret_cast<uint32_t*>(dst), f32_to_bf16(v0) | (f32_to_bf16(v1) << 16));
+      st_u32(reinterpret_cast<uint32_t*>(dst), pair);
+      ll_put(kvll + (isk ? 0 : kR / 2) + rr / 2, pair, k1);
     }
   }
-  arrive(cx, S_QKV, st.k1, nwg);
   stamp(a, cx, st, TR_QKV_DONE);
   return true;
 }
 
 // ------------------------------------------------------------------ attention (GQA)
 // One workgroup = one (kv head g, token chunk) pair. Scores for the G query heads of
-// the group, chunk-local softmax, P.V, then a partial (m, l, acc[HD]) per head. The
-// group's last arriver merges the partials into o.
+// the group, chunk-local softmax, P.V, then a partial (m, l, acc[HD]) per head; then
+// each workgroup of the group merges its own slice of the group's outputs.
 //  * scores: 16-byte K loads, HD/8 lanes per token row, ATT_NB row passes held in
 //    registers; the per-token dot is reduced with DPP moves inside each 16-lane row;
 //  * P.V: each wave owns a contiguous token range and each lane HD/64 dims, so the sum
 //    over tokens needs no lane exchange, only one cross-wave pass through LDS;
-//  * the static history rows of the first batch (K and V) are issued before the wait
-//    for this step's q/k/v; rows written in this launch are read coherently after it.
+//  * the static history rows of the first batch (K and V) are issued before q is read;
+//    the row of this step comes from the LL words of the QKV stage, and rows written by
+//    earlier steps of this launch are read with coherent loads.
 template <class SH>
 __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Step& st, Lds& L) {
   const KCfg& c = a.c;
@@ -415,35 +482,56 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
   constexpr int PASS = NWAVES * TPW;   // tokens per workgroup pass
   constexpr int DPL = HD / 64;         // dims per lane in the P.V pass
   static_assert(DPL == 1 || DPL == 2, "head dim 64 or 128");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave index as a provably uniform value: per-wave bounds then branch on scalars
+  const int lane = tid_opaque() & 63, wave = __builtin_amdgcn_readfirstlane(tid_opaque() >> 6);
   const int dl = lane % LPT, tl = lane / LPT;
   const int cpg = c.cpg;
   const int g = cx.w / cpg, ch = cx.w % cpg;
-  if (g < SH::NKV) {   // workgroups past the last group only take part in the final arrive
-  const int T = st.pos + 1;
+  if (g >= SH::NKV) return true;   // workgroups past the last group have no attention work
+  const int pos = st.pos;
+  const int T = pos + 1;
   const int t0 = split_at(T, cpg, ch), t1 = split_at(T, cpg, ch + 1), n = t1 - t0;
   const int tw = (n + NWAVES - 1) / NWAVES;             // P.V tokens per wave
   const int pv0 = min(n, wave * tw), pv1 = min(n, pv0 + tw);
   const uint16_t* kbase = Ly.kc + (size_t)g * c.max_seq * HD + dl * 8;
   const uint16_t* vbase = Ly.vc + (size_t)g * c.max_seq * HD + lane * DPL;
-  const int fresh = a.pos0;   // rows >= fresh were written inside this launch: coherent loads only
+  const int fresh = a.pos0;   // rows >= fresh were written inside this launch
+  // LDS: q of the group [G][HD], the new k and v rows [HD/2 + HD/2 words], scores, ...
+  float* qs = L.act;
+  uint32_t* kvn = reinterpret_cast<uint32_t*>(L.act + G * HD);
+  float* sc = L.act + G * HD + HD;                 // [G][chmax]
+  float* red2 = sc + G * c.chmax;                  // [NWAVES][G][HD]
+  float* ml = red2 + NWAVES * G * HD;              // [2G]
+  // Rows [0, nst) of the chunk are static history (written before this launch) and are
+  // streamed with plain loads; rows [nst, n) were written inside this launch (row pos by
+  // this step) and are handled by a separate short pass. Static loads are unconditional:
+  // an index past the static rows is clamped to the last one (its result is unused), so
+  // no load sits under a condition and the in-order load waits stay exact.
+  const int nst = max(0, min(n, fresh - t0));
+  auto srow = [&](int t) -> size_t { return (size_t)(nst > 0 ? t0 + min(t, nst - 1) : 0); };
   auto tok = [&](int tb0, int b) { return tb0 + b * PASS + wave * TPW + tl; };
-  auto k_static = [&](int t) -> uint4 {
-    return (t < n && t0 + t < fresh) ? ld_g16(kbase + (size_t)(t0 + t) * HD) : make_uint4(0u, 0u, 0u, 0u);
+  auto k_static = [&](int t) -> uint4 { return ld_g16(kbase + srow(t) * HD); };
+  // V element(s) of this lane for token t (DPL bf16 values packed in a word)
+  auto v_static = [&](int t) -> uint32_t {
+    const uint16_t* p = vbase + srow(t) * HD;
+    if constexpr (DPL == 2) return *(const PLD_GLOBAL uint32_t*)(p);
+    else return (uint32_t)(*(const PLD_GLOBAL uint16_t*)(p));
   };
+  // fresh rows: row pos from the LL copy in LDS, earlier rows of this launch coherently
   auto k_fresh = [&](int t) -> uint4 {
+    if (t0 + t == pos) {
+      const uint32_t* q = kvn + dl * 4;
+      return make_uint4(q[0], q[1], q[2], q[3]);
+    }
     const uint64_t* q = reinterpret_cast<const uint64_t*>(kbase + (size_t)(t0 + t) * HD);
     const uint64_t x = ld_u64(q), y = ld_u64(q + 1);
     return make_uint4((uint32_t)x, (uint32_t)(x >> 32), (uint32_t)y, (uint32_t)(y >> 32));
   };
-  // V element(s) of this lane for token t (DPL bf16 values packed in a word)
-  auto v_static = [&](int t) -> uint32_t {
-    if (t >= pv1 || t0 + t >= fresh) return 0u;
-    const uint16_t* p = vbase + (size_t)(t0 + t) * HD;
-    if constexpr (DPL == 2) return *(const PLD_GLOBAL uint32_t*)(p);
-    else return (uint32_t)(*(const PLD_GLOBAL uint16_t*)(p));
-  };
   auto v_fresh = [&](int t) -> uint32_t {
+    if (t0 + t == pos) {
+      if constexpr (DPL == 2) return kvn[HD / 2 + lane];
+      else return (kvn[HD / 2 + lane / 2] >> (16 * (lane & 1))) & 0xffffu;
+    }
     const uint16_t* p = vbase + (size_t)(t0 + t) * HD;
     if constexpr (DPL == 2) return ld_u32(reinterpret_cast<const uint32_t*>(p));
     else {
@@ -451,53 +539,56 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
       return (lane & 1) ? (w2 >> 16) : (w2 & 0xffffu);
     }
   };
+  const int pvs = min(pv1, max(pv0, nst));   // this wave's static P.V rows are [pv0, pvs)
   uint4 kb[NB];
   uint32_t vb[NV];
 #pragma unroll
   for (int b = 0; b < NB; b++) kb[b] = k_static(tok(0, b));
 #pragma unroll
   for (int b = 0; b < NV; b++) vb[b] = v_static(pv0 + b);
-  if (!wait_all(cx, S_QKV, k1, cx.nwg)) return false;
+  // q of the group, and the new k/v row for the chunk that holds position pos
+  if (!ll_fetch<per_for(G * HD)>(cx, reinterpret_cast<uint32_t*>(qs), wsp<uint64_t>(a, a.off.q) + (size_t)g * G * HD,
+                                 G * HD, k1, W_QKV))
+    return false;
+  if (t0 <= pos && pos < t1) {
+    constexpr int kR2 = SH::NKV * HD / 2;
+    auto kv_idx = [g](int i) { return i < HD / 2 ? g * (HD / 2) + i : kR2 + g * (HD / 2) + (i - HD / 2); };
+    if (!ll_fetch<1>(cx, kvn, wsp<uint64_t>(a, a.off.kv), HD, k1, W_KV, kv_idx)) return false;
+  }
   stamp(a, cx, st, TR_ATT_READY);
-
-  const uint64_t* qg = reinterpret_cast<const uint64_t*>(wsp<float>(a, a.off.q) + (size_t)g * G * HD + dl * 8);
   const float scale = 1.0f / sqrtf((float)HD);
   float qr[G][8];
 #pragma unroll
   for (int h = 0; h < G; h++)
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-      const uint64_t v = ld_u64(qg + h * HD / 2 + j);
-      qr[h][2 * j] = __uint_as_float((uint32_t)v) * scale;
-      qr[h][2 * j + 1] = __uint_as_float((uint32_t)(v >> 32)) * scale;
-    }
+    for (int j = 0; j < 8; j++) qr[h][j] = qs[h * HD + dl * 8 + j] * scale;
   stamp(a, cx, st, TR_ATT_Q);
-  float* sc = L.act;                               // [G][chmax]
-  float* red2 = L.act + G * c.chmax;               // [NWAVES][G][HD]
-  float* ml = red2 + NWAVES * G * HD;              // [2G]
-  // ---- pass 1: scores
-  for (int tb0 = 0; tb0 < n; tb0 += NB * PASS) {
+  auto score = [&](int t, const uint4& kv, int lim) {
+    const float kf[8] = {bf_lo(kv.x), bf_hi(kv.x), bf_lo(kv.y), bf_hi(kv.y),
+                         bf_lo(kv.z), bf_hi(kv.z), bf_lo(kv.w), bf_hi(kv.w)};
 #pragma unroll
-    for (int b = 0; b < NB; b++) {
-      const int t = tok(tb0, b);
-      if (tb0 > 0) kb[b] = k_static(t);
-      if (t < n && t0 + t >= fresh) kb[b] = k_fresh(t);
+    for (int h = 0; h < G; h++) {
+      float sh = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; j++) sh = fmaf(qr[h][j], kf[j], sh);
+      sh = dpp_sum<LPT>(sh);
+      if (dl == LPT - 1 && t < lim) sc[h * c.chmax + t] = sh;
     }
+  };
+  // ---- pass 1: scores of the static rows (next batch issued as each register frees up)
+  // (no per-row branches: rows past nst are computed on clamped data and not stored)
+  for (int tb0 = 0; tb0 < nst; tb0 += NB * PASS) {
 #pragma unroll
-    for (int b = 0; b < NB; b++) {
-      const int t = tok(tb0, b);
-      const uint4 kv = kb[b];
-      const float kf[8] = {bf_lo(kv.x), bf_hi(kv.x), bf_lo(kv.y), bf_hi(kv.y),
-                           bf_lo(kv.z), bf_hi(kv.z), bf_lo(kv.w), bf_hi(kv.w)};
+    for (int b = 0; b < NB; b++) score(tok(tb0, b), kb[b], nst);
+    if (tb0 + NB * PASS < nst) {
 #pragma unroll
-      for (int h = 0; h < G; h++) {
-        float sh = 0.f;
-#pragma unroll
-        for (int j = 0; j < 8; j++) sh = fmaf(qr[h][j], kf[j], sh);
-        sh = dpp_sum<LPT>(sh);
-        if (dl == LPT - 1 && t < n) sc[h * c.chmax + t] = sh;
-      }
+      for (int b = 0; b < NB; b++) kb[b] = k_static(tok(tb0 + NB * PASS, b));
     }
+  }
+  // ---- scores of the fresh rows
+  for (int t = nst + wave * TPW + tl; t - tl < n; t += PASS) {
+    const uint4 kv = t < n ? k_fresh(t) : make_uint4(0u, 0u, 0u, 0u);
+    score(t, kv, n);
   }
   stamp(a, cx, st, TR_ATT_SCORES);
   __syncthreads();
@@ -522,99 +613,110 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
   for (int h = 0; h < G; h++)
 #pragma unroll
     for (int e = 0; e < DPL; e++) acc[h][e] = 0.f;
-  for (int tb = pv0; tb < pv1; tb += NV) {
+  // p of row t, or 0 past `lim` (a select, not a branch: the reads stay in flight
+  // together; sc has slack past the last row of every head, inside the LDS carve)
+  auto pv = [&](int t, uint32_t vv, int lim) {
+    const float v0 = bf_lo(vv);
+    const float v1 = DPL == 2 ? bf_hi(vv) : 0.f;
 #pragma unroll
-    for (int b = 0; b < NV; b++) {
-      const int t = tb + b;
-      if (tb > pv0) vb[b] = v_static(t);
-      if (t < pv1 && t0 + t >= fresh) vb[b] = v_fresh(t);
+    for (int h = 0; h < G; h++) {
+      const float raw = sc[h * c.chmax + t];   // t < tb + NV: inside sc + red2 for every head
+      const float p = t < lim ? raw : 0.f;
+      acc[h][0] = fmaf(p, v0, acc[h][0]);
+      if constexpr (DPL == 2) acc[h][1] = fmaf(p, v1, acc[h][1]);
     }
+  };
+  for (int tb = pv0; tb < pvs; tb += NV) {
 #pragma unroll
     for (int b = 0; b < NV; b++) {
-      const int t = tb + b;
-      if (t < pv1) {
-        const float v0 = bf_lo(vb[b]);
-        const float v1 = DPL == 2 ? bf_hi(vb[b]) : 0.f;
+      pv(tb + b, vb[b], pvs);
+      // at most 8 rows of LDS reads in flight: bounds register pressure (no spills)
+      if ((b & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+    if (tb + NV < pvs) {
 #pragma unroll
-        for (int h = 0; h < G; h++) {
-          const float p = sc[h * c.chmax + t];
-          acc[h][0] = fmaf(p, v0, acc[h][0]);
-          if constexpr (DPL == 2) acc[h][1] = fmaf(p, v1, acc[h][1]);
-        }
-      }
+      for (int b = 0; b < NV; b++) vb[b] = v_static(tb + NV + b);
     }
   }
+  for (int t = pvs; t < pv1; t++) pv(t, v_fresh(t), pv1);
 #pragma unroll
   for (int h = 0; h < G; h++)
 #pragma unroll
     for (int e = 0; e < DPL; e++) red2[(wave * G + h) * HD + lane * DPL + e] = acc[h][e];
-  __syncthreads();
-  // partial of head h for this chunk: [m, l, acc[0..HD)] at ((g*G + h)*cpg + ch)*(HD+2)
-  float* part = wsp<float>(a, a.off.part);
-  for (int i = threadIdx.x; i < G * HD / 2; i += BLOCK) {
-    const int h = (2 * i) / HD, d = (2 * i) % HD;
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int wv = 0; wv < NWAVES; wv++) {
-      s0 += red2[(wv * G + h) * HD + d];
-      s1 += red2[(wv * G + h) * HD + d + 1];
-    }
-    st_u64(reinterpret_cast<uint64_t*>(part + ((size_t)(g * G + h) * cpg + ch) * (HD + 2) + 2 + d),
-           (uint64_t)__float_as_uint(s0) | ((uint64_t)__float_as_uint(s1) << 32));
-  }
-  if (threadIdx.x < G) {
-    const int h = threadIdx.x;
-    st_u64(reinterpret_cast<uint64_t*>(part + ((size_t)(g * G + h) * cpg + ch) * (HD + 2)),
-           (uint64_t)__float_as_uint(ml[2 * h]) | ((uint64_t)__float_as_uint(ml[2 * h + 1]) << 32));
-  }
-  // Distributed merge: once all cpg partials of the group are stored, workgroup ch of
-  // the group merges dims [d0, d1) of the group's G*HD outputs (flash-decoding rescale:
-  // o = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c over the chunks with l_c > 0).
+  stamp(a, cx, st, TR_ATT_PV);
+  // The cache rows this workgroup appended (QKV stage) must be visible before its next
+  // publication: later steps of the launch read them with coherent loads.
   vm_wait();
   __syncthreads();
+  stamp(a, cx, st, TR_ATT_DRAINED);
+  // partial of head h for this chunk: LL words [m, l, acc[0..HD)] at ((g*G + h)*cpg + ch)*(HD+2)
+  uint64_t* pll = wsp<uint64_t>(a, a.off.part);
+  for (int i = tid_opaque(); i < G * HD; i += BLOCK) {
+    const int h = i / HD, d = i % HD;
+    float s = 0.f;
+#pragma unroll
+    for (int wv = 0; wv < NWAVES; wv++) s += red2[(wv * G + h) * HD + d];
+    ll_put_f32(pll + ((size_t)(g * G + h) * cpg + ch) * (HD + 2) + 2 + d, s, k1);
+  }
+  if (tid_opaque() < 2 * G) {
+    const int h = tid_opaque() >> 1;
+    ll_put_f32(pll + ((size_t)(g * G + h) * cpg + ch) * (HD + 2) + (tid_opaque() & 1), ml[tid_opaque()], k1);
+  }
   stamp(a, cx, st, TR_ATT_PARTIAL);
-  if (threadIdx.x == 0) atomic_add_u32(cx.ctr_grp + g * CTR_STRIDE, 1u);
-  if (!spin_until(cx, cx.ctr_grp + g * CTR_STRIDE, k1 * (uint32_t)cpg, 9)) return false;
-  stamp(a, cx, st, TR_MERGE_FLAG);
+  // Distributed merge: workgroup ch of the group merges dims [d0, d1) of the group's G*HD
+  // outputs (flash-decoding rescale: o = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c
+  // over the chunks with l_c > 0), reading the cpg partials' LL words it needs.
   {
     const int d0 = split_at(G * HD, cpg, ch), d1 = split_at(G * HD, cpg, ch + 1), nd = d1 - d0;
-    const float* pg = part + (size_t)g * G * cpg * (HD + 2);
-    float* mls = L.act;              // [cpg][2] (m, l) of the head of dim d0 .. (two heads at most)
-    float* accs = L.act + 4 * cpg;   // [cpg][nd]
-    const int h0 = d0 / HD, hlast = (d1 - 1) / HD;
-    for (int i = threadIdx.x; i < cpg * nd; i += BLOCK) {
-      const int cc = i / nd, j = i % nd, d = d0 + j;
-      accs[i] = ld_f32(pg + ((size_t)(d / HD) * cpg + cc) * (HD + 2) + 2 + d % HD);
-    }
-    for (int i = threadIdx.x; i < cpg * (hlast - h0 + 1); i += BLOCK) {
-      const int hh = i / cpg, cc = i % cpg;
-      const uint64_t v = ld_u64(reinterpret_cast<const uint64_t*>(pg + ((size_t)(h0 + hh) * cpg + cc) * (HD + 2)));
-      mls[2 * i] = __uint_as_float((uint32_t)v);
-      mls[2 * i + 1] = __uint_as_float((uint32_t)(v >> 32));
+    const int h0 = d0 / HD, nh2 = nd > 0 ? (d1 - 1) / HD - h0 + 1 : 0;
+    const uint64_t* pg = pll + (size_t)g * G * cpg * (HD + 2);
+    // word i < cpg*nd: acc of (chunk i / nd, dim d0 + i % nd); then (m, l) of head h0 + hh, chunk cc
+    const int nacc = cpg * nd;
+    auto pidx = [=](int i) -> int {
+      if (i < nacc) {
+        const int cc = i / nd, d = d0 + i % nd;
+        return ((d / HD) * cpg + cc) * (HD + 2) + 2 + d % HD;
+      }
+      const int j = i - nacc, hh = j / (2 * cpg), r = j % (2 * cpg);
+      return ((h0 + hh) * cpg + (r >> 1)) * (HD + 2) + (r & 1);
+    };
+    float* accs = L.act;              // [cpg][nd]
+    float* mls = L.act + nacc;        // [nh2][cpg][2]
+    __syncthreads();                  // L.act (scores) is free again
+    stamp(a, cx, st, TR_MERGE_START);
+    if (!ll_fetch<2>(cx, reinterpret_cast<uint32_t*>(L.act), pg, nacc + 2 * cpg * nh2, k1, W_PART, pidx)) return false;
+    stamp(a, cx, st, TR_MERGE_COPIED);
+    // wave hh computes the chunk weights of head h0 + hh: f_c = e^(m_c - M) for l_c > 0
+    // (else 0) with M the max over those chunks, and Ls = sum_c f_c l_c
+    float* fw = mls + 2 * cpg * nh2;   // [nh2][cpg]
+    float* lsum = fw + cpg * nh2;      // [nh2]
+    if (wave < nh2) {
+      const float* ml2 = mls + 2 * cpg * wave;
+      float M = -INFINITY;
+      for (int cc = lane; cc < cpg; cc += 64)
+        if (ml2[2 * cc + 1] > 0.f) M = fmaxf(M, ml2[2 * cc]);
+      M = wave_max(M);
+      float ls = 0.f;
+      for (int cc = lane; cc < cpg; cc += 64) {
+        const float l = ml2[2 * cc + 1];
+        const float f = l > 0.f ? __expf(ml2[2 * cc] - M) : 0.f;
+        fw[wave * cpg + cc] = f;
+        ls += f * l;
+      }
+      ls = wave_sum(ls);
+      if (lane == 0) lsum[wave] = ls;
     }
     __syncthreads();
-    stamp(a, cx, st, TR_MERGE_COPIED);
-    float* obuf = wsp<float>(a, a.off.o) + (size_t)g * G * HD;
-    for (int j = threadIdx.x; j < nd; j += BLOCK) {
-      const int d = d0 + j;
-      const float* ml2 = mls + 2 * cpg * (d / HD - h0);
-      float M = -INFINITY;
-      for (int cc = 0; cc < cpg; cc++)
-        if (ml2[2 * cc + 1] > 0.f) M = fmaxf(M, ml2[2 * cc]);
-      float Ls = 0.f, o = 0.f;
-      for (int cc = 0; cc < cpg; cc++) {
-        const float l = ml2[2 * cc + 1];
-        if (l > 0.f) {
-          const float f = __expf(ml2[2 * cc] - M);
-          Ls += f * l;
-          o += f * accs[cc * nd + j];
-        }
-      }
-      st_f32(obuf + d, o / Ls);
+    uint64_t* oll = wsp<uint64_t>(a, a.off.o) + (size_t)g * G * HD;
+    for (int j = tid_opaque(); j < nd; j += BLOCK) {
+      const int d = d0 + j, hh = d / HD - h0;
+      const float* f = fw + hh * cpg;
+      float o = 0.f;
+#pragma unroll 8
+      for (int cc = 0; cc < cpg; cc++) o = fmaf(f[cc], accs[cc * nd + j], o);
+      ll_put_f32(oll + d, o / lsum[hh], k1);
     }
   }
-  }   // grouped workgroups
-  arrive(cx, S_ATT, k1, cx.nwg);
   stamp(a, cx, st, TR_ATT_MERGED);
   stamp(a, cx, st, TR_ATT_DONE);
   return true;
@@ -626,11 +728,10 @@ __device__ __forceinline__ bool stage_wo(Ctx& cx, const KArgs& a, const Step& st
   int r0, r1;
   hrows(SH::H, cx.nwg, cx.w, &r0, &r1);
   auto pre_o = [&]() -> bool {
-    if (!wait_all(cx, S_ATT, st.k1, cx.nwg)) return false;
+    if (!ll_fetch<per_for(SH::ODIM)>(cx, reinterpret_cast<uint32_t*>(L.act), wsp<uint64_t>(a, a.off.o), SH::ODIM,
+                                     st.k1, W_O))
+      return false;
     stamp(a, cx, st, TR_O_READY);
-    coh_copy_to_lds(reinterpret_cast<uint32_t*>(L.act), wsp<uint32_t>(a, a.off.o), SH::ODIM);
-    __syncthreads();
-    stamp(a, cx, st, TR_O_COPIED);
     return true;
   };
   {
@@ -641,19 +742,22 @@ __device__ __forceinline__ bool stage_wo(Ctx& cx, const KArgs& a, const Step& st
     if (!gemv_list<SH::FP8, SH::ODIM, PLD_IF_WO>(L.segs, r1 > r0 ? 1 : 0, L.act, L.outb, OUT_STORE, pre_o)) return false;
   }
   __syncthreads();
-  float* h2 = wsp<float>(a, a.off.h2);
-  for (int r = r0 + 2 * threadIdx.x; r < r1; r += 2 * BLOCK)
-    st_u64(reinterpret_cast<uint64_t*>(h2 + r), (uint64_t)__float_as_uint(L.xres[r - r0] + L.outb[r - r0]) |
-                                                    ((uint64_t)__float_as_uint(L.xres[r + 1 - r0] + L.outb[r + 1 - r0]) << 32));
-  arrive(cx, S_H2, st.k1, cx.nwg);
+  // h2 = x + W_o o: LL words for every consumer, and this workgroup's rows kept in LDS
+  // for the FFN residual (the down stage owns the same rows)
+  uint64_t* h2ll = wsp<uint64_t>(a, a.off.h2);
+  for (int r = r0 + tid_opaque(); r < r1; r += BLOCK) {
+    const float v = L.xres[r - r0] + L.outb[r - r0];
+    L.h2res[r - r0] = v;
+    ll_put_f32(h2ll + r, v, st.k1);
+  }
   stamp(a, cx, st, TR_WO_DONE);
   return true;
 }
 
 // ------------------------------------------------------------------ stage: FFN gate/up (+ router)
 // Gate/up rows of several (expert, slot, row range) pieces as one GEMV list, then
-// m[slot][j] = silu(gate_j . b) * (up_j . b). Each piece contributes a gate segment and
-// an up segment; results come back in list order.
+// m[slot][j] = silu(gate_j . b) * (up_j . b), published as LL words. Each piece
+// contributes a gate segment and an up segment; results come back in list order.
 struct GuPiece { int expert, slot, j0, j1; };
 template <class SH, int INFL, typename Pre>
 __device__ __forceinline__ bool gate_up_list(const KArgs& a, const Step& st, Lds& L, const GuPiece* pc, int np, Pre&& pre) {
@@ -670,12 +774,13 @@ __device__ __forceinline__ bool gate_up_list(const KArgs& a, const Step& st, Lds
   seg_end();
   if (!gemv_list<SH::FP8, SH::H, INFL>(L.segs, 2 * np, L.act, L.outb, OUT_STORE, pre)) return false;
   __syncthreads();
-  float* mbuf = wsp<float>(a, a.off.m);
+  uint64_t* mll = wsp<uint64_t>(a, a.off.m);
   int base = 0;
   for (int p = 0; p < np; p++) {
     const int n = pc[p].j1 - pc[p].j0;
-    for (int j = threadIdx.x; j < n; j += BLOCK)
-      st_f32(mbuf + (size_t)pc[p].slot * SH::INTER + pc[p].j0 + j, silu_f(L.outb[base + j]) * L.outb[base + n + j]);
+    for (int j = tid_opaque(); j < n; j += BLOCK)
+      ll_put_f32(mll + (size_t)pc[p].slot * SH::INTER + pc[p].j0 + j, silu_f(L.outb[base + j]) * L.outb[base + n + j],
+                 st.k1);
     base += 2 * n;
   }
   return true;
@@ -686,6 +791,7 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
   const KCfg& c = a.c;
   const DLayer Ly = *gp(st.Ly);
   const int w = cx.w, nwg = cx.nwg;
+  const uint32_t k1 = st.k1;
   RegVec<SH::H> gam;
   gam.load(Ly.ffn_norm);
   // router workgroups: their router row, loaded ahead of the expert weights
@@ -696,44 +802,43 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
       const uint16_t* rp0 = Ly.router + (size_t)w * SH::H;
 #pragma unroll
       for (int k = 0; k < RPT; k++) {
-        const int q = threadIdx.x + k * BLOCK;
+        const int q = tid_opaque() + k * BLOCK;
         rrow[k] = q < RCH ? ld_g16(rp0 + q * 8) : make_uint4(0u, 0u, 0u, 0u);
       }
     }
   }
   bool pending = true;
-  // wait for h2, RMSNorm it into LDS; router workgroups compute their logit (fp64)
+  // read h2, RMSNorm it into LDS; router workgroups publish their logit (fp64)
   auto pre_b = [&]() -> bool {
     if (!pending) return true;
     pending = false;
-    if (!wait_all(cx, S_H2, st.k1, nwg)) return false;
+    if (!ll_fetch<per_for(SH::H)>(cx, reinterpret_cast<uint32_t*>(L.act), wsp<uint64_t>(a, a.off.h2), SH::H, k1, W_H2))
+      return false;
     stamp(a, cx, st, TR_H2_READY);
-    coh_copy_to_lds(reinterpret_cast<uint32_t*>(L.act), wsp<uint32_t>(a, a.off.h2), SH::H);
-    __syncthreads();
     rmsnorm_reg<SH::H>(L.act, gam, c.eps, L.red);
     if (w == 0)
-      for (int i = threadIdx.x; i < SH::H; i += BLOCK) st_f32(wsp<float>(a, a.off.b_dbg) + i, L.act[i]);
+      for (int i = tid_opaque(); i < SH::H; i += BLOCK) st_f32(wsp<float>(a, a.off.b_dbg) + i, L.act[i]);
     if constexpr (SH::MOE) {
       if (w < c.E) {
         // logit of expert w (fp64 accumulation) and its selection key: the logit itself
-        // (softmax router) or sigmoid(logit) + bias (biased-score router)
+        // (softmax router) or sigmoid(logit) + bias (biased-score router); published as
+        // four LL words (logit lo, hi, key lo, hi)
         double s = 0.0;
 #pragma unroll
         for (int k = 0; k < RPT; k++) {
-          const int q = threadIdx.x + k * BLOCK;
+          const int q = tid_opaque() + k * BLOCK;
           if (q < RCH) s += dot8_bf16_f64(rrow[k], L.act + q * 8);
         }
         s = block_sum(s, L.red);
-        if (threadIdx.x == 0) {
+        if (tid_opaque() < 4) {
           const double key = c.router == PLD_ROUTER_SIGMOID_BIAS
-                                 ? (1.0 / (1.0 + exp(-s))) + (double)gp(Ly.router_bias)[w] : s;
-          double* lk = wsp<double>(a, a.off.logits) + 2 * w;
-          st_u64(reinterpret_cast<uint64_t*>(lk), (uint64_t)__double_as_longlong(s));
-          st_u64(reinterpret_cast<uint64_t*>(lk + 1), (uint64_t)__double_as_longlong(key));
+                                 ? (1.0 / (1.0 + exp_f64(-s, L.dk))) + (double)gp(Ly.router_bias)[w] : s;
+          const uint64_t bits = (uint64_t)__double_as_longlong(tid_opaque() < 2 ? s : key);
+          ll_put(wsp<uint64_t>(a, a.off.logits) + 4 * w + tid_opaque(),
+                 (uint32_t)(bits >> (32 * (tid_opaque() & 1))), k1);
         }
         stamp(a, cx, st, TR_RT_LOGIT);
       }
-      arrive(cx, S_RT, st.k1, c.E);
     }
     return true;
   };
@@ -750,15 +855,15 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
     if (!pre_b()) return false;
     stamp(a, cx, st, TR_SHARED_GEMV);
     // router top-k (every workgroup computes the same selection)
-    if (!wait_all(cx, S_RT, st.k1, c.E)) return false;
+    double* lk = reinterpret_cast<double*>(L.outb);   // [E][2] (logit, key); outb is free here
+    if (!ll_fetch<per_for(4 * 512)>(cx, reinterpret_cast<uint32_t*>(lk), wsp<uint64_t>(a, a.off.logits), 4 * c.E, k1,
+                                    W_RT))
+      return false;
     stamp(a, cx, st, TR_RT_READY);
     // top-k by rank: expert e is selected at position rank(e) = #{j : key_j > key_e or
     // (key_j == key_e and j < e)} when that rank is < topk (lowest index wins ties)
-    double* lk = reinterpret_cast<double*>(L.outb);   // [E][2] (logit, key); outb is free here
-    coh_copy_to_lds(reinterpret_cast<uint32_t*>(lk), wsp<uint32_t>(a, a.off.logits), 4 * c.E);
-    __syncthreads();
     const bool sig = c.router == PLD_ROUTER_SIGMOID_BIAS;
-    for (int e = threadIdx.x; e < c.E; e += BLOCK) {
+    for (int e = tid_opaque(); e < c.E; e += BLOCK) {
       const double ke = lk[2 * e + 1];
       int rank = 0;
       for (int j = 0; j < c.E; j++) {
@@ -771,20 +876,20 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
     stamp(a, cx, st, TR_TOPK);
     // gates: softmax over the selected logits, or sigmoid scores normalised over the selection
     double* num = reinterpret_cast<double*>(L.outc);
-    if (threadIdx.x < c.topk) {
-      const double r = lk[2 * L.isel[threadIdx.x]];
-      num[threadIdx.x] = sig ? 1.0 / (1.0 + exp(-r)) : exp(r - lk[2 * L.isel[0]]);
+    if (tid_opaque() < c.topk) {
+      const double r = lk[2 * L.isel[tid_opaque()]];
+      num[tid_opaque()] = sig ? 1.0 / (1.0 + exp_f64(-r, L.dk)) : exp_f64(r - lk[2 * L.isel[0]], L.dk);
     }
     __syncthreads();
-    if (threadIdx.x < c.topk) {
+    if (tid_opaque() < c.topk) {
       double gsum = 0.0;
       for (int j = 0; j < c.topk; j++) gsum += num[j];
-      L.fgate[threadIdx.x] = (float)(num[threadIdx.x] / gsum);
+      L.fgate[tid_opaque()] = (float)(num[tid_opaque()] / gsum);
     }
     __syncthreads();
-    if (w == 0 && threadIdx.x < c.topk) {
-      st_u32(reinterpret_cast<uint32_t*>(wsp<int>(a, a.off.sel)) + threadIdx.x, (uint32_t)L.isel[threadIdx.x]);
-      st_f32(wsp<float>(a, a.off.gates) + threadIdx.x, L.fgate[threadIdx.x]);
+    if (w == 0 && tid_opaque() < c.topk) {
+      st_u32(reinterpret_cast<uint32_t*>(wsp<int>(a, a.off.sel)) + tid_opaque(), (uint32_t)L.isel[tid_opaque()]);
+      st_f32(wsp<float>(a, a.off.gates) + tid_opaque(), L.fgate[tid_opaque()]);
     }
     // routed experts: this workgroup's share of the topk*inter (slot, row) pairs, one list
     const int tot = c.topk * SH::INTER;
@@ -798,7 +903,6 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
     if (!gate_up_list<SH, PLD_IF_ROUTED>(a, st, L, rp, nr, NoPre{})) return false;
   }
   stamp(a, cx, st, TR_M_STORED);
-  arrive(cx, S_M, st.k1, nwg);
   stamp(a, cx, st, TR_FFN_DONE);
   return true;
 }
@@ -814,11 +918,10 @@ __device__ __forceinline__ bool stage_down(Ctx& cx, const KArgs& a, const Step& 
   auto pre_m = [&]() -> bool {
     if (!pending) return true;
     pending = false;
-    if (!wait_all(cx, S_M, st.k1, cx.nwg)) return false;
+    if (!ll_fetch<per_for(SH::INTER * MAX_SEGS)>(cx, reinterpret_cast<uint32_t*>(L.act), wsp<uint64_t>(a, a.off.m),
+                                                  c.slots * SH::INTER, st.k1, W_M))
+      return false;
     stamp(a, cx, st, TR_M_READY);
-    coh_copy_to_lds(reinterpret_cast<uint32_t*>(L.act), wsp<uint32_t>(a, a.off.m), c.slots * SH::INTER);
-    __syncthreads();
-    stamp(a, cx, st, TR_M_COPIED);
     return true;
   };
   {
@@ -837,29 +940,26 @@ __device__ __forceinline__ bool stage_down(Ctx& cx, const KArgs& a, const Step& 
   }
   stamp(a, cx, st, TR_DOWN_GEMV);
   if (!pre_m()) return false;
+  stamp(a, cx, st, TR_DOWN_EPI);
   __syncthreads();
   // f_r = sum_s gate_s * down_s[r] (fixed slot order)
   {
     const int nr = r1 - r0;
-    for (int r = threadIdx.x; r < nr; r += BLOCK) {
+    for (int r = tid_opaque(); r < nr; r += BLOCK) {
       float f = 0.f;
       for (int s = 0; s < c.slots; s++) f += ((!SH::MOE || s >= c.topk) ? 1.0f : L.fgate[s]) * L.outb[s * nr + r];
       L.outc[r] = f;
     }
   }
   __syncthreads();
-  // out = h2 + f, rounded to bf16; h2 rows are this workgroup's own (same pair split)
-  const uint64_t* h2 = reinterpret_cast<const uint64_t*>(wsp<float>(a, a.off.h2));
-  uint32_t* xb = wsp<uint32_t>(a, a.off.xbuf);
-  for (int r = r0 + 2 * threadIdx.x; r < r1; r += 2 * BLOCK) {
-    const uint64_t hv = ld_u64(h2 + r / 2);
-    const uint32_t lo = f32_to_bf16(__uint_as_float((uint32_t)hv) + L.outc[r - r0]);
-    const uint32_t hi = f32_to_bf16(__uint_as_float((uint32_t)(hv >> 32)) + L.outc[r + 1 - r0]);
-    st_u32(xb + r / 2, lo | (hi << 16));
+  // out = h2 + f, rounded to bf16: LL words of bf16 pairs (next step's input)
+  uint64_t* xll = wsp<uint64_t>(a, a.off.x);
+  for (int r = r0 + 2 * tid_opaque(); r < r1; r += 2 * BLOCK) {
+    const uint32_t lo = f32_to_bf16(L.h2res[r - r0] + L.outc[r - r0]);
+    const uint32_t hi = f32_to_bf16(L.h2res[r + 1 - r0] + L.outc[r + 1 - r0]);
+    ll_put(xll + r / 2, lo | (hi << 16), st.k1);
     if (out_hidden) gp(reinterpret_cast<uint32_t*>(out_hidden))[r / 2] = lo | (hi << 16);
   }
-  stamp(a, cx, st, TR_DOWN_EPI);
-  arrive(cx, S_OUT, st.k1, cx.nwg);
   stamp(a, cx, st, TR_DOWN_DONE);
   return true;
 }
@@ -871,13 +971,14 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_gqa(KArgs a) {
   cx.budget = a.budget;
   cx.w = blockIdx.x;
   cx.nwg = gridDim.x;
-  cx.ctr_xcd = wsp<uint32_t>(a, a.off.ctr_xcd);
-  cx.ctr_glob = wsp<uint32_t>(a, a.off.ctr_glob);
-  cx.ctr_grp = wsp<uint32_t>(a, a.off.ctr_grp);
-  cx.ctr_att = wsp<uint32_t>(a, a.off.ctr_att);
   cx.status = wsp<uint32_t>(a, a.off.status);
   const DLayer* layers = wsp<DLayer>(a, a.off.layers);
-  Lds L = carve(lds_raw, a.c);
+  {
+    Lds L0 = carve(lds_raw, a.c);
+    if (tid_opaque() < TR_SLOTS) L0.tr[tid_opaque()] = 0;
+    exp_f64_init(L0.dk);
+    __syncthreads();
+  }
   for (int t = 0; t < a.n_tokens; t++) {
     for (int li = 0; li < a.n_layers; li++) {
       cx.layer = a.layer0 + li;
@@ -890,12 +991,23 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_gqa(KArgs a) {
       st.in_hidden = st.first ? a.in_hidden : nullptr;
       st.pos = a.pos0 + t;
       const bool last = (t == a.n_tokens - 1) && (li == a.n_layers - 1);
-      stamp(a, cx, st, TR_START);
-      if (!stage_qkv_gqa<SH>(cx, a, st, L)) return;
-      if (!attention_gqa<SH>(cx, a, st, L)) return;
-      if (!stage_wo<SH>(cx, a, st, L)) return;
-      if (!stage_ffn<SH>(cx, a, st, L)) return;
-      if (!stage_down<SH>(cx, a, st, L, last ? a.out_hidden : nullptr)) return;
+      // The workspace base is made opaque for every step: per-lane addresses derived from
+      // it are then recomputed inside the step instead of being hoisted out of the loop
+      // and held (spilled) across all stages.
+      KArgs as = a;
+      asm volatile("" : "+s"(as.ws));
+      // the same for the LDS carve (a 32-bit offset, so the pointers stay LDS pointers)
+      uint32_t lds0 = 0;
+      asm volatile("" : "+s"(lds0));
+      Lds L = carve(lds_raw + lds0, a.c);
+      st.tr = L.tr;
+      stamp(as, cx, st, TR_START);
+      if (!stage_qkv_gqa<SH>(cx, as, st, L)) return;
+      if (!attention_gqa<SH>(cx, as, st, L)) return;
+      if (!stage_wo<SH>(cx, as, st, L)) return;
+      if (!stage_ffn<SH>(cx, as, st, L)) return;
+      if (!stage_down<SH>(cx, as, st, L, last ? as.out_hidden : nullptr)) return;
+      trace_flush(as, cx, st);
     }
   }
 }
@@ -990,12 +1102,19 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
     k->G = c->n_heads / c->n_kv_heads;
     if (!pick_kernel(c)) return PLD_E_UNSUPPORTED;
     if (nwg % c->n_kv_heads) return PLD_E_UNSUPPORTED;
+    // One LL buffer per activation is safe when every workgroup that reads a buffer is
+    // an ancestor of its next writer: every workgroup must publish some q/k/v rows and
+    // some expert activations (m) each step.
+    if ((c->n_heads + 2 * c->n_kv_heads) * c->head_dim / 2 < nwg) return PLD_E_UNSUPPORTED;
+    if (c->inter < nwg) return PLD_E_UNSUPPORTED;
     k->cpg = nwg / c->n_kv_heads;
     k->chmax = (c->max_seq + k->cpg - 1) / k->cpg + 1;
     const int R = (c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
+    // attention: q [G*HD] + new k/v row [HD] + scores [G*chmax] + wave sums [8*G*HD] + (m, l);
+    // merge staging: at most G*HD/cpg + 1 dims of cpg chunks, (m, l) and weights of two heads
     int act = std::max({c->hidden, c->n_heads * c->head_dim, k->slots * c->inter,
-                        k->G * k->chmax + NWAVES * k->G * c->head_dim + 2 * k->G,
-                        k->G * k->cpg * (c->head_dim + 2)});
+                        k->G * c->head_dim + c->head_dim + k->G * k->chmax + NWAVES * k->G * c->head_dim + 2 * k->G,
+                        k->cpg * (k->G * c->head_dim / k->cpg + 1) + 8 * k->cpg + 8});
     k->act_floats = (int)al(act, 64);
     k->stage_words = (int)al(c->hidden / 2 + 2, 64);
     int outb = std::max({R / nwg + 4, k->slots * (c->hidden / nwg + 4), 2 * ((k->slots * c->inter) / nwg + 2),
@@ -1011,21 +1130,19 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
 WsOff layout(const KCfg& k, int n_layers) {
   WsOff o;
   size_t p = 0;
-  o.ctr_xcd = p; p += al((size_t)NSTG * NXCD * CTR_STRIDE * 4);
-  o.ctr_glob = p; p += al((size_t)NSTG * CTR_STRIDE * 4);
-  const int ngrp = std::max(k.nkv, 1);
-  o.ctr_grp = p; p += al((size_t)ngrp * CTR_STRIDE * 4);
-  o.ctr_att = p; p += al((size_t)CTR_STRIDE * 4);
+  const size_t W = 8;   // LL word
   o.status = p; p += al(64);
-  o.xbuf = p; p += al((size_t)k.H * 4);
-  o.q = p; p += al((size_t)std::max(k.nh * k.hd, 1) * 4);
-  o.part = p; p += al((size_t)k.nh * k.cpg * (k.hd + 2) * 4);
-  o.o = p; p += al((size_t)std::max(k.nh * k.hd, 1) * 4);
-  o.h2 = p; p += al((size_t)k.H * 4);
-  o.logits = p; p += al((size_t)std::max(k.E, 1) * 16);
+  o.x = p; p += al((size_t)(k.H / 2) * W);
+  o.q = p; p += al((size_t)std::max(k.nh * k.hd, 1) * W);
+  o.kv = p; p += al((size_t)std::max(k.nkv * k.hd, 1) * W);   // k half then v half, bf16 pairs
+  o.part = p; p += al((size_t)k.nh * k.cpg * (k.hd + 2) * W);
+  o.o = p; p += al((size_t)std::max(k.nh * k.hd, 1) * W);
+  o.h2 = p; p += al((size_t)k.H * W);
+  o.logits = p; p += al((size_t)std::max(k.E, 1) * 4 * W);
+  o.m = p; p += al((size_t)k.slots * k.inter * W);
+  o.ll_end = p;
   o.sel = p; p += al(64 * 4);
   o.gates = p; p += al(64 * 4);
-  o.m = p; p += al((size_t)k.slots * k.inter * 4);
   o.a_dbg = p; p += al((size_t)k.H * 4);
   o.b_dbg = p; p += al((size_t)k.H * 4);
   o.rope = p; p += al((size_t)k.max_seq * std::max(k.hd, 2) * 4);
@@ -1161,7 +1278,7 @@ pld_status decode_layer_init(const pld_config* cfg, int32_t n_layers, const pld_
     }
   bool ok = hipMemcpy(h->ws + off.rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice) == hipSuccess;
   ok = ok && hipMemcpy(h->ws + off.layers, dl.data(), dl.size() * sizeof(DLayer), hipMemcpyHostToDevice) == hipSuccess;
-  ok = ok && hipMemset(h->ws, 0, off.xbuf) == hipSuccess;   // counters + status
+  ok = ok && hipMemset(h->ws, 0, off.ll_end) == hipSuccess;   // status + LL buffers
   ok = ok && hipFuncSetAttribute((const void*)h->fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->lds_bytes) == hipSuccess;
   int per_cu = 0;
   ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)h->fn, BLOCK, h->lds_bytes) == hipSuccess;
@@ -1249,9 +1366,10 @@ pld_status decode_poll_status(pld_handle* h, pld_device_status* out) {
 pld_status decode_reset(pld_handle* h) {
   if (!h) return PLD_E_INVALID;
   if (hipDeviceSynchronize() != hipSuccess) return PLD_E_HIP;
-  if (hipMemset(h->ws, 0, h->off.xbuf) != hipSuccess) return PLD_E_HIP;
+  // status and LL buffers cleared; the step counter (LL epoch) keeps counting, so no word
+  // left by an aborted launch can carry an epoch that a later launch waits for
+  if (hipMemset(h->ws, 0, h->off.ll_end) != hipSuccess) return PLD_E_HIP;
   if (hipDeviceSynchronize() != hipSuccess) return PLD_E_HIP;
-  h->steps = 0;
   h->bad = false;
   return PLD_OK;
 }
@@ -1263,15 +1381,15 @@ pld_status pld_debug_buffer(pld_handle* h, const char* name, void** ptr, size_t*
   const KCfg& k = h->kc;
   struct E { const char* n; size_t off, sz; } tab[] = {
       {"a", h->off.a_dbg, (size_t)k.H * 4},
-      {"q", h->off.q, (size_t)k.nh * k.hd * 4},
-      {"o", h->off.o, (size_t)k.nh * k.hd * 4},
-      {"h2", h->off.h2, (size_t)k.H * 4},
+      {"q", h->off.q, (size_t)k.nh * k.hd * 8},
+      {"o", h->off.o, (size_t)k.nh * k.hd * 8},
+      {"h2", h->off.h2, (size_t)k.H * 8},
       {"b", h->off.b_dbg, (size_t)k.H * 4},
-      {"logits", h->off.logits, (size_t)k.E * 16},
+      {"logits", h->off.logits, (size_t)k.E * 32},
       {"sel", h->off.sel, (size_t)k.topk * 4},
       {"gates", h->off.gates, (size_t)k.topk * 4},
-      {"m", h->off.m, (size_t)k.slots * k.inter * 4},
-      {"x", h->off.xbuf, (size_t)k.H * 2},
+      {"m", h->off.m, (size_t)k.slots * k.inter * 8},
+      {"x", h->off.x, (size_t)k.H * 4},
   };
   for (auto& e : tab)
     if (!strcmp(e.n, name)) {
