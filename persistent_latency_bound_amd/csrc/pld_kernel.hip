@@ -270,6 +270,10 @@ __device__ __forceinline__ void rmsnorm_reg(float* act, const RegVec<N>& gam, do
 #define PLD_IF_DOWN 8
 #endif
 
+// One (expert, slot, row range) piece of a gate/up GEMV list.
+struct GuPiece { int expert, slot, j0, j1; };
+constexpr int MAX_PIECES = MAX_SEGS / 2;
+
 // ------------------------------------------------------------------ LDS layout
 struct Lds {
   float* act;        // [act_floats]   activation vector / attention scratch / merge staging
@@ -284,6 +288,8 @@ struct Lds {
   RowSeg* segs;      // [MAX_SEGS] GEMV segment list of the current stage
   uint64_t* tr;      // [TR_SLOTS] trace stamps of the current step (flushed at its end)
   double* dk;        // [16] fp64 constants of exp_f64 (kept in LDS, see there)
+  GuPiece* pcs;      // [MAX_PIECES] gate/up pieces of the current list (LDS: a per-lane
+                     // array indexed at run time would live in scratch memory)
 };
 __device__ __forceinline__ Lds carve(float* base, const KCfg& c) {
   Lds L;
@@ -299,11 +305,12 @@ __device__ __forceinline__ Lds carve(float* base, const KCfg& c) {
   L.segs = reinterpret_cast<RowSeg*>(L.fgate + 32);
   L.tr = reinterpret_cast<uint64_t*>(L.segs + MAX_SEGS);
   L.dk = reinterpret_cast<double*>(L.tr + TR_SLOTS);
+  L.pcs = reinterpret_cast<GuPiece*>(L.dk + 16);
   return L;
 }
 __host__ __device__ inline size_t lds_bytes_for(int act_floats, int stage_words, int outb_floats) {
   return (size_t)4 * (act_floats + stage_words + 4 * outb_floats) + 8 * 16 + 4 * 32 + 4 * 32 +
-         sizeof(RowSeg) * MAX_SEGS + 8 * TR_SLOTS + 8 * 16;
+         sizeof(RowSeg) * MAX_SEGS + 8 * TR_SLOTS + 8 * 16 + sizeof(GuPiece) * MAX_PIECES;
 }
 
 // Publishes a segment list to the workgroup (the previous list must be out of use).
@@ -758,9 +765,9 @@ __device__ __forceinline__ bool stage_wo(Ctx& cx, const KArgs& a, const Step& st
 // Gate/up rows of several (expert, slot, row range) pieces as one GEMV list, then
 // m[slot][j] = silu(gate_j . b) * (up_j . b), published as LL words. Each piece
 // contributes a gate segment and an up segment; results come back in list order.
-struct GuPiece { int expert, slot, j0, j1; };
 template <class SH, int INFL, typename Pre>
-__device__ __forceinline__ bool gate_up_list(const KArgs& a, const Step& st, Lds& L, const GuPiece* pc, int np, Pre&& pre) {
+__device__ __forceinline__ bool gate_up_list(const KArgs& a, const Step& st, Lds& L, int np, Pre&& pre) {
+  const GuPiece* pc = L.pcs;   // written by thread 0 before the call, published by seg_begin
   const DLayer Ly = *gp(st.Ly);
   constexpr size_t RB = (size_t)SH::H * (SH::FP8 ? 1 : 2);
   seg_begin();
@@ -844,14 +851,16 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
   };
   const int j0 = split_at(SH::INTER, nwg, w), j1 = split_at(SH::INTER, nwg, w + 1);
   if constexpr (!SH::MOE) {
-    const GuPiece pc[1] = {{0, 0, j0, j1}};
-    if (!gate_up_list<SH, PLD_IF_SHARED>(a, st, L, pc, j1 > j0 ? 1 : 0, pre_b)) return false;
+    __syncthreads();
+    if (tid_opaque() == 0) L.pcs[0] = {0, 0, j0, j1};
+    if (!gate_up_list<SH, PLD_IF_SHARED>(a, st, L, j1 > j0 ? 1 : 0, pre_b)) return false;
   } else {
     // shared experts first: they do not depend on the router
-    GuPiece pc[2];
-    int np = 0;
-    for (int sj = 0; sj < c.nshared && j1 > j0; sj++) pc[np++] = {c.E + sj, c.topk + sj, j0, j1};
-    if (!gate_up_list<SH, PLD_IF_SHARED>(a, st, L, pc, np, pre_b)) return false;
+    const int np = j1 > j0 ? c.nshared : 0;
+    __syncthreads();
+    if (tid_opaque() == 0)
+      for (int sj = 0; sj < np; sj++) L.pcs[sj] = {c.E + sj, c.topk + sj, j0, j1};
+    if (!gate_up_list<SH, PLD_IF_SHARED>(a, st, L, np, pre_b)) return false;
     if (!pre_b()) return false;
     stamp(a, cx, st, TR_SHARED_GEMV);
     // router top-k (every workgroup computes the same selection)
@@ -894,13 +903,17 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
     // routed experts: this workgroup's share of the topk*inter (slot, row) pairs, one list
     const int tot = c.topk * SH::INTER;
     const int i0 = split_at(tot, nwg, w), i1 = split_at(tot, nwg, w + 1);
-    GuPiece rp[MAX_SEGS / 2];
+    // (every thread counts the pieces; thread 0 writes them; the previous list's readers
+    // are past the __syncthreads that follows the gates)
     int nr = 0;
-    for (int s = i0 / SH::INTER; s < c.topk && s * SH::INTER < i1 && nr < MAX_SEGS / 2; s++) {
+    for (int s = i0 / SH::INTER; s < c.topk && s * SH::INTER < i1 && nr < MAX_PIECES; s++) {
       const int lo = max(i0, s * SH::INTER) - s * SH::INTER, hi = min(i1, (s + 1) * SH::INTER) - s * SH::INTER;
-      if (lo < hi) rp[nr++] = {L.isel[s], s, lo, hi};
+      if (lo < hi) {
+        if (tid_opaque() == 0) L.pcs[nr] = {L.isel[s], s, lo, hi};
+        nr++;
+      }
     }
-    if (!gate_up_list<SH, PLD_IF_ROUTED>(a, st, L, rp, nr, NoPre{})) return false;
+    if (!gate_up_list<SH, PLD_IF_ROUTED>(a, st, L, nr, NoPre{})) return false;
   }
   stamp(a, cx, st, TR_M_STORED);
   stamp(a, cx, st, TR_FFN_DONE);
