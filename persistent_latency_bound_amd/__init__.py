@@ -68,7 +68,7 @@ class PldPersistentArgs(ctypes.Structure):
 
 
 # intermediates kept as LL words (32-bit payload, 32-bit epoch) in the workspace
-LL_BUFFERS = ("q", "o", "h2", "logits", "m", "x")
+LL_BUFFERS = ("q", "o", "h2", "logits", "m", "x", "cq", "ckv", "qrope", "qlat", "olat")
 
 _lib = None
 

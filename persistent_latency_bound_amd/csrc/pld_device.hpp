@@ -242,7 +242,8 @@ template <bool FP8, int K, int INFL>
 struct GemvLayout {
   static constexpr int EPC = FP8 ? 16 : 8;
   static constexpr int CHUNKS = K / EPC;
-  static constexpr int LPR = CHUNKS >= 64 ? 64 : CHUNKS;
+  // lanes per row: the largest of 64 / 32 / 16 that divides the row's chunk count
+  static constexpr int LPR = CHUNKS % 64 == 0 ? 64 : CHUNKS % 32 == 0 ? 32 : CHUNKS % 16 == 0 ? 16 : CHUNKS;
   static constexpr int CPL = CHUNKS / LPR;
   static constexpr int U0 = INFL / CPL;
   static constexpr int U = U0 < 1 ? 1 : (U0 > 12 ? 12 : U0);

@@ -41,7 +41,8 @@ namespace pld {
 
 // ------------------------------------------------------------------ shared structs
 // Watchdog wait ids (pld_device_status.stage): which LL activation a workgroup waited for.
-enum WaitId { W_X = 0, W_QKV = 1, W_KV = 2, W_PART = 3, W_O = 4, W_H2 = 5, W_RT = 6, W_M = 7 };
+enum WaitId { W_X = 0, W_QKV = 1, W_KV = 2, W_PART = 3, W_O = 4, W_H2 = 5, W_RT = 6, W_M = 7, W_CQ = 8,
+              W_QN = 9, W_QLAT = 10, W_OLAT = 11 };
 enum { ST_CODE = 0, ST_STAGE = 1, ST_LAYER = 2, ST_TOKEN = 3, ST_WG = 4, ST_ABORT = 8 };
 // device trace: wall-clock stamps per (step, workgroup)
 enum TraceSlot {
@@ -62,6 +63,8 @@ struct KCfg {
   int chmax;   // max tokens in one attention chunk
   int act_floats, stage_words, outb_floats;
   int nwg;
+  int cpw;     // MLA: q_lat / o_lat outputs per workgroup (absorb, merge)
+  int rdim;    // width of the RoPE table rows (head_dim for GQA, rope_dim for MLA)
 };
 
 struct DLayer {
@@ -79,7 +82,8 @@ struct DLayer {
 // Workspace layout. The LL buffers (8-byte words: payload | epoch << 32) follow the
 // status words; both are zeroed at init and by decode_reset.
 struct WsOff {
-  size_t status, x, q, kv, part, o, h2, logits, m, ll_end, sel, gates, a_dbg, b_dbg, rope, layers, total;
+  size_t status, x, q, kv, part, o, h2, logits, m, cqr, ckvr, qr, qlat, olat, ll_end, sel, gates, a_dbg, b_dbg, rope,
+      layers, total;
 };
 
 struct KArgs {
@@ -372,6 +376,34 @@ __device__ __forceinline__ void hrows(int H, int nwg, int w, int* r0, int* r1) {
   *r1 = 2 * split_at(H / 2, nwg, w + 1);
 }
 
+// The layer input of a step: the caller's bf16 vector (first step of the launch) or the
+// previous step's output (LL words of bf16 pairs, previous epoch); expanded to fp32 in
+// L.act, this workgroup's residual rows [h0, h1) kept in L.xres, then RMSNorm in place.
+template <int H>
+__device__ __forceinline__ bool layer_input(Ctx& cx, const KArgs& a, const Step& st, Lds& L, const RegVec<H>& gam,
+                                            int h0, int h1) {
+  if (st.first) {
+    const PLD_GLOBAL uint32_t* src = gp(reinterpret_cast<const uint32_t*>(st.in_hidden));
+    for (int i = tid_opaque(); i < H / 2; i += BLOCK) L.stage[i] = src[i];
+    __syncthreads();
+  } else if (!ll_fetch<per_for(H / 2)>(cx, L.stage, wsp<uint64_t>(a, a.off.x), H / 2, st.k1 - 1u, W_X)) {
+    return false;
+  }
+  stamp(a, cx, st, TR_X_READY);
+  for (int i = tid_opaque(); i < H / 2; i += BLOCK) {
+    const uint32_t v = L.stage[i];
+    L.act[2 * i] = bf_lo(v);
+    L.act[2 * i + 1] = bf_hi(v);
+  }
+  __syncthreads();
+  for (int r = h0 + tid_opaque(); r < h1; r += BLOCK) L.xres[r - h0] = L.act[r];
+  rmsnorm_reg<H>(L.act, gam, a.c.eps, L.red);
+  stamp(a, cx, st, TR_X_NORMED);
+  if (cx.w == 0)
+    for (int i = tid_opaque(); i < H; i += BLOCK) st_f32(wsp<float>(a, a.off.a_dbg) + i, L.act[i]);
+  return true;
+}
+
 // ------------------------------------------------------------------ stage: RMSNorm + QKV + RoPE + cache append
 template <class SH>
 __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Step& st, Lds& L) {
@@ -391,28 +423,7 @@ __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Ste
   auto pre_x = [&]() -> bool {
     if (!pending) return true;
     pending = false;
-    // the layer input: the caller's bf16 vector (first step of the launch) or the previous
-    // step's output, LL words of bf16 pairs published with the previous step's epoch
-    if (st.first) {
-      const PLD_GLOBAL uint32_t* src = gp(reinterpret_cast<const uint32_t*>(st.in_hidden));
-      for (int i = tid_opaque(); i < SH::H / 2; i += BLOCK) L.stage[i] = src[i];
-      __syncthreads();
-    } else if (!ll_fetch<per_for(SH::H / 2)>(cx, L.stage, wsp<uint64_t>(a, a.off.x), SH::H / 2, k1 - 1u, W_X)) {
-      return false;
-    }
-    stamp(a, cx, st, TR_X_READY);
-    for (int i = tid_opaque(); i < SH::H / 2; i += BLOCK) {
-      const uint32_t v = L.stage[i];
-      L.act[2 * i] = bf_lo(v);
-      L.act[2 * i + 1] = bf_hi(v);
-    }
-    __syncthreads();
-    for (int r = h0 + tid_opaque(); r < h1; r += BLOCK) L.xres[r - h0] = L.act[r];
-    rmsnorm_reg<SH::H>(L.act, gam, c.eps, L.red);
-    stamp(a, cx, st, TR_X_NORMED);
-    if (w == 0)
-      for (int i = tid_opaque(); i < SH::H; i += BLOCK) st_f32(wsp<float>(a, a.off.a_dbg) + i, L.act[i]);
-    return true;
+    return layer_input<SH::H>(cx, a, st, L, gam, h0, h1);
   };
   {
     // one pipelined pass over this workgroup's rows of [W_q; W_k; W_v]
@@ -1025,12 +1036,17 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_gqa(KArgs a) {
   }
 }
 
+#include "pld_mla.hpp"
+
 typedef void (*KernelFn)(KArgs);
 
 // The compiled shapes: the tiny dense MHA layer (hidden 256, 4x64 heads, FFN 1024) and
 // the GQA MoE layer (hidden 4096, 32 q / 8 kv heads x 128, 64 experts of width 1536).
 using ShapeTinyDense = GqaShape<256, 4, 4, 64, 1024, false, false, 1, 2>;
 using ShapeGqaMoe = GqaShape<4096, 32, 8, 128, 1536, false, true, 9, 33>;
+// the FP8 MLA MoE layer: hidden 6144, 64 heads, q_lora 1536, kv_lora 512 + rope 64,
+// nope 128, v 128, 256 experts of width 2048 (biased-score router)
+using ShapeMlaFp8 = MlaShape<6144, 64, 1536, 512, 64, 128, 128, 2048, true, true, false>;
 
 template <class SH>
 static bool matches(const pld_config* c) {
@@ -1039,9 +1055,18 @@ static bool matches(const pld_config* c) {
          (c->ffn_kind == PLD_FFN_MOE) == SH::MOE;
 }
 
+template <class SH>
+static bool matches_mla(const pld_config* c) {
+  return c->attn_kind == PLD_ATTN_MLA && c->hidden == SH::H && c->n_heads == SH::NH && c->q_lora == SH::QL &&
+         c->kv_lora == SH::KL && c->rope_dim == SH::RD && c->nope_dim == SH::ND && c->v_dim == SH::VD &&
+         c->inter == SH::INTER && (c->wfmt == PLD_WFMT_FP8_BLOCK128) == SH::FP8 &&
+         (c->ffn_kind == PLD_FFN_MOE) == SH::MOE && (c->index_topk > 0) == SH::SPARSE;
+}
+
 static KernelFn pick_kernel(const pld_config* c) {
   if (matches<ShapeTinyDense>(c)) return k_decode_gqa<ShapeTinyDense>;
   if (matches<ShapeGqaMoe>(c)) return k_decode_gqa<ShapeGqaMoe>;
+  if (matches_mla<ShapeMlaFp8>(c)) return k_decode_mla<ShapeMlaFp8>;
   return nullptr;
 }
 
@@ -1134,8 +1159,40 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
                          2 * (c->inter / nwg + 2) * std::max(1, c->n_shared), 4 * c->n_experts + 4});
     k->outb_floats = (int)al(outb, 64);
     if (lds_bytes_for(k->act_floats, k->stage_words, k->outb_floats) > 160 * 1024) return PLD_E_UNSUPPORTED;
+    k->rdim = c->head_dim;
+  } else if (c->attn_kind == PLD_ATTN_MLA) {
+    if (!pick_kernel(c)) return PLD_E_UNSUPPORTED;
+    const int HPW = 8, NH = c->n_heads, KL = c->kv_lora, LAT = c->kv_lora + c->rope_dim, VD = c->v_dim;
+    const int nhg = NH / HPW;
+    if (NH % HPW || nwg % nhg) return PLD_E_UNSUPPORTED;
+    k->cpg = nwg / nhg;                            // attention chunks per head group
+    k->rdim = c->rope_dim;
+    // absorb / merge: cpw outputs of one head per workgroup, whole 16-byte chunks, <= 4 row passes
+    if ((NH * KL) % nwg) return PLD_E_UNSUPPORTED;
+    k->cpw = NH * KL / nwg;
+    const int epc = c->wfmt == PLD_WFMT_FP8_BLOCK128 ? 16 : 8;
+    if (KL % k->cpw || k->cpw % epc || BLOCK % (k->cpw / epc) || c->nope_dim > 4 * (BLOCK / (k->cpw / epc)))
+      return PLD_E_UNSUPPORTED;
+    // W_UV: each workgroup's rows inside one head
+    if ((NH * VD) % nwg || VD % (NH * VD / nwg)) return PLD_E_UNSUPPORTED;
+    // one LL buffer per activation: every workgroup publishes rows in every stage
+    if (c->q_lora + LAT < nwg || c->inter < nwg || c->hidden / 2 < nwg) return PLD_E_UNSUPPORTED;
+    const int TB = 32, CSTR = LAT + 4;
+    const int attn_bytes = 2 * 16 * CSTR + 2 * 2 * TB * CSTR + 2 * 16 * TB + 4 * (8 * 256 + 16) + 2 * LAT + 4 * LAT;
+    const int nope_rows = std::min(c->nope_dim, 4 * (BLOCK / (k->cpw / epc)));
+    int act = std::max({c->hidden, c->q_lora, k->slots * c->inter, (attn_bytes + 3) / 4 + 16,
+                        c->nope_dim + (BLOCK / (k->cpw / epc)) * k->cpw + nope_rows,
+                        k->cpg * k->cpw + 4 * k->cpg + 8});
+    k->act_floats = (int)al(act, 64);
+    k->stage_words = (int)al(c->hidden / 2 + 2, 64);
+    const int rx = c->q_lora + LAT, rq = NH * (c->nope_dim + c->rope_dim);
+    int outb = std::max({rx / nwg + 4, rq / nwg + 4, NH * VD / nwg + 4, c->hidden / nwg + 4,
+                         k->slots * (c->hidden / nwg + 4), 2 * ((k->slots * c->inter) / nwg + 2),
+                         2 * (c->inter / nwg + 2) * std::max(1, c->n_shared), 4 * c->n_experts + 4});
+    k->outb_floats = (int)al(outb, 64);
+    if (lds_bytes_for(k->act_floats, k->stage_words, k->outb_floats) > 160 * 1024) return PLD_E_UNSUPPORTED;
   } else {
-    return PLD_E_UNSUPPORTED;   // MLA path: not built yet
+    return PLD_E_UNSUPPORTED;
   }
   return PLD_OK;
 }
@@ -1153,12 +1210,25 @@ WsOff layout(const KCfg& k, int n_layers) {
   o.h2 = p; p += al((size_t)k.H * W);
   o.logits = p; p += al((size_t)std::max(k.E, 1) * 4 * W);
   o.m = p; p += al((size_t)k.slots * k.inter * W);
+  if (k.attn == PLD_ATTN_MLA) {
+    const size_t LAT = (size_t)k.kv_lora + k.rope;
+    o.q = p; p += al((size_t)k.nh * k.nope * W);                     // q_nope
+    o.qr = p; p += al((size_t)k.nh * k.rope * W);                    // q_rope (rotated)
+    o.cqr = p; p += al((size_t)k.q_lora * W);                        // c_q before its RMSNorm
+    o.ckvr = p; p += al(LAT * W);                                    // c_kv and k_rope before norm / RoPE
+    o.qlat = p; p += al((size_t)k.nh * k.kv_lora * W);
+    o.part = p; p += al((size_t)k.nh * k.cpg * (k.kv_lora + 2) * W);
+    o.olat = p; p += al((size_t)k.nh * k.kv_lora * W);
+    o.o = p; p += al((size_t)k.nh * k.vdim * W);
+  } else {
+    o.cqr = o.ckvr = o.qr = o.qlat = o.olat = 0;
+  }
   o.ll_end = p;
   o.sel = p; p += al(64 * 4);
   o.gates = p; p += al(64 * 4);
   o.a_dbg = p; p += al((size_t)k.H * 4);
   o.b_dbg = p; p += al((size_t)k.H * 4);
-  o.rope = p; p += al((size_t)k.max_seq * std::max(k.hd, 2) * 4);
+  o.rope = p; p += al((size_t)k.max_seq * std::max(k.rdim, 2) * 4);
   o.layers = p; p += al((size_t)n_layers * sizeof(DLayer));
   o.total = p;
   return o;
@@ -1230,12 +1300,30 @@ pld_status decode_layer_init(const pld_config* cfg, int32_t n_layers, const pld_
     if (!L.attn_norm || !L.ffn_norm || !aligned16(L.attn_norm) || !aligned16(L.ffn_norm)) return PLD_E_INVALID;
     d.attn_norm = L.attn_norm;
     d.ffn_norm = L.ffn_norm;
-    const int hd = cfg->head_dim;
-    if (!mat_ok(L.wq, fp8) || !mat_ok(L.wk, fp8) || !mat_ok(L.wv, fp8) || !mat_ok(L.wo, fp8)) return PLD_E_INVALID;
-    d.wq = dmat(L.wq, cfg->n_heads * hd, H, fp8);
-    d.wk = dmat(L.wk, cfg->n_kv_heads * hd, H, fp8);
-    d.wv = dmat(L.wv, cfg->n_kv_heads * hd, H, fp8);
-    d.wo = dmat(L.wo, H, cfg->n_heads * hd, fp8);
+    const bool mla = cfg->attn_kind == PLD_ATTN_MLA;
+    if (!mla) {
+      const int hd = cfg->head_dim;
+      if (!mat_ok(L.wq, fp8) || !mat_ok(L.wk, fp8) || !mat_ok(L.wv, fp8) || !mat_ok(L.wo, fp8)) return PLD_E_INVALID;
+      d.wq = dmat(L.wq, cfg->n_heads * hd, H, fp8);
+      d.wk = dmat(L.wk, cfg->n_kv_heads * hd, H, fp8);
+      d.wv = dmat(L.wv, cfg->n_kv_heads * hd, H, fp8);
+      d.wo = dmat(L.wo, H, cfg->n_heads * hd, fp8);
+    } else {
+      const int NH = cfg->n_heads, QL = cfg->q_lora, KL = cfg->kv_lora, RD = cfg->rope_dim, ND = cfg->nope_dim,
+                VD = cfg->v_dim;
+      if (!mat_ok(L.w_dq, fp8) || !mat_ok(L.w_uq, fp8) || !mat_ok(L.w_dkv, fp8) || !mat_ok(L.w_uk, fp8) ||
+          !mat_ok(L.w_uv, fp8) || !mat_ok(L.wo, fp8))
+        return PLD_E_INVALID;
+      if (!L.q_norm || !L.kv_norm || !aligned16(L.q_norm) || !aligned16(L.kv_norm)) return PLD_E_INVALID;
+      d.q_norm = L.q_norm;
+      d.kv_norm = L.kv_norm;
+      d.w_dq = dmat(L.w_dq, QL, H, fp8);
+      d.w_uq = dmat(L.w_uq, NH * (ND + RD), QL, fp8);
+      d.w_dkv = dmat(L.w_dkv, KL + RD, H, fp8);
+      d.w_uk = dmat(L.w_uk, NH * ND, KL, fp8);
+      d.w_uv = dmat(L.w_uv, NH * VD, KL, fp8);
+      d.wo = dmat(L.wo, H, NH * VD, fp8);
+    }
     if (!mat_ok(L.w_gate, fp8) || !mat_ok(L.w_up, fp8) || !mat_ok(L.w_down, fp8)) return PLD_E_INVALID;
     d.w_gate = dmat(L.w_gate, cfg->inter, H, fp8);
     d.w_up = dmat(L.w_up, cfg->inter, H, fp8);
@@ -1254,9 +1342,14 @@ pld_status decode_layer_init(const pld_config* cfg, int32_t n_layers, const pld_
       }
     }
     const pld_kv_cache& C = kv[l];
-    if (!C.k || !C.v || !aligned16(C.k) || !aligned16(C.v)) return PLD_E_INVALID;
-    d.kc = (uint16_t*)C.k;
-    d.vc = (uint16_t*)C.v;
+    if (!mla) {
+      if (!C.k || !C.v || !aligned16(C.k) || !aligned16(C.v)) return PLD_E_INVALID;
+      d.kc = (uint16_t*)C.k;
+      d.vc = (uint16_t*)C.v;
+    } else {
+      if (!C.latent || !aligned16(C.latent)) return PLD_E_INVALID;
+      d.lat = (uint16_t*)C.latent;
+    }
   }
   pld_handle* h = new (std::nothrow) pld_handle();
   if (!h) return PLD_E_INVALID;
@@ -1281,7 +1374,8 @@ pld_status decode_layer_init(const pld_config* cfg, int32_t n_layers, const pld_
   h->wallclock_khz = khz;
   h->budget = (long long)khz * 1000LL * 2;   // 2 s
   // RoPE table: (cos, sin) of pos * base^(-2i/d) for the interleaved pairs, fp64 -> fp32
-  const int d = cfg->head_dim;
+  // (d = head_dim for GQA; MLA rotates only its rope_dim dims)
+  const int d = k.rdim;
   std::vector<float> rope((size_t)cfg->max_seq * d);
   for (int p = 0; p < cfg->max_seq; p++)
     for (int i = 0; i < d / 2; i++) {
@@ -1394,8 +1488,8 @@ pld_status pld_debug_buffer(pld_handle* h, const char* name, void** ptr, size_t*
   const KCfg& k = h->kc;
   struct E { const char* n; size_t off, sz; } tab[] = {
       {"a", h->off.a_dbg, (size_t)k.H * 4},
-      {"q", h->off.q, (size_t)k.nh * k.hd * 8},
-      {"o", h->off.o, (size_t)k.nh * k.hd * 8},
+      {"q", h->off.q, (size_t)k.nh * (k.attn == PLD_ATTN_MLA ? k.nope : k.hd) * 8},
+      {"o", h->off.o, (size_t)k.nh * (k.attn == PLD_ATTN_MLA ? k.vdim : k.hd) * 8},
       {"h2", h->off.h2, (size_t)k.H * 8},
       {"b", h->off.b_dbg, (size_t)k.H * 4},
       {"logits", h->off.logits, (size_t)k.E * 32},
@@ -1403,6 +1497,11 @@ pld_status pld_debug_buffer(pld_handle* h, const char* name, void** ptr, size_t*
       {"gates", h->off.gates, (size_t)k.topk * 4},
       {"m", h->off.m, (size_t)k.slots * k.inter * 8},
       {"x", h->off.x, (size_t)k.H * 4},
+      {"cq", h->off.cqr, (size_t)k.q_lora * 8},
+      {"ckv", h->off.ckvr, (size_t)(k.kv_lora + k.rope) * 8},
+      {"qrope", h->off.qr, (size_t)k.nh * k.rope * 8},
+      {"qlat", h->off.qlat, (size_t)k.nh * k.kv_lora * 8},
+      {"olat", h->off.olat, (size_t)k.nh * k.kv_lora * 8},
   };
   for (auto& e : tab)
     if (!strcmp(e.n, name)) {
