@@ -2,9 +2,11 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers R] [--no-cpu-baseline]
 
-Workload: the single MoE decode layer, batch 1, bf16 — hidden 4096, GQA 32 q / 8 kv heads x
-128, 8192-token KV cache, router over 64 experts (top-8, softmax renormalised), expert
-SwiGLU width 1536 plus one shared expert; weights N(0, 0.02), router N(0, 0.1). A step
+Workload (default): the single MoE decode layer, batch 1, bf16 — hidden 4096, GQA 32 q / 8 kv
+heads x 128, 8192-token KV cache, router over 64 experts (top-8, softmax renormalised),
+expert SwiGLU width 1536 plus one shared expert; weights N(0, 0.02), router N(0, 0.1).
+--workload mla_moe256_fp8_decode_layer measures the FP8 MLA layer (hidden 6144, 64 heads,
+latent 512+64, 256 experts of width 2048, biased-score router) the same way. A step
 decodes one token through a stack of R independent seeded copies of that layer in ONE
 launch of the persistent kernel (decode_layers_persistent). R copies keep the weights
 cold: R x 458 MB is far larger than the 256 MB Infinity Cache, so the bytes come from
@@ -29,10 +31,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
-WORKLOAD = "gqa_moe_bf16_decode_layer"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gqa_moe_bf16.json")
+WORKLOADS = {   # name -> (synth.configs attribute, traffic file stem, dtype of the arithmetic)
+    "gqa_moe_bf16_decode_layer": ("C2", "traffic_gqa_moe_bf16", "bf16"),
+    "mla_moe256_fp8_decode_layer": ("C3", "traffic_mla_moe256_fp8", "fp8-e4m3 weights, fp32 accumulate"),
+}
+DEFAULT_WORKLOAD = "gqa_moe_bf16_decode_layer"
 KERNEL_SOURCES = [os.path.join(ROOT, "persistent_latency_bound_amd", "csrc", f)
-                  for f in ("pld_kernel.hip", "pld_device.hpp")]
+                  for f in ("pld_kernel.hip", "pld_device.hpp", "pld_mla.hpp")]
 
 
 def kernel_sha() -> str:
@@ -42,11 +47,12 @@ def kernel_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_per_launch(layers: int):
+def traffic_per_launch(workload: str, layers: int):
     """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+    path = os.path.join(ROOT, "profiles", WORKLOADS[workload][1] + ".json")
+    if not os.path.exists(path):
         return None
-    t = json.load(open(TRAFFIC_FILE))
+    t = json.load(open(path))
     if t.get("kernel_sha") != kernel_sha() or t.get("layers_per_launch") != layers:
         return None
     return t.get("hbm_bytes_per_launch")
@@ -77,12 +83,17 @@ def cpu_baseline(shape, pos: int, budget_s: float = 20.0) -> dict:
                       f"generates the weights; fp64 NumPy, BLAS and generator threads = {cores}"}
 
 
-STAMPS = ["start", "x_ready", "qkv_done", "att_ready", "att_done", "o_ready", "wo_done", "h2_ready",
-          "router_ready", "ffn_done", "m_ready", "down_done"]
+SLOT_NAMES = {0: "start", 1: "x_ready", 2: "qkv_done", 3: "att_ready", 4: "att_done", 5: "o_ready", 6: "wo_done",
+              7: "h2_ready", 8: "router_ready", 9: "ffn_done", 10: "m_ready", 11: "down_done", 12: "att_q",
+              13: "att_softmax", 14: "att_partial", 15: "att_merged", 16: "topk", 18: "m_stored", 19: "down_gemv",
+              20: "down_epi", 21: "qkv_gemv", 22: "shared_gemv", 23: "att_pv", 24: "x_normed", 25: "merge_start",
+              26: "merge_fetched", 27: "router_logit", 28: "att_drained", 30: "att_scores", 17: "blk0_staged", 31: "blk0_done"}
 
 
-def write_trace_summary(dec, shape, pos, x, out, R, path):
-    """One extra (untimed) launch with the device trace on; per-stage wait and work times."""
+def write_trace_summary(dec, x, out, R, path, pos):
+    """One extra (untimed) launch with the device trace on. For every stamped slot: median
+    time since the step's first stamp (over workgroups and layers), in stamp order, and the
+    gaps between consecutive medians."""
     import numpy as np
     import torch
     nwg, _ = dec.launch_shape()
@@ -91,38 +102,26 @@ def write_trace_summary(dec, shape, pos, x, out, R, path):
     dec.persistent(start_pos=pos, in_hidden=x, out_hidden=out)
     torch.cuda.synchronize()
     dec.set_trace(None)
-    t = buf.cpu().numpy().reshape(R, nwg, 32)[:, :, :len(STAMPS)].astype(np.float64)
+    t = buf.cpu().numpy().reshape(R, nwg, 32).astype(np.float64)
     tick_us = 1e-2   # wall_clock64 runs at 100 MHz on MI355X (hipDeviceAttributeWallClockRate = 100000 kHz)
-    rel = (t - t[:, :, :1].min(axis=1, keepdims=True)) * tick_us
-    seg = {}
-    names = list(zip(STAMPS[:-1], STAMPS[1:]))
-    for i, (a_, b_) in enumerate(names):
-        d = (t[:, :, i + 1] - t[:, :, i]) * tick_us
-        seg[f"{a_}->{b_}"] = {"median_us": round(float(np.median(d)), 2), "max_us": round(float(d.max()), 2)}
-    full = buf.cpu().numpy().reshape(R, nwg, 32).astype(np.float64)
-    att = {}
-    for name, i0, i1 in (("att_ready->q_regs", 3, 12), ("q_regs->scores", 12, 30), ("scores->softmax", 30, 13),
-                         ("softmax->pv", 13, 23), ("pv->drained", 23, 28), ("drained->partial_stored", 28, 14),
-                         ("partial_stored->merge_start", 14, 25), ("merge_start->merge_fetched", 25, 26),
-                         ("merge_fetched->merged", 26, 15),
-                         ("x_ready->x_normed", 1, 24), ("x_normed->qkv_gemv", 24, 21), ("qkv_gemv->qkv_done", 21, 2),
-                         ("o_ready->wo_done", 5, 6),
-                         ("h2_ready->shared_gemv", 7, 22), ("shared_gemv->router_ready", 22, 8),
-                         ("router_ready->topk", 8, 16), ("topk->m_stored", 16, 18),
-                         ("m_ready->down_gemv", 10, 19), ("down_gemv->epilogue", 19, 20), ("epilogue->down_done", 20, 11)):
-        d = (full[:, :, i1] - full[:, :, i0]) * tick_us
-        att[name] = {"median_us": round(float(np.median(d)), 2), "max_us": round(float(d.max()), 2)}
-    for name, i0, i1, sel in (("h2_ready->router_logit (router wgs)", 7, 27, 27),
-                              ("router_logit->router_ready (router wgs)", 27, 8, 27)):
-        msk = full[:, :, sel] > 0
-        if msk.any():
-            d = (full[:, :, i1] - full[:, :, i0])[msk] * tick_us
-            att[name] = {"median_us": round(float(np.median(d)), 2), "max_us": round(float(d.max()), 2)}
-    seg["attention_detail"] = att
-    layer_us = [(t[l, :, -1].max() - t[l, :, 0].min()) * tick_us for l in range(R)]
-    summary = {"layers": R, "nwg": nwg, "segments": seg,
-               "layer_critical_path_us": [round(float(v), 2) for v in layer_us],
-               "stamp_median_us_from_layer_start": {n: round(float(np.median(rel[:, :, i])), 2) for i, n in enumerate(STAMPS)}}
+    start = t[:, :, 0].min(axis=1, keepdims=True)
+    rows = []
+    for slot in range(32):
+        v = t[:, :, slot]
+        msk = v > 0
+        if not msk.any():
+            continue
+        rel = (v - start)[msk] * tick_us
+        rows.append((float(np.median(rel)), slot, float(np.max(rel)), int(msk.sum())))
+    rows.sort()
+    stamps, prev = [], 0.0
+    for med, slot, mx, cnt in rows:
+        stamps.append({"slot": SLOT_NAMES.get(slot, str(slot)), "median_us": round(med, 2), "max_us": round(mx, 2),
+                       "gap_us": round(med - prev, 2), "stamps": cnt})
+        prev = med
+    layer_us = [(t[l, :, 11].max() - t[l, :, 0].min()) * tick_us for l in range(R)]
+    summary = {"layers": R, "nwg": nwg, "stamps_from_layer_start": stamps,
+               "layer_critical_path_us": [round(float(v), 2) for v in layer_us]}
     with open(path, "w") as f:
         json.dump(summary, f, indent=1)
 
@@ -137,6 +136,7 @@ def main():
     ap.add_argument("--single-launch", action="store_true",
                     help="also time decode_step (one layer per launch, launch cost included)")
     ap.add_argument("--trace", default=None, help="write a per-stage device-trace summary (JSON) to this path")
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -157,7 +157,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    shape = configs.C2
+    shape = getattr(configs, WORKLOADS[args.workload][0])
     pos = shape.cache_len
     R = args.layers
     Ws = [sdev.layer_weights(shape, 0, l) for l in range(R)]
@@ -212,12 +212,12 @@ def main():
         single_us = e0.elapsed_time(e1) * 1e3 / n1
 
     if args.trace:
-        write_trace_summary(dec, shape, pos, xs[0], out, R, args.trace)
+        write_trace_summary(dec, xs[0], out, R, args.trace, pos)
 
     bytes_layer = accounting.layer_bytes(shape, pos)
     bytes_launch = bytes_layer * R
     achieved = bytes_launch / (ms_per_step * 1e-3) / 1e9
-    traffic = traffic_per_launch(R)
+    traffic = traffic_per_launch(args.workload, R)
     line = {
         "metric": "batch-1 decode us/layer (achieved HBM TB/s vs peak, implied tokens/s/user)",
         "value": round(us_per_layer, 3),
@@ -229,10 +229,13 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": WORKLOADS[args.workload][2],
         "data": "synthetic",
-        "config": {"workload": WORKLOAD, "hidden": shape.hidden, "heads": f"{shape.n_heads}q/{shape.n_kv_heads}kv x {shape.head_dim}",
-                   "kv_cache_tokens": pos, "experts": f"{shape.n_experts} top-{shape.top_k} + {shape.n_shared} shared",
+        "config": {"workload": args.workload, "hidden": shape.hidden,
+                   "attention": (f"GQA {shape.n_heads}q/{shape.n_kv_heads}kv x {shape.head_dim}" if shape.attn == "gqa" else
+                                 f"MLA {shape.n_heads} heads, latent {shape.kv_lora}+{shape.rope_dim}, q_lora {shape.q_lora}"),
+                   "weights": shape.wfmt, "kv_cache_tokens": pos,
+                   "experts": f"{shape.n_experts} top-{shape.top_k} + {shape.n_shared} shared ({shape.router})",
                    "expert_inter": shape.inter, "layers_per_launch": R, "tokens_per_step": 1, "batch": 1},
         "achieved_TBps": round(achieved / 1e3, 3),
         "frac_of_peak": round(achieved / PEAK_HBM_GBPS, 4),

@@ -149,6 +149,27 @@ __device__ __forceinline__ float dpp_sum(float v) {
   return v;
 }
 
+// Wave-wide max and sum with DPP lane moves (no LDS permutes), result in every lane.
+// The moves keep a lane's own value where a move does not write it (old = the value,
+// bound_ctrl off), so max is not polluted by zeros; same move sequence as dpp_sum.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_keep(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), CTRL, ROW_MASK, 0xf, false));
+}
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = fmaxf(v, dpp_keep<0xB1, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x4E, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x141, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x140, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x142, 0xa>(v));
+  v = fmaxf(v, dpp_keep<0x143, 0xc>(v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = dpp_sum<64>(v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
 // Block-wide sum in a fixed order (wave sums, then wave 0..7 in order). All threads get the result.
 template <typename T>
 __device__ __forceinline__ T block_sum(T v, T* red) {

@@ -886,9 +886,13 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
     for (int e = tid_opaque(); e < c.E; e += BLOCK) {
       const double ke = lk[2 * e + 1];
       int rank = 0;
-      for (int j = 0; j < c.E; j++) {
-        const double kj = lk[2 * j + 1];
-        rank += (kj > ke) || (kj == ke && j < e);
+      // (E is a multiple of 8: the unrolled reads of 8 keys are in flight together)
+      for (int j0 = 0; j0 < c.E; j0 += 8) {
+#pragma unroll
+        for (int j = j0; j < j0 + 8; j++) {
+          const double kj = lk[2 * j + 1];
+          rank += (kj > ke) || (kj == ke && j < e);
+        }
       }
       if (rank < c.topk) L.isel[rank] = e;
     }
@@ -1125,7 +1129,7 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
   if (c->ffn_kind == PLD_FFN_DENSE) {
     k->slots = 1;
   } else if (c->ffn_kind == PLD_FFN_MOE) {
-    if (c->n_experts < 8 || c->n_experts > nwg || c->n_experts > 512) return PLD_E_UNSUPPORTED;
+    if (c->n_experts < 8 || c->n_experts > nwg || c->n_experts > 512 || c->n_experts % 8) return PLD_E_UNSUPPORTED;
     if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts) return PLD_E_UNSUPPORTED;
     if (c->n_shared < 0 || c->n_shared > 2) return PLD_E_UNSUPPORTED;
     if (c->router_kind != PLD_ROUTER_SOFTMAX_TOPK && c->router_kind != PLD_ROUTER_SIGMOID_BIAS) return PLD_E_UNSUPPORTED;

@@ -246,39 +246,59 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
   uint16_t* newrow = reinterpret_cast<uint16_t*>(alph + 16);   // [LAT] the row of position pos
   float* ntmp = reinterpret_cast<float*>(newrow + LAT);  // [LAT] its fp32 raw values
   auto srow = [&](int t) -> size_t { return (size_t)(nst > 0 ? t0 + min(t, nst - 1) : 0); };
-  // staging registers of one sub-block: chunk i of the block covers (row i / CPRW, chunk i % CPRW)
-  uint4 cb[NLD];
-  auto issue = [&](int tb0) {
+  // Staging registers: three sub-blocks in flight (sets A, B, C in turn); chunk i of a
+  // block covers (row i / CPRW, chunk i % CPRW). A block's loads are issued three blocks
+  // before it is staged into LDS, so the wait at staging time covers ~3 blocks of work.
+  // Rows are streamed through register sets A, B, C in turn: a block's loads are issued
+  // DEPTH blocks before it is staged into LDS. All loads are unconditional (clamped rows;
+  // blocks past the chunk read one uniform address and are masked), and a chunk that holds
+  // rows written inside this launch reads all its rows coherently (the two load kinds are
+  // separate template instances), so the in-order load waits stay exact. The row of
+  // position pos is patched in from LDS after staging.
+  constexpr int DEPTH = 3;
+  const int nsb = (n + TB - 1) / TB;
+  const int nsbp = (nsb + DEPTH - 1) / DEPTH * DEPTH;
+  const bool coh = n > 0 && t0 + n > fresh;
+  uint4 cb[DEPTH][NLD];
+  auto issue = [&](int set, int sb, auto coh_tag) {
+    constexpr bool COH = decltype(coh_tag)::value;
+    const bool live = sb < nsb;
 #pragma unroll
     for (int i = 0; i < NLD; i++) {
       const int idx = min(tid + i * BLOCK, TB * CPRW - 1);
       const int r = idx / CPRW, k = idx % CPRW;
-      cb[i] = ld_g16(lat + srow(tb0 + r) * LAT + k * 8);
+      const int t = max(min(sb * TB + r, n - 1), 0);
+      const size_t row = COH ? (size_t)(t0 + t) : srow(t);
+      const uint16_t* p = live ? lat + row * LAT + k * 8 : lat;
+      cb[set][i] = COH ? ld_coh16(p) : ld_g16(p);
     }
   };
-  auto store = [&](int tb0, int buf) {
+  // registers -> LDS, then the row of pos from LDS (DS operations only)
+  auto store = [&](int set, int sb, int buf) {
     uint16_t* C = Cs + buf * TB * CSTR;
 #pragma unroll
     for (int i = 0; i < NLD; i++) {
       const int idx = tid + i * BLOCK;
       if (idx < TB * CPRW) {
-        const int r = idx / CPRW, k = idx % CPRW, t = tb0 + r;
-        uint4 v = cb[i];
-        if (t >= nst && t < n) {   // a row written inside this launch
-          if (t0 + t == pos) {
-            const uint32_t* q = reinterpret_cast<const uint32_t*>(newrow + k * 8);
-            v = make_uint4(q[0], q[1], q[2], q[3]);
-          } else {
-            v = ld_coh16(lat + (size_t)(t0 + t) * LAT + k * 8);
-          }
-        }
+        const int r = idx / CPRW, k = idx % CPRW;
         uint32_t* d = reinterpret_cast<uint32_t*>(C + r * CSTR + k * 8);
-        d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+        d[0] = cb[set][i].x; d[1] = cb[set][i].y; d[2] = cb[set][i].z; d[3] = cb[set][i].w;
       }
     }
+    const int rp = pos - t0 - sb * TB;   // row of pos inside this block
+    if (rp >= 0 && rp < TB && pos < t1) {
+      __syncthreads();
+      for (int k = tid; k < LAT / 2; k += BLOCK)
+        reinterpret_cast<uint32_t*>(C + rp * CSTR)[k] = reinterpret_cast<const uint32_t*>(newrow)[k];
+    }
   };
-  const int nsb = (n + TB - 1) / TB;
-  if (nsb > 0) issue(0);
+  if (coh) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; d++) issue(d, d, std::true_type{});
+  } else {
+#pragma unroll
+    for (int d = 0; d < DEPTH; d++) issue(d, d, std::false_type{});
+  }
   // q of the head group: q_lat [HPW][KL] and q_rope [HPW][RD] (LL) -> bf16 rows of Qs
   if (!ll_fetch<per_for(HPW * KL)>(cx, reinterpret_cast<uint32_t*>(qtmp),
                                    wsp<uint64_t>(a, a.off.qlat) + (size_t)hbase * KL, HPW * KL, k1, W_QLAT))
@@ -327,28 +347,27 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
 #pragma unroll
   for (int t = 0; t < 4; t++) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int ln = lane & 15, lq = lane >> 4;
-  for (int sb = 0; sb < nsb; sb++) {
-    const int tb0 = sb * TB, buf = sb & 1;
-    const uint16_t* C = Cs + buf * TB * CSTR;
-    store(tb0, buf);
-    __syncthreads();
-    if (sb + 1 < nsb) issue(tb0 + TB);   // next block's rows in flight during the products
+  auto block = [&](const uint16_t* C, int tb0) {
     // ---- S partial: wave pair (wave >> 1) covers k-steps [kq*KQ, kq*KQ+KQ), tile nt = wave & 1
     {
       const int nt = wave & 1, kq = wave >> 1;
-      f32x4 s4 = {0.f, 0.f, 0.f, 0.f};
+      // two independent accumulator chains (even / odd k-steps)
+      f32x4 s4 = {0.f, 0.f, 0.f, 0.f}, s5 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KQ; kk++) {
         const int k0 = (kq * KQ + kk) * 16 + 4 * lq;
         const bf16x4 av = *reinterpret_cast<const bf16x4*>(Qs + ln * CSTR + k0);
         const bf16x4 bv = *reinterpret_cast<const bf16x4*>(C + (nt * 16 + ln) * CSTR + k0);
-        s4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, s4, 0, 0, 0);
+        if (kk & 1) s5 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, s5, 0, 0, 0);
+        else s4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, s4, 0, 0, 0);
       }
+      s4 += s5;
       float* dst = Ssc + (kq * 2 + nt) * 256;
 #pragma unroll
       for (int q = 0; q < 4; q++) dst[(4 * lq + q) * 16 + ln] = s4[q];
     }
     __syncthreads();
+    if (tb0 == 0) stamp(a, cx, st, 23);
     // ---- online softmax: wave h owns head h; lane t < TB is token tb0 + t
     {
       const int h = wave;
@@ -360,16 +379,17 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
         for (int kq = 0; kq < 4; kq++) s += Ssc[(kq * 2 + nt) * 256 + h * 16 + col];
         s *= scale;
       }
-      const float mb = wave_max(s);
+      const float mb = wave_max_dpp(s);
       const float mnew = fmaxf(m_run, mb);
       const float al = m_run == -INFINITY ? 0.f : __expf(m_run - mnew);
       const float p = s == -INFINITY ? 0.f : __expf(s - mnew);
-      l_run = l_run * al + wave_sum(p);
+      l_run = l_run * al + wave_sum_dpp(p);
       m_run = mnew;
       if (lane < TB) Ps[h * TB + lane] = (uint16_t)bf16_bits(p);
       if (lane == 0) alph[h] = al;
     }
     __syncthreads();
+    if (tb0 == 0) stamp(a, cx, st, 28);
     // ---- O = alpha * O + P . C: wave owns columns [wave*64, wave*64 + 64) (4 tiles)
     {
       float fa[4];
@@ -392,7 +412,25 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
         }
       }
     }
-  }
+  };
+  auto main_loop = [&](auto coh_tag) {
+    for (int sb0 = 0; sb0 < nsbp; sb0 += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; d++) {
+        const int sb = sb0 + d;
+        const int tb0 = sb * TB, buf = sb & 1;
+        const uint16_t* C = Cs + buf * TB * CSTR;
+        store(d, sb, buf);
+        __syncthreads();
+        if (sb == 0) stamp(a, cx, st, 17);
+        issue(d, sb + DEPTH, coh_tag);   // refill this set, DEPTH blocks ahead
+        block(C, tb0);
+        if (sb == 0) stamp(a, cx, st, 31);
+      }
+    }
+  };
+  if (coh) main_loop(std::true_type{});
+  else main_loop(std::false_type{});
   stamp(a, cx, st, TR_ATT_SOFTMAX);
   // publish the partial of each head: LL words [m, l, acc[0..KL)] at ((h * nch) + ch) * (KL + 2)
   vm_wait();   // the cache row appended above is visible before this workgroup's next publication
