@@ -83,7 +83,8 @@ def cpu_baseline(shape, pos: int, budget_s: float = 20.0) -> dict:
                       f"generates the weights; fp64 NumPy, BLAS and generator threads = {cores}"}
 
 
-SLOT_NAMES = {0: "start", 1: "x_ready", 2: "qkv_done", 3: "att_ready", 4: "att_done", 5: "o_ready", 6: "wo_done",
+TR_SLOTS = 48   # stamps per (step, workgroup) written by the device trace
+SLOT_NAMES = {32: "head_ready", 33: "head_gemv", 34: "token", 0: "start", 1: "x_ready", 2: "qkv_done", 3: "att_ready", 4: "att_done", 5: "o_ready", 6: "wo_done",
               7: "h2_ready", 8: "router_ready", 9: "ffn_done", 10: "m_ready", 11: "down_done", 12: "att_q",
               13: "att_softmax", 14: "att_partial", 15: "att_merged", 16: "topk", 18: "m_stored", 19: "down_gemv",
               20: "down_epi", 21: "qkv_gemv", 22: "shared_gemv", 23: "att_pv", 24: "x_normed", 25: "merge_start",
@@ -97,16 +98,16 @@ def write_trace_summary(dec, x, out, R, path, pos):
     import numpy as np
     import torch
     nwg, _ = dec.launch_shape()
-    buf = torch.zeros(R * nwg * 32, dtype=torch.int64, device="cuda")
+    buf = torch.zeros(R * nwg * TR_SLOTS, dtype=torch.int64, device="cuda")
     dec.set_trace(buf)
     dec.persistent(start_pos=pos, in_hidden=x, out_hidden=out)
     torch.cuda.synchronize()
     dec.set_trace(None)
-    t = buf.cpu().numpy().reshape(R, nwg, 32).astype(np.float64)
+    t = buf.cpu().numpy().reshape(R, nwg, TR_SLOTS).astype(np.float64)
     tick_us = 1e-2   # wall_clock64 runs at 100 MHz on MI355X (hipDeviceAttributeWallClockRate = 100000 kHz)
     start = t[:, :, 0].min(axis=1, keepdims=True)
     rows = []
-    for slot in range(32):
+    for slot in range(TR_SLOTS):
         v = t[:, :, slot]
         msk = v > 0
         if not msk.any():

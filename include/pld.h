@@ -222,15 +222,18 @@ pld_status pld_debug_buffer(pld_handle* h, const char* name, void** ptr, size_t*
 /* Launch geometry actually used: number of workgroups and threads per workgroup. */
 pld_status pld_launch_shape(pld_handle* h, int32_t* n_wg, int32_t* block);
 
-/* Device trace for profiling inside one launch: while set, every later launch writes,
- * for each (step, workgroup) of its first bytes/(n_wg*16*8) steps (a step is one layer of
- * one token), 16 uint64 wall-clock stamps (hipDeviceAttributeWallClockRate ticks) at
- * fixed points of the step: 0 start, 1 input ready, 2 q/k/v published, 3 attention inputs
- * ready, 4 attention done, 5 attention output ready, 6 residual h2 published, 7 h2 ready,
- * 8 router top-k ready, 9 expert activations published, 10 expert activations ready,
- * 11 layer output published (unused slots are left untouched). buffer: device memory of
- * `bytes` bytes, 8-aligned, owned by the caller; NULL turns tracing off. Returns
- * PLD_E_CAPACITY if the buffer cannot hold one step. */
+/* Device trace for profiling inside one launch: while set, every later launch writes, for
+ * each (step, workgroup) of its first bytes/(n_wg*48*8) steps (a step is one layer of one
+ * token), 48 uint64 wall-clock stamps (hipDeviceAttributeWallClockRate ticks) taken by the
+ * workgroup's first thread at fixed points of the step; a slot the step does not pass
+ * stays 0. Slots: 0 start, 1 layer input ready, 2 q/k/v (MLA: c_q, c_kv) published,
+ * 3/12/13/30 attention phases, 4 attention done, 5 attention output ready, 6 h2
+ * published, 7 h2 ready, 8 router logits ready, 16 top-k, 9/18 expert activations
+ * published, 10 expert activations ready, 19/20 down projection, 11 layer output
+ * published, 32 head input ready, 33 head GEMV done, 34 token chosen (last layer of a
+ * token with an LM head); the others mark sub-phases. buffer: device memory of `bytes`
+ * bytes, 8-aligned, owned by the caller; NULL turns tracing off. Returns PLD_E_CAPACITY if
+ * the buffer cannot hold one step. */
 pld_status pld_set_trace(pld_handle* h, void* buffer, size_t bytes);
 
 /* Set the watchdog budget of every bounded device wait, in microseconds (default 2e6). */

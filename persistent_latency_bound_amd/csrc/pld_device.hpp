@@ -149,6 +149,25 @@ __device__ __forceinline__ float dpp_sum(float v) {
   return v;
 }
 
+// fp64 sum over groups of 64 lanes with DPP moves applied to both 32-bit halves (same
+// move sequence as dpp_sum<64>); the total is valid in lane 63.
+template <int CTRL, int ROW_MASK, bool BOUND>
+__device__ __forceinline__ double dpp_mov_f64(double x) {
+  const long long b = __double_as_longlong(x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffff), CTRL, ROW_MASK, 0xf, BOUND);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, ROW_MASK, 0xf, BOUND);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ double dpp_sum64_f64(double v) {
+  v += dpp_mov_f64<0xB1, 0xf, false>(v);
+  v += dpp_mov_f64<0x4E, 0xf, false>(v);
+  v += dpp_mov_f64<0x141, 0xf, false>(v);
+  v += dpp_mov_f64<0x140, 0xf, false>(v);
+  v += dpp_mov_f64<0x142, 0xa, true>(v);
+  v += dpp_mov_f64<0x143, 0xc, true>(v);
+  return v;
+}
+
 // Wave-wide max and sum with DPP lane moves (no LDS permutes), result in every lane.
 // The moves keep a lane's own value where a move does not write it (old = the value,
 // bound_ctrl off), so max is not polluted by zeros; same move sequence as dpp_sum.

@@ -42,7 +42,7 @@ namespace pld {
 // ------------------------------------------------------------------ shared structs
 // Watchdog wait ids (pld_device_status.stage): which LL activation a workgroup waited for.
 enum WaitId { W_X = 0, W_QKV = 1, W_KV = 2, W_PART = 3, W_O = 4, W_H2 = 5, W_RT = 6, W_M = 7, W_CQ = 8,
-              W_QN = 9, W_QLAT = 10, W_OLAT = 11 };
+              W_QN = 9, W_QLAT = 10, W_OLAT = 11, W_AMAX = 12 };
 enum { ST_CODE = 0, ST_STAGE = 1, ST_LAYER = 2, ST_TOKEN = 3, ST_WG = 4, ST_ABORT = 8 };
 // device trace: wall-clock stamps per (step, workgroup)
 enum TraceSlot {
@@ -50,7 +50,8 @@ enum TraceSlot {
   TR_RT_READY, TR_FFN_DONE, TR_M_READY, TR_DOWN_DONE, TR_ATT_Q = 12, TR_ATT_SOFTMAX = 13, TR_ATT_PARTIAL = 14,
   TR_ATT_MERGED = 15, TR_TOPK = 16, TR_ROUTED_GEMV = 17, TR_M_STORED = 18, TR_DOWN_GEMV = 19, TR_DOWN_EPI = 20,
   TR_QKV_GEMV = 21, TR_SHARED_GEMV = 22, TR_ATT_PV = 23, TR_X_NORMED = 24, TR_MERGE_START = 25,
-  TR_MERGE_COPIED = 26, TR_RT_LOGIT = 27, TR_ATT_DRAINED = 28, TR_ATT_SCORES = 30, TR_SLOTS = 32
+  TR_MERGE_COPIED = 26, TR_RT_LOGIT = 27, TR_ATT_DRAINED = 28, TR_ATT_SCORES = 30, TR_HEAD_READY = 32,
+  TR_HEAD_GEMV = 33, TR_TOKEN = 34, TR_SLOTS = 48
 };
 
 struct KCfg {
@@ -82,8 +83,8 @@ struct DLayer {
 // Workspace layout. The LL buffers (8-byte words: payload | epoch << 32) follow the
 // status words; both are zeroed at init and by decode_reset.
 struct WsOff {
-  size_t status, x, q, kv, part, o, h2, logits, m, cqr, ckvr, qr, qlat, olat, ll_end, sel, gates, a_dbg, b_dbg, rope,
-      layers, total;
+  size_t status, x, q, kv, part, o, h2, logits, m, cqr, ckvr, qr, qlat, olat, amax, ll_end, sel, gates, a_dbg, b_dbg,
+      rope, layers, total;
 };
 
 struct KArgs {
@@ -97,6 +98,14 @@ struct KArgs {
   long long budget;
   uint64_t* trace;     // [trace_steps][nwg][TR_SLOTS] or null
   int trace_steps;
+  // LM head (vocab > 0): greedy decode loop inside the launch
+  const uint16_t* embed;   // bf16 [vocab][H]
+  const float* fnorm;      // [H]
+  DMat head;               // [vocab][H]
+  float* out_logits;       // fp32 [n_tokens][vocab] or null
+  int32_t* out_tokens;     // [n_tokens] or null
+  int in_token;            // >= 0: first input is embed[in_token]
+  int head_on;             // run the head after the last layer of every token
 };
 
 // ------------------------------------------------------------------ device context
@@ -351,6 +360,7 @@ struct Step {
   int pos;
   int idx;                     // step index within the launch (trace row)
   uint64_t* tr;                // LDS stamps of this step (thread 0)
+  const uint16_t* emb_row;     // embedding row that is this step's input (first layer of a token), or null
 };
 
 // Device trace: thread 0 keeps the step's stamps in LDS (a global store here would be
@@ -376,14 +386,15 @@ __device__ __forceinline__ void hrows(int H, int nwg, int w, int* r0, int* r1) {
   *r1 = 2 * split_at(H / 2, nwg, w + 1);
 }
 
-// The layer input of a step: the caller's bf16 vector (first step of the launch) or the
-// previous step's output (LL words of bf16 pairs, previous epoch); expanded to fp32 in
+// The layer input of a step: an embedding row (first layer of a token with a head), the
+// caller's bf16 vector (first step of the launch) or the previous step's output (LL
+// words of bf16 pairs, previous epoch); expanded to fp32 in
 // L.act, this workgroup's residual rows [h0, h1) kept in L.xres, then RMSNorm in place.
 template <int H>
 __device__ __forceinline__ bool layer_input(Ctx& cx, const KArgs& a, const Step& st, Lds& L, const RegVec<H>& gam,
                                             int h0, int h1) {
-  if (st.first) {
-    const PLD_GLOBAL uint32_t* src = gp(reinterpret_cast<const uint32_t*>(st.in_hidden));
+  if (st.emb_row || st.first) {
+    const PLD_GLOBAL uint32_t* src = gp(reinterpret_cast<const uint32_t*>(st.emb_row ? st.emb_row : st.in_hidden));
     for (int i = tid_opaque(); i < H / 2; i += BLOCK) L.stage[i] = src[i];
     __syncthreads();
   } else if (!ll_fetch<per_for(H / 2)>(cx, L.stage, wsp<uint64_t>(a, a.off.x), H / 2, st.k1 - 1u, W_X)) {
@@ -992,6 +1003,139 @@ __device__ __forceinline__ bool stage_down(Ctx& cx, const KArgs& a, const Step& 
   return true;
 }
 
+// ------------------------------------------------------------------ LM head + greedy argmax
+// logits = W_head RMSNorm(x; gamma_final) for this workgroup's vocab rows, accumulated in
+// fp64: an FP8 code times its fp32 block scale times an fp64 activation is exact in fp64,
+// so the logits equal an fp64 evaluation up to summation rounding and the argmax is
+// decided in fp64. The global argmax (lowest token id on ties) is formed from every
+// workgroup's local best, published as LL words; every workgroup derives the same token,
+// whose embedding row is the next token's input.
+template <class SH>
+__device__ __forceinline__ bool stage_head(Ctx& cx, const KArgs& a, const Step& st, Lds& L, int t, int* token) {
+  const KCfg& c = a.c;
+  constexpr int H = SH::H;
+  constexpr int EPC = 16, CHUNKS = H / EPC, CPL = CHUNKS / 64, SBK = (H + 127) / 128;
+  static_assert(SH::FP8 && CHUNKS % 64 == 0, "FP8 head with whole 64-lane rows");
+  const int V = c.vocab, nwg = cx.nwg, w = cx.w;
+  const uint32_t k1 = st.k1;
+  const int r0 = split_at(V, nwg, w), r1 = split_at(V, nwg, w + 1), nr = r1 - r0;
+  const int tid = tid_opaque(), lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  RegVec<H> gf;
+  gf.load(a.fnorm);
+  constexpr int U = 2;                                   // rows in flight per wave
+  const int nrw = max(0, (nr - wave + NWAVES - 1) / NWAVES);   // rows r0 + wave + i*NWAVES
+  uint4 buf[U][CPL];
+  float sc[U][CPL];
+  auto issue = [&](int u, int i) {   // unconditional: rows past the wave's last are clamped
+    const int r = r0 + wave + min(i, max(nrw - 1, 0)) * NWAVES;
+    const uint8_t* p = a.head.w + (size_t)min(r, V - 1) * H + lane * 16;
+    const PLD_GLOBAL float* srow = gp(a.head.s) + (size_t)(min(r, V - 1) >> 7) * SBK;
+#pragma unroll
+    for (int j = 0; j < CPL; j++) {
+      buf[u][j] = ld_stream16(p + (size_t)j * 64 * 16);
+      sc[u][j] = srow[((j * 64 + lane) * 16) >> 7];
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < U; u++) issue(u, u);
+  // input: x of the token's last layer (LL), RMSNorm in fp64
+  double* dact = reinterpret_cast<double*>(L.act);   // [H]
+  if (!ll_fetch<per_for(H / 2)>(cx, L.stage, wsp<uint64_t>(a, a.off.x), H / 2, k1, W_X)) return false;
+  double ss = 0.0;
+  for (int i = tid; i < H / 2; i += BLOCK) {
+    const uint32_t v = L.stage[i];
+    const double x0 = bf_lo(v), x1 = bf_hi(v);
+    ss += x0 * x0 + x1 * x1;
+  }
+  ss = block_sum(ss, L.red);
+  const double rr = 1.0 / sqrt(ss / (double)H + c.eps);
+#pragma unroll
+  for (int k = 0; k < RegVec<H>::K; k++) {
+    const int i = tid + k * BLOCK;
+    if (i < H) {
+      const uint32_t v = L.stage[i >> 1];
+      const double x = (i & 1) ? bf_hi(v) : bf_lo(v);
+      dact[i] = (x * rr) * (double)gf.v[k];
+    }
+  }
+  __syncthreads();
+  stamp(a, cx, st, TR_HEAD_READY);
+  double* lg = reinterpret_cast<double*>(L.outb);    // [nr]
+  for (int i0 = 0; i0 < nrw; i0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int i = i0 + u;
+      double acc = 0.0;
+#pragma unroll
+      for (int j = 0; j < CPL; j++) {
+        const int e0 = (j * 64 + lane) * 16;
+        const uint32_t d[4] = {buf[u][j].x, buf[u][j].y, buf[u][j].z, buf[u][j].w};
+        const double s = (double)sc[u][j];
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)d[q], false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)d[q], true);
+          acc = fma((double)lo.x * s, dact[e0 + 4 * q + 0], acc);
+          acc = fma((double)lo.y * s, dact[e0 + 4 * q + 1], acc);
+          acc = fma((double)hi.x * s, dact[e0 + 4 * q + 2], acc);
+          acc = fma((double)hi.y * s, dact[e0 + 4 * q + 3], acc);
+        }
+      }
+      issue(u, i + U);
+      acc = dpp_sum64_f64(acc);
+      if (lane == 63 && i < nrw) lg[wave + i * NWAVES] = acc;
+    }
+  }
+  __syncthreads();
+  stamp(a, cx, st, TR_HEAD_GEMV);
+  if (a.out_logits)
+    for (int i = tid; i < nr; i += BLOCK) gp(a.out_logits)[(size_t)t * V + r0 + i] = (float)lg[i];
+  // best of this workgroup: (logit desc, token id asc)
+  auto better = [](double v, int i, double bv, int bi) { return v > bv || (v == bv && i < bi); };
+  uint64_t* am = wsp<uint64_t>(a, a.off.amax);
+  if (wave == 0) {
+    double bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int i = lane; i < nr; i += 64)
+      if (better(lg[i], r0 + i, bv, bi)) { bv = lg[i]; bi = r0 + i; }
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ov = __shfl_xor(bv, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    if (lane == 0) {
+      const uint64_t b = (uint64_t)__double_as_longlong(bv);
+      ll_put(am + 3 * w, (uint32_t)b, k1);
+      ll_put(am + 3 * w + 1, (uint32_t)(b >> 32), k1);
+      ll_put(am + 3 * w + 2, (uint32_t)bi, k1);
+    }
+  }
+  // the global best from every workgroup's candidate (the same token in every workgroup)
+  uint32_t* cand = L.stage;   // [3 * nwg]
+  if (!ll_fetch<per_for(3 * 512)>(cx, cand, am, 3 * nwg, k1, W_AMAX)) return false;
+  if (wave == 0) {
+    double bv = -INFINITY;
+    int bi = 0x7fffffff;
+    for (int g = lane; g < nwg; g += 64) {
+      const double v = __longlong_as_double((long long)(((uint64_t)cand[3 * g + 1] << 32) | cand[3 * g]));
+      const int i = (int)cand[3 * g + 2];
+      if (better(v, i, bv, bi)) { bv = v; bi = i; }
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ov = __shfl_xor(bv, off, 64);
+      const int oi = __shfl_xor(bi, off, 64);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    if (lane == 0) L.isel[0] = bi;
+  }
+  __syncthreads();
+  *token = L.isel[0];
+  __syncthreads();
+  if (w == 0 && tid == 0 && a.out_tokens) gp(a.out_tokens)[t] = *token;
+  stamp(a, cx, st, TR_TOKEN);
+  return true;
+}
+
 template <class SH>
 __global__ void __launch_bounds__(BLOCK, 1) k_decode_gqa(KArgs a) {
   extern __shared__ float lds_raw[];
@@ -1007,6 +1151,7 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_gqa(KArgs a) {
     exp_f64_init(L0.dk);
     __syncthreads();
   }
+  int token = a.in_token;   // greedy decode loop: the token whose embedding feeds the next layer 0
   for (int t = 0; t < a.n_tokens; t++) {
     for (int li = 0; li < a.n_layers; li++) {
       cx.layer = a.layer0 + li;
@@ -1018,6 +1163,7 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_gqa(KArgs a) {
       st.first = (t == 0 && li == 0);
       st.in_hidden = st.first ? a.in_hidden : nullptr;
       st.pos = a.pos0 + t;
+      st.emb_row = (li == 0 && a.head_on && token >= 0) ? a.embed + (size_t)token * SH::H : nullptr;
       const bool last = (t == a.n_tokens - 1) && (li == a.n_layers - 1);
       // The workspace base is made opaque for every step: per-lane addresses derived from
       // it are then recomputed inside the step instead of being hoisted out of the loop
@@ -1035,6 +1181,9 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_gqa(KArgs a) {
       if (!stage_wo<SH>(cx, as, st, L)) return;
       if (!stage_ffn<SH>(cx, as, st, L)) return;
       if (!stage_down<SH>(cx, as, st, L, last ? as.out_hidden : nullptr)) return;
+      if constexpr (SH::FP8) {
+        if (a.head_on && li == a.n_layers - 1 && !stage_head<SH>(cx, as, st, L, t, &token)) return;
+      }
       trace_flush(as, cx, st);
     }
   }
@@ -1097,6 +1246,9 @@ struct pld_handle {
   int device;
   uint64_t* trace;
   int trace_steps;
+  const uint16_t* embed;   // LM head (vocab > 0)
+  const float* fnorm;
+  DMat head;
 };
 
 namespace {
@@ -1198,6 +1350,14 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
   } else {
     return PLD_E_UNSUPPORTED;
   }
+  if (c->vocab < 0) return PLD_E_INVALID;
+  if (c->vocab > 0) {
+    // LM head: FP8 block-scaled [vocab, hidden] on the FP8 shapes; every workgroup owns rows
+    if (c->wfmt != PLD_WFMT_FP8_BLOCK128 || c->vocab < nwg || (c->hidden / 16) % 64) return PLD_E_UNSUPPORTED;
+    if (k->outb_floats < 2 * ((c->vocab + nwg - 1) / nwg) || k->act_floats < 2 * c->hidden ||
+        k->stage_words < 3 * nwg)
+      return PLD_E_UNSUPPORTED;
+  }
   return PLD_OK;
 }
 
@@ -1227,6 +1387,7 @@ WsOff layout(const KCfg& k, int n_layers) {
   } else {
     o.cqr = o.ckvr = o.qr = o.qlat = o.olat = 0;
   }
+  o.amax = p; p += al((size_t)3 * std::max(k.nwg, 1) * W);   // per-workgroup (logit lo, hi, index)
   o.ll_end = p;
   o.sel = p; p += al(64 * 4);
   o.gates = p; p += al(64 * 4);
@@ -1290,7 +1451,10 @@ pld_status decode_layer_init(const pld_config* cfg, int32_t n_layers, const pld_
   KCfg k;
   pld_status st = derive(cfg, nwg, &k);
   if (st != PLD_OK) return st;
-  if (cfg->vocab > 0 || head) return PLD_E_UNSUPPORTED;   // LM head: MLA stack only (not built yet)
+  if ((cfg->vocab > 0) != (head != nullptr)) return PLD_E_INVALID;
+  if (head && (!head->embed || !head->final_norm || !aligned16(head->embed) || !aligned16(head->final_norm) ||
+               !mat_ok(head->head, true)))
+    return PLD_E_INVALID;
   const WsOff off = layout(k, n_layers);
   if (ws_bytes < off.total) return PLD_E_CAPACITY;
   const bool fp8 = cfg->wfmt == PLD_WFMT_FP8_BLOCK128;
@@ -1370,6 +1534,9 @@ pld_status decode_layer_init(const pld_config* cfg, int32_t n_layers, const pld_
   h->last_stream = nullptr;
   h->trace = nullptr;
   h->trace_steps = 0;
+  h->embed = head ? (const uint16_t*)head->embed : nullptr;
+  h->fnorm = head ? head->final_norm : nullptr;
+  if (head) h->head = dmat(head->head, cfg->vocab, H, true);
   const char* coop = getenv("PLD_COOPERATIVE");
   h->coop = coop && atoi(coop) != 0;
   h->fn = pick_kernel(cfg);
@@ -1406,8 +1573,14 @@ pld_status decode_layer_init(const pld_config* cfg, int32_t n_layers, const pld_
   return PLD_OK;
 }
 
+struct HeadArgs {
+  int on, in_token;
+  float* out_logits;
+  int32_t* out_tokens;
+};
+
 static pld_status launch(pld_handle* h, int layer0, int n_layers, int n_tokens, int pos0, const void* in_hidden,
-                         void* out_hidden, hipStream_t s) {
+                         void* out_hidden, hipStream_t s, HeadArgs hd = {0, -1, nullptr, nullptr}) {
   KArgs a;
   memset(&a, 0, sizeof(a));
   a.c = h->kc;
@@ -1423,6 +1596,13 @@ static pld_status launch(pld_handle* h, int layer0, int n_layers, int n_tokens, 
   a.budget = h->budget;
   a.trace = h->trace;
   a.trace_steps = h->trace_steps;
+  a.head_on = hd.on;
+  a.in_token = hd.in_token;
+  a.out_logits = hd.out_logits;
+  a.out_tokens = hd.out_tokens;
+  a.embed = h->embed;
+  a.fnorm = h->fnorm;
+  a.head = h->head;
   hipError_t e;
   if (h->coop) {
     void* args[] = {&a};
@@ -1449,11 +1629,16 @@ pld_status decode_layers_persistent(pld_handle* h, const pld_persistent_args* a,
   if (!h || !a) return PLD_E_INVALID;
   if (h->bad) return PLD_E_STATE;
   if (a->n_tokens < 1 || a->n_query != 1) return a->n_query > 1 ? PLD_E_UNSUPPORTED : PLD_E_INVALID;
-  if (a->in_token >= 0) return PLD_E_UNSUPPORTED;   // embedding input needs the LM head path
-  if (a->n_tokens != 1) return PLD_E_UNSUPPORTED;   // several tokens need the head (greedy loop)
-  if (!a->in_hidden || !a->out_hidden || !aligned16(a->in_hidden) || !aligned16(a->out_hidden)) return PLD_E_INVALID;
+  const bool head = h->cfg.vocab > 0;
+  if (!head && (a->in_token >= 0 || a->n_tokens != 1 || a->out_logits || a->out_tokens))
+    return PLD_E_INVALID;   // embedding input, several tokens and logits/tokens need the LM head
+  if (a->in_token >= h->cfg.vocab && head) return PLD_E_INVALID;
+  if (a->in_token < 0 && (!a->in_hidden || !aligned16(a->in_hidden))) return PLD_E_INVALID;
+  if (!a->out_hidden || !aligned16(a->out_hidden)) return PLD_E_INVALID;
   if (a->start_pos < 0 || a->start_pos + a->n_tokens > h->cfg.max_seq) return PLD_E_CAPACITY;
-  return launch(h, 0, h->n_layers, a->n_tokens, a->start_pos, a->in_hidden, a->out_hidden, (hipStream_t)stream);
+  HeadArgs hd{head ? 1 : 0, head ? a->in_token : -1, a->out_logits, a->out_tokens};
+  return launch(h, 0, h->n_layers, a->n_tokens, a->start_pos, a->in_token >= 0 ? nullptr : a->in_hidden, a->out_hidden,
+                (hipStream_t)stream, hd);
 }
 
 pld_status decode_poll_status(pld_handle* h, pld_device_status* out) {

@@ -549,6 +549,7 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_mla(KArgs a) {
     exp_f64_init(L0.dk);
     __syncthreads();
   }
+  int token = a.in_token;   // greedy decode loop: the token whose embedding feeds the next layer 0
   for (int t = 0; t < a.n_tokens; t++) {
     for (int li = 0; li < a.n_layers; li++) {
       cx.layer = a.layer0 + li;
@@ -560,6 +561,7 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_mla(KArgs a) {
       st.first = (t == 0 && li == 0);
       st.in_hidden = st.first ? a.in_hidden : nullptr;
       st.pos = a.pos0 + t;
+      st.emb_row = (li == 0 && a.head_on && token >= 0) ? a.embed + (size_t)token * SH::H : nullptr;
       const bool last = (t == a.n_tokens - 1) && (li == a.n_layers - 1);
       KArgs as = a;
       asm volatile("" : "+s"(as.ws));
@@ -577,6 +579,9 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_mla(KArgs a) {
       if (!stage_wo<SH>(cx, as, st, L)) return;
       if (!stage_ffn<SH>(cx, as, st, L)) return;
       if (!stage_down<SH>(cx, as, st, L, last ? as.out_hidden : nullptr)) return;
+      if constexpr (SH::FP8) {
+        if (a.head_on && li == a.n_layers - 1 && !stage_head<SH>(cx, as, st, L, t, &token)) return;
+      }
       trace_flush(as, cx, st);
     }
   }

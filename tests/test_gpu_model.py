@@ -1,0 +1,110 @@
+"""GPU parity of the multi-layer greedy decode loop with the LM head.
+
+A stack of FP8 MLA MoE layers (the c5 layer shape) with an FP8 LM head over a vocabulary of
+32768 runs in ONE persistent launch per call: per token, every layer, then RMSNorm + head
+GEMV (fp64 accumulation) + argmax (lowest token id on ties) + the embedding row of the
+chosen token as the next token's input.
+
+Checks:
+* head stage, exact: the oracle's fp64 head on the GPU's own final hidden state picks the
+  same token, and the logits agree to fp64 rounding (the decision is taken in fp64 on
+  both sides);
+* the loop: one launch of n tokens gives bit-identical tokens, logits and hidden state to
+  n chained one-token launches;
+* end to end with teacher forcing: the oracle, fed the same input tokens, gives logits
+  within TOL; where its argmax differs, the two logits it compares are within TOL.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from gpu_common import TOL, host_cache, rel_err, say  # noqa: E402
+from oracle import layer as OL  # noqa: E402
+from oracle import model as OM  # noqa: E402
+from synth import configs, gen  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _model(n_layers, cache_len, n_tokens):
+    L = configs.scaled(configs.C5_LAYER, cache_len=cache_len, max_seq=cache_len + 64)
+    return configs.ModelShape(layer=L, n_layers=n_layers, vocab=32768, n_tokens=n_tokens)
+
+
+def _decoder(m):
+    import persistent_latency_bound_amd as pld
+    from synth import device as sdev
+    Ws = [sdev.layer_weights(m.layer, 0, l) for l in range(m.n_layers)]
+    Cs = [sdev.kv_cache(m.layer, 0, l) for l in range(m.n_layers)]
+    head = {"embed": sdev.embedding(m), "final_norm": sdev.final_norm(m), "head": sdev.head(m)}
+    return pld.Decoder(m.layer, Ws, Cs, head=head, vocab=m.vocab)
+
+
+def _launch(dec, m, pos, tok, n):
+    H, V = m.layer.hidden, m.vocab
+    out = torch.zeros(H, dtype=torch.int16, device="cuda")
+    lg = torch.zeros((n, V), dtype=torch.float32, device="cuda")
+    tk = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    dec.persistent(start_pos=pos, in_token=tok, n_tokens=n, out_hidden=out, out_logits=lg, out_tokens=tk)
+    torch.cuda.synchronize()
+    st = dec.status()
+    assert st.code == 0, f"device status {st.code} wait {st.stage} layer {st.layer} token {st.token} wg {st.wg}"
+    return out.cpu().numpy().view(np.uint16), lg.cpu().numpy(), [int(v) for v in tk.cpu().numpy()]
+
+
+def test_greedy_loop_with_head():
+    _need_gpu()
+    m = _model(n_layers=2, cache_len=100, n_tokens=3)
+    pos, n = 100, 3
+    tok0 = gen.first_token(m)
+    say(f"case: 2-layer FP8 MLA stack + head (vocab {m.vocab}), pos {pos}, {n} tokens from token {tok0}")
+    # chained one-token launches: every token's final hidden state is visible
+    decA = _decoder(m)
+    toks, logits, xs = [], [], []
+    tin = tok0
+    for t in range(n):
+        x, lg, tk = _launch(decA, m, pos + t, tin, 1)
+        toks.append(tk[0])
+        logits.append(lg[0])
+        xs.append(x)
+        tin = tk[0]
+    say(f"tokens (chained launches): {toks}")
+    # one launch of n tokens on fresh caches: identical bits
+    decB = _decoder(m)
+    xB, lgB, tkB = _launch(decB, m, pos, tok0, n)
+    assert tkB == toks, f"one launch {tkB} vs chained {toks}"
+    assert np.array_equal(lgB, np.stack(logits)), "logits differ between one launch and chained launches"
+    assert np.array_equal(xB, xs[-1]), "final hidden state differs"
+    # head stage: oracle fp64 head on the GPU's own hidden state decides the same token
+    head_m = gen.head_matrix(m)
+    fg = gen.final_norm(m)
+    for t in range(n):
+        lo = OM.head_logits(m.layer, head_m, fg, xs[t])
+        e = rel_err(logits[t], lo)
+        say(f"token {t}: head logits rel err {e:.2e} (GPU fp64 -> fp32 output)")
+        assert e < 1e-6, t
+        assert OM.argmax_lowest(lo) == toks[t], f"token {t}: oracle argmax {OM.argmax_lowest(lo)} vs GPU {toks[t]}"
+    # end to end, teacher forced with the GPU's tokens
+    Wl = [gen.LayerWeights(m.layer, 0, l) for l in range(m.n_layers)]
+    caches = [host_cache(m.layer, 0, l) for l in range(m.n_layers)]
+    tin = tok0
+    for t in range(n):
+        x = gen.embedding_rows(m, [tin])[0]
+        for l in range(m.n_layers):
+            rec = OL.decode_layer(m.layer, Wl[l], caches[l], x, pos + t)
+            OL.append_to_cache(m.layer, caches[l], rec, pos + t)
+            x = rec["out_bits"]
+        lo = OM.head_logits(m.layer, head_m, fg, x)
+        e = rel_err(logits[t], lo)
+        to = OM.argmax_lowest(lo)
+        say(f"token {t}: end-to-end logits rel err {e:.2e}; oracle token {to}, GPU token {toks[t]}")
+        assert e < TOL, t
+        if to != toks[t]:
+            assert abs(lo[to] - lo[toks[t]]) <= TOL * np.max(np.abs(lo)), f"token {t}: decisive difference"
+        tin = toks[t]
