@@ -34,6 +34,8 @@ PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 WORKLOADS = {   # name -> (synth.configs attribute, traffic file stem, dtype of the arithmetic)
     "gqa_moe_bf16_decode_layer": ("C2", "traffic_gqa_moe_bf16", "bf16"),
     "mla_moe256_fp8_decode_layer": ("C3", "traffic_mla_moe256_fp8", "fp8-e4m3 weights, fp32 accumulate"),
+    # 24 stacked FP8 MLA layers + FP8 LM head, greedy loop over 256 tokens in one launch
+    "mla_stack24_fp8_greedy256": ("C5", "traffic_mla_stack24_fp8", "fp8-e4m3 weights, fp32 accumulate, fp64 head"),
 }
 DEFAULT_WORKLOAD = "gqa_moe_bf16_decode_layer"
 KERNEL_SOURCES = [os.path.join(ROOT, "persistent_latency_bound_amd", "csrc", f)
@@ -127,6 +129,92 @@ def write_trace_summary(dec, x, out, R, path, pos):
         json.dump(summary, f, indent=1)
 
 
+def run_stack(args):
+    """The multi-layer workload: one launch = n_tokens greedy tokens through every layer and the head."""
+    import torch
+    import persistent_latency_bound_amd as pld
+    from oracle import accounting
+    from synth import configs, device as sdev, gen
+    m = configs.C5
+    L = m.layer
+    pos0, n_tok = L.cache_len, args.tokens
+    Ws = [sdev.layer_weights(L, 0, l) for l in range(m.n_layers)]
+    Cs = [sdev.kv_cache(L, 0, l) for l in range(m.n_layers)]
+    head = {"embed": sdev.embedding(m), "final_norm": sdev.final_norm(m), "head": sdev.head(m)}
+    dec = pld.Decoder(L, Ws, Cs, head=head, vocab=m.vocab)
+    out = torch.zeros(L.hidden, dtype=torch.int16, device="cuda")
+    toks = torch.zeros(n_tok, dtype=torch.int32, device="cuda")
+    tok0 = gen.first_token(m)
+    torch.cuda.synchronize()
+
+    def one():
+        dec.persistent(start_pos=pos0, in_token=tok0, n_tokens=n_tok, out_hidden=out, out_tokens=toks)
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    st = dec.status()
+    if st.code != 0:
+        raise SystemExit(f"device status {st.code} wait {st.stage}")
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t_wall = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        one()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    st = dec.status()
+    if st.code != 0:
+        raise SystemExit(f"device status {st.code} wait {st.stage}")
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    lt = m.n_layers * n_tok
+    us_lt = ms * 1e3 / lt
+    layer_b = sum(accounting.layer_bytes(L, pos0 + t) for t in range(n_tok)) * m.n_layers
+    head_b = accounting.head_bytes(L.hidden, m.vocab) * n_tok
+    achieved = (layer_b + head_b) / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "batch-1 decode us/layer (achieved HBM TB/s vs peak, implied tokens/s/user)",
+        "value": round(us_lt, 3), "unit": "us/layer", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 3), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+        "dtype": WORKLOADS[args.workload][2], "data": "synthetic",
+        "config": {"workload": args.workload, "layers": m.n_layers, "tokens_per_launch": n_tok, "start_pos": pos0,
+                   "vocab": m.vocab, "hidden": L.hidden, "batch": 1},
+        "tokens_per_s_user": round(n_tok / (ms * 1e-3), 1),
+        "us_per_token": round(ms * 1e3 / n_tok, 2),
+        "p90_ms_per_launch": round(per[min(len(per) - 1, int(0.9 * len(per)))], 3),
+        "achieved_TBps": round(achieved / 1e3, 3), "frac_of_peak": round(achieved / PEAK_HBM_GBPS, 4),
+        "algorithmic_bytes_per_launch": int(layer_b + head_b), "launches_per_token": round(1.0 / n_tok, 5),
+        "wall_s_timed_region": round(wall, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None},
+    }
+    if args.trace:
+        # trace the first two tokens (all layers) of one extra launch
+        nwg, _ = dec.launch_shape()
+        nst = 2 * m.n_layers
+        buf = torch.zeros(nst * nwg * TR_SLOTS, dtype=torch.int64, device="cuda")
+        dec.set_trace(buf)
+        one()
+        torch.cuda.synchronize()
+        dec.set_trace(None)
+        import numpy as np
+        t = buf.cpu().numpy().reshape(nst, nwg, TR_SLOTS).astype(np.float64) * 1e-2
+        rows = []
+        for step in range(nst):
+            st0 = t[step, :, 0].min()
+            for slot in range(TR_SLOTS):
+                v = t[step, :, slot]
+                if (v > 0).any():
+                    rows.append({"step": step, "slot": SLOT_NAMES.get(slot, str(slot)),
+                                 "median_us": round(float(np.median(v[v > 0] - st0)), 2)})
+        with open(args.trace, "w") as f:
+            json.dump({"steps": nst, "stamps": rows}, f, indent=0)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +226,7 @@ def main():
                     help="also time decode_step (one layer per launch, launch cost included)")
     ap.add_argument("--trace", default=None, help="write a per-stage device-trace summary (JSON) to this path")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
+    ap.add_argument("--tokens", type=int, default=256, help="tokens per launch (multi-layer workload)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -145,6 +234,9 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is not built.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "mla_stack24_fp8_greedy256":
+        return run_stack(args)
 
     import torch
     import persistent_latency_bound_amd as pld

@@ -1038,8 +1038,11 @@ __device__ __forceinline__ bool stage_head(Ctx& cx, const KArgs& a, const Step& 
   };
 #pragma unroll
   for (int u = 0; u < U; u++) issue(u, u);
-  // input: x of the token's last layer (LL), RMSNorm in fp64
+  // input: x of the token's last layer (LL), RMSNorm in fp64. Stored swizzled: element
+  // (chunk c = 64 j + l, offset e) at ((j * 16 + e) * 64 + l), so that the 64 lanes of a
+  // wave (chunk l of chunk group j) read 64 consecutive doubles (no LDS bank conflicts).
   double* dact = reinterpret_cast<double*>(L.act);   // [H]
+  auto swz = [](int i) { const int c = i >> 4; return ((c >> 6) * 16 + (i & 15)) * 64 + (c & 63); };
   if (!ll_fetch<per_for(H / 2)>(cx, L.stage, wsp<uint64_t>(a, a.off.x), H / 2, k1, W_X)) return false;
   double ss = 0.0;
   for (int i = tid; i < H / 2; i += BLOCK) {
@@ -1055,7 +1058,7 @@ __device__ __forceinline__ bool stage_head(Ctx& cx, const KArgs& a, const Step& 
     if (i < H) {
       const uint32_t v = L.stage[i >> 1];
       const double x = (i & 1) ? bf_hi(v) : bf_lo(v);
-      dact[i] = (x * rr) * (double)gf.v[k];
+      dact[swz(i)] = (x * rr) * (double)gf.v[k];
     }
   }
   __syncthreads();
@@ -1068,17 +1071,17 @@ __device__ __forceinline__ bool stage_head(Ctx& cx, const KArgs& a, const Step& 
       double acc = 0.0;
 #pragma unroll
       for (int j = 0; j < CPL; j++) {
-        const int e0 = (j * 64 + lane) * 16;
+        const double* av = dact + j * 16 * 64 + lane;   // element e of this lane's chunk at av[e * 64]
         const uint32_t d[4] = {buf[u][j].x, buf[u][j].y, buf[u][j].z, buf[u][j].w};
         const double s = (double)sc[u][j];
 #pragma unroll
         for (int q = 0; q < 4; q++) {
           const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)d[q], false);
           const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)d[q], true);
-          acc = fma((double)lo.x * s, dact[e0 + 4 * q + 0], acc);
-          acc = fma((double)lo.y * s, dact[e0 + 4 * q + 1], acc);
-          acc = fma((double)hi.x * s, dact[e0 + 4 * q + 2], acc);
-          acc = fma((double)hi.y * s, dact[e0 + 4 * q + 3], acc);
+          acc = fma((double)lo.x * s, av[(4 * q + 0) * 64], acc);
+          acc = fma((double)lo.y * s, av[(4 * q + 1) * 64], acc);
+          acc = fma((double)hi.x * s, av[(4 * q + 2) * 64], acc);
+          acc = fma((double)hi.y * s, av[(4 * q + 3) * 64], acc);
         }
       }
       issue(u, i + U);
