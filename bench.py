@@ -6,12 +6,15 @@ Workload (default): the single MoE decode layer, batch 1, bf16 — hidden 4096, 
 heads x 128, 8192-token KV cache, router over 64 experts (top-8, softmax renormalised),
 expert SwiGLU width 1536 plus one shared expert; weights N(0, 0.02), router N(0, 0.1).
 --workload mla_moe256_fp8_decode_layer measures the FP8 MLA layer (hidden 6144, 64 heads,
-latent 512+64, 256 experts of width 2048, biased-score router) the same way. A step
+latent 512+64, 256 experts of width 2048, biased-score router) the same way;
+--workload sparse_mla_moe64_bf16_decode_layer the sparse MLA layer (hidden 4096, 32 heads,
+indexer 8x64 with FP8 keys choosing 2048 of the 32769 cached tokens, 64 experts of width
+1536, bf16 weights) at cache position 32768. A step
 decodes one token through a stack of R independent seeded copies of that layer in ONE
 launch of the persistent kernel (decode_layers_persistent). R copies keep the weights
 cold: R x 458 MB is far larger than the 256 MB Infinity Cache, so the bytes come from
 HBM. Each step gets its own seeded input vector (all resident before timing), so the
-routed experts change from step to step. The cache position stays at 8192 (the step
+routed experts change from step to step. The cache position stays at the cache length (the step
 rewrites the same row), so every step does the same work.
 
 Prints ONE JSON line: value = microseconds per layer (lower is better), plus the HBM
@@ -34,6 +37,9 @@ PEAK_HBM_GBPS = 8000.0          # MI355X published HBM3E bandwidth
 WORKLOADS = {   # name -> (synth.configs attribute, traffic file stem, dtype of the arithmetic)
     "gqa_moe_bf16_decode_layer": ("C2", "traffic_gqa_moe_bf16", "bf16"),
     "mla_moe256_fp8_decode_layer": ("C3", "traffic_mla_moe256_fp8", "fp8-e4m3 weights, fp32 accumulate"),
+    # sparse MLA: indexer (fp64 scores over every cached token) + top-2048 attention, bf16 weights
+    "sparse_mla_moe64_bf16_decode_layer": ("C4", "traffic_sparse_mla_moe64_bf16",
+                                           "bf16 weights, fp32 accumulate; indexer scores fp64"),
     # 24 stacked FP8 MLA layers + FP8 LM head, greedy loop over 256 tokens in one launch
     "mla_stack24_fp8_greedy256": ("C5", "traffic_mla_stack24_fp8", "fp8-e4m3 weights, fp32 accumulate, fp64 head"),
 }
@@ -90,7 +96,8 @@ SLOT_NAMES = {32: "head_ready", 33: "head_gemv", 34: "token", 0: "start", 1: "x_
               7: "h2_ready", 8: "router_ready", 9: "ffn_done", 10: "m_ready", 11: "down_done", 12: "att_q",
               13: "att_softmax", 14: "att_partial", 15: "att_merged", 16: "topk", 18: "m_stored", 19: "down_gemv",
               20: "down_epi", 21: "qkv_gemv", 22: "shared_gemv", 23: "att_pv", 24: "x_normed", 25: "merge_start",
-              26: "merge_fetched", 27: "router_logit", 28: "att_drained", 30: "att_scores", 17: "blk0_staged", 31: "blk0_done"}
+              26: "merge_fetched", 27: "router_logit", 28: "att_drained", 30: "att_scores", 17: "blk0_staged", 31: "blk0_done",
+              35: "idx_done", 36: "sel_keys", 37: "sel_passes", 38: "sel_done"}
 
 
 def write_trace_summary(dec, x, out, R, path, pos):
@@ -326,7 +333,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "hidden": shape.hidden,
                    "attention": (f"GQA {shape.n_heads}q/{shape.n_kv_heads}kv x {shape.head_dim}" if shape.attn == "gqa" else
-                                 f"MLA {shape.n_heads} heads, latent {shape.kv_lora}+{shape.rope_dim}, q_lora {shape.q_lora}"),
+                                 f"MLA {shape.n_heads} heads, latent {shape.kv_lora}+{shape.rope_dim}, q_lora {shape.q_lora}"
+                                 + (f", indexer {shape.index_heads}x{shape.index_dim} top-{shape.index_topk}"
+                                    if shape.index_topk else "")),
                    "weights": shape.wfmt, "kv_cache_tokens": pos,
                    "experts": f"{shape.n_experts} top-{shape.top_k} + {shape.n_shared} shared ({shape.router})",
                    "expert_inter": shape.inter, "layers_per_launch": R, "tokens_per_step": 1, "batch": 1},

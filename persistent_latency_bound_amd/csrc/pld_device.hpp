@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace pld {
 
 constexpr int BLOCK = 512;
@@ -45,6 +47,14 @@ template <typename T>
 __device__ __forceinline__ PLD_GLOBAL T* gp(T* p) { return (PLD_GLOBAL T*)(p); }
 template <typename T>
 __device__ __forceinline__ const PLD_GLOBAL T* gp(const T* p) { return (const PLD_GLOBAL T*)(p); }
+// The same for LDS (atomics then compile to ds_* instead of flat_* instructions).
+#if defined(__HIP_DEVICE_COMPILE__)
+#define PLD_LDS __attribute__((address_space(3)))
+#else
+#define PLD_LDS
+#endif
+template <typename T>
+__device__ __forceinline__ PLD_LDS T* lds_ptr(T* p) { return (PLD_LDS T*)(p); }
 
 // tid_opaque() as a value the compiler cannot treat as loop-invariant: per-lane addresses
 // computed from it inside a helper are then not hoisted out of the layer loop, where they
@@ -114,6 +124,45 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
+// fp64 -> bf16, round to nearest even in ONE rounding (going through fp32 would round
+// twice): the 45 low mantissa bits are rounded away on the fp64 bit pattern, after
+// which the value has 8 significant bits and converts to fp32 exactly. Finite values in
+// the fp32 normal range.
+__device__ __forceinline__ uint32_t f64_to_bf16(double x) {
+  uint64_t b = (uint64_t)__double_as_longlong(x);
+  b += 0x00000FFFFFFFFFFFull + ((b >> 45) & 1ull);
+  b &= ~0x00001FFFFFFFFFFFull;
+  return __float_as_uint((float)__longlong_as_double((long long)b)) >> 16;
+}
+// fp32 -> OCP E4M3FN code, round to nearest with ties to the even code, for |q| <= 448
+// (no saturation or NaN handling needed in that range). Normal codes keep 3 mantissa
+// bits of q's fp32 significand; below 2^-6 the grid is the subnormal step 2^-9, reached
+// from the 24-bit significand by a right shift of 14 - e. A value that rounds up to the
+// next binade lands on its code because code = (biased exponent << 3) + mantissa is
+// continuous. The sign bit is kept for values that round to zero.
+__device__ __forceinline__ uint32_t e4m3_encode(float q) {
+  const uint32_t u = __float_as_uint(q);
+  const uint32_t sgn = (u >> 24) & 0x80u;
+  const uint32_t mag = u & 0x7fffffffu;
+  const int e = (int)(mag >> 23) - 127;
+  const uint32_t full = (mag & 0x7fffffu) | 0x800000u;
+  uint32_t code;
+  if (e >= -6) {
+    uint32_t q3 = (mag >> 20) & 7u;
+    const uint32_t rem = mag & 0xfffffu;
+    q3 += (rem > 0x80000u || (rem == 0x80000u && (q3 & 1u))) ? 1u : 0u;
+    code = ((uint32_t)(e + 7) << 3) + q3;
+  } else if (e >= -10) {
+    const int sh = 14 - e;   // 21 .. 24
+    uint32_t qq = full >> sh;
+    const uint32_t rem = full & ((1u << sh) - 1u), half = 1u << (sh - 1);
+    qq += (rem > half || (rem == half && (qq & 1u))) ? 1u : 0u;
+    code = qq;
+  } else {
+    code = 0u;   // below half of the smallest subnormal step (fp32 zero and denormals included)
+  }
+  return sgn | code;
+}
 
 // ----------------------------------------------------------------- reductions
 template <typename T>
@@ -158,15 +207,18 @@ __device__ __forceinline__ double dpp_mov_f64(double x) {
   const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, ROW_MASK, 0xf, BOUND);
   return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
 }
-__device__ __forceinline__ double dpp_sum64_f64(double v) {
+template <int N>
+__device__ __forceinline__ double dpp_sum_f64(double v) {
+  static_assert(N == 8 || N == 16 || N == 32 || N == 64, "group size");
   v += dpp_mov_f64<0xB1, 0xf, false>(v);
   v += dpp_mov_f64<0x4E, 0xf, false>(v);
   v += dpp_mov_f64<0x141, 0xf, false>(v);
-  v += dpp_mov_f64<0x140, 0xf, false>(v);
-  v += dpp_mov_f64<0x142, 0xa, true>(v);
-  v += dpp_mov_f64<0x143, 0xc, true>(v);
+  if constexpr (N >= 16) v += dpp_mov_f64<0x140, 0xf, false>(v);
+  if constexpr (N >= 32) v += dpp_mov_f64<0x142, 0xa, true>(v);
+  if constexpr (N >= 64) v += dpp_mov_f64<0x143, 0xc, true>(v);
   return v;
 }
+__device__ __forceinline__ double dpp_sum64_f64(double v) { return dpp_sum_f64<64>(v); }
 
 // Wave-wide max and sum with DPP lane moves (no LDS permutes), result in every lane.
 // The moves keep a lane's own value where a move does not write it (old = the value,
@@ -314,9 +366,13 @@ constexpr int MAX_SEGS = 12;
 //  * partial sums are reduced across the LPR lanes and the row's first lane writes the
 //    result into out[i] (LDS) per OutMode.
 // `segs` lives in LDS. Returns false if pre() reported an abort.
-template <bool FP8, int K, int INFL, typename Pre>
+//  * ACC64 (bf16 weights only): products and sums in fp64 (bf16 x fp32 products are exact
+//    there) and fp64 results, stored to ((double*)out)[i] (OUT_STORE only).
+template <bool FP8, int K, int INFL, bool ACC64 = false, typename Pre>
 __device__ __forceinline__ bool gemv_list(const RowSeg* segs, int nseg, const float* act, float* out, int mode,
                                           Pre&& pre) {
+  static_assert(!(ACC64 && FP8), "fp64 accumulation is for bf16 weights");
+  using AccT = typename std::conditional<ACC64, double, float>::type;
   using LY = GemvLayout<FP8, K, INFL>;
   constexpr int EPC = LY::EPC, LPR = LY::LPR, CPL = LY::CPL, U = LY::U;
   constexpr int RPW = 64 / LPR;
@@ -383,7 +439,7 @@ __device__ __forceinline__ bool gemv_list(const RowSeg* segs, int nseg, const fl
       const float* a = act + S.act_off;
       const float alpha = S.alpha;
       const int oi = i;
-      float acc = 0.f;
+      AccT acc = 0;
 #pragma unroll
       for (int j = 0; j < CPL; j++) {
         float at[EPC];
@@ -394,6 +450,7 @@ __device__ __forceinline__ bool gemv_list(const RowSeg* segs, int nseg, const fl
           at[4 * q] = t.x; at[4 * q + 1] = t.y; at[4 * q + 2] = t.z; at[4 * q + 3] = t.w;
         }
         if constexpr (FP8) acc += sc[u][j] * dot16_fp8(buf[u][j], at);
+        else if constexpr (ACC64) acc += dot8_bf16_f64(buf[u][j], at);
         else acc += dot8_bf16(buf[u][j], at);
       }
       if (cur + U < iters) {
@@ -401,10 +458,15 @@ __device__ __forceinline__ bool gemv_list(const RowSeg* segs, int nseg, const fl
         issue(u);
       }
       advance(cc, STEP);
-      acc = dpp_sum<LPR>(acc);
-      if (li == LPR - 1 && cur < iters && oi < nrows) {
-        if (mode == OUT_STORE) out[oi] = acc;
-        else out[oi] += alpha * acc;
+      if constexpr (ACC64) {
+        acc = dpp_sum_f64<LPR>(acc);
+        if (li == LPR - 1 && cur < iters && oi < nrows) reinterpret_cast<double*>(out)[oi] = acc;
+      } else {
+        acc = dpp_sum<LPR>(acc);
+        if (li == LPR - 1 && cur < iters && oi < nrows) {
+          if (mode == OUT_STORE) out[oi] = acc;
+          else out[oi] += alpha * acc;
+        }
       }
     }
   }

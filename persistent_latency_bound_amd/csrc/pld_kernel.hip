@@ -42,7 +42,7 @@ namespace pld {
 // ------------------------------------------------------------------ shared structs
 // Watchdog wait ids (pld_device_status.stage): which LL activation a workgroup waited for.
 enum WaitId { W_X = 0, W_QKV = 1, W_KV = 2, W_PART = 3, W_O = 4, W_H2 = 5, W_RT = 6, W_M = 7, W_CQ = 8,
-              W_QN = 9, W_QLAT = 10, W_OLAT = 11, W_AMAX = 12 };
+              W_QN = 9, W_QLAT = 10, W_OLAT = 11, W_AMAX = 12, W_IX = 13, W_IDONE = 14, W_ISEL = 15 };
 enum { ST_CODE = 0, ST_STAGE = 1, ST_LAYER = 2, ST_TOKEN = 3, ST_WG = 4, ST_ABORT = 8 };
 // device trace: wall-clock stamps per (step, workgroup)
 enum TraceSlot {
@@ -51,7 +51,8 @@ enum TraceSlot {
   TR_ATT_MERGED = 15, TR_TOPK = 16, TR_ROUTED_GEMV = 17, TR_M_STORED = 18, TR_DOWN_GEMV = 19, TR_DOWN_EPI = 20,
   TR_QKV_GEMV = 21, TR_SHARED_GEMV = 22, TR_ATT_PV = 23, TR_X_NORMED = 24, TR_MERGE_START = 25,
   TR_MERGE_COPIED = 26, TR_RT_LOGIT = 27, TR_ATT_DRAINED = 28, TR_ATT_SCORES = 30, TR_HEAD_READY = 32,
-  TR_HEAD_GEMV = 33, TR_TOKEN = 34, TR_SLOTS = 48
+  TR_HEAD_GEMV = 33, TR_TOKEN = 34, TR_IDX_DONE = 35, TR_SEL_KEYS = 36, TR_SEL_PASSES = 37, TR_SEL_DONE = 38,
+  TR_SLOTS = 48
 };
 
 struct KCfg {
@@ -83,8 +84,8 @@ struct DLayer {
 // Workspace layout. The LL buffers (8-byte words: payload | epoch << 32) follow the
 // status words; both are zeroed at init and by decode_reset.
 struct WsOff {
-  size_t status, x, q, kv, part, o, h2, logits, m, cqr, ckvr, qr, qlat, olat, amax, ll_end, sel, gates, a_dbg, b_dbg,
-      rope, layers, total;
+  size_t status, x, q, kv, part, o, h2, logits, m, cqr, ckvr, qr, qlat, olat, amax, ixr, qi, idone, isel, ll_end, sel,
+      gates, a_dbg, b_dbg, ikh, ikl, rope, layers, total;
 };
 
 struct KArgs {
@@ -1203,6 +1204,9 @@ using ShapeGqaMoe = GqaShape<4096, 32, 8, 128, 1536, false, true, 9, 33>;
 // the FP8 MLA MoE layer: hidden 6144, 64 heads, q_lora 1536, kv_lora 512 + rope 64,
 // nope 128, v 128, 256 experts of width 2048 (biased-score router)
 using ShapeMlaFp8 = MlaShape<6144, 64, 1536, 512, 64, 128, 128, 2048, true, true, false>;
+// the sparse MLA MoE layer: hidden 4096, 32 heads, the same latent sizes, bf16 weights,
+// indexer of 8 heads x 64 dims, 64 experts of width 1536 (softmax router)
+using ShapeSparseMla = MlaShape<4096, 32, 1536, 512, 64, 128, 128, 1536, false, true, true, 8, 64>;
 
 template <class SH>
 static bool matches(const pld_config* c) {
@@ -1216,13 +1220,15 @@ static bool matches_mla(const pld_config* c) {
   return c->attn_kind == PLD_ATTN_MLA && c->hidden == SH::H && c->n_heads == SH::NH && c->q_lora == SH::QL &&
          c->kv_lora == SH::KL && c->rope_dim == SH::RD && c->nope_dim == SH::ND && c->v_dim == SH::VD &&
          c->inter == SH::INTER && (c->wfmt == PLD_WFMT_FP8_BLOCK128) == SH::FP8 &&
-         (c->ffn_kind == PLD_FFN_MOE) == SH::MOE && (c->index_topk > 0) == SH::SPARSE;
+         (c->ffn_kind == PLD_FFN_MOE) == SH::MOE && (c->index_topk > 0) == SH::SPARSE &&
+         (!SH::SPARSE || (c->index_heads == SH::IH && c->index_dim == SH::ID));
 }
 
 static KernelFn pick_kernel(const pld_config* c) {
   if (matches<ShapeTinyDense>(c)) return k_decode_gqa<ShapeTinyDense>;
   if (matches<ShapeGqaMoe>(c)) return k_decode_gqa<ShapeGqaMoe>;
   if (matches_mla<ShapeMlaFp8>(c)) return k_decode_mla<ShapeMlaFp8>;
+  if (matches_mla<ShapeSparseMla>(c)) return k_decode_mla<ShapeSparseMla>;
   return nullptr;
 }
 
@@ -1336,16 +1342,33 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
     if ((NH * VD) % nwg || VD % (NH * VD / nwg)) return PLD_E_UNSUPPORTED;
     // one LL buffer per activation: every workgroup publishes rows in every stage
     if (c->q_lora + LAT < nwg || c->inter < nwg || c->hidden / 2 < nwg) return PLD_E_UNSUPPORTED;
+    const bool sparse = c->index_topk > 0;
     const int TB = 32, CSTR = LAT + 4;
-    const int attn_bytes = 2 * 16 * CSTR + 2 * 2 * TB * CSTR + 2 * 16 * TB + 4 * (8 * 256 + 16) + 2 * LAT + 4 * LAT;
+    // sparse: the chunk's selected-row list follows the attention scratch
+    const int srows_max = sparse ? (std::min(c->index_topk, c->max_seq) + k->cpg - 1) / k->cpg : 0;
+    const int attn_bytes = 2 * 16 * CSTR + 2 * 2 * TB * CSTR + 2 * 16 * TB + 4 * (8 * 256 + 16) + 2 * LAT + 4 * LAT +
+                           4 * srows_max;
     const int nope_rows = std::min(c->nope_dim, 4 * (BLOCK / (k->cpw / epc)));
     int act = std::max({c->hidden, c->q_lora, k->slots * c->inter, (attn_bytes + 3) / 4 + 16,
                         c->nope_dim + (BLOCK / (k->cpw / epc)) * k->cpw + nope_rows,
                         k->cpg * k->cpw + 4 * k->cpg + 8});
+    if (sparse) {
+      // indexer: 8 heads x 64 dims (4 lanes x 2 heads per token); selection keys per thread;
+      // one workgroup's done-word fetch; selected rows per chunk (LL fetch, one pass)
+      if (c->index_heads != 8 || c->index_dim != 64 || c->index_topk < 1) return PLD_E_UNSUPPORTED;
+      if (c->max_seq > SEL_MAXJ * BLOCK || nwg > BLOCK || srows_max > BLOCK || srows_max > 8 * TB)
+        return PLD_E_UNSUPPORTED;
+      const int idx_words = 2 * (c->index_heads * c->index_dim + c->index_heads) + c->index_heads * c->index_dim / 2 +
+                            c->index_heads + c->index_dim + c->index_dim / 4 + 1;
+      act = std::max({act, 3 * c->q_lora, SEL_LDS_WORDS, idx_words});
+      if (c->q_lora + LAT + c->index_heads + c->index_dim < nwg) return PLD_E_UNSUPPORTED;
+    }
     k->act_floats = (int)al(act, 64);
     k->stage_words = (int)al(c->hidden / 2 + 2, 64);
-    const int rx = c->q_lora + LAT, rq = NH * (c->nope_dim + c->rope_dim);
-    int outb = std::max({rx / nwg + 4, rq / nwg + 4, NH * VD / nwg + 4, c->hidden / nwg + 4,
+    const int rx = c->q_lora + LAT + (sparse ? c->index_heads + c->index_dim : 0);
+    const int rq = NH * (c->nope_dim + c->rope_dim) + (sparse ? c->index_heads * c->index_dim : 0);
+    const int f64x = sparse ? 2 : 1;   // fp64 row results take two floats
+    int outb = std::max({f64x * (rx / nwg + 4), f64x * (rq / nwg + 4), NH * VD / nwg + 4, c->hidden / nwg + 4,
                          k->slots * (c->hidden / nwg + 4), 2 * ((k->slots * c->inter) / nwg + 2),
                          2 * (c->inter / nwg + 2) * std::max(1, c->n_shared), 4 * c->n_experts + 4});
     k->outb_floats = (int)al(outb, 64);
@@ -1381,7 +1404,7 @@ WsOff layout(const KCfg& k, int n_layers) {
     const size_t LAT = (size_t)k.kv_lora + k.rope;
     o.q = p; p += al((size_t)k.nh * k.nope * W);                     // q_nope
     o.qr = p; p += al((size_t)k.nh * k.rope * W);                    // q_rope (rotated)
-    o.cqr = p; p += al((size_t)k.q_lora * W);                        // c_q before its RMSNorm
+    o.cqr = p; p += al((size_t)2 * k.q_lora * W);                    // c_q before its RMSNorm (fp64: 2 words)
     o.ckvr = p; p += al(LAT * W);                                    // c_kv and k_rope before norm / RoPE
     o.qlat = p; p += al((size_t)k.nh * k.kv_lora * W);
     o.part = p; p += al((size_t)k.nh * k.cpg * (k.kv_lora + 2) * W);
@@ -1391,11 +1414,25 @@ WsOff layout(const KCfg& k, int n_layers) {
     o.cqr = o.ckvr = o.qr = o.qlat = o.olat = 0;
   }
   o.amax = p; p += al((size_t)3 * std::max(k.nwg, 1) * W);   // per-workgroup (logit lo, hi, index)
+  if (k.itopk > 0) {
+    o.ixr = p; p += al((size_t)(k.ih + k.idim) * W);       // indexer head weights w and new key k_I (fp32)
+    o.qi = p; p += al((size_t)(k.ih * k.idim / 2) * W);    // indexer queries (bf16 pairs)
+    o.idone = p; p += al((size_t)k.nwg * W);               // per-workgroup "keys stored"
+    o.isel = p; p += al((size_t)k.itopk * W);              // selected rows, ascending
+  } else {
+    o.ixr = o.qi = o.idone = o.isel = 0;
+  }
   o.ll_end = p;
   o.sel = p; p += al(64 * 4);
   o.gates = p; p += al(64 * 4);
   o.a_dbg = p; p += al((size_t)k.H * 4);
   o.b_dbg = p; p += al((size_t)k.H * 4);
+  if (k.itopk > 0) {
+    o.ikh = p; p += al((size_t)k.max_seq * 4);   // indexer score keys, high and low halves
+    o.ikl = p; p += al((size_t)k.max_seq * 4);
+  } else {
+    o.ikh = o.ikl = 0;
+  }
   o.rope = p; p += al((size_t)k.max_seq * std::max(k.rdim, 2) * 4);
   o.layers = p; p += al((size_t)n_layers * sizeof(DLayer));
   o.total = p;
@@ -1494,6 +1531,13 @@ pld_status decode_layer_init(const pld_config* cfg, int32_t n_layers, const pld_
       d.w_uk = dmat(L.w_uk, NH * ND, KL, fp8);
       d.w_uv = dmat(L.w_uv, NH * VD, KL, fp8);
       d.wo = dmat(L.wo, H, NH * VD, fp8);
+      if (cfg->index_topk > 0) {
+        const int IH = cfg->index_heads, ID = cfg->index_dim;
+        if (!mat_ok(L.w_qi, fp8) || !mat_ok(L.w_w, false) || !mat_ok(L.w_ki, fp8)) return PLD_E_INVALID;
+        d.w_qi = dmat(L.w_qi, IH * ID, QL, fp8);
+        d.w_w = dmat(L.w_w, IH, H, false);
+        d.w_ki = dmat(L.w_ki, ID, H, fp8);
+      }
     }
     if (!mat_ok(L.w_gate, fp8) || !mat_ok(L.w_up, fp8) || !mat_ok(L.w_down, fp8)) return PLD_E_INVALID;
     d.w_gate = dmat(L.w_gate, cfg->inter, H, fp8);
@@ -1520,6 +1564,12 @@ pld_status decode_layer_init(const pld_config* cfg, int32_t n_layers, const pld_
     } else {
       if (!C.latent || !aligned16(C.latent)) return PLD_E_INVALID;
       d.lat = (uint16_t*)C.latent;
+      if (cfg->index_topk > 0) {
+        if (!C.index_codes || !C.index_scales || !aligned16(C.index_codes) || !aligned16(C.index_scales))
+          return PLD_E_INVALID;
+        d.icodes = (uint8_t*)C.index_codes;
+        d.iscales = C.index_scales;
+      }
     }
   }
   pld_handle* h = new (std::nothrow) pld_handle();
@@ -1689,11 +1739,16 @@ pld_status pld_debug_buffer(pld_handle* h, const char* name, void** ptr, size_t*
       {"gates", h->off.gates, (size_t)k.topk * 4},
       {"m", h->off.m, (size_t)k.slots * k.inter * 8},
       {"x", h->off.x, (size_t)k.H * 4},
-      {"cq", h->off.cqr, (size_t)k.q_lora * 8},
+      {"cq", h->off.cqr, (size_t)k.q_lora * (k.itopk > 0 ? 2 : 1) * 8},
       {"ckv", h->off.ckvr, (size_t)(k.kv_lora + k.rope) * 8},
       {"qrope", h->off.qr, (size_t)k.nh * k.rope * 8},
       {"qlat", h->off.qlat, (size_t)k.nh * k.kv_lora * 8},
       {"olat", h->off.olat, (size_t)k.nh * k.kv_lora * 8},
+      {"qi", h->off.qi, (size_t)k.ih * k.idim / 2 * 8},
+      {"ixr", h->off.ixr, (size_t)(k.ih + k.idim) * 8},
+      {"isel", h->off.isel, (size_t)k.itopk * 8},
+      {"ikh", h->off.ikh, (size_t)k.max_seq * 4},
+      {"ikl", h->off.ikl, (size_t)k.max_seq * 4},
   };
   for (auto& e : tab)
     if (!strcmp(e.n, name)) {

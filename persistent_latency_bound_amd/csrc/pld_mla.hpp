@@ -14,10 +14,13 @@
 // (attention over the compressed latent with the up-projections folded into q and o).
 #pragma once
 
-template <int H_, int NH_, int QL_, int KL_, int RD_, int ND_, int VD_, int INTER_, bool FP8_, bool MOE_, bool SPARSE_>
+template <int H_, int NH_, int QL_, int KL_, int RD_, int ND_, int VD_, int INTER_, bool FP8_, bool MOE_, bool SPARSE_,
+          int IH_ = 0, int ID_ = 0>
 struct MlaShape {
   static constexpr int H = H_, NH = NH_, QL = QL_, KL = KL_, RD = RD_, ND = ND_, VD = VD_, INTER = INTER_;
   static constexpr bool FP8 = FP8_, MOE = MOE_, SPARSE = SPARSE_;
+  static constexpr int IH = IH_, ID = ID_;        // indexer heads and key width (sparse layers)
+  static_assert(!SPARSE || (!FP8 && IH > 0 && ID > 0), "the sparse layer has bf16 weights and an indexer");
   static constexpr int LAT = KL + RD, QH = ND + RD, ODIM = NH * VD;
   static constexpr int HPW = 8, NHG = NH / HPW;   // heads per attention workgroup, head groups
   static constexpr int TB = 32;                   // latent rows per attention sub-block
@@ -37,12 +40,16 @@ __device__ __forceinline__ uint4 ld_coh16(const void* p) {
   return make_uint4((uint32_t)x, (uint32_t)(x >> 32), (uint32_t)y, (uint32_t)(y >> 32));
 }
 
-// ------------------------------------------------------------------ X: RMSNorm + [W_DQ ; W_DKV]
+// ------------------------------------------------------------------ X: RMSNorm + [W_DQ ; W_DKV (; W_w ; W_kI)]
+// The sparse layer accumulates these rows in fp64: c_q' feeds the indexer's selection,
+// an integer result, so it travels as fp64 (two LL words per value) and the indexer head
+// weights w and key k_I are rounded to fp32 once, from fp64 sums.
 template <class SH>
 __device__ __forceinline__ bool stage_x_mla(Ctx& cx, const KArgs& a, const Step& st, Lds& L) {
   const DLayer Ly = *gp(st.Ly);
   const int w = cx.w, nwg = cx.nwg;
-  constexpr int R = SH::QL + SH::LAT;
+  constexpr int NIX = SH::SPARSE ? SH::IH + SH::ID : 0;
+  constexpr int R = SH::QL + SH::LAT + NIX;
   constexpr size_t RB = (size_t)SH::H * (SH::FP8 ? 1 : 2);
   const int r0 = split_at(R, nwg, w), r1 = split_at(R, nwg, w + 1);
   int h0, h1;
@@ -55,41 +62,91 @@ __device__ __forceinline__ bool stage_x_mla(Ctx& cx, const KArgs& a, const Step&
     pending = false;
     return layer_input<SH::H>(cx, a, st, L, gam, h0, h1);
   };
-  seg_begin();
-  int ns = 0;
-  if (r0 < SH::QL) {
-    seg_set(L, ns, Ly.w_dq.w + (size_t)r0 * RB, Ly.w_dq.s, min(r1, SH::QL) - r0, r0, 0, 1.f);
-    ns++;
+  {
+    constexpr int NM = SH::SPARSE ? 4 : 2;
+    const DMat* mats[4] = {&Ly.w_dq, &Ly.w_dkv, &Ly.w_w, &Ly.w_ki};
+    constexpr int b[5] = {0, SH::QL, SH::QL + SH::LAT, SH::QL + SH::LAT + SH::IH, R};
+    seg_begin();
+    int ns = 0;
+#pragma unroll
+    for (int m = 0; m < NM; m++) {
+      const int lo = max(r0, b[m]), hi = min(r1, b[m + 1]);
+      if (lo < hi) {
+        seg_set(L, ns, mats[m]->w + (size_t)(lo - b[m]) * RB, mats[m]->s, hi - lo, lo - b[m], 0, 1.f);
+        ns++;
+      }
+    }
+    seg_end();
+    if (!gemv_list<SH::FP8, SH::H, PLD_IF_QKV, SH::SPARSE>(L.segs, ns, L.act, L.outb, OUT_STORE, pre_x)) return false;
   }
-  if (r1 > SH::QL) {
-    const int lo = max(r0, SH::QL) - SH::QL;
-    seg_set(L, ns, Ly.w_dkv.w + (size_t)lo * RB, Ly.w_dkv.s, r1 - max(r0, SH::QL), lo, 0, 1.f);
-    ns++;
-  }
-  seg_end();
-  if (!gemv_list<SH::FP8, SH::H, PLD_IF_QKV>(L.segs, ns, L.act, L.outb, OUT_STORE, pre_x)) return false;
   stamp(a, cx, st, TR_QKV_GEMV);
   if (!pre_x()) return false;
   __syncthreads();
   uint64_t* cqr = wsp<uint64_t>(a, a.off.cqr);
   uint64_t* ckvr = wsp<uint64_t>(a, a.off.ckvr);
   for (int r = r0 + tid_opaque(); r < r1; r += BLOCK) {
-    const float v = L.outb[r - r0];
-    if (r < SH::QL) ll_put_f32(cqr + r, v, st.k1);
-    else ll_put_f32(ckvr + (r - SH::QL), v, st.k1);
+    if constexpr (SH::SPARSE) {
+      const double v = reinterpret_cast<const double*>(L.outb)[r - r0];
+      if (r < SH::QL) {
+        const uint64_t bits = (uint64_t)__double_as_longlong(v);
+        ll_put(cqr + 2 * r, (uint32_t)bits, st.k1);
+        ll_put(cqr + 2 * r + 1, (uint32_t)(bits >> 32), st.k1);
+      } else if (r < SH::QL + SH::LAT) {
+        ll_put_f32(ckvr + (r - SH::QL), (float)v, st.k1);
+      } else {
+        ll_put_f32(wsp<uint64_t>(a, a.off.ixr) + (r - SH::QL - SH::LAT), (float)v, st.k1);
+      }
+    } else {
+      const float v = L.outb[r - r0];
+      if (r < SH::QL) ll_put_f32(cqr + r, v, st.k1);
+      else ll_put_f32(ckvr + (r - SH::QL), v, st.k1);
+    }
   }
   stamp(a, cx, st, TR_QKV_DONE);
   return true;
 }
 
-// ------------------------------------------------------------------ Q: RMSNorm(c_q) + W_UQ + RoPE
+// RMSNorm of an fp64 vector held as (lo, hi) 32-bit word pairs in LDS, written as fp32:
+// dst[i] = fp32((x_i * r) * gamma_i), r = 1/sqrt(sum(x^2)/N + eps), all in fp64.
+template <int N>
+__device__ __forceinline__ void rmsnorm_f64src(float* dst, const uint32_t* src, const RegVec<N>& gam, double eps,
+                                               double* red) {
+  auto x_at = [&](int i) -> double {
+    return __longlong_as_double((long long)(((uint64_t)src[2 * i + 1] << 32) | src[2 * i]));
+  };
+  double ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < RegVec<N>::K; k++) {
+    const int i = tid_opaque() + k * BLOCK;
+    if (i < N) {
+      const double x = x_at(i);
+      ss += x * x;
+    }
+  }
+  ss = block_sum(ss, red);
+  const double r = 1.0 / sqrt(ss / (double)N + eps);
+#pragma unroll
+  for (int k = 0; k < RegVec<N>::K; k++) {
+    const int i = tid_opaque() + k * BLOCK;
+    if (i < N) dst[i] = (float)((x_at(i) * r) * (double)gam.v[k]);
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ Q: RMSNorm(c_q) + W_UQ (+ W_qI) + RoPE
+// Sparse layer: c_q' arrives in fp64 and is normalised to fp32 exactly as the indexer's
+// definition has it; the W_qI rows (indexer queries) accumulate in fp64 and are rounded
+// to bf16 once, from the fp64 sum.
 template <class SH>
 __device__ __forceinline__ bool stage_q_mla(Ctx& cx, const KArgs& a, const Step& st, Lds& L) {
   const KCfg& c = a.c;
   const DLayer Ly = *gp(st.Ly);
   const int w = cx.w, nwg = cx.nwg;
-  constexpr int R = SH::NH * SH::QH;
+  constexpr int RQ = SH::NH * SH::QH;
+  constexpr int NQI = SH::SPARSE ? SH::IH * SH::ID : 0;
+  constexpr int R = RQ + NQI;
   constexpr size_t RB = (size_t)SH::QL * (SH::FP8 ? 1 : 2);
+  static_assert(RQ % 2 == 0 && NQI % 2 == 0, "row pairs");
   const int r0 = 2 * split_at(R / 2, nwg, w), r1 = 2 * split_at(R / 2, nwg, w + 1);
   RegVec<SH::QL> gq;
   gq.load(Ly.q_norm);
@@ -97,25 +154,50 @@ __device__ __forceinline__ bool stage_q_mla(Ctx& cx, const KArgs& a, const Step&
   auto pre_q = [&]() -> bool {
     if (!pending) return true;
     pending = false;
-    if (!ll_fetch<per_for(SH::QL)>(cx, reinterpret_cast<uint32_t*>(L.act), wsp<uint64_t>(a, a.off.cqr), SH::QL, st.k1,
-                                   W_CQ))
-      return false;
-    rmsnorm_reg<SH::QL>(L.act, gq, c.eps, L.red);
+    if constexpr (SH::SPARSE) {
+      uint32_t* raw = reinterpret_cast<uint32_t*>(L.act + SH::QL);   // [2*QL] fp64 words
+      if (!ll_fetch<per_for(2 * SH::QL)>(cx, raw, wsp<uint64_t>(a, a.off.cqr), 2 * SH::QL, st.k1, W_CQ)) return false;
+      rmsnorm_f64src<SH::QL>(L.act, raw, gq, c.eps, L.red);
+    } else {
+      if (!ll_fetch<per_for(SH::QL)>(cx, reinterpret_cast<uint32_t*>(L.act), wsp<uint64_t>(a, a.off.cqr), SH::QL,
+                                     st.k1, W_CQ))
+        return false;
+      rmsnorm_reg<SH::QL>(L.act, gq, c.eps, L.red);
+    }
     stamp(a, cx, st, TR_ATT_READY);
     return true;
   };
   seg_begin();
-  seg_set(L, 0, Ly.w_uq.w + (size_t)r0 * RB, Ly.w_uq.s, r1 - r0, r0, 0, 1.f);
+  int ns = 0;
+  if (r0 < RQ) {
+    seg_set(L, ns, Ly.w_uq.w + (size_t)r0 * RB, Ly.w_uq.s, min(r1, RQ) - r0, r0, 0, 1.f);
+    ns++;
+  }
+  if (r1 > RQ) {
+    const int lo = max(r0, RQ) - RQ;
+    seg_set(L, ns, Ly.w_qi.w + (size_t)lo * RB, Ly.w_qi.s, r1 - max(r0, RQ), lo, 0, 1.f);
+    ns++;
+  }
   seg_end();
-  if (!gemv_list<SH::FP8, SH::QL, PLD_IF_WO>(L.segs, r1 > r0 ? 1 : 0, L.act, L.outb, OUT_STORE, pre_q)) return false;
+  if (!gemv_list<SH::FP8, SH::QL, PLD_IF_WO, SH::SPARSE>(L.segs, ns, L.act, L.outb, OUT_STORE, pre_q)) return false;
   if (!pre_q()) return false;
   __syncthreads();
+  auto outv = [&](int i) -> float {
+    if constexpr (SH::SPARSE) return (float)reinterpret_cast<const double*>(L.outb)[i];
+    else return L.outb[i];
+  };
   const PLD_GLOBAL float* rope = gp(wsp<float>(a, a.off.rope)) + (size_t)st.pos * SH::RD;   // (cos, sin) pairs
   uint64_t* qn = wsp<uint64_t>(a, a.off.q);
   uint64_t* qr = wsp<uint64_t>(a, a.off.qr);
   for (int p = r0 / 2 + tid_opaque(); p < r1 / 2; p += BLOCK) {
     const int r = 2 * p, h = r / SH::QH, k = r % SH::QH;
-    const float v0 = L.outb[r - r0], v1 = L.outb[r + 1 - r0];
+    if (SH::SPARSE && r >= RQ) {   // indexer query pair, bf16 from fp64
+      const double* od = reinterpret_cast<const double*>(L.outb);
+      ll_put(wsp<uint64_t>(a, a.off.qi) + (r - RQ) / 2,
+             f64_to_bf16(od[r - r0]) | (f64_to_bf16(od[r + 1 - r0]) << 16), st.k1);
+      continue;
+    }
+    const float v0 = outv(r - r0), v1 = outv(r + 1 - r0);
     if (k < SH::ND) {
       ll_put_f32(qn + h * SH::ND + k, v0, st.k1);
       ll_put_f32(qn + h * SH::ND + k + 1, v1, st.k1);
@@ -127,6 +209,398 @@ __device__ __forceinline__ bool stage_q_mla(Ctx& cx, const KArgs& a, const Step&
     }
   }
   stamp(a, cx, st, TR_ATT_Q);
+  return true;
+}
+
+// ------------------------------------------------------------------ IDX: indexer scores of the T = pos + 1 tokens
+// The sparse indexer of the TileRT article ("But What Exactly is TileRT?", its Sparse
+// Indexer worker): every cached token t has an FP8 key row (E4M3 codes + fp32 scale s_t);
+// its score is sum_h w_h * max(0, s_t * sum_i q_I[h,i] * dec(code_t,i)). The selection is
+// an integer result decided by these scores, so they are computed exactly as defined: in
+// fp64, i ascending, then h ascending, each product rounded on its own before its add.
+// (q_I is bf16 and a decoded code has 4 significant bits, so q_I * dec is exact in fp64
+// and a fused multiply-add of it rounds exactly once, like the separate add.)
+// Workgroup w scores tokens [split(T, nwg, w), split(T, nwg, w + 1)); four lanes per token,
+// each with two heads. The workgroup holding the new token encodes its key (fp32 scale
+// amax/448, fp32 quotient, E4M3 round to nearest even) and appends it to the cache.
+// Scores leave as order-preserving 64-bit keys (two u32 halves, coherent stores), then
+// one LL "done" word per workgroup.
+template <class SH>
+__device__ __forceinline__ bool stage_idx_mla(Ctx& cx, const KArgs& a, const Step& st, Lds& L) {
+  constexpr int IH = SH::IH, ID = SH::ID;
+  static_assert(IH == 8 && ID == 64, "indexer lanes: 4 lanes x 2 heads per token, 64-byte key rows");
+  constexpr int TPR = BLOCK / 4;   // tokens per round
+  const DLayer Ly = *gp(st.Ly);
+  const uint32_t k1 = st.k1;
+  const int tid = tid_opaque();
+  const int pos = st.pos, T = pos + 1;
+  const int t0 = split_at(T, cx.nwg, cx.w), t1 = split_at(T, cx.nwg, cx.w + 1);
+  if (t1 <= t0) {   // no tokens here: only the done word (the selector waits for every workgroup)
+    if (tid == 0) ll_put(wsp<uint64_t>(a, a.off.idone) + cx.w, 1u, k1);
+    return true;
+  }
+  const int fresh = a.pos0;   // rows >= fresh were written inside this launch
+  const bool owner = t0 <= pos && pos < t1;
+  // LDS
+  double* qd = reinterpret_cast<double*>(L.act);           // [ID][IH] q_I as fp64
+  double* wd = qd + ID * IH;                                // [IH] head weights
+  uint32_t* raw = reinterpret_cast<uint32_t*>(wd + IH);     // [IH*ID/2] q_I bf16 pairs, [IH] w, [ID] k_I
+  uint32_t* ncw = raw + IH * ID / 2 + IH + ID;              // [ID/4] code words of the new row, [1] its scale
+  const int hp = tid & 3;
+  uint4 cw[4];
+  float ks;
+  auto load_rows = [&](int tb) {
+    const int tt = min(tb + (tid >> 2), t1 - 1);
+    const uint8_t* row = Ly.icodes + (size_t)tt * ID;
+    if (tt >= fresh) {
+#pragma unroll
+      for (int q = 0; q < 4; q++) cw[q] = ld_coh16(row + 16 * q);
+      ks = ld_f32(Ly.iscales + tt);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; q++) cw[q] = ld_g16(row + 16 * q);
+      ks = gp(Ly.iscales)[tt];
+    }
+  };
+  load_rows(t0);
+  // q_I (Q stage), w and, for the new token's workgroup, k_I (X stage)
+  {
+    const uint32_t qiw = (uint32_t)(a.off.qi / 8), ixw = (uint32_t)(a.off.ixr / 8);
+    auto idx = [=](int i) -> int { return i < IH * ID / 2 ? (int)qiw + i : (int)ixw + (i - IH * ID / 2); };
+    const int nw = IH * ID / 2 + IH + (owner ? ID : 0);
+    if (!ll_fetch<1>(cx, raw, reinterpret_cast<const uint64_t*>(a.ws), nw, k1, W_IX, idx)) return false;
+  }
+  for (int i = tid; i < IH * ID; i += BLOCK) {
+    const int h = i / ID, k = i % ID;
+    const uint32_t pr = raw[i / 2];
+    qd[k * IH + h] = (double)((i & 1) ? bf_hi(pr) : bf_lo(pr));
+  }
+  if (tid < IH) wd[tid] = (double)__uint_as_float(raw[IH * ID / 2 + tid]);
+  if (owner && tid < 64) {   // one wave: the new key row (ID == 64 lanes)
+    const float k = __uint_as_float(raw[IH * ID / 2 + IH + tid]);
+    const float amax = wave_max(fabsf(k));
+    const float sig = amax > 0.f ? (float)((double)amax / 448.0) : 1.0f;
+    const float quo = fminf(fmaxf((float)((double)k / (double)sig), -448.f), 448.f);
+    reinterpret_cast<uint8_t*>(ncw)[tid] = (uint8_t)e4m3_encode(quo);
+    if (tid == 0) reinterpret_cast<float*>(ncw)[ID / 4] = sig;
+  }
+  __syncthreads();
+  if (owner && tid < ID / 4 + 1) {   // cache append (coherent stores; drained before the done word)
+    if (tid < ID / 4) st_u32(reinterpret_cast<uint32_t*>(Ly.icodes + (size_t)pos * ID) + tid, ncw[tid]);
+    else st_u32(reinterpret_cast<uint32_t*>(Ly.iscales + pos), ncw[ID / 4]);
+  }
+  uint32_t* kh = wsp<uint32_t>(a, a.off.ikh);
+  uint32_t* kl = wsp<uint32_t>(a, a.off.ikl);
+  for (int tb = t0; tb < t1; tb += TPR) {
+    if (tb != t0) load_rows(tb);
+    const int tt = tb + (tid >> 2);
+    uint32_t wv[16] = {cw[0].x, cw[0].y, cw[0].z, cw[0].w, cw[1].x, cw[1].y, cw[1].z, cw[1].w,
+                       cw[2].x, cw[2].y, cw[2].z, cw[2].w, cw[3].x, cw[3].y, cw[3].z, cw[3].w};
+    float sc = ks;
+    if (tt == pos) {
+#pragma unroll
+      for (int j = 0; j < 16; j++) wv[j] = ncw[j];
+      sc = reinterpret_cast<const float*>(ncw)[ID / 4];
+    }
+    double d0 = 0.0, d1 = 0.0;
+#pragma unroll
+    for (int j = 0; j < 16; j++) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[j], false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wv[j], true);
+      const float dv[4] = {lo.x, lo.y, hi.x, hi.y};
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const double2 q2 = *reinterpret_cast<const double2*>(qd + (4 * j + e) * IH + 2 * hp);
+        d0 = fma(q2.x, (double)dv[e], d0);
+        d1 = fma(q2.y, (double)dv[e], d1);
+      }
+    }
+    double score;
+    {
+#pragma clang fp contract(off)
+      const double s64 = (double)sc;
+      const double r0 = fmax(s64 * d0, 0.0), r1 = fmax(s64 * d1, 0.0);
+      const double p0 = wd[2 * hp] * r0, p1 = wd[2 * hp + 1] * r1;
+      // the 8 products of the token, from the 4 lanes of its quad, added in head order
+      const double p[8] = {dpp_mov_f64<0x00, 0xf, false>(p0), dpp_mov_f64<0x00, 0xf, false>(p1),
+                           dpp_mov_f64<0x55, 0xf, false>(p0), dpp_mov_f64<0x55, 0xf, false>(p1),
+                           dpp_mov_f64<0xAA, 0xf, false>(p0), dpp_mov_f64<0xAA, 0xf, false>(p1),
+                           dpp_mov_f64<0xFF, 0xf, false>(p0), dpp_mov_f64<0xFF, 0xf, false>(p1)};
+      score = 0.0;
+#pragma unroll
+      for (int h = 0; h < IH; h++) score = score + p[h];
+    }
+    if (score == 0.0) score = 0.0;   // one key for +0 and -0
+    const uint64_t bits = (uint64_t)__double_as_longlong(score);
+    const uint64_t key = (bits >> 63) ? ~bits : (bits | (1ull << 63));
+    if (hp == 0 && tt < t1) {
+      st_u32(kh + tt, (uint32_t)(key >> 32));
+      st_u32(kl + tt, (uint32_t)key);
+    }
+  }
+  vm_wait();
+  __syncthreads();
+  if (tid == 0) ll_put(wsp<uint64_t>(a, a.off.idone) + cx.w, 1u, k1);
+  stamp(a, cx, st, TR_IDX_DONE);
+  return true;
+}
+
+// ------------------------------------------------------------------ SEL: exact top-k of the indexer keys
+// One workgroup selects the K = min(topk, T) largest keys (ties to the lower token index,
+// the order the selection is defined with) and publishes the chosen token indices in
+// ascending order as LL words.
+//  * keys: thread tid holds the high halves of tokens tid + j*BLOCK in registers;
+//  * radix select, most significant digit first (6-bit digits): each pass counts the
+//    candidates' digits into per-lane private 16-bit counters in LDS (lane-owned columns:
+//    no atomic contention, no bank conflicts), sums the 64 bins, and keeps the bin that
+//    holds the K-th key; tokens in higher bins are taken;
+//  * once at most SEL_CMAX candidates are left they are ranked directly by (key, index)
+//    with the full 64-bit keys; if a whole 32-bit half ties with more candidates than
+//    that, the low halves get the same passes, and fully equal keys are cut by index.
+constexpr int SEL_WG = 0;
+constexpr int SEL_MAXJ = 66;    // keys per thread: T <= SEL_MAXJ * BLOCK
+constexpr int SEL_CMAX = 128;   // candidates ranked directly
+constexpr int SEL_LDS_WORDS = 32 * BLOCK + 16 + 32 + 2 * SEL_MAXJ * NWAVES + 2 * 128 + 3 * SEL_CMAX;
+
+template <class SH>
+__device__ __forceinline__ bool stage_sel_mla(Ctx& cx, const KArgs& a, const Step& st, Lds& L) {
+  if (cx.w != SEL_WG) return true;
+  const uint32_t k1 = st.k1;
+  const int tid = tid_opaque(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = st.pos + 1, K = min(a.c.itopk, T);
+  uint64_t* isel = wsp<uint64_t>(a, a.off.isel);
+  if (T <= K) {   // every token
+    for (int j = tid; j < T; j += BLOCK) ll_put(isel + j, (uint32_t)j, k1);
+    stamp(a, cx, st, TR_SEL_DONE);
+    return true;
+  }
+  uint32_t* hist = reinterpret_cast<uint32_t*>(L.act);     // [32][BLOCK] packed 16-bit counters
+  uint32_t* sv = hist + 32 * BLOCK;                         // [16] scalars
+  uint32_t* tot = sv + 16;                                  // [32] bin-pair totals
+  uint32_t* cc = tot + 32;                                  // [SEL_MAXJ][NWAVES] selected per (column, wave)
+  uint32_t* lp = cc + SEL_MAXJ * NWAVES;                    // [SEL_MAXJ][NWAVES] exclusive prefix over waves
+  uint32_t* csum = lp + SEL_MAXJ * NWAVES;                  // [128] column totals
+  uint32_t* cbase = csum + 128;                             // [128] column offsets
+  uint32_t* ct = cbase + 128;                               // [SEL_CMAX] candidate token
+  uint32_t* chi = ct + SEL_CMAX;                            // [SEL_CMAX] its key, high half
+  uint32_t* clo = chi + SEL_CMAX;                           // [SEL_CMAX] low half
+  uint8_t* fl = reinterpret_cast<uint8_t*>(hist);           // [T] selection flags of candidates (after the passes)
+  if (!ll_fetch<1>(cx, hist, wsp<uint64_t>(a, a.off.idone), cx.nwg, k1, W_IDONE)) return false;
+  const uint32_t* kh = wsp<uint32_t>(a, a.off.ikh);
+  const uint32_t* kl = wsp<uint32_t>(a, a.off.ikl);
+  const int J = (T + BLOCK - 1) / BLOCK;
+  uint32_t key[SEL_MAXJ];
+#pragma unroll
+  for (int j = 0; j < SEL_MAXJ; j++) {
+    const int t = tid + j * BLOCK;
+    key[j] = t < T ? ld_u32(kh + t) : 0u;
+  }
+  stamp(a, cx, st, TR_SEL_KEYS);
+  int need = K, ncand = T;
+  // one radix pass over the candidates' digits (val(j) >> shift) & (2^width - 1)
+  auto pass = [&](auto&& val, auto&& is_cand, int width, int shift) -> uint32_t {
+    const uint32_t nb = 1u << width;
+#pragma unroll 4
+    for (int r = 0; r < 32; r++) hist[r * BLOCK + tid] = 0u;
+#pragma unroll
+    for (int j = 0; j < SEL_MAXJ; j++) {
+      if (j < J && is_cand(j)) {
+        const uint32_t d = (val(j) >> shift) & (nb - 1u);
+        __hip_atomic_fetch_add(lds_ptr(&hist[(d >> 1) * BLOCK + tid]), 1u << ((d & 1u) * 16u), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    }
+    __syncthreads();
+    {
+      const int wr = tid >> 4, sg = tid & 15;
+      const uint4* src = reinterpret_cast<const uint4*>(hist + wr * BLOCK + sg * 32);
+      uint32_t sum = 0;
+#pragma unroll
+      for (int q = 0; q < 8; q++) {
+        const uint4 v = src[q];
+        sum += v.x + v.y + v.z + v.w;
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
+      if (sg == 0) tot[wr] = sum;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const uint32_t cnt = (uint32_t)lane < nb ? (tot[lane >> 1] >> ((lane & 1) * 16)) & 0xffffu : 0u;
+      uint32_t cum = cnt;   // sum over bins >= lane
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_down(cum, o, 64);
+        if (lane + o < 64) cum += v;
+      }
+      const uint64_t m = __ballot(cum >= (uint32_t)need);
+      const int bs = 63 - __clzll(m);
+      const uint32_t cb = __shfl(cnt, bs, 64), cumb = __shfl(cum, bs, 64);
+      if (lane == 0) {
+        sv[0] = (uint32_t)bs;
+        sv[1] = (uint32_t)need - (cumb - cb);
+        sv[2] = cb;
+      }
+    }
+    __syncthreads();
+    need = (int)sv[1];
+    ncand = (int)sv[2];
+    return sv[0];
+  };
+  // ---- high halves
+  uint32_t pre = 0, pm = 0;
+  {
+    constexpr int widths[6] = {6, 6, 6, 6, 6, 2};
+    int shift = 32;
+    for (int p = 0; p < 6 && ncand > SEL_CMAX; p++) {
+      const int wdt = widths[p];
+      shift -= wdt;
+      const uint32_t b = pass([&](int j) { return key[j]; },
+                              [&](int j) { return tid + j * BLOCK < T && (key[j] & pm) == pre; }, wdt, shift);
+      pre |= b << shift;
+      pm |= ((1u << wdt) - 1u) << shift;
+    }
+  }
+  // selection and candidate bits per (thread, column)
+  uint32_t sb[3] = {0u, 0u, 0u}, cb[3] = {0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < SEL_MAXJ; j++) {
+    const bool v = tid + j * BLOCK < T;
+    const uint32_t mk = key[j] & pm;
+    if (v && mk > pre) sb[j >> 5] |= 1u << (j & 31);
+    if (v && mk == pre) cb[j >> 5] |= 1u << (j & 31);
+  }
+  auto bit = [](const uint32_t* b, int j) { return (b[j >> 5] >> (j & 31)) & 1u; };
+  if (ncand > SEL_CMAX) {
+    // ---- the candidates share all 32 high bits: the same passes over the low halves
+    uint32_t lo[SEL_MAXJ];
+#pragma unroll
+    for (int j = 0; j < SEL_MAXJ; j++) lo[j] = bit(cb, j) ? ld_u32(kl + tid + j * BLOCK) : 0u;
+    uint32_t lpre = 0, lpm = 0;
+    constexpr int widths[6] = {6, 6, 6, 6, 6, 2};
+    int shift = 32;
+    for (int p = 0; p < 6 && ncand > SEL_CMAX; p++) {
+      const int wdt = widths[p];
+      shift -= wdt;
+      const uint32_t b = pass([&](int j) { return lo[j]; },
+                              [&](int j) { return bit(cb, j) && (lo[j] & lpm) == lpre; }, wdt, shift);
+      lpre |= b << shift;
+      lpm |= ((1u << wdt) - 1u) << shift;
+    }
+#pragma unroll
+    for (int j = 0; j < SEL_MAXJ; j++) {
+      if (bit(cb, j)) {
+        const uint32_t mk = lo[j] & lpm;
+        if (mk > lpre) sb[j >> 5] |= 1u << (j & 31);
+        if (mk != lpre) cb[j >> 5] &= ~(1u << (j & 31));
+      }
+    }
+    if (ncand > SEL_CMAX) {
+      // ---- equal 64-bit keys: the `need` lowest token indices, cut M found by bisection
+      int lo_m = 0, hi_m = T;
+      while (lo_m < hi_m) {
+        const int mid = (lo_m + hi_m) >> 1;
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < SEL_MAXJ; j++) cnt += (bit(cb, j) && tid + j * BLOCK < mid) ? 1 : 0;
+        const double tc = block_sum((double)cnt, L.red);
+        if (tc >= (double)need) hi_m = mid;
+        else lo_m = mid + 1;
+      }
+#pragma unroll
+      for (int j = 0; j < SEL_MAXJ; j++)
+        if (bit(cb, j) && tid + j * BLOCK < lo_m) sb[j >> 5] |= 1u << (j & 31);
+      ncand = 0;
+    }
+  }
+  if (ncand > 0) {
+    // ---- at most SEL_CMAX candidates: rank each by (key desc, index asc) on full keys
+    if (tid == 0) sv[3] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < SEL_MAXJ; j++) {
+      if (bit(cb, j)) {
+        const uint32_t i = __hip_atomic_fetch_add(lds_ptr(&sv[3]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (i < (uint32_t)SEL_CMAX) ct[i] = (uint32_t)(tid + j * BLOCK);
+      }
+    }
+    __syncthreads();
+    const int nc = min((int)sv[3], SEL_CMAX);
+    if (tid < nc) {
+      chi[tid] = ld_u32(kh + ct[tid]);
+      clo[tid] = ld_u32(kl + ct[tid]);
+    }
+    __syncthreads();
+    {
+      const int c = tid >> 2, part = tid & 3;
+      int rank = 0;
+      if (c < nc) {
+        const uint32_t h = chi[c], l = clo[c], t = ct[c];
+        for (int d = part; d < nc; d += 4) {
+          const uint32_t hd = chi[d], ld = clo[d];
+          rank += (hd > h || (hd == h && (ld > l || (ld == l && ct[d] < t)))) ? 1 : 0;
+        }
+      }
+      rank += __shfl_xor(rank, 1, 64);
+      rank += __shfl_xor(rank, 2, 64);
+      if (c < nc && part == 0) fl[ct[c]] = rank < need ? 1 : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < SEL_MAXJ; j++)
+      if (bit(cb, j) && fl[tid + j * BLOCK]) sb[j >> 5] |= 1u << (j & 31);
+  }
+  stamp(a, cx, st, TR_SEL_PASSES);
+  // ---- emit the chosen tokens in ascending order: t = tid + j*BLOCK orders as (j, wave, lane)
+#pragma unroll
+  for (int j = 0; j < SEL_MAXJ; j++) {
+    if (j < J) {
+      const uint64_t m = __ballot(bit(sb, j));
+      if (lane == 0) cc[j * NWAVES + wave] = (uint32_t)__popcll(m);
+    }
+  }
+  __syncthreads();
+  if (tid < J) {
+    uint32_t s = 0;
+#pragma unroll
+    for (int w = 0; w < NWAVES; w++) {
+      const uint32_t v = cc[tid * NWAVES + w];
+      lp[tid * NWAVES + w] = s;
+      s += v;
+    }
+    csum[tid] = s;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t x0 = lane < J ? csum[lane] : 0u, x1 = lane + 64 < J ? csum[lane + 64] : 0u;
+    const uint32_t c0 = x0, c1 = x1;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t v0 = __shfl_up(x0, o, 64), v1 = __shfl_up(x1, o, 64);
+      if (lane >= o) {
+        x0 += v0;
+        x1 += v1;
+      }
+    }
+    const uint32_t t0s = __shfl(x0, 63, 64);
+    if (lane < J) cbase[lane] = x0 - c0;
+    if (lane + 64 < J) cbase[lane + 64] = t0s + x1 - c1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < SEL_MAXJ; j++) {
+    if (j < J) {
+      const uint32_t b = bit(sb, j);
+      const uint64_t m = __ballot(b);
+      if (b) {
+        const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        const uint32_t off = cbase[j] + lp[j * NWAVES + wave] + below;
+        if (off < (uint32_t)K) ll_put(isel + off, (uint32_t)(tid + j * BLOCK), k1);
+      }
+    }
+  }
+  stamp(a, cx, st, TR_SEL_DONE);
   return true;
 }
 
@@ -232,9 +706,12 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
   const int hg = cx.w / nch, ch = cx.w % nch;
   const int hbase = hg * HPW;
   const int pos = st.pos, T = pos + 1;
-  const int t0 = split_at(T, nch, ch), t1 = split_at(T, nch, ch + 1), n = t1 - t0;
+  // dense: the chunk's rows are [t0, t1) of the T cache rows; sparse: entries [t0, t1) of
+  // the indexer's ascending list of K selected rows (the new row, if chosen, is the last)
+  const int K = SH::SPARSE ? min(c.itopk, T) : T;
+  const int t0 = split_at(K, nch, ch), t1 = split_at(K, nch, ch + 1), n = t1 - t0;
   const int fresh = a.pos0;
-  const int nst = max(0, min(n, fresh - t0));            // static rows of the chunk: [0, nst)
+  const int nst = max(0, min(n, fresh - t0));            // dense: static rows of the chunk: [0, nst)
   const uint16_t* lat = Ly.lat;
   // LDS (inside L.act)
   uint16_t* Qs = reinterpret_cast<uint16_t*>(L.act);     // [16][CSTR] bf16 (rows >= HPW zero)
@@ -245,7 +722,21 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
   float* qtmp = reinterpret_cast<float*>(Cs + TB * CSTR); // q staging (Cs buffer 1, free at start)
   uint16_t* newrow = reinterpret_cast<uint16_t*>(alph + 16);   // [LAT] the row of position pos
   float* ntmp = reinterpret_cast<float*>(newrow + LAT);  // [LAT] its fp32 raw values
-  auto srow = [&](int t) -> size_t { return (size_t)(nst > 0 ? t0 + min(t, nst - 1) : 0); };
+  int* srows = reinterpret_cast<int*>(ntmp + LAT);        // sparse: [n] rows of this chunk
+  if constexpr (SH::SPARSE) {
+    if (n > 0 && !ll_fetch<1>(cx, reinterpret_cast<uint32_t*>(srows), wsp<uint64_t>(a, a.off.isel) + t0, n, k1,
+                              W_ISEL))
+      return false;
+  }
+  auto srow = [&](int t) -> size_t {
+    if constexpr (SH::SPARSE) return (size_t)srows[min(t, n - 1)];
+    else return (size_t)(nst > 0 ? t0 + min(t, nst - 1) : 0);
+  };
+  // index inside the chunk of the row of position pos (its bf16 row is patched in from
+  // LDS), or -1; the chunk that computes the new row and appends it to the cache
+  const int pidx = SH::SPARSE ? ((ch == nch - 1 && n > 0 && srows[n - 1] == pos) ? n - 1 : -1)
+                              : ((t0 <= pos && pos < t1) ? pos - t0 : -1);
+  const bool newrow_here = SH::SPARSE ? ch == nch - 1 : (t0 <= pos && pos < t1);
   // Staging registers: three sub-blocks in flight (sets A, B, C in turn); chunk i of a
   // block covers (row i / CPRW, chunk i % CPRW). A block's loads are issued three blocks
   // before it is staged into LDS, so the wait at staging time covers ~3 blocks of work.
@@ -258,7 +749,7 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
   constexpr int DEPTH = 3;
   const int nsb = (n + TB - 1) / TB;
   const int nsbp = (nsb + DEPTH - 1) / DEPTH * DEPTH;
-  const bool coh = n > 0 && t0 + n > fresh;
+  const bool coh = SH::SPARSE ? (n > 0 && srows[n - 1] >= fresh) : (n > 0 && t0 + n > fresh);
   uint4 cb[DEPTH][NLD];
   auto issue = [&](int set, int sb, auto coh_tag) {
     constexpr bool COH = decltype(coh_tag)::value;
@@ -268,7 +759,7 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
       const int idx = min(tid + i * BLOCK, TB * CPRW - 1);
       const int r = idx / CPRW, k = idx % CPRW;
       const int t = max(min(sb * TB + r, n - 1), 0);
-      const size_t row = COH ? (size_t)(t0 + t) : srow(t);
+      const size_t row = (COH && !SH::SPARSE) ? (size_t)(t0 + t) : srow(t);
       const uint16_t* p = live ? lat + row * LAT + k * 8 : lat;
       cb[set][i] = COH ? ld_coh16(p) : ld_g16(p);
     }
@@ -285,8 +776,8 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
         d[0] = cb[set][i].x; d[1] = cb[set][i].y; d[2] = cb[set][i].z; d[3] = cb[set][i].w;
       }
     }
-    const int rp = pos - t0 - sb * TB;   // row of pos inside this block
-    if (rp >= 0 && rp < TB && pos < t1) {
+    const int rp = pidx - sb * TB;   // row of pos inside this block
+    if (pidx >= 0 && rp >= 0 && rp < TB) {
       __syncthreads();
       for (int k = tid; k < LAT / 2; k += BLOCK)
         reinterpret_cast<uint32_t*>(C + rp * CSTR)[k] = reinterpret_cast<const uint32_t*>(newrow)[k];
@@ -312,8 +803,8 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
     Qs[h * CSTR + k] = (uint16_t)bf16_bits(v);
   }
   for (int i = tid; i < 16 * TB; i += BLOCK) Ps[i] = 0;
-  // the row of position pos (chunk that holds it): RMSNorm(c_kv') and RoPE(k_r'), bf16
-  if (t0 <= pos && pos < t1) {
+  // the row of position pos: RMSNorm(c_kv') and RoPE(k_r'), bf16
+  if (newrow_here) {
     if (!ll_fetch<per_for(LAT)>(cx, reinterpret_cast<uint32_t*>(ntmp), wsp<uint64_t>(a, a.off.ckvr), LAT, k1, W_KV))
       return false;
     double ss = 0.0;
@@ -565,24 +1056,33 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_mla(KArgs a) {
       const bool last = (t == a.n_tokens - 1) && (li == a.n_layers - 1);
       KArgs as = a;
       asm volatile("" : "+s"(as.ws));
+      // the launch geometry as per-step values: row splits and pass counts derived from
+      // it are then computed inside the step instead of being hoisted to kernel entry,
+      // where they would hold scalar registers (and spill) across every stage
+      Ctx cs = cx;
+      asm volatile("" : "+s"(cs.w), "+s"(cs.nwg), "+s"(as.c.cpw), "+s"(as.c.cpg), "+s"(as.c.itopk));
       uint32_t lds0 = 0;
       asm volatile("" : "+s"(lds0));
       Lds L = carve(lds_raw + lds0, a.c);
       st.tr = L.tr;
-      stamp(as, cx, st, TR_START);
-      if (!stage_x_mla<SH>(cx, as, st, L)) return;
-      if (!stage_q_mla<SH>(cx, as, st, L)) return;
-      if (!stage_absorb_mla<SH>(cx, as, st, L)) return;
-      if (!stage_attn_mla<SH>(cx, as, st, L)) return;
-      if (!stage_merge_mla<SH>(cx, as, st, L)) return;
-      if (!stage_uv_mla<SH>(cx, as, st, L)) return;
-      if (!stage_wo<SH>(cx, as, st, L)) return;
-      if (!stage_ffn<SH>(cx, as, st, L)) return;
-      if (!stage_down<SH>(cx, as, st, L, last ? as.out_hidden : nullptr)) return;
-      if constexpr (SH::FP8) {
-        if (a.head_on && li == a.n_layers - 1 && !stage_head<SH>(cx, as, st, L, t, &token)) return;
+      stamp(as, cs, st, TR_START);
+      if (!stage_x_mla<SH>(cs, as, st, L)) return;
+      if (!stage_q_mla<SH>(cs, as, st, L)) return;
+      if constexpr (SH::SPARSE) {
+        if (!stage_idx_mla<SH>(cs, as, st, L)) return;
+        if (!stage_sel_mla<SH>(cs, as, st, L)) return;
       }
-      trace_flush(as, cx, st);
+      if (!stage_absorb_mla<SH>(cs, as, st, L)) return;
+      if (!stage_attn_mla<SH>(cs, as, st, L)) return;
+      if (!stage_merge_mla<SH>(cs, as, st, L)) return;
+      if (!stage_uv_mla<SH>(cs, as, st, L)) return;
+      if (!stage_wo<SH>(cs, as, st, L)) return;
+      if (!stage_ffn<SH>(cs, as, st, L)) return;
+      if (!stage_down<SH>(cs, as, st, L, last ? as.out_hidden : nullptr)) return;
+      if constexpr (SH::FP8) {
+        if (a.head_on && li == a.n_layers - 1 && !stage_head<SH>(cs, as, st, L, t, &token)) return;
+      }
+      trace_flush(as, cs, st);
     }
   }
 }
