@@ -97,7 +97,9 @@ SLOT_NAMES = {32: "head_ready", 33: "head_gemv", 34: "token", 0: "start", 1: "x_
               13: "att_softmax", 14: "att_partial", 15: "att_merged", 16: "topk", 18: "m_stored", 19: "down_gemv",
               20: "down_epi", 21: "qkv_gemv", 22: "shared_gemv", 23: "att_pv", 24: "x_normed", 25: "merge_start",
               26: "merge_fetched", 27: "router_logit", 28: "att_drained", 30: "att_scores", 17: "blk0_staged", 31: "blk0_done",
-              35: "idx_done", 36: "sel_keys", 37: "sel_passes", 38: "sel_done"}
+              35: "idx_done", 36: "sel_keys", 37: "sel_passes", 38: "sel_done", 39: "sel_pass0", 40: "sel_pass1",
+              41: "sel_pass2", 42: "sel_pass3", 43: "sel_pass4", 44: "sel_pass5", 45: "sel_rank_loaded",
+              46: "sel_keys_arrived"}
 
 
 def write_trace_summary(dec, x, out, R, path, pos):

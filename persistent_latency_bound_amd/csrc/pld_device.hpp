@@ -107,6 +107,10 @@ __device__ __forceinline__ uint64_t ld_u64_off(const void* base, uint32_t byte_o
   const PLD_GLOBAL char* b = gp(reinterpret_cast<const char*>(base));
   return __hip_atomic_load((PLD_GLOBAL uint64_t*)(b + byte_off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ uint32_t ld_u32_off(const void* base, uint32_t byte_off) {
+  const PLD_GLOBAL char* b = gp(reinterpret_cast<const char*>(base));
+  return __hip_atomic_load((PLD_GLOBAL uint32_t*)(b + byte_off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void st_u64_off(void* base, uint32_t byte_off, uint64_t v) {
   PLD_GLOBAL char* b = gp(reinterpret_cast<char*>(base));
   __hip_atomic_store((PLD_GLOBAL uint64_t*)(b + byte_off), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -196,6 +200,32 @@ __device__ __forceinline__ float dpp_sum(float v) {
   // row_bcast31: lane 31 is added into rows 2 and 3
   if constexpr (N >= 64) v += dpp_mov<0x143, 0xc, true>(v);
   return v;
+}
+
+// 32-bit integer DPP move (bound_ctrl: lanes whose source is out of range read 0).
+template <int CTRL, int ROW_MASK, bool BOUND>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xf, BOUND);
+}
+// Inclusive prefix sum over the 64 lanes of a wave: Hillis-Steele inside each row of 16
+// (row_shr 1, 2, 4, 8), then row 0's total into row 1 and row 2's into row 3 (row_bcast15),
+// then the total of rows 0-1 into rows 2 and 3 (row_bcast31).
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
+  x += dpp_u32<0x111, 0xf, true>(x);
+  x += dpp_u32<0x112, 0xf, true>(x);
+  x += dpp_u32<0x114, 0xf, true>(x);
+  x += dpp_u32<0x118, 0xf, true>(x);
+  x += dpp_u32<0x142, 0xa, true>(x);
+  x += dpp_u32<0x143, 0xc, true>(x);
+  return x;
+}
+// Sum over each row of 16 lanes, valid in every lane of the row.
+__device__ __forceinline__ uint32_t row16_sum_u32(uint32_t x) {
+  x += dpp_u32<0xB1, 0xf, false>(x);
+  x += dpp_u32<0x4E, 0xf, false>(x);
+  x += dpp_u32<0x141, 0xf, false>(x);
+  x += dpp_u32<0x140, 0xf, false>(x);
+  return x;
 }
 
 // fp64 sum over groups of 64 lanes with DPP moves applied to both 32-bit halves (same

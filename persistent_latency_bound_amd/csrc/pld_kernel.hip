@@ -333,6 +333,9 @@ __device__ __forceinline__ void seg_set(Lds& L, int i, const uint8_t* w, const f
                                         float alpha) {
   if (tid_opaque() == 0) {
     RowSeg& S = L.segs[i];
+    // alpha as a per-call value: a constant alpha would be paired with act_off into one
+    // 64-bit constant, hoisted to kernel entry and kept live (and spilled) across stages
+    asm volatile("" : "+v"(alpha));
     S.w = w; S.s = sc; S.n = n; S.srow = srow; S.act_off = act_off; S.alpha = alpha;
   }
 }
@@ -1356,10 +1359,11 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
       // indexer: 8 heads x 64 dims (4 lanes x 2 heads per token); selection keys per thread;
       // one workgroup's done-word fetch; selected rows per chunk (LL fetch, one pass)
       if (c->index_heads != 8 || c->index_dim != 64 || c->index_topk < 1) return PLD_E_UNSUPPORTED;
-      if (c->max_seq > SEL_MAXJ * BLOCK || nwg > BLOCK || srows_max > BLOCK || srows_max > 8 * TB)
+      if (c->max_seq > SEL_MAXJ * BLOCK || c->max_seq > SEL_LKMAX * nwg || nwg > BLOCK || srows_max > BLOCK ||
+          srows_max > 8 * TB)
         return PLD_E_UNSUPPORTED;
-      const int idx_words = 2 * (c->index_heads * c->index_dim + c->index_heads) + c->index_heads * c->index_dim / 2 +
-                            c->index_heads + c->index_dim + c->index_dim / 4 + 1;
+      const int idx_words = 2 * (c->index_heads * c->index_dim + c->index_heads) + 2 * SEL_LKMAX +
+                            c->index_heads * c->index_dim / 2 + c->index_heads + c->index_dim + c->index_dim / 4 + 3;
       act = std::max({act, 3 * c->q_lora, SEL_LDS_WORDS, idx_words});
       if (c->q_lora + LAT + c->index_heads + c->index_dim < nwg) return PLD_E_UNSUPPORTED;
     }

@@ -220,11 +220,15 @@ __device__ __forceinline__ bool stage_q_mla(Ctx& cx, const KArgs& a, const Step&
 // fp64, i ascending, then h ascending, each product rounded on its own before its add.
 // (q_I is bf16 and a decoded code has 4 significant bits, so q_I * dec is exact in fp64
 // and a fused multiply-add of it rounds exactly once, like the separate add.)
-// Workgroup w scores tokens [split(T, nwg, w), split(T, nwg, w + 1)); four lanes per token,
-// each with two heads. The workgroup holding the new token encodes its key (fp32 scale
-// amax/448, fp32 quotient, E4M3 round to nearest even) and appends it to the cache.
-// Scores leave as order-preserving 64-bit keys (two u32 halves, coherent stores), then
-// one LL "done" word per workgroup.
+// Workgroup w scores tokens t = w + i*nwg (interleaved, so that each workgroup's keys are
+// a sample of the whole cache); four lanes per token, each with two heads. The workgroup
+// holding the new token encodes its key (fp32 scale amax/448, fp32 quotient, E4M3 round to
+// nearest even) and appends it to the cache. Scores leave as order-preserving 64-bit keys
+// (two u32 halves, coherent stores), then one LL "done" word per workgroup whose payload
+// is the high half of the workgroup's r-th largest key, r = ceil(K / nwg): every workgroup
+// holds r keys at or above its own, so the K-th largest key of all is at least the
+// smallest of these, and the selector can discard every key below that bound.
+constexpr int SEL_LKMAX = 256;   // keys per scoring workgroup: T <= SEL_LKMAX * nwg
 template <class SH>
 __device__ __forceinline__ bool stage_idx_mla(Ctx& cx, const KArgs& a, const Step& st, Lds& L) {
   constexpr int IH = SH::IH, ID = SH::ID;
@@ -233,36 +237,44 @@ __device__ __forceinline__ bool stage_idx_mla(Ctx& cx, const KArgs& a, const Ste
   const DLayer Ly = *gp(st.Ly);
   const uint32_t k1 = st.k1;
   const int tid = tid_opaque();
-  const int pos = st.pos, T = pos + 1;
-  const int t0 = split_at(T, cx.nwg, cx.w), t1 = split_at(T, cx.nwg, cx.w + 1);
-  if (t1 <= t0) {   // no tokens here: only the done word (the selector waits for every workgroup)
-    if (tid == 0) ll_put(wsp<uint64_t>(a, a.off.idone) + cx.w, 1u, k1);
+  const int pos = st.pos, T = pos + 1, nwg = cx.nwg, w = cx.w;
+  const int nt = w < T ? (T - 1 - w) / nwg + 1 : 0;   // this workgroup's tokens w + i*nwg, i < nt
+  const int K = min(a.c.itopk, T);
+  const int r = (K + nwg - 1) / nwg;
+  uint64_t* idone = wsp<uint64_t>(a, a.off.idone);
+  if (nt == 0) {   // no tokens here: a done word without a bound (the selector waits for every workgroup)
+    if (tid == 0) ll_put(idone + w, 0u, k1);
     return true;
   }
   const int fresh = a.pos0;   // rows >= fresh were written inside this launch
-  const bool owner = t0 <= pos && pos < t1;
+  const bool owner = pos % nwg == w;
   // LDS
   double* qd = reinterpret_cast<double*>(L.act);           // [ID][IH] q_I as fp64
   double* wd = qd + ID * IH;                                // [IH] head weights
-  uint32_t* raw = reinterpret_cast<uint32_t*>(wd + IH);     // [IH*ID/2] q_I bf16 pairs, [IH] w, [ID] k_I
+  uint64_t* lk = reinterpret_cast<uint64_t*>(wd + IH);      // [SEL_LKMAX] this workgroup's keys
+  uint32_t* raw = reinterpret_cast<uint32_t*>(lk + SEL_LKMAX);   // [IH*ID/2] q_I bf16 pairs, [IH] w, [ID] k_I
   uint32_t* ncw = raw + IH * ID / 2 + IH + ID;              // [ID/4] code words of the new row, [1] its scale
+  uint32_t* mv = ncw + ID / 4 + 2;                          // [1] high half of the local r-th largest key
   const int hp = tid & 3;
-  uint4 cw[4];
-  float ks;
-  auto load_rows = [&](int tb) {
-    const int tt = min(tb + (tid >> 2), t1 - 1);
+  // key rows of both rounds (a workgroup has at most 2 * TPR tokens), issued before the
+  // wait for q_I so that neither round pays its own load latency afterwards
+  uint4 cw[2][4];
+  float ks[2];
+  auto load_rows = [&](int rd) {
+    const int tt = w + min(rd * TPR + (tid >> 2), nt - 1) * nwg;
     const uint8_t* row = Ly.icodes + (size_t)tt * ID;
     if (tt >= fresh) {
 #pragma unroll
-      for (int q = 0; q < 4; q++) cw[q] = ld_coh16(row + 16 * q);
-      ks = ld_f32(Ly.iscales + tt);
+      for (int q = 0; q < 4; q++) cw[rd][q] = ld_coh16(row + 16 * q);
+      ks[rd] = ld_f32(Ly.iscales + tt);
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; q++) cw[q] = ld_g16(row + 16 * q);
-      ks = gp(Ly.iscales)[tt];
+      for (int q = 0; q < 4; q++) cw[rd][q] = ld_g16(row + 16 * q);
+      ks[rd] = gp(Ly.iscales)[tt];
     }
   };
-  load_rows(t0);
+  load_rows(0);
+  if (nt > TPR) load_rows(1);
   // q_I (Q stage), w and, for the new token's workgroup, k_I (X stage)
   {
     const uint32_t qiw = (uint32_t)(a.off.qi / 8), ixw = (uint32_t)(a.off.ixr / 8);
@@ -276,6 +288,7 @@ __device__ __forceinline__ bool stage_idx_mla(Ctx& cx, const KArgs& a, const Ste
     qd[k * IH + h] = (double)((i & 1) ? bf_hi(pr) : bf_lo(pr));
   }
   if (tid < IH) wd[tid] = (double)__uint_as_float(raw[IH * ID / 2 + tid]);
+  if (tid == 0) mv[0] = 0u;   // no bound unless this workgroup holds r keys
   if (owner && tid < 64) {   // one wave: the new key row (ID == 64 lanes)
     const float k = __uint_as_float(raw[IH * ID / 2 + IH + tid]);
     const float amax = wave_max(fabsf(k));
@@ -291,12 +304,15 @@ __device__ __forceinline__ bool stage_idx_mla(Ctx& cx, const KArgs& a, const Ste
   }
   uint32_t* kh = wsp<uint32_t>(a, a.off.ikh);
   uint32_t* kl = wsp<uint32_t>(a, a.off.ikl);
-  for (int tb = t0; tb < t1; tb += TPR) {
-    if (tb != t0) load_rows(tb);
-    const int tt = tb + (tid >> 2);
-    uint32_t wv[16] = {cw[0].x, cw[0].y, cw[0].z, cw[0].w, cw[1].x, cw[1].y, cw[1].z, cw[1].w,
-                       cw[2].x, cw[2].y, cw[2].z, cw[2].w, cw[3].x, cw[3].y, cw[3].z, cw[3].w};
-    float sc = ks;
+#pragma unroll
+  for (int rd = 0; rd < 2; rd++) {
+    if (rd * TPR >= nt) break;
+    const int i = rd * TPR + (tid >> 2);
+    const int tt = w + i * nwg;
+    uint32_t wv[16] = {cw[rd][0].x, cw[rd][0].y, cw[rd][0].z, cw[rd][0].w, cw[rd][1].x, cw[rd][1].y,
+                       cw[rd][1].z, cw[rd][1].w, cw[rd][2].x, cw[rd][2].y, cw[rd][2].z, cw[rd][2].w,
+                       cw[rd][3].x, cw[rd][3].y, cw[rd][3].z, cw[rd][3].w};
+    float sc = ks[rd];
     if (tt == pos) {
 #pragma unroll
       for (int j = 0; j < 16; j++) wv[j] = ncw[j];
@@ -333,14 +349,34 @@ __device__ __forceinline__ bool stage_idx_mla(Ctx& cx, const KArgs& a, const Ste
     if (score == 0.0) score = 0.0;   // one key for +0 and -0
     const uint64_t bits = (uint64_t)__double_as_longlong(score);
     const uint64_t key = (bits >> 63) ? ~bits : (bits | (1ull << 63));
-    if (hp == 0 && tt < t1) {
+    if (hp == 0 && i < nt) {
       st_u32(kh + tt, (uint32_t)(key >> 32));
       st_u32(kl + tt, (uint32_t)key);
+      lk[i] = key;
+    }
+  }
+  __syncthreads();
+  if (nt >= r) {   // the local r-th largest key: rank by (key desc, index asc), four lanes per key
+    for (int c0 = 0; c0 < nt; c0 += TPR) {
+      const int c = c0 + (tid >> 2);
+      int rank = 0;
+      uint64_t kc = 0;
+      if (c < nt) {
+        kc = lk[c];
+#pragma unroll 8
+        for (int d = hp; d < nt; d += 4) {
+          const uint64_t kd = lk[d];
+          rank += (kd > kc || (kd == kc && d < c)) ? 1 : 0;
+        }
+      }
+      rank += __shfl_xor(rank, 1, 64);
+      rank += __shfl_xor(rank, 2, 64);
+      if (c < nt && hp == 0 && rank == r - 1) mv[0] = (uint32_t)(kc >> 32);
     }
   }
   vm_wait();
   __syncthreads();
-  if (tid == 0) ll_put(wsp<uint64_t>(a, a.off.idone) + cx.w, 1u, k1);
+  if (tid == 0) ll_put(idone + w, mv[0], k1);
   stamp(a, cx, st, TR_IDX_DONE);
   return true;
 }
@@ -348,19 +384,289 @@ __device__ __forceinline__ bool stage_idx_mla(Ctx& cx, const KArgs& a, const Ste
 // ------------------------------------------------------------------ SEL: exact top-k of the indexer keys
 // One workgroup selects the K = min(topk, T) largest keys (ties to the lower token index,
 // the order the selection is defined with) and publishes the chosen token indices in
-// ascending order as LL words.
-//  * keys: thread tid holds the high halves of tokens tid + j*BLOCK in registers;
-//  * radix select, most significant digit first (6-bit digits): each pass counts the
-//    candidates' digits into per-lane private 16-bit counters in LDS (lane-owned columns:
-//    no atomic contention, no bank conflicts), sums the 64 bins, and keeps the bin that
-//    holds the K-th key; tokens in higher bins are taken;
-//  * once at most SEL_CMAX candidates are left they are ranked directly by (key, index)
-//    with the full 64-bit keys; if a whole 32-bit half ties with more candidates than
-//    that, the low halves get the same passes, and fully equal keys are cut by index.
+// ascending order as LL words. Thread tid owns tokens tid + j*BLOCK (coalesced loads of
+// the keys' high halves); a padding key is 0, which no score's key can be.
+//  * Bound: every chosen key is at least the smallest of the scorers' published bounds.
+//    The tokens whose high half reaches it are compacted into per-wave LDS lists (ballot
+//    offsets, a running count per wave) while the keys stream through in chunks. Up to
+//    SEL_WCAP per wave are selected from there, 16 entries per thread; a larger set goes to
+//    sel_all_tokens, which takes the same steps over every token.
+//  * Radix select, most significant digit first (5-bit digits, starting below the bits
+//    all candidates share): each pass adds every entry's candidacy into per-lane private
+//    16-bit counters in LDS (lane-owned columns: no atomic contention, no bank conflicts,
+//    no branches), sums the 32 bins and keeps the bin that holds the K-th key; entries in
+//    higher bins are taken.
+//  * Once at most SEL_CMAX candidates are left they are ranked directly by (key, index)
+//    with the full 64-bit keys; if the high halves tie among more candidates than that,
+//    the low halves get the same passes, and fully equal keys are cut by token index.
+//  * Taken tokens are set in an LDS bitmap; the output walks it in contiguous per-thread
+//    ranges with one block-wide exclusive scan, which gives ascending order.
 constexpr int SEL_WG = 0;
-constexpr int SEL_MAXJ = 66;    // keys per thread: T <= SEL_MAXJ * BLOCK
-constexpr int SEL_CMAX = 128;   // candidates ranked directly
-constexpr int SEL_LDS_WORDS = 32 * BLOCK + 16 + 32 + 2 * SEL_MAXJ * NWAVES + 2 * 128 + 3 * SEL_CMAX;
+constexpr int SEL_MAXJ = 68;                  // token columns per thread: T <= SEL_MAXJ * BLOCK
+constexpr int SEL_CH = 17;                    // columns per load chunk
+constexpr int SEL_WCAP = 1024;                // compacted entries per wave
+constexpr int SEL_CAP = SEL_WCAP * NWAVES;
+constexpr int SEL_EPT = SEL_CAP / BLOCK;      // entries per thread
+constexpr int SEL_CMAX = 128;                 // candidates ranked directly
+constexpr int SEL_ROWS = 16;                  // counter words per lane: 32 bins of 16 bits
+constexpr int SEL_BMW = 3;                    // bitmap words per thread: tokens [96 tid, 96 tid + 96)
+static_assert(SEL_MAXJ % SEL_CH == 0 && SEL_BMW * 32 >= SEL_MAXJ && SEL_EPT % 4 == 0, "selector tiling");
+// LDS words: counters | entry keys | entry tokens | entry flags | bitmap | scalars | rank lists
+constexpr int SEL_LDS_WORDS = SEL_ROWS * BLOCK + 2 * SEL_CAP + SEL_CAP / 4 + SEL_BMW * BLOCK + 64 + 4 * SEL_CMAX;
+static_assert(SEL_MAXJ * BLOCK / 4 <= 2 * SEL_CAP, "all-token flags share the entry region");
+
+// Exclusive prefix sum of v over the workgroup (thread order); every thread must call.
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum) {
+  const int tid = tid_opaque(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t x = wave_incl_scan_u32(v);
+  __syncthreads();
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  uint32_t off = 0;
+  for (int w = 0; w < wave; w++) off += wsum[w];
+  return off + x - v;
+}
+
+struct SelLds {
+  uint32_t *hist, *ech, *ett, *bm, *sv, *tot, *wsum, *wcnt, *chi, *clo, *ctk, *cix;
+  uint8_t *efl, *fl;
+};
+__device__ __forceinline__ SelLds sel_carve(float* act) {
+  SelLds S;
+  S.hist = reinterpret_cast<uint32_t*>(act);     // [SEL_ROWS][BLOCK] packed 16-bit counters
+  S.ech = S.hist + SEL_ROWS * BLOCK;              // [SEL_CAP] entry keys (high halves), per-wave lists
+  S.ett = S.ech + SEL_CAP;                        // [SEL_CAP] entry tokens
+  S.fl = reinterpret_cast<uint8_t*>(S.ech);      // [SEL_MAXJ*BLOCK] token flags (all-token path)
+  S.efl = reinterpret_cast<uint8_t*>(S.ett + SEL_CAP);   // [SEL_CAP] entry flags
+  S.bm = reinterpret_cast<uint32_t*>(S.efl + SEL_CAP);   // [SEL_BMW*BLOCK] taken tokens
+  S.sv = S.bm + SEL_BMW * BLOCK;                  // [16] scalars
+  S.tot = S.sv + 16;                              // [16] bin-pair totals
+  S.wsum = S.tot + 16;                            // [16] scan partials
+  S.wcnt = S.wsum + 16;                           // [16] per-wave entry counts
+  S.chi = S.wcnt + 16;                            // [SEL_CMAX] ranked candidates: key high half
+  S.clo = S.chi + SEL_CMAX;                       //   low half
+  S.ctk = S.clo + SEL_CMAX;                       //   token
+  S.cix = S.ctk + SEL_CMAX;                       //   entry
+  return S;
+}
+
+// After a counting pass: bin totals (each thread clears the counters it read), the bin
+// holding the need-th largest candidate; need and ncand updated. `pad` non-candidates were
+// counted in bin 0.
+__device__ __forceinline__ uint32_t sel_finish_pass(const SelLds& S, uint32_t nb, uint32_t pad, int& need, int& ncand) {
+  const int tid = tid_opaque(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __syncthreads();
+  {
+    const int wr = tid >> 5, sg = tid & 31;   // 16 rows x 32 segments of 16 counters
+    uint4* src = reinterpret_cast<uint4*>(S.hist + wr * BLOCK + sg * 16);
+    uint32_t sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const uint4 v = src[q];
+      sum += v.x + v.y + v.z + v.w;
+    }
+    uint32_t z = 0u;   // made here, not a zero vector hoisted to kernel entry
+    asm volatile("" : "+v"(z));
+#pragma unroll
+    for (int q = 0; q < 4; q++) src[q] = make_uint4(z, z, z, z);
+    sum = row16_sum_u32(sum);
+    sum += dpp_u32<0x142, 0xa, true>(sum);   // rows 0+1 (and 2+3): valid in lanes 16..31, 48..63
+    if (sg == 31) S.tot[wr] = sum;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t c = 0, cum = 0;   // lane b: count of bin b, count of bins >= b
+#pragma unroll
+    for (int w = 0; w < SEL_ROWS; w++) {
+      const uint32_t tw = S.tot[w];
+      const uint32_t c0 = (tw & 0xffffu) - (w == 0 ? pad : 0u), c1 = tw >> 16;
+      cum += (2 * w >= lane ? c0 : 0u) + (2 * w + 1 >= lane ? c1 : 0u);
+      c += (2 * w == lane ? c0 : 0u) + (2 * w + 1 == lane ? c1 : 0u);
+    }
+    if ((uint32_t)lane >= nb) cum = c = 0u;
+    const uint64_t m = __ballot(cum >= (uint32_t)need);
+    const int bs = 63 - __clzll(m);
+    const uint32_t cb = (uint32_t)__builtin_amdgcn_readlane((int)c, bs);
+    const uint32_t cumb = (uint32_t)__builtin_amdgcn_readlane((int)cum, bs);
+    if (lane == 0) {
+      S.sv[0] = (uint32_t)bs;
+      S.sv[1] = (uint32_t)need - (cumb - cb);
+      S.sv[2] = cb;
+    }
+  }
+  __syncthreads();
+  need = (int)S.sv[1];
+  ncand = (int)S.sv[2];
+  return S.sv[0];
+}
+// Counting of NC register columns: adds the candidacy of column j's digit (val(j) >> shift) & nbm1.
+template <int NC, typename V, typename C>
+__device__ __forceinline__ void sel_count(const SelLds& S, V&& val, C&& is_cand, int shift, uint32_t nbm1) {
+  const int tid = tid_opaque();
+#pragma unroll
+  for (int j = 0; j < NC; j++) {
+    const uint32_t d = (val(j) >> shift) & nbm1;
+    const uint32_t inc = is_cand(j) ? (1u << ((d & 1u) << 4)) : 0u;
+    __hip_atomic_fetch_add(lds_ptr(&S.hist[(d >> 1) * BLOCK + tid]), inc, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+}
+// Ranks up to SEL_CMAX candidates (S.chi/clo/ctk[0, nc)) by (key desc, token asc); calls
+// taken(c, rank < need) from one lane per candidate.
+template <typename F>
+__device__ __forceinline__ void sel_rank(const SelLds& S, int nc, int need, F&& taken) {
+  const int tid = tid_opaque();
+  const int c = tid >> 2, part = tid & 3;
+  int rank = 0;
+  if (c < nc) {
+    const uint32_t h = S.chi[c], l = S.clo[c], t = S.ctk[c];
+    for (int d = part; d < nc; d += 4) {
+      const uint32_t hd = S.chi[d], ld = S.clo[d];
+      rank += (hd > h || (hd == h && (ld > l || (ld == l && S.ctk[d] < t)))) ? 1 : 0;
+    }
+  }
+  rank += __shfl_xor(rank, 1, 64);
+  rank += __shfl_xor(rank, 2, 64);
+  if (c < nc && part == 0) taken(c, rank < need);
+}
+
+// Selection over every token (the bound left more candidates than the per-wave lists
+// hold): keys reloaded into 68 registers per thread, flags per token in LDS. Kept out of
+// line so that its registers do not weigh on the rest of the kernel.
+__device__ __noinline__ void sel_all_tokens(const uint32_t* kh, const uint32_t* kl, uint64_t* isel, int T, int K,
+                                            uint32_t k1, float* act, double* red) {
+  const SelLds S = sel_carve(act);
+  const int tid = tid_opaque();
+  int need = K, ncand = T;
+  uint32_t key[SEL_MAXJ];
+#pragma unroll
+  for (int j = 0; j < SEL_MAXJ; j++) {
+    const int t = tid + j * BLOCK;
+    key[j] = t < T ? ld_u32(kh + t) : 0u;
+  }
+  for (int rr = 0; rr < SEL_ROWS; rr++) S.hist[rr * BLOCK + tid] = 0u;   // passes clear while reducing
+  uint32_t pre = 0, pm = 0;
+  const uint32_t npad = (uint32_t)(SEL_MAXJ * BLOCK - T);   // padding keys (0): bin 0 while the prefix is 0
+  {
+    int shift = 32;
+    while (ncand > SEL_CMAX && shift > 0) {
+      const int wdt = min(5, shift);
+      shift -= wdt;
+      sel_count<SEL_MAXJ>(S, [&](int j) { return key[j]; }, [&](int j) { return (key[j] & pm) == pre; }, shift,
+                          (1u << wdt) - 1u);
+      const uint32_t b = sel_finish_pass(S, 1u << wdt, pre == 0u ? npad : 0u, need, ncand);
+      pre |= b << shift;
+      pm |= ((1u << wdt) - 1u) << shift;
+    }
+  }
+  uint32_t cb0 = 0u, cb1 = 0u, cb2 = 0u;   // candidate bits per column j
+#pragma unroll
+  for (int j = 0; j < SEL_MAXJ; j++) {   // every column: the contiguous ranges below read them all
+    const uint32_t mk = key[j] & pm;
+    const bool cand = key[j] != 0u && mk == pre;
+    S.fl[tid + j * BLOCK] = (uint8_t)((key[j] != 0u && mk > pre ? 1u : 0u) | (cand ? 2u : 0u));
+    const uint32_t bt = cand ? 1u << (j & 31) : 0u;
+    if (j < 32) cb0 |= bt;
+    else if (j < 64) cb1 |= bt;
+    else cb2 |= bt;
+  }
+  auto cbit = [&](int j) -> bool { return ((j < 32 ? cb0 : j < 64 ? cb1 : cb2) >> (j & 31)) & 1u; };
+  if (ncand > SEL_CMAX) {
+    // the candidates share all 32 high bits: the same passes over the low halves
+    uint32_t lo[SEL_MAXJ];
+#pragma unroll
+    for (int j = 0; j < SEL_MAXJ; j++) lo[j] = cbit(j) ? ld_u32(kl + tid + j * BLOCK) : 0u;
+    uint32_t lpre = 0, lpm = 0;
+    int shift = 32;
+    while (ncand > SEL_CMAX && shift > 0) {
+      const int wdt = min(5, shift);
+      shift -= wdt;
+      sel_count<SEL_MAXJ>(S, [&](int j) { return lo[j]; }, [&](int j) { return cbit(j) && (lo[j] & lpm) == lpre; },
+                          shift, (1u << wdt) - 1u);
+      const uint32_t b = sel_finish_pass(S, 1u << wdt, 0u, need, ncand);
+      lpre |= b << shift;
+      lpm |= ((1u << wdt) - 1u) << shift;
+    }
+    int cut = T;   // fully equal keys beyond SEL_CMAX: the `need` lowest indices, cut found by bisection
+    if (ncand > SEL_CMAX) {
+      int lo_m = 0, hi_m = T;
+      while (lo_m < hi_m) {
+        const int mid = (lo_m + hi_m) >> 1;
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < SEL_MAXJ; j++) c += (cbit(j) && (lo[j] & lpm) == lpre && tid + j * BLOCK < mid) ? 1 : 0;
+        const double tc = block_sum((double)c, red);
+        if (tc >= (double)need) hi_m = mid;
+        else lo_m = mid + 1;
+      }
+      cut = lo_m;
+      ncand = 0;
+    }
+#pragma unroll
+    for (int j = 0; j < SEL_MAXJ; j++) {
+      if (cbit(j)) {
+        const uint32_t mk = lo[j] & lpm;
+        const int t = tid + j * BLOCK;
+        S.fl[t] = (uint8_t)(mk > lpre || (mk == lpre && ncand == 0 && t < cut) ? 1u
+                            : (mk == lpre && ncand > 0) ? 2u : 0u);
+      }
+    }
+  }
+  __syncthreads();
+  // this thread's contiguous token range [r0, r0 + SEL_MAXJ) of the flags
+  const int r0 = tid * SEL_MAXJ;
+  auto load_range = [&](uint32_t* wds) {
+#pragma unroll
+    for (int q = 0; q < SEL_MAXJ / 4; q++) wds[q] = reinterpret_cast<const uint32_t*>(S.fl + r0)[q];
+  };
+  if (ncand > 0) {
+    uint32_t wds[SEL_MAXJ / 4];
+    load_range(wds);
+    uint32_t cn = 0;
+#pragma unroll
+    for (int q = 0; q < SEL_MAXJ / 4; q++) cn += __popc((wds[q] >> 1) & 0x01010101u);
+    uint32_t o = block_excl_scan(cn, S.wsum);
+#pragma unroll
+    for (int q = 0; q < SEL_MAXJ / 4; q++) {
+      uint32_t m = (wds[q] >> 1) & 0x01010101u;
+      while (m) {
+        const int b = __ffs(m) - 1;
+        m &= m - 1u;
+        if (o < (uint32_t)SEL_CMAX) S.ctk[o] = (uint32_t)(r0 + 4 * q + (b >> 3));
+        o++;
+      }
+    }
+    __syncthreads();
+    const int nc = min(ncand, SEL_CMAX);
+    if (tid < nc) {
+      S.chi[tid] = ld_u32(kh + S.ctk[tid]);
+      S.clo[tid] = ld_u32(kl + S.ctk[tid]);
+    }
+    __syncthreads();
+    sel_rank(S, nc, need, [&](int c, bool tk) { S.fl[S.ctk[c]] = tk ? 1 : 0; });
+    __syncthreads();
+  }
+  {
+    uint32_t wds[SEL_MAXJ / 4];
+    load_range(wds);
+    uint32_t cn = 0;
+#pragma unroll
+    for (int q = 0; q < SEL_MAXJ / 4; q++) cn += __popc(wds[q] & 0x01010101u);
+    uint32_t o = block_excl_scan(cn, S.wsum);
+#pragma unroll
+    for (int q = 0; q < SEL_MAXJ / 4; q++) {
+      uint32_t m = wds[q] & 0x01010101u;
+      while (m) {
+        const int b = __ffs(m) - 1;
+        m &= m - 1u;
+        if (o < (uint32_t)K) ll_put(isel + o, (uint32_t)(r0 + 4 * q + (b >> 3)), k1);
+        o++;
+      }
+    }
+  }
+}
 
 template <class SH>
 __device__ __forceinline__ bool stage_sel_mla(Ctx& cx, const KArgs& a, const Step& st, Lds& L) {
@@ -375,228 +681,236 @@ __device__ __forceinline__ bool stage_sel_mla(Ctx& cx, const KArgs& a, const Ste
     stamp(a, cx, st, TR_SEL_DONE);
     return true;
   }
-  uint32_t* hist = reinterpret_cast<uint32_t*>(L.act);     // [32][BLOCK] packed 16-bit counters
-  uint32_t* sv = hist + 32 * BLOCK;                         // [16] scalars
-  uint32_t* tot = sv + 16;                                  // [32] bin-pair totals
-  uint32_t* cc = tot + 32;                                  // [SEL_MAXJ][NWAVES] selected per (column, wave)
-  uint32_t* lp = cc + SEL_MAXJ * NWAVES;                    // [SEL_MAXJ][NWAVES] exclusive prefix over waves
-  uint32_t* csum = lp + SEL_MAXJ * NWAVES;                  // [128] column totals
-  uint32_t* cbase = csum + 128;                             // [128] column offsets
-  uint32_t* ct = cbase + 128;                               // [SEL_CMAX] candidate token
-  uint32_t* chi = ct + SEL_CMAX;                            // [SEL_CMAX] its key, high half
-  uint32_t* clo = chi + SEL_CMAX;                           // [SEL_CMAX] low half
-  uint8_t* fl = reinterpret_cast<uint8_t*>(hist);           // [T] selection flags of candidates (after the passes)
-  if (!ll_fetch<1>(cx, hist, wsp<uint64_t>(a, a.off.idone), cx.nwg, k1, W_IDONE)) return false;
+  const SelLds S = sel_carve(L.act);
   const uint32_t* kh = wsp<uint32_t>(a, a.off.ikh);
   const uint32_t* kl = wsp<uint32_t>(a, a.off.ikl);
-  const int J = (T + BLOCK - 1) / BLOCK;
-  uint32_t key[SEL_MAXJ];
+  // the scorers' bounds: wait for every done word, take the smallest
+  if (!ll_fetch<1>(cx, S.hist, wsp<uint64_t>(a, a.off.idone), cx.nwg, k1, W_IDONE)) return false;
+  {
+    uint32_t b = tid < cx.nwg ? S.hist[tid] : 0xffffffffu;
 #pragma unroll
-  for (int j = 0; j < SEL_MAXJ; j++) {
-    const int t = tid + j * BLOCK;
-    key[j] = t < T ? ld_u32(kh + t) : 0u;
+    for (int o = 32; o >= 1; o >>= 1) b = min(b, (uint32_t)__shfl_xor((int)b, o, 64));
+    if (lane == 0) S.wsum[wave] = b;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t m = S.wsum[0];
+      for (int i = 1; i < NWAVES; i++) m = min(m, S.wsum[i]);
+      S.sv[4] = m;
+    }
+    for (int i = tid; i < SEL_BMW * BLOCK; i += BLOCK) S.bm[i] = 0u;
+    for (int rr = 0; rr < SEL_ROWS; rr++) S.hist[rr * BLOCK + tid] = 0u;   // passes clear while reducing
+    __syncthreads();
+  }
+  const uint32_t lb = S.sv[4];
+  // ---- stream the keys (chunks of SEL_CH columns) into the per-wave candidate lists
+  const int J = (T + BLOCK - 1) / BLOCK;
+  uint32_t wc = 0, mx = 0u, mn = 0xffffffffu;
+  uint32_t* wk = S.ech + wave * SEL_WCAP;
+  uint32_t* wt = S.ett + wave * SEL_WCAP;
+  // one chunk of SEL_CH keys per thread in registers at a time (a second chunk in flight
+  // would not fit the register budget of the whole kernel without spills)
+  uint32_t ka[SEL_CH];
+  auto load_chunk = [&](uint32_t* k, int c0) {
+#pragma unroll
+    for (int i = 0; i < SEL_CH; i++) {
+      const int t = tid + (c0 + i) * BLOCK;
+      k[i] = t < T ? ld_u32_off(kh, (uint32_t)t * 4u) : 0u;
+    }
+  };
+  auto compact_chunk = [&](const uint32_t* k, int c0) {
+#pragma unroll
+    for (int i = 0; i < SEL_CH; i++) {
+      const bool c = k[i] != 0u && k[i] >= lb;
+      const uint64_t m = __ballot(c);
+      if (c) {
+        const uint32_t p = wc + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (p < (uint32_t)SEL_WCAP) {
+          wk[p] = k[i];
+          wt[p] = (uint32_t)(tid_opaque() + (c0 + i) * BLOCK);   // recomputed, not kept from the load
+        }
+        mx = max(mx, k[i]);
+        mn = min(mn, k[i]);
+      }
+      wc += (uint32_t)__popcll(m);
+    }
+  };
+#pragma unroll 1
+  for (int c0 = 0; c0 < J; c0 += SEL_CH) {
+    load_chunk(ka, c0);
+    compact_chunk(ka, c0);
   }
   stamp(a, cx, st, TR_SEL_KEYS);
-  int need = K, ncand = T;
-  // one radix pass over the candidates' digits (val(j) >> shift) & (2^width - 1)
-  auto pass = [&](auto&& val, auto&& is_cand, int width, int shift) -> uint32_t {
-    const uint32_t nb = 1u << width;
-#pragma unroll 4
-    for (int r = 0; r < 32; r++) hist[r * BLOCK + tid] = 0u;
 #pragma unroll
-    for (int j = 0; j < SEL_MAXJ; j++) {
-      if (j < J && is_cand(j)) {
-        const uint32_t d = (val(j) >> shift) & (nb - 1u);
-        __hip_atomic_fetch_add(lds_ptr(&hist[(d >> 1) * BLOCK + tid]), 1u << ((d & 1u) * 16u), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
-      }
-    }
-    __syncthreads();
-    {
-      const int wr = tid >> 4, sg = tid & 15;
-      const uint4* src = reinterpret_cast<const uint4*>(hist + wr * BLOCK + sg * 32);
-      uint32_t sum = 0;
-#pragma unroll
-      for (int q = 0; q < 8; q++) {
-        const uint4 v = src[q];
-        sum += v.x + v.y + v.z + v.w;
-      }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
-      if (sg == 0) tot[wr] = sum;
-    }
-    __syncthreads();
-    if (wave == 0) {
-      const uint32_t cnt = (uint32_t)lane < nb ? (tot[lane >> 1] >> ((lane & 1) * 16)) & 0xffffu : 0u;
-      uint32_t cum = cnt;   // sum over bins >= lane
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t v = __shfl_down(cum, o, 64);
-        if (lane + o < 64) cum += v;
-      }
-      const uint64_t m = __ballot(cum >= (uint32_t)need);
-      const int bs = 63 - __clzll(m);
-      const uint32_t cb = __shfl(cnt, bs, 64), cumb = __shfl(cum, bs, 64);
-      if (lane == 0) {
-        sv[0] = (uint32_t)bs;
-        sv[1] = (uint32_t)need - (cumb - cb);
-        sv[2] = cb;
-      }
-    }
-    __syncthreads();
-    need = (int)sv[1];
-    ncand = (int)sv[2];
-    return sv[0];
-  };
-  // ---- high halves
-  uint32_t pre = 0, pm = 0;
-  {
-    constexpr int widths[6] = {6, 6, 6, 6, 6, 2};
-    int shift = 32;
-    for (int p = 0; p < 6 && ncand > SEL_CMAX; p++) {
-      const int wdt = widths[p];
-      shift -= wdt;
-      const uint32_t b = pass([&](int j) { return key[j]; },
-                              [&](int j) { return tid + j * BLOCK < T && (key[j] & pm) == pre; }, wdt, shift);
-      pre |= b << shift;
-      pm |= ((1u << wdt) - 1u) << shift;
-    }
+  for (int o = 32; o >= 1; o >>= 1) {
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
   }
-  // selection and candidate bits per (thread, column)
-  uint32_t sb[3] = {0u, 0u, 0u}, cb[3] = {0u, 0u, 0u};
-#pragma unroll
-  for (int j = 0; j < SEL_MAXJ; j++) {
-    const bool v = tid + j * BLOCK < T;
-    const uint32_t mk = key[j] & pm;
-    if (v && mk > pre) sb[j >> 5] |= 1u << (j & 31);
-    if (v && mk == pre) cb[j >> 5] |= 1u << (j & 31);
+  if (lane == 0) {
+    S.wcnt[wave] = wc;
+    S.tot[wave] = mx;
+    S.tot[8 + wave] = mn;
   }
-  auto bit = [](const uint32_t* b, int j) { return (b[j >> 5] >> (j & 31)) & 1u; };
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t X = S.tot[0], N = S.tot[8], C = S.wcnt[0], over = S.wcnt[0] > (uint32_t)SEL_WCAP;
+    for (int i = 1; i < NWAVES; i++) {
+      X = max(X, S.tot[i]);
+      N = min(N, S.tot[8 + i]);
+      C += S.wcnt[i];
+      over |= S.wcnt[i] > (uint32_t)SEL_WCAP;
+    }
+    S.sv[5] = C;
+    S.sv[6] = X;
+    S.sv[7] = N;
+    S.sv[8] = over;
+  }
+  __syncthreads();
+  if (S.sv[8]) {   // too many keys at or above the bound for the lists
+    sel_all_tokens(kh, kl, isel, T, K, k1, L.act, L.red);
+    stamp(a, cx, st, TR_SEL_DONE);
+    return true;
+  }
+  const int C = (int)S.sv[5];
+  // ---- selection among the C entries: e = tid + q*BLOCK, valid when its list has it
+  uint32_t eh[SEL_EPT];
+  uint32_t ev = 0u;   // valid bits
+#pragma unroll
+  for (int q = 0; q < SEL_EPT; q++) {
+    const int e = tid + q * BLOCK;
+    const bool v = (uint32_t)(e % SEL_WCAP) < S.wcnt[e / SEL_WCAP];
+    eh[q] = v ? S.ech[e] : 0u;
+    if (v) ev |= 1u << q;
+  }
+  const uint32_t dif = S.sv[6] ^ S.sv[7];
+  const int common = dif ? __clz(dif) : 32;   // leading bits every entry shares
+  uint32_t pm = common >= 32 ? 0xffffffffu : ~(0xffffffffu >> common);
+  uint32_t pre = S.sv[6] & pm;
+  int need = K, ncand = C;
+  int shift = 32 - common, npass = 0;
+  while (ncand > SEL_CMAX && shift > 0) {
+    const int wdt = min(5, shift);
+    shift -= wdt;
+    sel_count<SEL_EPT>(S, [&](int q) { return eh[q]; }, [&](int q) { return (ev >> q & 1u) && (eh[q] & pm) == pre; },
+                       shift, (1u << wdt) - 1u);
+    const uint32_t b = sel_finish_pass(S, 1u << wdt, 0u, need, ncand);
+    pre |= b << shift;
+    pm |= ((1u << wdt) - 1u) << shift;
+    stamp(a, cx, st, 39 + min(npass++, 5));
+  }
+  uint32_t ecb = 0u;   // candidate bits per entry column
+#pragma unroll
+  for (int q = 0; q < SEL_EPT; q++) {
+    const int e = tid + q * BLOCK;
+    const uint32_t mk = eh[q] & pm;
+    const bool v = ev >> q & 1u;
+    S.efl[e] = (uint8_t)((v && mk > pre) ? 1u : (v && mk == pre) ? 2u : 0u);
+    if (v && mk == pre) ecb |= 1u << q;
+  }
   if (ncand > SEL_CMAX) {
-    // ---- the candidates share all 32 high bits: the same passes over the low halves
-    uint32_t lo[SEL_MAXJ];
+    // ---- the candidates share the whole high half: the low halves, then the token order
+    uint32_t elo[SEL_EPT];
 #pragma unroll
-    for (int j = 0; j < SEL_MAXJ; j++) lo[j] = bit(cb, j) ? ld_u32(kl + tid + j * BLOCK) : 0u;
+    for (int q = 0; q < SEL_EPT; q++) elo[q] = (ecb >> q & 1u) ? ld_u32(kl + S.ett[tid + q * BLOCK]) : 0u;
     uint32_t lpre = 0, lpm = 0;
-    constexpr int widths[6] = {6, 6, 6, 6, 6, 2};
-    int shift = 32;
-    for (int p = 0; p < 6 && ncand > SEL_CMAX; p++) {
-      const int wdt = widths[p];
-      shift -= wdt;
-      const uint32_t b = pass([&](int j) { return lo[j]; },
-                              [&](int j) { return bit(cb, j) && (lo[j] & lpm) == lpre; }, wdt, shift);
-      lpre |= b << shift;
-      lpm |= ((1u << wdt) - 1u) << shift;
+    int ls = 32;
+    while (ncand > SEL_CMAX && ls > 0) {
+      const int wdt = min(5, ls);
+      ls -= wdt;
+      sel_count<SEL_EPT>(S, [&](int q) { return elo[q]; },
+                         [&](int q) { return (ecb >> q & 1u) && (elo[q] & lpm) == lpre; }, ls, (1u << wdt) - 1u);
+      const uint32_t b = sel_finish_pass(S, 1u << wdt, 0u, need, ncand);
+      lpre |= b << ls;
+      lpm |= ((1u << wdt) - 1u) << ls;
     }
-#pragma unroll
-    for (int j = 0; j < SEL_MAXJ; j++) {
-      if (bit(cb, j)) {
-        const uint32_t mk = lo[j] & lpm;
-        if (mk > lpre) sb[j >> 5] |= 1u << (j & 31);
-        if (mk != lpre) cb[j >> 5] &= ~(1u << (j & 31));
-      }
-    }
-    if (ncand > SEL_CMAX) {
-      // ---- equal 64-bit keys: the `need` lowest token indices, cut M found by bisection
+    int cut = 0;
+    if (ncand > SEL_CMAX) {   // equal 64-bit keys: the `need` lowest tokens, cut found by bisection
       int lo_m = 0, hi_m = T;
       while (lo_m < hi_m) {
         const int mid = (lo_m + hi_m) >> 1;
-        int cnt = 0;
+        int c = 0;
 #pragma unroll
-        for (int j = 0; j < SEL_MAXJ; j++) cnt += (bit(cb, j) && tid + j * BLOCK < mid) ? 1 : 0;
-        const double tc = block_sum((double)cnt, L.red);
+        for (int q = 0; q < SEL_EPT; q++)
+          c += ((ecb >> q & 1u) && (elo[q] & lpm) == lpre && S.ett[tid + q * BLOCK] < (uint32_t)mid) ? 1 : 0;
+        const double tc = block_sum((double)c, L.red);
         if (tc >= (double)need) hi_m = mid;
         else lo_m = mid + 1;
       }
-#pragma unroll
-      for (int j = 0; j < SEL_MAXJ; j++)
-        if (bit(cb, j) && tid + j * BLOCK < lo_m) sb[j >> 5] |= 1u << (j & 31);
+      cut = lo_m;
       ncand = 0;
     }
+#pragma unroll
+    for (int q = 0; q < SEL_EPT; q++) {
+      if (ecb >> q & 1u) {
+        const int e = tid + q * BLOCK;
+        const uint32_t mk = elo[q] & lpm;
+        S.efl[e] = (uint8_t)((mk > lpre || (mk == lpre && ncand == 0 && S.ett[e] < (uint32_t)cut)) ? 1u
+                             : (mk == lpre && ncand > 0) ? 2u : 0u);
+      }
+    }
   }
+  __syncthreads();
   if (ncand > 0) {
-    // ---- at most SEL_CMAX candidates: rank each by (key desc, index asc) on full keys
-    if (tid == 0) sv[3] = 0u;
-    __syncthreads();
+    // ---- at most SEL_CMAX candidates: rank by (key desc, token asc) on full keys
+    const uint32_t* f4 = reinterpret_cast<const uint32_t*>(S.efl + tid * SEL_EPT);
+    uint32_t fw[SEL_EPT / 4];
+    uint32_t cn = 0;
 #pragma unroll
-    for (int j = 0; j < SEL_MAXJ; j++) {
-      if (bit(cb, j)) {
-        const uint32_t i = __hip_atomic_fetch_add(lds_ptr(&sv[3]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        if (i < (uint32_t)SEL_CMAX) ct[i] = (uint32_t)(tid + j * BLOCK);
+    for (int q = 0; q < SEL_EPT / 4; q++) {
+      fw[q] = f4[q];
+      cn += __popc((fw[q] >> 1) & 0x01010101u);
+    }
+    uint32_t o = block_excl_scan(cn, S.wsum);
+#pragma unroll
+    for (int q = 0; q < SEL_EPT / 4; q++) {
+      uint32_t m = (fw[q] >> 1) & 0x01010101u;
+      while (m) {
+        const int b = __ffs(m) - 1;
+        m &= m - 1u;
+        if (o < (uint32_t)SEL_CMAX) S.cix[o] = (uint32_t)(tid * SEL_EPT + 4 * q + (b >> 3));
+        o++;
       }
     }
     __syncthreads();
-    const int nc = min((int)sv[3], SEL_CMAX);
+    const int nc = min(ncand, SEL_CMAX);
     if (tid < nc) {
-      chi[tid] = ld_u32(kh + ct[tid]);
-      clo[tid] = ld_u32(kl + ct[tid]);
+      const uint32_t e = S.cix[tid];
+      S.chi[tid] = S.ech[e];
+      S.ctk[tid] = S.ett[e];
+      S.clo[tid] = ld_u32(kl + S.ett[e]);
     }
     __syncthreads();
-    {
-      const int c = tid >> 2, part = tid & 3;
-      int rank = 0;
-      if (c < nc) {
-        const uint32_t h = chi[c], l = clo[c], t = ct[c];
-        for (int d = part; d < nc; d += 4) {
-          const uint32_t hd = chi[d], ld = clo[d];
-          rank += (hd > h || (hd == h && (ld > l || (ld == l && ct[d] < t)))) ? 1 : 0;
-        }
-      }
-      rank += __shfl_xor(rank, 1, 64);
-      rank += __shfl_xor(rank, 2, 64);
-      if (c < nc && part == 0) fl[ct[c]] = rank < need ? 1 : 0;
-    }
+    stamp(a, cx, st, 45);
+    sel_rank(S, nc, need, [&](int c, bool tk) { S.efl[S.cix[c]] = tk ? 1 : 0; });
     __syncthreads();
-#pragma unroll
-    for (int j = 0; j < SEL_MAXJ; j++)
-      if (bit(cb, j) && fl[tid + j * BLOCK]) sb[j >> 5] |= 1u << (j & 31);
   }
+  // ---- taken entries into the token bitmap, then the output in ascending token order
+#pragma unroll
+  for (int q = 0; q < SEL_EPT; q++) {
+    const int e = tid + q * BLOCK;
+    if (S.efl[e] == 1) {
+      const uint32_t t = S.ett[e];
+      __hip_atomic_fetch_or(lds_ptr(&S.bm[t >> 5]), 1u << (t & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+  __syncthreads();
   stamp(a, cx, st, TR_SEL_PASSES);
-  // ---- emit the chosen tokens in ascending order: t = tid + j*BLOCK orders as (j, wave, lane)
+  {
+    uint32_t bw[SEL_BMW];
+    uint32_t cn = 0;
 #pragma unroll
-  for (int j = 0; j < SEL_MAXJ; j++) {
-    if (j < J) {
-      const uint64_t m = __ballot(bit(sb, j));
-      if (lane == 0) cc[j * NWAVES + wave] = (uint32_t)__popcll(m);
+    for (int q = 0; q < SEL_BMW; q++) {
+      bw[q] = S.bm[tid * SEL_BMW + q];
+      cn += __popc(bw[q]);
     }
-  }
-  __syncthreads();
-  if (tid < J) {
-    uint32_t s = 0;
+    uint32_t o = block_excl_scan(cn, S.wsum);
 #pragma unroll
-    for (int w = 0; w < NWAVES; w++) {
-      const uint32_t v = cc[tid * NWAVES + w];
-      lp[tid * NWAVES + w] = s;
-      s += v;
-    }
-    csum[tid] = s;
-  }
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t x0 = lane < J ? csum[lane] : 0u, x1 = lane + 64 < J ? csum[lane + 64] : 0u;
-    const uint32_t c0 = x0, c1 = x1;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t v0 = __shfl_up(x0, o, 64), v1 = __shfl_up(x1, o, 64);
-      if (lane >= o) {
-        x0 += v0;
-        x1 += v1;
-      }
-    }
-    const uint32_t t0s = __shfl(x0, 63, 64);
-    if (lane < J) cbase[lane] = x0 - c0;
-    if (lane + 64 < J) cbase[lane + 64] = t0s + x1 - c1;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < SEL_MAXJ; j++) {
-    if (j < J) {
-      const uint32_t b = bit(sb, j);
-      const uint64_t m = __ballot(b);
-      if (b) {
-        const uint32_t below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        const uint32_t off = cbase[j] + lp[j * NWAVES + wave] + below;
-        if (off < (uint32_t)K) ll_put(isel + off, (uint32_t)(tid + j * BLOCK), k1);
+    for (int q = 0; q < SEL_BMW; q++) {
+      uint32_t m = bw[q];
+      while (m) {
+        const int b = __ffs(m) - 1;
+        m &= m - 1u;
+        if (o < (uint32_t)K) ll_put(isel + o, (uint32_t)((tid * SEL_BMW + q) * 32 + b), k1);
+        o++;
       }
     }
   }

@@ -199,3 +199,55 @@ def test_sparse_two_layer_stack_one_launch():
     say(f"2-layer sparse stack rel err {err:.3e}")
     assert err < TOL
     assert np.array_equal(dec.debug("isel").cpu().numpy()[:128], rec["index_sel"]), "layer 1 selection"
+
+
+def _full_cache_case(tag, edit):
+    """The full 32768-token cache with the host and device index keys edited the same way."""
+    s = configs.C4
+    dec, Ws, Cs = _decoder(s, [(0, 0)])
+    hc = host_cache(s)
+    edit(hc)
+    Cs[0]["index_codes"].copy_(torch.from_numpy(hc["index_codes"]).cuda())
+    Cs[0]["index_scales"].copy_(torch.from_numpy(hc["index_scales"]).cuda())
+    torch.cuda.synchronize()
+    from synth import device as sdev
+    out = _run_step(dec, s, 0, sdev.input_hidden(s, 0, 0), s.cache_len)
+    rec = oracle_step(s, 0, 0, hc, gen.input_hidden(s, 0, 0), s.cache_len)
+    _check_layer(dec, s, rec, out, s.cache_len, Cs[0], tag)
+    return rec
+
+
+def test_sparse_selection_weak_bound_all_tokens():
+    """Tokens t with t % 256 < 128 get scales 2^-20 smaller: half of the scoring workgroups
+    hold only tiny keys, the published bound admits more than 8192 keys, and the selection
+    runs over every token (distinct keys)."""
+    _need_gpu()
+    say("case: sparse selection, weak bound (half the scales x 2^-20), top-2048 of 32769")
+
+    def edit(hc):
+        t = np.arange(configs.C4.cache_len)
+        hc["index_scales"][: configs.C4.cache_len] = np.where(
+            t % 256 < 128, hc["index_scales"][: configs.C4.cache_len] * np.float32(2.0 ** -20),
+            hc["index_scales"][: configs.C4.cache_len]).astype(np.float32)
+
+    rec = _full_cache_case("weak bound", edit)
+    sc = rec["index_score"]
+    say(f"  {np.count_nonzero(sc > 0)} positive scores, {np.unique(sc).size} distinct")
+
+
+def test_sparse_selection_massive_tie_all_tokens():
+    """Only every 16th token keeps its key codes; the other ~30700 score exactly 0, so the
+    top-2048 cut falls inside a tie far larger than any candidate list and is decided by
+    token index over every token."""
+    _need_gpu()
+    say("case: sparse selection, ~30700 tied zero keys, top-2048 of 32769")
+
+    def edit(hc):
+        n = configs.C4.cache_len
+        keep = np.arange(n) % 16 == 0
+        hc["index_codes"][:n][~keep] = 0
+
+    rec = _full_cache_case("massive tie", edit)
+    sc = rec["index_score"]
+    say(f"  {np.count_nonzero(sc > 0)} tokens score above 0, {np.count_nonzero(sc == 0)} score 0")
+    assert np.count_nonzero(sc > 0) < 2048 <= np.count_nonzero(sc >= 0)
