@@ -42,6 +42,9 @@ WORKLOADS = {   # name -> (synth.configs attribute, traffic file stem, dtype of 
                                            "bf16 weights, fp32 accumulate; indexer scores fp64"),
     # 24 stacked FP8 MLA layers + FP8 LM head, greedy loop over 256 tokens in one launch
     "mla_stack24_fp8_greedy256": ("C5", "traffic_mla_stack24_fp8", "fp8-e4m3 weights, fp32 accumulate, fp64 head"),
+    # the same stack, one 6-position speculative verify per launch (seeded drafts)
+    "mla_stack24_fp8_verify6": ("C5", "traffic_mla_stack24_fp8_verify6",
+                                "fp8-e4m3 weights, fp32 accumulate, fp64 head"),
 }
 DEFAULT_WORKLOAD = "gqa_moe_bf16_decode_layer"
 KERNEL_SOURCES = [os.path.join(ROOT, "persistent_latency_bound_amd", "csrc", f)
@@ -224,6 +227,75 @@ def run_stack(args):
     print(json.dumps(line), flush=True)
 
 
+def run_verify(args):
+    """One launch = one 6-position verify through every layer and the head (seeded drafts).
+    Reported per verify step, per layer, and as tokens/s at an acceptance length of six."""
+    import torch
+    import persistent_latency_bound_amd as pld
+    from oracle import accounting
+    from synth import configs, device as sdev, gen
+    m = configs.C5
+    L = m.layer
+    nq = m.n_verify
+    pos0 = L.cache_len
+    Ws = [sdev.layer_weights(L, 0, l) for l in range(m.n_layers)]
+    Cs = [sdev.kv_cache(L, 0, l) for l in range(m.n_layers)]
+    head = {"embed": sdev.embedding(m), "final_norm": sdev.final_norm(m), "head": sdev.head(m)}
+    dec = pld.Decoder(L, Ws, Cs, head=head, vocab=m.vocab)
+    out = torch.zeros(L.hidden, dtype=torch.int16, device="cuda")
+    toks = torch.zeros(nq, dtype=torch.int32, device="cuda")
+    acc = torch.zeros(1, dtype=torch.int32, device="cuda")
+    drafts = torch.tensor([int(d) for d in gen.draft_tokens(m, nq - 1)], dtype=torch.int32, device="cuda")
+    tok0 = gen.first_token(m)
+    torch.cuda.synchronize()
+
+    def one():
+        dec.persistent(start_pos=pos0, in_token=tok0, n_query=nq, draft_tokens=drafts, out_hidden=out,
+                       out_tokens=toks, out_accepted=acc)
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    if dec.status().code != 0:
+        raise SystemExit("device status after warm-up")
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t_wall = time.perf_counter()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        one()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    if dec.status().code != 0:
+        raise SystemExit("device status after the timed launches")
+    ms = ev[0].elapsed_time(ev[-1]) / args.steps
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+    layer_b = accounting.verify_layer_bytes(L, pos0, nq) * m.n_layers
+    head_b = accounting.head_bytes(L.hidden, m.vocab)   # the head matrix once per verify step
+    achieved = (layer_b + head_b) / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "batch-1 decode us/layer (achieved HBM TB/s vs peak, implied tokens/s/user)",
+        "value": round(ms * 1e3 / m.n_layers, 3), "unit": "us/layer (6-position verify step)", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": WORKLOADS[args.workload][2], "data": "synthetic",
+        "config": {"workload": args.workload, "layers": m.n_layers, "positions_per_verify": nq, "start_pos": pos0,
+                   "vocab": m.vocab, "hidden": L.hidden, "batch": 1,
+                   "expected_union_routed_experts": round(
+                       accounting.expected_union_experts(L.n_experts, L.top_k, nq), 2)},
+        "ms_per_verify_step": round(ms, 3),
+        "tokens_per_s_user_at_AL6": round(nq / (ms * 1e-3), 1),
+        "accepted_drafts_last_step": int(acc.item()),
+        "p90_ms_per_launch": round(per[min(len(per) - 1, int(0.9 * len(per)))], 3),
+        "achieved_TBps": round(achieved / 1e3, 3), "frac_of_peak": round(achieved / PEAK_HBM_GBPS, 4),
+        "algorithmic_bytes_per_launch": int(layer_b + head_b), "wall_s_timed_region": round(wall, 3),
+        "implementation": "positions run as sequential steps inside the launch (weights read once per position)",
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -246,6 +318,8 @@ def main():
 
     if args.workload == "mla_stack24_fp8_greedy256":
         return run_stack(args)
+    if args.workload == "mla_stack24_fp8_verify6":
+        return run_verify(args)
 
     import torch
     import persistent_latency_bound_amd as pld

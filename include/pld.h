@@ -144,11 +144,15 @@ typedef struct pld_device_status {
 
 typedef struct pld_persistent_args {
   int32_t start_pos;          /* cache position of the first token */
-  int32_t n_tokens;           /* tokens to decode in this launch (greedy loop when a head is present) */
-  int32_t n_query;            /* 1; >1 = multi-position verify (head required) */
-  int32_t in_token;           /* >= 0: first input is embed[in_token]; < 0: use in_hidden */
+  int32_t n_tokens;           /* tokens to decode in this launch (greedy loop when a head is present);
+                                 must be 1 when n_query > 1 */
+  int32_t n_query;            /* 1; >1 = verify n_query positions in one launch (head required) */
+  int32_t in_token;           /* >= 0: first input is embed[in_token]; < 0: use in_hidden
+                                 (verify: the last accepted token, required) */
   const void* in_hidden;      /* bf16 [hidden] first input when in_token < 0 */
-  const int32_t* draft_tokens;/* verify: device int32 [n_query-1] */
+  const int32_t* draft_tokens;/* verify: device int32 [n_query-1], 4-byte aligned; draft j feeds
+                                 position start_pos + j + 1. Ids outside [0, vocab) are never
+                                 accepted (their embedding row is read at the clamped id). */
   void* out_hidden;           /* bf16 [hidden]: output of the last layer for the last position */
   float* out_logits;          /* fp32 [n_tokens or n_query][vocab], or NULL */
   int32_t* out_tokens;        /* int32 [n_tokens or n_query] greedy tokens, or NULL */
@@ -193,6 +197,14 @@ pld_status decode_step(pld_handle* h, int32_t layer, const void* x_in, int32_t p
  * verify positions), every layer of the stack in order, then (with a head) final
  * RMSNorm -> LM head -> greedy argmax (lowest id on ties) -> embedding of the chosen
  * token as the next input. Asynchronous on `stream`.
+ * Verify (n_query > 1): positions start_pos .. start_pos + n_query - 1 are fed in_token,
+ * then the drafts; every position's logits and argmax are written; out_accepted[0] =
+ * the number of leading drafts equal to the argmax of the position before them
+ * (greedy acceptance, the speculative decoding with a draft of six tokens in the vLLM
+ * Kimi K3 backend article). Rows of all n_query positions are appended; the caller
+ * continues at start_pos + out_accepted[0] + 1 and later launches overwrite the rest.
+ * The positions run as sequential steps inside the launch (the plain definition of a
+ * causal multi-token verify).
  * Errors: PLD_E_INVALID, PLD_E_UNSUPPORTED (verify without head), PLD_E_CAPACITY,
  * PLD_E_STATE, PLD_E_HIP. */
 pld_status decode_layers_persistent(pld_handle* h, const pld_persistent_args* a, void* stream);

@@ -83,3 +83,23 @@ def layer_bytes(s: LayerShape, pos: int) -> int:
 
 def head_bytes(hidden: int, vocab: int, fmt: str = "fp8") -> int:
     return _mat_bytes(vocab, hidden, fmt) + 4 * hidden + 2 * hidden   # head, final gain, embedding row
+
+
+def expected_union_experts(n_experts: int, top_k: int, n_query: int) -> float:
+    """Expected number of distinct routed experts over n_query positions that each pick top_k
+    of n_experts, under uniform independent routing: E * (1 - (1 - k/E)^n)."""
+    return n_experts * (1.0 - (1.0 - top_k / n_experts) ** n_query)
+
+
+def verify_layer_bytes(s: LayerShape, pos: int, n_query: int) -> float:
+    """Algorithmic bytes of one layer in an n_query-position verify (positions pos..pos+n-1):
+    attention weights and the cache rows once, the expected union of the positions' routed
+    experts plus the shared ones, the n appended rows and the n input/output vectors."""
+    g = layer_weight_bytes(s)
+    f = s.wfmt
+    one_expert = 2 * _mat_bytes(s.inter, s.hidden, f) + _mat_bytes(s.hidden, s.inter, f)
+    experts = (expected_union_experts(s.n_experts, s.top_k, n_query) + s.n_shared) * one_expert
+    other = sum(v for k, v in g.items() if k != "experts")
+    last = pos + n_query - 1
+    kv = layer_kv_bytes(s, last)["kv_read"] + n_query * layer_kv_bytes(s, last)["kv_write"]
+    return other + experts + kv + n_query * 2 * 2 * s.hidden

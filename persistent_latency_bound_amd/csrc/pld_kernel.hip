@@ -107,6 +107,8 @@ struct KArgs {
   int32_t* out_tokens;     // [n_tokens] or null
   int in_token;            // >= 0: first input is embed[in_token]
   int head_on;             // run the head after the last layer of every token
+  const int32_t* drafts;   // verify: [n_tokens - 1] draft tokens fed to positions 1.., or null
+  int32_t* out_accepted;   // verify: [1] accepted draft count, or null
 };
 
 // ------------------------------------------------------------------ device context
@@ -1634,10 +1636,12 @@ struct HeadArgs {
   int on, in_token;
   float* out_logits;
   int32_t* out_tokens;
+  const int32_t* drafts;
+  int32_t* out_accepted;
 };
 
 static pld_status launch(pld_handle* h, int layer0, int n_layers, int n_tokens, int pos0, const void* in_hidden,
-                         void* out_hidden, hipStream_t s, HeadArgs hd = {0, -1, nullptr, nullptr}) {
+                         void* out_hidden, hipStream_t s, HeadArgs hd = {0, -1, nullptr, nullptr, nullptr, nullptr}) {
   KArgs a;
   memset(&a, 0, sizeof(a));
   a.c = h->kc;
@@ -1657,6 +1661,8 @@ static pld_status launch(pld_handle* h, int layer0, int n_layers, int n_tokens, 
   a.in_token = hd.in_token;
   a.out_logits = hd.out_logits;
   a.out_tokens = hd.out_tokens;
+  a.drafts = hd.drafts;
+  a.out_accepted = hd.out_accepted;
   a.embed = h->embed;
   a.fnorm = h->fnorm;
   a.head = h->head;
@@ -1685,16 +1691,27 @@ pld_status decode_step(pld_handle* h, int32_t layer, const void* x_in, int32_t p
 pld_status decode_layers_persistent(pld_handle* h, const pld_persistent_args* a, void* stream) {
   if (!h || !a) return PLD_E_INVALID;
   if (h->bad) return PLD_E_STATE;
-  if (a->n_tokens < 1 || a->n_query != 1) return a->n_query > 1 ? PLD_E_UNSUPPORTED : PLD_E_INVALID;
   const bool head = h->cfg.vocab > 0;
+  if (a->n_tokens < 1 || a->n_query < 1) return PLD_E_INVALID;
+  const bool verify = a->n_query > 1;
+  if (verify) {
+    // n_query positions start_pos.. fed in_token then the n_query - 1 drafts; one verify per launch
+    if (!head) return PLD_E_UNSUPPORTED;
+    if (a->n_tokens != 1 || a->in_token < 0 || !a->draft_tokens || ((uintptr_t)a->draft_tokens & 3u))
+      return PLD_E_INVALID;
+  } else if (a->draft_tokens || a->out_accepted) {
+    return PLD_E_INVALID;
+  }
+  const int n_pos = verify ? a->n_query : a->n_tokens;
   if (!head && (a->in_token >= 0 || a->n_tokens != 1 || a->out_logits || a->out_tokens))
     return PLD_E_INVALID;   // embedding input, several tokens and logits/tokens need the LM head
   if (a->in_token >= h->cfg.vocab && head) return PLD_E_INVALID;
   if (a->in_token < 0 && (!a->in_hidden || !aligned16(a->in_hidden))) return PLD_E_INVALID;
   if (!a->out_hidden || !aligned16(a->out_hidden)) return PLD_E_INVALID;
-  if (a->start_pos < 0 || a->start_pos + a->n_tokens > h->cfg.max_seq) return PLD_E_CAPACITY;
-  HeadArgs hd{head ? 1 : 0, head ? a->in_token : -1, a->out_logits, a->out_tokens};
-  return launch(h, 0, h->n_layers, a->n_tokens, a->start_pos, a->in_token >= 0 ? nullptr : a->in_hidden, a->out_hidden,
+  if (a->start_pos < 0 || a->start_pos + n_pos > h->cfg.max_seq) return PLD_E_CAPACITY;
+  HeadArgs hd{head ? 1 : 0, head ? a->in_token : -1, a->out_logits, a->out_tokens,
+              verify ? a->draft_tokens : nullptr, verify ? a->out_accepted : nullptr};
+  return launch(h, 0, h->n_layers, n_pos, a->start_pos, a->in_token >= 0 ? nullptr : a->in_hidden, a->out_hidden,
                 (hipStream_t)stream, hd);
 }
 

@@ -1355,6 +1355,10 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_mla(KArgs a) {
     __syncthreads();
   }
   int token = a.in_token;   // greedy decode loop: the token whose embedding feeds the next layer 0
+  // verify (a.drafts set): position t > 0 is fed draft t-1 instead of the argmax; greedy
+  // acceptance counts the leading drafts that equal the argmax of the position before
+  int accepted = 0;
+  bool accepting = true;
   for (int t = 0; t < a.n_tokens; t++) {
     for (int li = 0; li < a.n_layers; li++) {
       cx.layer = a.layer0 + li;
@@ -1394,7 +1398,17 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_mla(KArgs a) {
       if (!stage_ffn<SH>(cs, as, st, L)) return;
       if (!stage_down<SH>(cs, as, st, L, last ? as.out_hidden : nullptr)) return;
       if constexpr (SH::FP8) {
-        if (a.head_on && li == a.n_layers - 1 && !stage_head<SH>(cs, as, st, L, t, &token)) return;
+        if (a.head_on && li == a.n_layers - 1) {
+          if (!stage_head<SH>(cs, as, st, L, t, &token)) return;
+          if (a.drafts && t + 1 < a.n_tokens) {
+            const int d = gp(a.drafts)[t];   // caller's draft for position t + 1
+            accepting = accepting && d == token;
+            accepted += accepting ? 1 : 0;
+            token = min(max(d, 0), a.c.vocab - 1);   // an out-of-range draft is never accepted; its row is clamped
+          }
+          if (a.drafts && t + 1 == a.n_tokens && cs.w == 0 && tid_opaque() == 0 && a.out_accepted)
+            gp(a.out_accepted)[0] = accepted;
+        }
       }
       trace_flush(as, cs, st);
     }

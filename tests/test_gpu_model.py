@@ -108,3 +108,63 @@ def test_greedy_loop_with_head():
         if to != toks[t]:
             assert abs(lo[to] - lo[toks[t]]) <= TOL * np.max(np.abs(lo)), f"token {t}: decisive difference"
         tin = toks[t]
+
+
+def _verify(dec, m, pos, tok, drafts):
+    V = m.vocab
+    n = len(drafts) + 1
+    out = torch.zeros(m.layer.hidden, dtype=torch.int16, device="cuda")
+    lg = torch.zeros((n, V), dtype=torch.float32, device="cuda")
+    tk = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    acc = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    dr = torch.tensor(list(drafts), dtype=torch.int32, device="cuda")
+    dec.persistent(start_pos=pos, in_token=tok, n_query=n, draft_tokens=dr, out_hidden=out, out_logits=lg,
+                   out_tokens=tk, out_accepted=acc)
+    torch.cuda.synchronize()
+    st = dec.status()
+    assert st.code == 0, f"device status {st.code} wait {st.stage} layer {st.layer} token {st.token} wg {st.wg}"
+    return lg.cpu().numpy(), [int(v) for v in tk.cpu().numpy()], int(acc.item())
+
+
+def test_verify_six_positions():
+    """Six-position verify in one launch: position j > 0 is fed draft j-1, every position's
+    logits and argmax come out, and greedy acceptance counts the leading drafts equal to
+    the argmax before them. Drafts that follow the greedy continuation give the greedy
+    run's logits bit for bit; a wrong draft stops the acceptance; the oracle's verify
+    step agrees within TOL (same tokens unless two logits are within TOL)."""
+    _need_gpu()
+    m = _model(n_layers=2, cache_len=100, n_tokens=6)
+    pos, n = 100, 6
+    tok0 = gen.first_token(m)
+    say(f"case: 2-layer FP8 MLA stack + head, verify {n} positions at pos {pos} from token {tok0}")
+    decG = _decoder(m)
+    _, lgG, tkG = _launch(decG, m, pos, tok0, n)   # greedy reference: 6 tokens, one launch
+    say(f"greedy tokens: {tkG}")
+    # all drafts follow the greedy continuation: everything accepted, logits identical
+    decA = _decoder(m)
+    lgA, tkA, accA = _verify(decA, m, pos, tok0, tkG[:5])
+    say(f"verify (greedy drafts): tokens {tkA}, accepted {accA}")
+    assert accA == 5 and tkA == tkG
+    assert np.array_equal(lgA, lgG), "verify logits differ from the greedy launch"
+    # a wrong draft at position 4: three accepted, positions 0..3 as in the greedy run
+    wrong = (tkG[3] + 1) % m.vocab
+    drafts = [tkG[0], tkG[1], tkG[2], wrong, tkG[4]]
+    decB = _decoder(m)
+    lgB, tkB, accB = _verify(decB, m, pos, tok0, drafts)
+    say(f"verify (wrong draft 4): tokens {tkB}, accepted {accB}")
+    assert accB == 3, accB
+    assert np.array_equal(lgB[:4], lgG[:4]) and tkB[:4] == tkG[:4]
+    # the oracle's verify step on the same drafts
+    Wl = [gen.LayerWeights(m.layer, 0, l) for l in range(m.n_layers)]
+    caches = [host_cache(m.layer, 0, l) for l in range(m.n_layers)]
+    ref = OM.verify_step(m.layer, Wl, caches, lambda t: gen.embedding_rows(m, [t])[0], gen.head_matrix(m),
+                         gen.final_norm(m), tok0, drafts, pos)
+    say(f"oracle verify: tokens {ref['tokens']}, accepted {ref['accepted']}")
+    assert ref["accepted"] == accB
+    for j in range(n):
+        e = rel_err(lgB[j], ref["logits"][j])
+        say(f"position {j}: logits rel err {e:.2e}")
+        assert e < TOL, j
+        if ref["tokens"][j] != tkB[j]:
+            lo = ref["logits"][j]
+            assert abs(lo[ref["tokens"][j]] - lo[tkB[j]]) <= TOL * np.max(np.abs(lo)), f"position {j}: decisive"

@@ -497,3 +497,17 @@ def test_layer_residuals_closed_form():
     h = nx.bf16_to_f64(x)
     f = OL.ffn(s, base, nx.rmsnorm(h, base.norm("ffn_norm"), s.eps), {})
     assert np.allclose(rec2["out_f64"], h + f, rtol=1e-13, atol=1e-13)
+
+
+def test_expected_union_of_routed_experts_by_enumeration():
+    """E * (1 - (1 - k/E)^n) equals the mean number of distinct experts over every
+    combination of n independent top-k choices (uniform routing), enumerated exactly."""
+    import itertools
+    from oracle import accounting
+    for E, k, n in [(4, 2, 2), (5, 2, 3), (6, 3, 2)]:
+        subsets = list(itertools.combinations(range(E), k))
+        tot = 0
+        for combo in itertools.product(subsets, repeat=n):
+            tot += len(set().union(*combo))
+        mean = tot / len(subsets) ** n
+        assert abs(mean - accounting.expected_union_experts(E, k, n)) < 1e-12, (E, k, n)
