@@ -182,9 +182,12 @@ __device__ __forceinline__ bool ll_fetch(Ctx& cx, uint32_t* dst, const uint64_t*
 #pragma unroll
         for (int j = 0; j < PER; j++)
           if (pend >> j & 1u) v[j] = ld_u64_off(src, (uint32_t)idx(base + j * BLOCK + tid) * 8u);
+        // (a mask of the words that arrived, built with shifts: constant masks ~(1 << j)
+        // would be hoisted into registers that stay live across the whole kernel)
+        uint32_t got = 0;
 #pragma unroll
-        for (int j = 0; j < PER; j++)
-          if ((uint32_t)(v[j] >> 32) == ep) pend &= ~(1u << j);
+        for (int j = 0; j < PER; j++) got |= (uint32_t)((uint32_t)(v[j] >> 32) == ep) << j;
+        pend &= ~got;
         if ((++it & 15) == 0 && pend) {
           if (ld_u32(cx.status + ST_ABORT)) { failed = 1; break; }
           if (wall_clock64() > deadline) { raise_timeout(cx.status, wid, cx.layer, cx.token, cx.w); failed = 1; break; }
@@ -898,20 +901,41 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
       return false;
     stamp(a, cx, st, TR_RT_READY);
     // top-k by rank: expert e is selected at position rank(e) = #{j : key_j > key_e or
-    // (key_j == key_e and j < e)} when that rank is < topk (lowest index wins ties)
+    // (key_j == key_e and j < e)} when that rank is < topk (lowest index wins ties).
+    // Keys become order-preserving 64-bit integers (x >= 0: bits | 2^63, x < 0: ~bits;
+    // -0 folded into +0), and each expert's comparisons are split over P = BLOCK / E
+    // thread partitions so that every thread of the workgroup counts.
     const bool sig = c.router == PLD_ROUTER_SIGMOID_BIAS;
-    for (int e = tid_opaque(); e < c.E; e += BLOCK) {
-      const double ke = lk[2 * e + 1];
+    {
+      uint64_t* uk = reinterpret_cast<uint64_t*>(L.outc);         // [E] keys (outc is free here)
+      int* rk = reinterpret_cast<int*>(uk + c.E);                  // [P][E] partial ranks
+      for (int e = tid_opaque(); e < c.E; e += BLOCK) {
+        const double ke = lk[2 * e + 1];
+        const uint64_t b = (uint64_t)__double_as_longlong(ke == 0.0 ? 0.0 : ke);
+        uk[e] = (b >> 63) ? ~b : (b | (1ull << 63));
+      }
+      __syncthreads();
+      const int P = BLOCK / c.E;                  // host: E divides BLOCK
+      const int seg = c.E / P;
+      const int tid = tid_opaque();
+      const int e = tid % c.E, p = tid / c.E;
+      const uint64_t ue = uk[e];
       int rank = 0;
-      // (E is a multiple of 8: the unrolled reads of 8 keys are in flight together)
-      for (int j0 = 0; j0 < c.E; j0 += 8) {
+      // (seg is a multiple of 8: the unrolled reads of 8 keys are in flight together)
+      for (int j0 = p * seg; j0 < (p + 1) * seg; j0 += 8) {
 #pragma unroll
         for (int j = j0; j < j0 + 8; j++) {
-          const double kj = lk[2 * j + 1];
-          rank += (kj > ke) || (kj == ke && j < e);
+          const uint64_t uj = uk[j];
+          rank += (uj > ue || (uj == ue && j < e)) ? 1 : 0;
         }
       }
-      if (rank < c.topk) L.isel[rank] = e;
+      rk[p * c.E + e] = rank;
+      __syncthreads();
+      for (int ee = tid; ee < c.E; ee += BLOCK) {
+        int r = 0;
+        for (int pp = 0; pp < P; pp++) r += rk[pp * c.E + ee];
+        if (r < c.topk) L.isel[r] = ee;
+      }
     }
     __syncthreads();
     stamp(a, cx, st, TR_TOPK);
@@ -1295,7 +1319,9 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
   if (c->ffn_kind == PLD_FFN_DENSE) {
     k->slots = 1;
   } else if (c->ffn_kind == PLD_FFN_MOE) {
-    if (c->n_experts < 8 || c->n_experts > nwg || c->n_experts > 512 || c->n_experts % 8) return PLD_E_UNSUPPORTED;
+    if (c->n_experts < 8 || c->n_experts > nwg || c->n_experts > 512 || c->n_experts % 8 || BLOCK % c->n_experts ||
+        (c->n_experts / (BLOCK / c->n_experts)) % 8)
+      return PLD_E_UNSUPPORTED;
     if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts) return PLD_E_UNSUPPORTED;
     if (c->n_shared < 0 || c->n_shared > 2) return PLD_E_UNSUPPORTED;
     if (c->router_kind != PLD_ROUTER_SOFTMAX_TOPK && c->router_kind != PLD_ROUTER_SIGMOID_BIAS) return PLD_E_UNSUPPORTED;
@@ -1326,7 +1352,8 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
     k->act_floats = (int)al(act, 64);
     k->stage_words = (int)al(c->hidden / 2 + 2, 64);
     int outb = std::max({R / nwg + 4, k->slots * (c->hidden / nwg + 4), 2 * ((k->slots * c->inter) / nwg + 2),
-                         2 * (c->inter / nwg + 2) * std::max(1, c->n_shared), 4 * c->n_experts + 4});
+                         2 * (c->inter / nwg + 2) * std::max(1, c->n_shared), 4 * c->n_experts + 4,
+                         2 * c->n_experts + BLOCK});
     k->outb_floats = (int)al(outb, 64);
     if (lds_bytes_for(k->act_floats, k->stage_words, k->outb_floats) > 160 * 1024) return PLD_E_UNSUPPORTED;
     k->rdim = c->head_dim;
@@ -1376,7 +1403,8 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
     const int f64x = sparse ? 2 : 1;   // fp64 row results take two floats
     int outb = std::max({f64x * (rx / nwg + 4), f64x * (rq / nwg + 4), NH * VD / nwg + 4, c->hidden / nwg + 4,
                          k->slots * (c->hidden / nwg + 4), 2 * ((k->slots * c->inter) / nwg + 2),
-                         2 * (c->inter / nwg + 2) * std::max(1, c->n_shared), 4 * c->n_experts + 4});
+                         2 * (c->inter / nwg + 2) * std::max(1, c->n_shared), 4 * c->n_experts + 4,
+                         2 * c->n_experts + BLOCK});
     k->outb_floats = (int)al(outb, 64);
     if (lds_bytes_for(k->act_floats, k->stage_words, k->outb_floats) > 160 * 1024) return PLD_E_UNSUPPORTED;
   } else {

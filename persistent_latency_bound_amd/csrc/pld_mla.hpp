@@ -508,7 +508,7 @@ __device__ __forceinline__ void sel_count(const SelLds& S, V&& val, C&& is_cand,
 #pragma unroll
   for (int j = 0; j < NC; j++) {
     const uint32_t d = (val(j) >> shift) & nbm1;
-    const uint32_t inc = is_cand(j) ? (1u << ((d & 1u) << 4)) : 0u;
+    const uint32_t inc = (uint32_t)is_cand(j) << ((d & 1u) << 4);
     __hip_atomic_fetch_add(lds_ptr(&S.hist[(d >> 1) * BLOCK + tid]), inc, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_WORKGROUP);
   }
@@ -567,7 +567,7 @@ __device__ __noinline__ void sel_all_tokens(const uint32_t* kh, const uint32_t* 
     const uint32_t mk = key[j] & pm;
     const bool cand = key[j] != 0u && mk == pre;
     S.fl[tid + j * BLOCK] = (uint8_t)((key[j] != 0u && mk > pre ? 1u : 0u) | (cand ? 2u : 0u));
-    const uint32_t bt = cand ? 1u << (j & 31) : 0u;
+    const uint32_t bt = (uint32_t)cand << (j & 31);
     if (j < 32) cb0 |= bt;
     else if (j < 64) cb1 |= bt;
     else cb2 |= bt;
@@ -668,24 +668,48 @@ __device__ __noinline__ void sel_all_tokens(const uint32_t* kh, const uint32_t* 
   }
 }
 
-template <class SH>
-__device__ __forceinline__ bool stage_sel_mla(Ctx& cx, const KArgs& a, const Step& st, Lds& L) {
-  if (cx.w != SEL_WG) return true;
-  const uint32_t k1 = st.k1;
+// Everything the selecting workgroup needs, passed by value to the out-of-line selection.
+struct SelArgs {
+  uint64_t* isel;
+  const uint32_t* kh;
+  const uint32_t* kl;
+  const uint64_t* idone;
+  uint32_t* status;
+  long long budget;
+  int nwg, layer, token, w, T, K;
+  uint32_t k1;
+  int red_off, tr_off;   // float offsets of L.red and L.tr from the LDS base (L.act is the base)
+  int tron;              // device trace on for this step
+};
+
+// The selection proper (the selecting workgroup, T > K), kept out of line: its registers
+// and constants stay inside this function instead of weighing on the whole kernel.
+// Returns 0 when a wait expired or another workgroup aborted.
+__device__ __noinline__ int sel_select(SelArgs sa) {
+  extern __shared__ float lds_raw[];
+  float* act = lds_raw;
+  double* red = reinterpret_cast<double*>(lds_raw + sa.red_off);
+  uint64_t* tr = reinterpret_cast<uint64_t*>(lds_raw + sa.tr_off);
+  Ctx cx;
+  cx.budget = sa.budget;
+  cx.w = sa.w;
+  cx.nwg = sa.nwg;
+  cx.status = sa.status;
+  cx.layer = sa.layer;
+  cx.token = sa.token;
+  const uint32_t k1 = sa.k1;
   const int tid = tid_opaque(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int T = st.pos + 1, K = min(a.c.itopk, T);
-  uint64_t* isel = wsp<uint64_t>(a, a.off.isel);
-  if (T <= K) {   // every token
-    for (int j = tid; j < T; j += BLOCK) ll_put(isel + j, (uint32_t)j, k1);
-    stamp(a, cx, st, TR_SEL_DONE);
-    return true;
-  }
-  const SelLds S = sel_carve(L.act);
-  const uint32_t* kh = wsp<uint32_t>(a, a.off.ikh);
-  const uint32_t* kl = wsp<uint32_t>(a, a.off.ikl);
+  const int T = sa.T, K = sa.K;
+  uint64_t* isel = sa.isel;
+  auto stp = [&](int slot) {
+    if (sa.tron && tid_opaque() == 0) tr[slot] = wall_clock64();
+  };
+  const SelLds S = sel_carve(act);
+  const uint32_t* kh = sa.kh;
+  const uint32_t* kl = sa.kl;
   // the scorers' bounds: wait for every done word, take the smallest
-  if (!ll_fetch<1>(cx, S.hist, wsp<uint64_t>(a, a.off.idone), cx.nwg, k1, W_IDONE)) return false;
+  if (!ll_fetch<1>(cx, S.hist, sa.idone, cx.nwg, k1, W_IDONE)) return 0;
   {
     uint32_t b = tid < cx.nwg ? S.hist[tid] : 0xffffffffu;
 #pragma unroll
@@ -739,7 +763,7 @@ __device__ __forceinline__ bool stage_sel_mla(Ctx& cx, const KArgs& a, const Ste
     load_chunk(ka, c0);
     compact_chunk(ka, c0);
   }
-  stamp(a, cx, st, TR_SEL_KEYS);
+  stp(TR_SEL_KEYS);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
@@ -766,9 +790,9 @@ __device__ __forceinline__ bool stage_sel_mla(Ctx& cx, const KArgs& a, const Ste
   }
   __syncthreads();
   if (S.sv[8]) {   // too many keys at or above the bound for the lists
-    sel_all_tokens(kh, kl, isel, T, K, k1, L.act, L.red);
-    stamp(a, cx, st, TR_SEL_DONE);
-    return true;
+    sel_all_tokens(kh, kl, isel, T, K, k1, act, red);
+    stp(TR_SEL_DONE);
+    return 1;
   }
   const int C = (int)S.sv[5];
   // ---- selection among the C entries: e = tid + q*BLOCK, valid when its list has it
@@ -779,7 +803,7 @@ __device__ __forceinline__ bool stage_sel_mla(Ctx& cx, const KArgs& a, const Ste
     const int e = tid + q * BLOCK;
     const bool v = (uint32_t)(e % SEL_WCAP) < S.wcnt[e / SEL_WCAP];
     eh[q] = v ? S.ech[e] : 0u;
-    if (v) ev |= 1u << q;
+    ev |= (uint32_t)v << q;   // (shift form: a literal mask would be hoisted into a register)
   }
   const uint32_t dif = S.sv[6] ^ S.sv[7];
   const int common = dif ? __clz(dif) : 32;   // leading bits every entry shares
@@ -795,7 +819,7 @@ __device__ __forceinline__ bool stage_sel_mla(Ctx& cx, const KArgs& a, const Ste
     const uint32_t b = sel_finish_pass(S, 1u << wdt, 0u, need, ncand);
     pre |= b << shift;
     pm |= ((1u << wdt) - 1u) << shift;
-    stamp(a, cx, st, 39 + min(npass++, 5));
+    stp(39 + min(npass++, 5));
   }
   uint32_t ecb = 0u;   // candidate bits per entry column
 #pragma unroll
@@ -804,7 +828,7 @@ __device__ __forceinline__ bool stage_sel_mla(Ctx& cx, const KArgs& a, const Ste
     const uint32_t mk = eh[q] & pm;
     const bool v = ev >> q & 1u;
     S.efl[e] = (uint8_t)((v && mk > pre) ? 1u : (v && mk == pre) ? 2u : 0u);
-    if (v && mk == pre) ecb |= 1u << q;
+    ecb |= (uint32_t)(v && mk == pre) << q;
   }
   if (ncand > SEL_CMAX) {
     // ---- the candidates share the whole high half: the low halves, then the token order
@@ -831,7 +855,7 @@ __device__ __forceinline__ bool stage_sel_mla(Ctx& cx, const KArgs& a, const Ste
 #pragma unroll
         for (int q = 0; q < SEL_EPT; q++)
           c += ((ecb >> q & 1u) && (elo[q] & lpm) == lpre && S.ett[tid + q * BLOCK] < (uint32_t)mid) ? 1 : 0;
-        const double tc = block_sum((double)c, L.red);
+        const double tc = block_sum((double)c, red);
         if (tc >= (double)need) hi_m = mid;
         else lo_m = mid + 1;
       }
@@ -879,7 +903,7 @@ __device__ __forceinline__ bool stage_sel_mla(Ctx& cx, const KArgs& a, const Ste
       S.clo[tid] = ld_u32(kl + S.ett[e]);
     }
     __syncthreads();
-    stamp(a, cx, st, 45);
+    stp(45);
     sel_rank(S, nc, need, [&](int c, bool tk) { S.efl[S.cix[c]] = tk ? 1 : 0; });
     __syncthreads();
   }
@@ -893,7 +917,7 @@ __device__ __forceinline__ bool stage_sel_mla(Ctx& cx, const KArgs& a, const Ste
     }
   }
   __syncthreads();
-  stamp(a, cx, st, TR_SEL_PASSES);
+  stp(TR_SEL_PASSES);
   {
     uint32_t bw[SEL_BMW];
     uint32_t cn = 0;
@@ -914,8 +938,38 @@ __device__ __forceinline__ bool stage_sel_mla(Ctx& cx, const KArgs& a, const Ste
       }
     }
   }
-  stamp(a, cx, st, TR_SEL_DONE);
-  return true;
+  stp(TR_SEL_DONE);
+  return 1;
+}
+
+template <class SH>
+__device__ __forceinline__ bool stage_sel_mla(Ctx& cx, const KArgs& a, const Step& st, Lds& L) {
+  if (cx.w != SEL_WG) return true;
+  const int T = st.pos + 1, K = min(a.c.itopk, T);
+  uint64_t* isel = wsp<uint64_t>(a, a.off.isel);
+  if (T <= K) {   // every token
+    for (int j = tid_opaque(); j < T; j += BLOCK) ll_put(isel + j, (uint32_t)j, st.k1);
+    stamp(a, cx, st, TR_SEL_DONE);
+    return true;
+  }
+  SelArgs sa;
+  sa.isel = isel;
+  sa.kh = wsp<uint32_t>(a, a.off.ikh);
+  sa.kl = wsp<uint32_t>(a, a.off.ikl);
+  sa.idone = wsp<uint64_t>(a, a.off.idone);
+  sa.status = cx.status;
+  sa.budget = cx.budget;
+  sa.nwg = cx.nwg;
+  sa.layer = cx.layer;
+  sa.token = cx.token;
+  sa.w = cx.w;
+  sa.T = T;
+  sa.K = K;
+  sa.k1 = st.k1;
+  sa.red_off = (int)(reinterpret_cast<float*>(L.red) - L.act);
+  sa.tr_off = (int)(reinterpret_cast<float*>(L.tr) - L.act);
+  sa.tron = (a.trace && st.idx < a.trace_steps) ? 1 : 0;
+  return sel_select(sa) != 0;
 }
 
 // ------------------------------------------------------------------ ABS: q_lat_h = W_UK_h^T q_nope_h
