@@ -102,7 +102,7 @@ SLOT_NAMES = {32: "head_ready", 33: "head_gemv", 34: "token", 0: "start", 1: "x_
               26: "merge_fetched", 27: "router_logit", 28: "att_drained", 30: "att_scores", 17: "blk0_staged", 31: "blk0_done",
               35: "idx_done", 36: "sel_keys", 37: "sel_passes", 38: "sel_done", 39: "sel_pass0", 40: "sel_pass1",
               41: "sel_pass2", 42: "sel_pass3", 43: "sel_pass4", 44: "sel_pass5", 45: "sel_rank_loaded",
-              46: "sel_keys_arrived"}
+              46: "sel_lists_arrived"}
 
 
 def write_trace_summary(dec, x, out, R, path, pos):

@@ -68,7 +68,7 @@ class PldPersistentArgs(ctypes.Structure):
 
 
 # intermediates kept as LL words (32-bit payload, 32-bit epoch) in the workspace
-LL_BUFFERS = ("q", "o", "h2", "logits", "m", "x", "cq", "ckv", "qrope", "qlat", "olat", "qi", "ixr", "isel")
+LL_BUFFERS = ("q", "o", "h2", "logits", "m", "x", "cq", "ckv", "qrope", "qlat", "olat", "qi", "ixr", "isel", "ilist")
 
 _lib = None
 
@@ -254,7 +254,8 @@ class Decoder:
         if name in LL_BUFFERS:   # 8-byte LL words: keep the 32-bit payloads (low halves)
             raw = raw.view(torch.int32)[0::2].contiguous().view(torch.uint8)
         default = {"logits": torch.float64, "sel": torch.int32, "x": torch.int16, "qi": torch.int16,
-                   "isel": torch.int32, "ikh": torch.int32, "ikl": torch.int32}
+                   "isel": torch.int32, "ikh": torch.int32, "ikl": torch.int32,
+                   "ilist": torch.int32, "ilo": torch.int32, "itok": torch.int32}
         if name == "cq" and getattr(self.shape, "index_topk", 0):
             default["cq"] = torch.float64   # the sparse layer passes c_q' in fp64 (word pairs)
         return raw.view(dtype or default.get(name, torch.float32))

@@ -219,6 +219,23 @@ __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t x) {
   x += dpp_u32<0x143, 0xc, true>(x);
   return x;
 }
+// Wave-wide min / max of u32 with DPP moves (a lane keeps its own value where a move does
+// not write it); the result, from lane 63, in every lane.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_keep_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, CTRL, ROW_MASK, 0xf, false);
+}
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t v) {
+  auto op = [](uint32_t a, uint32_t b) { return MAX ? max(a, b) : min(a, b); };
+  v = op(v, dpp_keep_u32<0xB1, 0xf>(v));
+  v = op(v, dpp_keep_u32<0x4E, 0xf>(v));
+  v = op(v, dpp_keep_u32<0x141, 0xf>(v));
+  v = op(v, dpp_keep_u32<0x140, 0xf>(v));
+  v = op(v, dpp_keep_u32<0x142, 0xa>(v));
+  v = op(v, dpp_keep_u32<0x143, 0xc>(v));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
 // Sum over each row of 16 lanes, valid in every lane of the row.
 __device__ __forceinline__ uint32_t row16_sum_u32(uint32_t x) {
   x += dpp_u32<0xB1, 0xf, false>(x);
@@ -226,6 +243,15 @@ __device__ __forceinline__ uint32_t row16_sum_u32(uint32_t x) {
   x += dpp_u32<0x141, 0xf, false>(x);
   x += dpp_u32<0x140, 0xf, false>(x);
   return x;
+}
+
+// Wave-wide sum of u32: row sums, then rows 0+1 and 2+3 (row_bcast15), then all four
+// (row_bcast31, valid in rows 2-3); the result, from lane 63, in every lane.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  x = row16_sum_u32(x);
+  x += dpp_u32<0x142, 0xa, true>(x);
+  x += dpp_u32<0x143, 0xc, true>(x);
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, 63);
 }
 
 // fp64 sum over groups of 64 lanes with DPP moves applied to both 32-bit halves (same

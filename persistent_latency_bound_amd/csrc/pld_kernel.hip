@@ -42,7 +42,7 @@ namespace pld {
 // ------------------------------------------------------------------ shared structs
 // Watchdog wait ids (pld_device_status.stage): which LL activation a workgroup waited for.
 enum WaitId { W_X = 0, W_QKV = 1, W_KV = 2, W_PART = 3, W_O = 4, W_H2 = 5, W_RT = 6, W_M = 7, W_CQ = 8,
-              W_QN = 9, W_QLAT = 10, W_OLAT = 11, W_AMAX = 12, W_IX = 13, W_IDONE = 14, W_ISEL = 15 };
+              W_QN = 9, W_QLAT = 10, W_OLAT = 11, W_AMAX = 12, W_IX = 13, W_ILIST = 14, W_ISEL = 15 };
 enum { ST_CODE = 0, ST_STAGE = 1, ST_LAYER = 2, ST_TOKEN = 3, ST_WG = 4, ST_ABORT = 8 };
 // device trace: wall-clock stamps per (step, workgroup)
 enum TraceSlot {
@@ -84,8 +84,8 @@ struct DLayer {
 // Workspace layout. The LL buffers (8-byte words: payload | epoch << 32) follow the
 // status words; both are zeroed at init and by decode_reset.
 struct WsOff {
-  size_t status, x, q, kv, part, o, h2, logits, m, cqr, ckvr, qr, qlat, olat, amax, ixr, qi, idone, isel, ll_end, sel,
-      gates, a_dbg, b_dbg, ikh, ikl, rope, layers, total;
+  size_t status, x, q, kv, part, o, h2, logits, m, cqr, ckvr, qr, qlat, olat, amax, ixr, qi, ilist, isel, ll_end, sel,
+      gates, a_dbg, b_dbg, ikh, ikl, ilo, itok, rope, layers, total;
 };
 
 struct KArgs {
@@ -1385,13 +1385,14 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
                         c->nope_dim + (BLOCK / (k->cpw / epc)) * k->cpw + nope_rows,
                         k->cpg * k->cpw + 4 * k->cpg + 8});
     if (sparse) {
-      // indexer: 8 heads x 64 dims (4 lanes x 2 heads per token); selection keys per thread;
-      // one workgroup's done-word fetch; selected rows per chunk (LL fetch, one pass)
+      // indexer: 8 heads x 64 dims (4 lanes x 2 heads per token); selection: every scoring
+      // workgroup's list in LDS, keys per thread on the all-token path; selected rows per
+      // chunk (LL fetch, one pass)
       if (c->index_heads != 8 || c->index_dim != 64 || c->index_topk < 1) return PLD_E_UNSUPPORTED;
-      if (c->max_seq > SEL_MAXJ * BLOCK || c->max_seq > SEL_LKMAX * nwg || nwg > BLOCK || srows_max > BLOCK ||
+      if (c->max_seq > SEL_MAXJ * BLOCK || c->max_seq > SEL_LKMAX * nwg || nwg > SEL_MAXWG || srows_max > BLOCK ||
           srows_max > 8 * TB)
         return PLD_E_UNSUPPORTED;
-      const int idx_words = 2 * (c->index_heads * c->index_dim + c->index_heads) + 2 * SEL_LKMAX +
+      const int idx_words = 2 * (c->index_heads * c->index_dim + c->index_heads) + 2 * SEL_LKMAX + SEL_LIST +
                             c->index_heads * c->index_dim / 2 + c->index_heads + c->index_dim + c->index_dim / 4 + 3;
       act = std::max({act, 3 * c->q_lora, SEL_LDS_WORDS, idx_words});
       if (c->q_lora + LAT + c->index_heads + c->index_dim < nwg) return PLD_E_UNSUPPORTED;
@@ -1451,10 +1452,10 @@ WsOff layout(const KCfg& k, int n_layers) {
   if (k.itopk > 0) {
     o.ixr = p; p += al((size_t)(k.ih + k.idim) * W);       // indexer head weights w and new key k_I (fp32)
     o.qi = p; p += al((size_t)(k.ih * k.idim / 2) * W);    // indexer queries (bf16 pairs)
-    o.idone = p; p += al((size_t)k.nwg * W);               // per-workgroup "keys stored"
+    o.ilist = p; p += al((size_t)k.nwg * SEL_LIST * W);    // per-workgroup top key high halves, rank order
     o.isel = p; p += al((size_t)k.itopk * W);              // selected rows, ascending
   } else {
-    o.ixr = o.qi = o.idone = o.isel = 0;
+    o.ixr = o.qi = o.ilist = o.isel = 0;
   }
   o.ll_end = p;
   o.sel = p; p += al(64 * 4);
@@ -1464,8 +1465,10 @@ WsOff layout(const KCfg& k, int n_layers) {
   if (k.itopk > 0) {
     o.ikh = p; p += al((size_t)k.max_seq * 4);   // indexer score keys, high and low halves
     o.ikl = p; p += al((size_t)k.max_seq * 4);
+    o.ilo = p; p += al((size_t)k.nwg * SEL_LIST * 4);   // list entries: low halves and tokens
+    o.itok = p; p += al((size_t)k.nwg * SEL_LIST * 4);
   } else {
-    o.ikh = o.ikl = 0;
+    o.ikh = o.ikl = o.ilo = o.itok = 0;
   }
   o.rope = p; p += al((size_t)k.max_seq * std::max(k.rdim, 2) * 4);
   o.layers = p; p += al((size_t)n_layers * sizeof(DLayer));
@@ -1798,6 +1801,9 @@ pld_status pld_debug_buffer(pld_handle* h, const char* name, void** ptr, size_t*
       {"isel", h->off.isel, (size_t)k.itopk * 8},
       {"ikh", h->off.ikh, (size_t)k.max_seq * 4},
       {"ikl", h->off.ikl, (size_t)k.max_seq * 4},
+      {"ilist", h->off.ilist, (size_t)k.nwg * SEL_LIST * 8},
+      {"ilo", h->off.ilo, (size_t)k.nwg * SEL_LIST * 4},
+      {"itok", h->off.itok, (size_t)k.nwg * SEL_LIST * 4},
   };
   for (auto& e : tab)
     if (!strcmp(e.n, name)) {

@@ -224,11 +224,12 @@ __device__ __forceinline__ bool stage_q_mla(Ctx& cx, const KArgs& a, const Step&
 // a sample of the whole cache); four lanes per token, each with two heads. The workgroup
 // holding the new token encodes its key (fp32 scale amax/448, fp32 quotient, E4M3 round to
 // nearest even) and appends it to the cache. Scores leave as order-preserving 64-bit keys
-// (two u32 halves, coherent stores), then one LL "done" word per workgroup whose payload
-// is the high half of the workgroup's r-th largest key, r = ceil(K / nwg): every workgroup
-// holds r keys at or above its own, so the K-th largest key of all is at least the
-// smallest of these, and the selector can discard every key below that bound.
+// (two u32 halves, coherent stores, read only when the selection falls back to every
+// token). Each workgroup then ranks its own keys and publishes its SEL_LIST largest as a
+// list: the high halves as LL words in rank order, the low halves and token indices in
+// plain memory written before them (0 marks an empty slot: no score's key is 0).
 constexpr int SEL_LKMAX = 256;   // keys per scoring workgroup: T <= SEL_LKMAX * nwg
+constexpr int SEL_LIST = 40;     // keys each scoring workgroup publishes, in rank order
 template <class SH>
 __device__ __forceinline__ bool stage_idx_mla(Ctx& cx, const KArgs& a, const Step& st, Lds& L) {
   constexpr int IH = SH::IH, ID = SH::ID;
@@ -239,11 +240,9 @@ __device__ __forceinline__ bool stage_idx_mla(Ctx& cx, const KArgs& a, const Ste
   const int tid = tid_opaque();
   const int pos = st.pos, T = pos + 1, nwg = cx.nwg, w = cx.w;
   const int nt = w < T ? (T - 1 - w) / nwg + 1 : 0;   // this workgroup's tokens w + i*nwg, i < nt
-  const int K = min(a.c.itopk, T);
-  const int r = (K + nwg - 1) / nwg;
-  uint64_t* idone = wsp<uint64_t>(a, a.off.idone);
-  if (nt == 0) {   // no tokens here: a done word without a bound (the selector waits for every workgroup)
-    if (tid == 0) ll_put(idone + w, 0u, k1);
+  uint64_t* ilist = wsp<uint64_t>(a, a.off.ilist) + (size_t)w * SEL_LIST;
+  if (nt == 0) {   // no tokens here: an empty list (the selector reads every workgroup's)
+    if (tid < SEL_LIST) ll_put(ilist + tid, 0u, k1);
     return true;
   }
   const int fresh = a.pos0;   // rows >= fresh were written inside this launch
@@ -254,7 +253,7 @@ __device__ __forceinline__ bool stage_idx_mla(Ctx& cx, const KArgs& a, const Ste
   uint64_t* lk = reinterpret_cast<uint64_t*>(wd + IH);      // [SEL_LKMAX] this workgroup's keys
   uint32_t* raw = reinterpret_cast<uint32_t*>(lk + SEL_LKMAX);   // [IH*ID/2] q_I bf16 pairs, [IH] w, [ID] k_I
   uint32_t* ncw = raw + IH * ID / 2 + IH + ID;              // [ID/4] code words of the new row, [1] its scale
-  uint32_t* mv = ncw + ID / 4 + 2;                          // [1] high half of the local r-th largest key
+  uint32_t* lhi = ncw + ID / 4 + 2;                         // [SEL_LIST] high halves of the published list
   const int hp = tid & 3;
   // key rows of both rounds (a workgroup has at most 2 * TPR tokens), issued before the
   // wait for q_I so that neither round pays its own load latency afterwards
@@ -288,7 +287,7 @@ __device__ __forceinline__ bool stage_idx_mla(Ctx& cx, const KArgs& a, const Ste
     qd[k * IH + h] = (double)((i & 1) ? bf_hi(pr) : bf_lo(pr));
   }
   if (tid < IH) wd[tid] = (double)__uint_as_float(raw[IH * ID / 2 + tid]);
-  if (tid == 0) mv[0] = 0u;   // no bound unless this workgroup holds r keys
+  if (tid < SEL_LIST) lhi[tid] = 0u;   // entries past this workgroup's tokens stay padding (0)
   if (owner && tid < 64) {   // one wave: the new key row (ID == 64 lanes)
     const float k = __uint_as_float(raw[IH * ID / 2 + IH + tid]);
     const float amax = wave_max(fabsf(k));
@@ -356,7 +355,9 @@ __device__ __forceinline__ bool stage_idx_mla(Ctx& cx, const KArgs& a, const Ste
     }
   }
   __syncthreads();
-  if (nt >= r) {   // the local r-th largest key: rank by (key desc, index asc), four lanes per key
+  {   // local ranks (key desc, token asc), four lanes per key; the top SEL_LIST form the list
+    uint32_t* llo = wsp<uint32_t>(a, a.off.ilo) + (size_t)w * SEL_LIST;
+    uint32_t* ltk = wsp<uint32_t>(a, a.off.itok) + (size_t)w * SEL_LIST;
     for (int c0 = 0; c0 < nt; c0 += TPR) {
       const int c = c0 + (tid >> 2);
       int rank = 0;
@@ -371,12 +372,16 @@ __device__ __forceinline__ bool stage_idx_mla(Ctx& cx, const KArgs& a, const Ste
       }
       rank += __shfl_xor(rank, 1, 64);
       rank += __shfl_xor(rank, 2, 64);
-      if (c < nt && hp == 0 && rank == r - 1) mv[0] = (uint32_t)(kc >> 32);
+      if (c < nt && hp == 0 && rank < SEL_LIST) {
+        lhi[rank] = (uint32_t)(kc >> 32);
+        st_u32(llo + rank, (uint32_t)kc);
+        st_u32(ltk + rank, (uint32_t)(w + c * nwg));
+      }
     }
   }
-  vm_wait();
+  vm_wait();   // key halves, list low halves and tokens (and a new key row) before the list words
   __syncthreads();
-  if (tid == 0) ll_put(idone + w, mv[0], k1);
+  if (tid < SEL_LIST) ll_put(ilist + tid, lhi[tid], k1);
   stamp(a, cx, st, TR_IDX_DONE);
   return true;
 }
@@ -384,13 +389,13 @@ __device__ __forceinline__ bool stage_idx_mla(Ctx& cx, const KArgs& a, const Ste
 // ------------------------------------------------------------------ SEL: exact top-k of the indexer keys
 // One workgroup selects the K = min(topk, T) largest keys (ties to the lower token index,
 // the order the selection is defined with) and publishes the chosen token indices in
-// ascending order as LL words. Thread tid owns tokens tid + j*BLOCK (coalesced loads of
-// the keys' high halves); a padding key is 0, which no score's key can be.
-//  * Bound: every chosen key is at least the smallest of the scorers' published bounds.
-//    The tokens whose high half reaches it are compacted into per-wave LDS lists (ballot
-//    offsets, a running count per wave) while the keys stream through in chunks. Up to
-//    SEL_WCAP per wave are selected from there, 16 entries per thread; a larger set goes to
-//    sel_all_tokens, which takes the same steps over every token.
+// ascending order as LL words.
+//  * Bound: with r = ceil(K / nwg), every scorer holds r keys at or above its r-th largest,
+//    so the K-th largest key of all is at least the smallest of those r-th keys (0 if a
+//    scorer holds fewer than r). A scorer's unlisted keys are at most its last listed key;
+//    when that key's high half is below the bound for every scorer, the lists hold every
+//    key that can be chosen and the selection runs over the list entries alone (20 per
+//    thread). Otherwise sel_all_tokens takes the same steps over every token.
 //  * Radix select, most significant digit first (5-bit digits, starting below the bits
 //    all candidates share): each pass adds every entry's candidacy into per-lane private
 //    16-bit counters in LDS (lane-owned columns: no atomic contention, no bank conflicts,
@@ -402,18 +407,17 @@ __device__ __forceinline__ bool stage_idx_mla(Ctx& cx, const KArgs& a, const Ste
 //  * Taken tokens are set in an LDS bitmap; the output walks it in contiguous per-thread
 //    ranges with one block-wide exclusive scan, which gives ascending order.
 constexpr int SEL_WG = 0;
-constexpr int SEL_MAXJ = 68;                  // token columns per thread: T <= SEL_MAXJ * BLOCK
-constexpr int SEL_CH = 17;                    // columns per load chunk
-constexpr int SEL_WCAP = 1024;                // compacted entries per wave
-constexpr int SEL_CAP = SEL_WCAP * NWAVES;
-constexpr int SEL_EPT = SEL_CAP / BLOCK;      // entries per thread
+constexpr int SEL_MAXJ = 68;                  // all-token path: token columns per thread, T <= SEL_MAXJ * BLOCK
+constexpr int SEL_MAXWG = 256;                // scoring workgroups whose lists fit the LDS region
+constexpr int SEL_LENT = SEL_MAXWG * SEL_LIST;   // list entries
+constexpr int SEL_EPT = SEL_LENT / BLOCK;     // list entries per thread
 constexpr int SEL_CMAX = 128;                 // candidates ranked directly
 constexpr int SEL_ROWS = 16;                  // counter words per lane: 32 bins of 16 bits
 constexpr int SEL_BMW = 3;                    // bitmap words per thread: tokens [96 tid, 96 tid + 96)
-static_assert(SEL_MAXJ % SEL_CH == 0 && SEL_BMW * 32 >= SEL_MAXJ && SEL_EPT % 4 == 0, "selector tiling");
-// LDS words: counters | entry keys | entry tokens | entry flags | bitmap | scalars | rank lists
-constexpr int SEL_LDS_WORDS = SEL_ROWS * BLOCK + 2 * SEL_CAP + SEL_CAP / 4 + SEL_BMW * BLOCK + 64 + 4 * SEL_CMAX;
-static_assert(SEL_MAXJ * BLOCK / 4 <= 2 * SEL_CAP, "all-token flags share the entry region");
+static_assert(SEL_LENT % BLOCK == 0 && SEL_BMW * 32 >= SEL_MAXJ && SEL_EPT % 4 == 0, "selector tiling");
+// LDS words: counters | fetched lists | entry flags | token bitmap | scalars | rank lists
+constexpr int SEL_LDS_WORDS = SEL_ROWS * BLOCK + SEL_LENT + SEL_LENT / 4 + SEL_BMW * BLOCK + 64 + 4 * SEL_CMAX;
+static_assert(SEL_MAXJ * BLOCK / 4 <= SEL_LENT, "all-token flags share the list region");
 
 // Exclusive prefix sum of v over the workgroup (thread order); every thread must call.
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum) {
@@ -429,22 +433,20 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum) 
 }
 
 struct SelLds {
-  uint32_t *hist, *ech, *ett, *bm, *sv, *tot, *wsum, *wcnt, *chi, *clo, *ctk, *cix;
+  uint32_t *hist, *lst, *bm, *sv, *tot, *wsum, *chi, *clo, *ctk, *cix;
   uint8_t *efl, *fl;
 };
 __device__ __forceinline__ SelLds sel_carve(float* act) {
   SelLds S;
   S.hist = reinterpret_cast<uint32_t*>(act);     // [SEL_ROWS][BLOCK] packed 16-bit counters
-  S.ech = S.hist + SEL_ROWS * BLOCK;              // [SEL_CAP] entry keys (high halves), per-wave lists
-  S.ett = S.ech + SEL_CAP;                        // [SEL_CAP] entry tokens
-  S.fl = reinterpret_cast<uint8_t*>(S.ech);      // [SEL_MAXJ*BLOCK] token flags (all-token path)
-  S.efl = reinterpret_cast<uint8_t*>(S.ett + SEL_CAP);   // [SEL_CAP] entry flags
-  S.bm = reinterpret_cast<uint32_t*>(S.efl + SEL_CAP);   // [SEL_BMW*BLOCK] taken tokens
+  S.lst = S.hist + SEL_ROWS * BLOCK;              // [SEL_LENT] list entries: key high halves
+  S.fl = reinterpret_cast<uint8_t*>(S.lst);      // [SEL_MAXJ*BLOCK] token flags (all-token path)
+  S.efl = reinterpret_cast<uint8_t*>(S.lst + SEL_LENT);   // [SEL_LENT] entry flags
+  S.bm = reinterpret_cast<uint32_t*>(S.efl + SEL_LENT);   // [SEL_BMW*BLOCK] taken tokens
   S.sv = S.bm + SEL_BMW * BLOCK;                  // [16] scalars
   S.tot = S.sv + 16;                              // [16] bin-pair totals
-  S.wsum = S.tot + 16;                            // [16] scan partials
-  S.wcnt = S.wsum + 16;                           // [16] per-wave entry counts
-  S.chi = S.wcnt + 16;                            // [SEL_CMAX] ranked candidates: key high half
+  S.wsum = S.tot + 16;                            // [32] scan / reduction partials
+  S.chi = S.wsum + 32;                            // [SEL_CMAX] ranked candidates: key high half
   S.clo = S.chi + SEL_CMAX;                       //   low half
   S.ctk = S.clo + SEL_CMAX;                       //   token
   S.cix = S.ctk + SEL_CMAX;                       //   entry
@@ -477,21 +479,21 @@ __device__ __forceinline__ uint32_t sel_finish_pass(const SelLds& S, uint32_t nb
   }
   __syncthreads();
   if (wave == 0) {
-    uint32_t c = 0, cum = 0;   // lane b: count of bin b, count of bins >= b
-#pragma unroll
-    for (int w = 0; w < SEL_ROWS; w++) {
-      const uint32_t tw = S.tot[w];
-      const uint32_t c0 = (tw & 0xffffu) - (w == 0 ? pad : 0u), c1 = tw >> 16;
-      cum += (2 * w >= lane ? c0 : 0u) + (2 * w + 1 >= lane ? c1 : 0u);
-      c += (2 * w == lane ? c0 : 0u) + (2 * w + 1 == lane ? c1 : 0u);
+    // lane L holds bin nb-1-L, so the inclusive scan over lanes counts the bins at or above
+    // it; the first lane where that reaches need holds the bin of the need-th largest
+    const int bn = (int)nb - 1 - lane;
+    uint32_t c = 0u;
+    if (bn >= 0) {
+      const uint32_t tw = S.tot[bn >> 1];
+      c = ((bn & 1) ? tw >> 16 : tw & 0xffffu) - (bn == 0 ? pad : 0u);
     }
-    if ((uint32_t)lane >= nb) cum = c = 0u;
-    const uint64_t m = __ballot(cum >= (uint32_t)need);
-    const int bs = 63 - __clzll(m);
-    const uint32_t cb = (uint32_t)__builtin_amdgcn_readlane((int)c, bs);
-    const uint32_t cumb = (uint32_t)__builtin_amdgcn_readlane((int)cum, bs);
+    const uint32_t cum = wave_incl_scan_u32(c);
+    const uint64_t m = __ballot(bn >= 0 && cum >= (uint32_t)need);
+    const int L = __ffsll((unsigned long long)m) - 1;
+    const uint32_t cb = (uint32_t)__builtin_amdgcn_readlane((int)c, L);
+    const uint32_t cumb = (uint32_t)__builtin_amdgcn_readlane((int)cum, L);
     if (lane == 0) {
-      S.sv[0] = (uint32_t)bs;
+      S.sv[0] = nb - 1u - (uint32_t)L;
       S.sv[1] = (uint32_t)need - (cumb - cb);
       S.sv[2] = cb;
     }
@@ -671,9 +673,11 @@ __device__ __noinline__ void sel_all_tokens(const uint32_t* kh, const uint32_t* 
 // Everything the selecting workgroup needs, passed by value to the out-of-line selection.
 struct SelArgs {
   uint64_t* isel;
-  const uint32_t* kh;
-  const uint32_t* kl;
-  const uint64_t* idone;
+  const uint32_t* kh;      // [T] key high halves (all-token path)
+  const uint32_t* kl;      // [T] key low halves
+  const uint64_t* ilist;   // [nwg][SEL_LIST] LL words: each scorer's top key high halves, rank order
+  const uint32_t* ilo;     // [nwg][SEL_LIST] their low halves
+  const uint32_t* itok;    // [nwg][SEL_LIST] their tokens
   uint32_t* status;
   long long budget;
   int nwg, layer, token, w, T, K;
@@ -700,116 +704,82 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
   const uint32_t k1 = sa.k1;
   const int tid = tid_opaque(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int T = sa.T, K = sa.K;
+  const int T = sa.T, K = sa.K, nwg = cx.nwg, NE = nwg * SEL_LIST;
   uint64_t* isel = sa.isel;
   auto stp = [&](int slot) {
     if (sa.tron && tid_opaque() == 0) tr[slot] = wall_clock64();
   };
   const SelLds S = sel_carve(act);
-  const uint32_t* kh = sa.kh;
-  const uint32_t* kl = sa.kl;
-  // the scorers' bounds: wait for every done word, take the smallest
-  if (!ll_fetch<1>(cx, S.hist, sa.idone, cx.nwg, k1, W_IDONE)) return 0;
+  // every scorer's list, one word per thread and slot
+  if (!ll_fetch<SEL_EPT>(cx, S.lst, sa.ilist, NE, k1, W_ILIST)) return 0;
+  stp(46);
+  // the bound: the smallest of the scorers' r-th keys (0 when a scorer holds fewer than r)
   {
-    uint32_t b = tid < cx.nwg ? S.hist[tid] : 0xffffffffu;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) b = min(b, (uint32_t)__shfl_xor((int)b, o, 64));
-    if (lane == 0) S.wsum[wave] = b;
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t m = S.wsum[0];
-      for (int i = 1; i < NWAVES; i++) m = min(m, S.wsum[i]);
-      S.sv[4] = m;
-    }
+    const int r = (K + nwg - 1) / nwg;
+    uint32_t b = 0xffffffffu;
+    if (tid < nwg) b = r <= SEL_LIST ? S.lst[tid * SEL_LIST + r - 1] : 0u;
+    b = wave_minmax_u32<false>(b);
+    if (lane == 0) S.tot[wave] = b;
     for (int i = tid; i < SEL_BMW * BLOCK; i += BLOCK) S.bm[i] = 0u;
     for (int rr = 0; rr < SEL_ROWS; rr++) S.hist[rr * BLOCK + tid] = 0u;   // passes clear while reducing
-    __syncthreads();
-  }
-  const uint32_t lb = S.sv[4];
-  // ---- stream the keys (chunks of SEL_CH columns) into the per-wave candidate lists
-  const int J = (T + BLOCK - 1) / BLOCK;
-  uint32_t wc = 0, mx = 0u, mn = 0xffffffffu;
-  uint32_t* wk = S.ech + wave * SEL_WCAP;
-  uint32_t* wt = S.ett + wave * SEL_WCAP;
-  // one chunk of SEL_CH keys per thread in registers at a time (a second chunk in flight
-  // would not fit the register budget of the whole kernel without spills)
-  uint32_t ka[SEL_CH];
-  auto load_chunk = [&](uint32_t* k, int c0) {
-#pragma unroll
-    for (int i = 0; i < SEL_CH; i++) {
-      const int t = tid + (c0 + i) * BLOCK;
-      k[i] = t < T ? ld_u32_off(kh, (uint32_t)t * 4u) : 0u;
-    }
-  };
-  auto compact_chunk = [&](const uint32_t* k, int c0) {
-#pragma unroll
-    for (int i = 0; i < SEL_CH; i++) {
-      const bool c = k[i] != 0u && k[i] >= lb;
-      const uint64_t m = __ballot(c);
-      if (c) {
-        const uint32_t p = wc + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        if (p < (uint32_t)SEL_WCAP) {
-          wk[p] = k[i];
-          wt[p] = (uint32_t)(tid_opaque() + (c0 + i) * BLOCK);   // recomputed, not kept from the load
-        }
-        mx = max(mx, k[i]);
-        mn = min(mn, k[i]);
-      }
-      wc += (uint32_t)__popcll(m);
-    }
-  };
-#pragma unroll 1
-  for (int c0 = 0; c0 < J; c0 += SEL_CH) {
-    load_chunk(ka, c0);
-    compact_chunk(ka, c0);
-  }
-  stp(TR_SEL_KEYS);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
-  }
-  if (lane == 0) {
-    S.wcnt[wave] = wc;
-    S.tot[wave] = mx;
-    S.tot[8 + wave] = mn;
   }
   __syncthreads();
-  if (tid == 0) {
-    uint32_t X = S.tot[0], N = S.tot[8], C = S.wcnt[0], over = S.wcnt[0] > (uint32_t)SEL_WCAP;
-    for (int i = 1; i < NWAVES; i++) {
-      X = max(X, S.tot[i]);
-      N = min(N, S.tot[8 + i]);
-      C += S.wcnt[i];
-      over |= S.wcnt[i] > (uint32_t)SEL_WCAP;
-    }
-    S.sv[5] = C;
-    S.sv[6] = X;
-    S.sv[7] = N;
-    S.sv[8] = over;
-  }
-  __syncthreads();
-  if (S.sv[8]) {   // too many keys at or above the bound for the lists
-    sel_all_tokens(kh, kl, isel, T, K, k1, act, red);
-    stp(TR_SEL_DONE);
-    return 1;
-  }
-  const int C = (int)S.sv[5];
-  // ---- selection among the C entries: e = tid + q*BLOCK, valid when its list has it
-  uint32_t eh[SEL_EPT];
-  uint32_t ev = 0u;   // valid bits
+  uint32_t lb = S.tot[0];
+  for (int i = 1; i < NWAVES; i++) lb = min(lb, S.tot[i]);
+  // ---- entries e = tid + q*BLOCK; valid when a key (nonzero) reaches the bound
+  uint32_t etk[SEL_EPT];   // their tokens, in flight during the passes (used for the taken ones)
 #pragma unroll
   for (int q = 0; q < SEL_EPT; q++) {
     const int e = tid + q * BLOCK;
-    const bool v = (uint32_t)(e % SEL_WCAP) < S.wcnt[e / SEL_WCAP];
-    eh[q] = v ? S.ech[e] : 0u;
-    ev |= (uint32_t)v << q;   // (shift form: a literal mask would be hoisted into a register)
+    etk[q] = e < NE ? ld_u32_off(sa.itok, (uint32_t)e * 4u) : 0u;
   }
-  const uint32_t dif = S.sv[6] ^ S.sv[7];
-  const int common = dif ? __clz(dif) : 32;   // leading bits every entry shares
+  uint32_t eh[SEL_EPT];
+  uint32_t ev = 0u, cn = 0u, mx = 0u, mn = 0xffffffffu;
+#pragma unroll
+  for (int q = 0; q < SEL_EPT; q++) {
+    const int e = tid + q * BLOCK;
+    const uint32_t h = e < NE ? S.lst[e] : 0u;
+    const bool v = h != 0u && h >= lb;
+    eh[q] = v ? h : 0u;
+    ev |= (uint32_t)v << q;   // (shift form: a literal mask would be hoisted into a register)
+    cn += v ? 1u : 0u;
+    mx = v ? max(mx, h) : mx;
+    mn = v ? min(mn, h) : mn;
+  }
+  // the lists are complete when no scorer holds an unlisted key whose high half reaches
+  // the bound (its unlisted keys are at most its last listed one)
+  const int ntw = tid < T ? (T - 1 - tid) / nwg + 1 : 0;
+  uint32_t miss = (tid < nwg && ntw > SEL_LIST && S.lst[tid * SEL_LIST + SEL_LIST - 1] >= lb) ? 1u : 0u;
+  cn = wave_sum_u32(cn);
+  mx = wave_minmax_u32<true>(mx);
+  mn = wave_minmax_u32<false>(mn);
+  miss = wave_minmax_u32<true>(miss);
+  if (lane == 0) {
+    S.wsum[wave] = cn;
+    S.wsum[8 + wave] = mx;
+    S.wsum[16 + wave] = mn;
+    S.wsum[24 + wave] = miss;
+  }
+  __syncthreads();
+  uint32_t C = 0u, X = 0u, N = 0xffffffffu, M = 0u;
+  for (int i = 0; i < NWAVES; i++) {
+    C += S.wsum[i];
+    X = max(X, S.wsum[8 + i]);
+    N = min(N, S.wsum[16 + i]);
+    M |= S.wsum[24 + i];
+  }
+  if (M) {   // keys beyond the lists can be chosen: every token
+    stp(TR_SEL_KEYS);
+    sel_all_tokens(sa.kh, sa.kl, isel, T, K, k1, act, red);
+    stp(TR_SEL_DONE);
+    return 1;
+  }
+  stp(TR_SEL_KEYS);
+  const uint32_t dif = X ^ N;
+  const int common = dif ? __clz(dif) : 32;   // leading bits every valid entry shares
   uint32_t pm = common >= 32 ? 0xffffffffu : ~(0xffffffffu >> common);
-  uint32_t pre = S.sv[6] & pm;
-  int need = K, ncand = C;
+  uint32_t pre = X & pm;
+  int need = K, ncand = (int)C;
   int shift = 32 - common, npass = 0;
   while (ncand > SEL_CMAX && shift > 0) {
     const int wdt = min(5, shift);
@@ -834,7 +804,8 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
     // ---- the candidates share the whole high half: the low halves, then the token order
     uint32_t elo[SEL_EPT];
 #pragma unroll
-    for (int q = 0; q < SEL_EPT; q++) elo[q] = (ecb >> q & 1u) ? ld_u32(kl + S.ett[tid + q * BLOCK]) : 0u;
+    for (int q = 0; q < SEL_EPT; q++)
+      elo[q] = (ecb >> q & 1u) ? ld_u32_off(sa.ilo, (uint32_t)(tid + q * BLOCK) * 4u) : 0u;
     uint32_t lpre = 0, lpm = 0;
     int ls = 32;
     while (ncand > SEL_CMAX && ls > 0) {
@@ -854,7 +825,7 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
         int c = 0;
 #pragma unroll
         for (int q = 0; q < SEL_EPT; q++)
-          c += ((ecb >> q & 1u) && (elo[q] & lpm) == lpre && S.ett[tid + q * BLOCK] < (uint32_t)mid) ? 1 : 0;
+          c += ((ecb >> q & 1u) && (elo[q] & lpm) == lpre && etk[q] < (uint32_t)mid) ? 1 : 0;
         const double tc = block_sum((double)c, red);
         if (tc >= (double)need) hi_m = mid;
         else lo_m = mid + 1;
@@ -867,7 +838,7 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
       if (ecb >> q & 1u) {
         const int e = tid + q * BLOCK;
         const uint32_t mk = elo[q] & lpm;
-        S.efl[e] = (uint8_t)((mk > lpre || (mk == lpre && ncand == 0 && S.ett[e] < (uint32_t)cut)) ? 1u
+        S.efl[e] = (uint8_t)((mk > lpre || (mk == lpre && ncand == 0 && etk[q] < (uint32_t)cut)) ? 1u
                              : (mk == lpre && ncand > 0) ? 2u : 0u);
       }
     }
@@ -877,13 +848,13 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
     // ---- at most SEL_CMAX candidates: rank by (key desc, token asc) on full keys
     const uint32_t* f4 = reinterpret_cast<const uint32_t*>(S.efl + tid * SEL_EPT);
     uint32_t fw[SEL_EPT / 4];
-    uint32_t cn = 0;
+    uint32_t nf = 0;
 #pragma unroll
     for (int q = 0; q < SEL_EPT / 4; q++) {
       fw[q] = f4[q];
-      cn += __popc((fw[q] >> 1) & 0x01010101u);
+      nf += __popc((fw[q] >> 1) & 0x01010101u);
     }
-    uint32_t o = block_excl_scan(cn, S.wsum);
+    uint32_t o = block_excl_scan(nf, S.wsum);
 #pragma unroll
     for (int q = 0; q < SEL_EPT / 4; q++) {
       uint32_t m = (fw[q] >> 1) & 0x01010101u;
@@ -898,9 +869,9 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
     const int nc = min(ncand, SEL_CMAX);
     if (tid < nc) {
       const uint32_t e = S.cix[tid];
-      S.chi[tid] = S.ech[e];
-      S.ctk[tid] = S.ett[e];
-      S.clo[tid] = ld_u32(kl + S.ett[e]);
+      S.chi[tid] = S.lst[e];
+      S.ctk[tid] = ld_u32_off(sa.itok, e * 4u);
+      S.clo[tid] = ld_u32_off(sa.ilo, e * 4u);
     }
     __syncthreads();
     stp(45);
@@ -912,7 +883,7 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
   for (int q = 0; q < SEL_EPT; q++) {
     const int e = tid + q * BLOCK;
     if (S.efl[e] == 1) {
-      const uint32_t t = S.ett[e];
+      const uint32_t t = etk[q];
       __hip_atomic_fetch_or(lds_ptr(&S.bm[t >> 5]), 1u << (t & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
   }
@@ -920,13 +891,13 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
   stp(TR_SEL_PASSES);
   {
     uint32_t bw[SEL_BMW];
-    uint32_t cn = 0;
+    uint32_t nb = 0;
 #pragma unroll
     for (int q = 0; q < SEL_BMW; q++) {
       bw[q] = S.bm[tid * SEL_BMW + q];
-      cn += __popc(bw[q]);
+      nb += __popc(bw[q]);
     }
-    uint32_t o = block_excl_scan(cn, S.wsum);
+    uint32_t o = block_excl_scan(nb, S.wsum);
 #pragma unroll
     for (int q = 0; q < SEL_BMW; q++) {
       uint32_t m = bw[q];
@@ -956,7 +927,9 @@ __device__ __forceinline__ bool stage_sel_mla(Ctx& cx, const KArgs& a, const Ste
   sa.isel = isel;
   sa.kh = wsp<uint32_t>(a, a.off.ikh);
   sa.kl = wsp<uint32_t>(a, a.off.ikl);
-  sa.idone = wsp<uint64_t>(a, a.off.idone);
+  sa.ilist = wsp<uint64_t>(a, a.off.ilist);
+  sa.ilo = wsp<uint32_t>(a, a.off.ilo);
+  sa.itok = wsp<uint32_t>(a, a.off.itok);
   sa.status = cx.status;
   sa.budget = cx.budget;
   sa.nwg = cx.nwg;
@@ -1442,9 +1415,13 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_mla(KArgs a) {
       if (!stage_q_mla<SH>(cs, as, st, L)) return;
       if constexpr (SH::SPARSE) {
         if (!stage_idx_mla<SH>(cs, as, st, L)) return;
+      }
+      // the absorbed queries before the selection: the selecting workgroup's share of
+      // them then runs while it waits for the scorers' lists
+      if (!stage_absorb_mla<SH>(cs, as, st, L)) return;
+      if constexpr (SH::SPARSE) {
         if (!stage_sel_mla<SH>(cs, as, st, L)) return;
       }
-      if (!stage_absorb_mla<SH>(cs, as, st, L)) return;
       if (!stage_attn_mla<SH>(cs, as, st, L)) return;
       if (!stage_merge_mla<SH>(cs, as, st, L)) return;
       if (!stage_uv_mla<SH>(cs, as, st, L)) return;
