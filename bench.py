@@ -102,7 +102,7 @@ SLOT_NAMES = {32: "head_ready", 33: "head_gemv", 34: "token", 0: "start", 1: "x_
               26: "merge_fetched", 27: "router_logit", 28: "att_drained", 30: "att_scores", 17: "blk0_staged", 31: "blk0_done",
               35: "idx_done", 36: "sel_keys", 37: "sel_passes", 38: "sel_done", 39: "sel_pass0", 40: "sel_pass1",
               41: "sel_pass2", 42: "sel_pass3", 43: "sel_pass4", 44: "sel_pass5", 45: "sel_rank_loaded",
-              46: "sel_lists_arrived"}
+              46: "sel_lists_arrived", 47: "sel_fetch_start"}
 
 
 def write_trace_summary(dec, x, out, R, path, pos):
@@ -139,6 +139,7 @@ def write_trace_summary(dec, x, out, R, path, pos):
                "layer_critical_path_us": [round(float(v), 2) for v in layer_us]}
     with open(path, "w") as f:
         json.dump(summary, f, indent=1)
+    np.save(os.path.splitext(path)[0] + "_raw.npy", t)   # [layer][workgroup][slot] wall-clock ticks
 
 
 def run_stack(args):

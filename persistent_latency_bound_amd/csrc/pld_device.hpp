@@ -297,10 +297,20 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Wave sums with DPP moves (no LDS permutes); the result, from lane 63, in every lane.
+__device__ __forceinline__ float wave_sum_any(float v) { return wave_sum_dpp(v); }
+__device__ __forceinline__ double wave_sum_any(double v) {
+  v = dpp_sum64_f64(v);
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffff), 63);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), 63);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
 // Block-wide sum in a fixed order (wave sums, then wave 0..7 in order). All threads get the result.
 template <typename T>
 __device__ __forceinline__ T block_sum(T v, T* red) {
-  v = wave_sum(v);
+  v = wave_sum_any(v);
   const int lane = tid_opaque() & 63, wave = tid_opaque() >> 6;
   __syncthreads();
   if (lane == 0) red[wave] = v;

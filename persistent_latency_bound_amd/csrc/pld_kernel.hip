@@ -245,7 +245,7 @@ struct RegVec {
 #pragma unroll
     for (int k = 0; k < K; k++) {
       const int i = tid_opaque() + k * BLOCK;
-      v[k] = i < N ? g[i] : 0.f;
+      v[k] = (N % BLOCK == 0 || i < N) ? g[i] : 0.f;   // (a compile-time guard when it can be)
     }
   }
 };
@@ -257,14 +257,14 @@ __device__ __forceinline__ void rmsnorm_reg(float* act, const RegVec<N>& gam, do
 #pragma unroll
   for (int k = 0; k < RegVec<N>::K; k++) {
     const int i = tid_opaque() + k * BLOCK;
-    if (i < N) ss += (double)act[i] * (double)act[i];
+    if (N % BLOCK == 0 || i < N) ss += (double)act[i] * (double)act[i];
   }
   ss = block_sum(ss, red);
   const double r = 1.0 / sqrt(ss / (double)N + eps);
 #pragma unroll
   for (int k = 0; k < RegVec<N>::K; k++) {
     const int i = tid_opaque() + k * BLOCK;
-    if (i < N) act[i] = (float)(((double)act[i] * r) * (double)gam.v[k]);
+    if (N % BLOCK == 0 || i < N) act[i] = (float)(((double)act[i] * r) * (double)gam.v[k]);
   }
   __syncthreads();
 }
@@ -288,6 +288,9 @@ __device__ __forceinline__ void rmsnorm_reg(float* act, const RegVec<N>& gam, do
 #ifndef PLD_IF_DOWN
 #define PLD_IF_DOWN 8
 #endif
+
+constexpr int RT_SLOTS = 8;      // experts per lane in the router top-k: E <= 64 * RT_SLOTS
+constexpr int RT_RANK_MAX = 64;  // up to this many experts the top-k counts ranks instead
 
 // One (expert, slot, row range) piece of a gate/up GEMV list.
 struct GuPiece { int expert, slot, j0, j1; };
@@ -410,10 +413,13 @@ __device__ __forceinline__ bool layer_input(Ctx& cx, const KArgs& a, const Step&
     return false;
   }
   stamp(a, cx, st, TR_X_READY);
-  for (int i = tid_opaque(); i < H / 2; i += BLOCK) {
-    const uint32_t v = L.stage[i];
-    L.act[2 * i] = bf_lo(v);
-    L.act[2 * i + 1] = bf_hi(v);
+#pragma unroll
+  for (int k = 0; k < (H / 2 + BLOCK - 1) / BLOCK; k++) {
+    const int i = tid_opaque() + k * BLOCK;
+    if ((H / 2) % BLOCK == 0 || i < H / 2) {
+      const uint32_t v = L.stage[i];
+      reinterpret_cast<float2*>(L.act)[i] = make_float2(bf_lo(v), bf_hi(v));
+    }
   }
   __syncthreads();
   for (int r = h0 + tid_opaque(); r < h1; r += BLOCK) L.xres[r - h0] = L.act[r];
@@ -633,14 +639,14 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
   for (int h = wave; h < G; h += NWAVES) {
     float m = -INFINITY;
     for (int t = lane; t < n; t += 64) m = fmaxf(m, sc[h * c.chmax + t]);
-    m = wave_max(m);
+    m = wave_max_dpp(m);
     float l = 0.f;
     for (int t = lane; t < n; t += 64) {
       const float p = __expf(sc[h * c.chmax + t] - m);
       sc[h * c.chmax + t] = p;
       l += p;
     }
-    l = wave_sum(l);
+    l = wave_sum_dpp(l);
     if (lane == 0) { ml[2 * h] = m; ml[2 * h + 1] = l; }
   }
   __syncthreads();
@@ -900,41 +906,94 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
                                     W_RT))
       return false;
     stamp(a, cx, st, TR_RT_READY);
-    // top-k by rank: expert e is selected at position rank(e) = #{j : key_j > key_e or
-    // (key_j == key_e and j < e)} when that rank is < topk (lowest index wins ties).
-    // Keys become order-preserving 64-bit integers (x >= 0: bits | 2^63, x < 0: ~bits;
-    // -0 folded into +0), and each expert's comparisons are split over P = BLOCK / E
-    // thread partitions so that every thread of the workgroup counts.
+    // Top-k. The keys become order-preserving 64-bit integers
+    // (x >= 0: bits | 2^63, x < 0: ~bits; -0 folded into +0). With many experts one wave
+    // selects them in order: lane l holds experts l, l + 64, ... and its best remaining
+    // one; each round takes the wave-wide largest (key, lowest index on ties) with DPP
+    // moves and the winning lane moves to its next. Both ways place the expert of rank r
+    // at position r.
     const bool sig = c.router == PLD_ROUTER_SIGMOID_BIAS;
-    {
+    if (c.E <= RT_RANK_MAX) {
+      // few experts: each expert's rank = #{j : key_j > key_e or (key_j == key_e and
+      // j < e)}, its comparisons split over P = BLOCK / E thread partitions; expert e
+      // takes position rank(e) when that is < topk
       uint64_t* uk = reinterpret_cast<uint64_t*>(L.outc);         // [E] keys (outc is free here)
       int* rk = reinterpret_cast<int*>(uk + c.E);                  // [P][E] partial ranks
       for (int e = tid_opaque(); e < c.E; e += BLOCK) {
         const double ke = lk[2 * e + 1];
-        const uint64_t b = (uint64_t)__double_as_longlong(ke == 0.0 ? 0.0 : ke);
-        uk[e] = (b >> 63) ? ~b : (b | (1ull << 63));
+        const uint64_t bb = (uint64_t)__double_as_longlong(ke == 0.0 ? 0.0 : ke);
+        uk[e] = (bb >> 63) ? ~bb : (bb | (1ull << 63));
       }
       __syncthreads();
-      const int P = BLOCK / c.E;                  // host: E divides BLOCK
+      // E is a power of two dividing BLOCK here; P partitions of E / P comparisons each
+      const int P = min(BLOCK / c.E, c.E);
       const int seg = c.E / P;
       const int tid = tid_opaque();
       const int e = tid % c.E, p = tid / c.E;
-      const uint64_t ue = uk[e];
-      int rank = 0;
-      // (seg is a multiple of 8: the unrolled reads of 8 keys are in flight together)
-      for (int j0 = p * seg; j0 < (p + 1) * seg; j0 += 8) {
-#pragma unroll
-        for (int j = j0; j < j0 + 8; j++) {
+      if (p < P) {
+        const uint64_t ue = uk[e];
+        int rank = 0;
+        for (int j = p * seg; j < (p + 1) * seg; j++) {
           const uint64_t uj = uk[j];
           rank += (uj > ue || (uj == ue && j < e)) ? 1 : 0;
         }
+        rk[p * c.E + e] = rank;
       }
-      rk[p * c.E + e] = rank;
       __syncthreads();
       for (int ee = tid; ee < c.E; ee += BLOCK) {
-        int r = 0;
-        for (int pp = 0; pp < P; pp++) r += rk[pp * c.E + ee];
-        if (r < c.topk) L.isel[r] = ee;
+        int rr = 0;
+        for (int pp = 0; pp < P; pp++) rr += rk[pp * c.E + ee];
+        if (rr < c.topk) L.isel[rr] = ee;
+      }
+    } else if (tid_opaque() < 64) {
+      const int lane = tid_opaque();
+      const int ns = (c.E + 63) >> 6;   // slots in use (uniform)
+      uint64_t ks[RT_SLOTS];             // 0: no expert, or already taken (no score's key is 0)
+#pragma unroll
+      for (int i = 0; i < RT_SLOTS; i++) {
+        const int e = lane + 64 * i;
+        const double ke = e < c.E ? lk[2 * e + 1] : 0.0;
+        const uint64_t bb = (uint64_t)__double_as_longlong(ke == 0.0 ? 0.0 : ke);
+        ks[i] = e < c.E ? ((bb >> 63) ? ~bb : (bb | (1ull << 63))) : 0ull;
+      }
+      for (int r = 0; r < c.topk; r++) {
+        // this lane's best remaining expert (strict > keeps the lower index on ties)
+        uint64_t b = ks[0];
+        uint32_t bi = 0u;
+#pragma unroll
+        for (int i = 1; i < RT_SLOTS; i++) {
+          if (i >= ns) break;
+          const bool gt = ks[i] > b;
+          b = gt ? ks[i] : b;
+          bi = gt ? (uint32_t)i : bi;
+        }
+        // wave-wide largest key (DPP moves; a lane keeps its own value where a move
+        // does not write it)
+        uint64_t m = b;
+        auto step = [&](auto ctrl_tag) {
+          constexpr int CTRL = decltype(ctrl_tag)::value >> 4, RM = decltype(ctrl_tag)::value & 0xf;
+          const uint64_t o = ((uint64_t)dpp_keep_u32<CTRL, RM>((uint32_t)(m >> 32)) << 32) |
+                             dpp_keep_u32<CTRL, RM>((uint32_t)m);
+          m = o > m ? o : m;
+        };
+        step(std::integral_constant<int, (0xB1 << 4) | 0xf>{});
+        step(std::integral_constant<int, (0x4E << 4) | 0xf>{});
+        step(std::integral_constant<int, (0x141 << 4) | 0xf>{});
+        step(std::integral_constant<int, (0x140 << 4) | 0xf>{});
+        step(std::integral_constant<int, (0x142 << 4) | 0xa>{});
+        step(std::integral_constant<int, (0x143 << 4) | 0xc>{});
+        const uint64_t K = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(m >> 32), 63) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)m, 63);
+        // the expert: the lowest index among the lanes holding that key
+        const uint32_t mye = (uint32_t)lane + 64u * bi;
+        const bool hold = b == K;
+        const uint64_t hm = __ballot(hold);
+        uint32_t ee;
+        if (__popcll(hm) == 1) ee = (uint32_t)__builtin_amdgcn_readlane((int)mye, __ffsll((unsigned long long)hm) - 1);
+        else ee = wave_minmax_u32<false>(hold ? mye : 0xffffffffu);
+#pragma unroll
+        for (int i = 0; i < RT_SLOTS; i++) ks[i] = (mye == ee && bi == (uint32_t)i) ? 0ull : ks[i];
+        if (lane == 0) L.isel[r] = (int)ee;
       }
     }
     __syncthreads();
@@ -1075,17 +1134,21 @@ __device__ __forceinline__ bool stage_head(Ctx& cx, const KArgs& a, const Step& 
   auto swz = [](int i) { const int c = i >> 4; return ((c >> 6) * 16 + (i & 15)) * 64 + (c & 63); };
   if (!ll_fetch<per_for(H / 2)>(cx, L.stage, wsp<uint64_t>(a, a.off.x), H / 2, k1, W_X)) return false;
   double ss = 0.0;
-  for (int i = tid; i < H / 2; i += BLOCK) {
-    const uint32_t v = L.stage[i];
-    const double x0 = bf_lo(v), x1 = bf_hi(v);
-    ss += x0 * x0 + x1 * x1;
+#pragma unroll
+  for (int k = 0; k < (H / 2 + BLOCK - 1) / BLOCK; k++) {
+    const int i = tid + k * BLOCK;
+    if ((H / 2) % BLOCK == 0 || i < H / 2) {
+      const uint32_t v = L.stage[i];
+      const double x0 = bf_lo(v), x1 = bf_hi(v);
+      ss += x0 * x0 + x1 * x1;
+    }
   }
   ss = block_sum(ss, L.red);
   const double rr = 1.0 / sqrt(ss / (double)H + c.eps);
 #pragma unroll
   for (int k = 0; k < RegVec<H>::K; k++) {
     const int i = tid + k * BLOCK;
-    if (i < H) {
+    if (H % BLOCK == 0 || i < H) {
       const uint32_t v = L.stage[i >> 1];
       const double x = (i & 1) ? bf_hi(v) : bf_lo(v);
       dact[swz(i)] = (x * rr) * (double)gf.v[k];
@@ -1319,8 +1382,8 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
   if (c->ffn_kind == PLD_FFN_DENSE) {
     k->slots = 1;
   } else if (c->ffn_kind == PLD_FFN_MOE) {
-    if (c->n_experts < 8 || c->n_experts > nwg || c->n_experts > 512 || c->n_experts % 8 || BLOCK % c->n_experts ||
-        (c->n_experts / (BLOCK / c->n_experts)) % 8)
+    if (c->n_experts < 8 || c->n_experts > nwg || c->n_experts > 64 * RT_SLOTS || c->n_experts % 8 ||
+        (c->n_experts <= RT_RANK_MAX && BLOCK % c->n_experts))
       return PLD_E_UNSUPPORTED;
     if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts) return PLD_E_UNSUPPORTED;
     if (c->n_shared < 0 || c->n_shared > 2) return PLD_E_UNSUPPORTED;

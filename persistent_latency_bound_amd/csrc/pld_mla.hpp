@@ -118,7 +118,7 @@ __device__ __forceinline__ void rmsnorm_f64src(float* dst, const uint32_t* src, 
 #pragma unroll
   for (int k = 0; k < RegVec<N>::K; k++) {
     const int i = tid_opaque() + k * BLOCK;
-    if (i < N) {
+    if (N % BLOCK == 0 || i < N) {
       const double x = x_at(i);
       ss += x * x;
     }
@@ -128,7 +128,7 @@ __device__ __forceinline__ void rmsnorm_f64src(float* dst, const uint32_t* src, 
 #pragma unroll
   for (int k = 0; k < RegVec<N>::K; k++) {
     const int i = tid_opaque() + k * BLOCK;
-    if (i < N) dst[i] = (float)((x_at(i) * r) * (double)gam.v[k]);
+    if (N % BLOCK == 0 || i < N) dst[i] = (float)((x_at(i) * r) * (double)gam.v[k]);
   }
   __syncthreads();
 }
@@ -710,6 +710,7 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
     if (sa.tron && tid_opaque() == 0) tr[slot] = wall_clock64();
   };
   const SelLds S = sel_carve(act);
+  stp(47);
   // every scorer's list, one word per thread and slot
   if (!ll_fetch<SEL_EPT>(cx, S.lst, sa.ilist, NE, k1, W_ILIST)) return 0;
   stp(46);
