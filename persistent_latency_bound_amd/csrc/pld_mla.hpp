@@ -1048,9 +1048,10 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
   const int hg = cx.w / nch, ch = cx.w % nch;
   const int hbase = hg * HPW;
   const int pos = st.pos, T = pos + 1;
-  // dense: the chunk's rows are [t0, t1) of the T cache rows; sparse: entries [t0, t1) of
-  // the indexer's ascending list of K selected rows (the new row, if chosen, is the last)
-  const int K = SH::SPARSE ? min(c.itopk, T) : T;
+  // dense: the chunk's rows are [t0, t1) of the T - 1 history rows (the row of position pos
+  // is added by the last chunk after its blocks); sparse: entries [t0, t1) of the
+  // indexer's ascending list of K selected rows (the new row, if chosen, is the last)
+  const int K = SH::SPARSE ? min(c.itopk, T) : T - 1;
   const int t0 = split_at(K, nch, ch), t1 = split_at(K, nch, ch + 1), n = t1 - t0;
   const int fresh = a.pos0;
   const int nst = max(0, min(n, fresh - t0));            // dense: static rows of the chunk: [0, nst)
@@ -1076,9 +1077,8 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
   };
   // index inside the chunk of the row of position pos (its bf16 row is patched in from
   // LDS), or -1; the chunk that computes the new row and appends it to the cache
-  const int pidx = SH::SPARSE ? ((ch == nch - 1 && n > 0 && srows[n - 1] == pos) ? n - 1 : -1)
-                              : ((t0 <= pos && pos < t1) ? pos - t0 : -1);
-  const bool newrow_here = SH::SPARSE ? ch == nch - 1 : (t0 <= pos && pos < t1);
+  const int pidx = SH::SPARSE ? ((ch == nch - 1 && n > 0 && srows[n - 1] == pos) ? n - 1 : -1) : -1;
+  const bool newrow_here = ch == nch - 1;
   // Staging registers: three sub-blocks in flight (sets A, B, C in turn); chunk i of a
   // block covers (row i / CPRW, chunk i % CPRW). A block's loads are issued three blocks
   // before it is staged into LDS, so the wait at staging time covers ~3 blocks of work.
@@ -1090,7 +1090,6 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
   // position pos is patched in from LDS after staging.
   constexpr int DEPTH = 3;
   const int nsb = (n + TB - 1) / TB;
-  const int nsbp = (nsb + DEPTH - 1) / DEPTH * DEPTH;
   const bool coh = SH::SPARSE ? (n > 0 && srows[n - 1] >= fresh) : (n > 0 && t0 + n > fresh);
   uint4 cb[DEPTH][NLD];
   auto issue = [&](int set, int sb, auto coh_tag) {
@@ -1246,11 +1245,14 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
       }
     }
   };
+  // (only the chunk's own sub-blocks are computed; the loads of the sets past the last
+  // one read a uniform address and are never staged)
   auto main_loop = [&](auto coh_tag) {
-    for (int sb0 = 0; sb0 < nsbp; sb0 += DEPTH) {
+    for (int sb0 = 0; sb0 < nsb; sb0 += DEPTH) {
 #pragma unroll
       for (int d = 0; d < DEPTH; d++) {
         const int sb = sb0 + d;
+        if (sb >= nsb) break;
         const int tb0 = sb * TB, buf = sb & 1;
         const uint16_t* C = Cs + buf * TB * CSTR;
         store(d, sb, buf);
@@ -1264,6 +1266,46 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
   };
   if (coh) main_loop(std::true_type{});
   else main_loop(std::false_type{});
+  if constexpr (!SH::SPARSE) {
+    // dense: the row of position pos joins the last chunk's online softmax here, on the
+    // vector ALU (as a sub-block of its own it would cost a whole block for one row)
+    if (newrow_here) {
+      float* sn = Ssc;   // [16] scores, [16] alpha, [16] p (the score tiles are free now)
+      {
+        constexpr int DPJ = LAT / 32;   // dims per lane: 32 lanes per head row
+        const int hr = tid >> 5, j = tid & 31;
+        float sv = 0.f;
+#pragma unroll
+        for (int d = 0; d < DPJ; d++)
+          sv = fmaf(bf16_to_f32(Qs[hr * CSTR + j * DPJ + d]), bf16_to_f32(newrow[j * DPJ + d]), sv);
+        sv = dpp_sum<32>(sv);   // valid in the last lane of each half-wave
+        if (j == 31) sn[hr] = sv * scale;
+      }
+      __syncthreads();
+      if (wave < HPW) {   // wave h owns head h
+        const float sv = sn[wave];
+        const float mnew = fmaxf(m_run, sv);
+        const float al = m_run == -INFINITY ? 0.f : __expf(m_run - mnew);
+        const float pn = __expf(sv - mnew);
+        l_run = l_run * al + pn;
+        m_run = mnew;
+        if (lane == 0) {
+          sn[16 + wave] = al;
+          sn[32 + wave] = pn;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        const float v = bf16_to_f32(newrow[(wave * 4 + t) * 16 + ln]);
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+          const int h = 4 * lq + q;
+          if (h < HPW) O[t][q] = O[t][q] * sn[16 + h] + sn[32 + h] * v;
+        }
+      }
+    }
+  }
   stamp(a, cx, st, TR_ATT_SOFTMAX);
   // publish the partial of each head: LL words [m, l, acc[0..KL)] at ((h * nch) + ch) * (KL + 2)
   vm_wait();   // the cache row appended above is visible before this workgroup's next publication
