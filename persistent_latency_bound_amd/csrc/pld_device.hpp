@@ -292,6 +292,28 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   v = fmaxf(v, dpp_keep<0x143, 0xc>(v));
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+// Max and sum over each 32-lane half of a wave with DPP moves: row results in every lane,
+// then rows 0+1 and 2+3 (row_bcast15); each lane gets its half's result (lanes 31, 63).
+__device__ __forceinline__ float half_max_dpp(float v) {
+  v = fmaxf(v, dpp_keep<0xB1, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x4E, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x141, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x140, 0xf>(v));
+  v = fmaxf(v, dpp_keep<0x142, 0xa>(v));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  return (tid_opaque() & 32) ? b : a;
+}
+__device__ __forceinline__ float half_sum_dpp(float v) {
+  v += dpp_mov<0xB1, 0xf, false>(v);
+  v += dpp_mov<0x4E, 0xf, false>(v);
+  v += dpp_mov<0x141, 0xf, false>(v);
+  v += dpp_mov<0x140, 0xf, false>(v);
+  v += dpp_mov<0x142, 0xa, true>(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+  return (tid_opaque() & 32) ? b : a;
+}
 __device__ __forceinline__ float wave_sum_dpp(float v) {
   v = dpp_sum<64>(v);
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));

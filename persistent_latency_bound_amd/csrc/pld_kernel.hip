@@ -1295,7 +1295,7 @@ using ShapeTinyDense = GqaShape<256, 4, 4, 64, 1024, false, false, 1, 2>;
 using ShapeGqaMoe = GqaShape<4096, 32, 8, 128, 1536, false, true, 9, 33>;
 // the FP8 MLA MoE layer: hidden 6144, 64 heads, q_lora 1536, kv_lora 512 + rope 64,
 // nope 128, v 128, 256 experts of width 2048 (biased-score router)
-using ShapeMlaFp8 = MlaShape<6144, 64, 1536, 512, 64, 128, 128, 2048, true, true, false>;
+using ShapeMlaFp8 = MlaShape<6144, 64, 1536, 512, 64, 128, 128, 2048, true, true, false, 0, 0, 16>;
 // the sparse MLA MoE layer: hidden 4096, 32 heads, the same latent sizes, bf16 weights,
 // indexer of 8 heads x 64 dims, 64 experts of width 1536 (softmax router)
 using ShapeSparseMla = MlaShape<4096, 32, 1536, 512, 64, 128, 128, 1536, false, true, true, 8, 64>;
@@ -1314,6 +1314,13 @@ static bool matches_mla(const pld_config* c) {
          c->inter == SH::INTER && (c->wfmt == PLD_WFMT_FP8_BLOCK128) == SH::FP8 &&
          (c->ffn_kind == PLD_FFN_MOE) == SH::MOE && (c->index_topk > 0) == SH::SPARSE &&
          (!SH::SPARSE || (c->index_heads == SH::IH && c->index_dim == SH::ID));
+}
+
+// heads per MLA attention workgroup of the compiled shape the configuration selects
+static int mla_hpw(const pld_config* c) {
+  if (matches_mla<ShapeMlaFp8>(c)) return ShapeMlaFp8::HPW;
+  if (matches_mla<ShapeSparseMla>(c)) return ShapeSparseMla::HPW;
+  return 0;
 }
 
 static KernelFn pick_kernel(const pld_config* c) {
@@ -1422,7 +1429,7 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
     k->rdim = c->head_dim;
   } else if (c->attn_kind == PLD_ATTN_MLA) {
     if (!pick_kernel(c)) return PLD_E_UNSUPPORTED;
-    const int HPW = 8, NH = c->n_heads, KL = c->kv_lora, LAT = c->kv_lora + c->rope_dim, VD = c->v_dim;
+    const int HPW = mla_hpw(c), NH = c->n_heads, KL = c->kv_lora, LAT = c->kv_lora + c->rope_dim, VD = c->v_dim;
     const int nhg = NH / HPW;
     if (NH % HPW || nwg % nhg) return PLD_E_UNSUPPORTED;
     k->cpg = nwg / nhg;                            // attention chunks per head group
@@ -1431,7 +1438,7 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
     if ((NH * KL) % nwg) return PLD_E_UNSUPPORTED;
     k->cpw = NH * KL / nwg;
     const int epc = c->wfmt == PLD_WFMT_FP8_BLOCK128 ? 16 : 8;
-    if (KL % k->cpw || k->cpw % epc || BLOCK % (k->cpw / epc) || c->nope_dim > 4 * (BLOCK / (k->cpw / epc)))
+    if (KL % k->cpw || k->cpw % epc || BLOCK % k->cpw || c->nope_dim > 4 * (BLOCK / (k->cpw / epc)))
       return PLD_E_UNSUPPORTED;
     // W_UV: each workgroup's rows inside one head
     if ((NH * VD) % nwg || VD % (NH * VD / nwg)) return PLD_E_UNSUPPORTED;
@@ -1446,7 +1453,7 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
     const int nope_rows = std::min(c->nope_dim, 4 * (BLOCK / (k->cpw / epc)));
     int act = std::max({c->hidden, c->q_lora, k->slots * c->inter, (attn_bytes + 3) / 4 + 16,
                         c->nope_dim + (BLOCK / (k->cpw / epc)) * k->cpw + nope_rows,
-                        k->cpg * k->cpw + 4 * k->cpg + 8});
+                        k->cpg * k->cpw + 3 * k->cpg + 8 + BLOCK});
     if (sparse) {
       // indexer: 8 heads x 64 dims (4 lanes x 2 heads per token); selection: every scoring
       // workgroup's list in LDS, keys per thread on the all-token path; selected rows per

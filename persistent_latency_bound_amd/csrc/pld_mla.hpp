@@ -15,14 +15,15 @@
 #pragma once
 
 template <int H_, int NH_, int QL_, int KL_, int RD_, int ND_, int VD_, int INTER_, bool FP8_, bool MOE_, bool SPARSE_,
-          int IH_ = 0, int ID_ = 0>
+          int IH_ = 0, int ID_ = 0, int HPW_ = 8>
 struct MlaShape {
   static constexpr int H = H_, NH = NH_, QL = QL_, KL = KL_, RD = RD_, ND = ND_, VD = VD_, INTER = INTER_;
   static constexpr bool FP8 = FP8_, MOE = MOE_, SPARSE = SPARSE_;
   static constexpr int IH = IH_, ID = ID_;        // indexer heads and key width (sparse layers)
   static_assert(!SPARSE || (!FP8 && IH > 0 && ID > 0), "the sparse layer has bf16 weights and an indexer");
   static constexpr int LAT = KL + RD, QH = ND + RD, ODIM = NH * VD;
-  static constexpr int HPW = 8, NHG = NH / HPW;   // heads per attention workgroup, head groups
+  static constexpr int HPW = HPW_, NHG = NH / HPW;   // heads per attention workgroup (8 or 16), head groups
+  static_assert(HPW == 8 || HPW == 16, "one or two heads per wave");
   static constexpr int TB = 32;                   // latent rows per attention sub-block
   static constexpr int CSTR = LAT + 4;            // LDS row stride (bf16) of a staged latent row
   static_assert(NH % HPW == 0 && LAT % 64 == 0 && KL % 16 == 0 && RD % 2 == 0 && ND % 2 == 0, "MLA shape");
@@ -1041,7 +1042,10 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
   constexpr int KSTEPS = LAT / 16, KQ = KSTEPS / 4;   // k-steps per wave pair
   constexpr int CPRW = LAT / 8;                        // 16-byte chunks per latent row
   constexpr int NLD = (TB * CPRW + BLOCK - 1) / BLOCK; // staging loads per thread per sub-block
-  static_assert(KSTEPS % 4 == 0 && KL == 512 && HPW == NWAVES, "attention tiling");
+  static_assert(KSTEPS % 4 == 0 && KL == 512 && (HPW == NWAVES || HPW == 2 * NWAVES) && TB == 32, "attention tiling");
+  constexpr int HS = HPW / NWAVES;   // heads per wave: one, or one per 32-lane half
+  // the head this lane's softmax state belongs to
+  const int hown = (tid_opaque() >> 6) * HS + (HS == 2 ? ((tid_opaque() & 63) >> 5) : 0);
   const int tid = tid_opaque();
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nch = c.cpg;
@@ -1131,20 +1135,8 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
 #pragma unroll
     for (int d = 0; d < DEPTH; d++) issue(d, d, std::false_type{});
   }
-  // q of the head group: q_lat [HPW][KL] and q_rope [HPW][RD] (LL) -> bf16 rows of Qs
-  if (!ll_fetch<per_for(HPW * KL)>(cx, reinterpret_cast<uint32_t*>(qtmp),
-                                   wsp<uint64_t>(a, a.off.qlat) + (size_t)hbase * KL, HPW * KL, k1, W_QLAT))
-    return false;
-  if (!ll_fetch<per_for(HPW * RD)>(cx, reinterpret_cast<uint32_t*>(qtmp + HPW * KL),
-                                   wsp<uint64_t>(a, a.off.qr) + (size_t)hbase * RD, HPW * RD, k1, W_QLAT))
-    return false;
-  for (int i = tid; i < 16 * LAT; i += BLOCK) {
-    const int h = i / LAT, k = i % LAT;
-    const float v = h >= HPW ? 0.f : (k < KL ? qtmp[h * KL + k] : qtmp[HPW * KL + h * RD + (k - KL)]);
-    Qs[h * CSTR + k] = (uint16_t)bf16_bits(v);
-  }
-  for (int i = tid; i < 16 * TB; i += BLOCK) Ps[i] = 0;
-  // the row of position pos: RMSNorm(c_kv') and RoPE(k_r'), bf16
+  // the row of position pos: RMSNorm(c_kv') and RoPE(k_r'), bf16 (before the queries: its
+  // input was published by the X stage, so this runs while the absorbed queries are produced)
   if (newrow_here) {
     if (!ll_fetch<per_for(LAT)>(cx, reinterpret_cast<uint32_t*>(ntmp), wsp<uint64_t>(a, a.off.ckvr), LAT, k1, W_KV))
       return false;
@@ -1171,10 +1163,23 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
       if (hg == 0) st_u32(reinterpret_cast<uint32_t*>(Ly.lat + (size_t)pos * LAT) + i, pair);   // cache append
     }
   }
+  // q of the head group: q_lat [HPW][KL] and q_rope [HPW][RD] (LL) -> bf16 rows of Qs
+  if (!ll_fetch<per_for(HPW * KL)>(cx, reinterpret_cast<uint32_t*>(qtmp),
+                                   wsp<uint64_t>(a, a.off.qlat) + (size_t)hbase * KL, HPW * KL, k1, W_QLAT))
+    return false;
+  if (!ll_fetch<per_for(HPW * RD)>(cx, reinterpret_cast<uint32_t*>(qtmp + HPW * KL),
+                                   wsp<uint64_t>(a, a.off.qr) + (size_t)hbase * RD, HPW * RD, k1, W_QLAT))
+    return false;
+  for (int i = tid; i < 16 * LAT; i += BLOCK) {
+    const int h = i / LAT, k = i % LAT;
+    const float v = h >= HPW ? 0.f : (k < KL ? qtmp[h * KL + k] : qtmp[HPW * KL + h * RD + (k - KL)]);
+    Qs[h * CSTR + k] = (uint16_t)bf16_bits(v);
+  }
+  for (int i = tid; i < 16 * TB; i += BLOCK) Ps[i] = 0;
   __syncthreads();
   stamp(a, cx, st, TR_ATT_READY);
   const float scale = 1.0f / sqrtf((float)(SH::ND + SH::RD));
-  float m_run = -INFINITY, l_run = 0.f;   // wave h < HPW: head h
+  float m_run = -INFINITY, l_run = 0.f;   // of head hown
   f32x4 O[4];
 #pragma unroll
   for (int t = 0; t < 4; t++) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1200,25 +1205,26 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
     }
     __syncthreads();
     if (tb0 == 0) stamp(a, cx, st, 23);
-    // ---- online softmax: wave h owns head h; lane t < TB is token tb0 + t
+    // ---- online softmax: head hown; lane t (of its 32-lane half) is token tb0 + t
     {
-      const int h = wave;
+      const int h = hown, tl = lane & 31;
+      const bool act_lane = HS == 2 || lane < TB;
       float s = -INFINITY;
-      if (lane < TB && tb0 + lane < n) {
-        const int nt = lane >> 4, col = lane & 15;
+      if (act_lane && tb0 + tl < n) {
+        const int nt = tl >> 4, col = tl & 15;
         s = 0.f;
 #pragma unroll
         for (int kq = 0; kq < 4; kq++) s += Ssc[(kq * 2 + nt) * 256 + h * 16 + col];
         s *= scale;
       }
-      const float mb = wave_max_dpp(s);
+      const float mb = HS == 2 ? half_max_dpp(s) : wave_max_dpp(s);
       const float mnew = fmaxf(m_run, mb);
       const float al = m_run == -INFINITY ? 0.f : __expf(m_run - mnew);
       const float p = s == -INFINITY ? 0.f : __expf(s - mnew);
-      l_run = l_run * al + wave_sum_dpp(p);
+      l_run = l_run * al + (HS == 2 ? half_sum_dpp(p) : wave_sum_dpp(p));
       m_run = mnew;
-      if (lane < TB) Ps[h * TB + lane] = (uint16_t)bf16_bits(p);
-      if (lane == 0) alph[h] = al;
+      if (act_lane) Ps[h * TB + tl] = (uint16_t)bf16_bits(p);
+      if (tl == 0 && act_lane) alph[h] = al;
     }
     __syncthreads();
     if (tb0 == 0) stamp(a, cx, st, 28);
@@ -1282,16 +1288,16 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
         if (j == 31) sn[hr] = sv * scale;
       }
       __syncthreads();
-      if (wave < HPW) {   // wave h owns head h
-        const float sv = sn[wave];
+      {
+        const float sv = sn[hown];
         const float mnew = fmaxf(m_run, sv);
         const float al = m_run == -INFINITY ? 0.f : __expf(m_run - mnew);
         const float pn = __expf(sv - mnew);
         l_run = l_run * al + pn;
         m_run = mnew;
-        if (lane == 0) {
-          sn[16 + wave] = al;
-          sn[32 + wave] = pn;
+        if ((lane & 31) == 0 && (HS == 2 || lane == 0)) {
+          sn[16 + hown] = al;
+          sn[32 + hown] = pn;
         }
       }
       __syncthreads();
@@ -1311,8 +1317,8 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
   vm_wait();   // the cache row appended above is visible before this workgroup's next publication
   __syncthreads();
   uint64_t* pll = wsp<uint64_t>(a, a.off.part);
-  if (lane == 0 && wave < HPW) {
-    uint64_t* p = pll + ((size_t)(hbase + wave) * nch + ch) * (KL + 2);
+  if ((lane & 31) == 0 && (HS == 2 || lane == 0)) {
+    uint64_t* p = pll + ((size_t)(hbase + hown) * nch + ch) * (KL + 2);
     ll_put_f32(p, m_run, k1);
     ll_put_f32(p + 1, l_run, k1);
   }
@@ -1348,16 +1354,18 @@ __device__ __forceinline__ bool stage_merge_mla(Ctx& cx, const KArgs& a, const S
   float* mls = L.act + nacc;        // [nch][2]
   float* fw = mls + 2 * nch;        // [nch]
   float* lsum = fw + nch;           // [1]
+  float* part = lsum + 1;           // [BLOCK] partial sums over chunk subsets
   stamp(a, cx, st, TR_MERGE_START);
-  if (!ll_fetch<per_for(4096 + 64)>(cx, reinterpret_cast<uint32_t*>(L.act), wsp<uint64_t>(a, a.off.part),
-                                    nacc + 2 * nch, st.k1, W_PART, pidx))
+  // one round of loads covers up to 17 * BLOCK words (64 chunks x 128 columns + their m, l)
+  if (!ll_fetch<17>(cx, reinterpret_cast<uint32_t*>(L.act), wsp<uint64_t>(a, a.off.part), nacc + 2 * nch, st.k1,
+                    W_PART, pidx))
     return false;
   stamp(a, cx, st, TR_MERGE_COPIED);
   if (wave == 0) {
     float M = -INFINITY;
     for (int cc = lane; cc < nch; cc += 64)
       if (mls[2 * cc + 1] > 0.f) M = fmaxf(M, mls[2 * cc]);
-    M = wave_max(M);
+    M = wave_max_dpp(M);
     float ls = 0.f;
     for (int cc = lane; cc < nch; cc += 64) {
       const float l = mls[2 * cc + 1];
@@ -1365,16 +1373,25 @@ __device__ __forceinline__ bool stage_merge_mla(Ctx& cx, const KArgs& a, const S
       fw[cc] = f;
       ls += f * l;
     }
-    ls = wave_sum(ls);
+    ls = wave_sum_dpp(ls);
     if (lane == 0) lsum[0] = ls;
   }
   __syncthreads();
-  uint64_t* ol = wsp<uint64_t>(a, a.off.olat) + (size_t)h * KL + c0;
-  for (int j = tid; j < cpw; j += BLOCK) {
+  // column j: np = BLOCK / cpw threads each sum the chunks cc = q, q + np, ... (q = tid / cpw),
+  // then thread j adds the np partial sums in order
+  const int np = BLOCK / cpw;   // host: cpw divides BLOCK
+  {
+    const int j = tid % cpw, q = tid / cpw;
     float o = 0.f;
-#pragma unroll 8
-    for (int cc = 0; cc < nch; cc++) o = fmaf(fw[cc], accs[cc * cpw + j], o);
-    ll_put_f32(ol + j, o / lsum[0], st.k1);
+    for (int cc = q; cc < nch; cc += np) o = fmaf(fw[cc], accs[cc * cpw + j], o);
+    part[tid] = o;
+  }
+  __syncthreads();
+  uint64_t* ol = wsp<uint64_t>(a, a.off.olat) + (size_t)h * KL + c0;
+  if (tid < cpw) {
+    float o = 0.f;
+    for (int q = 0; q < np; q++) o += part[q * cpw + tid];
+    ll_put_f32(ol + tid, o / lsum[0], st.k1);
   }
   stamp(a, cx, st, TR_ATT_MERGED);
   return true;
