@@ -504,12 +504,18 @@ __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Ste
   return true;
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
 // ------------------------------------------------------------------ attention (GQA)
 // One workgroup = one (kv head g, token chunk) pair. Scores for the G query heads of
 // the group, chunk-local softmax, P.V, then a partial (m, l, acc[HD]) per head; then
 // each workgroup of the group merges its own slice of the group's outputs.
-//  * scores: 16-byte K loads, HD/8 lanes per token row, ATT_NB row passes held in
-//    registers; the per-token dot is reduced with DPP moves inside each 16-lane row;
+//  * scores of the static history rows on the matrix cores (mfma 16x16x32 bf16): a wave
+//    takes 16 rows per product, lane l holding 16 bytes of row l % 16 (its 16-byte chunks
+//    l / 16 + 4 ks), exactly the B operand; q (fp32) enters as a bf16 high and low part
+//    (two products), so the scores keep fp32-level q; the rows written inside the launch
+//    take the vector path (16-byte K loads, HD/8 lanes per row, DPP row sums);
 //  * P.V: each wave owns a contiguous token range and each lane HD/64 dims, so the sum
 //    over tokens needs no lane exchange, only one cross-wave pass through LDS;
 //  * the static history rows of the first batch (K and V) are issued before q is read;
@@ -546,6 +552,8 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
   float* sc = L.act + G * HD + HD;                 // [G][chmax]
   float* red2 = sc + G * c.chmax;                  // [NWAVES][G][HD]
   float* ml = red2 + NWAVES * G * HD;              // [2G]
+  // [2][G][HD] bf16: scaled q, high and low parts (16-byte aligned for the operand reads)
+  uint16_t* qhl = reinterpret_cast<uint16_t*>(L.act + (((int)(ml + 2 * G - L.act) + 3) & ~3));
   // Rows [0, nst) of the chunk are static history (written before this launch) and are
   // streamed with plain loads; rows [nst, n) were written inside this launch (row pos by
   // this step) and are handled by a separate short pass. Static loads are unconditional:
@@ -553,8 +561,6 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
   // no load sits under a condition and the in-order load waits stay exact.
   const int nst = max(0, min(n, fresh - t0));
   auto srow = [&](int t) -> size_t { return (size_t)(nst > 0 ? t0 + min(t, nst - 1) : 0); };
-  auto tok = [&](int tb0, int b) { return tb0 + b * PASS + wave * TPW + tl; };
-  auto k_static = [&](int t) -> uint4 { return ld_g16(kbase + srow(t) * HD); };
   // V element(s) of this lane for token t (DPL bf16 values packed in a word)
   auto v_static = [&](int t) -> uint32_t {
     const uint16_t* p = vbase + srow(t) * HD;
@@ -584,10 +590,20 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
     }
   };
   const int pvs = min(pv1, max(pv0, nst));   // this wave's static P.V rows are [pv0, pvs)
-  uint4 kb[NB];
+  // static K rows in the matrix-core layout: group pass gp holds rows gp*GT + 16*wave + (lane & 15)
+  constexpr int KS = HD / 32;                        // k-steps of 32 dims
+  constexpr int GT = NWAVES * 16;                    // rows per group pass
+  constexpr int NGR = NB * PASS / GT > 0 ? NB * PASS / GT : 1;   // group passes in registers
+  static_assert(HD % 32 == 0 && G <= 16, "matrix-core scores");
+  const uint16_t* kmat = Ly.kc + (size_t)g * c.max_seq * HD + ((lane >> 4) * 8);
+  auto k_mf = [&](int t, int ks) -> uint4 { return ld_g16(kmat + srow(t) * HD + ks * 32); };
+  auto mrow = [&](int tb0, int gp) { return tb0 + gp * GT + wave * 16 + (lane & 15); };
+  uint4 kb[NGR][KS];
   uint32_t vb[NV];
 #pragma unroll
-  for (int b = 0; b < NB; b++) kb[b] = k_static(tok(0, b));
+  for (int gp = 0; gp < NGR; gp++)
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) kb[gp][ks] = k_mf(mrow(0, gp), ks);
 #pragma unroll
   for (int b = 0; b < NV; b++) vb[b] = v_static(pv0 + b);
   // q of the group, and the new k/v row for the chunk that holds position pos
@@ -606,6 +622,14 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
   for (int h = 0; h < G; h++)
 #pragma unroll
     for (int j = 0; j < 8; j++) qr[h][j] = qs[h * HD + dl * 8 + j] * scale;
+  // scaled q as bf16 high + low parts for the matrix cores (the pair carries 16 bits)
+  for (int i = tid_opaque(); i < G * HD; i += BLOCK) {
+    const float v = qs[i] * scale;
+    const uint32_t hb = f32_to_bf16(v);
+    qhl[i] = (uint16_t)hb;
+    qhl[G * HD + i] = (uint16_t)f32_to_bf16(v - __uint_as_float(hb << 16));
+  }
+  __syncthreads();
   stamp(a, cx, st, TR_ATT_Q);
   auto score = [&](int t, const uint4& kv, int lim) {
     const float kf[8] = {bf_lo(kv.x), bf_hi(kv.x), bf_lo(kv.y), bf_hi(kv.y),
@@ -619,14 +643,39 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
       if (dl == LPT - 1 && t < lim) sc[h * c.chmax + t] = sh;
     }
   };
-  // ---- pass 1: scores of the static rows (next batch issued as each register frees up)
-  // (no per-row branches: rows past nst are computed on clamped data and not stored)
-  for (int tb0 = 0; tb0 < nst; tb0 += NB * PASS) {
+  // ---- pass 1: scores of the static rows on the matrix cores (next group issued as each
+  // register set frees up; rows past nst are computed on clamped data and not stored)
+  {
+    const int qm = lane & 15;   // A operand row (head); rows >= G are zero
+    auto qop = [&](int part, int ks) -> bf16x8_t {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (qm < G) v = *reinterpret_cast<const uint4*>(qhl + part * G * HD + qm * HD + ks * 32 + (lane >> 4) * 8);
+      return __builtin_bit_cast(bf16x8_t, v);
+    };
+    for (int tb0 = 0; tb0 < nst; tb0 += NGR * GT) {
 #pragma unroll
-    for (int b = 0; b < NB; b++) score(tok(tb0, b), kb[b], nst);
-    if (tb0 + NB * PASS < nst) {
+      for (int gp = 0; gp < NGR; gp++) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int b = 0; b < NB; b++) kb[b] = k_static(tok(tb0 + NB * PASS, b));
+        for (int ks = 0; ks < KS; ks++) {
+          const bf16x8_t kv = __builtin_bit_cast(bf16x8_t, kb[gp][ks]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop(0, ks), kv, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qop(1, ks), kv, acc, 0, 0, 0);
+        }
+        // lane l holds heads 4 (l / 16) + i of row (l % 16)
+        const int t = mrow(tb0, gp);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const int h = 4 * (lane >> 4) + i;
+          if (h < G && t < nst) sc[h * c.chmax + t] = acc[i];
+        }
+      }
+      if (tb0 + NGR * GT < nst) {
+#pragma unroll
+        for (int gp = 0; gp < NGR; gp++)
+#pragma unroll
+          for (int ks = 0; ks < KS; ks++) kb[gp][ks] = k_mf(mrow(tb0 + NGR * GT, gp), ks);
+      }
     }
   }
   // ---- scores of the fresh rows
@@ -739,7 +788,7 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
       float M = -INFINITY;
       for (int cc = lane; cc < cpg; cc += 64)
         if (ml2[2 * cc + 1] > 0.f) M = fmaxf(M, ml2[2 * cc]);
-      M = wave_max(M);
+      M = wave_max_dpp(M);
       float ls = 0.f;
       for (int cc = lane; cc < cpg; cc += 64) {
         const float l = ml2[2 * cc + 1];
@@ -747,7 +796,7 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
         fw[wave * cpg + cc] = f;
         ls += f * l;
       }
-      ls = wave_sum(ls);
+      ls = wave_sum_dpp(ls);
       if (lane == 0) lsum[wave] = ls;
     }
     __syncthreads();
@@ -755,9 +804,14 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
     for (int j = tid_opaque(); j < nd; j += BLOCK) {
       const int d = d0 + j, hh = d / HD - h0;
       const float* f = fw + hh * cpg;
-      float o = 0.f;
-#pragma unroll 8
-      for (int cc = 0; cc < cpg; cc++) o = fmaf(f[cc], accs[cc * nd + j], o);
+      float o4[4] = {0.f, 0.f, 0.f, 0.f};   // four independent chains, added in a fixed order
+      int cc = 0;
+      for (; cc + 4 <= cpg; cc += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; u++) o4[u] = fmaf(f[cc + u], accs[(cc + u) * nd + j], o4[u]);
+      }
+      for (; cc < cpg; cc++) o4[0] = fmaf(f[cc], accs[cc * nd + j], o4[0]);
+      const float o = (o4[0] + o4[1]) + (o4[2] + o4[3]);
       ll_put_f32(oll + d, o / lsum[hh], k1);
     }
   }
@@ -1417,7 +1471,7 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
     // attention: q [G*HD] + new k/v row [HD] + scores [G*chmax] + wave sums [8*G*HD] + (m, l);
     // merge staging: at most G*HD/cpg + 1 dims of cpg chunks, (m, l) and weights of two heads
     int act = std::max({c->hidden, c->n_heads * c->head_dim, k->slots * c->inter,
-                        k->G * c->head_dim + c->head_dim + k->G * k->chmax + NWAVES * k->G * c->head_dim + 2 * k->G,
+                        2 * k->G * c->head_dim + c->head_dim + k->G * k->chmax + NWAVES * k->G * c->head_dim + 2 * k->G + 8,
                         k->cpg * (k->G * c->head_dim / k->cpg + 1) + 8 * k->cpg + 8});
     k->act_floats = (int)al(act, 64);
     k->stage_words = (int)al(c->hidden / 2 + 2, 64);
