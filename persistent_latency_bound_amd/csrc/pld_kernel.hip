@@ -606,14 +606,20 @@ __device__ __forceinline__ bool attention_gqa(Ctx& cx, const KArgs& a, const Ste
     for (int ks = 0; ks < KS; ks++) kb[gp][ks] = k_mf(mrow(0, gp), ks);
 #pragma unroll
   for (int b = 0; b < NV; b++) vb[b] = v_static(pv0 + b);
-  // q of the group, and the new k/v row for the chunk that holds position pos
-  if (!ll_fetch<per_for(G * HD)>(cx, reinterpret_cast<uint32_t*>(qs), wsp<uint64_t>(a, a.off.q) + (size_t)g * G * HD,
-                                 G * HD, k1, W_QKV))
-    return false;
-  if (t0 <= pos && pos < t1) {
+  // q of the group and, for the chunk that holds position pos, the new k/v row: one fetch
+  // (both come from the QKV stage; kvn follows qs in LDS)
+  {
     constexpr int kR2 = SH::NKV * HD / 2;
-    auto kv_idx = [g](int i) { return i < HD / 2 ? g * (HD / 2) + i : kR2 + g * (HD / 2) + (i - HD / 2); };
-    if (!ll_fetch<1>(cx, kvn, wsp<uint64_t>(a, a.off.kv), HD, k1, W_KV, kv_idx)) return false;
+    const uint32_t qw = (uint32_t)(a.off.q / 8) + (uint32_t)(g * G * HD), kvw = (uint32_t)(a.off.kv / 8);
+    auto idx = [=](int i) -> int {
+      if (i < G * HD) return (int)qw + i;
+      const int j = i - G * HD;
+      return (int)kvw + (j < HD / 2 ? g * (HD / 2) + j : kR2 + g * (HD / 2) + (j - HD / 2));
+    };
+    const int nw = G * HD + ((t0 <= pos && pos < t1) ? HD : 0);
+    if (!ll_fetch<per_for(G * HD + HD)>(cx, reinterpret_cast<uint32_t*>(qs), reinterpret_cast<const uint64_t*>(a.ws),
+                                        nw, k1, W_QKV, idx))
+      return false;
   }
   stamp(a, cx, st, TR_ATT_READY);
   const float scale = 1.0f / sqrtf((float)HD);
