@@ -516,6 +516,60 @@ __device__ __forceinline__ void sel_count(const SelLds& S, V&& val, C&& is_cand,
                            __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 }
+// 8-bit digit passes (the list path): each wave adds its candidates' digits
+// (val(j) >> shift) & nbm1 into its own 256-bin histogram in LDS (S.hist rows, zero
+// before the first pass; sel_finish8 clears what it reads).
+template <int NC, typename V, typename C>
+__device__ __forceinline__ void sel_count8(const SelLds& S, V&& val, C&& is_cand, int shift, uint32_t nbm1) {
+  const int wave = __builtin_amdgcn_readfirstlane(tid_opaque() >> 6);
+  uint32_t* hw = S.hist + wave * 256;
+#pragma unroll
+  for (int j = 0; j < NC; j++) {
+    if (is_cand(j)) {
+      const uint32_t d = (val(j) >> shift) & nbm1;
+      __hip_atomic_fetch_add(lds_ptr(&hw[d]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    }
+  }
+}
+// After sel_count8 with nb <= 256 bins: thread t < nb owns bin nb-1-t; the inclusive scan
+// over t counts the candidates in bins at or above it, and the first t where that reaches
+// need holds the bin of the need-th largest candidate. Returns the bin; need and ncand
+// become the rank within the bin and the bin's count.
+__device__ __forceinline__ uint32_t sel_finish8(const SelLds& S, uint32_t nb, int& need, int& ncand) {
+  const int tid = tid_opaque(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __syncthreads();
+  uint32_t cnt = 0u;
+  const int bn = (int)nb - 1 - tid;
+  if (tid < 256 && bn >= 0) {
+#pragma unroll
+    for (int w = 0; w < NWAVES; w++) {
+      cnt += S.hist[w * 256 + bn];
+      S.hist[w * 256 + bn] = 0u;
+    }
+  }
+  const uint32_t x = wave_incl_scan_u32(cnt);
+  if (lane == 63 && wave < 4) S.wsum[wave] = x;
+  __syncthreads();
+  uint32_t cum = x;
+  for (int w = 0; w < wave && w < 4; w++) cum += S.wsum[w];
+  const bool hit = tid < 256 && bn >= 0 && cum >= (uint32_t)need;
+  const uint64_t m = __ballot(hit);
+  if (wave < 4 && lane == 0) S.tot[wave] = m ? (uint32_t)(wave * 64 + __ffsll((unsigned long long)m) - 1) : 0xffffffffu;
+  if (hit && (uint32_t)tid == (m ? (uint32_t)(wave * 64 + __ffsll((unsigned long long)m) - 1) : 0xffffffffu)) {
+    S.sv[4 + wave] = (uint32_t)need - (cum - cnt);   // rank inside the bin
+    S.sv[8 + wave] = cnt;
+  }
+  __syncthreads();
+  uint32_t tb = S.tot[0], wb = 0;
+  for (int w = 1; w < 4; w++)
+    if (S.tot[w] < tb) { tb = S.tot[w]; wb = (uint32_t)w; }
+  need = (int)S.sv[4 + wb];
+  ncand = (int)S.sv[8 + wb];
+  const uint32_t bin = nb - 1u - tb;
+  __syncthreads();   // S.tot / S.sv / S.wsum are reused by the next pass
+  return bin;
+}
 // Ranks up to SEL_CMAX candidates (S.chi/clo/ctk[0, nc)) by (key desc, token asc); calls
 // taken(c, rank < need) from one lane per candidate.
 template <typename F>
@@ -722,6 +776,7 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
     if (tid < nwg) b = r <= SEL_LIST ? S.lst[tid * SEL_LIST + r - 1] : 0u;
     b = wave_minmax_u32<false>(b);
     if (lane == 0) S.tot[wave] = b;
+    if (tid == 0) S.sv[12] = 0u;   // rank-array fill count
     for (int i = tid; i < SEL_BMW * BLOCK; i += BLOCK) S.bm[i] = 0u;
     for (int rr = 0; rr < SEL_ROWS; rr++) S.hist[rr * BLOCK + tid] = 0u;   // passes clear while reducing
   }
@@ -734,6 +789,12 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
   for (int q = 0; q < SEL_EPT; q++) {
     const int e = tid + q * BLOCK;
     etk[q] = e < NE ? ld_u32_off(sa.itok, (uint32_t)e * 4u) : 0u;
+  }
+  uint32_t elo[SEL_EPT];   // and their low halves (ranking and ties)
+#pragma unroll
+  for (int q = 0; q < SEL_EPT; q++) {
+    const int e = tid + q * BLOCK;
+    elo[q] = e < NE ? ld_u32_off(sa.ilo, (uint32_t)e * 4u) : 0u;
   }
   uint32_t eh[SEL_EPT];
   uint32_t ev = 0u, cn = 0u, mx = 0u, mn = 0xffffffffu;
@@ -784,11 +845,11 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
   int need = K, ncand = (int)C;
   int shift = 32 - common, npass = 0;
   while (ncand > SEL_CMAX && shift > 0) {
-    const int wdt = min(5, shift);
+    const int wdt = min(8, shift);
     shift -= wdt;
-    sel_count<SEL_EPT>(S, [&](int q) { return eh[q]; }, [&](int q) { return (ev >> q & 1u) && (eh[q] & pm) == pre; },
-                       shift, (1u << wdt) - 1u);
-    const uint32_t b = sel_finish_pass(S, 1u << wdt, 0u, need, ncand);
+    sel_count8<SEL_EPT>(S, [&](int q) { return eh[q]; }, [&](int q) { return (ev >> q & 1u) && (eh[q] & pm) == pre; },
+                        shift, (1u << wdt) - 1u);
+    const uint32_t b = sel_finish8(S, 1u << wdt, need, ncand);
     pre |= b << shift;
     pm |= ((1u << wdt) - 1u) << shift;
     stp(39 + min(npass++, 5));
@@ -802,20 +863,17 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
     S.efl[e] = (uint8_t)((v && mk > pre) ? 1u : (v && mk == pre) ? 2u : 0u);
     ecb |= (uint32_t)(v && mk == pre) << q;
   }
+  uint32_t pend = ecb;   // entries still undecided (to be ranked)
   if (ncand > SEL_CMAX) {
     // ---- the candidates share the whole high half: the low halves, then the token order
-    uint32_t elo[SEL_EPT];
-#pragma unroll
-    for (int q = 0; q < SEL_EPT; q++)
-      elo[q] = (ecb >> q & 1u) ? ld_u32_off(sa.ilo, (uint32_t)(tid + q * BLOCK) * 4u) : 0u;
     uint32_t lpre = 0, lpm = 0;
     int ls = 32;
     while (ncand > SEL_CMAX && ls > 0) {
-      const int wdt = min(5, ls);
+      const int wdt = min(8, ls);
       ls -= wdt;
-      sel_count<SEL_EPT>(S, [&](int q) { return elo[q]; },
-                         [&](int q) { return (ecb >> q & 1u) && (elo[q] & lpm) == lpre; }, ls, (1u << wdt) - 1u);
-      const uint32_t b = sel_finish_pass(S, 1u << wdt, 0u, need, ncand);
+      sel_count8<SEL_EPT>(S, [&](int q) { return elo[q]; },
+                          [&](int q) { return (ecb >> q & 1u) && (elo[q] & lpm) == lpre; }, ls, (1u << wdt) - 1u);
+      const uint32_t b = sel_finish8(S, 1u << wdt, need, ncand);
       lpre |= b << ls;
       lpm |= ((1u << wdt) - 1u) << ls;
     }
@@ -835,47 +893,36 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
       cut = lo_m;
       ncand = 0;
     }
+    pend = 0u;
 #pragma unroll
     for (int q = 0; q < SEL_EPT; q++) {
       if (ecb >> q & 1u) {
         const int e = tid + q * BLOCK;
         const uint32_t mk = elo[q] & lpm;
+        const bool und = mk == lpre && ncand > 0;
         S.efl[e] = (uint8_t)((mk > lpre || (mk == lpre && ncand == 0 && etk[q] < (uint32_t)cut)) ? 1u
-                             : (mk == lpre && ncand > 0) ? 2u : 0u);
+                             : und ? 2u : 0u);
+        pend |= (uint32_t)und << q;
       }
     }
   }
-  __syncthreads();
   if (ncand > 0) {
-    // ---- at most SEL_CMAX candidates: rank by (key desc, token asc) on full keys
-    const uint32_t* f4 = reinterpret_cast<const uint32_t*>(S.efl + tid * SEL_EPT);
-    uint32_t fw[SEL_EPT / 4];
-    uint32_t nf = 0;
+    // ---- at most SEL_CMAX undecided entries: their owners append them (hi, lo, token,
+    // entry) to the rank arrays (order of arrival; the ranking does not depend on it)
 #pragma unroll
-    for (int q = 0; q < SEL_EPT / 4; q++) {
-      fw[q] = f4[q];
-      nf += __popc((fw[q] >> 1) & 0x01010101u);
-    }
-    uint32_t o = block_excl_scan(nf, S.wsum);
-#pragma unroll
-    for (int q = 0; q < SEL_EPT / 4; q++) {
-      uint32_t m = (fw[q] >> 1) & 0x01010101u;
-      while (m) {
-        const int b = __ffs(m) - 1;
-        m &= m - 1u;
-        if (o < (uint32_t)SEL_CMAX) S.cix[o] = (uint32_t)(tid * SEL_EPT + 4 * q + (b >> 3));
-        o++;
+    for (int q = 0; q < SEL_EPT; q++) {
+      if (pend >> q & 1u) {
+        const uint32_t o = __hip_atomic_fetch_add(lds_ptr(&S.sv[12]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (o < (uint32_t)SEL_CMAX) {
+          S.chi[o] = eh[q];
+          S.clo[o] = elo[q];
+          S.ctk[o] = etk[q];
+          S.cix[o] = (uint32_t)(tid + q * BLOCK);
+        }
       }
     }
     __syncthreads();
     const int nc = min(ncand, SEL_CMAX);
-    if (tid < nc) {
-      const uint32_t e = S.cix[tid];
-      S.chi[tid] = S.lst[e];
-      S.ctk[tid] = ld_u32_off(sa.itok, e * 4u);
-      S.clo[tid] = ld_u32_off(sa.ilo, e * 4u);
-    }
-    __syncthreads();
     stp(45);
     sel_rank(S, nc, need, [&](int c, bool tk) { S.efl[S.cix[c]] = tk ? 1 : 0; });
     __syncthreads();
