@@ -94,7 +94,7 @@ def cpu_baseline(shape, pos: int, budget_s: float = 20.0) -> dict:
                       f"generates the weights; fp64 NumPy, BLAS and generator threads = {cores}"}
 
 
-TR_SLOTS = 48   # stamps per (step, workgroup) written by the device trace
+TR_SLOTS = 56   # stamps per (step, workgroup) written by the device trace
 SLOT_NAMES = {32: "head_ready", 33: "head_gemv", 34: "token", 0: "start", 1: "x_ready", 2: "qkv_done", 3: "att_ready", 4: "att_done", 5: "o_ready", 6: "wo_done",
               7: "h2_ready", 8: "router_ready", 9: "ffn_done", 10: "m_ready", 11: "down_done", 12: "att_q",
               13: "att_softmax", 14: "att_partial", 15: "att_merged", 16: "topk", 18: "m_stored", 19: "down_gemv",
@@ -102,7 +102,8 @@ SLOT_NAMES = {32: "head_ready", 33: "head_gemv", 34: "token", 0: "start", 1: "x_
               26: "merge_fetched", 27: "router_logit", 28: "att_drained", 30: "att_scores", 17: "blk0_staged", 31: "blk0_done",
               35: "idx_done", 36: "sel_keys", 37: "sel_passes", 38: "sel_done", 39: "sel_pass0", 40: "sel_pass1",
               41: "sel_pass2", 42: "sel_pass3", 43: "sel_pass4", 44: "sel_pass5", 45: "sel_rank_loaded",
-              46: "sel_lists_arrived", 47: "sel_fetch_start"}
+              46: "sel_lists_arrived", 47: "sel_fetch_start",
+              48: "cq_ready", 49: "q_gemv"}
 
 
 def write_trace_summary(dec, x, out, R, path, pos):

@@ -235,8 +235,8 @@ pld_status pld_debug_buffer(pld_handle* h, const char* name, void** ptr, size_t*
 pld_status pld_launch_shape(pld_handle* h, int32_t* n_wg, int32_t* block);
 
 /* Device trace for profiling inside one launch: while set, every later launch writes, for
- * each (step, workgroup) of its first bytes/(n_wg*48*8) steps (a step is one layer of one
- * token), 48 uint64 wall-clock stamps (hipDeviceAttributeWallClockRate ticks) taken by the
+ * each (step, workgroup) of its first bytes/(n_wg*56*8) steps (a step is one layer of one
+ * token), 56 uint64 wall-clock stamps (hipDeviceAttributeWallClockRate ticks) taken by the
  * workgroup's first thread at fixed points of the step; a slot the step does not pass
  * stays 0. Slots: 0 start, 1 layer input ready, 2 q/k/v (MLA: c_q, c_kv) published,
  * 3/12/13/30 attention phases, 4 attention done, 5 attention output ready, 6 h2

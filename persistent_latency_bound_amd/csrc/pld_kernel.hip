@@ -52,7 +52,8 @@ enum TraceSlot {
   TR_QKV_GEMV = 21, TR_SHARED_GEMV = 22, TR_ATT_PV = 23, TR_X_NORMED = 24, TR_MERGE_START = 25,
   TR_MERGE_COPIED = 26, TR_RT_LOGIT = 27, TR_ATT_DRAINED = 28, TR_ATT_SCORES = 30, TR_HEAD_READY = 32,
   TR_HEAD_GEMV = 33, TR_TOKEN = 34, TR_IDX_DONE = 35, TR_SEL_KEYS = 36, TR_SEL_PASSES = 37, TR_SEL_DONE = 38,
-  TR_SLOTS = 48
+  TR_CQ_READY = 48, TR_Q_GEMV = 49,
+  TR_SLOTS = 56
 };
 
 struct KCfg {

@@ -165,7 +165,7 @@ __device__ __forceinline__ bool stage_q_mla(Ctx& cx, const KArgs& a, const Step&
         return false;
       rmsnorm_reg<SH::QL>(L.act, gq, c.eps, L.red);
     }
-    stamp(a, cx, st, TR_ATT_READY);
+    stamp(a, cx, st, TR_CQ_READY);
     return true;
   };
   seg_begin();
@@ -182,6 +182,7 @@ __device__ __forceinline__ bool stage_q_mla(Ctx& cx, const KArgs& a, const Step&
   seg_end();
   if (!gemv_list<SH::FP8, SH::QL, PLD_IF_WO, SH::SPARSE>(L.segs, ns, L.act, L.outb, OUT_STORE, pre_q)) return false;
   if (!pre_q()) return false;
+  stamp(a, cx, st, TR_Q_GEMV);
   __syncthreads();
   auto outv = [&](int i) -> float {
     if constexpr (SH::SPARSE) return (float)reinterpret_cast<const double*>(L.outb)[i];
