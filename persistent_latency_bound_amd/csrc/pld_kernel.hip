@@ -24,6 +24,7 @@
 //  * the shared expert runs while the router top-k is pending, as the same article
 //    describes for its side stream.
 #include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -155,14 +156,18 @@ __device__ __forceinline__ void ll_put_f32(uint64_t* p, float v, uint32_t ep) { 
 struct IdxLinear {
   __device__ __forceinline__ int operator()(int i) const { return i; }
 };
+// Where a fetched 32-bit payload goes: the word itself (default), or another placement.
+struct StU32 {
+  __device__ __forceinline__ void operator()(uint32_t* dst, int i, uint32_t v) const { dst[i] = v; }
+};
 
 // Reads the LL words src[idx(i)], i in [0, n), of epoch ep into dst[i] (LDS). PER loads
 // per thread are issued together; words that are not yet published are re-read in a
 // bounded loop (watchdog wait id wid). Every thread of the block must call; returns
 // false (in every thread) on expiry or when another workgroup raised the abort flag.
-template <int PER, typename Idx = IdxLinear>
+template <int PER, typename Idx = IdxLinear, typename St = StU32>
 __device__ __forceinline__ bool ll_fetch(Ctx& cx, uint32_t* dst, const uint64_t* src, int n, uint32_t ep, int wid,
-                                         Idx idx = Idx{}) {
+                                         Idx idx = Idx{}, St store = St{}) {
   int failed = 0;
   const int tid = tid_opaque();
   for (int base = 0; base < n; base += BLOCK * PER) {
@@ -198,7 +203,7 @@ __device__ __forceinline__ bool ll_fetch(Ctx& cx, uint32_t* dst, const uint64_t*
 #pragma unroll
     for (int j = 0; j < PER; j++) {
       const int i = base + j * BLOCK + tid;
-      if (i < n) dst[i] = (uint32_t)v[j];
+      if (i < n) store(dst, i, (uint32_t)v[j]);
     }
   }
   return !__syncthreads_or(failed);

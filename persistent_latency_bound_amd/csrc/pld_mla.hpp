@@ -1361,22 +1361,30 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
     }
   }
   stamp(a, cx, st, TR_ATT_SOFTMAX);
-  // publish the partial of each head: LL words [m, l, acc[0..KL)] at ((h * nch) + ch) * (KL + 2)
+  // publish the partial of each head: LL words [m, l, acc as fp16 pairs] at
+  // ((h * nch) + ch) * PSTR (fp16 keeps the merged result at fp32 accuracy here: the
+  // partial sums stay far inside its range, and the error is set by the bf16 P operand)
+  constexpr int PSTR = KL / 2 + 2;
   vm_wait();   // the cache row appended above is visible before this workgroup's next publication
   __syncthreads();
   uint64_t* pll = wsp<uint64_t>(a, a.off.part);
   if ((lane & 31) == 0 && (HS == 2 || lane == 0)) {
-    uint64_t* p = pll + ((size_t)(hbase + hown) * nch + ch) * (KL + 2);
+    uint64_t* p = pll + ((size_t)(hbase + hown) * nch + ch) * PSTR;
     ll_put_f32(p, m_run, k1);
     ll_put_f32(p + 1, l_run, k1);
   }
 #pragma unroll
   for (int t = 0; t < 4; t++) {
-    const int col = (wave * 4 + t) * 16 + ln;
+    const int col = (wave * 4 + t) * 16 + ln;   // even lanes publish columns (col, col + 1)
 #pragma unroll
     for (int q = 0; q < 4; q++) {
+      const float nb = dpp_mov<0xB1, 0xf, false>(O[t][q]);   // the odd neighbour's value
       const int h = 4 * lq + q;
-      if (h < HPW) ll_put_f32(pll + ((size_t)(hbase + h) * nch + ch) * (KL + 2) + 2 + col, O[t][q], k1);
+      if (h < HPW && (ln & 1) == 0) {
+        const uint32_t pr = (uint32_t)__half_as_ushort(__float2half_rn(O[t][q])) |
+                            ((uint32_t)__half_as_ushort(__float2half_rn(nb)) << 16);
+        ll_put(pll + ((size_t)(hbase + h) * nch + ch) * PSTR + 2 + col / 2, pr, k1);
+      }
     }
   }
   stamp(a, cx, st, TR_ATT_PARTIAL);
@@ -1392,11 +1400,27 @@ __device__ __forceinline__ bool stage_merge_mla(Ctx& cx, const KArgs& a, const S
   const int h = (cx.w * cpw) / KL, c0 = (cx.w * cpw) % KL;
   const int tid = tid_opaque();
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nacc = nch * cpw;
+  constexpr int PSTR = KL / 2 + 2;
+  const int cpw2 = cpw / 2;             // fp16-pair words per chunk
+  const int nacc = nch * cpw;           // floats
+  const int naw = nch * cpw2;           // their words
   auto pidx = [=](int i) -> int {
-    if (i < nacc) return (h * nch + i / cpw) * (KL + 2) + 2 + c0 + i % cpw;
-    const int j = i - nacc;
-    return (h * nch + (j >> 1)) * (KL + 2) + (j & 1);
+    if (i < naw) return (h * nch + i / cpw2) * PSTR + 2 + c0 / 2 + i % cpw2;
+    const int j = i - naw;
+    return (h * nch + (j >> 1)) * PSTR + (j & 1);
+  };
+  // word i < naw: the fp16 pair of chunk i / cpw2 at columns 2 (i % cpw2), +1 -> floats 2i, 2i + 1;
+  // then the (m, l) words after the nacc floats
+  struct StMerge {
+    int naw;
+    __device__ __forceinline__ void operator()(uint32_t* dst, int i, uint32_t v) const {
+      if (i < naw) {
+        reinterpret_cast<float2*>(dst)[i] = make_float2(__half2float(__ushort_as_half((unsigned short)(v & 0xffffu))),
+                                                         __half2float(__ushort_as_half((unsigned short)(v >> 16))));
+      } else {
+        dst[naw + i] = v;
+      }
+    }
   };
   float* accs = L.act;              // [nch][cpw]
   float* mls = L.act + nacc;        // [nch][2]
@@ -1404,9 +1428,9 @@ __device__ __forceinline__ bool stage_merge_mla(Ctx& cx, const KArgs& a, const S
   float* lsum = fw + nch;           // [1]
   float* part = lsum + 1;           // [BLOCK] partial sums over chunk subsets
   stamp(a, cx, st, TR_MERGE_START);
-  // one round of loads covers up to 17 * BLOCK words (64 chunks x 128 columns + their m, l)
-  if (!ll_fetch<17>(cx, reinterpret_cast<uint32_t*>(L.act), wsp<uint64_t>(a, a.off.part), nacc + 2 * nch, st.k1,
-                    W_PART, pidx))
+  // one round of loads covers up to 9 * BLOCK words (64 chunks x 64 fp16-pair words + their m, l)
+  if (!ll_fetch<9>(cx, reinterpret_cast<uint32_t*>(L.act), wsp<uint64_t>(a, a.off.part), naw + 2 * nch, st.k1,
+                   W_PART, pidx, StMerge{naw}))
     return false;
   stamp(a, cx, st, TR_MERGE_COPIED);
   if (wave == 0) {
