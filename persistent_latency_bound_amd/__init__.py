@@ -255,7 +255,8 @@ class Decoder:
             raw = raw.view(torch.int32)[0::2].contiguous().view(torch.uint8)
         default = {"logits": torch.float64, "sel": torch.int32, "x": torch.int16, "qi": torch.int16,
                    "isel": torch.int32, "ikh": torch.int32, "ikl": torch.int32,
-                   "ilist": torch.int32, "ilo": torch.int32, "itok": torch.int32}
+                   "ilist": torch.int32, "ilo": torch.int32, "itok": torch.int32,
+                   "qlat": torch.int16, "qrope": torch.int16}   # bf16 bits
         if name == "cq" and getattr(self.shape, "index_topk", 0):
             default["cq"] = torch.float64   # the sparse layer passes c_q' in fp64 (word pairs)
         return raw.view(dtype or default.get(name, torch.float32))

@@ -204,10 +204,11 @@ __device__ __forceinline__ bool stage_q_mla(Ctx& cx, const KArgs& a, const Step&
       ll_put_f32(qn + h * SH::ND + k, v0, st.k1);
       ll_put_f32(qn + h * SH::ND + k + 1, v1, st.k1);
     } else {
+      // q_rope as bf16 pairs: the attention's matrix cores take it in bf16 (same rounding)
       const int d = k - SH::ND;
       const float cs = rope[d], sn = rope[d + 1];
-      ll_put_f32(qr + h * SH::RD + d, v0 * cs - v1 * sn, st.k1);
-      ll_put_f32(qr + h * SH::RD + d + 1, v0 * sn + v1 * cs, st.k1);
+      ll_put(qr + (h * SH::RD + d) / 2, f32_to_bf16(v0 * cs - v1 * sn) | (f32_to_bf16(v0 * sn + v1 * cs) << 16),
+             st.k1);
     }
   }
   stamp(a, cx, st, TR_ATT_Q);
@@ -1062,11 +1063,15 @@ __device__ __forceinline__ bool stage_absorb_mla(Ctx& cx, const KArgs& a, const 
 #pragma unroll
   for (int e = 0; e < EPC; e++) red[rr * cpw + ck * EPC + e] = acc[e];
   __syncthreads();
-  uint64_t* ql = wsp<uint64_t>(a, a.off.qlat) + (size_t)h * SH::KL + c0;
-  for (int j = tid; j < cpw; j += BLOCK) {
-    float s = 0.f;
-    for (int g = 0; g < rpp; g++) s += red[g * cpw + j];
-    ll_put_f32(ql + j, s, st.k1);
+  // q_lat as bf16 pairs: the attention's matrix cores take it in bf16 (same rounding)
+  uint64_t* ql = wsp<uint64_t>(a, a.off.qlat) + ((size_t)h * SH::KL + c0) / 2;
+  for (int j = 2 * tid; j < cpw; j += 2 * BLOCK) {
+    float s0 = 0.f, s1 = 0.f;
+    for (int g = 0; g < rpp; g++) {
+      s0 += red[g * cpw + j];
+      s1 += red[g * cpw + j + 1];
+    }
+    ll_put(ql + j / 2, f32_to_bf16(s0) | (f32_to_bf16(s1) << 16), st.k1);
   }
   __syncthreads();
   stamp(a, cx, st, TR_ATT_SCORES);
@@ -1211,17 +1216,21 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
       if (hg == 0) st_u32(reinterpret_cast<uint32_t*>(Ly.lat + (size_t)pos * LAT) + i, pair);   // cache append
     }
   }
-  // q of the head group: q_lat [HPW][KL] and q_rope [HPW][RD] (LL) -> bf16 rows of Qs
-  if (!ll_fetch<per_for(HPW * KL)>(cx, reinterpret_cast<uint32_t*>(qtmp),
-                                   wsp<uint64_t>(a, a.off.qlat) + (size_t)hbase * KL, HPW * KL, k1, W_QLAT))
-    return false;
-  if (!ll_fetch<per_for(HPW * RD)>(cx, reinterpret_cast<uint32_t*>(qtmp + HPW * KL),
-                                   wsp<uint64_t>(a, a.off.qr) + (size_t)hbase * RD, HPW * RD, k1, W_QLAT))
-    return false;
-  for (int i = tid; i < 16 * LAT; i += BLOCK) {
-    const int h = i / LAT, k = i % LAT;
-    const float v = h >= HPW ? 0.f : (k < KL ? qtmp[h * KL + k] : qtmp[HPW * KL + h * RD + (k - KL)]);
-    Qs[h * CSTR + k] = (uint16_t)bf16_bits(v);
+  // q of the head group: q_lat [HPW][KL] and q_rope [HPW][RD] as bf16 pairs (LL) -> rows of Qs
+  {
+    uint32_t* qw = reinterpret_cast<uint32_t*>(qtmp);   // [HPW][KL/2] then [HPW][RD/2] words
+    if (!ll_fetch<per_for(HPW * KL / 2)>(cx, qw, wsp<uint64_t>(a, a.off.qlat) + (size_t)hbase * KL / 2, HPW * KL / 2,
+                                         k1, W_QLAT))
+      return false;
+    if (!ll_fetch<per_for(HPW * RD / 2)>(cx, qw + HPW * KL / 2, wsp<uint64_t>(a, a.off.qr) + (size_t)hbase * RD / 2,
+                                         HPW * RD / 2, k1, W_QLAT))
+      return false;
+    static_assert(CSTR % 2 == 0, "Qs rows hold whole bf16 pairs");
+    for (int i = tid; i < 16 * LAT / 2; i += BLOCK) {
+      const int h = i / (LAT / 2), k2 = i % (LAT / 2);
+      const uint32_t v = h >= HPW ? 0u : (k2 < KL / 2 ? qw[h * (KL / 2) + k2] : qw[HPW * KL / 2 + h * (RD / 2) + (k2 - KL / 2)]);
+      reinterpret_cast<uint32_t*>(Qs + h * CSTR)[k2] = v;
+    }
   }
   for (int i = tid; i < 16 * TB; i += BLOCK) Ps[i] = 0;
   __syncthreads();
