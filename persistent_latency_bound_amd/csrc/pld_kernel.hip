@@ -1012,55 +1012,60 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
         if (rr < c.topk) L.isel[rr] = ee;
       }
     } else if (tid_opaque() < 64) {
-      const int lane = tid_opaque();
-      const int ns = (c.E + 63) >> 6;   // slots in use (uniform)
-      uint64_t ks[RT_SLOTS];             // 0: no expert, or already taken (no score's key is 0)
+      // NS slots per lane, a compile-time count (4 up to 256 experts): the unused slots
+      // hold key 0, which never wins, so every loop below is branch-free
+      auto select = [&](auto ns_tag) {
+        constexpr int NS = decltype(ns_tag)::value;
+        const int lane = tid_opaque();
+        uint64_t ks[NS];   // 0: no expert, or already taken (no score's key is 0)
 #pragma unroll
-      for (int i = 0; i < RT_SLOTS; i++) {
-        const int e = lane + 64 * i;
-        const double ke = e < c.E ? lk[2 * e + 1] : 0.0;
-        const uint64_t bb = (uint64_t)__double_as_longlong(ke == 0.0 ? 0.0 : ke);
-        ks[i] = e < c.E ? ((bb >> 63) ? ~bb : (bb | (1ull << 63))) : 0ull;
-      }
-      for (int r = 0; r < c.topk; r++) {
-        // this lane's best remaining expert (strict > keeps the lower index on ties)
-        uint64_t b = ks[0];
-        uint32_t bi = 0u;
-#pragma unroll
-        for (int i = 1; i < RT_SLOTS; i++) {
-          if (i >= ns) break;
-          const bool gt = ks[i] > b;
-          b = gt ? ks[i] : b;
-          bi = gt ? (uint32_t)i : bi;
+        for (int i = 0; i < NS; i++) {
+          const int e = lane + 64 * i;
+          const double ke = e < c.E ? lk[2 * e + 1] : 0.0;
+          const uint64_t bb = (uint64_t)__double_as_longlong(ke == 0.0 ? 0.0 : ke);
+          ks[i] = e < c.E ? ((bb >> 63) ? ~bb : (bb | (1ull << 63))) : 0ull;
         }
-        // wave-wide largest key (DPP moves; a lane keeps its own value where a move
-        // does not write it)
-        uint64_t m = b;
-        auto step = [&](auto ctrl_tag) {
-          constexpr int CTRL = decltype(ctrl_tag)::value >> 4, RM = decltype(ctrl_tag)::value & 0xf;
-          const uint64_t o = ((uint64_t)dpp_keep_u32<CTRL, RM>((uint32_t)(m >> 32)) << 32) |
-                             dpp_keep_u32<CTRL, RM>((uint32_t)m);
-          m = o > m ? o : m;
-        };
-        step(std::integral_constant<int, (0xB1 << 4) | 0xf>{});
-        step(std::integral_constant<int, (0x4E << 4) | 0xf>{});
-        step(std::integral_constant<int, (0x141 << 4) | 0xf>{});
-        step(std::integral_constant<int, (0x140 << 4) | 0xf>{});
-        step(std::integral_constant<int, (0x142 << 4) | 0xa>{});
-        step(std::integral_constant<int, (0x143 << 4) | 0xc>{});
-        const uint64_t K = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(m >> 32), 63) << 32) |
-                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)m, 63);
-        // the expert: the lowest index among the lanes holding that key
-        const uint32_t mye = (uint32_t)lane + 64u * bi;
-        const bool hold = b == K;
-        const uint64_t hm = __ballot(hold);
-        uint32_t ee;
-        if (__popcll(hm) == 1) ee = (uint32_t)__builtin_amdgcn_readlane((int)mye, __ffsll((unsigned long long)hm) - 1);
-        else ee = wave_minmax_u32<false>(hold ? mye : 0xffffffffu);
+        for (int r = 0; r < c.topk; r++) {
+          // this lane's best remaining expert (strict > keeps the lower index on ties)
+          uint64_t b = ks[0];
+          uint32_t bi = 0u;
 #pragma unroll
-        for (int i = 0; i < RT_SLOTS; i++) ks[i] = (mye == ee && bi == (uint32_t)i) ? 0ull : ks[i];
-        if (lane == 0) L.isel[r] = (int)ee;
-      }
+          for (int i = 1; i < NS; i++) {
+            const bool gt = ks[i] > b;
+            b = gt ? ks[i] : b;
+            bi = gt ? (uint32_t)i : bi;
+          }
+          // wave-wide largest key (DPP moves; a lane keeps its own value where a move
+          // does not write it)
+          uint64_t m = b;
+          auto step = [&](auto ctrl_tag) {
+            constexpr int CTRL = decltype(ctrl_tag)::value >> 4, RM = decltype(ctrl_tag)::value & 0xf;
+            const uint64_t o = ((uint64_t)dpp_keep_u32<CTRL, RM>((uint32_t)(m >> 32)) << 32) |
+                               dpp_keep_u32<CTRL, RM>((uint32_t)m);
+            m = o > m ? o : m;
+          };
+          step(std::integral_constant<int, (0xB1 << 4) | 0xf>{});
+          step(std::integral_constant<int, (0x4E << 4) | 0xf>{});
+          step(std::integral_constant<int, (0x141 << 4) | 0xf>{});
+          step(std::integral_constant<int, (0x140 << 4) | 0xf>{});
+          step(std::integral_constant<int, (0x142 << 4) | 0xa>{});
+          step(std::integral_constant<int, (0x143 << 4) | 0xc>{});
+          const uint64_t K = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(m >> 32), 63) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)m, 63);
+          // the expert: the lowest index among the lanes holding that key
+          const uint32_t mye = (uint32_t)lane + 64u * bi;
+          const bool hold = b == K;
+          const uint64_t hm = __ballot(hold);
+          uint32_t ee;
+          if (__popcll(hm) == 1) ee = (uint32_t)__builtin_amdgcn_readlane((int)mye, __ffsll((unsigned long long)hm) - 1);
+          else ee = wave_minmax_u32<false>(hold ? mye : 0xffffffffu);
+#pragma unroll
+          for (int i = 0; i < NS; i++) ks[i] = (mye == ee && bi == (uint32_t)i) ? 0ull : ks[i];
+          if (lane == 0) L.isel[r] = (int)ee;
+        }
+      };
+      if (c.E <= 256) select(std::integral_constant<int, 4>{});
+      else select(std::integral_constant<int, RT_SLOTS>{});
     }
     __syncthreads();
     stamp(a, cx, st, TR_TOPK);
