@@ -415,6 +415,18 @@ __device__ __forceinline__ void coh_copy_to_lds(uint32_t* dst, const uint32_t* s
 // Output handling of a GEMV: out[r - r0] = v (store) or out[r - r0] += alpha * v.
 enum OutMode { OUT_STORE = 0, OUT_ACCUM = 1 };
 
+// Activation vectors that an FP8 gemv_list reads are stored padded in LDS: element e at
+// float e + 4 * (e / 64). A lane reads its 16 consecutive elements (64 bytes) as float4s;
+// unpadded, the spans of 16 neighbouring lanes start on only four distinct 4-bank groups
+// of the 64 banks, a 4-way conflict on every activation read (measured: 186 M conflict
+// cycles per 8-layer step of the FP8 MLA layer, 21 M padded). With four spare floats after
+// every 64 they start on 16 distinct groups. A 16-element chunk never crosses a 64-element
+// block, so it stays contiguous. Vectors of length n take apad<true>(n) floats (n a
+// multiple of 64). bf16 GEMVs (32-byte spans) measured no conflicts unpadded and keep the
+// plain layout (PAD = false: the identity).
+template <bool PAD>
+__host__ __device__ constexpr int apad(int e) { return PAD ? e + ((e >> 6) << 2) : e; }
+
 // Lane layout per reduction length K (elements) and weight format, fixed at compile time:
 // LPR lanes per row, CPL 16-byte chunks per lane and row, U rows in flight per wave
 // (U*CPL ~ INFL loads of 16 bytes per lane: INFL * 8 KB in flight per 512-thread workgroup).
@@ -434,6 +446,8 @@ struct GemvLayout {
 // consecutive rows starting at w (row stride K elements), FP8 scales s (row-block
 // stride ceil(K/128)) with row offset srow, reads the activation at act + act_off, and
 // scales its row results by alpha (OUT_ACCUM). Results land in out[] in list order.
+// Activations are in the layout apad<FP8>, and act_off is an offset in that layout (the
+// apad of a multiple of 64 elements).
 struct RowSeg {
   const uint8_t* w;
   const float* s;
@@ -460,6 +474,7 @@ template <bool FP8, int K, int INFL, bool ACC64 = false, typename Pre>
 __device__ __forceinline__ bool gemv_list(const RowSeg* segs, int nseg, const float* act, float* out, int mode,
                                           Pre&& pre) {
   static_assert(!(ACC64 && FP8), "fp64 accumulation is for bf16 weights");
+  static_assert(!FP8 || K % 64 == 0, "whole 64-element blocks of the padded activation layout");
   using AccT = typename std::conditional<ACC64, double, float>::type;
   using LY = GemvLayout<FP8, K, INFL>;
   constexpr int EPC = LY::EPC, LPR = LY::LPR, CPL = LY::CPL, U = LY::U;
@@ -531,7 +546,7 @@ __device__ __forceinline__ bool gemv_list(const RowSeg* segs, int nseg, const fl
 #pragma unroll
       for (int j = 0; j < CPL; j++) {
         float at[EPC];
-        const float4* ap = reinterpret_cast<const float4*>(a + (j * LPR + li) * EPC);
+        const float4* ap = reinterpret_cast<const float4*>(a + apad<FP8>((j * LPR + li) * EPC));
 #pragma unroll
         for (int q = 0; q < EPC / 4; q++) {
           const float4 t = ap[q];

@@ -160,6 +160,11 @@ struct IdxLinear {
 struct StU32 {
   __device__ __forceinline__ void operator()(uint32_t* dst, int i, uint32_t v) const { dst[i] = v; }
 };
+// Word i of an activation vector into the layout apad<PAD> that gemv_list reads.
+template <bool PAD>
+struct StPad {
+  __device__ __forceinline__ void operator()(uint32_t* dst, int i, uint32_t v) const { dst[apad<PAD>(i)] = v; }
+};
 
 // Reads the LL words src[idx(i)], i in [0, n), of epoch ep into dst[i] (LDS). PER loads
 // per thread are issued together; words that are not yet published are re-read in a
@@ -255,22 +260,23 @@ struct RegVec {
     }
   }
 };
-// In-place RMSNorm of act[0..N): act = fp32((act * r) * gamma), r = 1/sqrt(sum(act^2)/N + eps),
-// statistics in fp64 (bf16 and fp32 squares are exact in fp64); gamma in registers.
-template <int N>
+// In-place RMSNorm of the activation vector act (N elements, element i at act[apad<PAD>(i)]):
+// act = fp32((act * r) * gamma), r = 1/sqrt(sum(act^2)/N + eps), statistics in fp64 (bf16
+// and fp32 squares are exact in fp64); gamma in registers.
+template <int N, bool PAD>
 __device__ __forceinline__ void rmsnorm_reg(float* act, const RegVec<N>& gam, double eps, double* red) {
   double ss = 0.0;
 #pragma unroll
   for (int k = 0; k < RegVec<N>::K; k++) {
     const int i = tid_opaque() + k * BLOCK;
-    if (N % BLOCK == 0 || i < N) ss += (double)act[i] * (double)act[i];
+    if (N % BLOCK == 0 || i < N) ss += (double)act[apad<PAD>(i)] * (double)act[apad<PAD>(i)];
   }
   ss = block_sum(ss, red);
   const double r = 1.0 / sqrt(ss / (double)N + eps);
 #pragma unroll
   for (int k = 0; k < RegVec<N>::K; k++) {
     const int i = tid_opaque() + k * BLOCK;
-    if (N % BLOCK == 0 || i < N) act[i] = (float)(((double)act[i] * r) * (double)gam.v[k]);
+    if (N % BLOCK == 0 || i < N) act[apad<PAD>(i)] = (float)(((double)act[apad<PAD>(i)] * r) * (double)gam.v[k]);
   }
   __syncthreads();
 }
@@ -406,9 +412,9 @@ __device__ __forceinline__ void hrows(int H, int nwg, int w, int* r0, int* r1) {
 
 // The layer input of a step: an embedding row (first layer of a token with a head), the
 // caller's bf16 vector (first step of the launch) or the previous step's output (LL
-// words of bf16 pairs, previous epoch); expanded to fp32 in
-// L.act, this workgroup's residual rows [h0, h1) kept in L.xres, then RMSNorm in place.
-template <int H>
+// words of bf16 pairs, previous epoch); expanded to fp32 in L.act (layout apad<PAD>),
+// this workgroup's residual rows [h0, h1) kept in L.xres, then RMSNorm in place.
+template <int H, bool PAD>
 __device__ __forceinline__ bool layer_input(Ctx& cx, const KArgs& a, const Step& st, Lds& L, const RegVec<H>& gam,
                                             int h0, int h1) {
   if (st.emb_row || st.first) {
@@ -424,15 +430,15 @@ __device__ __forceinline__ bool layer_input(Ctx& cx, const KArgs& a, const Step&
     const int i = tid_opaque() + k * BLOCK;
     if ((H / 2) % BLOCK == 0 || i < H / 2) {
       const uint32_t v = L.stage[i];
-      reinterpret_cast<float2*>(L.act)[i] = make_float2(bf_lo(v), bf_hi(v));
+      *reinterpret_cast<float2*>(L.act + apad<PAD>(2 * i)) = make_float2(bf_lo(v), bf_hi(v));
     }
   }
   __syncthreads();
-  for (int r = h0 + tid_opaque(); r < h1; r += BLOCK) L.xres[r - h0] = L.act[r];
-  rmsnorm_reg<H>(L.act, gam, a.c.eps, L.red);
+  for (int r = h0 + tid_opaque(); r < h1; r += BLOCK) L.xres[r - h0] = L.act[apad<PAD>(r)];
+  rmsnorm_reg<H, PAD>(L.act, gam, a.c.eps, L.red);
   stamp(a, cx, st, TR_X_NORMED);
   if (cx.w == 0)
-    for (int i = tid_opaque(); i < H; i += BLOCK) st_f32(wsp<float>(a, a.off.a_dbg) + i, L.act[i]);
+    for (int i = tid_opaque(); i < H; i += BLOCK) st_f32(wsp<float>(a, a.off.a_dbg) + i, L.act[apad<PAD>(i)]);
   return true;
 }
 
@@ -455,7 +461,7 @@ __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Ste
   auto pre_x = [&]() -> bool {
     if (!pending) return true;
     pending = false;
-    return layer_input<SH::H>(cx, a, st, L, gam, h0, h1);
+    return layer_input<SH::H, SH::FP8>(cx, a, st, L, gam, h0, h1);
   };
   {
     // one pipelined pass over this workgroup's rows of [W_q; W_k; W_v]
@@ -839,7 +845,7 @@ __device__ __forceinline__ bool stage_wo(Ctx& cx, const KArgs& a, const Step& st
   hrows(SH::H, cx.nwg, cx.w, &r0, &r1);
   auto pre_o = [&]() -> bool {
     if (!ll_fetch<per_for(SH::ODIM)>(cx, reinterpret_cast<uint32_t*>(L.act), wsp<uint64_t>(a, a.off.o), SH::ODIM,
-                                     st.k1, W_O))
+                                     st.k1, W_O, IdxLinear{}, StPad<SH::FP8>{}))
       return false;
     stamp(a, cx, st, TR_O_READY);
     return true;
@@ -922,12 +928,13 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
   auto pre_b = [&]() -> bool {
     if (!pending) return true;
     pending = false;
-    if (!ll_fetch<per_for(SH::H)>(cx, reinterpret_cast<uint32_t*>(L.act), wsp<uint64_t>(a, a.off.h2), SH::H, k1, W_H2))
+    if (!ll_fetch<per_for(SH::H)>(cx, reinterpret_cast<uint32_t*>(L.act), wsp<uint64_t>(a, a.off.h2), SH::H, k1, W_H2,
+                                  IdxLinear{}, StPad<SH::FP8>{}))
       return false;
     stamp(a, cx, st, TR_H2_READY);
-    rmsnorm_reg<SH::H>(L.act, gam, c.eps, L.red);
+    rmsnorm_reg<SH::H, SH::FP8>(L.act, gam, c.eps, L.red);
     if (w == 0)
-      for (int i = tid_opaque(); i < SH::H; i += BLOCK) st_f32(wsp<float>(a, a.off.b_dbg) + i, L.act[i]);
+      for (int i = tid_opaque(); i < SH::H; i += BLOCK) st_f32(wsp<float>(a, a.off.b_dbg) + i, L.act[apad<SH::FP8>(i)]);
     if constexpr (SH::MOE) {
       if (w < c.E) {
         // logit of expert w (fp64 accumulation) and its selection key: the logit itself
@@ -937,7 +944,7 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
 #pragma unroll
         for (int k = 0; k < RPT; k++) {
           const int q = tid_opaque() + k * BLOCK;
-          if (q < RCH) s += dot8_bf16_f64(rrow[k], L.act + q * 8);
+          if (q < RCH) s += dot8_bf16_f64(rrow[k], L.act + apad<SH::FP8>(q * 8));
         }
         s = block_sum(s, L.red);
         if (tid_opaque() < 4) {
@@ -1118,7 +1125,7 @@ __device__ __forceinline__ bool stage_down(Ctx& cx, const KArgs& a, const Step& 
     if (!pending) return true;
     pending = false;
     if (!ll_fetch<per_for(SH::INTER * MAX_SEGS)>(cx, reinterpret_cast<uint32_t*>(L.act), wsp<uint64_t>(a, a.off.m),
-                                                  c.slots * SH::INTER, st.k1, W_M))
+                                                  c.slots * SH::INTER, st.k1, W_M, IdxLinear{}, StPad<SH::FP8>{}))
       return false;
     stamp(a, cx, st, TR_M_READY);
     return true;
@@ -1131,7 +1138,7 @@ __device__ __forceinline__ bool stage_down(Ctx& cx, const KArgs& a, const Step& 
       const int expert = !SH::MOE ? 0 : (s < c.topk ? L.isel[s] : c.E + (s - c.topk));
       const size_t bo = (size_t)expert * Ly.dn_slot_bytes + (size_t)r0 * RB;
       const float* sd = SH::FP8 ? Ly.w_down.s + (size_t)expert * Ly.dn_slot_scales : nullptr;
-      seg_set(L, s, Ly.w_down.w + bo, sd, r1 - r0, r0, s * SH::INTER, 1.f);
+      seg_set(L, s, Ly.w_down.w + bo, sd, r1 - r0, r0, apad<SH::FP8>(s * SH::INTER), 1.f);
     }
     seg_end();
     if (!gemv_list<SH::FP8, SH::INTER, PLD_IF_DOWN>(L.segs, r1 > r0 ? c.slots : 0, L.act, L.outb, OUT_STORE, pre_m))
@@ -1487,7 +1494,10 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
     const int R = (c->n_heads + 2 * c->n_kv_heads) * c->head_dim;
     // attention: q [G*HD] + new k/v row [HD] + scores [G*chmax] + wave sums [8*G*HD] + (m, l);
     // merge staging: at most G*HD/cpg + 1 dims of cpg chunks, (m, l) and weights of two heads
-    int act = std::max({c->hidden, c->n_heads * c->head_dim, k->slots * c->inter,
+    // (the GEMV inputs in their LDS layout: padded for FP8 weights)
+    const bool pad = c->wfmt == PLD_WFMT_FP8_BLOCK128;
+    auto ap = [pad](int n) { return pad ? apad<true>(n) : n; };
+    int act = std::max({ap(c->hidden), ap(c->n_heads * c->head_dim), ap(k->slots * c->inter),
                         2 * k->G * c->head_dim + c->head_dim + k->G * k->chmax + NWAVES * k->G * c->head_dim + 2 * k->G + 8,
                         k->cpg * (k->G * c->head_dim / k->cpg + 1) + 8 * k->cpg + 8});
     k->act_floats = (int)al(act, 64);
@@ -1522,7 +1532,11 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
     const int attn_bytes = 2 * 16 * CSTR + 2 * 2 * TB * CSTR + 2 * 16 * TB + 4 * (8 * 256 + 16) + 2 * LAT + 4 * LAT +
                            4 * srows_max;
     const int nope_rows = std::min(c->nope_dim, 4 * (BLOCK / (k->cpw / epc)));
-    int act = std::max({c->hidden, c->q_lora, k->slots * c->inter, (attn_bytes + 3) / 4 + 16,
+    // (the GEMV inputs in their LDS layout: padded for FP8 weights)
+    const bool pad = c->wfmt == PLD_WFMT_FP8_BLOCK128;
+    auto ap = [pad](int n) { return pad ? apad<true>(n) : n; };
+    int act = std::max({ap(c->hidden), ap(c->q_lora), ap(k->slots * c->inter), ap(NH * VD), ap(KL),
+                        (attn_bytes + 3) / 4 + 16,
                         c->nope_dim + (BLOCK / (k->cpw / epc)) * k->cpw + nope_rows,
                         k->cpg * k->cpw + 3 * k->cpg + 8 + BLOCK});
     if (sparse) {
@@ -1535,7 +1549,7 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
         return PLD_E_UNSUPPORTED;
       const int idx_words = 2 * (c->index_heads * c->index_dim + c->index_heads) + 2 * SEL_LKMAX + SEL_LIST +
                             c->index_heads * c->index_dim / 2 + c->index_heads + c->index_dim + c->index_dim / 4 + 3;
-      act = std::max({act, 3 * c->q_lora, SEL_LDS_WORDS, idx_words});
+      act = std::max({act, ap(c->q_lora) + 2 * c->q_lora, SEL_LDS_WORDS, idx_words});
       if (c->q_lora + LAT + c->index_heads + c->index_dim < nwg) return PLD_E_UNSUPPORTED;
     }
     k->act_floats = (int)al(act, 64);

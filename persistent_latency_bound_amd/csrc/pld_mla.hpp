@@ -61,7 +61,7 @@ __device__ __forceinline__ bool stage_x_mla(Ctx& cx, const KArgs& a, const Step&
   auto pre_x = [&]() -> bool {
     if (!pending) return true;
     pending = false;
-    return layer_input<SH::H>(cx, a, st, L, gam, h0, h1);
+    return layer_input<SH::H, SH::FP8>(cx, a, st, L, gam, h0, h1);
   };
   {
     constexpr int NM = SH::SPARSE ? 4 : 2;
@@ -107,9 +107,10 @@ __device__ __forceinline__ bool stage_x_mla(Ctx& cx, const KArgs& a, const Step&
   return true;
 }
 
-// RMSNorm of an fp64 vector held as (lo, hi) 32-bit word pairs in LDS, written as fp32:
-// dst[i] = fp32((x_i * r) * gamma_i), r = 1/sqrt(sum(x^2)/N + eps), all in fp64.
-template <int N>
+// RMSNorm of an fp64 vector held as (lo, hi) 32-bit word pairs in LDS, written as fp32 into
+// the activation layout apad<PAD>: dst[apad<PAD>(i)] = fp32((x_i * r) * gamma_i),
+// r = 1/sqrt(sum(x^2)/N + eps), all in fp64.
+template <int N, bool PAD>
 __device__ __forceinline__ void rmsnorm_f64src(float* dst, const uint32_t* src, const RegVec<N>& gam, double eps,
                                                double* red) {
   auto x_at = [&](int i) -> double {
@@ -129,7 +130,7 @@ __device__ __forceinline__ void rmsnorm_f64src(float* dst, const uint32_t* src, 
 #pragma unroll
   for (int k = 0; k < RegVec<N>::K; k++) {
     const int i = tid_opaque() + k * BLOCK;
-    if (N % BLOCK == 0 || i < N) dst[i] = (float)((x_at(i) * r) * (double)gam.v[k]);
+    if (N % BLOCK == 0 || i < N) dst[apad<PAD>(i)] = (float)((x_at(i) * r) * (double)gam.v[k]);
   }
   __syncthreads();
 }
@@ -156,14 +157,14 @@ __device__ __forceinline__ bool stage_q_mla(Ctx& cx, const KArgs& a, const Step&
     if (!pending) return true;
     pending = false;
     if constexpr (SH::SPARSE) {
-      uint32_t* raw = reinterpret_cast<uint32_t*>(L.act + SH::QL);   // [2*QL] fp64 words
+      uint32_t* raw = reinterpret_cast<uint32_t*>(L.act + apad<SH::FP8>(SH::QL));   // [2*QL] fp64 words
       if (!ll_fetch<per_for(2 * SH::QL)>(cx, raw, wsp<uint64_t>(a, a.off.cqr), 2 * SH::QL, st.k1, W_CQ)) return false;
-      rmsnorm_f64src<SH::QL>(L.act, raw, gq, c.eps, L.red);
+      rmsnorm_f64src<SH::QL, SH::FP8>(L.act, raw, gq, c.eps, L.red);
     } else {
       if (!ll_fetch<per_for(SH::QL)>(cx, reinterpret_cast<uint32_t*>(L.act), wsp<uint64_t>(a, a.off.cqr), SH::QL,
-                                     st.k1, W_CQ))
+                                     st.k1, W_CQ, IdxLinear{}, StPad<SH::FP8>{}))
         return false;
-      rmsnorm_reg<SH::QL>(L.act, gq, c.eps, L.red);
+      rmsnorm_reg<SH::QL, SH::FP8>(L.act, gq, c.eps, L.red);
     }
     stamp(a, cx, st, TR_CQ_READY);
     return true;
@@ -1491,7 +1492,8 @@ __device__ __forceinline__ bool stage_uv_mla(Ctx& cx, const KArgs& a, const Step
     if (!pending) return true;
     pending = false;
     if (!ll_fetch<per_for(SH::KL)>(cx, reinterpret_cast<uint32_t*>(L.act),
-                                   wsp<uint64_t>(a, a.off.olat) + (size_t)h * SH::KL, SH::KL, st.k1, W_OLAT))
+                                   wsp<uint64_t>(a, a.off.olat) + (size_t)h * SH::KL, SH::KL, st.k1, W_OLAT,
+                                   IdxLinear{}, StPad<SH::FP8>{}))
       return false;
     return true;
   };
