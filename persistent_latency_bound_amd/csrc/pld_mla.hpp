@@ -1559,11 +1559,21 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_mla(KArgs a) {
       if constexpr (SH::SPARSE) {
         if (!stage_idx_mla<SH>(cs, as, st, L)) return;
       }
-      // the absorbed queries before the selection: the selecting workgroup's share of
-      // them then runs while it waits for the scorers' lists
-      if (!stage_absorb_mla<SH>(cs, as, st, L)) return;
       if constexpr (SH::SPARSE) {
+        // the selecting workgroup goes straight from its scores to the selection (it is the
+        // critical path: every attention workgroup waits for it); its share of the absorbed
+        // queries is done by the last workgroup after that one's own share
+        const int nabs = cs.w == SEL_WG ? 0 : (cs.w == cs.nwg - 1 ? 2 : 1);
+        for (int pass = 0; pass < nabs; pass++) {
+          Ctx ca = cs;
+          int wsel = SEL_WG;
+          asm volatile("" : "+s"(wsel));
+          ca.w = pass == 0 ? cs.w : wsel;
+          if (!stage_absorb_mla<SH>(ca, as, st, L)) return;
+        }
         if (!stage_sel_mla<SH>(cs, as, st, L)) return;
+      } else {
+        if (!stage_absorb_mla<SH>(cs, as, st, L)) return;
       }
       if (!stage_attn_mla<SH>(cs, as, st, L)) return;
       if (!stage_merge_mla<SH>(cs, as, st, L)) return;
