@@ -226,6 +226,7 @@ def run_stack(args):
                                  "median_us": round(float(np.median(v[v > 0] - st0)), 2)})
         with open(args.trace, "w") as f:
             json.dump({"steps": nst, "stamps": rows}, f, indent=0)
+        np.save(os.path.splitext(args.trace)[0] + "_raw.npy", t)   # [step][workgroup][slot] us
     print(json.dumps(line), flush=True)
 
 

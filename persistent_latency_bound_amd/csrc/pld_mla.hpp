@@ -1138,19 +1138,23 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
   const int pidx = SH::SPARSE ? ((ch == nch - 1 && n > 0 && srows[n - 1] == pos) ? n - 1 : -1) : -1;
   const bool newrow_here = ch == nch - 1;
   // Staging registers: three sub-blocks in flight (sets A, B, C in turn); chunk i of a
-  // block covers (row i / CPRW, chunk i % CPRW). A block's loads are issued three blocks
+  // block covers (row i / CPRW, chunk i % CPRW). A block's loads are issued DEPTH blocks
   // before it is staged into LDS, so the wait at staging time covers ~3 blocks of work.
-  // Rows are streamed through register sets A, B, C in turn: a block's loads are issued
-  // DEPTH blocks before it is staged into LDS. All loads are unconditional (clamped rows;
-  // blocks past the chunk read one uniform address and are masked), and a chunk that holds
-  // rows written inside this launch reads all its rows coherently (the two load kinds are
-  // separate template instances), so the in-order load waits stay exact. The row of
-  // position pos is patched in from LDS after staging.
+  // All loads are unconditional (clamped rows; blocks past the chunk read one uniform
+  // address and are masked), so the in-order load waits stay exact. A sub-block that holds
+  // rows written inside this launch reads its rows coherently; every other sub-block (in
+  // particular the static rows of the same chunk) reads through L2, where the head groups
+  // of a chunk share them. Both kinds issue the same number of loads into the same
+  // registers. The row of position pos is patched in from LDS after staging.
   constexpr int DEPTH = 3;
   const int nsb = (n + TB - 1) / TB;
-  const bool coh = SH::SPARSE ? (n > 0 && srows[n - 1] >= fresh) : (n > 0 && t0 + n > fresh);
+  auto fresh_block = [&](int sb) -> bool {   // does sub-block sb hold a row written in this launch?
+    const int last = min(sb * TB + TB, n) - 1;
+    if (last < 0) return false;
+    return SH::SPARSE ? srows[last] >= fresh : t0 + last >= fresh;
+  };
   uint4 cb[DEPTH][NLD];
-  auto issue = [&](int set, int sb, auto coh_tag) {
+  auto issue_k = [&](int set, int sb, auto coh_tag) {
     constexpr bool COH = decltype(coh_tag)::value;
     const bool live = sb < nsb;
 #pragma unroll
@@ -1162,6 +1166,10 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
       const uint16_t* p = live ? lat + row * LAT + k * 8 : lat;
       cb[set][i] = COH ? ld_coh16(p) : ld_g16(p);
     }
+  };
+  auto issue = [&](int set, int sb) {
+    if (sb < nsb && fresh_block(sb)) issue_k(set, sb, std::true_type{});
+    else issue_k(set, sb, std::false_type{});
   };
   // registers -> LDS, then the row of pos from LDS (DS operations only)
   auto store = [&](int set, int sb, int buf) {
@@ -1182,13 +1190,8 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
         reinterpret_cast<uint32_t*>(C + rp * CSTR)[k] = reinterpret_cast<const uint32_t*>(newrow)[k];
     }
   };
-  if (coh) {
 #pragma unroll
-    for (int d = 0; d < DEPTH; d++) issue(d, d, std::true_type{});
-  } else {
-#pragma unroll
-    for (int d = 0; d < DEPTH; d++) issue(d, d, std::false_type{});
-  }
+  for (int d = 0; d < DEPTH; d++) issue(d, d);
   // the row of position pos: RMSNorm(c_kv') and RoPE(k_r'), bf16 (before the queries: its
   // input was published by the X stage, so this runs while the absorbed queries are produced)
   if (newrow_here) {
@@ -1311,7 +1314,7 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
   };
   // (only the chunk's own sub-blocks are computed; the loads of the sets past the last
   // one read a uniform address and are never staged)
-  auto main_loop = [&](auto coh_tag) {
+  {
     for (int sb0 = 0; sb0 < nsb; sb0 += DEPTH) {
 #pragma unroll
       for (int d = 0; d < DEPTH; d++) {
@@ -1322,14 +1325,12 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
         store(d, sb, buf);
         __syncthreads();
         if (sb == 0) stamp(a, cx, st, 17);
-        issue(d, sb + DEPTH, coh_tag);   // refill this set, DEPTH blocks ahead
+        issue(d, sb + DEPTH);   // refill this set, DEPTH blocks ahead
         block(C, tb0);
         if (sb == 0) stamp(a, cx, st, 31);
       }
     }
-  };
-  if (coh) main_loop(std::true_type{});
-  else main_loop(std::false_type{});
+  }
   if constexpr (!SH::SPARSE) {
     // dense: the row of position pos joins the last chunk's online softmax here, on the
     // vector ALU (as a sub-block of its own it would cost a whole block for one row)
