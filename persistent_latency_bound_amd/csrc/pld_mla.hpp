@@ -1124,7 +1124,28 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
   uint16_t* newrow = reinterpret_cast<uint16_t*>(alph + 16);   // [LAT] the row of position pos
   float* ntmp = reinterpret_cast<float*>(newrow + LAT);  // [LAT] its fp32 raw values
   int* srows = reinterpret_cast<int*>(ntmp + LAT);        // sparse: [n] rows of this chunk
+  // q of the head group: q_lat [HPW][KL] and q_rope [HPW][RD] as bf16 pairs (LL) -> rows of Qs
+  auto fetch_q = [&]() -> bool {
+    uint32_t* qw = reinterpret_cast<uint32_t*>(qtmp);   // [HPW][KL/2] then [HPW][RD/2] words
+    if (!ll_fetch<per_for(HPW * KL / 2)>(cx, qw, wsp<uint64_t>(a, a.off.qlat) + (size_t)hbase * KL / 2, HPW * KL / 2,
+                                         k1, W_QLAT))
+      return false;
+    if (!ll_fetch<per_for(HPW * RD / 2)>(cx, qw + HPW * KL / 2, wsp<uint64_t>(a, a.off.qr) + (size_t)hbase * RD / 2,
+                                         HPW * RD / 2, k1, W_QLAT))
+      return false;
+    static_assert(CSTR % 2 == 0, "Qs rows hold whole bf16 pairs");
+    for (int i = tid; i < 16 * LAT / 2; i += BLOCK) {
+      const int h = i / (LAT / 2), k2 = i % (LAT / 2);
+      const uint32_t v = h >= HPW ? 0u : (k2 < KL / 2 ? qw[h * (KL / 2) + k2] : qw[HPW * KL / 2 + h * (RD / 2) + (k2 - KL / 2)]);
+      reinterpret_cast<uint32_t*>(Qs + h * CSTR)[k2] = v;
+    }
+    return true;
+  };
   if constexpr (SH::SPARSE) {
+    // the queries were ready long before the selection: fetched first, so that only the
+    // selected rows' loads remain once the selection arrives (dense: fetched after the
+    // first latent rows are issued, overlapping their latency)
+    if (!fetch_q()) return false;
     if (n > 0 && !ll_fetch<1>(cx, reinterpret_cast<uint32_t*>(srows), wsp<uint64_t>(a, a.off.isel) + t0, n, k1,
                               W_ISEL))
       return false;
@@ -1220,21 +1241,8 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
       if (hg == 0) st_u32(reinterpret_cast<uint32_t*>(Ly.lat + (size_t)pos * LAT) + i, pair);   // cache append
     }
   }
-  // q of the head group: q_lat [HPW][KL] and q_rope [HPW][RD] as bf16 pairs (LL) -> rows of Qs
-  {
-    uint32_t* qw = reinterpret_cast<uint32_t*>(qtmp);   // [HPW][KL/2] then [HPW][RD/2] words
-    if (!ll_fetch<per_for(HPW * KL / 2)>(cx, qw, wsp<uint64_t>(a, a.off.qlat) + (size_t)hbase * KL / 2, HPW * KL / 2,
-                                         k1, W_QLAT))
-      return false;
-    if (!ll_fetch<per_for(HPW * RD / 2)>(cx, qw + HPW * KL / 2, wsp<uint64_t>(a, a.off.qr) + (size_t)hbase * RD / 2,
-                                         HPW * RD / 2, k1, W_QLAT))
-      return false;
-    static_assert(CSTR % 2 == 0, "Qs rows hold whole bf16 pairs");
-    for (int i = tid; i < 16 * LAT / 2; i += BLOCK) {
-      const int h = i / (LAT / 2), k2 = i % (LAT / 2);
-      const uint32_t v = h >= HPW ? 0u : (k2 < KL / 2 ? qw[h * (KL / 2) + k2] : qw[HPW * KL / 2 + h * (RD / 2) + (k2 - KL / 2)]);
-      reinterpret_cast<uint32_t*>(Qs + h * CSTR)[k2] = v;
-    }
+  if constexpr (!SH::SPARSE) {
+    if (!fetch_q()) return false;
   }
   for (int i = tid; i < 16 * TB; i += BLOCK) Ps[i] = 0;
   __syncthreads();
