@@ -29,7 +29,6 @@ namespace pld {
 constexpr int BLOCK = 512;
 constexpr int NWAVES = BLOCK / 64;
 constexpr int NXCD = 8;
-constexpr int CTR_STRIDE = 64;       // uint32 words between counters (256 B)
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -86,14 +85,6 @@ __device__ __forceinline__ uint32_t ld_u32(const uint32_t* p) {
 }
 __device__ __forceinline__ void st_f32(float* p, float v) { st_u32(reinterpret_cast<uint32_t*>(p), __float_as_uint(v)); }
 __device__ __forceinline__ float ld_f32(const float* p) { return __uint_as_float(ld_u32(reinterpret_cast<const uint32_t*>(p))); }
-__device__ __forceinline__ void st_f64(double* p, double v) {
-  __hip_atomic_store(gp(reinterpret_cast<uint64_t*>(p)), (uint64_t)__double_as_longlong(v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ double ld_f64(const double* p) {
-  return __longlong_as_double((long long)__hip_atomic_load(gp(reinterpret_cast<uint64_t*>(const_cast<double*>(p))),
-                                                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-}
 __device__ __forceinline__ uint64_t ld_u64(const uint64_t* p) {
   return __hip_atomic_load(gp(const_cast<uint64_t*>(p)), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -110,13 +101,6 @@ __device__ __forceinline__ uint64_t ld_u64_off(const void* base, uint32_t byte_o
 __device__ __forceinline__ uint32_t ld_u32_off(const void* base, uint32_t byte_off) {
   const PLD_GLOBAL char* b = gp(reinterpret_cast<const char*>(base));
   return __hip_atomic_load((PLD_GLOBAL uint32_t*)(b + byte_off), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_u64_off(void* base, uint32_t byte_off, uint64_t v) {
-  PLD_GLOBAL char* b = gp(reinterpret_cast<char*>(base));
-  __hip_atomic_store((PLD_GLOBAL uint64_t*)(b + byte_off), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t atomic_add_u32(uint32_t* p, uint32_t v) {
-  return __hip_atomic_fetch_add(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ----------------------------------------------------------------- number formats
@@ -169,12 +153,6 @@ __device__ __forceinline__ uint32_t e4m3_encode(float q) {
 }
 
 // ----------------------------------------------------------------- reductions
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
 #pragma unroll
@@ -385,32 +363,6 @@ struct DMat {
   const float* s;      // FP8 scales [ceil(rows/128)][sbk]
   int rows, cols, sbk; // sbk = ceil(cols/128)
 };
-
-// Copies n 32-bit words of cross-workgroup data (written with write-through stores by
-// other workgroups) into LDS. Each thread issues PER independent 8-byte agent-scope
-// loads before using any of them, so the copy costs about one device-coherence-point
-// latency per PER*BLOCK*2 words instead of one per word. n must be even, src 8-aligned.
-template <int PER = 8>
-__device__ __forceinline__ void coh_copy_to_lds(uint32_t* dst, const uint32_t* src, int n) {
-  const uint64_t* s = reinterpret_cast<const uint64_t*>(src);
-  const int n2 = n >> 1;
-  for (int base = 0; base < n2; base += BLOCK * PER) {
-    uint64_t v[PER];
-#pragma unroll
-    for (int j = 0; j < PER; j++) {
-      const int i = base + j * BLOCK + tid_opaque();
-      v[j] = i < n2 ? ld_u64(s + i) : 0ull;
-    }
-#pragma unroll
-    for (int j = 0; j < PER; j++) {
-      const int i = base + j * BLOCK + tid_opaque();
-      if (i < n2) {
-        dst[2 * i] = (uint32_t)v[j];
-        dst[2 * i + 1] = (uint32_t)(v[j] >> 32);
-      }
-    }
-  }
-}
 
 // Output handling of a GEMV: out[r - r0] = v (store) or out[r - r0] += alpha * v.
 enum OutMode { OUT_STORE = 0, OUT_ACCUM = 1 };
