@@ -1531,13 +1531,12 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
     const int srows_max = sparse ? (std::min(c->index_topk, c->max_seq) + k->cpg - 1) / k->cpg : 0;
     const int attn_bytes = 2 * 16 * CSTR + 2 * 2 * TB * CSTR + 2 * 16 * TB + 4 * (8 * 256 + 16) + 2 * LAT + 4 * LAT +
                            4 * srows_max;
-    const int nope_rows = std::min(c->nope_dim, 4 * (BLOCK / (k->cpw / epc)));
     // (the GEMV inputs in their LDS layout: padded for FP8 weights)
     const bool pad = c->wfmt == PLD_WFMT_FP8_BLOCK128;
     auto ap = [pad](int n) { return pad ? apad<true>(n) : n; };
     int act = std::max({ap(c->hidden), ap(c->q_lora), ap(k->slots * c->inter), ap(NH * VD), ap(KL),
                         (attn_bytes + 3) / 4 + 16,
-                        c->nope_dim + (BLOCK / (k->cpw / epc)) * k->cpw + nope_rows,
+                        c->nope_dim + (BLOCK / (k->cpw / epc) + 1) * k->cpw + BLOCK,   // absorb: q_nope, partials, sums
                         k->cpg * k->cpw + 3 * k->cpg + 8 + BLOCK});
     if (sparse) {
       // indexer: 8 heads x 64 dims (4 lanes x 2 heads per token); selection: every scoring

@@ -1029,7 +1029,9 @@ __device__ __forceinline__ bool stage_absorb_mla(Ctx& cx, const KArgs& a, const 
     }
   }
   float* qv = L.act;                    // [ND] q_nope of head h
-  float* red = L.act + SH::ND;          // [rpp][cpw]
+  const int rs = rpp + 1;               // column stride of red (padded: spreads the stores over the banks)
+  float* red = L.act + SH::ND;          // [cpw][rs] per-thread partial sums, column-major
+  float* red2 = red + cpw * rs;         // [BLOCK / cpw][cpw] sums of row groups, then [cpw] totals
   if (!ll_fetch<per_for(SH::ND)>(cx, reinterpret_cast<uint32_t*>(qv), wsp<uint64_t>(a, a.off.q) + (size_t)h * SH::ND,
                                  SH::ND, st.k1, W_QN))
     return false;
@@ -1062,18 +1064,35 @@ __device__ __forceinline__ bool stage_absorb_mla(Ctx& cx, const KArgs& a, const 
     }
   }
 #pragma unroll
-  for (int e = 0; e < EPC; e++) red[rr * cpw + ck * EPC + e] = acc[e];
+  for (int e = 0; e < EPC; e++) red[(ck * EPC + e) * rs + rr] = acc[e];
   __syncthreads();
+  // column sums over the rpp row partials, all threads at once: thread t adds the rows
+  // [gq * rpg, (gq + 1) * rpg) of column t % cpw (four independent chains), then the
+  // BLOCK / cpw group sums of a column are added in group order
+  {
+    const int ng = BLOCK / cpw, rpg = rpp / ng;   // host: cpw divides BLOCK (so ng divides rpp)
+    const int j = tid % cpw, gq = tid / cpw;
+    const float* col = red + j * rs + gq * rpg;
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+    int g = 0;
+    for (; g + 4 <= rpg; g += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; u++) s4[u] += col[g + u];
+    }
+    for (; g < rpg; g++) s4[0] += col[g];
+    red2[gq * cpw + j] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+    __syncthreads();
+    float tot = 0.f;
+    if (tid < cpw)
+      for (int q = 0; q < ng; q++) tot += red2[q * cpw + tid];
+    __syncthreads();
+    if (tid < cpw) red2[tid] = tot;
+    __syncthreads();
+  }
   // q_lat as bf16 pairs: the attention's matrix cores take it in bf16 (same rounding)
   uint64_t* ql = wsp<uint64_t>(a, a.off.qlat) + ((size_t)h * SH::KL + c0) / 2;
-  for (int j = 2 * tid; j < cpw; j += 2 * BLOCK) {
-    float s0 = 0.f, s1 = 0.f;
-    for (int g = 0; g < rpp; g++) {
-      s0 += red[g * cpw + j];
-      s1 += red[g * cpw + j + 1];
-    }
-    ll_put(ql + j / 2, f32_to_bf16(s0) | (f32_to_bf16(s1) << 16), st.k1);
-  }
+  for (int j = 2 * tid; j < cpw; j += 2 * BLOCK)
+    ll_put(ql + j / 2, f32_to_bf16(red2[j]) | (f32_to_bf16(red2[j + 1]) << 16), st.k1);
   __syncthreads();
   stamp(a, cx, st, TR_ATT_SCORES);
   return true;
