@@ -263,20 +263,25 @@ struct RegVec {
 // In-place RMSNorm of the activation vector act (N elements, element i at act[apad<PAD>(i)]):
 // act = fp32((act * r) * gamma), r = 1/sqrt(sum(act^2)/N + eps), statistics in fp64 (bf16
 // and fp32 squares are exact in fp64); gamma in registers.
+// (The thread's elements stay in registers between the two passes: re-reading them from
+// LDS after writing earlier ones would serialize a full LDS round trip per element, since
+// the compiler cannot tell the computed indices apart.)
 template <int N, bool PAD>
 __device__ __forceinline__ void rmsnorm_reg(float* act, const RegVec<N>& gam, double eps, double* red) {
+  float xv[RegVec<N>::K];
   double ss = 0.0;
 #pragma unroll
   for (int k = 0; k < RegVec<N>::K; k++) {
     const int i = tid_opaque() + k * BLOCK;
-    if (N % BLOCK == 0 || i < N) ss += (double)act[apad<PAD>(i)] * (double)act[apad<PAD>(i)];
+    xv[k] = (N % BLOCK == 0 || i < N) ? act[apad<PAD>(i)] : 0.f;
+    ss += (double)xv[k] * (double)xv[k];
   }
   ss = block_sum(ss, red);
   const double r = 1.0 / sqrt(ss / (double)N + eps);
 #pragma unroll
   for (int k = 0; k < RegVec<N>::K; k++) {
     const int i = tid_opaque() + k * BLOCK;
-    if (N % BLOCK == 0 || i < N) act[apad<PAD>(i)] = (float)(((double)act[apad<PAD>(i)] * r) * (double)gam.v[k]);
+    if (N % BLOCK == 0 || i < N) act[apad<PAD>(i)] = (float)(((double)xv[k] * r) * (double)gam.v[k]);
   }
   __syncthreads();
 }

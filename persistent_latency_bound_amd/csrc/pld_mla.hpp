@@ -116,21 +116,20 @@ __device__ __forceinline__ void rmsnorm_f64src(float* dst, const uint32_t* src, 
   auto x_at = [&](int i) -> double {
     return __longlong_as_double((long long)(((uint64_t)src[2 * i + 1] << 32) | src[2 * i]));
   };
+  double xv[RegVec<N>::K];   // kept in registers between the passes (see rmsnorm_reg)
   double ss = 0.0;
 #pragma unroll
   for (int k = 0; k < RegVec<N>::K; k++) {
     const int i = tid_opaque() + k * BLOCK;
-    if (N % BLOCK == 0 || i < N) {
-      const double x = x_at(i);
-      ss += x * x;
-    }
+    xv[k] = (N % BLOCK == 0 || i < N) ? x_at(i) : 0.0;
+    ss += xv[k] * xv[k];
   }
   ss = block_sum(ss, red);
   const double r = 1.0 / sqrt(ss / (double)N + eps);
 #pragma unroll
   for (int k = 0; k < RegVec<N>::K; k++) {
     const int i = tid_opaque() + k * BLOCK;
-    if (N % BLOCK == 0 || i < N) dst[apad<PAD>(i)] = (float)((x_at(i) * r) * (double)gam.v[k]);
+    if (N % BLOCK == 0 || i < N) dst[apad<PAD>(i)] = (float)((xv[k] * r) * (double)gam.v[k]);
   }
   __syncthreads();
 }
