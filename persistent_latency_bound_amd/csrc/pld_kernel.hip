@@ -462,6 +462,18 @@ __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Ste
   hrows(SH::H, nwg, w, &h0, &h1);
   RegVec<SH::H> gam;
   gam.load(Ly.attn_norm);
+  // RoPE (cos, sin) of this thread's first output pair, loaded before the GEMV: after it,
+  // a global load would queue behind the GEMV's trailing weight loads
+  const PLD_GLOBAL float* rope = gp(wsp<float>(a, a.off.rope)) + (size_t)pos * HD;   // (cos, sin) pairs
+  float rcs = 1.f, rsn = 0.f;
+  {
+    const int r = 2 * (r0 / 2 + tid_opaque());
+    if (r < r1 && r < qR + kR) {
+      const int d = (r < qR ? r : r - qR) % HD;
+      rcs = rope[d];
+      rsn = rope[d + 1];
+    }
+  }
   bool pending = true;   // the input read + RMSNorm has not run yet
   auto pre_x = [&]() -> bool {
     if (!pending) return true;
@@ -491,7 +503,6 @@ __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Ste
   __syncthreads();
   // RoPE on q and k; q -> LL (fp32); k, v -> cache row (bf16) and LL (bf16 pairs) for
   // this step's attention
-  const PLD_GLOBAL float* rope = gp(wsp<float>(a, a.off.rope)) + (size_t)pos * HD;   // (cos, sin) pairs
   uint64_t* qll = wsp<uint64_t>(a, a.off.q);
   uint64_t* kvll = wsp<uint64_t>(a, a.off.kv);   // [k: NKV*HD/2 | v: NKV*HD/2] bf16-pair words
   for (int p = r0 / 2 + tid_opaque(); p < r1 / 2; p += BLOCK) {
@@ -499,7 +510,8 @@ __device__ __forceinline__ bool stage_qkv_gqa(Ctx& cx, const KArgs& a, const Ste
     float v0 = L.outb[r - r0], v1 = L.outb[r + 1 - r0];
     if (r < qR + kR) {
       const int d = (r < qR ? r : r - qR) % HD;
-      const float cs = rope[d], sn = rope[d + 1];
+      const bool first = p == r0 / 2 + tid_opaque();
+      const float cs = first ? rcs : rope[d], sn = first ? rsn : rope[d + 1];
       const float x0 = v0 * cs - v1 * sn, x1 = v0 * sn + v1 * cs;
       v0 = x0;
       v1 = x1;

@@ -168,6 +168,17 @@ __device__ __forceinline__ bool stage_q_mla(Ctx& cx, const KArgs& a, const Step&
     stamp(a, cx, st, TR_CQ_READY);
     return true;
   };
+  // RoPE (cos, sin) of this thread's first output pair, loaded before the GEMV: after it,
+  // a global load would queue behind the GEMV's trailing weight loads
+  const PLD_GLOBAL float* rope = gp(wsp<float>(a, a.off.rope)) + (size_t)st.pos * SH::RD;   // (cos, sin) pairs
+  float rcs = 1.f, rsn = 0.f;
+  {
+    const int r = 2 * (r0 / 2 + tid_opaque()), k = r % SH::QH;
+    if (r < r1 && r < RQ && k >= SH::ND) {
+      rcs = rope[k - SH::ND];
+      rsn = rope[k - SH::ND + 1];
+    }
+  }
   seg_begin();
   int ns = 0;
   if (r0 < RQ) {
@@ -188,7 +199,6 @@ __device__ __forceinline__ bool stage_q_mla(Ctx& cx, const KArgs& a, const Step&
     if constexpr (SH::SPARSE) return (float)reinterpret_cast<const double*>(L.outb)[i];
     else return L.outb[i];
   };
-  const PLD_GLOBAL float* rope = gp(wsp<float>(a, a.off.rope)) + (size_t)st.pos * SH::RD;   // (cos, sin) pairs
   uint64_t* qn = wsp<uint64_t>(a, a.off.q);
   uint64_t* qr = wsp<uint64_t>(a, a.off.qr);
   for (int p = r0 / 2 + tid_opaque(); p < r1 / 2; p += BLOCK) {
@@ -206,7 +216,8 @@ __device__ __forceinline__ bool stage_q_mla(Ctx& cx, const KArgs& a, const Step&
     } else {
       // q_rope as bf16 pairs: the attention's matrix cores take it in bf16 (same rounding)
       const int d = k - SH::ND;
-      const float cs = rope[d], sn = rope[d + 1];
+      const bool first = p == r0 / 2 + tid_opaque();
+      const float cs = first ? rcs : rope[d], sn = first ? rsn : rope[d + 1];
       ll_put(qr + (h * SH::RD + d) / 2, f32_to_bf16(v0 * cs - v1 * sn) | (f32_to_bf16(v0 * sn + v1 * cs) << 16),
              st.k1);
     }
