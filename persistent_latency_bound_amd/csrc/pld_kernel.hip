@@ -930,8 +930,10 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
   // router workgroups: their router row, loaded ahead of the expert weights
   constexpr int RCH = SH::H / 8, RPT = (RCH + BLOCK - 1) / BLOCK;
   uint4 rrow[SH::MOE ? RPT : 1];
+  float rbias = 0.f;   // the expert's selection bias (biased-score router), loaded ahead too
   if constexpr (SH::MOE) {
     if (w < c.E) {
+      if (c.router == PLD_ROUTER_SIGMOID_BIAS && tid_opaque() < 4) rbias = gp(Ly.router_bias)[w];
       const uint16_t* rp0 = Ly.router + (size_t)w * SH::H;
 #pragma unroll
       for (int k = 0; k < RPT; k++) {
@@ -966,7 +968,7 @@ __device__ __forceinline__ bool stage_ffn(Ctx& cx, const KArgs& a, const Step& s
         s = block_sum(s, L.red);
         if (tid_opaque() < 4) {
           const double key = c.router == PLD_ROUTER_SIGMOID_BIAS
-                                 ? (1.0 / (1.0 + exp_f64(-s, L.dk))) + (double)gp(Ly.router_bias)[w] : s;
+                                 ? (1.0 / (1.0 + exp_f64(-s, L.dk))) + (double)rbias : s;
           const uint64_t bits = (uint64_t)__double_as_longlong(tid_opaque() < 2 ? s : key);
           ll_put(wsp<uint64_t>(a, a.off.logits) + 4 * w + tid_opaque(),
                  (uint32_t)(bits >> (32 * (tid_opaque() & 1))), k1);

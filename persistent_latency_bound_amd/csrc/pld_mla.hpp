@@ -1135,6 +1135,15 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
   const int hg = cx.w / nch, ch = cx.w % nch;
   const int hbase = hg * HPW;
   const int pos = st.pos, T = pos + 1;
+  // the last chunk's new row: this thread's RMSNorm weights (c_kv) or RoPE factors (k_rope),
+  // loaded before the latent rows so that they do not queue behind them
+  float nw0 = 0.f, nw1 = 0.f;
+  if (ch == nch - 1 && tid_opaque() < LAT / 2) {
+    const int k = 2 * tid_opaque();
+    const PLD_GLOBAL float* src = k < KL ? gp(Ly.kv_norm) + k : gp(wsp<float>(a, a.off.rope)) + (size_t)pos * RD + (k - KL);
+    nw0 = src[0];
+    nw1 = src[1];
+  }
   // dense: the chunk's rows are [t0, t1) of the T - 1 history rows (the row of position pos
   // is added by the last chunk after its blocks); sparse: entries [t0, t1) of the
   // indexer's ascending list of K selected rows (the new row, if chosen, is the last)
@@ -1255,13 +1264,14 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
     const PLD_GLOBAL float* rope = gp(wsp<float>(a, a.off.rope)) + (size_t)pos * RD;
     for (int i = tid; i < LAT / 2; i += BLOCK) {
       const int k = 2 * i;
+      const bool first = i == tid;   // its factors were loaded at the start of the stage
       float v0, v1;
       if (k < KL) {
-        v0 = (float)(((double)ntmp[k] * r) * (double)g[k]);
-        v1 = (float)(((double)ntmp[k + 1] * r) * (double)g[k + 1]);
+        v0 = (float)(((double)ntmp[k] * r) * (double)(first ? nw0 : g[k]));
+        v1 = (float)(((double)ntmp[k + 1] * r) * (double)(first ? nw1 : g[k + 1]));
       } else {
         const int d = k - KL;
-        const float x0 = ntmp[k], x1 = ntmp[k + 1], cs = rope[d], sn = rope[d + 1];
+        const float x0 = ntmp[k], x1 = ntmp[k + 1], cs = first ? nw0 : rope[d], sn = first ? nw1 : rope[d + 1];
         v0 = x0 * cs - x1 * sn;
         v1 = x0 * sn + x1 * cs;
       }
