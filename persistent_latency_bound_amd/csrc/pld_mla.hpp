@@ -592,9 +592,19 @@ __device__ __forceinline__ void sel_rank(const SelLds& S, int nc, int need, F&& 
   int rank = 0;
   if (c < nc) {
     const uint32_t h = S.chi[c], l = S.clo[c], t = S.ctk[c];
-    for (int d = part; d < nc; d += 4) {
-      const uint32_t hd = S.chi[d], ld = S.clo[d];
-      rank += (hd > h || (hd == h && (ld > l || (ld == l && S.ctk[d] < t)))) ? 1 : 0;
+    // four candidates per trip, loaded together (one LDS round trip each, not per candidate)
+    for (int d0 = part; d0 < nc; d0 += 16) {
+      uint32_t hd[4], ld[4], td[4];
+#pragma unroll
+      for (int u = 0; u < 4; u++) {
+        const int d = min(d0 + 4 * u, nc - 1);
+        hd[u] = S.chi[d];
+        ld[u] = S.clo[d];
+        td[u] = S.ctk[d];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; u++)
+        rank += (d0 + 4 * u < nc && (hd[u] > h || (hd[u] == h && (ld[u] > l || (ld[u] == l && td[u] < t))))) ? 1 : 0;
     }
   }
   rank += __shfl_xor(rank, 1, 64);
@@ -941,10 +951,13 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
     __syncthreads();
   }
   // ---- taken entries into the token bitmap, then the output in ascending token order
+  // (every flag is read before the first atomic: a flag read placed after one waits for it)
+  uint32_t tkm = 0u;
+#pragma unroll
+  for (int q = 0; q < SEL_EPT; q++) tkm |= (uint32_t)(S.efl[tid + q * BLOCK] == 1) << q;
 #pragma unroll
   for (int q = 0; q < SEL_EPT; q++) {
-    const int e = tid + q * BLOCK;
-    if (S.efl[e] == 1) {
+    if (tkm >> q & 1u) {
       const uint32_t t = etk[q];
       __hip_atomic_fetch_or(lds_ptr(&S.bm[t >> 5]), 1u << (t & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     }
