@@ -555,9 +555,12 @@ __device__ __forceinline__ uint32_t sel_finish8(const SelLds& S, uint32_t nb, in
   uint32_t cnt = 0u;
   const int bn = (int)nb - 1 - tid;
   if (tid < 256 && bn >= 0) {
+    uint32_t hv[NWAVES];   // every row read before the clears (a read after a clear waits for it)
+#pragma unroll
+    for (int w = 0; w < NWAVES; w++) hv[w] = S.hist[w * 256 + bn];
 #pragma unroll
     for (int w = 0; w < NWAVES; w++) {
-      cnt += S.hist[w * 256 + bn];
+      cnt += hv[w];
       S.hist[w * 256 + bn] = 0u;
     }
   }
