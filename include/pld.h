@@ -67,7 +67,7 @@ enum { PLD_ROUTER_SOFTMAX_TOPK = 0, PLD_ROUTER_SIGMOID_BIAS = 1 };
 
 /* Layer shape. GQA fields are used when attn_kind == PLD_ATTN_GQA (MHA is
  * n_kv_heads == n_heads); MLA fields when attn_kind == PLD_ATTN_MLA; index_* when
- * index_topk > 0 (MLA only). */
+ * index_topk > 0 (MLA only; index_topk at most 8192, larger is PLD_E_UNSUPPORTED). */
 typedef struct pld_config {
   int32_t attn_kind;
   int32_t wfmt;

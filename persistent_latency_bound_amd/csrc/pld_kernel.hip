@@ -1561,7 +1561,8 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
       // indexer: 8 heads x 64 dims (4 lanes x 2 heads per token); selection: every scoring
       // workgroup's list in LDS, keys per thread on the all-token path; selected rows per
       // chunk (LL fetch, one pass)
-      if (c->index_heads != 8 || c->index_dim != 64 || c->index_topk < 1) return PLD_E_UNSUPPORTED;
+      if (c->index_heads != 8 || c->index_dim != 64 || c->index_topk < 1 || c->index_topk > SEL_STAGE_MAX)
+        return PLD_E_UNSUPPORTED;
       if (c->max_seq > SEL_MAXJ * BLOCK || c->max_seq > SEL_LKMAX * nwg || nwg > SEL_MAXWG || srows_max > BLOCK ||
           srows_max > 8 * TB)
         return PLD_E_UNSUPPORTED;

@@ -467,6 +467,16 @@ __device__ __forceinline__ SelLds sel_carve(float* act) {
   return S;
 }
 
+// The selected tokens, staged by rank in the counter words (free once the passes are
+// done; at most SEL_ROWS * BLOCK of them), written out by every thread at once. Stores
+// issued from the per-word bit loops instead each waited for the previous loop's stores
+// to complete.
+constexpr int SEL_STAGE_MAX = SEL_ROWS * BLOCK;
+__device__ __forceinline__ void sel_write_out(const SelLds& S, uint64_t* isel, int K, uint32_t k1) {
+  __syncthreads();
+  for (int j = tid_opaque(); j < K; j += BLOCK) ll_put(isel + j, S.hist[j], k1);
+}
+
 // After a counting pass: bin totals (each thread clears the counters it read), the bin
 // holding the need-th largest candidate; need and ncand updated. `pad` non-candidates were
 // counted in bin 0.
@@ -744,11 +754,12 @@ __device__ __noinline__ void sel_all_tokens(const uint32_t* kh, const uint32_t* 
       while (m) {
         const int b = __ffs(m) - 1;
         m &= m - 1u;
-        if (o < (uint32_t)K) ll_put(isel + o, (uint32_t)(r0 + 4 * q + (b >> 3)), k1);
+        if (o < (uint32_t)K) S.hist[o] = (uint32_t)(r0 + 4 * q + (b >> 3));
         o++;
       }
     }
   }
+  sel_write_out(S, isel, K, k1);
 }
 
 // Everything the selecting workgroup needs, passed by value to the out-of-line selection.
@@ -766,6 +777,16 @@ struct SelArgs {
   int red_off, tr_off;   // float offsets of L.red and L.tr from the LDS base (L.act is the base)
   int tron;              // device trace on for this step
 };
+
+// A pointer that arrived in vector registers (an out-of-line call's argument) made
+// wave-uniform, so that loads through it take the scalar-base + vector-offset form.
+template <typename P>
+__device__ __forceinline__ P* uniform_ptr(P* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
+}
 
 // The selection proper (the selecting workgroup, T > K), kept out of line: its registers
 // and constants stay inside this function instead of weighing on the whole kernel.
@@ -810,24 +831,23 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
   uint32_t lb = S.tot[0];
   for (int i = 1; i < NWAVES; i++) lb = min(lb, S.tot[i]);
   // ---- entries e = tid + q*BLOCK; valid when a key (nonzero) reaches the bound
+  // (entries past NE read the last one, unconditionally: no per-load branch; they are
+  // never valid, so their tokens and low halves are never used)
+  const uint32_t* itok = uniform_ptr(sa.itok);
+  const uint32_t* ilo = uniform_ptr(sa.ilo);
   uint32_t etk[SEL_EPT];   // their tokens, in flight during the passes (used for the taken ones)
 #pragma unroll
-  for (int q = 0; q < SEL_EPT; q++) {
-    const int e = tid + q * BLOCK;
-    etk[q] = e < NE ? ld_u32_off(sa.itok, (uint32_t)e * 4u) : 0u;
-  }
+  for (int q = 0; q < SEL_EPT; q++) etk[q] = ld_u32_off(itok, (uint32_t)min(tid + q * BLOCK, NE - 1) * 4u);
   uint32_t elo[SEL_EPT];   // and their low halves (ranking and ties)
 #pragma unroll
-  for (int q = 0; q < SEL_EPT; q++) {
-    const int e = tid + q * BLOCK;
-    elo[q] = e < NE ? ld_u32_off(sa.ilo, (uint32_t)e * 4u) : 0u;
-  }
+  for (int q = 0; q < SEL_EPT; q++) elo[q] = ld_u32_off(ilo, (uint32_t)min(tid + q * BLOCK, NE - 1) * 4u);
   uint32_t eh[SEL_EPT];
   uint32_t ev = 0u, cn = 0u, mx = 0u, mn = 0xffffffffu;
 #pragma unroll
   for (int q = 0; q < SEL_EPT; q++) {
     const int e = tid + q * BLOCK;
-    const uint32_t h = e < NE ? S.lst[e] : 0u;
+    const uint32_t hr = S.lst[min(e, NE - 1)];
+    const uint32_t h = e < NE ? hr : 0u;
     const bool v = h != 0u && h >= lb;
     eh[q] = v ? h : 0u;
     ev |= (uint32_t)v << q;   // (shift form: a literal mask would be hoisted into a register)
@@ -982,11 +1002,12 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
       while (m) {
         const int b = __ffs(m) - 1;
         m &= m - 1u;
-        if (o < (uint32_t)K) ll_put(isel + o, (uint32_t)((tid * SEL_BMW + q) * 32 + b), k1);
+        if (o < (uint32_t)K) S.hist[o] = (uint32_t)((tid * SEL_BMW + q) * 32 + b);
         o++;
       }
     }
   }
+  sel_write_out(S, isel, K, k1);
   stp(TR_SEL_DONE);
   return 1;
 }
