@@ -429,8 +429,8 @@ constexpr int SEL_CMAX = 128;                 // candidates ranked directly
 constexpr int SEL_ROWS = 16;                  // counter words per lane: 32 bins of 16 bits
 constexpr int SEL_BMW = 3;                    // bitmap words per thread: tokens [96 tid, 96 tid + 96)
 static_assert(SEL_LENT % BLOCK == 0 && SEL_BMW * 32 >= SEL_MAXJ && SEL_EPT % 4 == 0, "selector tiling");
-// LDS words: counters | fetched lists | entry flags | token bitmap | scalars | rank lists
-constexpr int SEL_LDS_WORDS = SEL_ROWS * BLOCK + SEL_LENT + SEL_LENT / 4 + SEL_BMW * BLOCK + 64 + 4 * SEL_CMAX;
+// LDS words: counters | fetched lists | token bitmap | scalars | rank lists
+constexpr int SEL_LDS_WORDS = SEL_ROWS * BLOCK + SEL_LENT + SEL_BMW * BLOCK + 64 + 3 * SEL_CMAX;
 static_assert(SEL_MAXJ * BLOCK / 4 <= SEL_LENT, "all-token flags share the list region");
 
 // Exclusive prefix sum of v over the workgroup (thread order); every thread must call.
@@ -447,23 +447,21 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* wsum) 
 }
 
 struct SelLds {
-  uint32_t *hist, *lst, *bm, *sv, *tot, *wsum, *chi, *clo, *ctk, *cix;
-  uint8_t *efl, *fl;
+  uint32_t *hist, *lst, *bm, *sv, *tot, *wsum, *chi, *clo, *ctk;
+  uint8_t* fl;
 };
 __device__ __forceinline__ SelLds sel_carve(float* act) {
   SelLds S;
   S.hist = reinterpret_cast<uint32_t*>(act);     // [SEL_ROWS][BLOCK] packed 16-bit counters
   S.lst = S.hist + SEL_ROWS * BLOCK;              // [SEL_LENT] list entries: key high halves
   S.fl = reinterpret_cast<uint8_t*>(S.lst);      // [SEL_MAXJ*BLOCK] token flags (all-token path)
-  S.efl = reinterpret_cast<uint8_t*>(S.lst + SEL_LENT);   // [SEL_LENT] entry flags
-  S.bm = reinterpret_cast<uint32_t*>(S.efl + SEL_LENT);   // [SEL_BMW*BLOCK] taken tokens
+  S.bm = S.lst + SEL_LENT;                        // [SEL_BMW*BLOCK] taken tokens
   S.sv = S.bm + SEL_BMW * BLOCK;                  // [16] scalars
   S.tot = S.sv + 16;                              // [16] bin-pair totals
   S.wsum = S.tot + 16;                            // [32] scan / reduction partials
   S.chi = S.wsum + 32;                            // [SEL_CMAX] ranked candidates: key high half
   S.clo = S.chi + SEL_CMAX;                       //   low half
   S.ctk = S.clo + SEL_CMAX;                       //   token
-  S.cix = S.ctk + SEL_CMAX;                       //   entry
   return S;
 }
 
@@ -812,6 +810,10 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
     if (sa.tron && tid_opaque() == 0) tr[slot] = wall_clock64();
   };
   const SelLds S = sel_carve(act);
+  // a taken token's bit, set where the entry is decided
+  auto take = [&](uint32_t t) {
+    __hip_atomic_fetch_or(lds_ptr(&S.bm[t >> 5]), 1u << (t & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
   stp(47);
   // every scorer's list, one word per thread and slot
   if (!ll_fetch<SEL_EPT>(cx, S.lst, sa.ilist, NE, k1, W_ILIST)) return 0;
@@ -903,10 +905,9 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
   uint32_t ecb = 0u;   // candidate bits per entry column
 #pragma unroll
   for (int q = 0; q < SEL_EPT; q++) {
-    const int e = tid + q * BLOCK;
     const uint32_t mk = eh[q] & pm;
     const bool v = ev >> q & 1u;
-    S.efl[e] = (uint8_t)((v && mk > pre) ? 1u : (v && mk == pre) ? 2u : 0u);
+    if (v && mk > pre) take(etk[q]);
     ecb |= (uint32_t)(v && mk == pre) << q;
   }
   uint32_t pend = ecb;   // entries still undecided (to be ranked)
@@ -943,18 +944,15 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
 #pragma unroll
     for (int q = 0; q < SEL_EPT; q++) {
       if (ecb >> q & 1u) {
-        const int e = tid + q * BLOCK;
         const uint32_t mk = elo[q] & lpm;
-        const bool und = mk == lpre && ncand > 0;
-        S.efl[e] = (uint8_t)((mk > lpre || (mk == lpre && ncand == 0 && etk[q] < (uint32_t)cut)) ? 1u
-                             : und ? 2u : 0u);
-        pend |= (uint32_t)und << q;
+        if (mk > lpre || (mk == lpre && ncand == 0 && etk[q] < (uint32_t)cut)) take(etk[q]);
+        pend |= (uint32_t)(mk == lpre && ncand > 0) << q;
       }
     }
   }
   if (ncand > 0) {
-    // ---- at most SEL_CMAX undecided entries: their owners append them (hi, lo, token,
-    // entry) to the rank arrays (order of arrival; the ranking does not depend on it)
+    // ---- at most SEL_CMAX undecided entries: their owners append them (hi, lo, token)
+    // to the rank arrays (order of arrival; the ranking does not depend on it)
 #pragma unroll
     for (int q = 0; q < SEL_EPT; q++) {
       if (pend >> q & 1u) {
@@ -963,28 +961,17 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
           S.chi[o] = eh[q];
           S.clo[o] = elo[q];
           S.ctk[o] = etk[q];
-          S.cix[o] = (uint32_t)(tid + q * BLOCK);
         }
       }
     }
     __syncthreads();
     const int nc = min(ncand, SEL_CMAX);
     stp(45);
-    sel_rank(S, nc, need, [&](int c, bool tk) { S.efl[S.cix[c]] = tk ? 1 : 0; });
-    __syncthreads();
+    sel_rank(S, nc, need, [&](int c, bool tk) {
+      if (tk) take(S.ctk[c]);
+    });
   }
-  // ---- taken entries into the token bitmap, then the output in ascending token order
-  // (every flag is read before the first atomic: a flag read placed after one waits for it)
-  uint32_t tkm = 0u;
-#pragma unroll
-  for (int q = 0; q < SEL_EPT; q++) tkm |= (uint32_t)(S.efl[tid + q * BLOCK] == 1) << q;
-#pragma unroll
-  for (int q = 0; q < SEL_EPT; q++) {
-    if (tkm >> q & 1u) {
-      const uint32_t t = etk[q];
-      __hip_atomic_fetch_or(lds_ptr(&S.bm[t >> 5]), 1u << (t & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    }
-  }
+  // ---- the token bitmap is complete: the output in ascending token order
   __syncthreads();
   stp(TR_SEL_PASSES);
   {
