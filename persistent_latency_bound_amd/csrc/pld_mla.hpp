@@ -825,7 +825,6 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
     if (tid < nwg) b = r <= SEL_LIST ? S.lst[tid * SEL_LIST + r - 1] : 0u;
     b = wave_minmax_u32<false>(b);
     if (lane == 0) S.tot[wave] = b;
-    if (tid == 0) S.sv[12] = 0u;   // rank-array fill count
     for (int i = tid; i < SEL_BMW * BLOCK; i += BLOCK) S.bm[i] = 0u;
     for (int rr = 0; rr < SEL_ROWS; rr++) S.hist[rr * BLOCK + tid] = 0u;   // passes clear while reducing
   }
@@ -951,17 +950,19 @@ __device__ __noinline__ int sel_select(SelArgs sa) {
     }
   }
   if (ncand > 0) {
-    // ---- at most SEL_CMAX undecided entries: their owners append them (hi, lo, token)
-    // to the rank arrays (order of arrival; the ranking does not depend on it)
+    // ---- at most SEL_CMAX undecided entries: their owners write them (hi, lo, token) to
+    // the rank arrays in thread order, at offsets from a scan of their counts (the ranking
+    // does not depend on the order; one counter bumped per entry serialized its owners)
+    uint32_t o = block_excl_scan((uint32_t)__popc(pend), S.wsum);
 #pragma unroll
     for (int q = 0; q < SEL_EPT; q++) {
       if (pend >> q & 1u) {
-        const uint32_t o = __hip_atomic_fetch_add(lds_ptr(&S.sv[12]), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         if (o < (uint32_t)SEL_CMAX) {
           S.chi[o] = eh[q];
           S.clo[o] = elo[q];
           S.ctk[o] = etk[q];
         }
+        o++;
       }
     }
     __syncthreads();
