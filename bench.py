@@ -1,24 +1,31 @@
-"""Benchmark of the persistent batch-1 decode layer on one MI355X.
+"""Benchmark of the persistent batch-1 decode path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers R] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-Workload (default): the single MoE decode layer, batch 1, bf16 — hidden 4096, GQA 32 q / 8 kv
-heads x 128, 8192-token KV cache, router over 64 experts (top-8, softmax renormalised),
-expert SwiGLU width 1536 plus one shared expert; weights N(0, 0.02), router N(0, 0.1).
---workload mla_moe256_fp8_decode_layer measures the FP8 MLA layer (hidden 6144, 64 heads,
-latent 512+64, 256 experts of width 2048, biased-score router) the same way;
---workload sparse_mla_moe64_bf16_decode_layer the sparse MLA layer (hidden 4096, 32 heads,
-indexer 8x64 with FP8 keys choosing 2048 of the 32769 cached tokens, 64 experts of width
-1536, bf16 weights) at cache position 32768. A step
-decodes one token through a stack of R independent seeded copies of that layer in ONE
-launch of the persistent kernel (decode_layers_persistent). R copies keep the weights
-cold: R x 458 MB is far larger than the 256 MB Infinity Cache, so the bytes come from
-HBM. Each step gets its own seeded input vector (all resident before timing), so the
-routed experts change from step to step. The cache position stays at the cache length (the step
-rewrites the same row), so every step does the same work.
+Workload (default, mla_stack24_fp8_greedy256): 24 stacked MLA + FP8 MoE decode layers
+(hidden 6144, 64 heads, latent 512 + rope 64, q_lora 1536, 256 experts top-8 of width 2048
+with the biased-score router, one shared expert, FP8 E4M3 weights with fp32 128x128 block
+scales, each layer with its own seeded weights) and an FP8 LM head over 32768 tokens. One
+step is ONE launch of decode_layers_persistent that decodes 256 consecutive greedy tokens
+from an 8192-token prefilled cache (positions 8192..8447) through every layer and the
+head. The 24 layers hold 235 GB of FP8 weights, far more than the 256 MB Infinity Cache,
+so every byte comes from HBM.
+
+Other workloads (--workload), one token through R = --layers independent seeded copies of
+one layer per launch (R copies keep the weights cold; each step has its own seeded input,
+so the routed experts change from step to step, and the step rewrites the same cache row):
+  gqa_moe_bf16_decode_layer           hidden 4096, GQA 32 q / 8 kv heads x 128, 8192-token
+                                      cache, 64 experts top-8 (softmax) of width 1536 + 1
+                                      shared, bf16 weights
+  mla_moe256_fp8_decode_layer         one layer of the default stack's shape, 8192-token cache
+  sparse_mla_moe64_bf16_decode_layer  hidden 4096, 32 MLA heads, indexer 8x64 with FP8 keys
+                                      choosing 2048 of 32769 cached tokens, 64 experts of
+                                      width 1536, bf16 weights, at position 32768
+  mla_stack24_fp8_verify6             the default stack, one 6-position verify per launch
 
 Prints ONE JSON line: value = microseconds per layer (lower is better), plus the HBM
-roofline of the kernel (algorithmic bytes per launch / measured launch time) and the
+roofline of the kernel (algorithmic bytes per launch / measured launch time), the HBM bytes
+the counters saw (when profiles/ holds counter runs of the current kernel sources), and the
 CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -46,7 +53,7 @@ WORKLOADS = {   # name -> (synth.configs attribute, traffic file stem, dtype of 
     "mla_stack24_fp8_verify6": ("C5", "traffic_mla_stack24_fp8_verify6",
                                 "fp8-e4m3 weights, fp32 accumulate, fp64 head"),
 }
-DEFAULT_WORKLOAD = "gqa_moe_bf16_decode_layer"
+DEFAULT_WORKLOAD = "mla_stack24_fp8_greedy256"
 KERNEL_SOURCES = [os.path.join(ROOT, "persistent_latency_bound_amd", "csrc", f)
                   for f in ("pld_kernel.hip", "pld_device.hpp", "pld_mla.hpp")]
 
@@ -58,7 +65,7 @@ def kernel_sha() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_per_launch(workload: str, layers: int):
+def traffic_per_launch(workload: str, layers: int, tokens: int = 1):
     """HBM bytes per launch from committed rocprofv3 counter runs, if taken on this kernel source."""
     path = os.path.join(ROOT, "profiles", WORKLOADS[workload][1] + ".json")
     if not os.path.exists(path):
@@ -66,35 +73,56 @@ def traffic_per_launch(workload: str, layers: int):
     t = json.load(open(path))
     if t.get("kernel_sha") != kernel_sha() or t.get("layers_per_launch") != layers:
         return None
+    if t.get("tokens_per_launch", 1) != tokens:
+        return None
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(shape, pos: int, budget_s: float = 20.0) -> dict:
+def cpu_baseline(shape, pos: int, budget_s: float = 20.0, max_n: int = 8) -> dict:
     """The CPU oracle (unchanged) on a bounded sample: whole layer-tokens of the same workload."""
-    import numpy as np
     from oracle import layer as OL
     from synth import gen
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from gpu_common import host_cache
 
     W = gen.LayerWeights(shape, 0, 0, cache_size=256)
-    cache = host_cache(shape)
+    cache = gen.padded_cache(shape)
     x = gen.input_hidden(shape, 0, 0)
     OL.decode_layer(shape, W, cache, x, pos)          # generates and caches the weights it touches
     n, t0 = 0, time.perf_counter()
     while True:
         OL.decode_layer(shape, W, cache, x, pos)
         n += 1
-        if time.perf_counter() - t0 > budget_s / 2 or n >= 8:
+        if time.perf_counter() - t0 > budget_s / 2 or n >= max_n:
             break
     dt = (time.perf_counter() - t0) / n
     cores = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
     return {"value": round(dt * 1e6, 1), "unit": "us/layer", "cores": cores, "kind": "oracle",
-            "sample": f"{n} layer-token(s) of the same layer at position {pos} after one warm-up call that "
+            "sample": f"{n} layer-token(s) of layer 0 ({shape.name}) at position {pos} after one warm-up call that "
                       f"generates the weights; fp64 NumPy, BLAS and generator threads = {cores}"}
 
 
+def stream_read_peak_gbps() -> float:
+    """Measured HBM read rate of a plain streaming reduction (torch.sum over 4 GiB of fp32),
+    reported beside the 8 TB/s published peak."""
+    import torch
+    x = torch.ones(1 << 30, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        x.sum()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 10
+    e0.record()
+    for _ in range(n):
+        x.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    gbps = x.numel() * 4 * n / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x
+    torch.cuda.empty_cache()
+    return gbps
+
+
 TR_SLOTS = 56   # stamps per (step, workgroup) written by the device trace
+TR_WAIT = 50    # not a stamp: ticks a workgroup spent inside its dependency waits during the step
+TICK_US = 1e-2  # wall_clock64 runs at 100 MHz on MI355X (hipDeviceAttributeWallClockRate = 100000 kHz)
 SLOT_NAMES = {32: "head_ready", 33: "head_gemv", 34: "token", 0: "start", 1: "x_ready", 2: "qkv_done", 3: "att_ready", 4: "att_done", 5: "o_ready", 6: "wo_done",
               7: "h2_ready", 8: "router_ready", 9: "ffn_done", 10: "m_ready", 11: "down_done", 12: "att_q",
               13: "att_softmax", 14: "att_partial", 15: "att_merged", 16: "topk", 18: "m_stored", 19: "down_gemv",
@@ -123,6 +151,8 @@ def write_trace_summary(dec, x, out, R, path, pos):
     start = t[:, :, 0].min(axis=1, keepdims=True)
     rows = []
     for slot in range(TR_SLOTS):
+        if slot == TR_WAIT:
+            continue
         v = t[:, :, slot]
         msk = v > 0
         if not msk.any():
@@ -136,11 +166,33 @@ def write_trace_summary(dec, x, out, R, path, pos):
                        "gap_us": round(med - prev, 2), "stamps": cnt})
         prev = med
     layer_us = [(t[l, :, 11].max() - t[l, :, 0].min()) * tick_us for l in range(R)]
+    wait = np.median(t[:, :, TR_WAIT], axis=1) * tick_us
     summary = {"layers": R, "nwg": nwg, "stamps_from_layer_start": stamps,
+               "wait_us_per_layer_median_wg": [round(float(v), 2) for v in wait],
                "layer_critical_path_us": [round(float(v), 2) for v in layer_us]}
     with open(path, "w") as f:
         json.dump(summary, f, indent=1)
     np.save(os.path.splitext(path)[0] + "_raw.npy", t)   # [layer][workgroup][slot] wall-clock ticks
+
+
+def idle_per_token(dec, one_launch, n_layers, tokens_traced=2):
+    """One extra (untimed) launch with the device trace on for its first tokens. Per step (one
+    layer of one token), every workgroup's summed dependency-wait time; the median over
+    workgroups, summed over the layers of a token, averaged over the traced tokens. Also the
+    per-token critical path from the first stamp to the token's last stamp."""
+    import numpy as np
+    import torch
+    nwg, _ = dec.launch_shape()
+    nst = tokens_traced * n_layers
+    buf = torch.zeros(nst * nwg * TR_SLOTS, dtype=torch.int64, device="cuda")
+    dec.set_trace(buf)
+    one_launch()
+    torch.cuda.synchronize()
+    dec.set_trace(None)
+    t = buf.cpu().numpy().reshape(nst, nwg, TR_SLOTS).astype(np.float64)
+    wait = np.median(t[:, :, TR_WAIT], axis=1) * TICK_US            # [steps]
+    per_tok = wait.reshape(tokens_traced, n_layers).sum(axis=1)
+    return float(per_tok.mean()), t
 
 
 def run_stack(args):
@@ -152,6 +204,7 @@ def run_stack(args):
     m = configs.C5
     L = m.layer
     pos0, n_tok = L.cache_len, args.tokens
+    read_peak = stream_read_peak_gbps()
     Ws = [sdev.layer_weights(L, 0, l) for l in range(m.n_layers)]
     Cs = [sdev.kv_cache(L, 0, l) for l in range(m.n_layers)]
     head = {"embed": sdev.embedding(m), "final_norm": sdev.final_norm(m), "head": sdev.head(m)}
@@ -172,6 +225,7 @@ def run_stack(args):
         raise SystemExit(f"device status {st.code} wait {st.stage}")
     stream = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
     t_wall = time.perf_counter()
     ev[0].record(stream)
     for i in range(args.steps):
@@ -189,6 +243,29 @@ def run_stack(args):
     layer_b = sum(accounting.layer_bytes(L, pos0 + t) for t in range(n_tok)) * m.n_layers
     head_b = accounting.head_bytes(L.hidden, m.vocab) * n_tok
     achieved = (layer_b + head_b) / (ms * 1e-3) / 1e9
+    traffic = traffic_per_launch(args.workload, m.n_layers, n_tok)
+    # one layer per launch through decode_step (launch cost included), after the timed region
+    single_us = None
+    if not args.no_single_launch:
+        x = sdev.input_hidden(L, 0, 0)
+        xo = torch.zeros(L.hidden, dtype=torch.int16, device="cuda")
+        for _ in range(3):
+            dec.step(0, x, pos0, xo)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n1 = 20
+        e0.record(stream)
+        for i in range(n1):
+            dec.step(i % m.n_layers, x, pos0, xo)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        single_us = e0.elapsed_time(e1) * 1e3 / n1
+    idle_us = None
+    if not args.no_idle:
+        idle_us, t = idle_per_token(dec, one, m.n_layers)
+        if args.trace:
+            import numpy as np
+            np.save(os.path.splitext(args.trace)[0] + "_raw.npy", t)   # [step][workgroup][slot] ticks
     line = {
         "metric": "batch-1 decode us/layer (achieved HBM TB/s vs peak, implied tokens/s/user)",
         "value": round(us_lt, 3), "unit": "us/layer", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -200,33 +277,20 @@ def run_stack(args):
         "us_per_token": round(ms * 1e3 / n_tok, 2),
         "p90_ms_per_launch": round(per[min(len(per) - 1, int(0.9 * len(per)))], 3),
         "achieved_TBps": round(achieved / 1e3, 3), "frac_of_peak": round(achieved / PEAK_HBM_GBPS, 4),
-        "algorithmic_bytes_per_launch": int(layer_b + head_b), "launches_per_token": round(1.0 / n_tok, 5),
+        "stream_read_peak_GBps": round(read_peak, 1),
+        "frac_of_measured_read_peak": round(achieved / read_peak, 4),
+        "algorithmic_bytes_per_launch": int(layer_b + head_b),
+        "launches_per_token": round(1.0 / n_tok, 6),
+        "idle_us_per_token": None if idle_us is None else round(idle_us, 1),
+        "single_launch_us_per_layer": None if single_us is None else round(single_us, 2),
         "wall_s_timed_region": round(wall, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None},
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": None if traffic is None else round(traffic / (ms * 1e-3) / 1e9, 1)},
+        "hbm_bytes_per_launch_counters": traffic,
     }
-    if args.trace:
-        # trace the first two tokens (all layers) of one extra launch
-        nwg, _ = dec.launch_shape()
-        nst = 2 * m.n_layers
-        buf = torch.zeros(nst * nwg * TR_SLOTS, dtype=torch.int64, device="cuda")
-        dec.set_trace(buf)
-        one()
-        torch.cuda.synchronize()
-        dec.set_trace(None)
-        import numpy as np
-        t = buf.cpu().numpy().reshape(nst, nwg, TR_SLOTS).astype(np.float64) * 1e-2
-        rows = []
-        for step in range(nst):
-            st0 = t[step, :, 0].min()
-            for slot in range(TR_SLOTS):
-                v = t[step, :, slot]
-                if (v > 0).any():
-                    rows.append({"step": step, "slot": SLOT_NAMES.get(slot, str(slot)),
-                                 "median_us": round(float(np.median(v[v > 0] - st0)), 2)})
-        with open(args.trace, "w") as f:
-            json.dump({"steps": nst, "stamps": rows}, f, indent=0)
-        np.save(os.path.splitext(args.trace)[0] + "_raw.npy", t)   # [step][workgroup][slot] us
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(L, pos0, budget_s=30.0, max_n=2)
     print(json.dumps(line), flush=True)
 
 
@@ -302,8 +366,8 @@ def run_verify(args):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=None, help="timed launches (default 20 for the stack, 100 for a layer)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed launches first (default 3 / 10)")
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--single-launch", action="store_true",
@@ -313,12 +377,27 @@ def main():
     ap.add_argument("--tokens", type=int, default=256, help="tokens per launch (multi-layer workload)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (reference for HBM byte counters)")
+    ap.add_argument("--no-single-launch", action="store_true",
+                    help="stack: skip the decode_step (one layer per launch) timing")
+    ap.add_argument("--no-idle", action="store_true", help="stack: skip the traced launch that measures wait time")
     args = ap.parse_args()
+    stack = args.workload.startswith("mla_stack24")
+    if args.steps is None:
+        args.steps = 20 if args.workload == "mla_stack24_fp8_greedy256" else 10 if stack else 100
+    if args.warmup is None:
+        args.warmup = 3 if stack else 10
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is not built.",
               file=sys.stderr)
         sys.exit(2)
 
+    if args.calib_copy:
+        import torch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.workload == "mla_stack24_fp8_greedy256":
         return run_stack(args)
     if args.workload == "mla_stack24_fp8_verify6":
@@ -328,13 +407,6 @@ def main():
     import persistent_latency_bound_amd as pld
     from oracle import accounting
     from synth import configs, device as sdev
-
-    if args.calib_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
 
     shape = getattr(configs, WORKLOADS[args.workload][0])
     pos = shape.cache_len
@@ -424,7 +496,8 @@ def main():
         "p50_us_per_layer": round(p50, 3),
         "p90_us_per_layer": round(p90, 3),
         "single_launch_us_per_layer": None if single_us is None else round(single_us, 3),
-        "launches_per_token": round(1.0 / R, 4),
+        "launches_per_layer": round(1.0 / R, 4),
+        "launches_per_token_24_layers": round(24.0 / R, 2),
         "algorithmic_bytes_per_layer": bytes_layer,
         "wall_s_timed_region": round(wall, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",

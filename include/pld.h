@@ -157,7 +157,9 @@ typedef struct pld_persistent_args {
   float* out_logits;          /* fp32 [n_tokens or n_query][vocab], or NULL */
   int32_t* out_tokens;        /* int32 [n_tokens or n_query] greedy tokens, or NULL */
   int32_t* out_accepted;      /* verify: int32 [1] accepted draft count, or NULL */
-  int32_t reserved[4];
+  double temperature;         /* 0: greedy argmax; > 0: each token is sampled from softmax(logits / T)
+                                 (LM head required; finite, >= 0, else PLD_E_INVALID) */
+  uint64_t sample_seed;       /* seed of the sampling noise (see decode_layers_persistent) */
 } pld_persistent_args;
 
 typedef struct pld_handle pld_handle;
@@ -195,13 +197,23 @@ pld_status decode_step(pld_handle* h, int32_t layer, const void* x_in, int32_t p
 
 /* One launch for a whole decode run: for each of a->n_tokens tokens (or the n_query
  * verify positions), every layer of the stack in order, then (with a head) final
- * RMSNorm -> LM head -> greedy argmax (lowest id on ties) -> embedding of the chosen
- * token as the next input. Asynchronous on `stream`.
+ * RMSNorm -> LM head -> token choice -> embedding of the chosen token as the next input.
+ * Asynchronous on `stream`.
+ * Token choice: temperature 0 takes the greedy argmax (lowest id on ties). temperature T > 0
+ * samples softmax(logits / T) by the Gumbel-max rule: token = argmax_i (logit_i / T - log(-log
+ * u_i)) in fp64, ties to the lower id, with u_i in (0, 1) from a counter-based SplitMix64
+ * stream keyed by (sample_seed, the step's cache position, i): with G = 0x9E3779B97F4A7C15
+ * and mix the splitmix64 output mixer, k = mix(seed * G + pos), r = mix(k + (i + 1) * G),
+ * u = (2 (r >> 12) + 1) 2^-53. A token thus depends only on its position's logits and the
+ * seed; temperature sampling is a serving setting of the vLLM Kimi K3 backend article ("A
+ * narrow deployment lane"), which leaves the sampling policy to the caller.
  * Verify (n_query > 1): positions start_pos .. start_pos + n_query - 1 are fed in_token,
- * then the drafts; every position's logits and argmax are written; out_accepted[0] =
- * the number of leading drafts equal to the argmax of the position before them
- * (greedy acceptance, the speculative decoding with a draft of six tokens in the vLLM
- * Kimi K3 backend article). Rows of all n_query positions are appended; the caller
+ * then the drafts; every position's logits and chosen token are written; out_accepted[0] =
+ * the number of leading drafts equal to the token chosen at the position before them
+ * (the speculative decoding with a draft of six tokens in the vLLM Kimi K3 backend article;
+ * with T > 0 this is the speculative-sampling rule for a deterministic drafter: a draft is
+ * kept with probability p(draft), and on rejection the position's sample follows p without
+ * the draft, renormalised). Rows of all n_query positions are appended; the caller
  * continues at start_pos + out_accepted[0] + 1 and later launches overwrite the rest.
  * The positions run as sequential steps inside the launch (the plain definition of a
  * causal multi-token verify).
@@ -209,11 +221,44 @@ pld_status decode_step(pld_handle* h, int32_t layer, const void* x_in, int32_t p
  * PLD_E_STATE, PLD_E_HIP. */
 pld_status decode_layers_persistent(pld_handle* h, const pld_persistent_args* a, void* stream);
 
-/* Copy the device status word into *out (synchronises the handle's last stream).
- * Returns PLD_OK, or PLD_E_DEVICE_TIMEOUT if the last launch's watchdog fired. */
+/* Arguments of decode_speculative. */
+typedef struct pld_spec_args {
+  int32_t start_pos;     /* cache position of in_token; both caches hold rows 0 .. start_pos-1 */
+  int32_t in_token;      /* the last kept token (its rows are not yet in either cache) */
+  int32_t n_tokens;      /* tokens to produce */
+  int32_t n_draft;       /* drafts proposed per verify, 1 .. 15 */
+  double temperature;    /* 0 greedy, > 0 sampled (the rule of decode_layers_persistent) */
+  uint64_t sample_seed;
+  int32_t* out_tokens;   /* device int32 [n_tokens], 4-byte aligned */
+  int32_t* out_stats;    /* host int32 [2] or NULL: verify launches, drafts kept in total */
+} pld_spec_args;
+
+/* Speculative decoding with a draft stack (the draft-and-verify loop of the vLLM Kimi K3
+ * backend article's speculative decoding, where a cheap drafter proposes tokens that the
+ * full model checks in one step). `draft` is a second handle over a shallower stack that
+ * shares the target's vocabulary, embedding and LM head (the same device pointers) and
+ * has caches of its own holding the same history rows. Each round: one draft launch
+ * proposes min(n_draft, left - 1) tokens from the current position, one target verify
+ * launch scores them (decode_layers_persistent with n_query = drafts + 1), the leading
+ * drafts equal to the target's chosen token are kept together with the target's token after
+ * them, and both stacks continue after the last kept token (one extra draft step when all
+ * drafts were kept; a plain target step for a last single token). Because a token depends
+ * only on its position's logits and the seed, the tokens equal those of plain decoding of
+ * the target with the same temperature and seed; the drafts change only the number of
+ * launches. Host loop: synchronous on `stream` (one small device-to-host read per round).
+ * Rows past the last kept position may hold rejected drafts; later launches overwrite them.
+ * Uses 136 bytes of the target's workspace. Errors: PLD_E_INVALID (arguments, handles that
+ * do not share the head), PLD_E_CAPACITY (start_pos + n_tokens beyond either cache),
+ * PLD_E_STATE, PLD_E_HIP. */
+pld_status decode_speculative(pld_handle* target, pld_handle* draft, const pld_spec_args* a, void* stream);
+
+/* Copy the device status word into *out (synchronises the stream of the handle's last
+ * launch, nothing else). Returns PLD_OK, or PLD_E_DEVICE_TIMEOUT if the last launch's
+ * watchdog fired; the handle then refuses launches (PLD_E_STATE) until decode_reset. */
 pld_status decode_poll_status(pld_handle* h, pld_device_status* out);
 
 /* Clear the status and the inter-workgroup handoff buffers so the handle can be used
+ * again: waits for the stream of the handle's last launch, clears on that stream and waits
  * again (synchronous). The step epoch keeps counting across resets. */
 pld_status decode_reset(pld_handle* h);
 
@@ -224,11 +269,13 @@ void decode_layer_destroy(pld_handle* h);
 const char* pld_status_string(pld_status s);
 
 /* Device pointer and size in bytes of a named intermediate in the workspace, as left by
- * the last completed launch (for tests). Plain arrays: "a", "b" (fp32 [hidden]), "sel"
- * (int32 [top_k]), "gates" (fp32 [top_k]). LL arrays of 8-byte words whose low 32 bits
+ * the last completed launch (for tests). Plain arrays: "a", "b" (fp32 [hidden]), "f" (fp32
+ * [hidden], the FFN output before the residual add), "sel" (int32 [top_k]), "gates" (fp32 [top_k]). LL arrays of 8-byte words whose low 32 bits
  * are the payload and high 32 bits the step epoch: "q", "o", "h2", "m" (fp32 payloads),
  * "x" (bf16 pairs), "logits" (4 words per expert: logit and selection key as fp64,
- * low then high halves). Returns PLD_E_INVALID for an unknown name. */
+ * low then high halves), "part" (attention partials), "kv" (GQA: the new k/v row),
+ * "amax" (LM head: per-workgroup best logit and token). Returns PLD_E_INVALID for an
+ * unknown name. */
 pld_status pld_debug_buffer(pld_handle* h, const char* name, void** ptr, size_t* bytes);
 
 /* Launch geometry actually used: number of workgroups and threads per workgroup. */
@@ -250,6 +297,22 @@ pld_status pld_set_trace(pld_handle* h, void* buffer, size_t bytes);
 
 /* Set the watchdog budget of every bounded device wait, in microseconds (default 2e6). */
 pld_status pld_set_watchdog_us(pld_handle* h, int64_t us);
+
+/* Test hooks that force the failure and ordering conditions the vLLM Kimi K3 backend
+ * article's kernel audit worries about ("Agent-written kernels face evidence gates":
+ * reads hoisted above a synchronisation, bugs that only show under other timings), from
+ * the host, with every kernel still exiting normally:
+ *   PLD_HOOK_DROP_WG0  the next launch's workgroup 0 leaves at once without publishing
+ *                      anything (a producer that never arrives): the other workgroups'
+ *                      bounded waits expire, the watchdog records the first, and every
+ *                      workgroup exits; the flag clears itself after that launch.
+ *   PLD_HOOK_DELAY     every later launch: each workgroup waits a pseudo-random time of up
+ *                      to 16 us (a hash of `seed`, workgroup, step and stage) at the start of
+ *                      four stages, so workgroups reach every handoff in another order; the
+ *                      outputs must not change (every sum has a fixed order).
+ * flags = 0 turns the hooks off. Errors: PLD_E_INVALID for unknown flags. */
+enum { PLD_HOOK_DROP_WG0 = 1, PLD_HOOK_DELAY = 2 };
+pld_status pld_set_test_hooks(pld_handle* h, int32_t flags, uint32_t seed);
 
 #ifdef __cplusplus
 }

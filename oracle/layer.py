@@ -212,10 +212,15 @@ def mla_attention(s, W, cache, a, pos, rec):
 # ---------------------------------------------------------------------------
 # FFN
 # ---------------------------------------------------------------------------
-def expert(W, e, b):
+def expert(W, e, b, rec=None, slot=0):
+    """SwiGLU expert e on b; with ``rec``, its activation m = silu(g) * u is recorded under
+    rec["m"][slot] (slot = rank of a routed expert in the selection, then the shared ones)."""
     g = _linear(W, "w_gate", b, e)
     u = _linear(W, "w_up", b, e)
-    return _linear(W, "w_down", nx.silu(g) * u, e)
+    m = nx.silu(g) * u
+    if rec is not None:
+        rec.setdefault("m", {})[slot] = m
+    return _linear(W, "w_down", m, e)
 
 
 def route(s, W, b, rec):
@@ -235,13 +240,13 @@ def route(s, W, b, rec):
 
 def ffn(s, W, b, rec):
     if s.ffn == "dense":
-        return expert(W, 0, b)
+        return expert(W, 0, b, rec, 0)
     sel, gates = route(s, W, b, rec)
     f = np.zeros(s.hidden)
-    for e, g in zip(sel, gates):
-        f = f + g * expert(W, int(e), b)
+    for slot, (e, g) in enumerate(zip(sel, gates)):
+        f = f + g * expert(W, int(e), b, rec, slot)
     for j in range(s.n_shared):
-        f = f + expert(W, s.n_experts + j, b)
+        f = f + expert(W, s.n_experts + j, b, rec, s.top_k + j)
     return f
 
 

@@ -24,8 +24,9 @@ PLD_ROUTER_SOFTMAX_TOPK, PLD_ROUTER_SIGMOID_BIAS = 0, 1
 EXPORTS = (
     "pld_workspace_bytes", "decode_layer_init", "decode_step", "decode_layers_persistent", "decode_poll_status",
     "decode_reset", "decode_layer_destroy", "pld_status_string", "pld_debug_buffer", "pld_launch_shape",
-    "pld_set_watchdog_us", "pld_set_trace",
+    "pld_set_watchdog_us", "pld_set_trace", "pld_set_test_hooks", "decode_speculative",
 )
+PLD_HOOK_DROP_WG0, PLD_HOOK_DELAY = 1, 2
 
 i32, vp, f64 = ctypes.c_int32, ctypes.c_void_p, ctypes.c_double
 
@@ -64,11 +65,17 @@ class PldDeviceStatus(ctypes.Structure):
 class PldPersistentArgs(ctypes.Structure):
     _fields_ = [("start_pos", i32), ("n_tokens", i32), ("n_query", i32), ("in_token", i32), ("in_hidden", vp),
                 ("draft_tokens", vp), ("out_hidden", vp), ("out_logits", vp), ("out_tokens", vp),
-                ("out_accepted", vp), ("reserved", i32 * 4)]
+                ("out_accepted", vp), ("temperature", f64), ("sample_seed", ctypes.c_uint64)]
+
+
+class PldSpecArgs(ctypes.Structure):
+    _fields_ = [("start_pos", i32), ("in_token", i32), ("n_tokens", i32), ("n_draft", i32), ("temperature", f64),
+                ("sample_seed", ctypes.c_uint64), ("out_tokens", vp), ("out_stats", vp)]
 
 
 # intermediates kept as LL words (32-bit payload, 32-bit epoch) in the workspace
-LL_BUFFERS = ("q", "o", "h2", "logits", "m", "x", "cq", "ckv", "qrope", "qlat", "olat", "qi", "ixr", "isel", "ilist")
+LL_BUFFERS = ("q", "o", "h2", "logits", "m", "x", "cq", "ckv", "qrope", "qlat", "olat", "qi", "ixr", "isel", "ilist",
+              "part", "kv", "amax")
 
 _lib = None
 
@@ -86,6 +93,7 @@ def lib():
                                         ctypes.POINTER(PldKvCache), ctypes.POINTER(PldHeadWeights), vp,
                                         ctypes.c_size_t, ctypes.POINTER(vp)]
         L.decode_step.argtypes = [vp, i32, vp, i32, vp, vp]
+        L.decode_speculative.argtypes = [vp, vp, ctypes.POINTER(PldSpecArgs), vp]
         L.decode_layers_persistent.argtypes = [vp, ctypes.POINTER(PldPersistentArgs), vp]
         L.decode_poll_status.argtypes = [vp, ctypes.POINTER(PldDeviceStatus)]
         L.decode_reset.argtypes = [vp]
@@ -97,8 +105,10 @@ def lib():
         L.pld_launch_shape.argtypes = [vp, ctypes.POINTER(i32), ctypes.POINTER(i32)]
         L.pld_set_watchdog_us.argtypes = [vp, ctypes.c_int64]
         L.pld_set_trace.argtypes = [vp, vp, ctypes.c_size_t]
-        for f in ("decode_layer_init", "decode_step", "decode_layers_persistent", "decode_poll_status",
-                  "decode_reset", "pld_debug_buffer", "pld_launch_shape", "pld_set_watchdog_us", "pld_set_trace"):
+        L.pld_set_test_hooks.argtypes = [vp, i32, ctypes.c_uint32]
+        for f in ("decode_layer_init", "decode_speculative", "decode_step", "decode_layers_persistent", "decode_poll_status",
+                  "decode_reset", "pld_debug_buffer", "pld_launch_shape", "pld_set_watchdog_us", "pld_set_trace",
+                  "pld_set_test_hooks"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -210,13 +220,28 @@ class Decoder:
               "decode_step")
 
     def persistent(self, start_pos: int, in_hidden=None, out_hidden=None, n_tokens: int = 1, n_query: int = 1,
-                   in_token: int = -1, draft_tokens=None, out_logits=None, out_tokens=None, out_accepted=None):
+                   in_token: int = -1, draft_tokens=None, out_logits=None, out_tokens=None, out_accepted=None,
+                   temperature: float = 0.0, sample_seed: int = 0):
         a = PldPersistentArgs()
         a.start_pos, a.n_tokens, a.n_query, a.in_token = start_pos, n_tokens, n_query, in_token
+        a.temperature, a.sample_seed = float(temperature), int(sample_seed) & 0xFFFFFFFFFFFFFFFF
         a.in_hidden, a.out_hidden = _ptr(in_hidden), _ptr(out_hidden)
         a.draft_tokens, a.out_logits = _ptr(draft_tokens), _ptr(out_logits)
         a.out_tokens, a.out_accepted = _ptr(out_tokens), _ptr(out_accepted)
         check(lib().decode_layers_persistent(self.handle, ctypes.byref(a), self._stream()), "decode_layers_persistent")
+
+    def speculative(self, draft: "Decoder", start_pos: int, in_token: int, n_tokens: int, n_draft: int, out_tokens,
+                    temperature: float = 0.0, sample_seed: int = 0):
+        """decode_speculative with this decoder as the target; returns (verify launches, drafts kept)."""
+        a = PldSpecArgs()
+        a.start_pos, a.in_token, a.n_tokens, a.n_draft = start_pos, in_token, n_tokens, n_draft
+        a.temperature, a.sample_seed = float(temperature), int(sample_seed) & 0xFFFFFFFFFFFFFFFF
+        a.out_tokens = out_tokens.data_ptr()
+        stats = (i32 * 2)()
+        a.out_stats = ctypes.cast(stats, vp)
+        check(lib().decode_speculative(self.handle, draft.handle, ctypes.byref(a), self._stream()),
+              "decode_speculative")
+        return stats[0], stats[1]
 
     def status(self) -> PldDeviceStatus:
         st = PldDeviceStatus()
@@ -227,6 +252,9 @@ class Decoder:
 
     def reset(self):
         check(lib().decode_reset(self.handle), "decode_reset")
+
+    def set_test_hooks(self, flags: int, seed: int = 0):
+        check(lib().pld_set_test_hooks(self.handle, int(flags), int(seed) & 0xFFFFFFFF), "pld_set_test_hooks")
 
     def set_watchdog_us(self, us: int):
         check(lib().pld_set_watchdog_us(self.handle, int(us)), "pld_set_watchdog_us")
@@ -243,6 +271,13 @@ class Decoder:
         n, b = i32(), i32()
         check(lib().pld_launch_shape(self.handle, ctypes.byref(n), ctypes.byref(b)), "pld_launch_shape")
         return n.value, b.value
+
+    def debug_raw(self, name: str):
+        """The workspace bytes of a named buffer as a uint8 view (not a copy)."""
+        p, nb = vp(), ctypes.c_size_t()
+        check(lib().pld_debug_buffer(self.handle, name.encode(), ctypes.byref(p), ctypes.byref(nb)), "pld_debug_buffer")
+        off = p.value - self.workspace.data_ptr()
+        return self.workspace[off: off + nb.value]
 
     def debug(self, name: str, dtype=None):
         """Copy of an intermediate left in the workspace by the last launch (after a sync)."""

@@ -54,6 +54,7 @@ enum TraceSlot {
   TR_MERGE_COPIED = 26, TR_RT_LOGIT = 27, TR_ATT_DRAINED = 28, TR_ATT_SCORES = 30, TR_HEAD_READY = 32,
   TR_HEAD_GEMV = 33, TR_TOKEN = 34, TR_IDX_DONE = 35, TR_SEL_KEYS = 36, TR_SEL_PASSES = 37, TR_SEL_DONE = 38,
   TR_CQ_READY = 48, TR_Q_GEMV = 49,
+  TR_WAIT = 50,   // not a stamp: total ticks the workgroup spent inside dependency waits (ll_fetch)
   TR_SLOTS = 56
 };
 
@@ -87,7 +88,7 @@ struct DLayer {
 // status words; both are zeroed at init and by decode_reset.
 struct WsOff {
   size_t status, x, q, kv, part, o, h2, logits, m, cqr, ckvr, qr, qlat, olat, amax, ixr, qi, ilist, isel, ll_end, sel,
-      gates, a_dbg, b_dbg, ikh, ikl, ilo, itok, rope, layers, total;
+      gates, spec, a_dbg, b_dbg, f_dbg, ikh, ikl, ilo, itok, rope, layers, total;
 };
 
 struct KArgs {
@@ -111,6 +112,10 @@ struct KArgs {
   int head_on;             // run the head after the last layer of every token
   const int32_t* drafts;   // verify: [n_tokens - 1] draft tokens fed to positions 1.., or null
   int32_t* out_accepted;   // verify: [1] accepted draft count, or null
+  int hooks;               // test hooks (PLD_HOOK_*), 0 in normal use
+  uint32_t hook_seed;
+  double temperature;      // LM head: 0 = greedy argmax, > 0 = Gumbel-max sample of softmax(logits / T)
+  uint64_t sample_seed;
 };
 
 // ------------------------------------------------------------------ device context
@@ -119,6 +124,7 @@ struct Ctx {
   int w, nwg;
   uint32_t* status;
   int layer, token;
+  uint64_t* wacc;     // traced steps: LDS slot that accumulates the wait time (thread 0), else null
 };
 
 template <typename T>
@@ -138,6 +144,20 @@ __device__ __noinline__ void raise_timeout(uint32_t* status, int wait_id, int la
   }
   st_u32(status + ST_ABORT, 1u);
 }
+
+// Test hook PLD_HOOK_DELAY: the workgroup waits a seeded pseudo-random time of up to 16 us
+// (a hash of seed, workgroup, step and point) so that the stages of different workgroups
+// run in another relative order. Every result is formed in a fixed order whatever the
+// timing, so the outputs must not change. Bounded by the wall clock; all threads call it.
+// The hash is Chris Wellons' "lowbias32" integer finalizer.
+__device__ __noinline__ void test_delay(uint32_t seed, int w, int idx, int point) {
+  uint32_t h = seed ^ ((uint32_t)w * 0x9E3779B9u) ^ ((uint32_t)idx * 0x85EBCA6Bu) ^ ((uint32_t)point * 0xC2B2AE35u);
+  h ^= h >> 16; h *= 0x7feb352du; h ^= h >> 15; h *= 0x846ca68bu; h ^= h >> 16;
+  const long long until = wall_clock64() + (long long)(h % 1600u);   // 100 MHz ticks
+  while (wall_clock64() < until) __builtin_amdgcn_s_sleep(2);
+}
+#define PLD_TEST_DELAY(a, w, idx, point) \
+  do { if ((a).hooks & PLD_HOOK_DELAY) test_delay((a).hook_seed, (w), (idx), (point)); } while (0)
 
 // ------------------------------------------------------------------ LL handoff
 // Every activation that crosses workgroups travels as LL words: one 8-byte atomic store
@@ -175,6 +195,8 @@ __device__ __forceinline__ bool ll_fetch(Ctx& cx, uint32_t* dst, const uint64_t*
                                          Idx idx = Idx{}, St store = St{}) {
   int failed = 0;
   const int tid = tid_opaque();
+  uint64_t t_in = 0;
+  if (cx.wacc && tid == 0) t_in = wall_clock64();
   for (int base = 0; base < n; base += BLOCK * PER) {
     uint64_t v[PER];
 #pragma unroll
@@ -211,7 +233,9 @@ __device__ __forceinline__ bool ll_fetch(Ctx& cx, uint32_t* dst, const uint64_t*
       if (i < n) store(dst, i, (uint32_t)v[j]);
     }
   }
-  return !__syncthreads_or(failed);
+  const bool ok = !__syncthreads_or(failed);
+  if (cx.wacc && tid == 0) *cx.wacc += wall_clock64() - t_in;
+  return ok;
 }
 constexpr int per_for(int n) { return n <= BLOCK ? 1 : (n + BLOCK - 1) / BLOCK > 16 ? 16 : (n + BLOCK - 1) / BLOCK; }
 
@@ -1174,6 +1198,7 @@ __device__ __forceinline__ bool stage_down(Ctx& cx, const KArgs& a, const Step& 
       float f = 0.f;
       for (int s = 0; s < c.slots; s++) f += ((!SH::MOE || s >= c.topk) ? 1.0f : L.fgate[s]) * L.outb[s * nr + r];
       L.outc[r] = f;
+      st_f32(wsp<float>(a, a.off.f_dbg) + r0 + r, f);   // debug copy of this workgroup's rows of f
     }
   }
   __syncthreads();
@@ -1189,7 +1214,27 @@ __device__ __forceinline__ bool stage_down(Ctx& cx, const KArgs& a, const Step& 
   return true;
 }
 
-// ------------------------------------------------------------------ LM head + greedy argmax
+// ------------------------------------------------------------------ sampling noise
+// Gumbel noise g = -log(-log u) of token i at the step of position pos. u comes from a
+// counter-based SplitMix64 stream (Steele, Lea and Flood, "Fast splittable pseudorandom
+// number generators", OOPSLA 2014; the output mixer of Vigna's splitmix64.c), mod 2^64
+// with G = 0x9E3779B97F4A7C15: k = mix(seed * G + pos), r = mix(k + (i + 1) * G),
+// u = (2 * (r >> 12) + 1) * 2^-53, exact in fp64 and never 0 or 1. The sampled token is
+// argmax_i(logit_i / T + g_i) in fp64 (ties to the lower id), a sample of softmax(logits / T).
+__device__ __forceinline__ uint64_t splitmix_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+__device__ __noinline__ double gumbel_noise(uint64_t seed, int pos, int i) {
+  const uint64_t G = 0x9E3779B97F4A7C15ull;
+  const uint64_t k = splitmix_mix(seed * G + (uint64_t)(uint32_t)pos);
+  const uint64_t r = splitmix_mix(k + (uint64_t)(uint32_t)(i + 1) * G);
+  const double u = ((double)(r >> 12) * 2.0 + 1.0) * 0x1p-53;
+  return -log(-log(u));
+}
+
+// ------------------------------------------------------------------ LM head + greedy argmax / sampling
 // logits = W_head RMSNorm(x; gamma_final) for this workgroup's vocab rows, accumulated in
 // fp64: an FP8 code times its fp32 block scale times an fp64 activation is exact in fp64,
 // so the logits equal an fp64 evaluation up to summation rounding and the argmax is
@@ -1283,14 +1328,17 @@ __device__ __forceinline__ bool stage_head(Ctx& cx, const KArgs& a, const Step& 
   stamp(a, cx, st, TR_HEAD_GEMV);
   if (a.out_logits)
     for (int i = tid; i < nr; i += BLOCK) gp(a.out_logits)[(size_t)t * V + r0 + i] = (float)lg[i];
-  // best of this workgroup: (logit desc, token id asc)
+  // best of this workgroup: (key desc, token id asc); key = logit (greedy) or logit / T + g
   auto better = [](double v, int i, double bv, int bi) { return v > bv || (v == bv && i < bi); };
   uint64_t* am = wsp<uint64_t>(a, a.off.amax);
   if (wave == 0) {
     double bv = -INFINITY;
     int bi = 0x7fffffff;
-    for (int i = lane; i < nr; i += 64)
-      if (better(lg[i], r0 + i, bv, bi)) { bv = lg[i]; bi = r0 + i; }
+    const double temp = a.temperature;
+    for (int i = lane; i < nr; i += 64) {
+      const double key = temp > 0.0 ? lg[i] / temp + gumbel_noise(a.sample_seed, st.pos, r0 + i) : lg[i];
+      if (better(key, r0 + i, bv, bi)) { bv = key; bi = r0 + i; }
+    }
     for (int off = 32; off >= 1; off >>= 1) {
       const double ov = __shfl_xor(bv, off, 64);
       const int oi = __shfl_xor(bi, off, 64);
@@ -1337,7 +1385,9 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_gqa(KArgs a) {
   cx.w = blockIdx.x;
   cx.nwg = gridDim.x;
   cx.status = wsp<uint32_t>(a, a.off.status);
+  cx.wacc = nullptr;
   const DLayer* layers = wsp<DLayer>(a, a.off.layers);
+  if ((a.hooks & PLD_HOOK_DROP_WG0) && cx.w == 0) return;   // test hook: a producer that never publishes
   {
     Lds L0 = carve(lds_raw, a.c);
     if (tid_opaque() < TR_SLOTS) L0.tr[tid_opaque()] = 0;
@@ -1368,11 +1418,16 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_gqa(KArgs a) {
       asm volatile("" : "+s"(lds0));
       Lds L = carve(lds_raw + lds0, a.c);
       st.tr = L.tr;
+      cx.wacc = (a.trace && st.idx < a.trace_steps) ? L.tr + TR_WAIT : nullptr;
       stamp(as, cx, st, TR_START);
+      PLD_TEST_DELAY(a, cx.w, st.idx, 0);
       if (!stage_qkv_gqa<SH>(cx, as, st, L)) return;
+      PLD_TEST_DELAY(a, cx.w, st.idx, 1);
       if (!attention_gqa<SH>(cx, as, st, L)) return;
       if (!stage_wo<SH>(cx, as, st, L)) return;
+      PLD_TEST_DELAY(a, cx.w, st.idx, 2);
       if (!stage_ffn<SH>(cx, as, st, L)) return;
+      PLD_TEST_DELAY(a, cx.w, st.idx, 3);
       if (!stage_down<SH>(cx, as, st, L, last ? as.out_hidden : nullptr)) return;
       if constexpr (SH::FP8) {
         if (a.head_on && li == a.n_layers - 1 && !stage_head<SH>(cx, as, st, L, t, &token)) return;
@@ -1454,6 +1509,8 @@ struct pld_handle {
   const uint16_t* embed;   // LM head (vocab > 0)
   const float* fnorm;
   DMat head;
+  int hooks;               // test hooks for the next launches (PLD_HOOK_DROP_WG0 lasts one launch)
+  uint32_t hook_seed;
 };
 
 namespace {
@@ -1634,8 +1691,10 @@ WsOff layout(const KCfg& k, int n_layers) {
   o.ll_end = p;
   o.sel = p; p += al(64 * 4);
   o.gates = p; p += al(64 * 4);
+  o.spec = p; p += al(64 * 4);   // decode_speculative: drafts [16], verify tokens [16], accepted, spare
   o.a_dbg = p; p += al((size_t)k.H * 4);
   o.b_dbg = p; p += al((size_t)k.H * 4);
+  o.f_dbg = p; p += al((size_t)k.H * 4);
   if (k.itopk > 0) {
     o.ikh = p; p += al((size_t)k.max_seq * 4);   // indexer score keys, high and low halves
     o.ikl = p; p += al((size_t)k.max_seq * 4);
@@ -1690,11 +1749,111 @@ size_t pld_workspace_bytes(const pld_config* cfg, int32_t n_layers) {
   return layout(k, n_layers).total;
 }
 
-pld_status decode_layer_init(const pld_config* cfg, int32_t n_layers, const pld_layer_weights* w,
-                             const pld_kv_cache* kv, const pld_head_weights* head, void* workspace, size_t ws_bytes,
-                             pld_handle** out) {
-  if (!cfg || !w || !kv || !workspace || !out || n_layers < 1) return PLD_E_INVALID;
-  *out = nullptr;
+}  // extern "C"
+
+namespace {
+
+// RoPE table (cos, sin) of pos * base^(-2i/d) for the interleaved pairs, fp64 -> fp32, written
+// to the device in chunks from a fixed host buffer (init allocates nothing).
+bool upload_rope(uint8_t* dst, int max_seq, int d, double base) {
+  constexpr int CH = 4096;   // floats per chunk
+  float buf[CH];
+  const size_t total = (size_t)max_seq * d;
+  for (size_t i0 = 0; i0 < total; i0 += CH) {
+    const size_t n = std::min((size_t)CH, total - i0);
+    for (size_t i = 0; i < n; i += 2) {
+      const size_t e = i0 + i;
+      const int p = (int)(e / d), j = (int)(e % d) / 2;
+      const double ang = (double)p * std::pow(base, -2.0 * j / d);
+      buf[i] = (float)std::cos(ang);
+      buf[i + 1] = (float)std::sin(ang);
+    }
+    if (hipMemcpy(dst + i0 * 4, buf, n * 4, hipMemcpyHostToDevice) != hipSuccess) return false;
+  }
+  return true;
+}
+
+// The layer descriptor of w[l] / kv[l], validated; PLD_E_INVALID for a missing or misaligned pointer.
+pld_status build_layer(const pld_config* cfg, const pld_layer_weights& L, const pld_kv_cache& C, DLayer* out) {
+  const bool fp8 = cfg->wfmt == PLD_WFMT_FP8_BLOCK128;
+  const bool moe = cfg->ffn_kind == PLD_FFN_MOE;
+  const int H = cfg->hidden;
+  DLayer& d = *out;
+  memset(&d, 0, sizeof(d));
+  if (!L.attn_norm || !L.ffn_norm || !aligned16(L.attn_norm) || !aligned16(L.ffn_norm)) return PLD_E_INVALID;
+  d.attn_norm = L.attn_norm;
+  d.ffn_norm = L.ffn_norm;
+  const bool mla = cfg->attn_kind == PLD_ATTN_MLA;
+  if (!mla) {
+    const int hd = cfg->head_dim;
+    if (!mat_ok(L.wq, fp8) || !mat_ok(L.wk, fp8) || !mat_ok(L.wv, fp8) || !mat_ok(L.wo, fp8)) return PLD_E_INVALID;
+    d.wq = dmat(L.wq, cfg->n_heads * hd, H, fp8);
+    d.wk = dmat(L.wk, cfg->n_kv_heads * hd, H, fp8);
+    d.wv = dmat(L.wv, cfg->n_kv_heads * hd, H, fp8);
+    d.wo = dmat(L.wo, H, cfg->n_heads * hd, fp8);
+  } else {
+    const int NH = cfg->n_heads, QL = cfg->q_lora, KL = cfg->kv_lora, RD = cfg->rope_dim, ND = cfg->nope_dim,
+              VD = cfg->v_dim;
+    if (!mat_ok(L.w_dq, fp8) || !mat_ok(L.w_uq, fp8) || !mat_ok(L.w_dkv, fp8) || !mat_ok(L.w_uk, fp8) ||
+        !mat_ok(L.w_uv, fp8) || !mat_ok(L.wo, fp8))
+      return PLD_E_INVALID;
+    if (!L.q_norm || !L.kv_norm || !aligned16(L.q_norm) || !aligned16(L.kv_norm)) return PLD_E_INVALID;
+    d.q_norm = L.q_norm;
+    d.kv_norm = L.kv_norm;
+    d.w_dq = dmat(L.w_dq, QL, H, fp8);
+    d.w_uq = dmat(L.w_uq, NH * (ND + RD), QL, fp8);
+    d.w_dkv = dmat(L.w_dkv, KL + RD, H, fp8);
+    d.w_uk = dmat(L.w_uk, NH * ND, KL, fp8);
+    d.w_uv = dmat(L.w_uv, NH * VD, KL, fp8);
+    d.wo = dmat(L.wo, H, NH * VD, fp8);
+    if (cfg->index_topk > 0) {
+      const int IH = cfg->index_heads, ID = cfg->index_dim;
+      if (!mat_ok(L.w_qi, fp8) || !mat_ok(L.w_w, false) || !mat_ok(L.w_ki, fp8)) return PLD_E_INVALID;
+      d.w_qi = dmat(L.w_qi, IH * ID, QL, fp8);
+      d.w_w = dmat(L.w_w, IH, H, false);
+      d.w_ki = dmat(L.w_ki, ID, H, fp8);
+    }
+  }
+  if (!mat_ok(L.w_gate, fp8) || !mat_ok(L.w_up, fp8) || !mat_ok(L.w_down, fp8)) return PLD_E_INVALID;
+  d.w_gate = dmat(L.w_gate, cfg->inter, H, fp8);
+  d.w_up = dmat(L.w_up, cfg->inter, H, fp8);
+  d.w_down = dmat(L.w_down, H, cfg->inter, fp8);
+  const size_t wb = fp8 ? 1 : 2;
+  d.gu_slot_bytes = (size_t)cfg->inter * H * wb;
+  d.dn_slot_bytes = (size_t)H * cfg->inter * wb;
+  d.gu_slot_scales = fp8 ? (size_t)((cfg->inter + 127) / 128) * ((H + 127) / 128) : 0;
+  d.dn_slot_scales = fp8 ? (size_t)((H + 127) / 128) * ((cfg->inter + 127) / 128) : 0;
+  if (moe) {
+    if (!L.router || !aligned16(L.router)) return PLD_E_INVALID;
+    d.router = (const uint16_t*)L.router;
+    if (cfg->router_kind == PLD_ROUTER_SIGMOID_BIAS) {
+      if (!L.router_bias) return PLD_E_INVALID;
+      d.router_bias = L.router_bias;
+    }
+  }
+  if (!mla) {
+    if (!C.k || !C.v || !aligned16(C.k) || !aligned16(C.v)) return PLD_E_INVALID;
+    d.kc = (uint16_t*)C.k;
+    d.vc = (uint16_t*)C.v;
+  } else {
+    if (!C.latent || !aligned16(C.latent)) return PLD_E_INVALID;
+    d.lat = (uint16_t*)C.latent;
+    if (cfg->index_topk > 0) {
+      if (!C.index_codes || !C.index_scales || !aligned16(C.index_codes) || !aligned16(C.index_scales))
+        return PLD_E_INVALID;
+      d.icodes = (uint8_t*)C.index_codes;
+      d.iscales = C.index_scales;
+    }
+  }
+  return PLD_OK;
+}
+
+// Validates the arguments and fills *h (caller-provided storage) for the workspace `ws`:
+// descriptors and the RoPE table uploaded, status and LL buffers zeroed, co-residency
+// checked. Allocates nothing, on the host or the device.
+pld_status init_into(pld_handle* h, const pld_config* cfg, int32_t n_layers, const pld_layer_weights* w,
+                     const pld_kv_cache* kv, const pld_head_weights* head, void* workspace, size_t ws_bytes) {
+  if (!cfg || !w || !kv || !workspace || n_layers < 1) return PLD_E_INVALID;
   if (!aligned16(workspace)) return PLD_E_INVALID;
   int dev = 0;
   const int nwg = device_cus(&dev);
@@ -1708,99 +1867,23 @@ pld_status decode_layer_init(const pld_config* cfg, int32_t n_layers, const pld_
     return PLD_E_INVALID;
   const WsOff off = layout(k, n_layers);
   if (ws_bytes < off.total) return PLD_E_CAPACITY;
-  const bool fp8 = cfg->wfmt == PLD_WFMT_FP8_BLOCK128;
-  const bool moe = cfg->ffn_kind == PLD_FFN_MOE;
-  const int H = cfg->hidden;
-  std::vector<DLayer> dl(n_layers);
-  for (int l = 0; l < n_layers; l++) {
-    const pld_layer_weights& L = w[l];
-    DLayer& d = dl[l];
-    memset(&d, 0, sizeof(d));
-    if (!L.attn_norm || !L.ffn_norm || !aligned16(L.attn_norm) || !aligned16(L.ffn_norm)) return PLD_E_INVALID;
-    d.attn_norm = L.attn_norm;
-    d.ffn_norm = L.ffn_norm;
-    const bool mla = cfg->attn_kind == PLD_ATTN_MLA;
-    if (!mla) {
-      const int hd = cfg->head_dim;
-      if (!mat_ok(L.wq, fp8) || !mat_ok(L.wk, fp8) || !mat_ok(L.wv, fp8) || !mat_ok(L.wo, fp8)) return PLD_E_INVALID;
-      d.wq = dmat(L.wq, cfg->n_heads * hd, H, fp8);
-      d.wk = dmat(L.wk, cfg->n_kv_heads * hd, H, fp8);
-      d.wv = dmat(L.wv, cfg->n_kv_heads * hd, H, fp8);
-      d.wo = dmat(L.wo, H, cfg->n_heads * hd, fp8);
-    } else {
-      const int NH = cfg->n_heads, QL = cfg->q_lora, KL = cfg->kv_lora, RD = cfg->rope_dim, ND = cfg->nope_dim,
-                VD = cfg->v_dim;
-      if (!mat_ok(L.w_dq, fp8) || !mat_ok(L.w_uq, fp8) || !mat_ok(L.w_dkv, fp8) || !mat_ok(L.w_uk, fp8) ||
-          !mat_ok(L.w_uv, fp8) || !mat_ok(L.wo, fp8))
-        return PLD_E_INVALID;
-      if (!L.q_norm || !L.kv_norm || !aligned16(L.q_norm) || !aligned16(L.kv_norm)) return PLD_E_INVALID;
-      d.q_norm = L.q_norm;
-      d.kv_norm = L.kv_norm;
-      d.w_dq = dmat(L.w_dq, QL, H, fp8);
-      d.w_uq = dmat(L.w_uq, NH * (ND + RD), QL, fp8);
-      d.w_dkv = dmat(L.w_dkv, KL + RD, H, fp8);
-      d.w_uk = dmat(L.w_uk, NH * ND, KL, fp8);
-      d.w_uv = dmat(L.w_uv, NH * VD, KL, fp8);
-      d.wo = dmat(L.wo, H, NH * VD, fp8);
-      if (cfg->index_topk > 0) {
-        const int IH = cfg->index_heads, ID = cfg->index_dim;
-        if (!mat_ok(L.w_qi, fp8) || !mat_ok(L.w_w, false) || !mat_ok(L.w_ki, fp8)) return PLD_E_INVALID;
-        d.w_qi = dmat(L.w_qi, IH * ID, QL, fp8);
-        d.w_w = dmat(L.w_w, IH, H, false);
-        d.w_ki = dmat(L.w_ki, ID, H, fp8);
-      }
-    }
-    if (!mat_ok(L.w_gate, fp8) || !mat_ok(L.w_up, fp8) || !mat_ok(L.w_down, fp8)) return PLD_E_INVALID;
-    d.w_gate = dmat(L.w_gate, cfg->inter, H, fp8);
-    d.w_up = dmat(L.w_up, cfg->inter, H, fp8);
-    d.w_down = dmat(L.w_down, H, cfg->inter, fp8);
-    const size_t wb = fp8 ? 1 : 2;
-    d.gu_slot_bytes = (size_t)cfg->inter * H * wb;
-    d.dn_slot_bytes = (size_t)H * cfg->inter * wb;
-    d.gu_slot_scales = fp8 ? (size_t)((cfg->inter + 127) / 128) * ((H + 127) / 128) : 0;
-    d.dn_slot_scales = fp8 ? (size_t)((H + 127) / 128) * ((cfg->inter + 127) / 128) : 0;
-    if (moe) {
-      if (!L.router || !aligned16(L.router)) return PLD_E_INVALID;
-      d.router = (const uint16_t*)L.router;
-      if (cfg->router_kind == PLD_ROUTER_SIGMOID_BIAS) {
-        if (!L.router_bias) return PLD_E_INVALID;
-        d.router_bias = L.router_bias;
-      }
-    }
-    const pld_kv_cache& C = kv[l];
-    if (!mla) {
-      if (!C.k || !C.v || !aligned16(C.k) || !aligned16(C.v)) return PLD_E_INVALID;
-      d.kc = (uint16_t*)C.k;
-      d.vc = (uint16_t*)C.v;
-    } else {
-      if (!C.latent || !aligned16(C.latent)) return PLD_E_INVALID;
-      d.lat = (uint16_t*)C.latent;
-      if (cfg->index_topk > 0) {
-        if (!C.index_codes || !C.index_scales || !aligned16(C.index_codes) || !aligned16(C.index_scales))
-          return PLD_E_INVALID;
-        d.icodes = (uint8_t*)C.index_codes;
-        d.iscales = C.index_scales;
-      }
-    }
+  uint8_t* ws = (uint8_t*)workspace;
+  for (int l = 0; l < n_layers; l++) {   // validate every layer before anything is written
+    DLayer d;
+    if ((st = build_layer(cfg, w[l], kv[l], &d)) != PLD_OK) return st;
   }
-  pld_handle* h = new (std::nothrow) pld_handle();
-  if (!h) return PLD_E_INVALID;
+  memset(h, 0, sizeof(*h));
   h->cfg = *cfg;
   h->kc = k;
   h->off = off;
   h->n_layers = n_layers;
-  h->ws = (uint8_t*)workspace;
+  h->ws = ws;
   h->ws_bytes = ws_bytes;
   h->lds_bytes = lds_bytes_for(k.act_floats, k.stage_words, k.outb_floats);
-  h->steps = 0;
-  h->bad = false;
   h->device = dev;
-  h->last_stream = nullptr;
-  h->trace = nullptr;
-  h->trace_steps = 0;
   h->embed = head ? (const uint16_t*)head->embed : nullptr;
   h->fnorm = head ? head->final_norm : nullptr;
-  if (head) h->head = dmat(head->head, cfg->vocab, H, true);
+  if (head) h->head = dmat(head->head, cfg->vocab, cfg->hidden, true);
   const char* coop = getenv("PLD_COOPERATIVE");
   h->coop = coop && atoi(coop) != 0;
   h->fn = pick_kernel(cfg);
@@ -1808,30 +1891,37 @@ pld_status decode_layer_init(const pld_config* cfg, int32_t n_layers, const pld_
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0) khz = 100000;
   h->wallclock_khz = khz;
   h->budget = (long long)khz * 1000LL * 2;   // 2 s
-  // RoPE table: (cos, sin) of pos * base^(-2i/d) for the interleaved pairs, fp64 -> fp32
-  // (d = head_dim for GQA; MLA rotates only its rope_dim dims)
-  const int d = k.rdim;
-  std::vector<float> rope((size_t)cfg->max_seq * d);
-  for (int p = 0; p < cfg->max_seq; p++)
-    for (int i = 0; i < d / 2; i++) {
-      const double ang = (double)p * std::pow(cfg->rope_base, -2.0 * i / d);
-      rope[(size_t)p * d + 2 * i] = (float)std::cos(ang);
-      rope[(size_t)p * d + 2 * i + 1] = (float)std::sin(ang);
-    }
-  bool ok = hipMemcpy(h->ws + off.rope, rope.data(), rope.size() * 4, hipMemcpyHostToDevice) == hipSuccess;
-  ok = ok && hipMemcpy(h->ws + off.layers, dl.data(), dl.size() * sizeof(DLayer), hipMemcpyHostToDevice) == hipSuccess;
-  ok = ok && hipMemset(h->ws, 0, off.ll_end) == hipSuccess;   // status + LL buffers
+  bool ok = upload_rope(ws + off.rope, cfg->max_seq, k.rdim, cfg->rope_base);
+  for (int l = 0; ok && l < n_layers; l++) {
+    DLayer d;
+    build_layer(cfg, w[l], kv[l], &d);
+    ok = hipMemcpy(ws + off.layers + (size_t)l * sizeof(DLayer), &d, sizeof(DLayer), hipMemcpyHostToDevice) == hipSuccess;
+  }
+  ok = ok && hipMemset(ws, 0, off.ll_end) == hipSuccess;   // status + LL buffers
   ok = ok && hipFuncSetAttribute((const void*)h->fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->lds_bytes) == hipSuccess;
   int per_cu = 0;
   ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)h->fn, BLOCK, h->lds_bytes) == hipSuccess;
   ok = ok && hipDeviceSynchronize() == hipSuccess;
-  if (!ok) {
+  if (!ok) return PLD_E_HIP;
+  if (per_cu < 1) return PLD_E_UNSUPPORTED;
+  return PLD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pld_status decode_layer_init(const pld_config* cfg, int32_t n_layers, const pld_layer_weights* w,
+                             const pld_kv_cache* kv, const pld_head_weights* head, void* workspace, size_t ws_bytes,
+                             pld_handle** out) {
+  if (!out) return PLD_E_INVALID;
+  *out = nullptr;
+  pld_handle* h = new (std::nothrow) pld_handle();
+  if (!h) return PLD_E_INVALID;
+  const pld_status st = init_into(h, cfg, n_layers, w, kv, head, workspace, ws_bytes);
+  if (st != PLD_OK) {
     delete h;
-    return PLD_E_HIP;
-  }
-  if (per_cu < 1) {
-    delete h;
-    return PLD_E_UNSUPPORTED;
+    return st;
   }
   *out = h;
   return PLD_OK;
@@ -1843,10 +1933,12 @@ struct HeadArgs {
   int32_t* out_tokens;
   const int32_t* drafts;
   int32_t* out_accepted;
+  double temperature;
+  uint64_t sample_seed;
 };
 
 static pld_status launch(pld_handle* h, int layer0, int n_layers, int n_tokens, int pos0, const void* in_hidden,
-                         void* out_hidden, hipStream_t s, HeadArgs hd = {0, -1, nullptr, nullptr, nullptr, nullptr}) {
+                         void* out_hidden, hipStream_t s, HeadArgs hd = {0, -1, nullptr, nullptr, nullptr, nullptr, 0.0, 0}) {
   KArgs a;
   memset(&a, 0, sizeof(a));
   a.c = h->kc;
@@ -1871,6 +1963,10 @@ static pld_status launch(pld_handle* h, int layer0, int n_layers, int n_tokens, 
   a.embed = h->embed;
   a.fnorm = h->fnorm;
   a.head = h->head;
+  a.hooks = h->hooks;
+  a.hook_seed = h->hook_seed;
+  a.temperature = hd.temperature;
+  a.sample_seed = hd.sample_seed;
   hipError_t e;
   if (h->coop) {
     void* args[] = {&a};
@@ -1880,6 +1976,7 @@ static pld_status launch(pld_handle* h, int layer0, int n_layers, int n_tokens, 
     e = hipLaunchKernel((const void*)h->fn, dim3(h->kc.nwg), dim3(BLOCK), args, h->lds_bytes, s);
   }
   if (e != hipSuccess) return PLD_E_HIP;
+  h->hooks &= ~PLD_HOOK_DROP_WG0;   // lasts one launch
   h->steps += (uint32_t)(n_layers * n_tokens);
   h->last_stream = s;
   return PLD_OK;
@@ -1914,17 +2011,22 @@ pld_status decode_layers_persistent(pld_handle* h, const pld_persistent_args* a,
   if (a->in_token < 0 && (!a->in_hidden || !aligned16(a->in_hidden))) return PLD_E_INVALID;
   if (!a->out_hidden || !aligned16(a->out_hidden)) return PLD_E_INVALID;
   if (a->start_pos < 0 || a->start_pos + n_pos > h->cfg.max_seq) return PLD_E_CAPACITY;
+  if (!(a->temperature >= 0.0) || !std::isfinite(a->temperature) || (a->temperature > 0.0 && !head))
+    return PLD_E_INVALID;
   HeadArgs hd{head ? 1 : 0, head ? a->in_token : -1, a->out_logits, a->out_tokens,
-              verify ? a->draft_tokens : nullptr, verify ? a->out_accepted : nullptr};
+              verify ? a->draft_tokens : nullptr, verify ? a->out_accepted : nullptr, a->temperature,
+              a->sample_seed};
   return launch(h, 0, h->n_layers, n_pos, a->start_pos, a->in_token >= 0 ? nullptr : a->in_hidden, a->out_hidden,
                 (hipStream_t)stream, hd);
 }
 
 pld_status decode_poll_status(pld_handle* h, pld_device_status* out) {
   if (!h || !out) return PLD_E_INVALID;
-  if (hipDeviceSynchronize() != hipSuccess) return PLD_E_HIP;
   int32_t st[8];
-  if (hipMemcpy(st, h->ws + h->off.status, sizeof(st), hipMemcpyDeviceToHost) != hipSuccess) return PLD_E_HIP;
+  if (hipStreamSynchronize(h->last_stream) != hipSuccess) return PLD_E_HIP;
+  if (hipMemcpyAsync(st, h->ws + h->off.status, sizeof(st), hipMemcpyDeviceToHost, h->last_stream) != hipSuccess ||
+      hipStreamSynchronize(h->last_stream) != hipSuccess)
+    return PLD_E_HIP;
   memset(out, 0, sizeof(*out));
   out->code = st[ST_CODE];
   out->stage = st[ST_STAGE];
@@ -1940,16 +2042,105 @@ pld_status decode_poll_status(pld_handle* h, pld_device_status* out) {
 
 pld_status decode_reset(pld_handle* h) {
   if (!h) return PLD_E_INVALID;
-  if (hipDeviceSynchronize() != hipSuccess) return PLD_E_HIP;
-  // status and LL buffers cleared; the step counter (LL epoch) keeps counting, so no word
-  // left by an aborted launch can carry an epoch that a later launch waits for
-  if (hipMemset(h->ws, 0, h->off.ll_end) != hipSuccess) return PLD_E_HIP;
-  if (hipDeviceSynchronize() != hipSuccess) return PLD_E_HIP;
+  // status and LL buffers cleared on the handle's stream; the step counter (LL epoch) keeps
+  // counting, so no word left by an aborted launch can carry an epoch that a later launch waits for
+  if (hipStreamSynchronize(h->last_stream) != hipSuccess) return PLD_E_HIP;
+  if (hipMemsetAsync(h->ws, 0, h->off.ll_end, h->last_stream) != hipSuccess) return PLD_E_HIP;
+  if (hipStreamSynchronize(h->last_stream) != hipSuccess) return PLD_E_HIP;
   h->bad = false;
   return PLD_OK;
 }
 
 void decode_layer_destroy(pld_handle* h) { delete h; }
+
+pld_status pld_set_test_hooks(pld_handle* h, int32_t flags, uint32_t seed) {
+  if (!h || (flags & ~(PLD_HOOK_DROP_WG0 | PLD_HOOK_DELAY))) return PLD_E_INVALID;
+  h->hooks = flags;
+  h->hook_seed = seed;
+  return PLD_OK;
+}
+
+// Host loop of speculative decoding over two handles that share the LM head and
+// embedding: the draft stack proposes n_draft tokens from the current position (one launch),
+// the target verifies them in one launch, the accepted drafts and the target's token after
+// them are kept, and both continue after the last kept token. Invariant at the top of the
+// loop: both caches hold correct rows for every position < p, and t is the (kept) token at p.
+// A verify writes target rows p .. p+nd (inputs t, d_0 .. d_{nd-1}); the draft launch wrote
+// draft rows p .. p+nd-1 (inputs t, d_0 .. d_{nd-2}); keeping m drafts needs rows up to p+m,
+// so only m == nd needs one more draft step (input d_{nd-1} at p+nd).
+pld_status decode_speculative(pld_handle* target, pld_handle* draft, const pld_spec_args* a, void* stream) {
+  if (!target || !draft || !a || !a->out_tokens || ((uintptr_t)a->out_tokens & 3u)) return PLD_E_INVALID;
+  if (target->bad || draft->bad) return PLD_E_STATE;
+  if (target->cfg.vocab <= 0 || draft->cfg.vocab != target->cfg.vocab || draft->embed != target->embed ||
+      draft->head.w != target->head.w)
+    return PLD_E_INVALID;   // the two stacks must share the vocabulary, embedding and head
+  if (a->n_tokens < 1 || a->n_draft < 1 || a->n_draft > 15 || a->in_token < 0 || a->in_token >= target->cfg.vocab)
+    return PLD_E_INVALID;
+  if (!(a->temperature >= 0.0) || !std::isfinite(a->temperature)) return PLD_E_INVALID;
+  const int last_pos = a->start_pos + a->n_tokens;   // no launch writes a row beyond this
+  if (a->start_pos < 0 || last_pos > target->cfg.max_seq || last_pos > draft->cfg.max_seq) return PLD_E_CAPACITY;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* sp = (int32_t*)(target->ws + target->off.spec);
+  int32_t* d_drafts = sp;            // [16]
+  int32_t* d_vtok = sp + 16;         // [16]
+  int32_t* d_acc = sp + 32;          // [1]
+  int32_t* d_junk = sp + 33;         // [1] output of a catch-up draft step
+  int p = a->start_pos, t = a->in_token, produced = 0, verifies = 0, acc_total = 0;
+  HeadArgs hd{1, 0, nullptr, nullptr, nullptr, nullptr, a->temperature, a->sample_seed};
+  pld_status st;
+  while (produced < a->n_tokens) {
+    const int remaining = a->n_tokens - produced;
+    if (remaining == 1) {   // one token left: a plain target step
+      HeadArgs h1 = hd;
+      h1.in_token = t;
+      h1.out_tokens = a->out_tokens + produced;
+      if ((st = launch(target, 0, target->n_layers, 1, p, nullptr, nullptr, s, h1)) != PLD_OK)
+        return st;
+      produced += 1;
+      break;
+    }
+    const int nd = std::min(a->n_draft, remaining - 1);
+    HeadArgs hdr = hd;
+    hdr.in_token = t;
+    hdr.out_tokens = d_drafts;
+    if ((st = launch(draft, 0, draft->n_layers, nd, p, nullptr, nullptr, s, hdr)) != PLD_OK)
+      return st;
+    HeadArgs hv = hd;
+    hv.in_token = t;
+    hv.out_tokens = d_vtok;
+    hv.drafts = d_drafts;
+    hv.out_accepted = d_acc;
+    if ((st = launch(target, 0, target->n_layers, nd + 1, p, nullptr, nullptr, s, hv)) != PLD_OK)
+      return st;
+    verifies++;
+    int32_t host[17];
+    if (hipMemcpyAsync(host, d_vtok, 17 * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return PLD_E_HIP;
+    const int m = host[16];
+    if (m < 0 || m > nd) return PLD_E_HIP;
+    const int keep = std::min(m + 1, remaining);
+    if (hipMemcpyAsync(a->out_tokens + produced, d_vtok, keep * sizeof(int32_t), hipMemcpyDeviceToDevice, s) !=
+        hipSuccess)
+      return PLD_E_HIP;
+    produced += keep;
+    acc_total += m;
+    if (m == nd && produced < a->n_tokens) {   // the draft cache lacks the row of its last draft
+      HeadArgs hc = hd;
+      hc.in_token = host[nd - 1];
+      hc.out_tokens = d_junk;
+      if ((st = launch(draft, 0, draft->n_layers, 1, p + nd, nullptr, nullptr, s, hc)) != PLD_OK)
+        return st;
+    }
+    p += m + 1;
+    t = host[m];
+  }
+  if (a->out_stats) {
+    a->out_stats[0] = verifies;
+    a->out_stats[1] = acc_total;
+  }
+  return PLD_OK;
+}
 
 pld_status pld_debug_buffer(pld_handle* h, const char* name, void** ptr, size_t* bytes) {
   if (!h || !name || !ptr || !bytes) return PLD_E_INVALID;
@@ -1960,6 +2151,7 @@ pld_status pld_debug_buffer(pld_handle* h, const char* name, void** ptr, size_t*
       {"o", h->off.o, (size_t)k.nh * (k.attn == PLD_ATTN_MLA ? k.vdim : k.hd) * 8},
       {"h2", h->off.h2, (size_t)k.H * 8},
       {"b", h->off.b_dbg, (size_t)k.H * 4},
+      {"f", h->off.f_dbg, (size_t)k.H * 4},
       {"logits", h->off.logits, (size_t)k.E * 32},
       {"sel", h->off.sel, (size_t)k.topk * 4},
       {"gates", h->off.gates, (size_t)k.topk * 4},
@@ -1978,6 +2170,10 @@ pld_status pld_debug_buffer(pld_handle* h, const char* name, void** ptr, size_t*
       {"ilist", h->off.ilist, (size_t)k.nwg * SEL_LIST * 8},
       {"ilo", h->off.ilo, (size_t)k.nwg * SEL_LIST * 4},
       {"itok", h->off.itok, (size_t)k.nwg * SEL_LIST * 4},
+      {"part", h->off.part, k.attn == PLD_ATTN_MLA ? (size_t)k.nh * k.cpg * (k.kv_lora + 2) * 8
+                                                    : (size_t)k.nh * k.cpg * (k.hd + 2) * 8},
+      {"kv", h->off.kv, (size_t)std::max(k.nkv * k.hd, 1) * 8},
+      {"amax", h->off.amax, (size_t)3 * std::max(k.nwg, 1) * 8},
   };
   for (auto& e : tab)
     if (!strcmp(e.n, name)) {

@@ -1590,7 +1590,9 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_mla(KArgs a) {
   cx.w = blockIdx.x;
   cx.nwg = gridDim.x;
   cx.status = wsp<uint32_t>(a, a.off.status);
+  cx.wacc = nullptr;
   const DLayer* layers = wsp<DLayer>(a, a.off.layers);
+  if ((a.hooks & PLD_HOOK_DROP_WG0) && cx.w == 0) return;   // test hook: a producer that never publishes
   {
     Lds L0 = carve(lds_raw, a.c);
     if (tid_opaque() < TR_SLOTS) L0.tr[tid_opaque()] = 0;
@@ -1626,7 +1628,9 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_mla(KArgs a) {
       asm volatile("" : "+s"(lds0));
       Lds L = carve(lds_raw + lds0, a.c);
       st.tr = L.tr;
+      cs.wacc = (a.trace && st.idx < a.trace_steps) ? L.tr + TR_WAIT : nullptr;
       stamp(as, cs, st, TR_START);
+      PLD_TEST_DELAY(a, cs.w, st.idx, 0);
       if (!stage_x_mla<SH>(cs, as, st, L)) return;
       if (!stage_q_mla<SH>(cs, as, st, L)) return;
       if constexpr (SH::SPARSE) {
@@ -1648,11 +1652,14 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_mla(KArgs a) {
       } else {
         if (!stage_absorb_mla<SH>(cs, as, st, L)) return;
       }
+      PLD_TEST_DELAY(a, cs.w, st.idx, 1);
       if (!stage_attn_mla<SH>(cs, as, st, L)) return;
       if (!stage_merge_mla<SH>(cs, as, st, L)) return;
       if (!stage_uv_mla<SH>(cs, as, st, L)) return;
       if (!stage_wo<SH>(cs, as, st, L)) return;
+      PLD_TEST_DELAY(a, cs.w, st.idx, 2);
       if (!stage_ffn<SH>(cs, as, st, L)) return;
+      PLD_TEST_DELAY(a, cs.w, st.idx, 3);
       if (!stage_down<SH>(cs, as, st, L, last ? as.out_hidden : nullptr)) return;
       if constexpr (SH::FP8) {
         if (a.head_on && li == a.n_layers - 1) {

@@ -375,3 +375,28 @@ def first_token(model: ModelShape, seed=0, step=0) -> int:
 def draft_tokens(model: ModelShape, n: int, seed=0, step=0) -> np.ndarray:
     r = raw_u64(seed, tensor_id("token", 1, step), np.arange(n, dtype=np.uint64))
     return (r % np.uint64(model.vocab)).astype(np.int64)
+
+
+def padded_cache(shape: LayerShape, seed=0, layer=0, fill_len=None) -> dict:
+    """Host copy of a prefilled cache with max_seq rows: positions 0..fill_len-1 (default
+    cache_len) hold the seeded rows, the rest zero (the layout the device fill writes)."""
+    n = shape.cache_len if fill_len is None else fill_len
+    out = {}
+    if shape.attn == "gqa":
+        pos = np.arange(n)
+        for kind, key in (("k_cache", "k"), ("v_cache", "v")):
+            z = np.zeros((shape.n_kv_heads, shape.max_seq, shape.head_dim), np.uint16)
+            for g in range(shape.n_kv_heads):
+                z[g, :n] = kv_rows(shape, kind, g, pos, seed, layer)
+            out[key] = z
+    else:
+        z = np.zeros((shape.max_seq, shape.latent_dim), np.uint16)
+        z[:n] = latent_rows(shape, np.arange(n), seed, layer)
+        out["latent"] = z
+        if shape.index_topk:
+            codes = np.zeros((shape.max_seq, shape.index_dim), np.uint8)
+            scales = np.zeros(shape.max_seq, np.float32)
+            c, sc = index_key_rows(shape, np.arange(n), seed, layer)
+            codes[:n], scales[:n] = c, sc
+            out["index_codes"], out["index_scales"] = codes, scales
+    return out

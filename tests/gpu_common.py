@@ -30,26 +30,7 @@ def bf16_tensor_to_f64(t) -> np.ndarray:
 
 def host_cache(s, seed=0, layer=0, fill_len=None):
     """Host copy of a prefilled cache, padded to max_seq rows (positions >= fill_len are zero)."""
-    n = s.cache_len if fill_len is None else fill_len
-    out = {}
-    if s.attn == "gqa":
-        pos = np.arange(n)
-        for kind, key in (("k_cache", "k"), ("v_cache", "v")):
-            z = np.zeros((s.n_kv_heads, s.max_seq, s.head_dim), np.uint16)
-            for g in range(s.n_kv_heads):
-                z[g, :n] = gen.kv_rows(s, kind, g, pos, seed, layer)
-            out[key] = z
-    else:
-        z = np.zeros((s.max_seq, s.latent_dim), np.uint16)
-        z[:n] = gen.latent_rows(s, np.arange(n), seed, layer)
-        out["latent"] = z
-        if s.index_topk:
-            codes = np.zeros((s.max_seq, s.index_dim), np.uint8)
-            scales = np.zeros(s.max_seq, np.float32)
-            c, sc = gen.index_key_rows(s, np.arange(n), seed, layer)
-            codes[:n], scales[:n] = c, sc
-            out["index_codes"], out["index_scales"] = codes, scales
-    return out
+    return gen.padded_cache(s, seed, layer, fill_len)
 
 
 def oracle_step(s, seed, layer, cache, x_bits, pos, weights=None):
@@ -57,3 +38,29 @@ def oracle_step(s, seed, layer, cache, x_bits, pos, weights=None):
     rec = OL.decode_layer(s, W, cache, x_bits, pos)
     OL.append_to_cache(s, cache, rec, pos)
     return rec
+
+
+# Direct bars on the two residual branches and the expert activations, each relative to its
+# own max-norm (the hidden state is dominated by the residual, so a bar on it alone would
+# admit a large error in y or f). y = h2 - x is recovered from the fp32 h2 words (the
+# subtraction is exact to an fp32 step of h2, far below these bars); f is the kernel's fp32
+# FFN output before the residual add; m[slot] = silu(gate) * up of each expert slot.
+BAR_Y = 5e-3
+BAR_F = 5e-3
+BAR_M = 5e-3
+
+
+def check_branches(dec, s, rec, x_bits, tag, bar_y=BAR_Y, bar_f=BAR_F, bar_m=BAR_M):
+    x = nx.bf16_to_f64(np.asarray(x_bits).view(np.uint16))
+    h2 = dec.debug("h2").cpu().numpy().astype(np.float64)
+    e_y = rel_err(h2 - x, rec["y"])
+    f = dec.debug("f").cpu().numpy().astype(np.float64)
+    e_f = rel_err(f, rec["f"])
+    slots = s.top_k + s.n_shared if s.ffn == "moe" else 1
+    m = dec.debug("m").cpu().numpy().astype(np.float64).reshape(slots, s.inter)
+    e_m = [rel_err(m[j], rec["m"][j]) for j in range(slots)]
+    say(f"{tag}: y {e_y:.2e} (|y| {np.abs(rec['y']).max():.3f}), f {e_f:.2e} (|f| {np.abs(rec['f']).max():.3f}), "
+        f"m max {max(e_m):.2e}")
+    assert e_y < bar_y, f"{tag}: W_O output y rel err {e_y}"
+    assert e_f < bar_f, f"{tag}: FFN output f rel err {e_f}"
+    assert max(e_m) < bar_m, f"{tag}: expert activations m rel err {e_m}"

@@ -57,6 +57,9 @@ int main(void) {
   P(pld_config, eps) P(pld_config, rope_base) P(pld_config, vocab) P(pld_config, max_seq)
   P(pld_layer_weights, wo) P(pld_layer_weights, router) P(pld_layer_weights, w_down)
   P(pld_persistent_args, in_hidden) P(pld_persistent_args, out_accepted)
+  P(pld_persistent_args, temperature) P(pld_persistent_args, sample_seed)
+  printf("pld_spec_args %zu\n", sizeof(pld_spec_args));
+  P(pld_spec_args, temperature) P(pld_spec_args, out_tokens) P(pld_spec_args, out_stats)
   return 0;
 }
 '''
@@ -78,11 +81,12 @@ def test_ctypes_struct_layout_matches_c():
     assert lay["pld_head_weights"] == ctypes.sizeof(pld.PldHeadWeights)
     assert lay["pld_device_status"] == ctypes.sizeof(pld.PldDeviceStatus)
     assert lay["pld_persistent_args"] == ctypes.sizeof(pld.PldPersistentArgs)
+    assert lay["pld_spec_args"] == ctypes.sizeof(pld.PldSpecArgs)
     for key, off in lay.items():
         if "." in key:
             T, f = key.split(".")
             cls = {"pld_config": pld.PldConfig, "pld_layer_weights": pld.PldLayerWeights,
-                   "pld_persistent_args": pld.PldPersistentArgs}[T]
+                   "pld_persistent_args": pld.PldPersistentArgs, "pld_spec_args": pld.PldSpecArgs}[T]
             assert getattr(cls, f).offset == off, key
 
 

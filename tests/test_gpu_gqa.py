@@ -14,7 +14,7 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
-from gpu_common import TOL, bf16_tensor_to_f64, host_cache, oracle_step, rel_err, say  # noqa: E402
+from gpu_common import TOL, bf16_tensor_to_f64, check_branches, host_cache, oracle_step, rel_err, say  # noqa: E402
 from oracle import numerics as nx  # noqa: E402
 from synth import configs, gen  # noqa: E402
 
@@ -75,7 +75,7 @@ def test_device_generator_matches_host():
     assert np.array_equal(x.cpu().numpy().view(np.uint16), gen.input_hidden(configs.C2, 0, 3))
 
 
-def _check_layer(dec, s, rec, out, pos, cache_dev, tag):
+def _check_layer(dec, s, rec, out, pos, cache_dev, tag, x_bits):
     err = rel_err(bf16_tensor_to_f64(out), rec["out"])
     say(f"{tag}: out rel err {err:.3e}")
     assert err < TOL, f"{tag}: out rel err {err}"
@@ -98,6 +98,7 @@ def _check_layer(dec, s, rec, out, pos, cache_dev, tag):
         assert list(sel) == list(rec["router_sel"]), f"{tag}: router selection {sel} vs {rec['router_sel']}"
         gates = dec.debug("gates").cpu().numpy()
         assert np.allclose(gates, rec["gates"], rtol=1e-3, atol=1e-5), tag
+    check_branches(dec, s, rec, x_bits, tag)
 
 
 @pytest.mark.parametrize("positions", [[128], [128, 129, 130], [0], [5, 6], [255]])
@@ -111,8 +112,9 @@ def test_tiny_dense_layer_parity(positions):
     for i, pos in enumerate(positions):
         x = sdev.input_hidden(s, 0, i)
         out = _run_step(dec, s, 0, x, pos)
-        rec = oracle_step(s, 0, 0, hc, gen.input_hidden(s, 0, i), pos)
-        _check_layer(dec, s, rec, out, pos, Cs[0], f"tiny pos {pos}")
+        xb = gen.input_hidden(s, 0, i)
+        rec = oracle_step(s, 0, 0, hc, xb, pos)
+        _check_layer(dec, s, rec, out, pos, Cs[0], f"tiny pos {pos}", xb)
 
 
 def test_gqa_moe_layer_parity_full_cache():
@@ -123,8 +125,9 @@ def test_gqa_moe_layer_parity_full_cache():
     from synth import device as sdev
     x = sdev.input_hidden(s, 0, 0)
     out = _run_step(dec, s, 0, x, s.cache_len)
-    rec = oracle_step(s, 0, 0, host_cache(s), gen.input_hidden(s, 0, 0), s.cache_len)
-    _check_layer(dec, s, rec, out, s.cache_len, Cs[0], "gqa-moe pos 8192")
+    xb = gen.input_hidden(s, 0, 0)
+    rec = oracle_step(s, 0, 0, host_cache(s), xb, s.cache_len)
+    _check_layer(dec, s, rec, out, s.cache_len, Cs[0], "gqa-moe pos 8192", xb)
 
 
 @pytest.mark.parametrize("cache_len,positions", [(300, [300, 301]), (37, [0, 37])])
@@ -139,8 +142,9 @@ def test_gqa_moe_layer_parity_ragged_cache(cache_len, positions):
     for i, pos in enumerate(positions):
         x = sdev.input_hidden(s, 1, i)
         out = _run_step(dec, s, 0, x, pos)
-        rec = oracle_step(s, 1, 0, hc, gen.input_hidden(s, 1, i), pos, weights=W)
-        _check_layer(dec, s, rec, out, pos, Cs[0], f"gqa-moe cache {cache_len} pos {pos}")
+        xb = gen.input_hidden(s, 1, i)
+        rec = oracle_step(s, 1, 0, hc, xb, pos, weights=W)
+        _check_layer(dec, s, rec, out, pos, Cs[0], f"gqa-moe cache {cache_len} pos {pos}", xb)
 
 
 def test_gqa_moe_two_layer_stack_one_launch():

@@ -14,7 +14,7 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
-from gpu_common import TOL, bf16_tensor_to_f64, host_cache, oracle_step, rel_err, say  # noqa: E402
+from gpu_common import TOL, bf16_tensor_to_f64, check_branches, host_cache, oracle_step, rel_err, say  # noqa: E402
 from oracle import numerics as nx  # noqa: E402
 from synth import configs, gen  # noqa: E402
 
@@ -43,7 +43,7 @@ def _run_step(dec, s, layer, x, pos):
     return out
 
 
-def _check_layer(dec, s, rec, out, pos, cache_dev, tag):
+def _check_layer(dec, s, rec, out, pos, cache_dev, tag, x_bits):
     err = rel_err(bf16_tensor_to_f64(out), rec["out"])
     say(f"{tag}: out rel err {err:.3e}")
     assert err < TOL, f"{tag}: out rel err {err}"
@@ -76,6 +76,7 @@ def _check_layer(dec, s, rec, out, pos, cache_dev, tag):
     assert list(sel) == list(rec["router_sel"]), f"{tag}: router selection {sel} vs {rec['router_sel']}"
     gates = dec.debug("gates").cpu().numpy()
     assert np.allclose(gates, rec["gates"], rtol=1e-3, atol=1e-5), tag
+    check_branches(dec, s, rec, x_bits, tag)
 
 
 @pytest.mark.parametrize("cache_len,positions", [(300, [300, 301]), (37, [0, 37])])
@@ -90,20 +91,43 @@ def test_mla_fp8_layer_parity_small_cache(cache_len, positions):
     for i, pos in enumerate(positions):
         x = sdev.input_hidden(s, 0, i)
         out = _run_step(dec, s, 0, x, pos)
-        rec = oracle_step(s, 0, 0, hc, gen.input_hidden(s, 0, i), pos, weights=W)
-        _check_layer(dec, s, rec, out, pos, Cs[0], f"mla cache {cache_len} pos {pos}")
+        xb = gen.input_hidden(s, 0, i)
+        rec = oracle_step(s, 0, 0, hc, xb, pos, weights=W)
+        _check_layer(dec, s, rec, out, pos, Cs[0], f"mla cache {cache_len} pos {pos}", xb)
 
 
-def test_mla_fp8_layer_parity_full_cache():
+def test_mla_fp8_layer_parity_full_cache_chain():
+    """The 8192-token cache, chained launches at positions 8192 and 8193. From 8193 on the
+    history rows no longer split into whole 32-row sub-blocks of 64 chunks: one chunk holds
+    129 rows (a fifth, one-row sub-block), and row 8192 was written by the previous launch."""
     _need_gpu()
     s = configs.C3
-    say("case: MLA FP8 layer, 8192-token cache, pos 8192")
+    say("case: MLA FP8 layer, 8192-token cache, chained positions 8192, 8193")
+    dec, Ws, Cs = _decoder(s, [(0, 0)])
+    from synth import device as sdev
+    hc = host_cache(s)
+    W = gen.LayerWeights(s, 0, 0)
+    for i, pos in enumerate((8192, 8193)):
+        x = sdev.input_hidden(s, 0, i)
+        out = _run_step(dec, s, 0, x, pos)
+        xb = gen.input_hidden(s, 0, i)
+        rec = oracle_step(s, 0, 0, hc, xb, pos, weights=W)
+        _check_layer(dec, s, rec, out, pos, Cs[0], f"mla pos {pos}", xb)
+
+
+def test_mla_fp8_layer_parity_ragged_chunks():
+    """An 8200-token cache at position 8200: 8200 history rows over 64 chunks, eight of
+    them 129 rows long."""
+    _need_gpu()
+    s = configs.scaled(configs.C3, cache_len=8200, max_seq=8264)
+    say("case: MLA FP8 layer, 8200-token cache, pos 8200")
     dec, Ws, Cs = _decoder(s, [(0, 0)])
     from synth import device as sdev
     x = sdev.input_hidden(s, 0, 0)
     out = _run_step(dec, s, 0, x, s.cache_len)
-    rec = oracle_step(s, 0, 0, host_cache(s), gen.input_hidden(s, 0, 0), s.cache_len)
-    _check_layer(dec, s, rec, out, s.cache_len, Cs[0], "mla pos 8192")
+    xb = gen.input_hidden(s, 0, 0)
+    rec = oracle_step(s, 0, 0, host_cache(s), xb, s.cache_len)
+    _check_layer(dec, s, rec, out, s.cache_len, Cs[0], "mla pos 8200", xb)
 
 
 def test_mla_fp8_two_layer_stack_one_launch():

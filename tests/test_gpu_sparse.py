@@ -20,7 +20,7 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
-from gpu_common import TOL, bf16_tensor_to_f64, host_cache, oracle_step, rel_err, say  # noqa: E402
+from gpu_common import TOL, bf16_tensor_to_f64, check_branches, host_cache, oracle_step, rel_err, say  # noqa: E402
 from oracle import numerics as nx  # noqa: E402
 from synth import configs, gen  # noqa: E402
 
@@ -86,7 +86,7 @@ def _check_indexer(dec, s, rec, pos, cache_dev, tag):
     say(f"{tag}: indexer exact (q_I, w, k_I, key row, {T} scores, {k} selected)")
 
 
-def _check_layer(dec, s, rec, out, pos, cache_dev, tag):
+def _check_layer(dec, s, rec, out, pos, cache_dev, tag, x_bits):
     _check_indexer(dec, s, rec, pos, cache_dev, tag)
     err = rel_err(bf16_tensor_to_f64(out), rec["out"])
     o = dec.debug("o").cpu().numpy().reshape(s.n_heads, s.v_dim)
@@ -99,6 +99,7 @@ def _check_layer(dec, s, rec, out, pos, cache_dev, tag):
     assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -7 + 1e-30), f"{tag}: latent row"
     sel = dec.debug("sel").cpu().numpy()
     assert list(sel) == list(rec["router_sel"]), f"{tag}: router selection {sel} vs {rec['router_sel']}"
+    check_branches(dec, s, rec, x_bits, tag)
 
 
 @pytest.mark.parametrize("cache_len,topk,positions", [(300, 64, [300, 301]), (37, 2048, [0, 37])])
@@ -113,8 +114,9 @@ def test_sparse_mla_layer_small_cache(cache_len, topk, positions):
     for i, pos in enumerate(positions):
         x = sdev.input_hidden(s, 0, i)
         out = _run_step(dec, s, 0, x, pos)
-        rec = oracle_step(s, 0, 0, hc, gen.input_hidden(s, 0, i), pos, weights=W)
-        _check_layer(dec, s, rec, out, pos, Cs[0], f"sparse cache {cache_len} top-{topk} pos {pos}")
+        xb = gen.input_hidden(s, 0, i)
+        rec = oracle_step(s, 0, 0, hc, xb, pos, weights=W)
+        _check_layer(dec, s, rec, out, pos, Cs[0], f"sparse cache {cache_len} top-{topk} pos {pos}", xb)
 
 
 def test_sparse_mla_layer_full_cache():
@@ -125,8 +127,9 @@ def test_sparse_mla_layer_full_cache():
     from synth import device as sdev
     x = sdev.input_hidden(s, 0, 0)
     out = _run_step(dec, s, 0, x, s.cache_len)
-    rec = oracle_step(s, 0, 0, host_cache(s), gen.input_hidden(s, 0, 0), s.cache_len)
-    _check_layer(dec, s, rec, out, s.cache_len, Cs[0], "sparse pos 32768")
+    xb = gen.input_hidden(s, 0, 0)
+    rec = oracle_step(s, 0, 0, host_cache(s), xb, s.cache_len)
+    _check_layer(dec, s, rec, out, s.cache_len, Cs[0], "sparse pos 32768", xb)
 
 
 def test_sparse_selection_ties_cut_by_index():
@@ -146,7 +149,7 @@ def test_sparse_selection_ties_cut_by_index():
     npos = int(np.count_nonzero(rec["index_score"] > 0))
     say(f"  {npos} tokens score above 0; the rest of the 64 come from the tie")
     assert npos < 64 and np.count_nonzero(rec["index_score"] == 0) >= 250
-    _check_layer(dec, s, rec, out, 300, Cs[0], "ties")
+    _check_layer(dec, s, rec, out, 300, Cs[0], "ties", gen.input_hidden(s, 0, 0))
 
 
 def test_sparse_selection_near_equal_cluster():
@@ -177,7 +180,7 @@ def test_sparse_selection_near_equal_cluster():
     hi = (cl.view(np.uint64) >> np.uint64(32))
     say(f"  cluster: {np.unique(cl).size} distinct scores, {np.unique(hi).size} distinct high halves; "
         f"{np.count_nonzero(rec['index_sel'] < 200)} of 64 chosen from it")
-    _check_layer(dec, s, rec, out, 300, Cs[0], "cluster")
+    _check_layer(dec, s, rec, out, 300, Cs[0], "cluster", gen.input_hidden(s, 0, 0))
 
 
 def test_sparse_two_layer_stack_one_launch():
@@ -227,7 +230,7 @@ def _full_cache_case(tag, edit):
     from synth import device as sdev
     out = _run_step(dec, s, 0, sdev.input_hidden(s, 0, 0), s.cache_len)
     rec = oracle_step(s, 0, 0, hc, gen.input_hidden(s, 0, 0), s.cache_len)
-    _check_layer(dec, s, rec, out, s.cache_len, Cs[0], tag)
+    _check_layer(dec, s, rec, out, s.cache_len, Cs[0], tag, gen.input_hidden(s, 0, 0))
     return rec
 
 

@@ -195,6 +195,45 @@ def test_sigmoid_gates_and_zero_bias_reduces_to_logit_topk():
     assert list(sel0) == sorted(range(s.n_experts), key=lambda i: (-rec0["router_logits"][i], i))[: s.top_k]
 
 
+def test_biased_router_selection_and_gates_by_hand():
+    """Biased-score routing with a nonzero bias, worked by hand. Logits r (via b = e_0 and a
+    router whose first column holds r) and biases over four live experts (the other four
+    have r = -6, bias -1 and never compete):
+
+        expert        0       1       2       3
+        r           6.0     0.0     0.5    -0.5
+        bias       -0.6     0.0     0.3     0.2
+        sigmoid(r) .9975   .5000   .6225   .3775
+        sig + bias .3975   .5000   .9225   .5775   -> top-2 = [2, 3]
+        r + bias    5.4     0.0     0.8    -0.3    -> top-2 = {0, 2}  (a misreading)
+        sigmoid(r) alone                           -> top-2 = {0, 2}  (bias ignored)
+
+    The gates are the unbiased sigmoid scores renormalised over the selection:
+    sigmoid(0.5) / (sigmoid(0.5) + sigmoid(-0.5)) = sigmoid(0.5), since sigmoid(x) +
+    sigmoid(-x) = 1; so gates = [sigmoid(0.5), sigmoid(-0.5)] = [0.62245933, 0.37754067].
+    The selection also equals a brute-force full sort of sigmoid(r) + bias."""
+    s = tiny_mla(n_experts=8, top_k=2)
+    r = np.array([6.0, 0.0, 0.5, -0.5, -6.0, -6.0, -6.0, -6.0])
+    bias = np.array([-0.6, 0.0, 0.3, 0.2, -1.0, -1.0, -1.0, -1.0], np.float32)
+    wr = np.zeros((s.n_experts, s.hidden), np.float32)
+    wr[:, 0] = r                                   # bf16-exact values
+    W = DictWeights(s, overrides={("router", None): wr}, bias=bias)
+    b = np.zeros(s.hidden)
+    b[0] = 1.0
+    rec = {}
+    sel, gates = OL.route(s, W, b, rec)
+    assert np.array_equal(rec["router_logits"], r)
+    assert list(sel) == [2, 3]
+    assert np.allclose(gates, [0.6224593312018546, 0.3775406687981454], rtol=0, atol=1e-15)
+    # the misreadings pick another set
+    assert set(np.argsort(-(r + bias))[:2]) == {0, 2}
+    assert set(np.argsort(-(1 / (1 + np.exp(-r))))[:2]) == {0, 2}
+    # brute force: a full sort of every expert's biased score, ties to the lower index
+    key = 1 / (1 + np.exp(-r)) + bias.astype(np.float64)
+    order = sorted(range(s.n_experts), key=lambda i: (-key[i], i))
+    assert list(sel) == order[:2]
+
+
 # --------------------------------------------------------------------------- attention
 def _tiny_case(s, seed=0):
     W = gen.LayerWeights(s, seed, 0)
@@ -511,3 +550,46 @@ def test_expected_union_of_routed_experts_by_enumeration():
             tot += len(set().union(*combo))
         mean = tot / len(subsets) ** n
         assert abs(mean - accounting.expected_union_experts(E, k, n)) < 1e-12, (E, k, n)
+
+
+# --------------------------------------------------------------------------- sampling
+def test_splitmix_reference_outputs_and_second_implementation():
+    """The sampler's mixer against the published SplitMix64 outputs from state 0 (Vigna's
+    splitmix64.c: the state advances by G, the output is the mix of the state) and against the
+    input generator's independent implementation of the same mixer."""
+    G = 0x9E3779B97F4A7C15
+    ref = [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+    for k, want in enumerate(ref, start=1):
+        assert int(OM.splitmix_mix(np.uint64((k * G) & ((1 << 64) - 1)))) == want
+    z = np.random.default_rng(3).integers(0, 2**63, 1000, dtype=np.int64).astype(np.uint64) * np.uint64(2)
+    assert np.array_equal(OM.splitmix_mix(z), gen._mix(z))
+
+
+def test_sampling_uniforms_range_and_moments():
+    u = np.concatenate([OM.sample_uniforms(7, p, 4096) for p in range(8)])
+    assert np.all(u > 0) and np.all(u < 1)
+    assert abs(u.mean() - 0.5) < 4 * math.sqrt(1 / 12 / u.size)
+    assert abs(u.var() - 1 / 12) < 0.01
+    # distinct positions and seeds give different streams
+    assert not np.array_equal(OM.sample_uniforms(7, 0, 64), OM.sample_uniforms(7, 1, 64))
+    assert not np.array_equal(OM.sample_uniforms(7, 0, 64), OM.sample_uniforms(8, 0, 64))
+
+
+def test_gumbel_max_sampling_follows_softmax():
+    """Over many positions the sampled tokens follow softmax(logits / T) (chi-square), T = 0
+    is the argmax, a constant added to every logit changes nothing, and a logit gap far above
+    the Gumbel spread always wins."""
+    from scipy.stats import chisquare
+    lg = np.array([1.0, 0.0, -1.0, 2.0, 0.5])
+    T = 0.7
+    p = np.exp(lg / T) / np.exp(lg / T).sum()
+    n = 20000
+    toks = np.array([OM.sample_token(lg, T, 11, pos) for pos in range(n)])
+    counts = np.bincount(toks, minlength=lg.size)
+    assert chisquare(counts, p * n).pvalue > 1e-4
+    assert OM.sample_token(lg, 0.0, 11, 5) == 3
+    for pos in range(50):
+        assert OM.sample_token(lg + 123.25, T, 11, pos) == OM.sample_token(lg, T, 11, pos)
+    big = np.zeros(1000)
+    big[417] = 200.0
+    assert all(OM.sample_token(big, 1.0, 5, pos) == 417 for pos in range(50))
