@@ -186,6 +186,24 @@ pld_status decode_layer_init(const pld_config* cfg, int32_t n_layers, const pld_
                              const pld_kv_cache* kv, const pld_head_weights* head, void* workspace,
                              size_t ws_bytes, pld_handle** out);
 
+/* decode_layer_init for callers that cannot allocate device memory (code that later runs
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same validation and set-up, but the workspace is the library's own static device array
+ * of 32 MiB per GPU (held from the first use on a GPU until the process ends), so no
+ * workspace argument is taken, and nothing is allocated on the device or the host.
+ *   Returns PLD_E_CAPACITY when pld_workspace_bytes(cfg, n_layers) exceeds 32 MiB (every
+ *   single-layer workload of this library fits; so does a 24-layer stack of the FP8 MLA
+ *   layer), else the errors of decode_layer_init.
+ *   The handle is library storage, one per GPU: every call on a GPU returns the same
+ *   handle and re-initialises it (and that GPU's array; the status and handoff buffers are
+ *   cleared, the step epoch keeps counting), so an earlier handle of the same GPU now runs
+ *   the new configuration. Launches of that handle that overlap with a re-initialisation
+ *   or with each other race. decode_layer_destroy on it does nothing. Synchronous; it is
+ *   not itself capturable, but the launches on the handle are plain kernel launches.
+ *   cfg, n_layers, w, kv, head: as for decode_layer_init; out receives the handle. */
+pld_status decode_layer_init_static(const pld_config* cfg, int32_t n_layers, const pld_layer_weights* w,
+                                    const pld_kv_cache* kv, const pld_head_weights* head, pld_handle** out);
+
 /* Decode one token through layer `layer` in one launch: RMSNorm -> projections ->
  * RoPE + cache append at row `pos` -> attention over rows 0..pos -> output projection +
  * residual -> RMSNorm -> router top-k -> routed + shared SwiGLU experts -> residual.
@@ -262,7 +280,8 @@ pld_status decode_poll_status(pld_handle* h, pld_device_status* out);
  * again (synchronous). The step epoch keeps counting across resets. */
 pld_status decode_reset(pld_handle* h);
 
-/* Free the host-side handle. Device memory stays with the caller. NULL is ignored. */
+/* Free the host-side handle. Device memory stays with the caller. NULL and handles of
+ * decode_layer_init_static are ignored. */
 void decode_layer_destroy(pld_handle* h);
 
 /* Static description of a status code. */

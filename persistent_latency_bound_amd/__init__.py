@@ -24,7 +24,7 @@ PLD_ROUTER_SOFTMAX_TOPK, PLD_ROUTER_SIGMOID_BIAS = 0, 1
 EXPORTS = (
     "pld_workspace_bytes", "decode_layer_init", "decode_step", "decode_layers_persistent", "decode_poll_status",
     "decode_reset", "decode_layer_destroy", "pld_status_string", "pld_debug_buffer", "pld_launch_shape",
-    "pld_set_watchdog_us", "pld_set_trace", "pld_set_test_hooks", "decode_speculative",
+    "pld_set_watchdog_us", "pld_set_trace", "pld_set_test_hooks", "decode_layer_init_static", "decode_speculative",
 )
 PLD_HOOK_DROP_WG0, PLD_HOOK_DELAY = 1, 2
 
@@ -92,6 +92,9 @@ def lib():
         L.decode_layer_init.argtypes = [ctypes.POINTER(PldConfig), i32, ctypes.POINTER(PldLayerWeights),
                                         ctypes.POINTER(PldKvCache), ctypes.POINTER(PldHeadWeights), vp,
                                         ctypes.c_size_t, ctypes.POINTER(vp)]
+        L.decode_layer_init_static.argtypes = [ctypes.POINTER(PldConfig), i32, ctypes.POINTER(PldLayerWeights),
+                                               ctypes.POINTER(PldKvCache), ctypes.POINTER(PldHeadWeights),
+                                               ctypes.POINTER(vp)]
         L.decode_step.argtypes = [vp, i32, vp, i32, vp, vp]
         L.decode_speculative.argtypes = [vp, vp, ctypes.POINTER(PldSpecArgs), vp]
         L.decode_layers_persistent.argtypes = [vp, ctypes.POINTER(PldPersistentArgs), vp]
@@ -106,7 +109,7 @@ def lib():
         L.pld_set_watchdog_us.argtypes = [vp, ctypes.c_int64]
         L.pld_set_trace.argtypes = [vp, vp, ctypes.c_size_t]
         L.pld_set_test_hooks.argtypes = [vp, i32, ctypes.c_uint32]
-        for f in ("decode_layer_init", "decode_speculative", "decode_step", "decode_layers_persistent", "decode_poll_status",
+        for f in ("decode_layer_init", "decode_layer_init_static", "decode_speculative", "decode_step", "decode_layers_persistent", "decode_poll_status",
                   "decode_reset", "pld_debug_buffer", "pld_launch_shape", "pld_set_watchdog_us", "pld_set_trace",
                   "pld_set_test_hooks"):
             getattr(L, f).restype = i32
@@ -180,17 +183,21 @@ class Decoder:
     """One decode handle over a stack of layers (weights and caches are caller-owned torch tensors)."""
 
     def __init__(self, shape, layers: Sequence[dict], caches: Sequence[dict], head: Optional[dict] = None,
-                 vocab: int = 0):
+                 vocab: int = 0, static: bool = False):
+        """static=True: decode_layer_init_static (the library's own device array, no workspace
+        allocation; one such handle per GPU, re-initialised by every such call)."""
         import torch
 
         self.shape = shape
         self.cfg = config_from_shape(shape, vocab)
         n = len(layers)
         self._keep = (list(layers), list(caches), head)   # keep the tensors alive
-        ws = lib().pld_workspace_bytes(ctypes.byref(self.cfg), n)
-        if ws == 0:
-            raise PldError(PLD_E_UNSUPPORTED, "pld_workspace_bytes")
-        self.workspace = torch.zeros(ws, dtype=torch.uint8, device="cuda")
+        self.static = static
+        if not static:
+            ws = lib().pld_workspace_bytes(ctypes.byref(self.cfg), n)
+            if ws == 0:
+                raise PldError(PLD_E_UNSUPPORTED, "pld_workspace_bytes")
+            self.workspace = torch.zeros(ws, dtype=torch.uint8, device="cuda")
         arr_w = (PldLayerWeights * n)(*[layer_struct(W) for W in layers])
         arr_c = (PldKvCache * n)(*[cache_struct(C) for C in caches])
         hp = None
@@ -201,8 +208,12 @@ class Decoder:
             h.head = _mat(head["head"])
             hp = ctypes.byref(h)
         self.handle = vp()
-        check(lib().decode_layer_init(ctypes.byref(self.cfg), n, arr_w, arr_c, hp, self.workspace.data_ptr(), ws,
-                                      ctypes.byref(self.handle)), "decode_layer_init")
+        if static:
+            check(lib().decode_layer_init_static(ctypes.byref(self.cfg), n, arr_w, arr_c, hp,
+                                                 ctypes.byref(self.handle)), "decode_layer_init_static")
+        else:
+            check(lib().decode_layer_init(ctypes.byref(self.cfg), n, arr_w, arr_c, hp, self.workspace.data_ptr(), ws,
+                                          ctypes.byref(self.handle)), "decode_layer_init")
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -274,6 +285,8 @@ class Decoder:
 
     def debug_raw(self, name: str):
         """The workspace bytes of a named buffer as a uint8 view (not a copy)."""
+        if self.static:
+            raise RuntimeError("the workspace of a static handle is the library's own array; no debug view")
         p, nb = vp(), ctypes.c_size_t()
         check(lib().pld_debug_buffer(self.handle, name.encode(), ctypes.byref(p), ctypes.byref(nb)), "pld_debug_buffer")
         off = p.value - self.workspace.data_ptr()
@@ -282,6 +295,8 @@ class Decoder:
     def debug(self, name: str, dtype=None):
         """Copy of an intermediate left in the workspace by the last launch (after a sync)."""
         import torch
+        if self.static:
+            raise RuntimeError("the workspace of a static handle is the library's own array; no debug view")
         p, nb = vp(), ctypes.c_size_t()
         check(lib().pld_debug_buffer(self.handle, name.encode(), ctypes.byref(p), ctypes.byref(nb)), "pld_debug_buffer")
         off = p.value - self.workspace.data_ptr()

@@ -1511,6 +1511,7 @@ struct pld_handle {
   DMat head;
   int hooks;               // test hooks for the next launches (PLD_HOOK_DROP_WG0 lasts one launch)
   uint32_t hook_seed;
+  bool is_static;          // made by decode_layer_init_static: library storage, never freed
 };
 
 namespace {
@@ -1907,7 +1908,17 @@ pld_status init_into(pld_handle* h, const pld_config* cfg, int32_t n_layers, con
   return PLD_OK;
 }
 
+constexpr size_t STATIC_WS_BYTES = (size_t)32 << 20;
+constexpr int MAX_DEVICES = 64;
+void* scratch_dev[MAX_DEVICES];         // device address of `scratch` on each device, once looked up
+pld_handle static_handle[MAX_DEVICES];  // the handle decode_layer_init_static returns on each device
+
 }  // namespace
+
+// Workspace of decode_layer_init_static (no allocation): 32 MiB that every device the library
+// runs on holds until the process ends. In host code `scratch` names a host-side stand-in;
+// its device address on the current device comes from hipGetSymbolAddress (scratch_dev[]).
+static __device__ __align__(256) uint8_t scratch[STATIC_WS_BYTES];
 
 extern "C" {
 
@@ -1923,6 +1934,35 @@ pld_status decode_layer_init(const pld_config* cfg, int32_t n_layers, const pld_
     delete h;
     return st;
   }
+  *out = h;
+  return PLD_OK;
+}
+
+pld_status decode_layer_init_static(const pld_config* cfg, int32_t n_layers, const pld_layer_weights* w,
+                                    const pld_kv_cache* kv, const pld_head_weights* head, pld_handle** out) {
+  if (!out) return PLD_E_INVALID;
+  *out = nullptr;
+  if (!cfg || n_layers < 1) return PLD_E_INVALID;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PLD_E_HIP;
+  if (dev < 0 || dev >= MAX_DEVICES) return PLD_E_UNSUPPORTED;
+  if (!scratch_dev[dev]) {   // once per device, with that device current
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PLD_E_HIP;
+    scratch_dev[dev] = p;
+  }
+  const int nwg = device_cus(nullptr);
+  if (nwg <= 0) return PLD_E_HIP;
+  KCfg k;
+  const pld_status sd = derive(cfg, nwg, &k);
+  if (sd != PLD_OK) return sd;
+  if (layout(k, n_layers).total > STATIC_WS_BYTES) return PLD_E_CAPACITY;
+  pld_handle* h = &static_handle[dev];
+  const uint32_t steps = h->steps;   // the LL epoch keeps counting across re-initialisations
+  const pld_status st = init_into(h, cfg, n_layers, w, kv, head, scratch_dev[dev], STATIC_WS_BYTES);
+  h->steps = steps;
+  h->is_static = true;
+  if (st != PLD_OK) return st;
   *out = h;
   return PLD_OK;
 }
@@ -2051,7 +2091,9 @@ pld_status decode_reset(pld_handle* h) {
   return PLD_OK;
 }
 
-void decode_layer_destroy(pld_handle* h) { delete h; }
+void decode_layer_destroy(pld_handle* h) {
+  if (h && !h->is_static) delete h;
+}
 
 pld_status pld_set_test_hooks(pld_handle* h, int32_t flags, uint32_t seed) {
   if (!h || (flags & ~(PLD_HOOK_DROP_WG0 | PLD_HOOK_DELAY))) return PLD_E_INVALID;
