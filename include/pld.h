@@ -60,14 +60,19 @@ typedef enum pld_status {
   PLD_E_STATE = -6           /* handle needs decode_reset after a device failure */
 } pld_status;
 
-enum { PLD_ATTN_GQA = 0, PLD_ATTN_MLA = 1 };
+enum { PLD_ATTN_GQA = 0, PLD_ATTN_MLA = 1, PLD_ATTN_KDA = 2 };
 enum { PLD_WFMT_BF16 = 0, PLD_WFMT_FP8_BLOCK128 = 1 };
 enum { PLD_FFN_DENSE = 0, PLD_FFN_MOE = 1 };
 enum { PLD_ROUTER_SOFTMAX_TOPK = 0, PLD_ROUTER_SIGMOID_BIAS = 1 };
 
 /* Layer shape. GQA fields are used when attn_kind == PLD_ATTN_GQA (MHA is
  * n_kv_heads == n_heads); MLA fields when attn_kind == PLD_ATTN_MLA; index_* when
- * index_topk > 0 (MLA only; index_topk at most 8192, larger is PLD_E_UNSUPPORTED). */
+ * index_topk > 0 (MLA only; index_topk at most 8192, larger is PLD_E_UNSUPPORTED).
+ * KDA (attn_kind == PLD_ATTN_KDA, the linear attention of the Kimi K3 article, section
+ * "FlashKDA Algorithm"): n_heads heads of head_dim key and value channels, a decay
+ * projection of rank kda_rank and a causal depthwise convolution of conv_width taps over
+ * the q, k and v projections (the compiled layout: head_dim 128, kda_rank 128,
+ * conv_width 4, FP8 weights). */
 typedef struct pld_config {
   int32_t attn_kind;
   int32_t wfmt;
@@ -84,7 +89,8 @@ typedef struct pld_config {
   double eps;                                            /* RMSNorm epsilon */
   double rope_base;                                      /* RoPE base (interleaved pairs) */
   int32_t vocab;                                         /* LM head rows; 0 = no head */
-  int32_t reserved[5];
+  int32_t kda_rank, conv_width;                          /* KDA */
+  int32_t reserved[3];
 } pld_config;
 
 typedef struct pld_matrix {
@@ -106,21 +112,32 @@ typedef struct pld_layer_weights {
   pld_matrix w_qi;          /* indexer: [index_heads*index_dim, q_lora] */
   pld_matrix w_w;           /* indexer head weights: [index_heads, H], always bf16 */
   pld_matrix w_ki;          /* indexer key: [index_dim, H] */
-  pld_matrix wo;            /* [H, n_heads*hd] (GQA) or [H, n_heads*v_dim] (MLA) */
+  pld_matrix wo;            /* [H, n_heads*hd] (GQA, KDA) or [H, n_heads*v_dim] (MLA) */
   const void* router;       /* MoE: bf16 [n_experts, H] */
   const float* router_bias; /* sigmoid router: [n_experts] */
   pld_matrix w_gate, w_up;  /* [slots][inter][H] (dense FFN: slots = 1) */
   pld_matrix w_down;        /* [slots][H][inter] */
+  /* KDA (q = n_heads*head_dim): wq, wk, wv above are its [q, H] projections, and */
+  pld_matrix w_g;           /* output gate [q, H] */
+  pld_matrix w_beta;        /* delta-rule strength [n_heads, H] */
+  pld_matrix w_adown;       /* decay, low rank [kda_rank, H] */
+  pld_matrix w_aup;         /* decay [q, kda_rank] */
+  const float* conv_taps;   /* fp32 [3*q][conv_width]: channels q, k, v; the last tap on the current position */
+  const float* o_norm;      /* fp32 [head_dim] gain of the per-head output RMSNorm */
 } pld_layer_weights;
 
 /* KV cache of one layer (caller-owned, device). Rows 0..pos-1 must hold the prefilled
- * history; decode writes row pos. */
+ * history; decode writes row pos. A KDA layer's "cache" is its state and convolution ring
+ * instead: every step reads and rewrites them in place. */
 typedef struct pld_kv_cache {
   void* k;              /* GQA: bf16 [n_kv_heads][max_seq][head_dim] */
   void* v;              /* GQA: bf16 [n_kv_heads][max_seq][head_dim] */
   void* latent;         /* MLA: bf16 [max_seq][kv_lora + rope_dim] (c_kv then k_rope) */
   void* index_codes;    /* indexer: E4M3FN [max_seq][index_dim] */
   float* index_scales;  /* indexer: fp32 [max_seq] */
+  float* kda_state;     /* KDA: fp32 [n_heads][head_dim (key)][head_dim (value)], advanced in place */
+  float* conv_ring;     /* KDA: fp32 [conv_width-1][3*q] projection outputs of the previous positions,
+                           slot = position mod (conv_width-1); the current one replaces slot pos mod 3 */
 } pld_kv_cache;
 
 /* LM head of a layer stack (only with vocab > 0). */

@@ -48,6 +48,11 @@ def layer_weight_bytes(s: LayerShape) -> dict:
     if s.attn == "gqa":
         g["attn"] = (_mat_bytes(s.n_heads * s.head_dim, H, f) + 2 * _mat_bytes(s.n_kv_heads * s.head_dim, H, f)
                      + _mat_bytes(H, s.o_dim, f))
+    elif s.attn == "kda":
+        qd = s.q_dim
+        g["attn"] = (4 * _mat_bytes(qd, H, f) + _mat_bytes(s.n_heads, H, f) + _mat_bytes(s.kda_rank, H, f)
+                     + _mat_bytes(qd, s.kda_rank, f) + _mat_bytes(H, s.o_dim, f))
+        g["conv"] = 4 * 3 * qd * s.conv_width
     else:
         g["attn"] = (_mat_bytes(s.q_lora, H, f) + _mat_bytes(s.n_heads * (s.nope_dim + s.rope_dim), s.q_lora, f)
                      + _mat_bytes(s.kv_lora + s.rope_dim, H, f) + _mat_bytes(s.n_heads * s.nope_dim, s.kv_lora, f)
@@ -59,11 +64,28 @@ def layer_weight_bytes(s: LayerShape) -> dict:
     g["experts"] = n_active * (2 * _mat_bytes(s.inter, H, f) + _mat_bytes(H, s.inter, f))
     if s.ffn == "moe":
         g["router"] = 2 * s.n_experts * H + (4 * s.n_experts if s.router == "sigmoid_bias" else 0)
-    g["norms"] = 4 * (2 * H + ((s.q_lora + s.kv_lora) if s.attn == "mla" else 0))
+    g["norms"] = 4 * (2 * H + ((s.q_lora + s.kv_lora) if s.attn == "mla" else 0)
+                      + (s.head_dim if s.attn == "kda" else 0))
     return g
 
 
+def kda_state_bytes_per_head(d: int) -> int:
+    """fp32 recurrent state of one KDA head, read once and written once per token: 8 d^2 bytes
+    (the page's decode memory-traffic estimate)."""
+    return 2 * 4 * d * d
+
+
+def kda_state_flops_per_head(d: int) -> int:
+    """Decode FLOPs of one KDA head's state step, counted as the page does (about 7 d^2): the
+    decay D S (d^2 multiplies), S'^T k (2 d^2), the update S' + k u^T (2 d^2), S^T q (2 d^2)."""
+    return d * d + 2 * d * d + 2 * d * d + 2 * d * d
+
+
 def layer_kv_bytes(s: LayerShape, pos: int) -> dict:
+    if s.attn == "kda":
+        ring = 4 * (s.conv_width - 1) * 3 * s.q_dim
+        st = s.n_heads * kda_state_bytes_per_head(s.head_dim) // 2
+        return {"kv_read": st + ring, "kv_write": st + 4 * 3 * s.q_dim}
     T = pos + 1
     if s.attn == "gqa":
         row = 2 * s.n_kv_heads * s.head_dim * 2          # K and V, bf16

@@ -23,6 +23,13 @@ What is computed, and where the pages describe it:
 * The indexer that scores every cached token and keeps the top 2048 follows the
   "Sparse Indexer worker" of the TileRT article (section "But What Exactly is
   TileRT?") and the DeepSeek sparse attention mentioned in the Kimi K3 article.
+* KDA linear attention follows the Kimi K3 article, section "FlashKDA Algorithm" (the
+  decode recurrence u_t = beta_t (v_t - (D_t S_{t-1})^T k_t), S_t = D_t S_{t-1} + k_t u_t^T,
+  o_t^T = q_t^T S_t with D_t the diagonal decay, and the cumulative decay written with
+  exp2), and the paragraph after it in "Kimi Linear" (linear projections and a short
+  convolution for q, k and v, L2-normalised q and k, a low-rank decay projection, a down
+  projection for beta, a per-head output norm and an output gate that is a linear layer,
+  then the output projection that mixes the heads).
 
 The pages fix none of the formulas below; each reading taken where they are silent
 is listed in the module-level table ``READINGS``.
@@ -62,6 +69,13 @@ READINGS = {
     "fp8": "OCP E4M3FN, fp32 scale per 128x128 block of [out, in] (edge blocks their own), weight-only",
     "ties": "every top-k breaks ties to the lower index",
     "output": "the layer output is stored as bf16; multi-layer stacks pass bf16 hidden states",
+    "kda": "32 heads of 128 key/value channels at hidden 6144; q, k, v = causal depthwise convolution (width 4, no "
+           "activation; taps fp32, the last tap on the current position; the previous projection outputs are kept as "
+           "fp32 in a ring indexed by position mod 3) of W_q a, W_k a, W_v a; q and k L2-normalised per head "
+           "(eps 1e-6) and q scaled by head_dim^-1/2; beta = sigmoid(W_beta a) per head; log2 decay "
+           "g = -softplus(W_aup W_adown a) per key channel (rank 128), D_t = diag(2^g); fp32 state [head][key][value] "
+           "stored after every step; o per head RMSNorm-ed (gain [head_dim], eps 1e-6) and multiplied by "
+           "sigmoid(W_g a); y = W_o concat(o)",
 }
 
 
@@ -95,6 +109,11 @@ class Counted:
         b = self.src.router_bias()
         self._count(("router_bias",), 4 * b.size)
         return b
+
+    def conv_weights(self):
+        w = self.src.conv_weights()
+        self._count(("conv_w",), 4 * w.size)
+        return w
 
 
 def weight_f64(m: Dict) -> np.ndarray:
@@ -172,6 +191,58 @@ def indexer_select(s, W, cache, a, pos, rec):
     sel = np.sort(nx.topk_desc(score, k))
     rec["index_sel"] = sel
     return sel
+
+
+def kda_state_step(S, q, k, v, beta, alpha):
+    """One decode step of a KDA head in the order of the recurrence: S' = diag(alpha) S,
+    u = beta (v - S'^T k), S_new = S' + k u^T, o = S_new^T q. S is [key][value]."""
+    Sd = alpha[:, None] * S
+    u = beta * (v - Sd.T @ k)
+    S_new = Sd + np.outer(k, u)
+    return S_new, S_new.T @ q
+
+
+def softplus(z):
+    z = np.asarray(z, dtype=np.float64)
+    return np.maximum(z, 0.0) + np.log1p(np.exp(-np.abs(z)))
+
+
+def kda_attention(s, W, cache, a, pos, rec):
+    """KDA linear attention for one token: convolution ring and per-head state advance in place."""
+    nh, D = s.n_heads, s.head_dim
+    qd = nh * D
+    cw = s.conv_width
+    x = np.concatenate([_linear(W, "wq", a), _linear(W, "wk", a), _linear(W, "wv", a)])   # [3 qd]
+    x32 = nx.round_to_f32(x)                                   # the stored projection outputs
+    taps = np.asarray(W.conv_weights(), np.float64)           # [3 qd][cw]
+    ring = np.asarray(cache["conv_ring"], np.float64)        # [cw-1][3 qd]
+    y = taps[:, cw - 1] * x32
+    for j in range(1, cw):                                     # tap cw-1-j sees position pos-j
+        y = y + taps[:, cw - 1 - j] * ring[(pos - j) % (cw - 1)]
+    q = y[:qd].reshape(nh, D)
+    k = y[qd:2 * qd].reshape(nh, D)
+    v = y[2 * qd:].reshape(nh, D)
+    q = q / np.sqrt(np.sum(q * q, axis=1, keepdims=True) + s.eps) / math.sqrt(D)
+    k = k / np.sqrt(np.sum(k * k, axis=1, keepdims=True) + s.eps)
+    beta = nx.sigmoid(_linear(W, "w_beta", a))                # [nh]
+    g = -softplus(_linear(W, "w_aup", _linear(W, "w_adown", a))).reshape(nh, D)
+    alpha = np.exp2(g)
+    gate = nx.sigmoid(_linear(W, "w_g", a)).reshape(nh, D)
+    gam = np.asarray(W.norm("o_norm"), np.float64)
+    S = np.asarray(cache["kda_state"], np.float64)
+    o = np.empty((nh, D))
+    S_new = np.empty_like(S)
+    for h in range(nh):
+        S_new[h], o[h] = kda_state_step(S[h], q[h], k[h], v[h], beta[h], alpha[h])
+    rec["kda_q"], rec["kda_k"], rec["kda_v"], rec["kda_beta"], rec["kda_alpha"] = q, k, v, beta, alpha
+    rec["kda_x32"] = x32
+    rec["kda_state_new"] = nx.round_to_f32(S_new)
+    rec["o_raw"] = o
+    on = np.stack([nx.rmsnorm(o[h], gam, s.eps) for h in range(nh)]) * gate
+    rec["o"] = on
+    rec["kv_bytes_read"] = 4 * S.size + 4 * ring.size
+    rec["kv_bytes_written"] = 4 * S.size + 4 * 3 * qd
+    return _linear(W, "wo", on.reshape(-1))
 
 
 def mla_attention(s, W, cache, a, pos, rec):
@@ -266,6 +337,8 @@ def decode_layer(s, W, cache, x_bits: np.ndarray, pos: int, record: Optional[dic
     rec["a"] = a
     if s.attn == "gqa":
         y = gqa_attention(s, CW, cache, a, pos, rec)
+    elif s.attn == "kda":
+        y = kda_attention(s, CW, cache, a, pos, rec)
     else:
         y = mla_attention(s, CW, cache, a, pos, rec)
     h2 = h + y
@@ -286,6 +359,9 @@ def append_to_cache(s, cache, rec, pos):
     if s.attn == "gqa":
         cache["k"][:, pos, :] = nx.bf16_bits_of(rec["k_new"])
         cache["v"][:, pos, :] = nx.bf16_bits_of(rec["v_new"])
+    elif s.attn == "kda":
+        cache["kda_state"][...] = rec["kda_state_new"]
+        cache["conv_ring"][pos % (s.conv_width - 1)] = rec["kda_x32"]
     else:
         cache["latent"][pos] = nx.bf16_bits_of(rec["latent_new"])
         if s.index_topk:

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libpld.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pld.h")
 
 PLD_OK, PLD_E_INVALID, PLD_E_UNSUPPORTED, PLD_E_CAPACITY, PLD_E_HIP, PLD_E_DEVICE_TIMEOUT, PLD_E_STATE = 0, -1, -2, -3, -4, -5, -6
-PLD_ATTN_GQA, PLD_ATTN_MLA = 0, 1
+PLD_ATTN_GQA, PLD_ATTN_MLA, PLD_ATTN_KDA = 0, 1, 2
 PLD_WFMT_BF16, PLD_WFMT_FP8_BLOCK128 = 0, 1
 PLD_FFN_DENSE, PLD_FFN_MOE = 0, 1
 PLD_ROUTER_SOFTMAX_TOPK, PLD_ROUTER_SIGMOID_BIAS = 0, 1
@@ -36,7 +36,7 @@ class PldConfig(ctypes.Structure):
         "attn_kind", "wfmt", "hidden", "n_heads", "n_kv_heads", "head_dim", "q_lora", "kv_lora", "rope_dim",
         "nope_dim", "v_dim", "index_heads", "index_dim", "index_topk", "ffn_kind", "inter", "n_experts", "top_k",
         "n_shared", "router_kind", "max_seq")] + [("eps", f64), ("rope_base", f64), ("vocab", i32),
-                                                   ("reserved", i32 * 5)]
+                                                   ("kda_rank", i32), ("conv_width", i32), ("reserved", i32 * 3)]
 
 
 class PldMatrix(ctypes.Structure):
@@ -47,11 +47,13 @@ class PldLayerWeights(ctypes.Structure):
     _fields_ = [("attn_norm", vp), ("ffn_norm", vp), ("q_norm", vp), ("kv_norm", vp)] + \
                [(n, PldMatrix) for n in ("wq", "wk", "wv", "w_dq", "w_uq", "w_dkv", "w_uk", "w_uv", "w_qi", "w_w",
                                          "w_ki", "wo")] + \
-               [("router", vp), ("router_bias", vp)] + [(n, PldMatrix) for n in ("w_gate", "w_up", "w_down")]
+               [("router", vp), ("router_bias", vp)] + [(n, PldMatrix) for n in ("w_gate", "w_up", "w_down")] + \
+               [(n, PldMatrix) for n in ("w_g", "w_beta", "w_adown", "w_aup")] + [("conv_taps", vp), ("o_norm", vp)]
 
 
 class PldKvCache(ctypes.Structure):
-    _fields_ = [("k", vp), ("v", vp), ("latent", vp), ("index_codes", vp), ("index_scales", vp)]
+    _fields_ = [("k", vp), ("v", vp), ("latent", vp), ("index_codes", vp), ("index_scales", vp), ("kda_state", vp),
+                ("conv_ring", vp)]
 
 
 class PldHeadWeights(ctypes.Structure):
@@ -132,7 +134,7 @@ def check(code: int, what: str):
 def config_from_shape(s, vocab: int = 0) -> PldConfig:
     """pld_config of a synth.configs.LayerShape."""
     c = PldConfig()
-    c.attn_kind = PLD_ATTN_GQA if s.attn == "gqa" else PLD_ATTN_MLA
+    c.attn_kind = {"gqa": PLD_ATTN_GQA, "mla": PLD_ATTN_MLA, "kda": PLD_ATTN_KDA}[s.attn]
     c.wfmt = PLD_WFMT_FP8_BLOCK128 if s.wfmt == "fp8" else PLD_WFMT_BF16
     c.hidden, c.n_heads, c.n_kv_heads, c.head_dim = s.hidden, s.n_heads, s.n_kv_heads, s.head_dim
     c.q_lora, c.kv_lora, c.rope_dim, c.nope_dim, c.v_dim = s.q_lora, s.kv_lora, s.rope_dim, s.nope_dim, s.v_dim
@@ -141,6 +143,7 @@ def config_from_shape(s, vocab: int = 0) -> PldConfig:
     c.inter, c.n_experts, c.top_k, c.n_shared = s.inter, s.n_experts, s.top_k, s.n_shared
     c.router_kind = PLD_ROUTER_SIGMOID_BIAS if s.router == "sigmoid_bias" else PLD_ROUTER_SOFTMAX_TOPK
     c.max_seq, c.eps, c.rope_base, c.vocab = s.max_seq, s.eps, s.rope_base, vocab
+    c.kda_rank, c.conv_width = s.kda_rank, s.conv_width
     return c
 
 
@@ -159,11 +162,11 @@ def _mat(m) -> PldMatrix:
 def layer_struct(W: dict) -> PldLayerWeights:
     """pld_layer_weights from a dict of device tensors (as made by synth.device.layer_weights)."""
     L = PldLayerWeights()
-    for n in ("attn_norm", "ffn_norm", "q_norm", "kv_norm", "router_bias"):
+    for n in ("attn_norm", "ffn_norm", "q_norm", "kv_norm", "router_bias", "conv_taps", "o_norm"):
         if n in W:
             setattr(L, n, W[n].data_ptr())
     for n in ("wq", "wk", "wv", "w_dq", "w_uq", "w_dkv", "w_uk", "w_uv", "w_qi", "w_w", "w_ki", "wo", "w_gate",
-              "w_up", "w_down"):
+              "w_up", "w_down", "w_g", "w_beta", "w_adown", "w_aup"):
         if n in W:
             setattr(L, n, _mat(W[n]))
     if "router" in W:
@@ -173,7 +176,7 @@ def layer_struct(W: dict) -> PldLayerWeights:
 
 def cache_struct(C: dict) -> PldKvCache:
     K = PldKvCache()
-    for n in ("k", "v", "latent", "index_codes", "index_scales"):
+    for n in ("k", "v", "latent", "index_codes", "index_scales", "kda_state", "conv_ring"):
         if n in C:
             setattr(K, n, C[n].data_ptr())
     return K

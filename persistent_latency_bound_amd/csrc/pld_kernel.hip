@@ -59,7 +59,7 @@ enum TraceSlot {
 };
 
 struct KCfg {
-  int attn, wfmt, H, nh, nkv, hd, q_lora, kv_lora, rope, nope, vdim, ih, idim, itopk;
+  int attn, wfmt, H, nh, nkv, hd, q_lora, kv_lora, rope, nope, vdim, ih, idim, itopk, krank, cwidth;
   int ffn, inter, E, topk, nshared, router, max_seq, vocab;
   double eps;
   int slots;   // expert slots used per token (routed + shared), 1 for a dense FFN
@@ -82,13 +82,16 @@ struct DLayer {
   uint16_t *kc, *vc, *lat;
   uint8_t* icodes;
   float* iscales;
+  DMat w_g, w_beta, w_adown, w_aup;   // KDA
+  const float *conv_taps, *o_norm;
+  float *kstate, *conv_ring;
 };
 
 // Workspace layout. The LL buffers (8-byte words: payload | epoch << 32) follow the
 // status words; both are zeroed at init and by decode_reset.
 struct WsOff {
   size_t status, x, q, kv, part, o, h2, logits, m, cqr, ckvr, qr, qlat, olat, amax, ixr, qi, ilist, isel, ll_end, sel,
-      gates, spec, a_dbg, b_dbg, f_dbg, ikh, ikl, ilo, itok, rope, layers, total;
+      gates, spec, a_dbg, b_dbg, f_dbg, ikh, ikl, ilo, itok, kx, rope, layers, total;
 };
 
 struct KArgs {
@@ -1438,6 +1441,7 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_gqa(KArgs a) {
 }
 
 #include "pld_mla.hpp"
+#include "pld_kda.hpp"
 
 typedef void (*KernelFn)(KArgs);
 
@@ -1451,6 +1455,16 @@ using ShapeMlaFp8 = MlaShape<6144, 64, 1536, 512, 64, 128, 128, 2048, true, true
 // the sparse MLA MoE layer: hidden 4096, 32 heads, the same latent sizes, bf16 weights,
 // indexer of 8 heads x 64 dims, 64 experts of width 1536 (softmax router)
 using ShapeSparseMla = MlaShape<4096, 32, 1536, 512, 64, 128, 128, 1536, false, true, true, 8, 64>;
+// the KDA MoE layer: hidden 6144, 32 KDA heads x 128, decay rank 128, convolution width 4,
+// FP8 weights, 256 experts of width 2048 (biased-score router)
+using ShapeKda = KdaShape<6144, 32, 128, 128, 4, 2048, true, true>;
+
+template <class SH>
+static bool matches_kda(const pld_config* c) {
+  return c->attn_kind == PLD_ATTN_KDA && c->hidden == SH::H && c->n_heads == SH::NH && c->head_dim == SH::D &&
+         c->kda_rank == SH::R && c->conv_width == SH::CW && c->inter == SH::INTER &&
+         (c->wfmt == PLD_WFMT_FP8_BLOCK128) == SH::FP8 && (c->ffn_kind == PLD_FFN_MOE) == SH::MOE;
+}
 
 template <class SH>
 static bool matches(const pld_config* c) {
@@ -1480,6 +1494,7 @@ static KernelFn pick_kernel(const pld_config* c) {
   if (matches<ShapeGqaMoe>(c)) return k_decode_gqa<ShapeGqaMoe>;
   if (matches_mla<ShapeMlaFp8>(c)) return k_decode_mla<ShapeMlaFp8>;
   if (matches_mla<ShapeSparseMla>(c)) return k_decode_mla<ShapeSparseMla>;
+  if (matches_kda<ShapeKda>(c)) return k_decode_kda<ShapeKda>;
   return nullptr;
 }
 
@@ -1538,6 +1553,7 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
   k->vdim = c->v_dim; k->ih = c->index_heads; k->idim = c->index_dim; k->itopk = c->index_topk; k->ffn = c->ffn_kind;
   k->inter = c->inter; k->E = c->n_experts; k->topk = c->top_k; k->nshared = c->n_shared; k->router = c->router_kind;
   k->max_seq = c->max_seq; k->vocab = c->vocab; k->eps = c->eps; k->nwg = nwg;
+  k->krank = c->kda_rank; k->cwidth = c->conv_width;
   if (c->hidden <= 0 || c->n_heads <= 0 || c->max_seq <= 0 || c->inter <= 0 || !(c->eps >= 0.0)) return PLD_E_INVALID;
   if (c->wfmt != PLD_WFMT_BF16 && c->wfmt != PLD_WFMT_FP8_BLOCK128) return PLD_E_UNSUPPORTED;
   if (nwg < NXCD || nwg % NXCD) return PLD_E_UNSUPPORTED;
@@ -1640,6 +1656,26 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
                          2 * c->n_experts + BLOCK});
     k->outb_floats = (int)al(outb, 64);
     if (lds_bytes_for(k->act_floats, k->stage_words, k->outb_floats) > 160 * 1024) return PLD_E_UNSUPPORTED;
+  } else if (c->attn_kind == PLD_ATTN_KDA) {
+    if (!pick_kernel(c)) return PLD_E_UNSUPPORTED;
+    const int NH = c->n_heads, D = c->head_dim, QD = NH * D, R = c->kda_rank;
+    const int rows = 4 * QD + R + NH;
+    // the state stage: each workgroup owns 16 value columns of one head
+    if (nwg != NH * (D / 16)) return PLD_E_UNSUPPORTED;
+    // the projection stage: one row per thread, and every workgroup publishes some rows
+    if ((rows + nwg - 1) / nwg > BLOCK || rows < nwg || c->inter < nwg || c->hidden / 2 < nwg) return PLD_E_UNSUPPORTED;
+    const bool pad = c->wfmt == PLD_WFMT_FP8_BLOCK128;
+    auto ap = [pad](int n) { return pad ? apad<true>(n) : n; };
+    int act = std::max({ap(c->hidden), ap(QD) + 2 * QD, ap(k->slots * c->inter),
+                        2 * D + 16 + R + 4 + NWAVES * 16 + 16 + 4 + 2 * NWAVES + 8});
+    k->act_floats = (int)al(act, 64);
+    k->stage_words = (int)al(c->hidden / 2 + 2, 64);
+    int outb = std::max({rows / nwg + 4, c->hidden / nwg + 4, k->slots * (c->hidden / nwg + 4),
+                         2 * ((k->slots * c->inter) / nwg + 2), 2 * (c->inter / nwg + 2) * std::max(1, c->n_shared),
+                         4 * c->n_experts + 4, 2 * c->n_experts + BLOCK});
+    k->outb_floats = (int)al(outb, 64);
+    if (lds_bytes_for(k->act_floats, k->stage_words, k->outb_floats) > 160 * 1024) return PLD_E_UNSUPPORTED;
+    k->rdim = 2;   // no RoPE
   } else {
     return PLD_E_UNSUPPORTED;
   }
@@ -1681,6 +1717,12 @@ WsOff layout(const KCfg& k, int n_layers) {
     o.cqr = o.ckvr = o.qr = o.qlat = o.olat = 0;
   }
   o.amax = p; p += al((size_t)3 * std::max(k.nwg, 1) * W);   // per-workgroup (logit lo, hi, index)
+  if (k.attn == PLD_ATTN_KDA) {
+    const int QD = k.nh * k.hd;
+    o.kx = p; p += al((size_t)(4 * QD + k.krank + k.nh) * W);   // conv outputs, gate, a_down, beta
+  } else {
+    o.kx = 0;
+  }
   if (k.itopk > 0) {
     o.ixr = p; p += al((size_t)(k.ih + k.idim) * W);       // indexer head weights w and new key k_I (fp32)
     o.qi = p; p += al((size_t)(k.ih * k.idim / 2) * W);    // indexer queries (bf16 pairs)
@@ -1785,7 +1827,24 @@ pld_status build_layer(const pld_config* cfg, const pld_layer_weights& L, const 
   d.attn_norm = L.attn_norm;
   d.ffn_norm = L.ffn_norm;
   const bool mla = cfg->attn_kind == PLD_ATTN_MLA;
-  if (!mla) {
+  const bool kda = cfg->attn_kind == PLD_ATTN_KDA;
+  if (kda) {
+    const int QD = cfg->n_heads * cfg->head_dim, R = cfg->kda_rank;
+    if (!mat_ok(L.wq, fp8) || !mat_ok(L.wk, fp8) || !mat_ok(L.wv, fp8) || !mat_ok(L.wo, fp8) || !mat_ok(L.w_g, fp8) ||
+        !mat_ok(L.w_beta, fp8) || !mat_ok(L.w_adown, fp8) || !mat_ok(L.w_aup, fp8))
+      return PLD_E_INVALID;
+    if (!L.conv_taps || !L.o_norm || !aligned16(L.conv_taps) || !aligned16(L.o_norm)) return PLD_E_INVALID;
+    d.wq = dmat(L.wq, QD, H, fp8);
+    d.wk = dmat(L.wk, QD, H, fp8);
+    d.wv = dmat(L.wv, QD, H, fp8);
+    d.wo = dmat(L.wo, H, QD, fp8);
+    d.w_g = dmat(L.w_g, QD, H, fp8);
+    d.w_beta = dmat(L.w_beta, cfg->n_heads, H, fp8);
+    d.w_adown = dmat(L.w_adown, R, H, fp8);
+    d.w_aup = dmat(L.w_aup, QD, R, fp8);
+    d.conv_taps = L.conv_taps;
+    d.o_norm = L.o_norm;
+  } else if (!mla) {
     const int hd = cfg->head_dim;
     if (!mat_ok(L.wq, fp8) || !mat_ok(L.wk, fp8) || !mat_ok(L.wv, fp8) || !mat_ok(L.wo, fp8)) return PLD_E_INVALID;
     d.wq = dmat(L.wq, cfg->n_heads * hd, H, fp8);
@@ -1832,7 +1891,11 @@ pld_status build_layer(const pld_config* cfg, const pld_layer_weights& L, const 
       d.router_bias = L.router_bias;
     }
   }
-  if (!mla) {
+  if (kda) {
+    if (!C.kda_state || !C.conv_ring || !aligned16(C.kda_state) || !aligned16(C.conv_ring)) return PLD_E_INVALID;
+    d.kstate = C.kda_state;
+    d.conv_ring = C.conv_ring;
+  } else if (!mla) {
     if (!C.k || !C.v || !aligned16(C.k) || !aligned16(C.v)) return PLD_E_INVALID;
     d.kc = (uint16_t*)C.k;
     d.vc = (uint16_t*)C.v;

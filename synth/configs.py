@@ -22,7 +22,7 @@ from typing import Dict
 class LayerShape:
     name: str
     hidden: int
-    attn: str                 # "gqa" (MHA is the n_kv_heads == n_heads case) or "mla"
+    attn: str                 # "gqa" (MHA is the n_kv_heads == n_heads case), "mla" or "kda"
     n_heads: int
     # GQA / MHA
     n_kv_heads: int = 0
@@ -33,6 +33,10 @@ class LayerShape:
     rope_dim: int = 0
     nope_dim: int = 0
     v_dim: int = 0
+    # KDA linear attention (attn == "kda"): n_heads heads of head_dim key/value channels,
+    # a low-rank decay projection and a causal depthwise convolution over q, k, v
+    kda_rank: int = 0
+    conv_width: int = 0
     # sparse indexer (MLA only); index_topk == 0 means dense attention
     index_heads: int = 0
     index_dim: int = 0
@@ -59,18 +63,20 @@ class LayerShape:
     norm_std: float = 0.02    # gamma = 1 + norm_std * N(0,1)
     x_std: float = 1.0
     cache_std: float = 1.0
+    state_std: float = 0.1    # prefilled KDA state entries
+    conv_std: float = 0.5     # KDA convolution taps
 
     # ---- derived sizes -------------------------------------------------
     @property
     def q_dim(self) -> int:
-        if self.attn == "gqa":
+        if self.attn in ("gqa", "kda"):
             return self.n_heads * self.head_dim
         return self.n_heads * (self.nope_dim + self.rope_dim)
 
     @property
     def o_dim(self) -> int:
         """Width of the concatenated attention output fed to W_O."""
-        if self.attn == "gqa":
+        if self.attn in ("gqa", "kda"):
             return self.n_heads * self.head_dim
         return self.n_heads * self.v_dim
 
@@ -138,9 +144,21 @@ C4 = LayerShape(
 )
 
 C5_LAYER = replace(C3, name="c5_layer_mla_moe256_fp8", max_seq=8192 + 256 + 8)
+
+# KDA linear-attention decode layer (the Kimi K3 article's KDA, "FlashKDA Algorithm"): the
+# FP8 MLA layer's hidden size and MoE, with 32 KDA heads of 128 key/value channels, a
+# rank-128 decay projection and a width-4 causal convolution; the per-head fp32 state
+# replaces the KV cache, so the position only indexes the convolution ring.
+C6 = LayerShape(
+    name="c6_kda_moe256_fp8",
+    hidden=6144, attn="kda", n_heads=32, head_dim=128, kda_rank=128, conv_width=4,
+    wfmt="fp8", ffn="moe", inter=2048, n_experts=256, top_k=8, n_shared=1,
+    router="sigmoid_bias", router_std=0.02,
+    cache_len=8192, max_seq=8192 + 64,
+)
 C5 = ModelShape(layer=C5_LAYER, n_layers=24, vocab=32768, n_tokens=256, n_verify=6)
 
-LAYERS: Dict[str, LayerShape] = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5_LAYER}
+LAYERS: Dict[str, LayerShape] = {"c1": C1, "c2": C2, "c3": C3, "c4": C4, "c5": C5_LAYER, "c6": C6}
 
 
 def scaled(shape: LayerShape, **kw) -> LayerShape:

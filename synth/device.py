@@ -111,6 +111,10 @@ def layer_weights(s: LayerShape, seed: int = 0, layer: int = 0, device="cuda") -
         t = torch.empty(s.n_experts, dtype=torch.float32, device=device)
         fill_f32(t, seed, gen.tensor_id("router_bias", layer), s.bias_std)
         W["router_bias"] = t
+    if s.attn == "kda":
+        t = torch.empty((3 * s.q_dim, s.conv_width), dtype=torch.float32, device=device)
+        fill_f32(t, seed, gen.tensor_id("conv_w", layer), s.conv_std)
+        W["conv_taps"] = t
     return W
 
 
@@ -122,6 +126,13 @@ def kv_cache(s: LayerShape, seed: int = 0, layer: int = 0, device="cuda", fill_l
     """A prefilled cache: positions 0..fill_len-1 (default cache_len) hold seeded values, the rest zero."""
     n = s.cache_len if fill_len is None else fill_len
     C = {}
+    if s.attn == "kda":
+        st = torch.empty((s.n_heads, s.head_dim, s.head_dim), dtype=torch.float32, device=device)
+        fill_f32(st, seed, gen.tensor_id("kda_state", layer), s.state_std)
+        ring = torch.empty((s.conv_width - 1, 3 * s.q_dim), dtype=torch.float32, device=device)
+        fill_f32(ring, seed, gen.tensor_id("conv_state", layer), s.cache_std)
+        C["kda_state"], C["conv_ring"] = st, ring
+        return C
     if s.attn == "gqa":
         for kind, key in (("k_cache", "k"), ("v_cache", "v")):
             t = _u16((s.n_kv_heads, s.max_seq, s.head_dim), device)

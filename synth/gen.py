@@ -53,6 +53,8 @@ KIND = {
     "ffn_norm": 17, "w_gate": 18, "w_up": 19, "w_down": 20, "router": 21, "router_bias": 22,
     "k_cache": 23, "v_cache": 24, "latent": 25, "index_k": 26,
     "embed": 27, "final_norm": 28, "head": 29, "token": 30,
+    "w_g": 31, "w_beta": 32, "w_adown": 33, "w_aup": 34, "conv_w": 35, "o_norm": 36, "kda_state": 37,
+    "conv_state": 38,
 }
 POS_STRIDE = 1 << 20  # cache element index = ((head << 20) | pos) * row + col
 
@@ -202,6 +204,15 @@ def layer_matrices(s: LayerShape):
         m["wq"] = (s.n_heads * s.head_dim, H)
         m["wk"] = (s.n_kv_heads * s.head_dim, H)
         m["wv"] = (s.n_kv_heads * s.head_dim, H)
+    elif s.attn == "kda":
+        qd = s.n_heads * s.head_dim
+        m["wq"] = (qd, H)
+        m["wk"] = (qd, H)
+        m["wv"] = (qd, H)
+        m["w_g"] = (qd, H)                # output gate
+        m["w_beta"] = (s.n_heads, H)      # delta-rule strength per head
+        m["w_adown"] = (s.kda_rank, H)    # low-rank decay projection
+        m["w_aup"] = (qd, s.kda_rank)
     else:
         m["w_dq"] = (s.q_lora, H)
         m["w_uq"] = (s.n_heads * (s.nope_dim + s.rope_dim), s.q_lora)
@@ -226,6 +237,8 @@ def layer_norms(s: LayerShape):
     if s.attn == "mla":
         n["q_norm"] = s.q_lora
         n["kv_norm"] = s.kv_lora
+    if s.attn == "kda":
+        n["o_norm"] = s.head_dim
     return n
 
 
@@ -286,6 +299,12 @@ class LayerWeights:
     def router_bias(self) -> np.ndarray:
         return scaled_normal(self.seed, tensor_id("router_bias", self.layer),
                              np.arange(self.s.n_experts, dtype=np.uint64), self.s.bias_std)
+
+    def conv_weights(self) -> np.ndarray:
+        """fp32 [3 * q_dim][conv_width] taps of the KDA causal convolution (q, k, v channels)."""
+        n = 3 * self.s.q_dim * self.s.conv_width
+        return scaled_normal(self.seed, tensor_id("conv_w", self.layer), np.arange(n, dtype=np.uint64),
+                             self.s.conv_std).reshape(3 * self.s.q_dim, self.s.conv_width)
 
 
 def input_hidden(shape: LayerShape, seed: int = 0, step: int = 0, layer: int = 0) -> np.ndarray:
@@ -382,6 +401,8 @@ def padded_cache(shape: LayerShape, seed=0, layer=0, fill_len=None) -> dict:
     cache_len) hold the seeded rows, the rest zero (the layout the device fill writes)."""
     n = shape.cache_len if fill_len is None else fill_len
     out = {}
+    if shape.attn == "kda":
+        return {"kda_state": kda_state(shape, seed, layer), "conv_ring": conv_state(shape, seed, layer)}
     if shape.attn == "gqa":
         pos = np.arange(n)
         for kind, key in (("k_cache", "k"), ("v_cache", "v")):
@@ -400,3 +421,20 @@ def padded_cache(shape: LayerShape, seed=0, layer=0, fill_len=None) -> dict:
             codes[:n], scales[:n] = c, sc
             out["index_codes"], out["index_scales"] = codes, scales
     return out
+
+
+def kda_state(shape: LayerShape, seed=0, layer=0) -> np.ndarray:
+    """fp32 [n_heads][head_dim][head_dim] prefilled KDA state (row: key channel, column: value)."""
+    D = shape.head_dim
+    n = shape.n_heads * D * D
+    return scaled_normal(seed, tensor_id("kda_state", layer), np.arange(n, dtype=np.uint64),
+                         shape.state_std).reshape(shape.n_heads, D, D)
+
+
+def conv_state(shape: LayerShape, seed=0, layer=0) -> np.ndarray:
+    """fp32 [conv_width - 1][3 * q_dim] ring of the last projection outputs (slot = position mod
+    (conv_width - 1)), prefilled."""
+    w = shape.conv_width - 1
+    n = w * 3 * shape.q_dim
+    return scaled_normal(seed, tensor_id("conv_state", layer), np.arange(n, dtype=np.uint64),
+                         shape.cache_std).reshape(w, 3 * shape.q_dim)

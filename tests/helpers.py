@@ -26,12 +26,13 @@ def tiny_mla(**kw) -> LayerShape:
 class DictWeights:
     """Weight source with explicit fp32 matrices (stored as bf16) and optional overrides."""
 
-    def __init__(self, shape, base=None, overrides=None, norms=None, bias=None):
+    def __init__(self, shape, base=None, overrides=None, norms=None, bias=None, conv=None):
         self.s = shape
         self.base = base if base is not None else gen.LayerWeights(shape, 0, 0)
         self.ov = overrides or {}
         self.norms = norms or {}
         self.bias = bias
+        self.conv = conv
 
     def matrix(self, name, expert=0):
         key = (name, expert)
@@ -52,3 +53,16 @@ class DictWeights:
         if self.bias is not None:
             return np.asarray(self.bias, np.float32)
         return self.base.router_bias()
+
+    def conv_weights(self):
+        if self.conv is not None:
+            return np.asarray(self.conv, np.float32)
+        return self.base.conv_weights()
+
+
+def tiny_kda(**kw) -> LayerShape:
+    base = dict(name="tiny_kda", hidden=128, attn="kda", n_heads=4, head_dim=16, kda_rank=16, conv_width=4,
+                wfmt="fp8", ffn="moe", inter=64, n_experts=8, top_k=2, n_shared=1, router="sigmoid_bias",
+                router_std=0.02, cache_len=9, max_seq=32)
+    base.update(kw)
+    return LayerShape(**base)

@@ -56,6 +56,7 @@ int main(void) {
   printf("pld_persistent_args %zu\n", sizeof(pld_persistent_args));
   P(pld_config, eps) P(pld_config, rope_base) P(pld_config, vocab) P(pld_config, max_seq)
   P(pld_layer_weights, wo) P(pld_layer_weights, router) P(pld_layer_weights, w_down)
+  P(pld_layer_weights, w_aup) P(pld_layer_weights, o_norm) P(pld_config, kda_rank)
   P(pld_persistent_args, in_hidden) P(pld_persistent_args, out_accepted)
   P(pld_persistent_args, temperature) P(pld_persistent_args, sample_seed)
   printf("pld_spec_args %zu\n", sizeof(pld_spec_args));

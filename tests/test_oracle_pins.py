@@ -18,7 +18,7 @@ from oracle import layer as OL
 from oracle import model as OM
 from synth import configs, gen
 
-from helpers import DictWeights, tiny_gqa, tiny_mla
+from helpers import DictWeights, tiny_gqa, tiny_kda, tiny_mla
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_worked_examples.json")
 
@@ -237,8 +237,7 @@ def test_biased_router_selection_and_gates_by_hand():
 # --------------------------------------------------------------------------- attention
 def _tiny_case(s, seed=0):
     W = gen.LayerWeights(s, seed, 0)
-    cache = gen.full_cache(s, seed)
-    cache = _pad_cache(s, cache)
+    cache = gen.padded_cache(s, seed)
     x = gen.input_hidden(s, seed)
     return W, cache, x
 
@@ -447,7 +446,7 @@ def test_page_worked_examples():
     assert lc["standard_launches"] - lc["specialized_launches"] == 10
 
 
-@pytest.mark.parametrize("shape_fn", [tiny_gqa, tiny_mla,
+@pytest.mark.parametrize("shape_fn", [tiny_gqa, tiny_mla, tiny_kda,
                                       lambda: tiny_mla(wfmt="bf16", router="softmax", index_heads=2,
                                                        index_dim=16, index_topk=4)])
 def test_oracle_byte_count_equals_closed_form(shape_fn):
@@ -593,3 +592,94 @@ def test_gumbel_max_sampling_follows_softmax():
     big = np.zeros(1000)
     big[417] = 200.0
     assert all(OM.sample_token(big, 1.0, 5, pos) == 417 for pos in range(50))
+
+
+# --------------------------------------------------------------------------- KDA
+def _kda_chunk_form(S, Q, K, V, beta, G):
+    """The chunked matrix form printed in the Kimi K3 article ("FlashKDA Algorithm"), written
+    out independently of the per-token recurrence: a = exp2(cumsum(g)), K_decay = Diag(a) K,
+    Q_decay = Diag(a) Q, K_inv = Diag(a)^-1 K, K_restore = a[-1] K_inv, L = StrictTril(Diag(beta)
+    K_decay K_inv^T), U = (I + L)^-1 Diag(beta) (V - K_decay S), O = Q_decay S + tril(Q_decay
+    K_inv^T) U, S_out = Diag(a[-1]) S + K_restore^T U."""
+    C = Q.shape[0]
+    a = np.exp2(np.cumsum(G, axis=0))
+    K_decay, Q_decay, K_inv = a * K, a * Q, K / a
+    K_restore = a[-1] * K_inv
+    L = np.tril(beta[:, None] * (K_decay @ K_inv.T), -1)
+    U = np.linalg.solve(np.eye(C) + L, beta[:, None] * (V - K_decay @ S))
+    O = Q_decay @ S + np.tril(Q_decay @ K_inv.T) @ U
+    return O, a[-1][:, None] * S + K_restore.T @ U
+
+
+def test_kda_recurrence_equals_the_pages_chunked_form():
+    """Eight tokens through the oracle's per-token state step equal two chunks of four through
+    the chunked form (outputs of every token and the final state, to rounding)."""
+    rng = np.random.default_rng(21)
+    Dk, Dv, T, C = 8, 6, 8, 4
+    S0 = rng.standard_normal((Dk, Dv))
+    Q, K, V = rng.standard_normal((T, Dk)), rng.standard_normal((T, Dk)), rng.standard_normal((T, Dv))
+    K /= np.linalg.norm(K, axis=1, keepdims=True)
+    beta = 1 / (1 + np.exp(-rng.standard_normal(T)))
+    G = -np.log1p(np.exp(rng.standard_normal((T, Dk))))        # log2 decays <= 0
+    S, outs = S0.copy(), []
+    for t in range(T):
+        S, o = OL.kda_state_step(S, Q[t], K[t], V[t], beta[t], np.exp2(G[t]))
+        outs.append(o)
+    Sc, oc = S0.copy(), []
+    for c0 in range(0, T, C):
+        O, Sc = _kda_chunk_form(Sc, Q[c0:c0 + C], K[c0:c0 + C], V[c0:c0 + C], beta[c0:c0 + C], G[c0:c0 + C])
+        oc.append(O)
+    assert np.allclose(np.stack(outs), np.concatenate(oc), rtol=0, atol=1e-12)
+    assert np.allclose(S, Sc, rtol=0, atol=1e-12)
+
+
+def test_kda_delta_rule_stores_the_value_at_its_key():
+    """With no decay and beta = 1, the delta rule overwrites what the state returns for a unit
+    key: after the step S^T k = v exactly (to rounding), whatever S held before."""
+    rng = np.random.default_rng(5)
+    S = rng.standard_normal((16, 12))
+    k = rng.standard_normal(16)
+    k /= np.linalg.norm(k)
+    v = rng.standard_normal(12)
+    S1, o = OL.kda_state_step(S, k, k, v, 1.0, np.ones(16))
+    assert np.allclose(S1.T @ k, v, atol=1e-13)
+    assert np.allclose(o, v, atol=1e-13)          # querying with the key itself
+    # beta = 0 only decays: S1 = diag(alpha) S
+    al = rng.uniform(0.2, 1.0, 16)
+    S2, _ = OL.kda_state_step(S, k, k, v, 0.0, al)
+    assert np.array_equal(S2, al[:, None] * S)
+
+
+def test_kda_state_cost_matches_the_pages_decode_figures():
+    """Per head and token: about 7 D^2 FLOPs and 8 D^2 bytes (fp32 state read and written)."""
+    for d in (64, 128, 256):
+        assert accounting.kda_state_flops_per_head(d) == 7 * d * d
+        assert accounting.kda_state_bytes_per_head(d) == 8 * d * d
+
+
+def test_kda_convolution_taps_by_hand():
+    """The causal depthwise convolution: taps [0, 0, 0, 1] pass the current projection through,
+    taps [1, 0, 0, 0] return the ring entry of position pos - 3, and the ring slot of pos is
+    overwritten by the current projection (fp32)."""
+    s = tiny_kda()
+    nq = 3 * s.q_dim
+    base = gen.LayerWeights(s, 0, 0)
+    cache = gen.padded_cache(s)
+    x = gen.input_hidden(s)
+    pos = 10
+    a = nx.rmsnorm(nx.bf16_to_f64(x), base.norm("attn_norm"), s.eps)
+    for taps, want in (([0, 0, 0, 1], None), ([1, 0, 0, 0], cache["conv_ring"][(pos - 3) % 3].astype(np.float64))):
+        W = DictWeights(s, base=base, conv=np.tile(np.asarray(taps, np.float32), (nq, 1)))
+        c = {k: v.copy() for k, v in cache.items()}
+        rec = {}
+        OL.kda_attention(s, W, c, a, pos, rec)
+        proj = rec["kda_x32"]
+        got = np.concatenate([rec["kda_v"].reshape(-1)])          # v is not normalised: the conv output itself
+        ref = (proj if want is None else want)[2 * s.q_dim:]
+        assert np.array_equal(got, ref)
+    # the ring slot of pos now holds the fp32 projection after append
+    c = {k: v.copy() for k, v in cache.items()}
+    rec = OL.decode_layer(s, base, c, x, pos)
+    OL.append_to_cache(s, c, rec, pos)
+    assert np.array_equal(c["conv_ring"][pos % 3], rec["kda_x32"].astype(np.float32))
+    assert np.array_equal(c["conv_ring"][(pos + 1) % 3], cache["conv_ring"][(pos + 1) % 3])
