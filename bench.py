@@ -49,6 +49,9 @@ WORKLOADS = {   # name -> (synth.configs attribute, traffic file stem, dtype of 
                                            "bf16 weights, fp32 accumulate; indexer scores fp64"),
     # 24 stacked FP8 MLA layers + FP8 LM head, greedy loop over 256 tokens in one launch
     "mla_stack24_fp8_greedy256": ("C5", "traffic_mla_stack24_fp8", "fp8-e4m3 weights, fp32 accumulate, fp64 head"),
+    # the FP8 MLA layer with LUT3 experts (3-bit indices into 8-entry E4M3 codebooks, 3.125 bits/weight)
+    "mla_moe256_lut3_decode_layer": ("C7", "traffic_mla_moe256_lut3",
+                                     "lut3 expert weights (E4M3 codebooks) + fp8 attention, fp32 accumulate"),
     # KDA linear attention (32 heads x 128, fp32 state) + the FP8 256-expert MoE
     "kda_moe256_fp8_decode_layer": ("C6", "traffic_kda_moe256_fp8", "fp8-e4m3 weights, fp32 accumulate and state"),
     # the same stack, one 6-position speculative verify per launch (seeded drafts)
@@ -492,7 +495,8 @@ def main():
                                  f"MLA {shape.n_heads} heads, latent {shape.kv_lora}+{shape.rope_dim}, q_lora {shape.q_lora}"
                                  + (f", indexer {shape.index_heads}x{shape.index_dim} top-{shape.index_topk}"
                                     if shape.index_topk else "")),
-                   "weights": shape.wfmt, "kv_cache_tokens": pos,
+                   "weights": shape.wfmt + (f", experts {shape.expert_fmt}" if shape.expert_fmt else ""),
+                   "kv_cache_tokens": pos,
                    "experts": f"{shape.n_experts} top-{shape.top_k} + {shape.n_shared} shared ({shape.router})",
                    "expert_inter": shape.inter, "layers_per_launch": R, "tokens_per_step": 1, "batch": 1},
         "achieved_TBps": round(achieved / 1e3, 3),

@@ -35,6 +35,8 @@ def swiglu_flops(d: int, m: int) -> int:
 
 
 def _mat_bytes(out_dim: int, in_dim: int, fmt: str) -> int:
+    if fmt == "lut3":   # 3-bit indices + one 8-byte codebook per 8 x 64 block = 3.125 bits per weight
+        return out_dim * in_dim * 3 // 8 + (out_dim // 8) * (in_dim // 64) * 8
     if fmt == "fp8":
         return out_dim * in_dim + 4 * math.ceil(out_dim / 128) * math.ceil(in_dim / 128)
     return 2 * out_dim * in_dim
@@ -61,7 +63,8 @@ def layer_weight_bytes(s: LayerShape) -> dict:
             g["indexer"] = (_mat_bytes(s.index_heads * s.index_dim, s.q_lora, f) + _mat_bytes(s.index_heads, H, "bf16")
                             + _mat_bytes(s.index_dim, H, f))
     n_active = 1 if s.ffn == "dense" else s.top_k + s.n_shared
-    g["experts"] = n_active * (2 * _mat_bytes(s.inter, H, f) + _mat_bytes(H, s.inter, f))
+    fe = s.expert_fmt or f
+    g["experts"] = n_active * (2 * _mat_bytes(s.inter, H, fe) + _mat_bytes(H, s.inter, fe))
     if s.ffn == "moe":
         g["router"] = 2 * s.n_experts * H + (4 * s.n_experts if s.router == "sigmoid_bias" else 0)
     g["norms"] = 4 * (2 * H + ((s.q_lora + s.kv_lora) if s.attn == "mla" else 0)
@@ -118,7 +121,7 @@ def verify_layer_bytes(s: LayerShape, pos: int, n_query: int) -> float:
     attention weights and the cache rows once, the expected union of the positions' routed
     experts plus the shared ones, the n appended rows and the n input/output vectors."""
     g = layer_weight_bytes(s)
-    f = s.wfmt
+    f = s.expert_fmt or s.wfmt
     one_expert = 2 * _mat_bytes(s.inter, s.hidden, f) + _mat_bytes(s.hidden, s.inter, f)
     experts = (expected_union_experts(s.n_experts, s.top_k, n_query) + s.n_shared) * one_expert
     other = sum(v for k, v in g.items() if k != "experts")

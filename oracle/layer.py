@@ -94,7 +94,9 @@ class Counted:
 
     def matrix(self, name, expert=0):
         m = self.src.matrix(name, expert)
-        if m["fmt"] == "fp8":
+        if m["fmt"] == "lut3":
+            self._count((name, expert), m["idx"].size + m["codebook"].size)
+        elif m["fmt"] == "fp8":
             self._count((name, expert), m["codes"].size + 4 * m["scales"].size)
         else:
             self._count((name, expert), 2 * m["bits"].size)
@@ -117,6 +119,8 @@ class Counted:
 
 
 def weight_f64(m: Dict) -> np.ndarray:
+    if m["fmt"] == "lut3":
+        return nx.dequant_lut3(m["idx"], m["codebook"])
     if m["fmt"] == "fp8":
         return nx.dequant_fp8_block(m["codes"], m["scales"])
     return nx.bf16_to_f64(m["bits"])

@@ -16,7 +16,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pld.h")
 
 PLD_OK, PLD_E_INVALID, PLD_E_UNSUPPORTED, PLD_E_CAPACITY, PLD_E_HIP, PLD_E_DEVICE_TIMEOUT, PLD_E_STATE = 0, -1, -2, -3, -4, -5, -6
 PLD_ATTN_GQA, PLD_ATTN_MLA, PLD_ATTN_KDA = 0, 1, 2
-PLD_WFMT_BF16, PLD_WFMT_FP8_BLOCK128 = 0, 1
+PLD_WFMT_BF16, PLD_WFMT_FP8_BLOCK128, PLD_WFMT_LUT3 = 0, 1, 2
 PLD_FFN_DENSE, PLD_FFN_MOE = 0, 1
 PLD_ROUTER_SOFTMAX_TOPK, PLD_ROUTER_SIGMOID_BIAS = 0, 1
 
@@ -36,7 +36,8 @@ class PldConfig(ctypes.Structure):
         "attn_kind", "wfmt", "hidden", "n_heads", "n_kv_heads", "head_dim", "q_lora", "kv_lora", "rope_dim",
         "nope_dim", "v_dim", "index_heads", "index_dim", "index_topk", "ffn_kind", "inter", "n_experts", "top_k",
         "n_shared", "router_kind", "max_seq")] + [("eps", f64), ("rope_base", f64), ("vocab", i32),
-                                                   ("kda_rank", i32), ("conv_width", i32), ("reserved", i32 * 3)]
+                                                   ("kda_rank", i32), ("conv_width", i32), ("expert_wfmt", i32),
+                                                   ("reserved", i32 * 2)]
 
 
 class PldMatrix(ctypes.Structure):
@@ -144,6 +145,7 @@ def config_from_shape(s, vocab: int = 0) -> PldConfig:
     c.router_kind = PLD_ROUTER_SIGMOID_BIAS if s.router == "sigmoid_bias" else PLD_ROUTER_SOFTMAX_TOPK
     c.max_seq, c.eps, c.rope_base, c.vocab = s.max_seq, s.eps, s.rope_base, vocab
     c.kda_rank, c.conv_width = s.kda_rank, s.conv_width
+    c.expert_wfmt = PLD_WFMT_LUT3 if s.expert_fmt == "lut3" else 0
     return c
 
 

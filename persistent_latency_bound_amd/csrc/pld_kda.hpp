@@ -32,6 +32,7 @@ template <int H_, int NH_, int D_, int R_, int CW_, int INTER_, bool FP8_, bool 
 struct KdaShape {
   static constexpr int H = H_, NH = NH_, D = D_, R = R_, CW = CW_, INTER = INTER_;
   static constexpr bool FP8 = FP8_, MOE = MOE_;
+  static constexpr bool LUTX = false;
   static constexpr int QD = NH * D, ODIM = QD;
   static constexpr int NCH = 3 * QD;                 // convolution channels (q, k, v)
   static constexpr int ROWS = 4 * QD + R + NH;       // [W_q; W_k; W_v; W_g; W_adown; W_beta]

@@ -79,6 +79,7 @@ struct DLayer {
   const float* router_bias;
   DMat w_gate, w_up, w_down;
   size_t gu_slot_bytes, gu_slot_scales, dn_slot_bytes, dn_slot_scales;
+  size_t gu_slot_cb, dn_slot_cb;   // LUT3 experts: codebook bytes per expert slot
   uint16_t *kc, *vc, *lat;
   uint8_t* icodes;
   float* iscales;
@@ -333,6 +334,11 @@ __device__ __forceinline__ void rmsnorm_reg(float* act, const RegVec<N>& gam, do
 #define PLD_IF_DOWN 8
 #endif
 
+// LUT3 expert GEMVs: (row, 128-weight group) items in flight per lane (4 loads of 16 bytes each)
+#ifndef PLD_LUT_ITEMS
+#define PLD_LUT_ITEMS 2
+#endif
+
 constexpr int RT_SLOTS = 8;      // experts per lane in the router top-k: E <= 64 * RT_SLOTS
 constexpr int RT_RANK_MAX = 64;  // up to this many experts the top-k counts ranks instead
 
@@ -404,6 +410,7 @@ struct GqaShape {
   static constexpr int H = H_, NH = NH_, NKV = NKV_, HD = HD_, INTER = INTER_, ATT_NB = ATT_NB_, ATT_NV = ATT_NV_;
   static constexpr int G = NH / NKV, ODIM = NH * HD;
   static constexpr bool FP8 = FP8_, MOE = MOE_;
+  static constexpr bool LUTX = false;   // expert matrices in the weight format of the layer
   static_assert(H % 2 == 0 && ODIM % 2 == 0, "hidden sizes must be even");
 };
 
@@ -922,17 +929,28 @@ template <class SH, int INFL, typename Pre>
 __device__ __forceinline__ bool gate_up_list(const KArgs& a, const Step& st, Lds& L, int np, Pre&& pre) {
   const GuPiece* pc = L.pcs;   // written by thread 0 before the call, published by seg_begin
   const DLayer Ly = *gp(st.Ly);
-  constexpr size_t RB = (size_t)SH::H * (SH::FP8 ? 1 : 2);
+  constexpr size_t RB = SH::LUTX ? (size_t)SH::H * 3 / 8 : (size_t)SH::H * (SH::FP8 ? 1 : 2);
   seg_begin();
   for (int p = 0; p < np; p++) {
     const size_t bo = (size_t)pc[p].expert * Ly.gu_slot_bytes + (size_t)pc[p].j0 * RB;
-    const float* sg = SH::FP8 ? Ly.w_gate.s + (size_t)pc[p].expert * Ly.gu_slot_scales : nullptr;
-    const float* su = SH::FP8 ? Ly.w_up.s + (size_t)pc[p].expert * Ly.gu_slot_scales : nullptr;
+    const float* sg;
+    const float* su;
+    if constexpr (SH::LUTX) {   // the slot's codebooks (bytes)
+      sg = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(Ly.w_gate.s) + pc[p].expert * Ly.gu_slot_cb);
+      su = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(Ly.w_up.s) + pc[p].expert * Ly.gu_slot_cb);
+    } else {
+      sg = SH::FP8 ? Ly.w_gate.s + (size_t)pc[p].expert * Ly.gu_slot_scales : nullptr;
+      su = SH::FP8 ? Ly.w_up.s + (size_t)pc[p].expert * Ly.gu_slot_scales : nullptr;
+    }
     seg_set(L, 2 * p, Ly.w_gate.w + bo, sg, pc[p].j1 - pc[p].j0, pc[p].j0, 0, 1.f);
     seg_set(L, 2 * p + 1, Ly.w_up.w + bo, su, pc[p].j1 - pc[p].j0, pc[p].j0, 0, 1.f);
   }
   seg_end();
-  if (!gemv_list<SH::FP8, SH::H, INFL>(L.segs, 2 * np, L.act, L.outb, OUT_STORE, pre)) return false;
+  if constexpr (SH::LUTX) {
+    if (!gemv_list_lut<SH::H, PLD_LUT_ITEMS>(L.segs, 2 * np, L.act, L.outb, OUT_STORE, pre)) return false;
+  } else {
+    if (!gemv_list<SH::FP8, SH::H, INFL>(L.segs, 2 * np, L.act, L.outb, OUT_STORE, pre)) return false;
+  }
   __syncthreads();
   uint64_t* mll = wsp<uint64_t>(a, a.off.m);
   int base = 0;
@@ -1178,17 +1196,26 @@ __device__ __forceinline__ bool stage_down(Ctx& cx, const KArgs& a, const Step& 
   };
   {
     // all slots' rows [r0, r1) as one list; slot s reads activation m_s
-    constexpr size_t RB = (size_t)SH::INTER * (SH::FP8 ? 1 : 2);
+    constexpr size_t RB = SH::LUTX ? (size_t)SH::INTER * 3 / 8 : (size_t)SH::INTER * (SH::FP8 ? 1 : 2);
     seg_begin();
     for (int s = 0; s < c.slots; s++) {
       const int expert = !SH::MOE ? 0 : (s < c.topk ? L.isel[s] : c.E + (s - c.topk));
       const size_t bo = (size_t)expert * Ly.dn_slot_bytes + (size_t)r0 * RB;
-      const float* sd = SH::FP8 ? Ly.w_down.s + (size_t)expert * Ly.dn_slot_scales : nullptr;
+      const float* sd;
+      if constexpr (SH::LUTX)
+        sd = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(Ly.w_down.s) + expert * Ly.dn_slot_cb);
+      else
+        sd = SH::FP8 ? Ly.w_down.s + (size_t)expert * Ly.dn_slot_scales : nullptr;
       seg_set(L, s, Ly.w_down.w + bo, sd, r1 - r0, r0, apad<SH::FP8>(s * SH::INTER), 1.f);
     }
     seg_end();
-    if (!gemv_list<SH::FP8, SH::INTER, PLD_IF_DOWN>(L.segs, r1 > r0 ? c.slots : 0, L.act, L.outb, OUT_STORE, pre_m))
-      return false;
+    if constexpr (SH::LUTX) {
+      if (!gemv_list_lut<SH::INTER, PLD_LUT_ITEMS>(L.segs, r1 > r0 ? c.slots : 0, L.act, L.outb, OUT_STORE, pre_m))
+        return false;
+    } else {
+      if (!gemv_list<SH::FP8, SH::INTER, PLD_IF_DOWN>(L.segs, r1 > r0 ? c.slots : 0, L.act, L.outb, OUT_STORE, pre_m))
+        return false;
+    }
   }
   stamp(a, cx, st, TR_DOWN_GEMV);
   if (!pre_m()) return false;
@@ -1458,6 +1485,8 @@ using ShapeSparseMla = MlaShape<4096, 32, 1536, 512, 64, 128, 128, 1536, false, 
 // the KDA MoE layer: hidden 6144, 32 KDA heads x 128, decay rank 128, convolution width 4,
 // FP8 weights, 256 experts of width 2048 (biased-score router)
 using ShapeKda = KdaShape<6144, 32, 128, 128, 4, 2048, true, true>;
+// the FP8 MLA MoE layer with LUT3 expert matrices (3-bit indices into 8-entry E4M3 codebooks)
+using ShapeMlaLut = MlaShape<6144, 64, 1536, 512, 64, 128, 128, 2048, true, true, false, 0, 0, 16, true>;
 
 template <class SH>
 static bool matches_kda(const pld_config* c) {
@@ -1479,12 +1508,14 @@ static bool matches_mla(const pld_config* c) {
          c->kv_lora == SH::KL && c->rope_dim == SH::RD && c->nope_dim == SH::ND && c->v_dim == SH::VD &&
          c->inter == SH::INTER && (c->wfmt == PLD_WFMT_FP8_BLOCK128) == SH::FP8 &&
          (c->ffn_kind == PLD_FFN_MOE) == SH::MOE && (c->index_topk > 0) == SH::SPARSE &&
-         (!SH::SPARSE || (c->index_heads == SH::IH && c->index_dim == SH::ID));
+         (!SH::SPARSE || (c->index_heads == SH::IH && c->index_dim == SH::ID)) &&
+         (c->expert_wfmt == PLD_WFMT_LUT3) == SH::LUTX;
 }
 
 // heads per MLA attention workgroup of the compiled shape the configuration selects
 static int mla_hpw(const pld_config* c) {
   if (matches_mla<ShapeMlaFp8>(c)) return ShapeMlaFp8::HPW;
+  if (matches_mla<ShapeMlaLut>(c)) return ShapeMlaLut::HPW;
   if (matches_mla<ShapeSparseMla>(c)) return ShapeSparseMla::HPW;
   return 0;
 }
@@ -1494,6 +1525,7 @@ static KernelFn pick_kernel(const pld_config* c) {
   if (matches<ShapeGqaMoe>(c)) return k_decode_gqa<ShapeGqaMoe>;
   if (matches_mla<ShapeMlaFp8>(c)) return k_decode_mla<ShapeMlaFp8>;
   if (matches_mla<ShapeSparseMla>(c)) return k_decode_mla<ShapeSparseMla>;
+  if (matches_mla<ShapeMlaLut>(c)) return k_decode_mla<ShapeMlaLut>;
   if (matches_kda<ShapeKda>(c)) return k_decode_kda<ShapeKda>;
   return nullptr;
 }
@@ -1556,6 +1588,11 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
   k->krank = c->kda_rank; k->cwidth = c->conv_width;
   if (c->hidden <= 0 || c->n_heads <= 0 || c->max_seq <= 0 || c->inter <= 0 || !(c->eps >= 0.0)) return PLD_E_INVALID;
   if (c->wfmt != PLD_WFMT_BF16 && c->wfmt != PLD_WFMT_FP8_BLOCK128) return PLD_E_UNSUPPORTED;
+  if (c->expert_wfmt != 0 && c->expert_wfmt != PLD_WFMT_LUT3) return PLD_E_UNSUPPORTED;
+  // LUT3 experts: whole 16-lane rows of 128-weight groups for both reduction lengths
+  if (c->expert_wfmt == PLD_WFMT_LUT3 && (c->ffn_kind != PLD_FFN_MOE || c->wfmt != PLD_WFMT_FP8_BLOCK128 ||
+                                          c->hidden % 2048 || c->inter % 2048 || c->inter % 8 || c->hidden % 8))
+    return PLD_E_UNSUPPORTED;
   if (nwg < NXCD || nwg % NXCD) return PLD_E_UNSUPPORTED;
   if (c->ffn_kind == PLD_FFN_DENSE) {
     k->slots = 1;
@@ -1874,15 +1911,24 @@ pld_status build_layer(const pld_config* cfg, const pld_layer_weights& L, const 
       d.w_ki = dmat(L.w_ki, ID, H, fp8);
     }
   }
-  if (!mat_ok(L.w_gate, fp8) || !mat_ok(L.w_up, fp8) || !mat_ok(L.w_down, fp8)) return PLD_E_INVALID;
-  d.w_gate = dmat(L.w_gate, cfg->inter, H, fp8);
-  d.w_up = dmat(L.w_up, cfg->inter, H, fp8);
-  d.w_down = dmat(L.w_down, H, cfg->inter, fp8);
-  const size_t wb = fp8 ? 1 : 2;
-  d.gu_slot_bytes = (size_t)cfg->inter * H * wb;
-  d.dn_slot_bytes = (size_t)H * cfg->inter * wb;
-  d.gu_slot_scales = fp8 ? (size_t)((cfg->inter + 127) / 128) * ((H + 127) / 128) : 0;
-  d.dn_slot_scales = fp8 ? (size_t)((H + 127) / 128) * ((cfg->inter + 127) / 128) : 0;
+  const bool lutx = cfg->expert_wfmt == PLD_WFMT_LUT3;   // codebooks are required like FP8 scales
+  if (!mat_ok(L.w_gate, fp8 || lutx) || !mat_ok(L.w_up, fp8 || lutx) || !mat_ok(L.w_down, fp8 || lutx))
+    return PLD_E_INVALID;
+  d.w_gate = dmat(L.w_gate, cfg->inter, H, fp8 || lutx);
+  d.w_up = dmat(L.w_up, cfg->inter, H, fp8 || lutx);
+  d.w_down = dmat(L.w_down, H, cfg->inter, fp8 || lutx);
+  if (lutx) {
+    d.gu_slot_bytes = (size_t)cfg->inter * H * 3 / 8;
+    d.dn_slot_bytes = (size_t)H * cfg->inter * 3 / 8;
+    d.gu_slot_cb = (size_t)(cfg->inter / 8) * (H / 64) * 8;
+    d.dn_slot_cb = (size_t)(H / 8) * (cfg->inter / 64) * 8;
+  } else {
+    const size_t wb = fp8 ? 1 : 2;
+    d.gu_slot_bytes = (size_t)cfg->inter * H * wb;
+    d.dn_slot_bytes = (size_t)H * cfg->inter * wb;
+    d.gu_slot_scales = fp8 ? (size_t)((cfg->inter + 127) / 128) * ((H + 127) / 128) : 0;
+    d.dn_slot_scales = fp8 ? (size_t)((H + 127) / 128) * ((cfg->inter + 127) / 128) : 0;
+  }
   if (moe) {
     if (!L.router || !aligned16(L.router)) return PLD_E_INVALID;
     d.router = (const uint16_t*)L.router;

@@ -15,10 +15,12 @@
 #pragma once
 
 template <int H_, int NH_, int QL_, int KL_, int RD_, int ND_, int VD_, int INTER_, bool FP8_, bool MOE_, bool SPARSE_,
-          int IH_ = 0, int ID_ = 0, int HPW_ = 8>
+          int IH_ = 0, int ID_ = 0, int HPW_ = 8, bool LUTX_ = false>
 struct MlaShape {
   static constexpr int H = H_, NH = NH_, QL = QL_, KL = KL_, RD = RD_, ND = ND_, VD = VD_, INTER = INTER_;
   static constexpr bool FP8 = FP8_, MOE = MOE_, SPARSE = SPARSE_;
+  static constexpr bool LUTX = LUTX_;   // expert matrices as LUT3 (3-bit indices, 8-entry E4M3 codebooks)
+  static_assert(!LUTX || FP8, "LUT3 experts sit in an FP8 layer (padded activation layout)");
   static constexpr int IH = IH_, ID = ID_;        // indexer heads and key width (sparse layers)
   static_assert(!SPARSE || (!FP8 && IH > 0 && ID > 0), "the sparse layer has bf16 weights and an indexer");
   static constexpr int LAT = KL + RD, QH = ND + RD, ODIM = NH * VD;

@@ -108,6 +108,39 @@ __global__ void __launch_bounds__(64) k_fp8_rows(uint8_t* codes, float* scales, 
   }
 }
 
+// LUT3 matrices [rows, cols] (rows % 8 == 0, cols % 128 == 0): one thread per (row, group of
+// 128 weights) writes the group's three 16-byte index planes; one thread per 8x64 block
+// writes its 8 codebook codes. Same definition as synth/gen.py (lut3_matrix).
+__constant__ float LUT_Z[8] = {-1.5341205f, -0.88714653f, -0.48877642f, -0.15731068f,
+                               0.15731068f, 0.48877642f, 0.88714653f, 1.5341205f};
+__global__ void k_lut3(uint8_t* idx, uint8_t* cb, int rows, int cols, uint64_t key, float stdv) {
+  const int64_t n_groups = (int64_t)rows * (cols / 128);
+  const int64_t n_blocks = (int64_t)(rows / 8) * (cols / 64);
+  const int64_t n_w = (int64_t)rows * cols;
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < n_groups + n_blocks;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    if (e < n_groups) {
+      const int64_t row = e / (cols / 128), g = e % (cols / 128);
+      uint32_t w[3][4] = {};
+      for (int d = 0; d < 4; d++)
+        for (int j = 0; j < 32; j++) {
+          const uint64_t i = (uint64_t)(row * cols + g * 128 + 32 * d + j);
+          const uint32_t v = (uint32_t)(mix64(key + (i + 1) * G) & 7u);
+          for (int p = 0; p < 3; p++) w[p][d] |= ((v >> p) & 1u) << j;
+        }
+      uint32_t* dst = reinterpret_cast<uint32_t*>(idx + row * (int64_t)(3 * cols / 8) + g * 48);
+      for (int p = 0; p < 3; p++)
+        for (int d = 0; d < 4; d++) dst[4 * p + d] = w[p][d];
+    } else {
+      const int64_t b = e - n_groups;
+      const uint64_t r = mix64(key + ((uint64_t)(n_w + b) + 1) * G);
+      const float u = __fmul_rn((float)(r >> 40), 0x1p-24f);
+      const float spread = __fadd_rn(0.75f, __fmul_rn(u, 0.5f));
+      for (int k = 0; k < 8; k++) cb[b * 8 + k] = e4m3(__fmul_rn(__fmul_rn(stdv, LUT_Z[k]), spread));
+    }
+  }
+}
+
 int grid_for(int64_t n) {
   int64_t g = (n + 255) / 256;
   if (g > 65536) g = 65536;
@@ -145,6 +178,14 @@ int synth_fill_fp8_block(void* codes, void* scales, int rows, int cols, uint64_t
   const int nb = ((rows + 127) / 128) * ((cols + 127) / 128);
   k_fp8_block<<<nb, 256, 0, (hipStream_t)stream>>>((uint8_t*)codes, (float*)scales, rows, cols, stream_key(seed, tid),
                                                    stdv, 0);
+  return (int)hipGetLastError();
+}
+
+int synth_fill_lut3(void* idx, void* cb, int rows, int cols, uint64_t seed, uint64_t tid, float stdv, void* stream) {
+  if (rows % 8 || cols % 128) return (int)hipErrorInvalidValue;
+  const int64_t n = (int64_t)rows * (cols / 128) + (int64_t)(rows / 8) * (cols / 64);
+  k_lut3<<<grid_for(n), 256, 0, (hipStream_t)stream>>>((uint8_t*)idx, (uint8_t*)cb, rows, cols, stream_key(seed, tid),
+                                                       stdv);
   return (int)hipGetLastError();
 }
 

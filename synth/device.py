@@ -29,7 +29,9 @@ def lib():
         L.synth_fill_f32.argtypes = [vp, i64, u64, u64, f32, f32, i32, vp]
         L.synth_fill_fp8_block.argtypes = [vp, vp, i32, i32, u64, u64, f32, vp]
         L.synth_fill_fp8_rows.argtypes = [vp, vp, i32, i32, u64, u64, f32, vp]
-        for f in (L.synth_fill_bf16_3d, L.synth_fill_f32, L.synth_fill_fp8_block, L.synth_fill_fp8_rows):
+        L.synth_fill_lut3.argtypes = [vp, vp, i32, i32, u64, u64, f32, vp]
+        for f in (L.synth_fill_bf16_3d, L.synth_fill_f32, L.synth_fill_fp8_block, L.synth_fill_fp8_rows,
+                  L.synth_fill_lut3):
             f.restype = ctypes.c_int
         _LIB = L
     return _LIB
@@ -66,6 +68,12 @@ def fill_fp8_matrix(codes: torch.Tensor, scales: torch.Tensor, seed: int, tid: i
                                     seed, tid, std, _stream()), "fill_fp8_matrix")
 
 
+def fill_lut3_matrix(idx: torch.Tensor, cb: torch.Tensor, seed: int, tid: int, std: float):
+    rows, cols = idx.shape[-2], idx.shape[-1] * 8 // 3
+    _chk(lib().synth_fill_lut3(ctypes.c_void_p(idx.data_ptr()), ctypes.c_void_p(cb.data_ptr()), rows, cols, seed, tid,
+                               std, _stream()), "fill_lut3_matrix")
+
+
 def fill_fp8_rows(codes: torch.Tensor, scales: torch.Tensor, n_rows: int, seed: int, tid: int, std: float):
     d = codes.shape[-1]
     _chk(lib().synth_fill_fp8_rows(ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()), n_rows, d,
@@ -78,6 +86,13 @@ def _mat(s: LayerShape, name: str, n_slots: int, dev, seed: int, layer: int):
     std = s.router_std if name == "router" else s.w_std
     expert = name in gen.EXPERT_MATS
     shape = (n_slots, out_dim, in_dim) if expert else (out_dim, in_dim)
+    if gen.weight_format(s, name) == "lut3":
+        idx = torch.empty(shape[:-1] + (in_dim * 3 // 8,), dtype=torch.uint8, device=dev)
+        cb = torch.empty(((n_slots,) if expert else ()) + (out_dim // 8, in_dim // 64, 8), dtype=torch.uint8, device=dev)
+        for e in range(n_slots if expert else 1):
+            fill_lut3_matrix(idx[e] if expert else idx, cb[e] if expert else cb, seed,
+                             gen.tensor_id(name, layer, e if expert else 0), std)
+        return {"fmt": "lut3", "data": idx, "scales": cb}
     if gen.weight_format(s, name) == "fp8":
         codes = torch.empty(shape, dtype=torch.uint8, device=dev)
         nb = (-(-out_dim // 128), -(-in_dim // 128))

@@ -29,6 +29,13 @@ host and device agree bit for bit):
   [-448, 448], then rounded to the nearest E4M3FN value, ties to the even code; the
   sign bit is the sign of ``q`` (a negative value that rounds to zero gives 0x80).
 * Index-key rows use the same FP8 rule with one scale per row.
+* Lookup-table (LUT3) matrices [out, in] (out a multiple of 8, in of 128): draw i = n*in + k
+  gives weight (n, k) the index r_i & 7; draw i = out*in + b gives block b = (n/8)*(in/64) +
+  k/64 its spread s_b = 0.75 + (r_i >> 40) * 2**-24 * 0.5 (fp32 operations), and the block's
+  codebook entry e is the E4M3FN code of fp32(fp32(std * Z_e) * s_b), Z_e the fixed fp32
+  normal quantiles below. Storage: codebook bytes [out/8][in/64][8]; indices as three bit
+  planes per group of 128 weights of a row: 48 bytes, plane p = bytes [16p, 16p + 16) as four
+  little-endian u32, bit j of word d = bit p of the index of weight 32d + j of the group.
 """
 from __future__ import annotations
 
@@ -185,6 +192,31 @@ def fp8_block_quantize(v: np.ndarray, block: int = 128):
     return np.ascontiguousarray(codes), scales
 
 
+# fp32 normal quantiles at (e + 0.5) / 8, the eight codebook positions before the block spread
+LUT_Z = np.array([-1.5341205, -0.88714653, -0.48877642, -0.15731068, 0.15731068, 0.48877642, 0.88714653,
+                  1.5341205], dtype=np.float32)
+
+
+def lut3_matrix(seed: int, tid: int, out_dim: int, in_dim: int, std: float):
+    """(indices uint8 [out, 3*in/8] in bit planes, codebook uint8 [out/8, in/64, 8]) of a LUT3 matrix."""
+    assert out_dim % 8 == 0 and in_dim % 128 == 0
+    n_w = out_dim * in_dim
+    idx = (raw_u64(seed, tid, np.arange(n_w, dtype=np.uint64)) & U64(7)).astype(np.uint8).reshape(out_dim, in_dim)
+    nb = (out_dim // 8) * (in_dim // 64)
+    rb = raw_u64(seed, tid, np.arange(n_w, n_w + nb, dtype=np.uint64))
+    u = (rb >> U64(40)).astype(np.float32) * np.float32(2.0 ** -24)
+    spread = np.float32(0.75) + u * np.float32(0.5)
+    vals = (np.float32(std) * LUT_Z)[None, :] * spread[:, None]          # [nb, 8] fp32
+    cb = f32_to_e4m3_codes(vals.astype(np.float32)).reshape(out_dim // 8, in_dim // 64, 8)
+    g = idx.reshape(out_dim, in_dim // 128, 4, 32)                        # [row, group, word, bit]
+    planes = np.zeros((out_dim, in_dim // 128, 3, 4), dtype=np.uint32)
+    for p in range(3):
+        bits = ((g >> p) & 1).astype(np.uint32)
+        planes[:, :, p, :] = np.sum(bits << np.arange(32, dtype=np.uint32), axis=3, dtype=np.uint32)
+    packed = planes.view(np.uint8).reshape(out_dim, 3 * in_dim // 8)
+    return np.ascontiguousarray(packed), np.ascontiguousarray(cb)
+
+
 def fp8_row_quantize(v: np.ndarray):
     """fp32 [rows, d] -> (codes [rows, d], scales [rows]) with one scale per row."""
     amax = np.abs(v).max(axis=1).astype(np.float32)
@@ -251,6 +283,8 @@ BF16_ALWAYS = ("router", "w_w")
 def weight_format(s: LayerShape, name: str) -> str:
     if name in BF16_ALWAYS:
         return "bf16"
+    if name in EXPERT_MATS and s.expert_fmt:
+        return s.expert_fmt
     return s.wfmt
 
 
@@ -279,6 +313,13 @@ class LayerWeights:
         out_dim, in_dim = self.mats[name]
         sub = expert if name in EXPERT_MATS else 0
         tid = tensor_id(name, self.layer, sub)
+        if weight_format(self.s, name) == "lut3":
+            idx, cb = lut3_matrix(self.seed, tid, out_dim, in_dim, self._std(name))
+            res = {"fmt": "lut3", "idx": idx, "codebook": cb}
+            if len(self._cache) >= self._cache_size:
+                self._cache.pop(next(iter(self._cache)))
+            self._cache[key] = res
+            return res
         v = scaled_normal(self.seed, tid, np.arange(out_dim * in_dim, dtype=np.uint64),
                           self._std(name)).reshape(out_dim, in_dim)
         if weight_format(self.s, name) == "fp8":

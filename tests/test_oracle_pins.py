@@ -683,3 +683,52 @@ def test_kda_convolution_taps_by_hand():
     OL.append_to_cache(s, c, rec, pos)
     assert np.array_equal(c["conv_ring"][pos % 3], rec["kda_x32"].astype(np.float32))
     assert np.array_equal(c["conv_ring"][(pos + 1) % 3], cache["conv_ring"][(pos + 1) % 3])
+
+
+# --------------------------------------------------------------------------- LUT3 weights
+def test_lut3_footprint_is_the_pages_3125_bits_per_weight():
+    """3 bits of index per weight plus one 8-byte codebook per 8 x 64 block: 3.125 bits per
+    weight, the stored footprint the page computes (2.8e12 x 3.125 / 8 = 1,093.75 GB)."""
+    for out_dim, in_dim in ((8, 128), (2048, 6144), (6144, 2048)):
+        b = accounting._mat_bytes(out_dim, in_dim, "lut3")
+        assert b * 8 == 3.125 * out_dim * in_dim
+    assert accounting.weight_bytes(2.8e12, 3.125) == 1093.75e9
+
+
+def test_lut3_decode_by_hand_from_bytes():
+    """The oracle's decode against a byte-level reading of the planes written out here
+    (bit j % 8 of byte 16 p + 4 d + j // 8 of the group), and every weight is one of the
+    8 E4M3 values of its block's codebook."""
+    out_dim, in_dim = 16, 256
+    idx, cb = gen.lut3_matrix(0, 77, out_dim, in_dim, 0.02)
+    W = nx.dequant_lut3(idx, cb)
+    for n in range(out_dim):
+        for k in range(in_dim):
+            g, w = divmod(k, 128)
+            d, j = divmod(w, 32)
+            i = 0
+            for p in range(3):
+                byte = idx[n, 48 * g + 16 * p + 4 * d + j // 8]
+                i |= ((int(byte) >> (j % 8)) & 1) << p
+            assert W[n, k] == nx.E4M3[cb[n // 8, k // 64, i]]
+    # the drawn indices are the low 3 bits of the generator's draws
+    raw = gen.raw_u64(0, 77, np.arange(out_dim * in_dim, dtype=np.uint64)) & np.uint64(7)
+    for n, k in ((0, 0), (3, 200), (15, 255)):
+        assert W[n, k] == nx.E4M3[cb[n // 8, k // 64, int(raw[n * in_dim + k])]]
+
+
+def test_layer_with_lut3_experts_equals_explicit_dequantised_weights():
+    """A layer whose experts are LUT3 equals the same layer given those experts as explicit
+    (bf16-exact E4M3) matrices: the lookup is the only difference in the definition."""
+    s = tiny_mla(wfmt="fp8", expert_fmt="lut3", hidden=128, inter=128)
+    base = gen.LayerWeights(s, 0, 0)
+    cache = gen.padded_cache(s)
+    x = gen.input_hidden(s)
+    ov = {}
+    for e in range(s.n_experts + s.n_shared):
+        for name in ("w_gate", "w_up", "w_down"):
+            ov[(name, e)] = nx.dequant_lut3(base.matrix(name, e)["idx"], base.matrix(name, e)["codebook"])
+    ref = OL.decode_layer(s, DictWeights(s, base=base, overrides=ov), {k: v.copy() for k, v in cache.items()}, x,
+                          s.cache_len)
+    got = OL.decode_layer(s, base, {k: v.copy() for k, v in cache.items()}, x, s.cache_len)
+    assert np.array_equal(got["out_f64"], ref["out_f64"])
