@@ -195,6 +195,10 @@ typedef struct pld_handle pld_handle;
  * Returns 0 for an invalid or unsupported configuration. */
 size_t pld_workspace_bytes(const pld_config* cfg, int32_t n_layers);
 
+/* The same size for a device with n_cus compute units (one workgroup per CU), without
+ * querying any device: for planning allocations off the GPU. */
+size_t pld_workspace_bytes_for_cus(const pld_config* cfg, int32_t n_layers, int32_t n_cus);
+
 /* Validate the configuration and pointers, build the static per-workgroup schedule
  * (the ahead-of-time scheduling of the TileRT article, section "Why Is TileRT
  * Development Slow?", done here at init), upload the RoPE table and layer

@@ -25,6 +25,7 @@ EXPORTS = (
     "pld_workspace_bytes", "decode_layer_init", "decode_step", "decode_layers_persistent", "decode_poll_status",
     "decode_reset", "decode_layer_destroy", "pld_status_string", "pld_debug_buffer", "pld_launch_shape",
     "pld_set_watchdog_us", "pld_set_trace", "pld_set_test_hooks", "decode_layer_init_static", "decode_speculative",
+    "pld_workspace_bytes_for_cus",
 )
 PLD_HOOK_DROP_WG0, PLD_HOOK_DELAY = 1, 2
 
@@ -92,6 +93,8 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.pld_workspace_bytes.argtypes = [ctypes.POINTER(PldConfig), i32]
         L.pld_workspace_bytes.restype = ctypes.c_size_t
+        L.pld_workspace_bytes_for_cus.argtypes = [ctypes.POINTER(PldConfig), i32, i32]
+        L.pld_workspace_bytes_for_cus.restype = ctypes.c_size_t
         L.decode_layer_init.argtypes = [ctypes.POINTER(PldConfig), i32, ctypes.POINTER(PldLayerWeights),
                                         ctypes.POINTER(PldKvCache), ctypes.POINTER(PldHeadWeights), vp,
                                         ctypes.c_size_t, ctypes.POINTER(vp)]

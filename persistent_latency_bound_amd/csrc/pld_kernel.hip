@@ -37,6 +37,7 @@
 
 #include "../../include/pld.h"
 #include "pld_device.hpp"
+#include "pld_math.hpp"
 
 namespace pld {
 
@@ -245,30 +246,9 @@ constexpr int per_for(int n) { return n <= BLOCK ? 1 : (n + BLOCK - 1) / BLOCK >
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// e^x in fp64 for the router (a handful of threads per step): x = k ln2 + r with ln2
-// split into a head with trailing zero bits and a tail (k ln2_hi is exact), |r| <= ln2/2,
-// e^r by its Taylor series to degree 13 in Horner form (truncation < 1e-17 relative),
-// then scaled by 2^k. The constants are read from LDS (dk, written at kernel start):
-// literal fp64 constants would be hoisted out of the layer loop into registers that
-// stay live, and spill, across every stage.
-constexpr int EXP_TERMS = 13;
+// The router's fp64 exp (pld_math.hpp) reads its constants from LDS (dk, written at kernel start).
 __device__ __forceinline__ void exp_f64_init(double* dk) {
-  if (tid_opaque() == 0) {
-    dk[0] = 1.4426950408889634;         // 1/ln2
-    dk[1] = 6.93147180369123816490e-01; // ln2 head
-    dk[2] = 1.90821492927058770002e-10; // ln2 tail
-    for (int n = 1; n <= EXP_TERMS; n++) dk[2 + n] = 1.0 / (double)n;
-  }
-}
-__device__ __forceinline__ double exp_f64(double x, const double* dk) {
-  if (x > 709.0) return INFINITY;
-  if (x < -745.0) return 0.0;
-  const double k = rint(x * dk[0]);
-  double r = fma(-k, dk[1], x);
-  r = fma(-k, dk[2], r);
-  double p = 1.0;
-  for (int n = EXP_TERMS; n >= 1; n--) p = fma(p, r * dk[2 + n], 1.0);
-  return ldexp(p, (int)k);
+  if (tid_opaque() == 0) exp_f64_consts(dk);
 }
 
 // This thread's elements i = tid_opaque() + k*BLOCK of a length-N fp32 vector, held in
@@ -1587,6 +1567,19 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
   k->max_seq = c->max_seq; k->vocab = c->vocab; k->eps = c->eps; k->nwg = nwg;
   k->krank = c->kda_rank; k->cwidth = c->conv_width;
   if (c->hidden <= 0 || c->n_heads <= 0 || c->max_seq <= 0 || c->inter <= 0 || !(c->eps >= 0.0)) return PLD_E_INVALID;
+  // every size field within bounds that keep the sizing arithmetic below in range (unused
+  // fields of another layer kind included), a finite eps and RoPE base
+  {
+    const int32_t dims[] = {c->hidden, c->n_heads, c->n_kv_heads, c->head_dim, c->q_lora, c->kv_lora, c->rope_dim,
+                            c->nope_dim, c->v_dim, c->index_heads, c->index_dim, c->index_topk, c->inter,
+                            c->n_experts, c->top_k, c->n_shared, c->kda_rank, c->conv_width};
+    for (int32_t d : dims)
+      if (d < 0 || d > (1 << 16)) return PLD_E_INVALID;
+    if (c->n_heads > 1024 || c->n_kv_heads > 1024 || c->head_dim > 1024 || c->max_seq > (1 << 22) ||
+        c->vocab > (1 << 22) || nwg < 1 || nwg > 4096 || !(c->eps <= 1.0) || !(c->rope_base > 0.0) ||
+        !(c->rope_base < 1e300))
+      return PLD_E_INVALID;
+  }
   if (c->wfmt != PLD_WFMT_BF16 && c->wfmt != PLD_WFMT_FP8_BLOCK128) return PLD_E_UNSUPPORTED;
   if (c->expert_wfmt != 0 && c->expert_wfmt != PLD_WFMT_LUT3) return PLD_E_UNSUPPORTED;
   // LUT3 experts: whole 16-lane rows of 128-weight groups for both reduction lengths
@@ -1627,10 +1620,13 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
     // (the GEMV inputs in their LDS layout: padded for FP8 weights)
     const bool pad = c->wfmt == PLD_WFMT_FP8_BLOCK128;
     auto ap = [pad](int n) { return pad ? apad<true>(n) : n; };
-    int act = std::max({ap(c->hidden), ap(c->n_heads * c->head_dim), ap(k->slots * c->inter),
-                        2 * k->G * c->head_dim + c->head_dim + k->G * k->chmax + NWAVES * k->G * c->head_dim + 2 * k->G + 8,
-                        k->cpg * (k->G * c->head_dim / k->cpg + 1) + 8 * k->cpg + 8});
-    k->act_floats = (int)al(act, 64);
+    using ll = long long;
+    const ll act = std::max<ll>({ap(c->hidden), ap(c->n_heads * c->head_dim), ap(k->slots * c->inter),
+                                 2LL * k->G * c->head_dim + c->head_dim + (ll)k->G * k->chmax +
+                                     (ll)NWAVES * k->G * c->head_dim + 2 * k->G + 8,
+                                 (ll)k->cpg * (k->G * c->head_dim / k->cpg + 1) + 8LL * k->cpg + 8});
+    if (act > (1 << 20)) return PLD_E_UNSUPPORTED;
+    k->act_floats = (int)al((size_t)act, 64);
     k->stage_words = (int)al(c->hidden / 2 + 2, 64);
     int outb = std::max({R / nwg + 4, k->slots * (c->hidden / nwg + 4), 2 * ((k->slots * c->inter) / nwg + 2),
                          2 * (c->inter / nwg + 2) * std::max(1, c->n_shared), 4 * c->n_experts + 4,
@@ -1821,11 +1817,15 @@ const char* pld_status_string(pld_status s) {
 }
 
 size_t pld_workspace_bytes(const pld_config* cfg, int32_t n_layers) {
-  if (!cfg || n_layers < 1) return 0;
   const int nwg = device_cus(nullptr);
   if (nwg <= 0) return 0;
+  return pld_workspace_bytes_for_cus(cfg, n_layers, nwg);
+}
+
+size_t pld_workspace_bytes_for_cus(const pld_config* cfg, int32_t n_layers, int32_t n_cus) {
+  if (!cfg || n_layers < 1 || n_cus < 1) return 0;
   KCfg k;
-  if (derive(cfg, nwg, &k) != PLD_OK) return 0;
+  if (derive(cfg, n_cus, &k) != PLD_OK) return 0;
   return layout(k, n_layers).total;
 }
 
