@@ -99,7 +99,10 @@ typedef struct pld_config {
                                 word d = bit p of the index of weight 32d+j of the group), 3*in/8 bytes
                                 per row; scales = the codebook bytes [out/8][in/64][8] (entry e of a
                                 block = byte e), cast to const float*. */
-  int32_t reserved[2];
+  int32_t max_query;         /* 0 or 1: no batched verify; 2..8: the workspace also holds the buffers of
+                                decode_verify_batched for up to max_query positions (FP8 MLA MoE layers
+                                with an LM head only, else PLD_E_UNSUPPORTED) */
+  int32_t reserved[1];
 } pld_config;
 
 typedef struct pld_matrix {
@@ -269,6 +272,28 @@ pld_status decode_step(pld_handle* h, int32_t layer, const void* x_in, int32_t p
  * PLD_E_STATE, PLD_E_HIP. */
 pld_status decode_layers_persistent(pld_handle* h, const pld_persistent_args* a, void* stream);
 
+/* The same verify with the positions batched: the n_query positions (2 .. cfg->max_query,
+ * at most 8) go through every layer together, so each weight matrix is read from HBM once
+ * per verify instead of once per position. The vLLM Kimi K3 backend article scores a draft
+ * of six tokens in one forward pass (its summary and "Throughput holds across the tested
+ * range") and lists shape-aware matmuls among its changes ("Four changes drive the gains").
+ * Here the dense projections (W_DQ, W_DKV, W_UQ, W_UV, W_O, the shared experts) and the
+ * union of the experts the positions route to run on the matrix cores as skinny GEMMs
+ * [rows x K] x [K x n_query]: the FP8 weights are widened to bf16 in registers (exactly),
+ * the normalised activations enter as bf16, accumulation is fp32; an expert chosen by
+ * several positions is read once for all of them. The router logits stay fp64 from fp32
+ * activations and the head stays the fp64 one, so the expert choice and the token choice
+ * are decided as in decode_layers_persistent. Attention reads the shared history once per
+ * pair of positions; position j sees the new rows of positions 0..j.
+ * Arguments as for a verify in decode_layers_persistent (n_tokens must be 1, in_token >= 0
+ * and draft_tokens set); out_hidden receives the last position's final hidden state. The
+ * results agree with the sequential verify to the rounding of the bf16 activation operands
+ * (they are not bit-identical to it).
+ * FP8 MLA MoE stacks with an LM head whose handle was created with cfg->max_query >= 2.
+ * Errors: PLD_E_UNSUPPORTED (handle without batched verify), PLD_E_INVALID, PLD_E_CAPACITY,
+ * PLD_E_STATE, PLD_E_HIP. */
+pld_status decode_verify_batched(pld_handle* h, const pld_persistent_args* a, void* stream);
+
 /* Arguments of decode_speculative. */
 typedef struct pld_spec_args {
   int32_t start_pos;     /* cache position of in_token; both caches hold rows 0 .. start_pos-1 */
@@ -323,8 +348,12 @@ const char* pld_status_string(pld_status s);
  * are the payload and high 32 bits the step epoch: "q", "o", "h2", "m" (fp32 payloads),
  * "x" (bf16 pairs), "logits" (4 words per expert: logit and selection key as fp64,
  * low then high halves), "part" (attention partials), "kv" (GQA: the new k/v row),
- * "amax" (LM head: per-workgroup best logit and token). Returns PLD_E_INVALID for an
- * unknown name. */
+ * "amax" (LM head: per-workgroup best logit and token). Batched verify (handles with
+ * max_query >= 2; per-position copies, position p at p * (size / 8)): "vx" (bf16 pairs, each
+ * layer's output), "vcq", "vckv", "volat", "vh2" (fp32), "vqlat", "vo" (bf16 pairs), and the
+ * plain arrays "vsel" (int32 [8][8] top-k experts per position, then fp32 [8][8] gates) and
+ * "vf" (fp32 [8][hidden], each position's FFN output before the residual add).
+ * Returns PLD_E_INVALID for an unknown name or a buffer the handle does not have. */
 pld_status pld_debug_buffer(pld_handle* h, const char* name, void** ptr, size_t* bytes);
 
 /* Launch geometry actually used: number of workgroups and threads per workgroup. */

@@ -25,7 +25,7 @@ EXPORTS = (
     "pld_workspace_bytes", "decode_layer_init", "decode_step", "decode_layers_persistent", "decode_poll_status",
     "decode_reset", "decode_layer_destroy", "pld_status_string", "pld_debug_buffer", "pld_launch_shape",
     "pld_set_watchdog_us", "pld_set_trace", "pld_set_test_hooks", "decode_layer_init_static", "decode_speculative",
-    "pld_workspace_bytes_for_cus",
+    "pld_workspace_bytes_for_cus", "decode_verify_batched",
 )
 PLD_HOOK_DROP_WG0, PLD_HOOK_DELAY = 1, 2
 
@@ -38,7 +38,7 @@ class PldConfig(ctypes.Structure):
         "nope_dim", "v_dim", "index_heads", "index_dim", "index_topk", "ffn_kind", "inter", "n_experts", "top_k",
         "n_shared", "router_kind", "max_seq")] + [("eps", f64), ("rope_base", f64), ("vocab", i32),
                                                    ("kda_rank", i32), ("conv_width", i32), ("expert_wfmt", i32),
-                                                   ("reserved", i32 * 2)]
+                                                   ("max_query", i32), ("reserved", i32 * 1)]
 
 
 class PldMatrix(ctypes.Structure):
@@ -79,7 +79,8 @@ class PldSpecArgs(ctypes.Structure):
 
 # intermediates kept as LL words (32-bit payload, 32-bit epoch) in the workspace
 LL_BUFFERS = ("q", "o", "h2", "logits", "m", "x", "cq", "ckv", "qrope", "qlat", "olat", "qi", "ixr", "isel", "ilist",
-              "part", "kv", "amax")
+              "part", "kv", "amax",
+              "vx", "vcq", "vckv", "vqlat", "volat", "vo", "vh2")
 
 _lib = None
 
@@ -115,7 +116,9 @@ def lib():
         L.pld_set_watchdog_us.argtypes = [vp, ctypes.c_int64]
         L.pld_set_trace.argtypes = [vp, vp, ctypes.c_size_t]
         L.pld_set_test_hooks.argtypes = [vp, i32, ctypes.c_uint32]
-        for f in ("decode_layer_init", "decode_layer_init_static", "decode_speculative", "decode_step", "decode_layers_persistent", "decode_poll_status",
+        L.decode_verify_batched.argtypes = [vp, vp, vp]
+        for f in ("decode_layer_init", "decode_layer_init_static", "decode_speculative", "decode_step",
+                  "decode_layers_persistent", "decode_verify_batched", "decode_poll_status",
                   "decode_reset", "pld_debug_buffer", "pld_launch_shape", "pld_set_watchdog_us", "pld_set_trace",
                   "pld_set_test_hooks"):
             getattr(L, f).restype = i32
@@ -135,7 +138,7 @@ def check(code: int, what: str):
         raise PldError(code, what)
 
 
-def config_from_shape(s, vocab: int = 0) -> PldConfig:
+def config_from_shape(s, vocab: int = 0, max_query: int = 0) -> PldConfig:
     """pld_config of a synth.configs.LayerShape."""
     c = PldConfig()
     c.attn_kind = {"gqa": PLD_ATTN_GQA, "mla": PLD_ATTN_MLA, "kda": PLD_ATTN_KDA}[s.attn]
@@ -149,6 +152,7 @@ def config_from_shape(s, vocab: int = 0) -> PldConfig:
     c.max_seq, c.eps, c.rope_base, c.vocab = s.max_seq, s.eps, s.rope_base, vocab
     c.kda_rank, c.conv_width = s.kda_rank, s.conv_width
     c.expert_wfmt = PLD_WFMT_LUT3 if s.expert_fmt == "lut3" else 0
+    c.max_query = int(max_query)
     return c
 
 
@@ -191,13 +195,14 @@ class Decoder:
     """One decode handle over a stack of layers (weights and caches are caller-owned torch tensors)."""
 
     def __init__(self, shape, layers: Sequence[dict], caches: Sequence[dict], head: Optional[dict] = None,
-                 vocab: int = 0, static: bool = False):
+                 vocab: int = 0, static: bool = False, max_query: int = 0):
         """static=True: decode_layer_init_static (the library's own device array, no workspace
-        allocation; one such handle per GPU, re-initialised by every such call)."""
+        allocation; one such handle per GPU, re-initialised by every such call).
+        max_query >= 2: the workspace also holds the batched verify's buffers (verify_batched)."""
         import torch
 
         self.shape = shape
-        self.cfg = config_from_shape(shape, vocab)
+        self.cfg = config_from_shape(shape, vocab, max_query)
         n = len(layers)
         self._keep = (list(layers), list(caches), head)   # keep the tensors alive
         self.static = static
@@ -248,6 +253,17 @@ class Decoder:
         a.draft_tokens, a.out_logits = _ptr(draft_tokens), _ptr(out_logits)
         a.out_tokens, a.out_accepted = _ptr(out_tokens), _ptr(out_accepted)
         check(lib().decode_layers_persistent(self.handle, ctypes.byref(a), self._stream()), "decode_layers_persistent")
+
+    def verify_batched(self, start_pos: int, in_token: int, draft_tokens, out_hidden, out_logits=None,
+                       out_tokens=None, out_accepted=None, temperature: float = 0.0, sample_seed: int = 0):
+        """decode_verify_batched: 1 + len(draft_tokens) positions through the stack together."""
+        a = PldPersistentArgs()
+        a.start_pos, a.n_tokens, a.n_query, a.in_token = start_pos, 1, int(draft_tokens.numel()) + 1, in_token
+        a.temperature, a.sample_seed = float(temperature), int(sample_seed) & 0xFFFFFFFFFFFFFFFF
+        a.in_hidden, a.out_hidden = None, _ptr(out_hidden)
+        a.draft_tokens, a.out_logits = _ptr(draft_tokens), _ptr(out_logits)
+        a.out_tokens, a.out_accepted = _ptr(out_tokens), _ptr(out_accepted)
+        check(lib().decode_verify_batched(self.handle, ctypes.byref(a), self._stream()), "decode_verify_batched")
 
     def speculative(self, draft: "Decoder", start_pos: int, in_token: int, n_tokens: int, n_draft: int, out_tokens,
                     temperature: float = 0.0, sample_seed: int = 0):
@@ -314,7 +330,8 @@ class Decoder:
         default = {"logits": torch.float64, "sel": torch.int32, "x": torch.int16, "qi": torch.int16,
                    "isel": torch.int32, "ikh": torch.int32, "ikl": torch.int32,
                    "ilist": torch.int32, "ilo": torch.int32, "itok": torch.int32,
-                   "qlat": torch.int16, "qrope": torch.int16}   # bf16 bits
+                   "qlat": torch.int16, "qrope": torch.int16, "vx": torch.int16, "vqlat": torch.int16,
+                   "vo": torch.int16, "vsel": torch.int32}   # bf16 bits
         if name == "cq" and getattr(self.shape, "index_topk", 0):
             default["cq"] = torch.float64   # the sparse layer passes c_q' in fp64 (word pairs)
         return raw.view(dtype or default.get(name, torch.float32))

@@ -1,0 +1,1390 @@
+// Batched verify of the FP8 MLA stack: the nq positions of one multi-token verify go
+// through every layer TOGETHER, so each weight is read from HBM once per step instead of
+// once per position (included by pld_kernel.hip after pld_mla.hpp).
+//
+// The vLLM Kimi K3 backend article scores the speculative drafts of one request in one
+// forward pass (summary and "Throughput holds across the tested range": DSpark with an
+// acceptance length of six), and names shape-aware matmuls as one of its four changes
+// ("Four changes drive the gains"). With nq <= 8 positions each dense projection is a
+// skinny GEMM [rows x K] x [K x nq]: on gfx950 it runs on the matrix cores,
+// v_mfma_f32_16x16x32_bf16, with the FP8 weights converted to bf16 in registers (exact:
+// every E4M3 value is a bf16 value) and their fp32 block scale applied to each 64-wide
+// k-step's fp32 partial. The activations enter the matrix cores as bf16 (one rounding of
+// each normalised input); accumulation is fp32.
+//
+// One batched step of a layer (LL buffers hold nq copies, one per position):
+//   BX  a_p = RMSNorm(x_p); [c_q' ; c_kv' | k_r']_p = [W_DQ ; W_DKV] a_p      (matrix cores)
+//   BQ  RMSNorm(c_q'_p); q_p = W_UQ c_q_p, RoPE at position pos + p          (matrix cores)
+//   BA  q_lat = W_UK^T q_nope per head and position (weights in registers, reused)
+//   BT  attention per (16-head group, chunk of the shared history), two positions per
+//       pass over the chunk; the nq new latent rows join the last chunk with the causal
+//       mask (position p sees new rows 0..p)
+//   BM  merge of the chunk partials, per position
+//   BU  o = W_UV o_lat per head                                               (matrix cores)
+//   BO  h2_p = x_p + W_O o_p                                                  (matrix cores)
+//   BF  RMSNorm(h2_p); router logits in fp64 from the fp32 activation (the selection
+//       must match an fp64 evaluation); shared experts (matrix cores); per-position
+//       top-k; the UNION of the selected experts, each read once for the positions
+//       that chose it (matrix cores)
+//   BD  down projections: this workgroup's output rows for every (expert, position)
+//       pair, the expert's rows read once; f_p = sum of gated results; x'_p = h2_p + f_p
+// then, after the last layer, the LM head and the token choice of each position and the
+// acceptance count.
+#pragma once
+
+constexpr int VB = 8;                    // positions per batched step (max)
+constexpr int VACT_BYTES = 147456;       // LDS region for matrix-core operands / attention (144 KiB)
+constexpr int VPP = 2;                   // positions per attention pass over a chunk
+
+typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+
+// ------------------------------------------------------------------ matrix-core segment list
+// A segment is n consecutive FP8 rows of one matrix (row stride K bytes, block scales s
+// with scale row (srow + r) >> 7). Its A operand: position p reads the bf16 vector at
+// A + a_off + vrow[p] * (K + 8) (LDS), or zeros when vrow[p] < 0. Results: position p,
+// row r at out[o_off + p * ostr + r].
+struct MSeg {
+  const uint8_t* w;
+  const float* s;
+  int n, srow, a_off, o_off;
+  int8_t vrow[VB];
+};
+constexpr int MAX_MSEGS = 24;
+__device__ __forceinline__ constexpr int vb_astr(int K) { return K + 8; }   // bf16 elements per A row
+
+__device__ __forceinline__ void mseg_set(MSeg* segs, int i, const uint8_t* w, const float* s, int n, int srow,
+                                         int a_off, int o_off, int nq) {
+  if (tid_opaque() == 0) {
+    MSeg& S = segs[i];
+    S.w = w; S.s = s; S.n = n; S.srow = srow; S.a_off = a_off; S.o_off = o_off;
+    for (int p = 0; p < VB; p++) S.vrow[p] = (int8_t)(p < nq ? p : -1);
+  }
+}
+
+// Rows of a segment list times up to 16 activation rows on the matrix cores.
+//  * Each segment is cut into tiles of 16 rows (the last one partial: its spare columns
+//    reload the segment's last row, which costs no extra HBM bytes); tile t is the B
+//    operand of v_mfma_f32_16x16x32_bf16, lane (n, g) = (lane & 15, lane >> 4) holding
+//    row n of the tile. One 16-byte load per lane covers k in [k0 + 16 g, k0 + 16 g + 16)
+//    of its row, and the 64 lanes cover a 64-wide k-step of 16 rows; its two halves are
+//    two products (the k order inside a product is the same permutation on both operands).
+//  * Work units are (tile, k-slice): with fewer than 8 tiles, K is split into KS slices
+//    so that every wave of the workgroup streams; the slices' partial sums are added in
+//    slice order afterwards (fixed order, so results do not depend on timing).
+//  * Each wave streams its units as one pipeline with D loads in flight per lane; the
+//    first D are issued before pre() (the dependency wait), like the vector GEMV.
+//  * The fp32 block scale of the lane's row multiplies each k-step's partial product
+//    (the output column of a lane is its own B row, so the lane holds its own scale).
+// `segs` lives in LDS; `part` is LDS scratch of 8 * 16 * VB floats. Returns false if
+// pre() reported an abort. Ends with a workgroup barrier.
+template <int K, int D, typename Pre>
+__device__ __forceinline__ bool mfma_list(const MSeg* segs, int nseg, const uint16_t* A, float* out, int ostr,
+                                          float* part, int nq, Pre&& pre) {
+  static_assert(K % 64 == 0, "whole 64-wide k-steps");
+  constexpr int AST = vb_astr(K);
+  constexpr int SBK = (K + 127) / 128;
+  const int tid = tid_opaque(), lane = tid & 63, wave = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;
+  int ntiles = 0;
+  for (int s = 0; s < nseg; s++) ntiles += (segs[s].n + 15) >> 4;
+  int KS = 1;
+  if (ntiles > 0 && ntiles < NWAVES) {
+    KS = NWAVES / ntiles;
+    while ((K / 64) % KS) KS--;
+  }
+  const int NS = K / 64 / KS;                   // k-steps per unit
+  const int nunits = ntiles * KS;
+  const int myunits = wave < nunits ? (nunits - wave + NWAVES - 1) / NWAVES : 0;
+  const int nit = myunits * NS;
+  // unit -> (segment, tile in segment, slice)
+  auto unit_of = [&](int ui, int* sg, int* tt, int* q) {
+    const int u = wave + ui * NWAVES;
+    int t = u % ntiles;
+    *q = u / ntiles;
+    int s = 0;
+    for (; s < nseg - 1; s++) {
+      const int nt = (segs[s].n + 15) >> 4;
+      if (t < nt) break;
+      t -= nt;
+    }
+    *sg = s;
+    *tt = t;
+  };
+  // issue cursor: unit iu, step is; per-unit row pointers
+  int iu = 0, is = 0;
+  const uint8_t* wrow = nullptr;
+  const PLD_GLOBAL float* srow = nullptr;
+  int kbeg = 0;
+  auto open_unit = [&](int ui) {
+    int sg, tt, q;
+    unit_of(ui, &sg, &tt, &q);
+    const MSeg& S = segs[sg];
+    const int r = min(16 * tt + n, S.n - 1);
+    wrow = S.w + (size_t)r * K;
+    srow = gp(S.s) + (size_t)((S.srow + r) >> 7) * SBK;
+    kbeg = q * (K / KS);
+  };
+  uint4 buf[D];
+  float scb[D];
+  auto issue = [&](int d) {
+    if (iu < myunits) {
+      const int k0 = kbeg + 64 * is;
+      buf[d] = ld_stream16(wrow + k0 + 16 * g);
+      scb[d] = srow[k0 >> 7];
+      if (++is == NS) {
+        is = 0;
+        if (++iu < myunits) open_unit(iu);
+      }
+    }
+  };
+  if (myunits > 0) open_unit(0);
+#pragma unroll
+  for (int d = 0; d < D; d++) issue(d);
+  if (!pre()) return false;
+  // compute cursor
+  int cu = 0, cs = 0;
+  const uint16_t* arow = nullptr;
+  int csg = 0, ctt = 0, cq = 0;
+  auto open_compute = [&](int ui) {
+    unit_of(ui, &csg, &ctt, &cq);
+    const MSeg& S = segs[csg];
+    const int vr = (n < VB) ? (int)S.vrow[n] : -1;
+    arow = vr >= 0 ? A + S.a_off + vr * AST : nullptr;
+  };
+  if (myunits > 0) open_compute(0);
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int it0 = 0; it0 < nit; it0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; d++) {
+      if (it0 + d < nit) {
+        const int k0 = (cq * (K / KS)) + 64 * cs;
+        uint4 a0 = make_uint4(0u, 0u, 0u, 0u), a1 = a0;
+        if (arow) {
+          a0 = *reinterpret_cast<const uint4*>(arow + k0 + 16 * g);
+          a1 = *reinterpret_cast<const uint4*>(arow + k0 + 16 * g + 8);
+        }
+        const uint4 wv = buf[d];
+        const float sc = scb[d];
+        issue(d);
+        const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
+        uint32_t bw[8];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const bf16x2_v lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[i], 1.0f, false);
+          const bf16x2_v hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[i], 1.0f, true);
+          bw[2 * i] = __builtin_bit_cast(uint32_t, lo);
+          bw[2 * i + 1] = __builtin_bit_cast(uint32_t, hi);
+        }
+        const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+        const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, make_uint4(bw[4], bw[5], bw[6], bw[7]));
+        f32x4_t pk = {0.f, 0.f, 0.f, 0.f};
+        pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), b0, pk, 0, 0, 0);
+        pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), b1, pk, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; i++) acc[i] = fmaf(sc, pk[i], acc[i]);
+        if (++cs == NS) {
+          // unit done: lane holds rows p = 4 g + i of column n
+          const MSeg& S = segs[csg];
+          const int r = 16 * ctt + n;
+          if (r < S.n) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+              const int p = 4 * g + i;
+              if (p < nq) {
+                if (KS == 1) out[S.o_off + p * ostr + r] = acc[i];
+                else part[((cq * ntiles + (wave + cu * NWAVES) % ntiles) * 16 + n) * VB + p] = acc[i];
+              }
+            }
+          }
+          acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          cs = 0;
+          if (++cu < myunits) open_compute(cu);
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (KS > 1) {
+    // slice partials of tile t, column n, position p, added in slice order
+    for (int i = tid; i < ntiles * 16 * VB; i += BLOCK) {
+      const int p = i % VB, nn = (i / VB) % 16, t = i / (16 * VB);
+      if (p >= nq) continue;
+      int s = 0, tt = t;
+      for (; s < nseg - 1; s++) {
+        const int nt = (segs[s].n + 15) >> 4;
+        if (tt < nt) break;
+        tt -= nt;
+      }
+      const int r = 16 * tt + nn;
+      if (r >= segs[s].n) continue;
+      float v = 0.f;
+      for (int q = 0; q < KS; q++) v += part[((q * ntiles + t) * 16 + nn) * VB + p];
+      out[segs[s].o_off + p * ostr + r] = v;
+    }
+    __syncthreads();
+  }
+  return true;
+}
+
+// ------------------------------------------------------------------ LDS of the batched kernel
+struct VLds {
+  uint16_t* A;     // [VACT_BYTES] matrix-core A rows / attention / merge scratch (also used as floats)
+  float* out;      // [VB * 64]     stage results (rows of this workgroup x positions)
+  float* part;     // [8 * 16 * VB] k-slice partials
+  float* xres;     // [VB][32]      this workgroup's rows of each position's layer input
+  float* h2res;    // [VB][32]      ... and of h2
+  float* facc;     // [VB][32]      FFN output accumulators
+  double* red;     // [16]
+  int* isel;       // [VB][8]       per-position top-k experts (rank order)
+  float* fgate;    // [VB][8]       their gates
+  int* uexp;       // [VB * 8 + 4]  union of the selected experts (ascending), then shared
+  int* umask;      // [VB * 8 + 4]  positions that use each union slot (bit p)
+  int* misc;       // [16]          union size; misc + 8: the head stage's argmax slot
+  int* tok;        // [2 * VB]      input tokens of the positions, then the chosen tokens
+  int* pcs;        // [3 * MAX_MSEGS / 2] routed pieces of this workgroup: union slot, j0, j1
+  MSeg* segs;      // [MAX_MSEGS]
+  uint64_t* tr;    // [TR_SLOTS]
+  double* dk;      // [16]
+  uint32_t* stage; // [3 * 1024]    LL staging for the head's inputs (aliases nothing live)
+};
+constexpr int VOUT_FLOATS = VB * 64;
+__host__ __device__ inline size_t vlds_bytes() {
+  return (size_t)VACT_BYTES + 4 * (VOUT_FLOATS + 8 * 16 * VB + 3 * VB * 32) + 8 * 16 + 4 * (VB * 8) * 2 +
+         4 * 2 * (VB * 8 + 4) + 4 * 16 + 4 * 2 * VB + 4 * 3 * (MAX_MSEGS / 2) + sizeof(MSeg) * MAX_MSEGS +
+         8 * TR_SLOTS + 8 * 16;
+}
+__device__ __forceinline__ VLds vcarve(float* base) {
+  VLds L;
+  char* p = reinterpret_cast<char*>(base);
+  L.A = reinterpret_cast<uint16_t*>(p); p += VACT_BYTES;
+  L.out = reinterpret_cast<float*>(p); p += 4 * VOUT_FLOATS;
+  L.part = reinterpret_cast<float*>(p); p += 4 * 8 * 16 * VB;
+  L.xres = reinterpret_cast<float*>(p); p += 4 * VB * 32;
+  L.h2res = reinterpret_cast<float*>(p); p += 4 * VB * 32;
+  L.facc = reinterpret_cast<float*>(p); p += 4 * VB * 32;
+  L.red = reinterpret_cast<double*>(p); p += 8 * 16;
+  L.isel = reinterpret_cast<int*>(p); p += 4 * VB * 8;
+  L.fgate = reinterpret_cast<float*>(p); p += 4 * VB * 8;
+  L.uexp = reinterpret_cast<int*>(p); p += 4 * (VB * 8 + 4);
+  L.umask = reinterpret_cast<int*>(p); p += 4 * (VB * 8 + 4);
+  L.misc = reinterpret_cast<int*>(p); p += 4 * 16;
+  L.tok = reinterpret_cast<int*>(p); p += 4 * 2 * VB;
+  L.pcs = reinterpret_cast<int*>(p); p += 4 * 3 * (MAX_MSEGS / 2);
+  L.segs = reinterpret_cast<MSeg*>(p); p += sizeof(MSeg) * MAX_MSEGS;
+  L.tr = reinterpret_cast<uint64_t*>(p); p += 8 * TR_SLOTS;
+  L.dk = reinterpret_cast<double*>(p);
+  L.stage = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(base) + 98432);   // inside A, past 8 rows of K = 6144
+  return L;
+}
+
+// The head stage of the single-position path runs once per position on this LDS: its
+// activation and candidate areas map into the A region.
+__device__ __forceinline__ Lds head_lds(const VLds& V) {
+  Lds L;
+  L.act = reinterpret_cast<float*>(V.A);                                       // [H] doubles = 48 KiB
+  L.stage = V.stage;                                                           // [H/2] words
+  L.outb = reinterpret_cast<float*>(reinterpret_cast<char*>(V.A) + 122880);    // [vocab/nwg] doubles
+  L.outc = nullptr;
+  L.xres = L.h2res = nullptr;
+  L.red = V.red;
+  L.isel = V.misc + 8;
+  L.fgate = nullptr;
+  L.segs = nullptr;
+  L.tr = V.tr;
+  L.dk = V.dk;
+  L.pcs = nullptr;
+  return L;
+}
+
+// Per-position LL buffers: buffer b of position p.
+template <typename T = uint64_t>
+__device__ __forceinline__ uint64_t* vbuf(const KArgs& a, size_t off, size_t words, int p) {
+  return wsp<uint64_t>(a, off) + (size_t)p * words;
+}
+
+// RMSNorm of a vector held in LDS as fp32 (src) into a bf16 A row (dst), in fp64 like the
+// single-position path (fp64 sum of squares, fp64 product, one rounding to bf16). All
+// threads call; ends with a barrier.
+template <int N>
+__device__ __forceinline__ void rms_to_bf16(uint16_t* dst, const float* src, const PLD_GLOBAL float* gam, double eps,
+                                            double* red) {
+  constexpr int KK = (N + BLOCK - 1) / BLOCK;
+  float xv[KK];
+  double ss = 0.0;
+#pragma unroll
+  for (int k = 0; k < KK; k++) {
+    const int i = tid_opaque() + k * BLOCK;
+    xv[k] = (N % BLOCK == 0 || i < N) ? src[i] : 0.f;
+    ss += (double)xv[k] * (double)xv[k];
+  }
+  ss = block_sum(ss, red);
+  const double r = 1.0 / sqrt(ss / (double)N + eps);
+#pragma unroll
+  for (int k = 0; k < KK; k++) {
+    const int i = tid_opaque() + k * BLOCK;
+    if (N % BLOCK == 0 || i < N) dst[i] = (uint16_t)f64_to_bf16(((double)xv[k] * r) * (double)gam[i]);
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------ BX
+template <class SH>
+__device__ __forceinline__ bool bstage_x(Ctx& cx, const KArgs& a, const Step& st, VLds& L, int nq, int li) {
+  const DLayer Ly = *gp(st.Ly);
+  const int w = cx.w, nwg = cx.nwg;
+  constexpr int H = SH::H, R = SH::QL + SH::LAT, AST = vb_astr(H);
+  const int r0 = split_at(R, nwg, w), r1 = split_at(R, nwg, w + 1);
+  int h0, h1;
+  hrows(H, nwg, w, &h0, &h1);
+  {
+    __syncthreads();
+    int ns = 0;
+    if (r0 < SH::QL) {
+      mseg_set(L.segs, ns, Ly.w_dq.w + (size_t)r0 * H, Ly.w_dq.s, min(r1, SH::QL) - r0, r0, 0, 0, nq);
+      ns++;
+    }
+    if (r1 > SH::QL) {
+      const int lo = max(r0, SH::QL) - SH::QL;
+      mseg_set(L.segs, ns, Ly.w_dkv.w + (size_t)lo * H, Ly.w_dkv.s, r1 - max(r0, SH::QL), lo, 0,
+               max(r0, SH::QL) - r0, nq);
+      ns++;
+    }
+    __syncthreads();
+    auto pre = [&]() -> bool {
+      for (int p = 0; p < nq; p++) {
+        uint16_t* Ar = L.A + p * AST;
+        uint32_t* Aw = reinterpret_cast<uint32_t*>(Ar);
+        if (li == 0) {
+          const PLD_GLOBAL uint32_t* src = gp(reinterpret_cast<const uint32_t*>(a.embed + (size_t)L.tok[p] * H));
+          for (int i = tid_opaque(); i < H / 2; i += BLOCK) Aw[i] = src[i];
+          __syncthreads();
+        } else if (!ll_fetch<per_for(H / 2)>(cx, Aw, vbuf(a, a.off.vx, H / 2, p), H / 2, st.k1 - 1u, W_X)) {
+          return false;
+        }
+        for (int r = h0 + tid_opaque(); r < h1; r += BLOCK) L.xres[p * 32 + (r - h0)] = bf16_to_f32(Ar[r]);
+        // RMSNorm in place: each thread reads its own elements into registers first
+        constexpr int KK = H / BLOCK;
+        static_assert(H % BLOCK == 0, "hidden size");
+        float xv[KK];
+        double ss = 0.0;
+#pragma unroll
+        for (int k = 0; k < KK; k++) {
+          xv[k] = bf16_to_f32(Ar[tid_opaque() + k * BLOCK]);
+          ss += (double)xv[k] * (double)xv[k];
+        }
+        ss = block_sum(ss, L.red);   // (its barrier also orders the xres reads before the writes)
+        const double rr = 1.0 / sqrt(ss / (double)H + a.c.eps);
+        const PLD_GLOBAL float* gm = gp(Ly.attn_norm);
+#pragma unroll
+        for (int k = 0; k < KK; k++) {
+          const int i = tid_opaque() + k * BLOCK;
+          Ar[i] = (uint16_t)f64_to_bf16(((double)xv[k] * rr) * (double)gm[i]);
+        }
+      }
+      __syncthreads();
+      stamp(a, cx, st, TR_X_NORMED);
+      return true;
+    };
+    if (!mfma_list<H, 8>(L.segs, ns, L.A, L.out, r1 - r0, L.part, nq, pre)) return false;
+  }
+  stamp(a, cx, st, TR_QKV_GEMV);
+  for (int i = tid_opaque(); i < nq * (r1 - r0); i += BLOCK) {
+    const int p = i / (r1 - r0), r = r0 + i % (r1 - r0);
+    const float v = L.out[i];
+    if (r < SH::QL) ll_put_f32(vbuf(a, a.off.vcqr, SH::QL, p) + r, v, st.k1);
+    else ll_put_f32(vbuf(a, a.off.vckv, SH::LAT, p) + (r - SH::QL), v, st.k1);
+  }
+  stamp(a, cx, st, TR_QKV_DONE);
+  return true;
+}
+
+// ------------------------------------------------------------------ BQ
+template <class SH>
+__device__ __forceinline__ bool bstage_q(Ctx& cx, const KArgs& a, const Step& st, VLds& L, int nq) {
+  const DLayer Ly = *gp(st.Ly);
+  const int w = cx.w, nwg = cx.nwg;
+  constexpr int QL = SH::QL, RQ = SH::NH * SH::QH, AST = vb_astr(QL);
+  const int r0 = 2 * split_at(RQ / 2, nwg, w), r1 = 2 * split_at(RQ / 2, nwg, w + 1);
+  float* tmp = reinterpret_cast<float*>(L.A + VB * AST);   // [QL] fp32
+  __syncthreads();
+  mseg_set(L.segs, 0, Ly.w_uq.w + (size_t)r0 * QL, Ly.w_uq.s, r1 - r0, r0, 0, 0, nq);
+  __syncthreads();
+  auto pre = [&]() -> bool {
+    for (int p = 0; p < nq; p++) {
+      if (!ll_fetch<per_for(QL)>(cx, reinterpret_cast<uint32_t*>(tmp), vbuf(a, a.off.vcqr, QL, p), QL, st.k1, W_CQ))
+        return false;
+      rms_to_bf16<QL>(L.A + p * AST, tmp, gp(Ly.q_norm), a.c.eps, L.red);
+    }
+    stamp(a, cx, st, TR_CQ_READY);
+    return true;
+  };
+  if (!mfma_list<QL, 8>(L.segs, r1 > r0 ? 1 : 0, L.A, L.out, r1 - r0, L.part, nq, pre)) return false;
+  stamp(a, cx, st, TR_Q_GEMV);
+  const int npair = (r1 - r0) / 2;
+  for (int i = tid_opaque(); i < nq * npair; i += BLOCK) {
+    const int p = i / npair, r = r0 + 2 * (i % npair), h = r / SH::QH, k = r % SH::QH;
+    const float v0 = L.out[p * (r1 - r0) + r - r0], v1 = L.out[p * (r1 - r0) + r + 1 - r0];
+    if (k < SH::ND) {
+      uint64_t* qn = vbuf(a, a.off.vqn, SH::NH * SH::ND, p) + h * SH::ND + k;
+      ll_put_f32(qn, v0, st.k1);
+      ll_put_f32(qn + 1, v1, st.k1);
+    } else {
+      const int d = k - SH::ND;
+      const PLD_GLOBAL float* rope = gp(wsp<float>(a, a.off.rope)) + (size_t)(st.pos + p) * SH::RD;
+      const float cs = rope[d], sn = rope[d + 1];
+      ll_put(vbuf(a, a.off.vqr, SH::NH * SH::RD / 2, p) + (h * SH::RD + d) / 2,
+             f32_to_bf16(v0 * cs - v1 * sn) | (f32_to_bf16(v0 * sn + v1 * cs) << 16), st.k1);
+    }
+  }
+  stamp(a, cx, st, TR_ATT_Q);
+  return true;
+}
+
+// ------------------------------------------------------------------ BA: q_lat = W_UK^T q_nope (per position)
+template <class SH>
+__device__ __forceinline__ bool bstage_absorb(Ctx& cx, const KArgs& a, const Step& st, VLds& L, int nq) {
+  const KCfg& c = a.c;
+  const DLayer Ly = *gp(st.Ly);
+  constexpr int EPC = 16, KL = SH::KL, ND = SH::ND;
+  constexpr int SBK = (KL + 127) / 128;
+  const int cpw = c.cpw;
+  const int h = (cx.w * cpw) / KL, c0 = (cx.w * cpw) % KL;
+  const int cpr = cpw / EPC, rpp = BLOCK / cpr;
+  constexpr int MAXP = 4;
+  const int tid = tid_opaque();
+  const int ck = tid % cpr, rr = tid / cpr;
+  uint4 wv[MAXP];
+  float sc[MAXP];
+#pragma unroll
+  for (int p = 0; p < MAXP; p++) {
+    wv[p] = make_uint4(0u, 0u, 0u, 0u);
+    sc[p] = 0.f;
+    if (p * rpp < ND) {
+      const int d = min(rr + p * rpp, ND - 1);
+      const size_t row = (size_t)h * ND + d;
+      wv[p] = ld_stream16(Ly.w_uk.w + row * KL + c0 + ck * EPC);
+      sc[p] = gp(Ly.w_uk.s)[(row >> 7) * SBK + ((c0 + ck * EPC) >> 7)];
+    }
+  }
+  float* base = reinterpret_cast<float*>(L.A);
+  float* qv = base;                     // [ND]
+  const int rs = rpp + 1;
+  float* red = base + ND;               // [cpw][rs]
+  float* red2 = red + cpw * rs;         // [BLOCK / cpw][cpw]
+  for (int q = 0; q < nq; q++) {
+    if (!ll_fetch<per_for(ND)>(cx, reinterpret_cast<uint32_t*>(qv), vbuf(a, a.off.vqn, SH::NH * ND, q) + (size_t)h * ND,
+                               ND, st.k1, W_QN))
+      return false;
+    float acc[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; e++) acc[e] = 0.f;
+#pragma unroll
+    for (int p = 0; p < MAXP; p++) {
+      const int d = rr + p * rpp;
+      if (p * rpp < ND) {
+        const float qq = d < ND ? qv[d] * sc[p] : 0.f;
+        const uint32_t wd[4] = {wv[p].x, wv[p].y, wv[p].z, wv[p].w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[i], false);
+          const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)wd[i], true);
+          acc[4 * i + 0] = fmaf(lo.x, qq, acc[4 * i + 0]);
+          acc[4 * i + 1] = fmaf(lo.y, qq, acc[4 * i + 1]);
+          acc[4 * i + 2] = fmaf(hi.x, qq, acc[4 * i + 2]);
+          acc[4 * i + 3] = fmaf(hi.y, qq, acc[4 * i + 3]);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPC; e++) red[(ck * EPC + e) * rs + rr] = acc[e];
+    __syncthreads();
+    {
+      const int ng = BLOCK / cpw, rpg = rpp / ng;
+      const int j = tid % cpw, gq = tid / cpw;
+      const float* col = red + j * rs + gq * rpg;
+      float s4[4] = {0.f, 0.f, 0.f, 0.f};
+      int gg = 0;
+      for (; gg + 4 <= rpg; gg += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; u++) s4[u] += col[gg + u];
+      }
+      for (; gg < rpg; gg++) s4[0] += col[gg];
+      red2[gq * cpw + j] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+      __syncthreads();
+      float tot = 0.f;
+      if (tid < cpw)
+        for (int qq = 0; qq < ng; qq++) tot += red2[qq * cpw + tid];
+      __syncthreads();
+      if (tid < cpw) red2[tid] = tot;
+      __syncthreads();
+    }
+    uint64_t* ql = vbuf(a, a.off.vqlat, SH::NH * KL / 2, q) + ((size_t)h * KL + c0) / 2;
+    for (int j = 2 * tid; j < cpw; j += 2 * BLOCK)
+      ll_put(ql + j / 2, f32_to_bf16(red2[j]) | (f32_to_bf16(red2[j + 1]) << 16), st.k1);
+    __syncthreads();
+  }
+  stamp(a, cx, st, TR_ATT_SCORES);
+  return true;
+}
+
+// ------------------------------------------------------------------ BT: attention, VPP positions per pass
+// Workgroup (head group hg of HPW = 16 heads, chunk ch) as in the single-position stage:
+// the chunk's rows [t0, t1) of the pos history rows (all written before this launch, so
+// read through L2, which the head groups of a chunk share). For each pass, the queries of
+// VPP positions are staged, the chunk's 32-row sub-blocks are staged once and used by
+// both positions (S = Q C^T and O += P C on the matrix cores, online softmax per head and
+// position), then the last chunk adds the nq new rows of this step on the vector ALU,
+// each position seeing the new rows up to its own. Partials go to the position's buffer.
+template <class SH>
+__device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step& st, VLds& V, int nq) {
+  const KCfg& c = a.c;
+  const DLayer Ly = *gp(st.Ly);
+  const uint32_t k1 = st.k1;
+  constexpr int LAT = SH::LAT, KL = SH::KL, RD = SH::RD, HPW = SH::HPW, TB = SH::TB, CSTR = SH::CSTR;
+  constexpr int KSTEPS = LAT / 16, KQ = KSTEPS / 4;
+  constexpr int CPRW = LAT / 8;
+  constexpr int NLD = (TB * CPRW + BLOCK - 1) / BLOCK;
+  static_assert(HPW == 2 * NWAVES && KL == 512 && TB == 32, "the batched attention tiling (16 heads per workgroup)");
+  constexpr int HS = 2;
+  const int tid = tid_opaque();
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hown = wave * HS + ((lane & 63) >> 5);
+  const int nch = c.cpg;
+  const int hg = cx.w / nch, ch = cx.w % nch;
+  const int hbase = hg * HPW;
+  const int pos = st.pos;                     // first position; history rows [0, pos)
+  const int t0 = split_at(pos, nch, ch), t1 = split_at(pos, nch, ch + 1), n = t1 - t0;
+  const uint16_t* lat = Ly.lat;
+  // LDS
+  uint16_t* Qs = V.A;                                        // [VPP][16][CSTR]
+  uint16_t* Cs = Qs + VPP * 16 * CSTR;                       // [2][TB][CSTR]
+  uint16_t* Ps = Cs + 2 * TB * CSTR;                         // [VPP][16][TB]
+  float* Ssc = reinterpret_cast<float*>(Ps + VPP * 16 * TB); // [VPP][4][2][256]
+  float* alph = Ssc + VPP * 4 * 2 * 256;                     // [VPP][16]
+  uint16_t* newr = reinterpret_cast<uint16_t*>(alph + VPP * 16);   // [VB][LAT] new rows (bf16)
+  float* ntmp = reinterpret_cast<float*>(newr + VB * LAT);   // [LAT]
+  float* sn = ntmp + LAT;                                    // [VPP][16][VB + 2] new-row scores, alpha, p
+  float* qtmp = reinterpret_cast<float*>(Cs + TB * CSTR);    // q staging (Cs buffer 1, free between passes)
+  const bool last = ch == nch - 1;
+  // the new rows of this step (last chunk): RMSNorm(c_kv') and RoPE(k_r'), bf16; appended
+  // to the cache by head group 0
+  if (last) {
+    for (int p = 0; p < nq; p++) {
+      if (!ll_fetch<per_for(LAT)>(cx, reinterpret_cast<uint32_t*>(ntmp), vbuf(a, a.off.vckv, LAT, p), LAT, k1, W_KV))
+        return false;
+      double ss = 0.0;
+      for (int i = tid; i < KL; i += BLOCK) ss += (double)ntmp[i] * (double)ntmp[i];
+      ss = block_sum(ss, V.red);
+      const double r = 1.0 / sqrt(ss / (double)KL + c.eps);
+      const PLD_GLOBAL float* gk = gp(Ly.kv_norm);
+      const PLD_GLOBAL float* rope = gp(wsp<float>(a, a.off.rope)) + (size_t)(pos + p) * RD;
+      for (int i = tid; i < LAT / 2; i += BLOCK) {
+        const int k = 2 * i;
+        float v0, v1;
+        if (k < KL) {
+          v0 = (float)(((double)ntmp[k] * r) * (double)gk[k]);
+          v1 = (float)(((double)ntmp[k + 1] * r) * (double)gk[k + 1]);
+        } else {
+          const int d = k - KL;
+          const float x0 = ntmp[k], x1 = ntmp[k + 1], cs = rope[d], sg = rope[d + 1];
+          v0 = x0 * cs - x1 * sg;
+          v1 = x0 * sg + x1 * cs;
+        }
+        const uint32_t pair = f32_to_bf16(v0) | (f32_to_bf16(v1) << 16);
+        reinterpret_cast<uint32_t*>(newr + p * LAT)[i] = pair;
+        if (hg == 0) st_u32(reinterpret_cast<uint32_t*>(Ly.lat + (size_t)(pos + p) * LAT) + i, pair);
+      }
+      __syncthreads();
+    }
+    vm_wait();   // the appended rows are written before this workgroup's next publication
+  }
+  const float scale = 1.0f / sqrtf((float)(SH::ND + SH::RD));
+  const int ln = lane & 15, lq = lane >> 4;
+  const int nsb = (n + TB - 1) / TB;
+  constexpr int DEPTH = 3;
+  uint4 cb[DEPTH][NLD];
+  auto issue = [&](int set, int sb) {
+    const bool live = sb < nsb;
+#pragma unroll
+    for (int i = 0; i < NLD; i++) {
+      const int idx = min(tid + i * BLOCK, TB * CPRW - 1);
+      const int r = idx / CPRW, k = idx % CPRW;
+      const int t = max(min(sb * TB + r, n - 1), 0);
+      const uint16_t* p = live ? lat + (size_t)(t0 + t) * LAT + k * 8 : lat;
+      cb[set][i] = ld_g16(p);
+    }
+  };
+  auto store = [&](int set, int buf) {
+    uint16_t* C = Cs + buf * TB * CSTR;
+#pragma unroll
+    for (int i = 0; i < NLD; i++) {
+      const int idx = tid + i * BLOCK;
+      if (idx < TB * CPRW) {
+        const int r = idx / CPRW, k = idx % CPRW;
+        uint32_t* d = reinterpret_cast<uint32_t*>(C + r * CSTR + k * 8);
+        d[0] = cb[set][i].x; d[1] = cb[set][i].y; d[2] = cb[set][i].z; d[3] = cb[set][i].w;
+      }
+    }
+  };
+  constexpr int PSTR = KL / 2 + 2;
+  uint64_t* pll = wsp<uint64_t>(a, a.off.vpart);
+  const size_t pwords = (size_t)SH::NH * nch * PSTR;   // words of one position's partials
+  for (int p0 = 0; p0 < nq; p0 += VPP) {
+    const int np = min(VPP, nq - p0);
+#pragma unroll
+    for (int d = 0; d < DEPTH; d++) issue(d, d);
+    // queries of the pass: q_lat [HPW][KL] and q_rope [HPW][RD] (bf16 pairs) -> rows of Qs
+    for (int j = 0; j < VPP; j++) {
+      uint16_t* Q = Qs + j * 16 * CSTR;
+      if (j < np) {
+        uint32_t* qw = reinterpret_cast<uint32_t*>(qtmp);
+        const int p = p0 + j;
+        if (!ll_fetch<per_for(HPW * KL / 2)>(cx, qw, vbuf(a, a.off.vqlat, SH::NH * KL / 2, p) + (size_t)hbase * KL / 2,
+                                             HPW * KL / 2, k1, W_QLAT))
+          return false;
+        if (!ll_fetch<per_for(HPW * RD / 2)>(cx, qw + HPW * KL / 2,
+                                             vbuf(a, a.off.vqr, SH::NH * RD / 2, p) + (size_t)hbase * RD / 2,
+                                             HPW * RD / 2, k1, W_QLAT))
+          return false;
+        for (int i = tid; i < 16 * LAT / 2; i += BLOCK) {
+          const int hh = i / (LAT / 2), k2 = i % (LAT / 2);
+          const uint32_t v = k2 < KL / 2 ? qw[hh * (KL / 2) + k2] : qw[HPW * KL / 2 + hh * (RD / 2) + (k2 - KL / 2)];
+          reinterpret_cast<uint32_t*>(Q + hh * CSTR)[k2] = v;
+        }
+        __syncthreads();
+      } else {
+        for (int i = tid; i < 16 * LAT / 2; i += BLOCK) reinterpret_cast<uint32_t*>(Q + (i / (LAT / 2)) * CSTR)[i % (LAT / 2)] = 0u;
+      }
+    }
+    for (int i = tid; i < VPP * 16 * TB; i += BLOCK) Ps[i] = 0;
+    __syncthreads();
+    if (p0 == 0) stamp(a, cx, st, TR_ATT_READY);
+    float m_run[VPP], l_run[VPP];
+    f32x4 O[VPP][4];
+#pragma unroll
+    for (int j = 0; j < VPP; j++) {
+      m_run[j] = -INFINITY;
+      l_run[j] = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; t++) O[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    auto block = [&](const uint16_t* C, int tb0) {
+      // S partials: wave pair (wave >> 1) covers k-steps [kq*KQ, +KQ), tile nt = wave & 1
+      {
+        const int nt = wave & 1, kq = wave >> 1;
+#pragma unroll
+        for (int j = 0; j < VPP; j++) {
+          const uint16_t* Q = Qs + j * 16 * CSTR;
+          f32x4 s4 = {0.f, 0.f, 0.f, 0.f}, s5 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < KQ; kk++) {
+            const int k0 = (kq * KQ + kk) * 16 + 4 * lq;
+            const bf16x4 av = *reinterpret_cast<const bf16x4*>(Q + ln * CSTR + k0);
+            const bf16x4 bv = *reinterpret_cast<const bf16x4*>(C + (nt * 16 + ln) * CSTR + k0);
+            if (kk & 1) s5 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, s5, 0, 0, 0);
+            else s4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, s4, 0, 0, 0);
+          }
+          s4 += s5;
+          float* dst = Ssc + ((j * 4 + kq) * 2 + nt) * 256;
+#pragma unroll
+          for (int q = 0; q < 4; q++) dst[(4 * lq + q) * 16 + ln] = s4[q];
+        }
+      }
+      __syncthreads();
+      // online softmax: head hown, token tb0 + (lane & 31), per position
+      {
+        const int h = hown, tl = lane & 31;
+#pragma unroll
+        for (int j = 0; j < VPP; j++) {
+          float s = -INFINITY;
+          if (tb0 + tl < n) {
+            const int nt = tl >> 4, col = tl & 15;
+            s = 0.f;
+#pragma unroll
+            for (int kq = 0; kq < 4; kq++) s += Ssc[((j * 4 + kq) * 2 + nt) * 256 + h * 16 + col];
+            s *= scale;
+          }
+          const float mb = half_max_dpp(s);
+          const float mnew = fmaxf(m_run[j], mb);
+          const float al = m_run[j] == -INFINITY ? 0.f : __expf(m_run[j] - mnew);
+          const float pv = s == -INFINITY ? 0.f : __expf(s - mnew);
+          l_run[j] = l_run[j] * al + half_sum_dpp(pv);
+          m_run[j] = mnew;
+          Ps[(j * 16 + h) * TB + tl] = (uint16_t)bf16_bits(pv);
+          if (tl == 0) alph[j * 16 + h] = al;
+        }
+      }
+      __syncthreads();
+      // O = alpha O + P C: wave owns columns [wave*64, +64)
+#pragma unroll
+      for (int j = 0; j < VPP; j++) {
+        float fa[4];
+#pragma unroll
+        for (int q = 0; q < 4; q++) fa[q] = alph[j * 16 + 4 * lq + q];
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+#pragma unroll
+          for (int q = 0; q < 4; q++) O[j][t][q] *= fa[q];
+#pragma unroll
+        for (int ks = 0; ks < TB / 16; ks++) {
+          const bf16x4 av = *reinterpret_cast<const bf16x4*>(Ps + (j * 16 + ln) * TB + ks * 16 + 4 * lq);
+#pragma unroll
+          for (int t = 0; t < 4; t++) {
+            const int col = (wave * 4 + t) * 16 + ln;
+            bf16x4 bv;
+#pragma unroll
+            for (int q = 0; q < 4; q++) bv[q] = (short)C[(ks * 16 + 4 * lq + q) * CSTR + col];
+            O[j][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, O[j][t], 0, 0, 0);
+          }
+        }
+      }
+    };
+    for (int sb0 = 0; sb0 < nsb; sb0 += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; d++) {
+        const int sb = sb0 + d;
+        if (sb >= nsb) break;
+        const int buf = sb & 1;
+        const uint16_t* C = Cs + buf * TB * CSTR;
+        store(d, buf);
+        __syncthreads();
+        issue(d, sb + DEPTH);
+        block(C, sb * TB);
+      }
+    }
+    __syncthreads();   // (the last block's LDS reads are done before Cs buffer 1 holds the next queries)
+    // the new rows (last chunk): position p0 + j sees new rows 0 .. p0 + j
+    if (last) {
+      // scores: thread (half-wave hr = head, lane j32) over the LAT dims of new row r
+      for (int j = 0; j < np; j++) {
+        const int p = p0 + j;
+        const uint16_t* Q = Qs + j * 16 * CSTR;
+        for (int r = 0; r <= p; r++) {
+          constexpr int DPJ = LAT / 32;
+          const int hr = tid >> 5, jj = tid & 31;
+          float sv = 0.f;
+#pragma unroll
+          for (int d = 0; d < DPJ; d++)
+            sv = fmaf(bf16_to_f32(Q[hr * CSTR + jj * DPJ + d]), bf16_to_f32(newr[r * LAT + jj * DPJ + d]), sv);
+          sv = dpp_sum<32>(sv);
+          if (jj == 31) sn[(j * 16 + hr) * (VB + 2) + r] = sv * scale;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < VPP; j++) {
+        if (j < np) {
+          const int p = p0 + j;
+          float* snh = sn + (j * 16 + hown) * (VB + 2);
+          float mb = -INFINITY;
+          for (int r = 0; r <= p; r++) mb = fmaxf(mb, snh[r]);
+          const float mnew = fmaxf(m_run[j], mb);
+          const float al = m_run[j] == -INFINITY ? 0.f : __expf(m_run[j] - mnew);
+          float ls = 0.f;
+          __syncthreads();
+          // p_r = exp(s_r - mnew), kept in snh[r] (written by one lane per head)
+          float pr[VB];
+#pragma unroll
+          for (int r = 0; r < VB; r++) {
+            pr[r] = r <= p ? __expf(snh[r] - mnew) : 0.f;
+            ls += pr[r];
+          }
+          __syncthreads();
+          if ((lane & 31) == 0) {
+#pragma unroll
+            for (int r = 0; r < VB; r++) snh[r] = pr[r];
+            snh[VB] = al;
+          }
+          l_run[j] = l_run[j] * al + ls;
+          m_run[j] = mnew;
+          __syncthreads();
+#pragma unroll
+          for (int t = 0; t < 4; t++) {
+            const int col = (wave * 4 + t) * 16 + ln;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+              const int hh = 4 * lq + q;
+              const float* sh = sn + (j * 16 + hh) * (VB + 2);
+              float o = O[j][t][q] * sh[VB];
+              for (int r = 0; r <= p; r++) o = fmaf(sh[r], bf16_to_f32(newr[r * LAT + col]), o);
+              O[j][t][q] = o;
+            }
+          }
+          __syncthreads();
+        }
+      }
+    }
+    // publish the partials of the pass's positions
+    if (p0 == 0) stamp(a, cx, st, TR_ATT_SOFTMAX);
+#pragma unroll
+    for (int j = 0; j < VPP; j++) {
+      if (j < np) {
+        uint64_t* pp = pll + (size_t)(p0 + j) * pwords;
+        if ((lane & 31) == 0) {
+          uint64_t* q = pp + ((size_t)(hbase + hown) * nch + ch) * PSTR;
+          ll_put_f32(q, m_run[j], k1);
+          ll_put_f32(q + 1, l_run[j], k1);
+        }
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+          const int col = (wave * 4 + t) * 16 + ln;
+#pragma unroll
+          for (int q = 0; q < 4; q++) {
+            const float nb = dpp_mov<0xB1, 0xf, false>(O[j][t][q]);
+            const int hh = 4 * lq + q;
+            if ((ln & 1) == 0) {
+              const uint32_t pr = (uint32_t)__half_as_ushort(__float2half_rn(O[j][t][q])) |
+                                  ((uint32_t)__half_as_ushort(__float2half_rn(nb)) << 16);
+              ll_put(pp + ((size_t)(hbase + hh) * nch + ch) * PSTR + 2 + col / 2, pr, k1);
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  stamp(a, cx, st, TR_ATT_PARTIAL);
+  return true;
+}
+
+// ------------------------------------------------------------------ BM: merge, per position
+template <class SH>
+__device__ __forceinline__ bool bstage_merge(Ctx& cx, const KArgs& a, const Step& st, VLds& V, int nq) {
+  const KCfg& c = a.c;
+  constexpr int KL = SH::KL;
+  const int nch = c.cpg, cpw = c.cpw;
+  const int h = (cx.w * cpw) / KL, c0 = (cx.w * cpw) % KL;
+  const int tid = tid_opaque();
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int PSTR = KL / 2 + 2;
+  const int cpw2 = cpw / 2, nacc = nch * cpw, naw = nch * cpw2;
+  auto pidx = [=](int i) -> int {
+    if (i < naw) return (h * nch + i / cpw2) * PSTR + 2 + c0 / 2 + i % cpw2;
+    const int j = i - naw;
+    return (h * nch + (j >> 1)) * PSTR + (j & 1);
+  };
+  struct StMerge {
+    int naw;
+    __device__ __forceinline__ void operator()(uint32_t* dst, int i, uint32_t v) const {
+      if (i < naw) {
+        reinterpret_cast<float2*>(dst)[i] = make_float2(__half2float(__ushort_as_half((unsigned short)(v & 0xffffu))),
+                                                         __half2float(__ushort_as_half((unsigned short)(v >> 16))));
+      } else {
+        dst[naw + i] = v;
+      }
+    }
+  };
+  float* base = reinterpret_cast<float*>(V.A);
+  float* accs = base;
+  float* mls = base + nacc;
+  float* fw = mls + 2 * nch;
+  float* lsum = fw + nch;
+  float* part = lsum + 1;
+  const size_t pwords = (size_t)SH::NH * nch * PSTR;
+  stamp(a, cx, st, TR_MERGE_START);
+  for (int p = 0; p < nq; p++) {
+    if (!ll_fetch<9>(cx, reinterpret_cast<uint32_t*>(base), wsp<uint64_t>(a, a.off.vpart) + (size_t)p * pwords,
+                     naw + 2 * nch, st.k1, W_PART, pidx, StMerge{naw}))
+      return false;
+    if (wave == 0) {
+      float M = -INFINITY;
+      for (int cc = lane; cc < nch; cc += 64)
+        if (mls[2 * cc + 1] > 0.f) M = fmaxf(M, mls[2 * cc]);
+      M = wave_max_dpp(M);
+      float ls = 0.f;
+      for (int cc = lane; cc < nch; cc += 64) {
+        const float l = mls[2 * cc + 1];
+        const float f = l > 0.f ? __expf(mls[2 * cc] - M) : 0.f;
+        fw[cc] = f;
+        ls += f * l;
+      }
+      ls = wave_sum_dpp(ls);
+      if (lane == 0) lsum[0] = ls;
+    }
+    __syncthreads();
+    const int npp = BLOCK / cpw;
+    {
+      const int j = tid % cpw, q = tid / cpw;
+      float o = 0.f;
+      for (int cc = q; cc < nch; cc += npp) o = fmaf(fw[cc], accs[cc * cpw + j], o);
+      part[tid] = o;
+    }
+    __syncthreads();
+    uint64_t* ol = vbuf(a, a.off.volat, SH::NH * KL, p) + (size_t)h * KL + c0;
+    if (tid < cpw) {
+      float o = 0.f;
+      for (int q = 0; q < npp; q++) o += part[q * cpw + tid];
+      ll_put_f32(ol + tid, o / lsum[0], st.k1);
+    }
+    __syncthreads();
+  }
+  stamp(a, cx, st, TR_ATT_MERGED);
+  return true;
+}
+
+// ------------------------------------------------------------------ BU: o = W_UV o_lat (matrix cores)
+template <class SH>
+__device__ __forceinline__ bool bstage_uv(Ctx& cx, const KArgs& a, const Step& st, VLds& L, int nq) {
+  const DLayer Ly = *gp(st.Ly);
+  constexpr int R = SH::NH * SH::VD, KL = SH::KL, AST = vb_astr(KL);
+  const int r0 = split_at(R, cx.nwg, cx.w), r1 = split_at(R, cx.nwg, cx.w + 1);
+  const int h = r0 / SH::VD;   // host: every workgroup's rows lie in one head, an even count
+  float* tmp = reinterpret_cast<float*>(L.A + VB * AST);
+  __syncthreads();
+  mseg_set(L.segs, 0, Ly.w_uv.w + (size_t)r0 * KL, Ly.w_uv.s, r1 - r0, r0, 0, 0, nq);
+  __syncthreads();
+  auto pre = [&]() -> bool {
+    for (int p = 0; p < nq; p++) {
+      if (!ll_fetch<per_for(KL)>(cx, reinterpret_cast<uint32_t*>(tmp), vbuf(a, a.off.volat, SH::NH * KL, p) + (size_t)h * KL,
+                                 KL, st.k1, W_OLAT))
+        return false;
+      for (int i = tid_opaque(); i < KL; i += BLOCK) L.A[p * AST + i] = (uint16_t)f32_to_bf16(tmp[i]);
+      __syncthreads();
+    }
+    return true;
+  };
+  if (!mfma_list<KL, 4>(L.segs, r1 > r0 ? 1 : 0, L.A, L.out, r1 - r0, L.part, nq, pre)) return false;
+  const int npair = (r1 - r0) / 2;
+  for (int i = tid_opaque(); i < nq * npair; i += BLOCK) {
+    const int p = i / npair, r = r0 + 2 * (i % npair);
+    ll_put(vbuf(a, a.off.vo, R / 2, p) + r / 2,
+           f32_to_bf16(L.out[p * (r1 - r0) + r - r0]) | (f32_to_bf16(L.out[p * (r1 - r0) + r + 1 - r0]) << 16), st.k1);
+  }
+  stamp(a, cx, st, TR_ATT_DONE);
+  return true;
+}
+
+// ------------------------------------------------------------------ BO: h2 = x + W_O o (matrix cores)
+template <class SH>
+__device__ __forceinline__ bool bstage_wo(Ctx& cx, const KArgs& a, const Step& st, VLds& L, int nq) {
+  constexpr int OD = SH::ODIM, AST = vb_astr(OD);
+  int r0, r1;
+  hrows(SH::H, cx.nwg, cx.w, &r0, &r1);
+  const DMat wo = gp(st.Ly)->wo;
+  __syncthreads();
+  mseg_set(L.segs, 0, wo.w + (size_t)r0 * OD, wo.s, r1 - r0, r0, 0, 0, nq);
+  __syncthreads();
+  auto pre = [&]() -> bool {
+    for (int p = 0; p < nq; p++)
+      if (!ll_fetch<per_for(OD / 2)>(cx, reinterpret_cast<uint32_t*>(L.A + p * AST), vbuf(a, a.off.vo, OD / 2, p), OD / 2,
+                                     st.k1, W_O))
+        return false;
+    stamp(a, cx, st, TR_O_READY);
+    return true;
+  };
+  if (!mfma_list<OD, 8>(L.segs, r1 > r0 ? 1 : 0, L.A, L.out, r1 - r0, L.part, nq, pre)) return false;
+  for (int i = tid_opaque(); i < nq * (r1 - r0); i += BLOCK) {
+    const int p = i / (r1 - r0), r = i % (r1 - r0);
+    const float v = L.xres[p * 32 + r] + L.out[i];
+    L.h2res[p * 32 + r] = v;
+    ll_put_f32(vbuf(a, a.off.vh2, SH::H, p) + r0 + r, v, st.k1);
+  }
+  stamp(a, cx, st, TR_WO_DONE);
+  return true;
+}
+
+// ------------------------------------------------------------------ BF: router, shared and union experts
+template <class SH>
+__device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& st, VLds& L, int nq) {
+  const KCfg& c = a.c;
+  const DLayer Ly = *gp(st.Ly);
+  const int w = cx.w, nwg = cx.nwg;
+  const uint32_t k1 = st.k1;
+  constexpr int H = SH::H, AST = vb_astr(H), INTER = SH::INTER;
+  static_assert(SH::MOE && SH::FP8, "the batched FFN is the FP8 MoE one");
+  float* tmp = reinterpret_cast<float*>(L.A + VB * AST);   // [H] fp32 normalised activation (router)
+  // router row of expert w (bf16), loaded ahead of the expert weights
+  constexpr int RCH = H / 8, RPT = (RCH + BLOCK - 1) / BLOCK;
+  uint4 rrow[RPT];
+  float rbias = 0.f;
+  if (w < c.E) {
+    if (c.router == PLD_ROUTER_SIGMOID_BIAS) rbias = gp(Ly.router_bias)[w];
+    const uint16_t* rp0 = Ly.router + (size_t)w * H;
+#pragma unroll
+    for (int k = 0; k < RPT; k++) {
+      const int q = tid_opaque() + k * BLOCK;
+      rrow[k] = q < RCH ? ld_g16(rp0 + q * 8) : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  const int ns = c.nshared;
+  uint64_t* mbase = wsp<uint64_t>(a, a.off.vm);
+  const size_t mwords = (size_t)VB * INTER / 2;   // words of one union slot
+  // shared experts: this workgroup's j range, gate and up segments
+  const int j0 = 2 * split_at(INTER / 2, nwg, w), j1 = 2 * split_at(INTER / 2, nwg, w + 1), nj = j1 - j0;
+  __syncthreads();
+  for (int s = 0; s < ns; s++) {
+    const size_t bo = (size_t)(c.E + s) * Ly.gu_slot_bytes + (size_t)j0 * H;
+    mseg_set(L.segs, 2 * s, Ly.w_gate.w + bo, Ly.w_gate.s + (size_t)(c.E + s) * Ly.gu_slot_scales, nj, j0, 0, 2 * s * nj, nq);
+    mseg_set(L.segs, 2 * s + 1, Ly.w_up.w + bo, Ly.w_up.s + (size_t)(c.E + s) * Ly.gu_slot_scales, nj, j0, 0,
+             (2 * s + 1) * nj, nq);
+  }
+  __syncthreads();
+  auto pre = [&]() -> bool {
+    for (int p = 0; p < nq; p++) {
+      if (!ll_fetch<per_for(H)>(cx, reinterpret_cast<uint32_t*>(tmp), vbuf(a, a.off.vh2, H, p), H, k1, W_H2)) return false;
+      // RMSNorm in fp64: the fp32 result (router) and its bf16 rounding (matrix cores)
+      constexpr int KK = H / BLOCK;
+      float xv[KK];
+      double ss = 0.0;
+#pragma unroll
+      for (int k = 0; k < KK; k++) {
+        xv[k] = tmp[tid_opaque() + k * BLOCK];
+        ss += (double)xv[k] * (double)xv[k];
+      }
+      ss = block_sum(ss, L.red);
+      const double rr = 1.0 / sqrt(ss / (double)H + c.eps);
+      const PLD_GLOBAL float* gm = gp(Ly.ffn_norm);
+#pragma unroll
+      for (int k = 0; k < KK; k++) {
+        const int i = tid_opaque() + k * BLOCK;
+        const double y = ((double)xv[k] * rr) * (double)gm[i];
+        tmp[i] = (float)y;
+        L.A[p * AST + i] = (uint16_t)f32_to_bf16((float)y);
+      }
+      __syncthreads();
+      if (w < c.E) {
+        double s = 0.0;
+#pragma unroll
+        for (int k = 0; k < RPT; k++) {
+          const int q = tid_opaque() + k * BLOCK;
+          if (q < RCH) s += dot8_bf16_f64(rrow[k], tmp + q * 8);
+        }
+        s = block_sum(s, L.red);
+        if (tid_opaque() < 4) {
+          const double key = c.router == PLD_ROUTER_SIGMOID_BIAS ? (1.0 / (1.0 + exp_f64(-s, L.dk))) + (double)rbias : s;
+          const uint64_t bits = (uint64_t)__double_as_longlong(tid_opaque() < 2 ? s : key);
+          ll_put(vbuf(a, a.off.vlog, 4 * (size_t)c.E, p) + 4 * w + tid_opaque(), (uint32_t)(bits >> (32 * (tid_opaque() & 1))),
+                 k1);
+        }
+      }
+      __syncthreads();
+    }
+    stamp(a, cx, st, TR_H2_READY);
+    return true;
+  };
+  if (!mfma_list<H, 8>(L.segs, nj > 0 ? 2 * ns : 0, L.A, L.out, 2 * ns * nj, L.part, nq, pre)) return false;
+  // shared m: silu(gate) * up as bf16 pairs, union slot s, position p
+  for (int i = tid_opaque(); i < ns * nq * (nj / 2); i += BLOCK) {
+    const int s = i / (nq * (nj / 2)), rem = i % (nq * (nj / 2)), p = rem / (nj / 2), jp = 2 * (rem % (nj / 2));
+    const float* go = L.out + p * (2 * ns * nj) + 2 * s * nj;
+    const float* uo = go + nj;
+    const float m0 = silu_f(go[jp]) * uo[jp], m1 = silu_f(go[jp + 1]) * uo[jp + 1];
+    ll_put(mbase + (size_t)s * mwords + (size_t)p * (INTER / 2) + (j0 + jp) / 2, f32_to_bf16(m0) | (f32_to_bf16(m1) << 16),
+           k1);
+  }
+  stamp(a, cx, st, TR_SHARED_GEMV);
+  // top-k per position (wave 0; the same selection in every workgroup), then the union
+  double* lk = reinterpret_cast<double*>(tmp);   // [E][2] (logit, key) of one position
+  for (int p = 0; p < nq; p++) {
+    if (!ll_fetch<per_for(4 * 512)>(cx, reinterpret_cast<uint32_t*>(lk), vbuf(a, a.off.vlog, 4 * (size_t)c.E, p), 4 * c.E,
+                                    k1, W_RT))
+      return false;
+    if (tid_opaque() < 64) {
+      const int lane = tid_opaque();
+      constexpr int NS = 4;   // E <= 256
+      uint64_t ks[NS];
+#pragma unroll
+      for (int i = 0; i < NS; i++) {
+        const int e = lane + 64 * i;
+        const double ke = e < c.E ? lk[2 * e + 1] : 0.0;
+        const uint64_t bb = (uint64_t)__double_as_longlong(ke == 0.0 ? 0.0 : ke);
+        ks[i] = e < c.E ? ((bb >> 63) ? ~bb : (bb | (1ull << 63))) : 0ull;
+      }
+      for (int r = 0; r < c.topk; r++) {
+        uint64_t b = ks[0];
+        uint32_t bi = 0u;
+#pragma unroll
+        for (int i = 1; i < NS; i++) {
+          const bool gt = ks[i] > b;
+          b = gt ? ks[i] : b;
+          bi = gt ? (uint32_t)i : bi;
+        }
+        uint64_t m = b;
+        for (int off = 32; off >= 1; off >>= 1) {
+          const uint64_t o = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(m >> 32), off, 64) << 32) |
+                             (uint32_t)__shfl_xor((int)(uint32_t)m, off, 64);
+          m = o > m ? o : m;
+        }
+        const uint32_t mye = (uint32_t)lane + 64u * bi;
+        const bool hold = b == m;
+        const uint32_t ee = wave_minmax_u32<false>(hold ? mye : 0xffffffffu);
+#pragma unroll
+        for (int i = 0; i < NS; i++) ks[i] = (mye == ee && bi == (uint32_t)i) ? 0ull : ks[i];
+        if (lane == 0) L.isel[p * 8 + r] = (int)ee;
+      }
+    }
+    __syncthreads();
+    const bool sig = c.router == PLD_ROUTER_SIGMOID_BIAS;
+    double* num = L.red;   // [topk <= 8]
+    if (tid_opaque() < c.topk) {
+      const double r = lk[2 * L.isel[p * 8 + tid_opaque()]];
+      num[tid_opaque()] = sig ? 1.0 / (1.0 + exp_f64(-r, L.dk)) : exp_f64(r - lk[2 * L.isel[p * 8]], L.dk);
+    }
+    __syncthreads();
+    if (tid_opaque() < c.topk) {
+      double gsum = 0.0;
+      for (int j = 0; j < c.topk; j++) gsum += num[j];
+      L.fgate[p * 8 + tid_opaque()] = (float)(num[tid_opaque()] / gsum);
+    }
+    __syncthreads();
+  }
+  // union of the selected experts, ascending (thread e tests expert e), slots after the shared ones
+  {
+    int* flag = reinterpret_cast<int*>(tmp);   // [E] position masks, then the prefix scan
+    for (int e = tid_opaque(); e < c.E; e += BLOCK) flag[e] = 0;
+    __syncthreads();
+    if (tid_opaque() == 0) {
+      for (int p = 0; p < nq; p++)
+        for (int r = 0; r < c.topk; r++) flag[L.isel[p * 8 + r]] |= 1 << p;
+      int u = 0;
+      for (int e = 0; e < c.E; e++)
+        if (flag[e]) {
+          L.uexp[ns + u] = e;
+          L.umask[ns + u] = flag[e];
+          u++;
+        }
+      for (int s = 0; s < ns; s++) {
+        L.uexp[s] = c.E + s;
+        L.umask[s] = (1 << nq) - 1;
+      }
+      L.misc[0] = ns + u;
+    }
+    __syncthreads();
+  }
+  if (w == 0 && tid_opaque() < nq * c.topk) {
+    const int p = tid_opaque() / c.topk, r = tid_opaque() % c.topk;
+    st_u32(reinterpret_cast<uint32_t*>(wsp<int>(a, a.off.vsel)) + p * 8 + r, (uint32_t)L.isel[p * 8 + r]);
+    st_f32(wsp<float>(a, a.off.vsel) + VB * 8 + p * 8 + r, L.fgate[p * 8 + r]);
+  }
+  // routed union slots: this workgroup's share of the (slot, row) pairs, in pairs of rows
+  const int nu = L.misc[0] - ns;
+  const int tot = nu * INTER;
+  const int i0 = 2 * split_at(tot / 2, nwg, w), i1 = 2 * split_at(tot / 2, nwg, w + 1);
+  // (pieces kept in LDS: a per-lane array indexed at run time would live in scratch memory)
+  int npc = 0;
+  int* pu = L.pcs;
+  int* pj0 = L.pcs + MAX_MSEGS / 2;
+  int* pj1 = L.pcs + MAX_MSEGS;
+  __syncthreads();
+  for (int u = i0 / INTER; u < nu && u * INTER < i1 && npc < MAX_MSEGS / 2; u++) {
+    const int lo = max(i0, u * INTER) - u * INTER, hi = min(i1, (u + 1) * INTER) - u * INTER;
+    if (lo < hi) {
+      if (tid_opaque() == 0) {
+        pu[npc] = u; pj0[npc] = lo; pj1[npc] = hi;
+      }
+      npc++;
+    }
+  }
+  __syncthreads();
+  int nrows = 0;
+  for (int q = 0; q < npc; q++) nrows += 2 * (pj1[q] - pj0[q]);
+  {
+    int oo = 0;
+    for (int q = 0; q < npc; q++) {
+      const int e = L.uexp[ns + pu[q]], nn = pj1[q] - pj0[q];
+      const size_t bo = (size_t)e * Ly.gu_slot_bytes + (size_t)pj0[q] * H;
+      mseg_set(L.segs, 2 * q, Ly.w_gate.w + bo, Ly.w_gate.s + (size_t)e * Ly.gu_slot_scales, nn, pj0[q], 0, oo, nq);
+      mseg_set(L.segs, 2 * q + 1, Ly.w_up.w + bo, Ly.w_up.s + (size_t)e * Ly.gu_slot_scales, nn, pj0[q], 0, oo + nn, nq);
+      oo += 2 * nn;
+    }
+  }
+  __syncthreads();
+  float* rout = tmp;   // [nq][nrows] (the router scratch is free now)
+  if (!mfma_list<H, 8>(L.segs, 2 * npc, L.A, rout, nrows, L.part, nq, NoPre{})) return false;
+  {
+    int oo = 0;
+    for (int q = 0; q < npc; q++) {
+      const int nn = pj1[q] - pj0[q], u = pu[q], msk = L.umask[ns + u];
+      for (int i = tid_opaque(); i < nq * (nn / 2); i += BLOCK) {
+        const int p = i / (nn / 2), jp = 2 * (i % (nn / 2));
+        if (!((msk >> p) & 1)) continue;
+        const float* go = rout + p * nrows + oo;
+        const float* uo = go + nn;
+        const float m0 = silu_f(go[jp]) * uo[jp], m1 = silu_f(go[jp + 1]) * uo[jp + 1];
+        ll_put(mbase + (size_t)(ns + u) * mwords + (size_t)p * (INTER / 2) + (pj0[q] + jp) / 2,
+               f32_to_bf16(m0) | (f32_to_bf16(m1) << 16), k1);
+      }
+      oo += 2 * nn;
+    }
+  }
+  stamp(a, cx, st, TR_M_STORED);
+  return true;
+}
+
+// ------------------------------------------------------------------ BD: down projections of every (slot, position)
+template <class SH>
+__device__ __forceinline__ bool bstage_down(Ctx& cx, const KArgs& a, const Step& st, VLds& L, int nq, bool last_layer,
+                                            uint16_t* out_hidden) {
+  const KCfg& c = a.c;
+  const DLayer Ly = *gp(st.Ly);
+  constexpr int INTER = SH::INTER, AST = vb_astr(INTER);
+  int r0, r1;
+  hrows(SH::H, cx.nwg, cx.w, &r0, &r1);
+  const int nr = r1 - r0;
+  const int ns = c.nshared, nslot = L.misc[0];
+  uint64_t* mbase = wsp<uint64_t>(a, a.off.vm);
+  const size_t mwords = (size_t)VB * INTER / 2;
+  constexpr int VMAX = (VACT_BYTES - 16384) / (AST * 2);   // vectors per pass (the rest holds the results)
+  float* res = reinterpret_cast<float*>(L.A + VMAX * AST);   // [slots in pass][nq][nr]
+  for (int i = tid_opaque(); i < nq * 32; i += BLOCK) L.facc[i] = 0.f;
+  int s0 = 0;
+  while (s0 < nslot) {
+    // the slots of this pass: as many as fit (vectors and results)
+    int s1 = s0, nv = 0;
+    while (s1 < nslot && s1 - s0 < MAX_MSEGS) {
+      const int cnt = __popc(L.umask[s1] & ((1 << nq) - 1));
+      if (nv + cnt > VMAX || (s1 - s0 + 1) * nq * nr * 4 > 16384) break;
+      nv += cnt;
+      s1++;
+    }
+    __syncthreads();
+    if (tid_opaque() == 0) {
+      int v = 0;
+      for (int s = s0; s < s1; s++) {
+        const int e = L.uexp[s];
+        const int msk = L.umask[s];
+        MSeg& S = L.segs[s - s0];
+        S.w = Ly.w_down.w + (size_t)e * Ly.dn_slot_bytes + (size_t)r0 * INTER;
+        S.s = Ly.w_down.s + (size_t)e * Ly.dn_slot_scales;
+        S.n = nr;
+        S.srow = r0;
+        S.a_off = 0;
+        S.o_off = (s - s0) * nq * nr;
+        for (int p = 0; p < VB; p++) S.vrow[p] = (int8_t)((p < nq && ((msk >> p) & 1)) ? v++ : -1);
+      }
+    }
+    __syncthreads();
+    auto pre = [&]() -> bool {
+      // fetch this pass's (slot, position) vectors, bf16 pairs, into their A rows
+      for (int s = s0; s < s1; s++) {
+        const MSeg& S = L.segs[s - s0];
+        for (int p = 0; p < nq; p++) {
+          const int v = S.vrow[p];
+          if (v < 0) continue;
+          if (!ll_fetch<per_for(INTER / 2)>(cx, reinterpret_cast<uint32_t*>(L.A + v * AST),
+                                            mbase + (size_t)s * mwords + (size_t)p * (INTER / 2), INTER / 2, st.k1, W_M))
+            return false;
+        }
+      }
+      if (s0 == 0) stamp(a, cx, st, TR_M_READY);
+      return true;
+    };
+    if (!mfma_list<INTER, 8>(L.segs, nr > 0 ? s1 - s0 : 0, L.A, res, nr, L.part, nq, pre)) return false;
+    // f_p += gate(slot, p) * down(slot, p), slots in union order
+    for (int i = tid_opaque(); i < nq * nr; i += BLOCK) {
+      const int p = i / nr, r = i % nr;
+      float f = L.facc[p * 32 + r];
+      for (int s = s0; s < s1; s++) {
+        if (!((L.umask[s] >> p) & 1)) continue;
+        float gte = 1.f;
+        if (s >= ns) {
+          const int e = L.uexp[s];
+          gte = 0.f;
+          for (int k = 0; k < c.topk; k++)
+            if (L.isel[p * 8 + k] == e) gte = L.fgate[p * 8 + k];
+        }
+        f = fmaf(gte, res[(s - s0) * nq * nr + p * nr + r], f);
+      }
+      L.facc[p * 32 + r] = f;
+      if (s1 == nslot) st_f32(wsp<float>(a, a.off.vf) + (size_t)p * SH::H + r0 + r, f);   // debug copy of f
+    }
+    s0 = s1;
+  }
+  __syncthreads();
+  stamp(a, cx, st, TR_DOWN_GEMV);
+  // x'_p = h2_p + f_p, bf16 pairs (next layer's input); the last layer's last position also to out_hidden
+  for (int i = tid_opaque(); i < nq * (nr / 2); i += BLOCK) {
+    const int p = i / (nr / 2), r = 2 * (i % (nr / 2));
+    const uint32_t lo = f32_to_bf16(L.h2res[p * 32 + r] + L.facc[p * 32 + r]);
+    const uint32_t hi = f32_to_bf16(L.h2res[p * 32 + r + 1] + L.facc[p * 32 + r + 1]);
+    ll_put(vbuf(a, a.off.vx, SH::H / 2, p) + (r0 + r) / 2, lo | (hi << 16), st.k1);
+    if (last_layer && out_hidden && p == nq - 1) gp(reinterpret_cast<uint32_t*>(out_hidden))[(r0 + r) / 2] = lo | (hi << 16);
+  }
+  stamp(a, cx, st, TR_DOWN_DONE);
+  return true;
+}
+
+// ------------------------------------------------------------------ the batched verify kernel
+// a.n_tokens = nq positions from a.pos0: position 0 takes a.in_token, position p > 0 the
+// caller's draft p - 1 (clamped into the vocabulary). Per-position logits and tokens,
+// and the count of leading drafts equal to the token chosen at the position before.
+template <class SH>
+__global__ void __launch_bounds__(BLOCK, 1) k_verify_mla(KArgs a) {
+  extern __shared__ float lds_raw[];
+  Ctx cx;
+  cx.budget = a.budget;
+  cx.w = blockIdx.x;
+  cx.nwg = gridDim.x;
+  cx.status = wsp<uint32_t>(a, a.off.status);
+  cx.wacc = nullptr;
+  const DLayer* layers = wsp<DLayer>(a, a.off.layers);
+  if ((a.hooks & PLD_HOOK_DROP_WG0) && cx.w == 0) return;
+  const int nq = a.n_tokens;
+  VLds L = vcarve(lds_raw);
+  if (tid_opaque() < TR_SLOTS) L.tr[tid_opaque()] = 0;
+  exp_f64_init(L.dk);
+  __syncthreads();
+  if (tid_opaque() < nq)
+    L.tok[tid_opaque()] = tid_opaque() == 0 ? a.in_token : min(max(gp(a.drafts)[tid_opaque() - 1], 0), a.c.vocab - 1);
+  __syncthreads();
+  for (int li = 0; li < a.n_layers; li++) {
+    cx.layer = a.layer0 + li;
+    cx.token = 0;
+    Step st;
+    st.Ly = layers + a.layer0 + li;
+    st.idx = li;
+    st.k1 = a.step0 + (uint32_t)li + 1u;
+    st.first = li == 0;
+    st.in_hidden = nullptr;
+    st.pos = a.pos0;
+    st.emb_row = nullptr;
+    st.tr = L.tr;
+    KArgs as = a;
+    asm volatile("" : "+s"(as.ws));
+    Ctx cs = cx;
+    asm volatile("" : "+s"(cs.w), "+s"(cs.nwg), "+s"(as.c.cpw), "+s"(as.c.cpg));
+    cs.wacc = (a.trace && st.idx < a.trace_steps) ? L.tr + TR_WAIT : nullptr;
+    stamp(as, cs, st, TR_START);
+    if (!bstage_x<SH>(cs, as, st, L, nq, li)) return;
+    if (!bstage_q<SH>(cs, as, st, L, nq)) return;
+    if (!bstage_absorb<SH>(cs, as, st, L, nq)) return;
+    if (!bstage_attn<SH>(cs, as, st, L, nq)) return;
+    if (!bstage_merge<SH>(cs, as, st, L, nq)) return;
+    if (!bstage_uv<SH>(cs, as, st, L, nq)) return;
+    if (!bstage_wo<SH>(cs, as, st, L, nq)) return;
+    if (!bstage_ffn<SH>(cs, as, st, L, nq)) return;
+    if (!bstage_down<SH>(cs, as, st, L, nq, li == a.n_layers - 1, as.out_hidden)) return;
+    trace_flush(as, cs, st);
+  }
+  // LM head and token choice of every position (the single-position head stage, on each
+  // position's final hidden state; its candidate words in a buffer of the position's own)
+  Lds HL = head_lds(L);
+  const uint32_t kl = a.step0 + (uint32_t)a.n_layers;
+  for (int p = 0; p < nq; p++) {
+    KArgs ah = a;
+    ah.off.x = a.off.vx + (size_t)p * (SH::H / 2) * 8;
+    ah.off.amax = a.off.vamax + (size_t)p * 3 * cx.nwg * 8;
+    Step st;
+    st.Ly = layers + a.layer0 + a.n_layers - 1;
+    st.idx = a.n_layers;
+    st.k1 = kl;
+    st.first = false;
+    st.in_hidden = nullptr;
+    st.pos = a.pos0 + p;
+    st.emb_row = nullptr;
+    st.tr = L.tr;
+    cx.token = p;
+    int tk = 0;
+    if (!stage_head<SH>(cx, ah, st, HL, p, &tk)) return;
+    if (tid_opaque() == 0) L.tok[VB + p] = tk;
+  }
+  __syncthreads();
+  if (cx.w == 0 && tid_opaque() == 0 && a.out_accepted) {
+    int acc = 0;
+    for (int p = 1; p < nq; p++) {
+      if (gp(a.drafts)[p - 1] != L.tok[VB + p - 1]) break;
+      acc++;
+    }
+    gp(a.out_accepted)[0] = acc;
+  }
+}

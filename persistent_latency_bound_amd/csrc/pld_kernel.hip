@@ -71,6 +71,7 @@ struct KCfg {
   int nwg;
   int cpw;     // MLA: q_lat / o_lat outputs per workgroup (absorb, merge)
   int rdim;    // width of the RoPE table rows (head_dim for GQA, rope_dim for MLA)
+  int vq;      // batched verify: max positions (0: not set up)
 };
 
 struct DLayer {
@@ -94,6 +95,8 @@ struct DLayer {
 struct WsOff {
   size_t status, x, q, kv, part, o, h2, logits, m, cqr, ckvr, qr, qlat, olat, amax, ixr, qi, ilist, isel, ll_end, sel,
       gates, spec, a_dbg, b_dbg, f_dbg, ikh, ikl, ilo, itok, kx, rope, layers, total;
+  // batched verify (per-position copies of the LL buffers; vsel is a plain debug area)
+  size_t vx, vcqr, vckv, vqn, vqr, vqlat, vpart, volat, vo, vh2, vlog, vm, vamax, vsel, vf;
 };
 
 struct KArgs {
@@ -1449,6 +1452,7 @@ __global__ void __launch_bounds__(BLOCK, 1) k_decode_gqa(KArgs a) {
 
 #include "pld_mla.hpp"
 #include "pld_kda.hpp"
+#include "pld_batch.hpp"
 
 typedef void (*KernelFn)(KArgs);
 
@@ -1510,6 +1514,12 @@ static KernelFn pick_kernel(const pld_config* c) {
   return nullptr;
 }
 
+// the batched verify kernel of a configuration (the FP8 MLA MoE shape with a head), or null
+static KernelFn pick_verify(const pld_config* c) {
+  if (matches_mla<ShapeMlaFp8>(c) && c->vocab > 0) return k_verify_mla<ShapeMlaFp8>;
+  return nullptr;
+}
+
 }  // namespace pld
 
 // ====================================================================== host runtime
@@ -1530,6 +1540,8 @@ struct pld_handle {
   bool coop;
   hipStream_t last_stream;
   KernelFn fn;
+  KernelFn vfn;            // batched verify kernel (cfg.max_query >= 2), else null
+  size_t vlds_bytes;
   int device;
   uint64_t* trace;
   int trace_steps;
@@ -1720,6 +1732,20 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
         k->stage_words < 3 * nwg)
       return PLD_E_UNSUPPORTED;
   }
+  if (c->max_query < 0 || c->max_query > VB) return PLD_E_INVALID;
+  if (c->max_query >= 2) {
+    // batched verify: the per-workgroup row counts must fit its LDS result areas
+    if (!pick_verify(c) || c->n_shared > 4 || c->top_k > 8 || c->n_experts > 256) return PLD_E_UNSUPPORTED;
+    auto per = [nwg](long long n) { return (n + nwg - 1) / nwg; };
+    const long long hr = 2 * per(c->hidden / 2), xr = per(c->q_lora + c->kv_lora + c->rope_dim);
+    const long long qr = 2 * per((long long)c->n_heads * (c->nope_dim + c->rope_dim) / 2);
+    const long long ur = per((long long)c->n_heads * c->v_dim), sr = 2 * per(c->inter / 2);
+    const long long gr = 2 * (2 * per((long long)c->max_query * c->top_k * c->inter / 2));
+    if (hr > 32 || xr > 64 || qr > 64 || ur > 64 || 2 * c->n_shared * sr > 64 ||
+        98432 + (long long)VB * gr * 4 > VACT_BYTES || ((long long)c->n_heads * c->v_dim) % nwg)
+      return PLD_E_UNSUPPORTED;
+    k->vq = c->max_query;
+  }
   return PLD_OK;
 }
 
@@ -1764,7 +1790,32 @@ WsOff layout(const KCfg& k, int n_layers) {
   } else {
     o.ixr = o.qi = o.ilist = o.isel = 0;
   }
+  if (k.vq >= 2) {
+    const size_t VBW = 8;   // positions per batched step (the kernel's per-position strides)
+    const size_t LAT = (size_t)k.kv_lora + k.rope;
+    o.vx = p; p += al(VBW * (k.H / 2) * W);
+    o.vcqr = p; p += al(VBW * k.q_lora * W);
+    o.vckv = p; p += al(VBW * LAT * W);
+    o.vqn = p; p += al(VBW * k.nh * k.nope * W);
+    o.vqr = p; p += al(VBW * (k.nh * k.rope / 2) * W);
+    o.vqlat = p; p += al(VBW * (k.nh * k.kv_lora / 2) * W);
+    o.vpart = p; p += al(VBW * k.nh * k.cpg * (k.kv_lora / 2 + 2) * W);
+    o.volat = p; p += al(VBW * k.nh * k.kv_lora * W);
+    o.vo = p; p += al(VBW * (k.nh * k.vdim / 2) * W);
+    o.vh2 = p; p += al(VBW * k.H * W);
+    o.vlog = p; p += al(VBW * 4 * k.E * W);
+    o.vm = p; p += al((size_t)(k.vq * k.topk + k.nshared) * VBW * (k.inter / 2) * W);
+    o.vamax = p; p += al(VBW * 3 * k.nwg * W);
+  } else {
+    o.vx = o.vcqr = o.vckv = o.vqn = o.vqr = o.vqlat = o.vpart = o.volat = o.vo = o.vh2 = o.vlog = o.vm = o.vamax = 0;
+  }
   o.ll_end = p;
+  if (k.vq >= 2) {
+    o.vsel = p; p += al(8 * 8 * 4 * 2);   // per-position top-k experts, then their gates
+    o.vf = p; p += al((size_t)8 * k.H * 4);   // per-position FFN output before the residual
+  } else {
+    o.vsel = o.vf = 0;
+  }
   o.sel = p; p += al(64 * 4);
   o.gates = p; p += al(64 * 4);
   o.spec = p; p += al(64 * 4);   // decode_speculative: drafts [16], verify tokens [16], accepted, spare
@@ -1997,6 +2048,8 @@ pld_status init_into(pld_handle* h, const pld_config* cfg, int32_t n_layers, con
   const char* coop = getenv("PLD_COOPERATIVE");
   h->coop = coop && atoi(coop) != 0;
   h->fn = pick_kernel(cfg);
+  h->vfn = k.vq >= 2 ? pick_verify(cfg) : nullptr;
+  h->vlds_bytes = vlds_bytes();
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0) khz = 100000;
   h->wallclock_khz = khz;
@@ -2011,6 +2064,13 @@ pld_status init_into(pld_handle* h, const pld_config* cfg, int32_t n_layers, con
   ok = ok && hipFuncSetAttribute((const void*)h->fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->lds_bytes) == hipSuccess;
   int per_cu = 0;
   ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)h->fn, BLOCK, h->lds_bytes) == hipSuccess;
+  if (ok && h->vfn) {
+    int per_v = 0;
+    ok = hipFuncSetAttribute((const void*)h->vfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->vlds_bytes) ==
+             hipSuccess &&
+         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_v, (const void*)h->vfn, BLOCK, h->vlds_bytes) == hipSuccess;
+    per_cu = std::min(per_cu, per_v);
+  }
   ok = ok && hipDeviceSynchronize() == hipSuccess;
   if (!ok) return PLD_E_HIP;
   if (per_cu < 1) return PLD_E_UNSUPPORTED;
@@ -2169,6 +2229,56 @@ pld_status decode_layers_persistent(pld_handle* h, const pld_persistent_args* a,
                 (hipStream_t)stream, hd);
 }
 
+pld_status decode_verify_batched(pld_handle* h, const pld_persistent_args* a, void* stream) {
+  if (!h || !a) return PLD_E_INVALID;
+  if (h->bad) return PLD_E_STATE;
+  if (!h->vfn) return PLD_E_UNSUPPORTED;
+  const int nq = a->n_query;
+  if (nq < 2 || nq > h->kc.vq || a->n_tokens != 1) return PLD_E_INVALID;
+  if (a->in_token < 0 || a->in_token >= h->cfg.vocab || !a->draft_tokens || ((uintptr_t)a->draft_tokens & 3u))
+    return PLD_E_INVALID;
+  if (!a->out_hidden || !aligned16(a->out_hidden)) return PLD_E_INVALID;
+  if (a->start_pos < 0 || a->start_pos + nq > h->cfg.max_seq) return PLD_E_CAPACITY;
+  if (!(a->temperature >= 0.0) || !std::isfinite(a->temperature)) return PLD_E_INVALID;
+  KArgs k;
+  memset(&k, 0, sizeof(k));
+  k.c = h->kc;
+  k.ws = h->ws;
+  k.off = h->off;
+  k.n_layers = h->n_layers;
+  k.n_tokens = nq;
+  k.pos0 = a->start_pos;
+  k.layer0 = 0;
+  k.step0 = h->steps;
+  k.out_hidden = (uint16_t*)a->out_hidden;
+  k.budget = h->budget;
+  k.trace = h->trace;
+  k.trace_steps = h->trace_steps;
+  k.head_on = 1;
+  k.in_token = a->in_token;
+  k.out_logits = a->out_logits;
+  k.out_tokens = a->out_tokens;
+  k.drafts = a->draft_tokens;
+  k.out_accepted = a->out_accepted;
+  k.embed = h->embed;
+  k.fnorm = h->fnorm;
+  k.head = h->head;
+  k.hooks = h->hooks;
+  k.hook_seed = h->hook_seed;
+  k.temperature = a->temperature;
+  k.sample_seed = a->sample_seed;
+  void* args[] = {&k};
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = h->coop ? hipLaunchCooperativeKernel((const void*)h->vfn, dim3(h->kc.nwg), dim3(BLOCK), args,
+                                                            (unsigned)h->vlds_bytes, s)
+                               : hipLaunchKernel((const void*)h->vfn, dim3(h->kc.nwg), dim3(BLOCK), args, h->vlds_bytes, s);
+  if (e != hipSuccess) return PLD_E_HIP;
+  h->hooks &= ~PLD_HOOK_DROP_WG0;
+  h->steps += (uint32_t)h->n_layers;
+  h->last_stream = s;
+  return PLD_OK;
+}
+
 pld_status decode_poll_status(pld_handle* h, pld_device_status* out) {
   if (!h || !out) return PLD_E_INVALID;
   int32_t st[8];
@@ -2325,9 +2435,20 @@ pld_status pld_debug_buffer(pld_handle* h, const char* name, void** ptr, size_t*
                                                     : (size_t)k.nh * k.cpg * (k.hd + 2) * 8},
       {"kv", h->off.kv, (size_t)std::max(k.nkv * k.hd, 1) * 8},
       {"amax", h->off.amax, (size_t)3 * std::max(k.nwg, 1) * 8},
+      // batched verify (handles made with max_query >= 2): per-position LL buffers, 8 positions
+      {"vx", h->off.vx, k.vq >= 2 ? (size_t)8 * (k.H / 2) * 8 : 0},
+      {"vcq", h->off.vcqr, k.vq >= 2 ? (size_t)8 * k.q_lora * 8 : 0},
+      {"vckv", h->off.vckv, k.vq >= 2 ? (size_t)8 * (k.kv_lora + k.rope) * 8 : 0},
+      {"vqlat", h->off.vqlat, k.vq >= 2 ? (size_t)8 * (k.nh * k.kv_lora / 2) * 8 : 0},
+      {"volat", h->off.volat, k.vq >= 2 ? (size_t)8 * k.nh * k.kv_lora * 8 : 0},
+      {"vo", h->off.vo, k.vq >= 2 ? (size_t)8 * (k.nh * k.vdim / 2) * 8 : 0},
+      {"vh2", h->off.vh2, k.vq >= 2 ? (size_t)8 * k.H * 8 : 0},
+      {"vsel", h->off.vsel, k.vq >= 2 ? (size_t)8 * 8 * 4 * 2 : 0},
+      {"vf", h->off.vf, k.vq >= 2 ? (size_t)8 * k.H * 4 : 0},
   };
   for (auto& e : tab)
     if (!strcmp(e.n, name)) {
+      if (e.sz == 0) return PLD_E_INVALID;
       *ptr = h->ws + e.off;
       *bytes = e.sz;
       return PLD_OK;

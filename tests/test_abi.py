@@ -57,6 +57,7 @@ int main(void) {
   P(pld_config, eps) P(pld_config, rope_base) P(pld_config, vocab) P(pld_config, max_seq)
   P(pld_layer_weights, wo) P(pld_layer_weights, router) P(pld_layer_weights, w_down)
   P(pld_layer_weights, w_aup) P(pld_layer_weights, o_norm) P(pld_config, kda_rank)
+  P(pld_config, expert_wfmt) P(pld_config, max_query)
   P(pld_persistent_args, in_hidden) P(pld_persistent_args, out_accepted)
   P(pld_persistent_args, temperature) P(pld_persistent_args, sample_seed)
   printf("pld_spec_args %zu\n", sizeof(pld_spec_args));
@@ -104,6 +105,7 @@ def test_null_arguments_are_rejected_before_any_device_work():
     assert L.decode_layer_init(None, 1, None, None, None, None, 0, ctypes.byref(h)) == pld.PLD_E_INVALID
     assert L.decode_step(None, 0, None, 0, None, None) == pld.PLD_E_INVALID
     assert L.decode_layers_persistent(None, None, None) == pld.PLD_E_INVALID
+    assert L.decode_verify_batched(None, None, None) == pld.PLD_E_INVALID
     assert L.decode_reset(None) == pld.PLD_E_INVALID
     L.decode_layer_destroy(None)
 
