@@ -33,7 +33,7 @@
 #pragma once
 
 constexpr int VB = 8;                    // positions per batched step (max)
-constexpr int VACT_BYTES = 147456;       // LDS region for matrix-core operands / attention (144 KiB)
+constexpr int VACT_BYTES = 150528;       // LDS region for matrix-core operands / attention (147 KiB)
 constexpr int VPP = 2;                   // positions per attention pass over a chunk
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
@@ -75,7 +75,8 @@ __device__ __forceinline__ void mseg_set(MSeg* segs, int i, const uint8_t* w, co
 //    first D are issued before pre() (the dependency wait), like the vector GEMV.
 //  * The fp32 block scale of the lane's row multiplies each k-step's partial product
 //    (the output column of a lane is its own B row, so the lane holds its own scale).
-// `segs` lives in LDS; `part` is LDS scratch of 8 * 16 * VB floats. Returns false if
+// `segs` lives in LDS; `part` is LDS scratch of 8 * 16 * VB floats; ostr 0 means each
+// segment's own row count. Returns false if
 // pre() reported an abort. Ends with a workgroup barrier.
 template <int K, int D, typename Pre>
 __device__ __forceinline__ bool mfma_list(const MSeg* segs, int nseg, const uint16_t* A, float* out, int ostr,
@@ -96,6 +97,11 @@ __device__ __forceinline__ bool mfma_list(const MSeg* segs, int nseg, const uint
   const int nunits = ntiles * KS;
   const int myunits = wave < nunits ? (nunits - wave + NWAVES - 1) / NWAVES : 0;
   const int nit = myunits * NS;
+  // The item loop below runs in whole groups of D with unconditional loads: a load issued
+  // under a condition leaves the compiler unsure how many are in flight, and it then waits
+  // for all of them before every use (the stream would run one load deep). Past the last
+  // item, loads repeat the last address and results are discarded.
+  const int nitD = (nit + D - 1) / D * D;
   // unit -> (segment, tile in segment, slice)
   auto unit_of = [&](int ui, int* sg, int* tt, int* q) {
     const int u = wave + ui * NWAVES;
@@ -127,19 +133,22 @@ __device__ __forceinline__ bool mfma_list(const MSeg* segs, int nseg, const uint
   uint4 buf[D];
   float scb[D];
   auto issue = [&](int d) {
-    if (iu < myunits) {
-      const int k0 = kbeg + 64 * is;
-      buf[d] = ld_stream16(wrow + k0 + 16 * g);
-      scb[d] = srow[k0 >> 7];
-      if (++is == NS) {
-        is = 0;
-        if (++iu < myunits) open_unit(iu);
-      }
+    const int k0 = kbeg + 64 * is;
+    buf[d] = ld_stream16(wrow + k0 + 16 * g);
+    scb[d] = srow[k0 >> 7];
+    if (is + 1 < NS) {
+      is++;
+    } else if (iu + 1 < myunits) {
+      is = 0;
+      iu++;
+      open_unit(iu);
     }
   };
-  if (myunits > 0) open_unit(0);
+  if (myunits > 0) {
+    open_unit(0);
 #pragma unroll
-  for (int d = 0; d < D; d++) issue(d);
+    for (int d = 0; d < D; d++) issue(d);
+  }
   if (!pre()) return false;
   // compute cursor
   int cu = 0, cs = 0;
@@ -153,10 +162,11 @@ __device__ __forceinline__ bool mfma_list(const MSeg* segs, int nseg, const uint
   };
   if (myunits > 0) open_compute(0);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-  for (int it0 = 0; it0 < nit; it0 += D) {
+  for (int it0 = 0; it0 < nitD; it0 += D) {
 #pragma unroll
     for (int d = 0; d < D; d++) {
-      if (it0 + d < nit) {
+      {
+        const bool live = it0 + d < nit;
         const int k0 = (cq * (K / KS)) + 64 * cs;
         uint4 a0 = make_uint4(0u, 0u, 0u, 0u), a1 = a0;
         if (arow) {
@@ -182,7 +192,7 @@ __device__ __forceinline__ bool mfma_list(const MSeg* segs, int nseg, const uint
         pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), b1, pk, 0, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; i++) acc[i] = fmaf(sc, pk[i], acc[i]);
-        if (++cs == NS) {
+        if (live && ++cs == NS) {
           // unit done: lane holds rows p = 4 g + i of column n
           const MSeg& S = segs[csg];
           const int r = 16 * ctt + n;
@@ -191,7 +201,7 @@ __device__ __forceinline__ bool mfma_list(const MSeg* segs, int nseg, const uint
             for (int i = 0; i < 4; i++) {
               const int p = 4 * g + i;
               if (p < nq) {
-                if (KS == 1) out[S.o_off + p * ostr + r] = acc[i];
+                if (KS == 1) out[S.o_off + p * (ostr ? ostr : S.n) + r] = acc[i];
                 else part[((cq * ntiles + (wave + cu * NWAVES) % ntiles) * 16 + n) * VB + p] = acc[i];
               }
             }
@@ -219,7 +229,7 @@ __device__ __forceinline__ bool mfma_list(const MSeg* segs, int nseg, const uint
       if (r >= segs[s].n) continue;
       float v = 0.f;
       for (int q = 0; q < KS; q++) v += part[((q * ntiles + t) * 16 + nn) * VB + p];
-      out[segs[s].o_off + p * ostr + r] = v;
+      out[segs[s].o_off + p * (ostr ? ostr : segs[s].n) + r] = v;
     }
     __syncthreads();
   }
@@ -233,8 +243,9 @@ struct VLds {
   float* part;     // [8 * 16 * VB] k-slice partials
   float* xres;     // [VB][32]      this workgroup's rows of each position's layer input
   float* h2res;    // [VB][32]      ... and of h2
-  float* facc;     // [VB][32]      FFN output accumulators
+  int* vslot;      // [VB][8] (+ pad to VB * 32 ints) union slot of each position's top-k expert
   double* red;     // [16]
+  double* redv;    // [NWAVES][VB]  per-position block reductions
   int* isel;       // [VB][8]       per-position top-k experts (rank order)
   float* fgate;    // [VB][8]       their gates
   int* uexp;       // [VB * 8 + 4]  union of the selected experts (ascending), then shared
@@ -242,6 +253,7 @@ struct VLds {
   int* misc;       // [16]          union size; misc + 8: the head stage's argmax slot
   int* tok;        // [2 * VB]      input tokens of the positions, then the chosen tokens
   int* pcs;        // [3 * MAX_MSEGS / 2] routed pieces of this workgroup: union slot, j0, j1
+  int* vsrc;       // [32]          down pass: LL word offset of each fetched (slot, position) vector
   MSeg* segs;      // [MAX_MSEGS]
   uint64_t* tr;    // [TR_SLOTS]
   double* dk;      // [16]
@@ -249,8 +261,8 @@ struct VLds {
 };
 constexpr int VOUT_FLOATS = VB * 64;
 __host__ __device__ inline size_t vlds_bytes() {
-  return (size_t)VACT_BYTES + 4 * (VOUT_FLOATS + 8 * 16 * VB + 3 * VB * 32) + 8 * 16 + 4 * (VB * 8) * 2 +
-         4 * 2 * (VB * 8 + 4) + 4 * 16 + 4 * 2 * VB + 4 * 3 * (MAX_MSEGS / 2) + sizeof(MSeg) * MAX_MSEGS +
+  return (size_t)VACT_BYTES + 4 * (VOUT_FLOATS + 8 * 16 * VB + 3 * VB * 32) + 8 * 16 + 8 * NWAVES * VB + 4 * (VB * 8) * 2 +
+         4 * 2 * (VB * 8 + 4) + 4 * 16 + 4 * 2 * VB + 4 * 3 * (MAX_MSEGS / 2) + 4 * 32 + sizeof(MSeg) * MAX_MSEGS +
          8 * TR_SLOTS + 8 * 16;
 }
 __device__ __forceinline__ VLds vcarve(float* base) {
@@ -261,8 +273,9 @@ __device__ __forceinline__ VLds vcarve(float* base) {
   L.part = reinterpret_cast<float*>(p); p += 4 * 8 * 16 * VB;
   L.xres = reinterpret_cast<float*>(p); p += 4 * VB * 32;
   L.h2res = reinterpret_cast<float*>(p); p += 4 * VB * 32;
-  L.facc = reinterpret_cast<float*>(p); p += 4 * VB * 32;
+  L.vslot = reinterpret_cast<int*>(p); p += 4 * VB * 32;
   L.red = reinterpret_cast<double*>(p); p += 8 * 16;
+  L.redv = reinterpret_cast<double*>(p); p += 8 * NWAVES * VB;
   L.isel = reinterpret_cast<int*>(p); p += 4 * VB * 8;
   L.fgate = reinterpret_cast<float*>(p); p += 4 * VB * 8;
   L.uexp = reinterpret_cast<int*>(p); p += 4 * (VB * 8 + 4);
@@ -270,6 +283,7 @@ __device__ __forceinline__ VLds vcarve(float* base) {
   L.misc = reinterpret_cast<int*>(p); p += 4 * 16;
   L.tok = reinterpret_cast<int*>(p); p += 4 * 2 * VB;
   L.pcs = reinterpret_cast<int*>(p); p += 4 * 3 * (MAX_MSEGS / 2);
+  L.vsrc = reinterpret_cast<int*>(p); p += 4 * 32;
   L.segs = reinterpret_cast<MSeg*>(p); p += sizeof(MSeg) * MAX_MSEGS;
   L.tr = reinterpret_cast<uint64_t*>(p); p += 8 * TR_SLOTS;
   L.dk = reinterpret_cast<double*>(p);
@@ -300,6 +314,95 @@ __device__ __forceinline__ Lds head_lds(const VLds& V) {
 template <typename T = uint64_t>
 __device__ __forceinline__ uint64_t* vbuf(const KArgs& a, size_t off, size_t words, int p) {
   return wsp<uint64_t>(a, off) + (size_t)p * words;
+}
+
+// LL fetch of nq per-position vectors of N words: position p's words at src + p * sstride
+// (LL words), into dst + p * dstride (32-bit words, LDS); one pass, all loads in flight.
+template <int N>
+struct IdxRows {
+  int sstride;
+  __device__ __forceinline__ int operator()(int i) const { return (i / N) * sstride + i % N; }
+};
+template <int N>
+struct StRows {
+  int dstride;
+  __device__ __forceinline__ void operator()(uint32_t* dst, int i, uint32_t v) const { dst[(i / N) * dstride + i % N] = v; }
+};
+template <int N>
+__device__ __forceinline__ bool ll_fetch_rows(Ctx& cx, uint32_t* dst, int dstride, const uint64_t* src, int sstride,
+                                              int nq, uint32_t ep, int wid) {
+  return ll_fetch<per_for(VB * N)>(cx, dst, src, nq * N, ep, wid, IdxRows<N>{sstride}, StRows<N>{dstride});
+}
+
+// Sums over the workgroup of VB per-thread values at once (one pair of barriers); every
+// thread gets the totals.
+__device__ __forceinline__ void block_sum_rows(double (&v)[VB], double* redv) {
+  const int lane = tid_opaque() & 63, wave = tid_opaque() >> 6;
+#pragma unroll
+  for (int p = 0; p < VB; p++) v[p] = wave_sum_any(v[p]);
+  __syncthreads();
+  if (lane == 0) {
+#pragma unroll
+    for (int p = 0; p < VB; p++) redv[wave * VB + p] = v[p];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int p = 0; p < VB; p++) {
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < NWAVES; w++) t += redv[w * VB + p];
+    v[p] = t;
+  }
+  __syncthreads();
+}
+
+// RMSNorm of the nq rows of an N-vector, in fp64 like the single-position path (fp64 sum of
+// squares and product, one rounding to bf16), into the bf16 A rows A + p * astr. The input
+// element (p, i) is ld(p, i) (LDS; it may be the A row itself: each element is read and then
+// written by the same thread); gamma in registers; the fp32 result also to f32 + p * fstr
+// when f32 is set. A thread's elements of one row are read together before any write.
+template <int N, typename Ld>
+__device__ __forceinline__ void rms_rows(uint16_t* A, int astr, Ld&& ld, const RegVec<N>& gam, double eps,
+                                         double* redv, int nq, float* f32 = nullptr, int fstr = 0) {
+  constexpr int KK = RegVec<N>::K;
+  double ss[VB];
+#pragma unroll
+  for (int p = 0; p < VB; p++) {
+    ss[p] = 0.0;
+    if (p < nq) {
+      float xv[KK];
+#pragma unroll
+      for (int k = 0; k < KK; k++) {
+        const int i = tid_opaque() + k * BLOCK;
+        xv[k] = (N % BLOCK == 0 || i < N) ? ld(p, i) : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < KK; k++) ss[p] += (double)xv[k] * (double)xv[k];
+    }
+  }
+  block_sum_rows(ss, redv);
+#pragma unroll
+  for (int p = 0; p < VB; p++) {
+    if (p < nq) {
+      const double r = 1.0 / sqrt(ss[p] / (double)N + eps);
+      float xv[KK];
+#pragma unroll
+      for (int k = 0; k < KK; k++) {
+        const int i = tid_opaque() + k * BLOCK;
+        xv[k] = (N % BLOCK == 0 || i < N) ? ld(p, i) : 0.f;
+      }
+#pragma unroll
+      for (int k = 0; k < KK; k++) {
+        const int i = tid_opaque() + k * BLOCK;
+        if (N % BLOCK == 0 || i < N) {
+          const double y = ((double)xv[k] * r) * (double)gam.v[k];
+          A[p * astr + i] = (uint16_t)f64_to_bf16(y);
+          if (f32) f32[p * fstr + i] = (float)y;
+        }
+      }
+    }
+  }
+  __syncthreads();
 }
 
 // RMSNorm of a vector held in LDS as fp32 (src) into a bf16 A row (dst), in fp64 like the
@@ -336,6 +439,8 @@ __device__ __forceinline__ bool bstage_x(Ctx& cx, const KArgs& a, const Step& st
   const int r0 = split_at(R, nwg, w), r1 = split_at(R, nwg, w + 1);
   int h0, h1;
   hrows(H, nwg, w, &h0, &h1);
+  RegVec<H> gam;
+  gam.load(Ly.attn_norm);
   {
     __syncthreads();
     int ns = 0;
@@ -351,37 +456,26 @@ __device__ __forceinline__ bool bstage_x(Ctx& cx, const KArgs& a, const Step& st
     }
     __syncthreads();
     auto pre = [&]() -> bool {
-      for (int p = 0; p < nq; p++) {
-        uint16_t* Ar = L.A + p * AST;
-        uint32_t* Aw = reinterpret_cast<uint32_t*>(Ar);
-        if (li == 0) {
+      // the nq inputs as bf16 rows in place: embedding rows (first layer) or the previous
+      // layer's outputs (LL words of bf16 pairs), all fetched together
+      if (li == 0) {
+        for (int p = 0; p < nq; p++) {
           const PLD_GLOBAL uint32_t* src = gp(reinterpret_cast<const uint32_t*>(a.embed + (size_t)L.tok[p] * H));
+          uint32_t* Aw = reinterpret_cast<uint32_t*>(L.A + p * AST);
           for (int i = tid_opaque(); i < H / 2; i += BLOCK) Aw[i] = src[i];
-          __syncthreads();
-        } else if (!ll_fetch<per_for(H / 2)>(cx, Aw, vbuf(a, a.off.vx, H / 2, p), H / 2, st.k1 - 1u, W_X)) {
-          return false;
         }
-        for (int r = h0 + tid_opaque(); r < h1; r += BLOCK) L.xres[p * 32 + (r - h0)] = bf16_to_f32(Ar[r]);
-        // RMSNorm in place: each thread reads its own elements into registers first
-        constexpr int KK = H / BLOCK;
-        static_assert(H % BLOCK == 0, "hidden size");
-        float xv[KK];
-        double ss = 0.0;
-#pragma unroll
-        for (int k = 0; k < KK; k++) {
-          xv[k] = bf16_to_f32(Ar[tid_opaque() + k * BLOCK]);
-          ss += (double)xv[k] * (double)xv[k];
-        }
-        ss = block_sum(ss, L.red);   // (its barrier also orders the xres reads before the writes)
-        const double rr = 1.0 / sqrt(ss / (double)H + a.c.eps);
-        const PLD_GLOBAL float* gm = gp(Ly.attn_norm);
-#pragma unroll
-        for (int k = 0; k < KK; k++) {
-          const int i = tid_opaque() + k * BLOCK;
-          Ar[i] = (uint16_t)f64_to_bf16(((double)xv[k] * rr) * (double)gm[i]);
-        }
+        __syncthreads();
+      } else if (!ll_fetch_rows<H / 2>(cx, reinterpret_cast<uint32_t*>(L.A), AST / 2, vbuf(a, a.off.vx, H / 2, 0), H / 2,
+                                       nq, st.k1 - 1u, W_X)) {
+        return false;
+      }
+      stamp(a, cx, st, TR_X_READY);
+      for (int i = tid_opaque(); i < nq * (h1 - h0); i += BLOCK) {
+        const int p = i / (h1 - h0), r = h0 + i % (h1 - h0);
+        L.xres[p * 32 + (r - h0)] = bf16_to_f32(L.A[p * AST + r]);
       }
       __syncthreads();
+      rms_rows<H>(L.A, AST, [&](int p, int i) { return bf16_to_f32(L.A[p * AST + i]); }, gam, a.c.eps, L.redv, nq);
       stamp(a, cx, st, TR_X_NORMED);
       return true;
     };
@@ -405,16 +499,16 @@ __device__ __forceinline__ bool bstage_q(Ctx& cx, const KArgs& a, const Step& st
   const int w = cx.w, nwg = cx.nwg;
   constexpr int QL = SH::QL, RQ = SH::NH * SH::QH, AST = vb_astr(QL);
   const int r0 = 2 * split_at(RQ / 2, nwg, w), r1 = 2 * split_at(RQ / 2, nwg, w + 1);
-  float* tmp = reinterpret_cast<float*>(L.A + VB * AST);   // [QL] fp32
+  float* tmp = reinterpret_cast<float*>(L.A + VB * AST);   // [VB][QL] fp32
+  RegVec<QL> gq;
+  gq.load(Ly.q_norm);
   __syncthreads();
   mseg_set(L.segs, 0, Ly.w_uq.w + (size_t)r0 * QL, Ly.w_uq.s, r1 - r0, r0, 0, 0, nq);
   __syncthreads();
   auto pre = [&]() -> bool {
-    for (int p = 0; p < nq; p++) {
-      if (!ll_fetch<per_for(QL)>(cx, reinterpret_cast<uint32_t*>(tmp), vbuf(a, a.off.vcqr, QL, p), QL, st.k1, W_CQ))
-        return false;
-      rms_to_bf16<QL>(L.A + p * AST, tmp, gp(Ly.q_norm), a.c.eps, L.red);
-    }
+    if (!ll_fetch_rows<QL>(cx, reinterpret_cast<uint32_t*>(tmp), QL, vbuf(a, a.off.vcqr, QL, 0), QL, nq, st.k1, W_CQ))
+      return false;
+    rms_rows<QL>(L.A, AST, [&](int p, int i) { return tmp[p * QL + i]; }, gq, a.c.eps, L.redv, nq);
     stamp(a, cx, st, TR_CQ_READY);
     return true;
   };
@@ -441,6 +535,10 @@ __device__ __forceinline__ bool bstage_q(Ctx& cx, const KArgs& a, const Step& st
 }
 
 // ------------------------------------------------------------------ BA: q_lat = W_UK^T q_nope (per position)
+// Workgroup (head h, cpw columns); thread (row group rr, 16-column chunk ck) holds its rows'
+// weights in registers for every position. Per position: the thread's partial column sums,
+// reduced over the 8 row groups of a wave with lane shuffles, then over the 8 waves in LDS
+// (all positions at once).
 template <class SH>
 __device__ __forceinline__ bool bstage_absorb(Ctx& cx, const KArgs& a, const Step& st, VLds& L, int nq) {
   const KCfg& c = a.c;
@@ -449,9 +547,10 @@ __device__ __forceinline__ bool bstage_absorb(Ctx& cx, const KArgs& a, const Ste
   constexpr int SBK = (KL + 127) / 128;
   const int cpw = c.cpw;
   const int h = (cx.w * cpw) / KL, c0 = (cx.w * cpw) % KL;
-  const int cpr = cpw / EPC, rpp = BLOCK / cpr;
+  const int cpr = cpw / EPC, rpp = BLOCK / cpr;   // host: cpw == 128 (8 chunks per row, 64 row groups)
   constexpr int MAXP = 4;
   const int tid = tid_opaque();
+  const int lane = tid & 63, wave = tid >> 6;
   const int ck = tid % cpr, rr = tid / cpr;
   uint4 wv[MAXP];
   float sc[MAXP];
@@ -466,15 +565,12 @@ __device__ __forceinline__ bool bstage_absorb(Ctx& cx, const KArgs& a, const Ste
       sc[p] = gp(Ly.w_uk.s)[(row >> 7) * SBK + ((c0 + ck * EPC) >> 7)];
     }
   }
-  float* base = reinterpret_cast<float*>(L.A);
-  float* qv = base;                     // [ND]
-  const int rs = rpp + 1;
-  float* red = base + ND;               // [cpw][rs]
-  float* red2 = red + cpw * rs;         // [BLOCK / cpw][cpw]
+  float* qv = reinterpret_cast<float*>(L.A);   // [VB][ND] q_nope of head h per position
+  float* red = qv + VB * ND;                   // [VB][NWAVES][cpw] wave partial column sums
+  if (!ll_fetch_rows<ND>(cx, reinterpret_cast<uint32_t*>(qv), ND, vbuf(a, a.off.vqn, SH::NH * ND, 0) + (size_t)h * ND,
+                         SH::NH * ND, nq, st.k1, W_QN))
+    return false;
   for (int q = 0; q < nq; q++) {
-    if (!ll_fetch<per_for(ND)>(cx, reinterpret_cast<uint32_t*>(qv), vbuf(a, a.off.vqn, SH::NH * ND, q) + (size_t)h * ND,
-                               ND, st.k1, W_QN))
-      return false;
     float acc[EPC];
 #pragma unroll
     for (int e = 0; e < EPC; e++) acc[e] = 0.f;
@@ -482,7 +578,7 @@ __device__ __forceinline__ bool bstage_absorb(Ctx& cx, const KArgs& a, const Ste
     for (int p = 0; p < MAXP; p++) {
       const int d = rr + p * rpp;
       if (p * rpp < ND) {
-        const float qq = d < ND ? qv[d] * sc[p] : 0.f;
+        const float qq = d < ND ? qv[q * ND + d] * sc[p] : 0.f;
         const uint32_t wd[4] = {wv[p].x, wv[p].y, wv[p].z, wv[p].w};
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -495,34 +591,34 @@ __device__ __forceinline__ bool bstage_absorb(Ctx& cx, const KArgs& a, const Ste
         }
       }
     }
+    // the 8 row groups of a wave are lane bits 3..5
 #pragma unroll
-    for (int e = 0; e < EPC; e++) red[(ck * EPC + e) * rs + rr] = acc[e];
-    __syncthreads();
-    {
-      const int ng = BLOCK / cpw, rpg = rpp / ng;
-      const int j = tid % cpw, gq = tid / cpw;
-      const float* col = red + j * rs + gq * rpg;
-      float s4[4] = {0.f, 0.f, 0.f, 0.f};
-      int gg = 0;
-      for (; gg + 4 <= rpg; gg += 4) {
-#pragma unroll
-        for (int u = 0; u < 4; u++) s4[u] += col[gg + u];
-      }
-      for (; gg < rpg; gg++) s4[0] += col[gg];
-      red2[gq * cpw + j] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-      __syncthreads();
-      float tot = 0.f;
-      if (tid < cpw)
-        for (int qq = 0; qq < ng; qq++) tot += red2[qq * cpw + tid];
-      __syncthreads();
-      if (tid < cpw) red2[tid] = tot;
-      __syncthreads();
+    for (int e = 0; e < EPC; e++) {
+      float v = acc[e];
+      v += __shfl_xor(v, 8, 64);
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      acc[e] = v;
     }
-    uint64_t* ql = vbuf(a, a.off.vqlat, SH::NH * KL / 2, q) + ((size_t)h * KL + c0) / 2;
-    for (int j = 2 * tid; j < cpw; j += 2 * BLOCK)
-      ll_put(ql + j / 2, f32_to_bf16(red2[j]) | (f32_to_bf16(red2[j + 1]) << 16), st.k1);
-    __syncthreads();
+    if (lane < 8) {
+#pragma unroll
+      for (int e = 0; e < EPC; e++) red[(q * NWAVES + wave) * cpw + ck * EPC + e] = acc[e];
+    }
   }
+  __syncthreads();
+  // q_lat as bf16 pairs: the attention's matrix cores take it in bf16 (same rounding)
+  for (int i = tid; i < nq * (cpw / 2); i += BLOCK) {
+    const int q = i / (cpw / 2), j = 2 * (i % (cpw / 2));
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+    for (int wv2 = 0; wv2 < NWAVES; wv2++) {
+      s0 += red[(q * NWAVES + wv2) * cpw + j];
+      s1 += red[(q * NWAVES + wv2) * cpw + j + 1];
+    }
+    ll_put(vbuf(a, a.off.vqlat, SH::NH * KL / 2, q) + ((size_t)h * KL + c0 + j) / 2,
+           f32_to_bf16(s0) | (f32_to_bf16(s1) << 16), st.k1);
+  }
+  __syncthreads();
   stamp(a, cx, st, TR_ATT_SCORES);
   return true;
 }
@@ -848,45 +944,56 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
 }
 
 // ------------------------------------------------------------------ BM: merge, per position
+// Workgroup (head h, cpw columns) as in the single-position stage; the partials of MG
+// positions are fetched together (one LL fetch), then wave p (< MG) forms position p's
+// chunk weights and thread (p, column) sums the chunks.
 template <class SH>
 __device__ __forceinline__ bool bstage_merge(Ctx& cx, const KArgs& a, const Step& st, VLds& V, int nq) {
   const KCfg& c = a.c;
-  constexpr int KL = SH::KL;
+  constexpr int KL = SH::KL, MG = 4;
   const int nch = c.cpg, cpw = c.cpw;
   const int h = (cx.w * cpw) / KL, c0 = (cx.w * cpw) % KL;
   const int tid = tid_opaque();
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int PSTR = KL / 2 + 2;
   const int cpw2 = cpw / 2, nacc = nch * cpw, naw = nch * cpw2;
-  auto pidx = [=](int i) -> int {
-    if (i < naw) return (h * nch + i / cpw2) * PSTR + 2 + c0 / 2 + i % cpw2;
-    const int j = i - naw;
-    return (h * nch + (j >> 1)) * PSTR + (j & 1);
+  const int per = naw + 2 * nch;                 // words of one position
+  const int pwords = SH::NH * nch * PSTR;        // LL words of one position's partials
+  const int fstr = nacc + 2 * nch;               // floats of one position in LDS
+  // word i of the group: position i / per, then as in the single-position stage
+  struct IdxM {
+    int per, naw, cpw2, nch, h, c0, pwords;
+    __device__ __forceinline__ int operator()(int i) const {
+      const int q = i / per, k = i % per;
+      if (k < naw) return q * pwords + (h * nch + k / cpw2) * PSTR + 2 + c0 / 2 + k % cpw2;
+      const int j = k - naw;
+      return q * pwords + (h * nch + (j >> 1)) * PSTR + (j & 1);
+    }
   };
-  struct StMerge {
-    int naw;
+  struct StM {
+    int per, naw, fstr;
     __device__ __forceinline__ void operator()(uint32_t* dst, int i, uint32_t v) const {
-      if (i < naw) {
-        reinterpret_cast<float2*>(dst)[i] = make_float2(__half2float(__ushort_as_half((unsigned short)(v & 0xffffu))),
-                                                         __half2float(__ushort_as_half((unsigned short)(v >> 16))));
+      const int q = i / per, k = i % per;
+      uint32_t* d = dst + q * fstr;
+      if (k < naw) {
+        reinterpret_cast<float2*>(d)[k] = make_float2(__half2float(__ushort_as_half((unsigned short)(v & 0xffffu))),
+                                                      __half2float(__ushort_as_half((unsigned short)(v >> 16))));
       } else {
-        dst[naw + i] = v;
+        d[naw + k] = v;
       }
     }
   };
-  float* base = reinterpret_cast<float*>(V.A);
-  float* accs = base;
-  float* mls = base + nacc;
-  float* fw = mls + 2 * nch;
-  float* lsum = fw + nch;
-  float* part = lsum + 1;
-  const size_t pwords = (size_t)SH::NH * nch * PSTR;
+  float* base = reinterpret_cast<float*>(V.A);     // [MG][nacc floats, then (m, l) per chunk]
+  float* fw = base + MG * fstr;                    // [MG][nch]
+  float* lsum = fw + MG * nch;                     // [MG]
   stamp(a, cx, st, TR_MERGE_START);
-  for (int p = 0; p < nq; p++) {
-    if (!ll_fetch<9>(cx, reinterpret_cast<uint32_t*>(base), wsp<uint64_t>(a, a.off.vpart) + (size_t)p * pwords,
-                     naw + 2 * nch, st.k1, W_PART, pidx, StMerge{naw}))
+  for (int p0 = 0; p0 < nq; p0 += MG) {
+    const int np = min(MG, nq - p0);
+    if (!ll_fetch<16>(cx, reinterpret_cast<uint32_t*>(base), wsp<uint64_t>(a, a.off.vpart) + (size_t)p0 * pwords,
+                      np * per, st.k1, W_PART, IdxM{per, naw, cpw2, nch, h, c0, pwords}, StM{per, naw, fstr}))
       return false;
-    if (wave == 0) {
+    if (wave < np) {
+      const float* mls = base + wave * fstr + nacc;
       float M = -INFINITY;
       for (int cc = lane; cc < nch; cc += 64)
         if (mls[2 * cc + 1] > 0.f) M = fmaxf(M, mls[2 * cc]);
@@ -895,26 +1002,19 @@ __device__ __forceinline__ bool bstage_merge(Ctx& cx, const KArgs& a, const Step
       for (int cc = lane; cc < nch; cc += 64) {
         const float l = mls[2 * cc + 1];
         const float f = l > 0.f ? __expf(mls[2 * cc] - M) : 0.f;
-        fw[cc] = f;
+        fw[wave * nch + cc] = f;
         ls += f * l;
       }
       ls = wave_sum_dpp(ls);
-      if (lane == 0) lsum[0] = ls;
+      if (lane == 0) lsum[wave] = ls;
     }
     __syncthreads();
-    const int npp = BLOCK / cpw;
-    {
-      const int j = tid % cpw, q = tid / cpw;
+    for (int i = tid; i < np * cpw; i += BLOCK) {
+      const int q = i / cpw, j = i % cpw;
+      const float* accs = base + q * fstr;
       float o = 0.f;
-      for (int cc = q; cc < nch; cc += npp) o = fmaf(fw[cc], accs[cc * cpw + j], o);
-      part[tid] = o;
-    }
-    __syncthreads();
-    uint64_t* ol = vbuf(a, a.off.volat, SH::NH * KL, p) + (size_t)h * KL + c0;
-    if (tid < cpw) {
-      float o = 0.f;
-      for (int q = 0; q < npp; q++) o += part[q * cpw + tid];
-      ll_put_f32(ol + tid, o / lsum[0], st.k1);
+      for (int cc = 0; cc < nch; cc++) o = fmaf(fw[q * nch + cc], accs[cc * cpw + j], o);
+      ll_put_f32(vbuf(a, a.off.volat, SH::NH * KL, p0 + q) + (size_t)h * KL + c0 + j, o / lsum[q], st.k1);
     }
     __syncthreads();
   }
@@ -934,13 +1034,11 @@ __device__ __forceinline__ bool bstage_uv(Ctx& cx, const KArgs& a, const Step& s
   mseg_set(L.segs, 0, Ly.w_uv.w + (size_t)r0 * KL, Ly.w_uv.s, r1 - r0, r0, 0, 0, nq);
   __syncthreads();
   auto pre = [&]() -> bool {
-    for (int p = 0; p < nq; p++) {
-      if (!ll_fetch<per_for(KL)>(cx, reinterpret_cast<uint32_t*>(tmp), vbuf(a, a.off.volat, SH::NH * KL, p) + (size_t)h * KL,
-                                 KL, st.k1, W_OLAT))
-        return false;
-      for (int i = tid_opaque(); i < KL; i += BLOCK) L.A[p * AST + i] = (uint16_t)f32_to_bf16(tmp[i]);
-      __syncthreads();
-    }
+    if (!ll_fetch_rows<KL>(cx, reinterpret_cast<uint32_t*>(tmp), KL, vbuf(a, a.off.volat, SH::NH * KL, 0) + (size_t)h * KL,
+                           SH::NH * KL, nq, st.k1, W_OLAT))
+      return false;
+    for (int i = tid_opaque(); i < nq * KL; i += BLOCK) L.A[(i / KL) * AST + i % KL] = (uint16_t)f32_to_bf16(tmp[i]);
+    __syncthreads();
     return true;
   };
   if (!mfma_list<KL, 4>(L.segs, r1 > r0 ? 1 : 0, L.A, L.out, r1 - r0, L.part, nq, pre)) return false;
@@ -965,10 +1063,9 @@ __device__ __forceinline__ bool bstage_wo(Ctx& cx, const KArgs& a, const Step& s
   mseg_set(L.segs, 0, wo.w + (size_t)r0 * OD, wo.s, r1 - r0, r0, 0, 0, nq);
   __syncthreads();
   auto pre = [&]() -> bool {
-    for (int p = 0; p < nq; p++)
-      if (!ll_fetch<per_for(OD / 2)>(cx, reinterpret_cast<uint32_t*>(L.A + p * AST), vbuf(a, a.off.vo, OD / 2, p), OD / 2,
-                                     st.k1, W_O))
-        return false;
+    if (!ll_fetch_rows<OD / 2>(cx, reinterpret_cast<uint32_t*>(L.A), AST / 2, vbuf(a, a.off.vo, OD / 2, 0), OD / 2, nq,
+                               st.k1, W_O))
+      return false;
     stamp(a, cx, st, TR_O_READY);
     return true;
   };
@@ -992,7 +1089,9 @@ __device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& 
   const uint32_t k1 = st.k1;
   constexpr int H = SH::H, AST = vb_astr(H), INTER = SH::INTER;
   static_assert(SH::MOE && SH::FP8, "the batched FFN is the FP8 MoE one");
-  float* tmp = reinterpret_cast<float*>(L.A + VB * AST);   // [H] fp32 normalised activation (router)
+  float* tmp = reinterpret_cast<float*>(L.A + VB * AST);   // [2][H] fp32 normalised activations (router)
+  RegVec<H> gmf;
+  gmf.load(Ly.ffn_norm);
   // router row of expert w (bf16), loaded ahead of the expert weights
   constexpr int RCH = H / 8, RPT = (RCH + BLOCK - 1) / BLOCK;
   uint4 rrow[RPT];
@@ -1020,41 +1119,33 @@ __device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& 
   }
   __syncthreads();
   auto pre = [&]() -> bool {
-    for (int p = 0; p < nq; p++) {
-      if (!ll_fetch<per_for(H)>(cx, reinterpret_cast<uint32_t*>(tmp), vbuf(a, a.off.vh2, H, p), H, k1, W_H2)) return false;
-      // RMSNorm in fp64: the fp32 result (router) and its bf16 rounding (matrix cores)
-      constexpr int KK = H / BLOCK;
-      float xv[KK];
-      double ss = 0.0;
-#pragma unroll
-      for (int k = 0; k < KK; k++) {
-        xv[k] = tmp[tid_opaque() + k * BLOCK];
-        ss += (double)xv[k] * (double)xv[k];
-      }
-      ss = block_sum(ss, L.red);
-      const double rr = 1.0 / sqrt(ss / (double)H + c.eps);
-      const PLD_GLOBAL float* gm = gp(Ly.ffn_norm);
-#pragma unroll
-      for (int k = 0; k < KK; k++) {
-        const int i = tid_opaque() + k * BLOCK;
-        const double y = ((double)xv[k] * rr) * (double)gm[i];
-        tmp[i] = (float)y;
-        L.A[p * AST + i] = (uint16_t)f32_to_bf16((float)y);
-      }
-      __syncthreads();
+    // two positions at a time (fp32 h2 rows in tmp): RMSNorm in fp64, the fp32 result for the
+    // router and its bf16 rounding for the matrix cores; then the router logits (fp64)
+    for (int p0 = 0; p0 < nq; p0 += 2) {
+      const int np = min(2, nq - p0);
+      if (!ll_fetch_rows<H>(cx, reinterpret_cast<uint32_t*>(tmp), H, vbuf(a, a.off.vh2, H, p0), H, np, k1, W_H2))
+        return false;
+      rms_rows<H>(L.A + p0 * AST, AST, [&](int p, int i) { return tmp[p * H + i]; }, gmf, c.eps, L.redv, np, tmp, H);
       if (w < c.E) {
-        double s = 0.0;
+        double sv[VB];
 #pragma unroll
-        for (int k = 0; k < RPT; k++) {
-          const int q = tid_opaque() + k * BLOCK;
-          if (q < RCH) s += dot8_bf16_f64(rrow[k], tmp + q * 8);
+        for (int p = 0; p < VB; p++) {
+          sv[p] = 0.0;
+          if (p < np) {
+#pragma unroll
+            for (int k = 0; k < RPT; k++) {
+              const int q = tid_opaque() + k * BLOCK;
+              if (q < RCH) sv[p] += dot8_bf16_f64(rrow[k], tmp + p * H + q * 8);
+            }
+          }
         }
-        s = block_sum(s, L.red);
-        if (tid_opaque() < 4) {
-          const double key = c.router == PLD_ROUTER_SIGMOID_BIAS ? (1.0 / (1.0 + exp_f64(-s, L.dk))) + (double)rbias : s;
-          const uint64_t bits = (uint64_t)__double_as_longlong(tid_opaque() < 2 ? s : key);
-          ll_put(vbuf(a, a.off.vlog, 4 * (size_t)c.E, p) + 4 * w + tid_opaque(), (uint32_t)(bits >> (32 * (tid_opaque() & 1))),
-                 k1);
+        block_sum_rows(sv, L.redv);
+        if (tid_opaque() < 4 * np) {
+          const int p = tid_opaque() >> 2, wd = tid_opaque() & 3;
+          const double sp = p == 0 ? sv[0] : sv[1];
+          const double key = c.router == PLD_ROUTER_SIGMOID_BIAS ? (1.0 / (1.0 + exp_f64(-sp, L.dk))) + (double)rbias : sp;
+          const uint64_t bits = (uint64_t)__double_as_longlong(wd < 2 ? sp : key);
+          ll_put(vbuf(a, a.off.vlog, 4 * (size_t)c.E, p0 + p) + 4 * w + wd, (uint32_t)(bits >> (32 * (wd & 1))), k1);
         }
       }
       __syncthreads();
@@ -1212,92 +1303,127 @@ __device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& 
 }
 
 // ------------------------------------------------------------------ BD: down projections of every (slot, position)
+// Work items are (union slot, 16-row tile of the output) pairs, slot-major, split evenly over
+// the workgroups: a workgroup streams whole tiles of one or two slots' down matrices and
+// fetches only those slots' activation vectors. Each tile's results, times the position's
+// gate, go out as LL words (fpart[slot][position][row]); then the workgroup that owns output
+// rows [r0, r1) adds, per position, its slots' partials in a fixed order (shared experts,
+// then the position's experts in rank order) and the residual.
 template <class SH>
 __device__ __forceinline__ bool bstage_down(Ctx& cx, const KArgs& a, const Step& st, VLds& L, int nq, bool last_layer,
                                             uint16_t* out_hidden) {
   const KCfg& c = a.c;
   const DLayer Ly = *gp(st.Ly);
-  constexpr int INTER = SH::INTER, AST = vb_astr(INTER);
-  int r0, r1;
-  hrows(SH::H, cx.nwg, cx.w, &r0, &r1);
-  const int nr = r1 - r0;
+  constexpr int H = SH::H, INTER = SH::INTER, AST = vb_astr(INTER), NT = H / 16;
+  static_assert(H % 16 == 0, "whole tiles");
+  const int w = cx.w, nwg = cx.nwg;
   const int ns = c.nshared, nslot = L.misc[0];
   uint64_t* mbase = wsp<uint64_t>(a, a.off.vm);
-  const size_t mwords = (size_t)VB * INTER / 2;
-  constexpr int VMAX = (VACT_BYTES - 16384) / (AST * 2);   // vectors per pass (the rest holds the results)
-  float* res = reinterpret_cast<float*>(L.A + VMAX * AST);   // [slots in pass][nq][nr]
-  for (int i = tid_opaque(); i < nq * 32; i += BLOCK) L.facc[i] = 0.f;
-  int s0 = 0;
-  while (s0 < nslot) {
-    // the slots of this pass: as many as fit (vectors and results)
-    int s1 = s0, nv = 0;
-    while (s1 < nslot && s1 - s0 < MAX_MSEGS) {
-      const int cnt = __popc(L.umask[s1] & ((1 << nq) - 1));
-      if (nv + cnt > VMAX || (s1 - s0 + 1) * nq * nr * 4 > 16384) break;
-      nv += cnt;
-      s1++;
-    }
-    __syncthreads();
+  uint64_t* fpart = wsp<uint64_t>(a, a.off.vfp);
+  const int mwords = VB * INTER / 2;
+  // this workgroup's (slot, tile) items [i0, i1): one segment per slot run
+  const int tot = nslot * NT;
+  const int i0 = split_at(tot, nwg, w), i1 = split_at(tot, nwg, w + 1);
+  __syncthreads();
+  int nseg = 0, nv = 0, nrows = 0;
+  for (int s = i0 / NT; s < nslot && s * NT < i1; s++) {
+    const int t0 = max(i0, s * NT) - s * NT, t1 = min(i1, (s + 1) * NT) - s * NT;
+    if (t0 >= t1) continue;
+    const int e = L.uexp[s], msk = L.umask[s];
     if (tid_opaque() == 0) {
-      int v = 0;
-      for (int s = s0; s < s1; s++) {
-        const int e = L.uexp[s];
-        const int msk = L.umask[s];
-        MSeg& S = L.segs[s - s0];
-        S.w = Ly.w_down.w + (size_t)e * Ly.dn_slot_bytes + (size_t)r0 * INTER;
-        S.s = Ly.w_down.s + (size_t)e * Ly.dn_slot_scales;
-        S.n = nr;
-        S.srow = r0;
-        S.a_off = 0;
-        S.o_off = (s - s0) * nq * nr;
-        for (int p = 0; p < VB; p++) S.vrow[p] = (int8_t)((p < nq && ((msk >> p) & 1)) ? v++ : -1);
+      MSeg& S = L.segs[nseg];
+      S.w = Ly.w_down.w + (size_t)e * Ly.dn_slot_bytes + (size_t)t0 * 16 * INTER;
+      S.s = Ly.w_down.s + (size_t)e * Ly.dn_slot_scales;
+      S.n = (t1 - t0) * 16;
+      S.srow = t0 * 16;
+      S.a_off = 0;
+      S.o_off = nrows * VB;
+      int v = nv;
+      for (int p = 0; p < VB; p++) {
+        const bool on = p < nq && ((msk >> p) & 1);
+        S.vrow[p] = (int8_t)(on ? v : -1);
+        if (on) L.vsrc[v++] = s * mwords + p * (INTER / 2);
       }
+      L.pcs[nseg] = s;   // the slot of segment nseg
     }
-    __syncthreads();
-    auto pre = [&]() -> bool {
-      // fetch this pass's (slot, position) vectors, bf16 pairs, into their A rows
-      for (int s = s0; s < s1; s++) {
-        const MSeg& S = L.segs[s - s0];
-        for (int p = 0; p < nq; p++) {
-          const int v = S.vrow[p];
-          if (v < 0) continue;
-          if (!ll_fetch<per_for(INTER / 2)>(cx, reinterpret_cast<uint32_t*>(L.A + v * AST),
-                                            mbase + (size_t)s * mwords + (size_t)p * (INTER / 2), INTER / 2, st.k1, W_M))
-            return false;
-        }
-      }
-      if (s0 == 0) stamp(a, cx, st, TR_M_READY);
-      return true;
+    nv += __popc(msk & ((1 << nq) - 1));
+    nrows += (t1 - t0) * 16;
+    nseg++;
+  }
+  __syncthreads();
+  // at most two slots per workgroup (items per workgroup <= tiles per slot): <= 2 * VB vectors
+  float* res = reinterpret_cast<float*>(L.A + 2 * VB * AST);   // segment g's results at (o_off + p * rows_g + r)
+  auto pre = [&]() -> bool {
+    struct IdxV {
+      const int* vs;
+      __device__ __forceinline__ int operator()(int i) const { return vs[i / (INTER / 2)] + i % (INTER / 2); }
     };
-    if (!mfma_list<INTER, 8>(L.segs, nr > 0 ? s1 - s0 : 0, L.A, res, nr, L.part, nq, pre)) return false;
-    // f_p += gate(slot, p) * down(slot, p), slots in union order
-    for (int i = tid_opaque(); i < nq * nr; i += BLOCK) {
-      const int p = i / nr, r = i % nr;
-      float f = L.facc[p * 32 + r];
-      for (int s = s0; s < s1; s++) {
-        if (!((L.umask[s] >> p) & 1)) continue;
+    if (!ll_fetch<per_for(32 * INTER / 2)>(cx, reinterpret_cast<uint32_t*>(L.A), mbase, nv * (INTER / 2), st.k1, W_M,
+                                           IdxV{L.vsrc}, StRows<INTER / 2>{AST / 2}))
+      return false;
+    stamp(a, cx, st, TR_M_READY);
+    return true;
+  };
+  // (ostr 0: segment g's results form a [VB][rows_g] block at o_off = rows before g * VB)
+  if (!mfma_list<INTER, 8>(L.segs, nseg, L.A, res, 0, L.part, nq, pre)) return false;
+  stamp(a, cx, st, TR_DOWN_GEMV);
+  // gated partials out: fpart[slot][p][row]
+  {
+    int ob = 0;
+    for (int g = 0; g < nseg; g++) {
+      const MSeg& S = L.segs[g];
+      const int sl = L.pcs[g], e = L.uexp[sl];
+      for (int i = tid_opaque(); i < nq * S.n; i += BLOCK) {
+        const int p = i / S.n, r = i % S.n;
+        if (S.vrow[p] < 0) continue;
         float gte = 1.f;
-        if (s >= ns) {
-          const int e = L.uexp[s];
+        if (sl >= ns) {
           gte = 0.f;
           for (int k = 0; k < c.topk; k++)
             if (L.isel[p * 8 + k] == e) gte = L.fgate[p * 8 + k];
         }
-        f = fmaf(gte, res[(s - s0) * nq * nr + p * nr + r], f);
+        ll_put_f32(fpart + ((size_t)sl * VB + p) * H + S.srow + r, gte * res[ob * VB + p * S.n + r], st.k1);
       }
-      L.facc[p * 32 + r] = f;
-      if (s1 == nslot) st_f32(wsp<float>(a, a.off.vf) + (size_t)p * SH::H + r0 + r, f);   // debug copy of f
+      ob += S.n;
     }
-    s0 = s1;
+  }
+  // the union slot of each position's experts (rank order), for the reduction
+  if (tid_opaque() < nq * c.topk) {
+    const int p = tid_opaque() / c.topk, k = tid_opaque() % c.topk, e = L.isel[p * 8 + k];
+    int sl = ns;
+    while (L.uexp[sl] != e) sl++;
+    L.vslot[p * 8 + k] = sl;
   }
   __syncthreads();
-  stamp(a, cx, st, TR_DOWN_GEMV);
-  // x'_p = h2_p + f_p, bf16 pairs (next layer's input); the last layer's last position also to out_hidden
+  // reduction of the rows [r0, r1) this workgroup owns: per position ns + topk partials
+  int r0, r1;
+  hrows(H, nwg, w, &r0, &r1);
+  const int nr = r1 - r0, per = (ns + c.topk) * nr;
+  struct IdxF {
+    const int* vslot;
+    int per, nr, ns, topk, r0;
+    __device__ __forceinline__ int operator()(int i) const {
+      const int p = i / per, k = (i % per) / nr, r = i % nr;
+      const int sl = k < ns ? k : vslot[p * 8 + (k - ns)];
+      return (sl * VB + p) * SH::H + r0 + r;
+    }
+  };
+  float* fr = reinterpret_cast<float*>(L.A);   // [nq][ns + topk][nr]
+  if (!ll_fetch<per_for(VB * 10 * 32)>(cx, reinterpret_cast<uint32_t*>(fr), fpart, nq * per, st.k1, W_M,
+                                       IdxF{L.vslot, per, nr, ns, c.topk, r0}))
+    return false;
   for (int i = tid_opaque(); i < nq * (nr / 2); i += BLOCK) {
     const int p = i / (nr / 2), r = 2 * (i % (nr / 2));
-    const uint32_t lo = f32_to_bf16(L.h2res[p * 32 + r] + L.facc[p * 32 + r]);
-    const uint32_t hi = f32_to_bf16(L.h2res[p * 32 + r + 1] + L.facc[p * 32 + r + 1]);
-    ll_put(vbuf(a, a.off.vx, SH::H / 2, p) + (r0 + r) / 2, lo | (hi << 16), st.k1);
+    float f0 = 0.f, f1 = 0.f;
+    for (int k = 0; k < ns + c.topk; k++) {
+      f0 += fr[p * per + k * nr + r];
+      f1 += fr[p * per + k * nr + r + 1];
+    }
+    st_f32(wsp<float>(a, a.off.vf) + (size_t)p * H + r0 + r, f0);   // debug copy of f
+    st_f32(wsp<float>(a, a.off.vf) + (size_t)p * H + r0 + r + 1, f1);
+    const uint32_t lo = f32_to_bf16(L.h2res[p * 32 + r] + f0);
+    const uint32_t hi = f32_to_bf16(L.h2res[p * 32 + r + 1] + f1);
+    ll_put(vbuf(a, a.off.vx, H / 2, p) + (r0 + r) / 2, lo | (hi << 16), st.k1);
     if (last_layer && out_hidden && p == nq - 1) gp(reinterpret_cast<uint32_t*>(out_hidden))[(r0 + r) / 2] = lo | (hi << 16);
   }
   stamp(a, cx, st, TR_DOWN_DONE);

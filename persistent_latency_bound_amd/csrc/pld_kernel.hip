@@ -96,7 +96,7 @@ struct WsOff {
   size_t status, x, q, kv, part, o, h2, logits, m, cqr, ckvr, qr, qlat, olat, amax, ixr, qi, ilist, isel, ll_end, sel,
       gates, spec, a_dbg, b_dbg, f_dbg, ikh, ikl, ilo, itok, kx, rope, layers, total;
   // batched verify (per-position copies of the LL buffers; vsel is a plain debug area)
-  size_t vx, vcqr, vckv, vqn, vqr, vqlat, vpart, volat, vo, vh2, vlog, vm, vamax, vsel, vf;
+  size_t vx, vcqr, vckv, vqn, vqr, vqlat, vpart, volat, vo, vh2, vlog, vm, vfp, vamax, vsel, vf;
 };
 
 struct KArgs {
@@ -1735,7 +1735,8 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
   if (c->max_query < 0 || c->max_query > VB) return PLD_E_INVALID;
   if (c->max_query >= 2) {
     // batched verify: the per-workgroup row counts must fit its LDS result areas
-    if (!pick_verify(c) || c->n_shared > 4 || c->top_k > 8 || c->n_experts > 256) return PLD_E_UNSUPPORTED;
+    if (!pick_verify(c) || c->n_shared > 4 || c->top_k > 8 || c->n_experts > 256 || k->cpw != 128)
+      return PLD_E_UNSUPPORTED;
     auto per = [nwg](long long n) { return (n + nwg - 1) / nwg; };
     const long long hr = 2 * per(c->hidden / 2), xr = per(c->q_lora + c->kv_lora + c->rope_dim);
     const long long qr = 2 * per((long long)c->n_heads * (c->nope_dim + c->rope_dim) / 2);
@@ -1805,9 +1806,11 @@ WsOff layout(const KCfg& k, int n_layers) {
     o.vh2 = p; p += al(VBW * k.H * W);
     o.vlog = p; p += al(VBW * 4 * k.E * W);
     o.vm = p; p += al((size_t)(k.vq * k.topk + k.nshared) * VBW * (k.inter / 2) * W);
+    o.vfp = p; p += al((size_t)(k.vq * k.topk + k.nshared) * VBW * k.H * W);   // gated down partials
     o.vamax = p; p += al(VBW * 3 * k.nwg * W);
   } else {
-    o.vx = o.vcqr = o.vckv = o.vqn = o.vqr = o.vqlat = o.vpart = o.volat = o.vo = o.vh2 = o.vlog = o.vm = o.vamax = 0;
+    o.vx = o.vcqr = o.vckv = o.vqn = o.vqr = o.vqlat = o.vpart = o.volat = o.vo = o.vh2 = o.vlog = o.vm = o.vfp =
+        o.vamax = 0;
   }
   o.ll_end = p;
   if (k.vq >= 2) {
