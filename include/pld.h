@@ -102,7 +102,10 @@ typedef struct pld_config {
   int32_t max_query;         /* 0 or 1: no batched verify; 2..8: the workspace also holds the buffers of
                                 decode_verify_batched for up to max_query positions (FP8 MLA MoE layers
                                 with an LM head only, else PLD_E_UNSUPPORTED) */
-  int32_t reserved[1];
+  int32_t max_batch;         /* 0 or 1: one sequence per handle; 2..8: decode_batch runs up to max_batch
+                                sequences, and every layer's latent cache holds max_batch sequences of
+                                max_seq rows back to back (sequence b's row r at row b * max_seq + r;
+                                the single-sequence calls use sequence 0). Same shapes as max_query. */
 } pld_config;
 
 typedef struct pld_matrix {
@@ -293,6 +296,37 @@ pld_status decode_layers_persistent(pld_handle* h, const pld_persistent_args* a,
  * Errors: PLD_E_UNSUPPORTED (handle without batched verify), PLD_E_INVALID, PLD_E_CAPACITY,
  * PLD_E_STATE, PLD_E_HIP. */
 pld_status decode_verify_batched(pld_handle* h, const pld_persistent_args* a, void* stream);
+
+/* Arguments of decode_batch. */
+typedef struct pld_batch_args {
+  int32_t n_seq;            /* sequences decoded together, 2 .. cfg->max_batch */
+  int32_t n_tokens;         /* tokens to decode per sequence (>= 1) */
+  int32_t start_pos[8];     /* cache position of each sequence's first token (sequence b's rows
+                               0 .. start_pos[b]-1 hold its history) */
+  int32_t in_token[8];      /* each sequence's input token, in [0, vocab) */
+  float* out_logits;        /* fp32 [n_tokens][n_seq][vocab], or NULL */
+  int32_t* out_tokens;      /* int32 [n_tokens][n_seq] chosen tokens (device, 4-byte aligned) */
+  void* out_hidden;         /* bf16 [hidden]: the last sequence's final hidden state after the last
+                               token, 16-byte aligned */
+  double temperature;       /* 0 greedy, > 0 sampled (the rule of decode_layers_persistent, keyed
+                               by each sequence's own cache position) */
+  uint64_t sample_seed;
+} pld_batch_args;
+
+/* Batched decoding of n_seq independent sequences in one launch: every step, the sequences'
+ * current tokens go through every layer TOGETHER (each weight read once per step for all
+ * of them, on the matrix cores as in decode_verify_batched; the union of the experts the
+ * sequences route to is read once), each sequence attends to its own cache and appends its
+ * own row, and the head chooses each sequence's next token, which feeds the next step. The
+ * vLLM Kimi K3 backend article serves batches of 1 to 64 requests on one node ("A narrow
+ * deployment lane") and switches its matmuls to split-K at larger batches ("Four changes
+ * drive the gains"); this is the small-batch end of that range on one GPU.
+ * Each sequence's tokens equal what decode_layers_persistent gives for it alone, up to the
+ * rounding of the bf16 activation operands (not bit-identical).
+ * Handles created with cfg->max_batch >= 2 (FP8 MLA MoE stacks with an LM head).
+ * Errors: PLD_E_UNSUPPORTED (handle without batch decode), PLD_E_INVALID, PLD_E_CAPACITY
+ * (start_pos[b] + n_tokens > max_seq), PLD_E_STATE, PLD_E_HIP. */
+pld_status decode_batch(pld_handle* h, const pld_batch_args* a, void* stream);
 
 /* Arguments of decode_speculative. */
 typedef struct pld_spec_args {

@@ -25,7 +25,7 @@ EXPORTS = (
     "pld_workspace_bytes", "decode_layer_init", "decode_step", "decode_layers_persistent", "decode_poll_status",
     "decode_reset", "decode_layer_destroy", "pld_status_string", "pld_debug_buffer", "pld_launch_shape",
     "pld_set_watchdog_us", "pld_set_trace", "pld_set_test_hooks", "decode_layer_init_static", "decode_speculative",
-    "pld_workspace_bytes_for_cus", "decode_verify_batched",
+    "pld_workspace_bytes_for_cus", "decode_verify_batched", "decode_batch",
 )
 PLD_HOOK_DROP_WG0, PLD_HOOK_DELAY = 1, 2
 
@@ -38,7 +38,7 @@ class PldConfig(ctypes.Structure):
         "nope_dim", "v_dim", "index_heads", "index_dim", "index_topk", "ffn_kind", "inter", "n_experts", "top_k",
         "n_shared", "router_kind", "max_seq")] + [("eps", f64), ("rope_base", f64), ("vocab", i32),
                                                    ("kda_rank", i32), ("conv_width", i32), ("expert_wfmt", i32),
-                                                   ("max_query", i32), ("reserved", i32 * 1)]
+                                                   ("max_query", i32), ("max_batch", i32)]
 
 
 class PldMatrix(ctypes.Structure):
@@ -75,6 +75,12 @@ class PldPersistentArgs(ctypes.Structure):
 class PldSpecArgs(ctypes.Structure):
     _fields_ = [("start_pos", i32), ("in_token", i32), ("n_tokens", i32), ("n_draft", i32), ("temperature", f64),
                 ("sample_seed", ctypes.c_uint64), ("out_tokens", vp), ("out_stats", vp)]
+
+
+class PldBatchArgs(ctypes.Structure):
+    _fields_ = [("n_seq", i32), ("n_tokens", i32), ("start_pos", i32 * 8), ("in_token", i32 * 8),
+                ("out_logits", vp), ("out_tokens", vp), ("out_hidden", vp), ("temperature", f64),
+                ("sample_seed", ctypes.c_uint64)]
 
 
 # intermediates kept as LL words (32-bit payload, 32-bit epoch) in the workspace
@@ -117,8 +123,9 @@ def lib():
         L.pld_set_trace.argtypes = [vp, vp, ctypes.c_size_t]
         L.pld_set_test_hooks.argtypes = [vp, i32, ctypes.c_uint32]
         L.decode_verify_batched.argtypes = [vp, vp, vp]
+        L.decode_batch.argtypes = [vp, vp, vp]
         for f in ("decode_layer_init", "decode_layer_init_static", "decode_speculative", "decode_step",
-                  "decode_layers_persistent", "decode_verify_batched", "decode_poll_status",
+                  "decode_layers_persistent", "decode_verify_batched", "decode_batch", "decode_poll_status",
                   "decode_reset", "pld_debug_buffer", "pld_launch_shape", "pld_set_watchdog_us", "pld_set_trace",
                   "pld_set_test_hooks"):
             getattr(L, f).restype = i32
@@ -138,7 +145,7 @@ def check(code: int, what: str):
         raise PldError(code, what)
 
 
-def config_from_shape(s, vocab: int = 0, max_query: int = 0) -> PldConfig:
+def config_from_shape(s, vocab: int = 0, max_query: int = 0, max_batch: int = 0) -> PldConfig:
     """pld_config of a synth.configs.LayerShape."""
     c = PldConfig()
     c.attn_kind = {"gqa": PLD_ATTN_GQA, "mla": PLD_ATTN_MLA, "kda": PLD_ATTN_KDA}[s.attn]
@@ -153,6 +160,7 @@ def config_from_shape(s, vocab: int = 0, max_query: int = 0) -> PldConfig:
     c.kda_rank, c.conv_width = s.kda_rank, s.conv_width
     c.expert_wfmt = PLD_WFMT_LUT3 if s.expert_fmt == "lut3" else 0
     c.max_query = int(max_query)
+    c.max_batch = int(max_batch)
     return c
 
 
@@ -195,14 +203,16 @@ class Decoder:
     """One decode handle over a stack of layers (weights and caches are caller-owned torch tensors)."""
 
     def __init__(self, shape, layers: Sequence[dict], caches: Sequence[dict], head: Optional[dict] = None,
-                 vocab: int = 0, static: bool = False, max_query: int = 0):
+                 vocab: int = 0, static: bool = False, max_query: int = 0, max_batch: int = 0):
         """static=True: decode_layer_init_static (the library's own device array, no workspace
         allocation; one such handle per GPU, re-initialised by every such call).
-        max_query >= 2: the workspace also holds the batched verify's buffers (verify_batched)."""
+        max_query >= 2: the workspace also holds the batched verify's buffers (verify_batched).
+        max_batch >= 2: batch decode of up to max_batch sequences (batch); every layer's latent
+        cache then holds max_batch sequences of max_seq rows back to back."""
         import torch
 
         self.shape = shape
-        self.cfg = config_from_shape(shape, vocab, max_query)
+        self.cfg = config_from_shape(shape, vocab, max_query, max_batch)
         n = len(layers)
         self._keep = (list(layers), list(caches), head)   # keep the tensors alive
         self.static = static
@@ -264,6 +274,17 @@ class Decoder:
         a.draft_tokens, a.out_logits = _ptr(draft_tokens), _ptr(out_logits)
         a.out_tokens, a.out_accepted = _ptr(out_tokens), _ptr(out_accepted)
         check(lib().decode_verify_batched(self.handle, ctypes.byref(a), self._stream()), "decode_verify_batched")
+
+    def batch(self, start_pos, in_token, n_tokens: int, out_tokens, out_hidden, out_logits=None,
+              temperature: float = 0.0, sample_seed: int = 0):
+        """decode_batch: len(start_pos) sequences, n_tokens steps."""
+        a = PldBatchArgs()
+        a.n_seq, a.n_tokens = len(start_pos), int(n_tokens)
+        for b, (p, t) in enumerate(zip(start_pos, in_token)):
+            a.start_pos[b], a.in_token[b] = int(p), int(t)
+        a.out_logits, a.out_tokens, a.out_hidden = _ptr(out_logits), _ptr(out_tokens), _ptr(out_hidden)
+        a.temperature, a.sample_seed = float(temperature), int(sample_seed) & 0xFFFFFFFFFFFFFFFF
+        check(lib().decode_batch(self.handle, ctypes.byref(a), self._stream()), "decode_batch")
 
     def speculative(self, draft: "Decoder", start_pos: int, in_token: int, n_tokens: int, n_draft: int, out_tokens,
                     temperature: float = 0.0, sample_seed: int = 0):

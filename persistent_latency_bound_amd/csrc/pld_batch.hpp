@@ -251,7 +251,8 @@ struct VLds {
   int* uexp;       // [VB * 8 + 4]  union of the selected experts (ascending), then shared
   int* umask;      // [VB * 8 + 4]  positions that use each union slot (bit p)
   int* misc;       // [16]          union size; misc + 8: the head stage's argmax slot
-  int* tok;        // [2 * VB]      input tokens of the positions, then the chosen tokens
+  int* tok;        // [2 * VB]      input tokens of the rows, then the chosen tokens
+  int* rpos;       // [VB]          cache position of each row in the current step
   int* pcs;        // [3 * MAX_MSEGS / 2] routed pieces of this workgroup: union slot, j0, j1
   int* vsrc;       // [32]          down pass: LL word offset of each fetched (slot, position) vector
   MSeg* segs;      // [MAX_MSEGS]
@@ -262,7 +263,7 @@ struct VLds {
 constexpr int VOUT_FLOATS = VB * 64;
 __host__ __device__ inline size_t vlds_bytes() {
   return (size_t)VACT_BYTES + 4 * (VOUT_FLOATS + 8 * 16 * VB + 3 * VB * 32) + 8 * 16 + 8 * NWAVES * VB + 4 * (VB * 8) * 2 +
-         4 * 2 * (VB * 8 + 4) + 4 * 16 + 4 * 2 * VB + 4 * 3 * (MAX_MSEGS / 2) + 4 * 32 + sizeof(MSeg) * MAX_MSEGS +
+         4 * 2 * (VB * 8 + 4) + 4 * 16 + 4 * 2 * VB + 4 * VB + 4 * 3 * (MAX_MSEGS / 2) + 4 * 32 + sizeof(MSeg) * MAX_MSEGS +
          8 * TR_SLOTS + 8 * 16;
 }
 __device__ __forceinline__ VLds vcarve(float* base) {
@@ -282,6 +283,7 @@ __device__ __forceinline__ VLds vcarve(float* base) {
   L.umask = reinterpret_cast<int*>(p); p += 4 * (VB * 8 + 4);
   L.misc = reinterpret_cast<int*>(p); p += 4 * 16;
   L.tok = reinterpret_cast<int*>(p); p += 4 * 2 * VB;
+  L.rpos = reinterpret_cast<int*>(p); p += 4 * VB;
   L.pcs = reinterpret_cast<int*>(p); p += 4 * 3 * (MAX_MSEGS / 2);
   L.vsrc = reinterpret_cast<int*>(p); p += 4 * 32;
   L.segs = reinterpret_cast<MSeg*>(p); p += sizeof(MSeg) * MAX_MSEGS;
@@ -524,7 +526,7 @@ __device__ __forceinline__ bool bstage_q(Ctx& cx, const KArgs& a, const Step& st
       ll_put_f32(qn + 1, v1, st.k1);
     } else {
       const int d = k - SH::ND;
-      const PLD_GLOBAL float* rope = gp(wsp<float>(a, a.off.rope)) + (size_t)(st.pos + p) * SH::RD;
+      const PLD_GLOBAL float* rope = gp(wsp<float>(a, a.off.rope)) + (size_t)L.rpos[p] * SH::RD;
       const float cs = rope[d], sn = rope[d + 1];
       ll_put(vbuf(a, a.off.vqr, SH::NH * SH::RD / 2, p) + (h * SH::RD + d) / 2,
              f32_to_bf16(v0 * cs - v1 * sn) | (f32_to_bf16(v0 * sn + v1 * cs) << 16), st.k1);
@@ -648,8 +650,12 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
   const int nch = c.cpg;
   const int hg = cx.w / nch, ch = cx.w % nch;
   const int hbase = hg * HPW;
-  const int pos = st.pos;                     // first position; history rows [0, pos)
-  const int t0 = split_at(pos, nch, ch), t1 = split_at(pos, nch, ch + 1), n = t1 - t0;
+  // verify (a.bmode == 0): the rows are consecutive positions of one sequence and share its
+  // history [0, rpos[0]); batch decode: row p is sequence p, with its own cache (rows
+  // p * max_seq ..) and history [0, rpos[p]); set per pass below
+  const bool shared = a.bmode == 0;
+  const size_t seq_rows = (size_t)c.max_seq;
+  int t0 = 0, n = 0;
   const uint16_t* lat = Ly.lat;
   // LDS
   uint16_t* Qs = V.A;                                        // [VPP][16][CSTR]
@@ -673,7 +679,8 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
       ss = block_sum(ss, V.red);
       const double r = 1.0 / sqrt(ss / (double)KL + c.eps);
       const PLD_GLOBAL float* gk = gp(Ly.kv_norm);
-      const PLD_GLOBAL float* rope = gp(wsp<float>(a, a.off.rope)) + (size_t)(pos + p) * RD;
+      const PLD_GLOBAL float* rope = gp(wsp<float>(a, a.off.rope)) + (size_t)V.rpos[p] * RD;
+      const size_t crow = (shared ? 0 : (size_t)p * seq_rows) + (size_t)V.rpos[p];   // cache row of the new row
       for (int i = tid; i < LAT / 2; i += BLOCK) {
         const int k = 2 * i;
         float v0, v1;
@@ -688,7 +695,7 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
         }
         const uint32_t pair = f32_to_bf16(v0) | (f32_to_bf16(v1) << 16);
         reinterpret_cast<uint32_t*>(newr + p * LAT)[i] = pair;
-        if (hg == 0) st_u32(reinterpret_cast<uint32_t*>(Ly.lat + (size_t)(pos + p) * LAT) + i, pair);
+        if (hg == 0) st_u32(reinterpret_cast<uint32_t*>(Ly.lat + crow * LAT) + i, pair);
       }
       __syncthreads();
     }
@@ -696,7 +703,7 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
   }
   const float scale = 1.0f / sqrtf((float)(SH::ND + SH::RD));
   const int ln = lane & 15, lq = lane >> 4;
-  const int nsb = (n + TB - 1) / TB;
+  int nsb = 0;
   constexpr int DEPTH = 3;
   uint4 cb[DEPTH][NLD];
   auto issue = [&](int set, int sb) {
@@ -725,8 +732,15 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
   constexpr int PSTR = KL / 2 + 2;
   uint64_t* pll = wsp<uint64_t>(a, a.off.vpart);
   const size_t pwords = (size_t)SH::NH * nch * PSTR;   // words of one position's partials
-  for (int p0 = 0; p0 < nq; p0 += VPP) {
-    const int np = min(VPP, nq - p0);
+  for (int p0 = 0; p0 < nq; p0 += shared ? VPP : 1) {
+    const int np = shared ? min(VPP, nq - p0) : 1;
+    {
+      const int hist = V.rpos[shared ? 0 : p0];   // history rows of the pass's rows
+      t0 = split_at(hist, nch, ch);
+      n = split_at(hist, nch, ch + 1) - t0;
+      nsb = (n + TB - 1) / TB;
+      lat = Ly.lat + (shared ? 0 : (size_t)p0 * seq_rows * LAT);
+    }
 #pragma unroll
     for (int d = 0; d < DEPTH; d++) issue(d, d);
     // queries of the pass: q_lat [HPW][KL] and q_rope [HPW][RD] (bf16 pairs) -> rows of Qs
@@ -855,7 +869,7 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
       for (int j = 0; j < np; j++) {
         const int p = p0 + j;
         const uint16_t* Q = Qs + j * 16 * CSTR;
-        for (int r = 0; r <= p; r++) {
+        for (int r = shared ? 0 : p; r <= p; r++) {
           constexpr int DPJ = LAT / 32;
           const int hr = tid >> 5, jj = tid & 31;
           float sv = 0.f;
@@ -872,8 +886,9 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
         if (j < np) {
           const int p = p0 + j;
           float* snh = sn + (j * 16 + hown) * (VB + 2);
+          const int rlo = shared ? 0 : p;   // the new rows this row sees: rlo .. p
           float mb = -INFINITY;
-          for (int r = 0; r <= p; r++) mb = fmaxf(mb, snh[r]);
+          for (int r = rlo; r <= p; r++) mb = fmaxf(mb, snh[r]);
           const float mnew = fmaxf(m_run[j], mb);
           const float al = m_run[j] == -INFINITY ? 0.f : __expf(m_run[j] - mnew);
           float ls = 0.f;
@@ -882,7 +897,7 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
           float pr[VB];
 #pragma unroll
           for (int r = 0; r < VB; r++) {
-            pr[r] = r <= p ? __expf(snh[r] - mnew) : 0.f;
+            pr[r] = (r >= rlo && r <= p) ? __expf(snh[r] - mnew) : 0.f;
             ls += pr[r];
           }
           __syncthreads();
@@ -902,7 +917,7 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
               const int hh = 4 * lq + q;
               const float* sh = sn + (j * 16 + hh) * (VB + 2);
               float o = O[j][t][q] * sh[VB];
-              for (int r = 0; r <= p; r++) o = fmaf(sh[r], bf16_to_f32(newr[r * LAT + col]), o);
+              for (int r = rlo; r <= p; r++) o = fmaf(sh[r], bf16_to_f32(newr[r * LAT + col]), o);
               O[j][t][q] = o;
             }
           }
@@ -1430,10 +1445,15 @@ __device__ __forceinline__ bool bstage_down(Ctx& cx, const KArgs& a, const Step&
   return true;
 }
 
-// ------------------------------------------------------------------ the batched verify kernel
-// a.n_tokens = nq positions from a.pos0: position 0 takes a.in_token, position p > 0 the
-// caller's draft p - 1 (clamped into the vocabulary). Per-position logits and tokens,
-// and the count of leading drafts equal to the token chosen at the position before.
+// ------------------------------------------------------------------ the batched kernel
+// Verify (a.bmode == 0): a.nrows positions from a.pos0 of one sequence; position 0 takes
+// a.in_token, position p > 0 the caller's draft p - 1 (clamped into the vocabulary).
+// Per-position logits and tokens, and the count of leading drafts equal to the token
+// chosen at the position before.
+// Batch decode (a.bmode == 1): a.nrows sequences, row p at cache position a.bpos[p] of its
+// own cache, fed a.btok[p]; a.n_tokens steps, each choosing every row's next token, which
+// is the row's input at the next step.
+static_assert(VB == 8, "KArgs holds 8 rows of batch positions and tokens");
 template <class SH>
 __global__ void __launch_bounds__(BLOCK, 1) k_verify_mla(KArgs a) {
   extern __shared__ float lds_raw[];
@@ -1445,67 +1465,83 @@ __global__ void __launch_bounds__(BLOCK, 1) k_verify_mla(KArgs a) {
   cx.wacc = nullptr;
   const DLayer* layers = wsp<DLayer>(a, a.off.layers);
   if ((a.hooks & PLD_HOOK_DROP_WG0) && cx.w == 0) return;
-  const int nq = a.n_tokens;
+  const int nq = a.nrows;
+  const int nsteps = a.bmode ? a.n_tokens : 1;
   VLds L = vcarve(lds_raw);
   if (tid_opaque() < TR_SLOTS) L.tr[tid_opaque()] = 0;
   exp_f64_init(L.dk);
   __syncthreads();
-  if (tid_opaque() < nq)
-    L.tok[tid_opaque()] = tid_opaque() == 0 ? a.in_token : min(max(gp(a.drafts)[tid_opaque() - 1], 0), a.c.vocab - 1);
-  __syncthreads();
-  for (int li = 0; li < a.n_layers; li++) {
-    cx.layer = a.layer0 + li;
-    cx.token = 0;
-    Step st;
-    st.Ly = layers + a.layer0 + li;
-    st.idx = li;
-    st.k1 = a.step0 + (uint32_t)li + 1u;
-    st.first = li == 0;
-    st.in_hidden = nullptr;
-    st.pos = a.pos0;
-    st.emb_row = nullptr;
-    st.tr = L.tr;
-    KArgs as = a;
-    asm volatile("" : "+s"(as.ws));
-    Ctx cs = cx;
-    asm volatile("" : "+s"(cs.w), "+s"(cs.nwg), "+s"(as.c.cpw), "+s"(as.c.cpg));
-    cs.wacc = (a.trace && st.idx < a.trace_steps) ? L.tr + TR_WAIT : nullptr;
-    stamp(as, cs, st, TR_START);
-    if (!bstage_x<SH>(cs, as, st, L, nq, li)) return;
-    if (!bstage_q<SH>(cs, as, st, L, nq)) return;
-    if (!bstage_absorb<SH>(cs, as, st, L, nq)) return;
-    if (!bstage_attn<SH>(cs, as, st, L, nq)) return;
-    if (!bstage_merge<SH>(cs, as, st, L, nq)) return;
-    if (!bstage_uv<SH>(cs, as, st, L, nq)) return;
-    if (!bstage_wo<SH>(cs, as, st, L, nq)) return;
-    if (!bstage_ffn<SH>(cs, as, st, L, nq)) return;
-    if (!bstage_down<SH>(cs, as, st, L, nq, li == a.n_layers - 1, as.out_hidden)) return;
-    trace_flush(as, cs, st);
+  if (tid_opaque() < nq) {
+    const int p = tid_opaque();
+    if (a.bmode) {
+      L.tok[p] = a.btok[p];
+      L.rpos[p] = a.bpos[p];
+    } else {
+      L.tok[p] = p == 0 ? a.in_token : min(max(gp(a.drafts)[p - 1], 0), a.c.vocab - 1);
+      L.rpos[p] = a.pos0 + p;
+    }
   }
-  // LM head and token choice of every position (the single-position head stage, on each
-  // position's final hidden state; its candidate words in a buffer of the position's own)
+  __syncthreads();
   Lds HL = head_lds(L);
-  const uint32_t kl = a.step0 + (uint32_t)a.n_layers;
-  for (int p = 0; p < nq; p++) {
-    KArgs ah = a;
-    ah.off.x = a.off.vx + (size_t)p * (SH::H / 2) * 8;
-    ah.off.amax = a.off.vamax + (size_t)p * 3 * cx.nwg * 8;
-    Step st;
-    st.Ly = layers + a.layer0 + a.n_layers - 1;
-    st.idx = a.n_layers;
-    st.k1 = kl;
-    st.first = false;
-    st.in_hidden = nullptr;
-    st.pos = a.pos0 + p;
-    st.emb_row = nullptr;
-    st.tr = L.tr;
-    cx.token = p;
-    int tk = 0;
-    if (!stage_head<SH>(cx, ah, st, HL, p, &tk)) return;
-    if (tid_opaque() == 0) L.tok[VB + p] = tk;
+  for (int t = 0; t < nsteps; t++) {
+    for (int li = 0; li < a.n_layers; li++) {
+      cx.layer = a.layer0 + li;
+      cx.token = t;
+      Step st;
+      st.Ly = layers + a.layer0 + li;
+      st.idx = t * a.n_layers + li;
+      st.k1 = a.step0 + (uint32_t)st.idx + 1u;
+      st.first = false;
+      st.in_hidden = nullptr;
+      st.pos = a.pos0;
+      st.emb_row = nullptr;
+      st.tr = L.tr;
+      KArgs as = a;
+      asm volatile("" : "+s"(as.ws));
+      Ctx cs = cx;
+      asm volatile("" : "+s"(cs.w), "+s"(cs.nwg), "+s"(as.c.cpw), "+s"(as.c.cpg));
+      cs.wacc = (a.trace && st.idx < a.trace_steps) ? L.tr + TR_WAIT : nullptr;
+      stamp(as, cs, st, TR_START);
+      if (!bstage_x<SH>(cs, as, st, L, nq, li)) return;
+      if (!bstage_q<SH>(cs, as, st, L, nq)) return;
+      if (!bstage_absorb<SH>(cs, as, st, L, nq)) return;
+      if (!bstage_attn<SH>(cs, as, st, L, nq)) return;
+      if (!bstage_merge<SH>(cs, as, st, L, nq)) return;
+      if (!bstage_uv<SH>(cs, as, st, L, nq)) return;
+      if (!bstage_wo<SH>(cs, as, st, L, nq)) return;
+      if (!bstage_ffn<SH>(cs, as, st, L, nq)) return;
+      if (!bstage_down<SH>(cs, as, st, L, nq, t == nsteps - 1 && li == a.n_layers - 1, as.out_hidden)) return;
+      trace_flush(as, cs, st);
+    }
+    // LM head and token choice of every row (the single-position head stage, on each row's
+    // final hidden state; its candidate words in a buffer of the row's own)
+    const uint32_t kl = a.step0 + (uint32_t)((t + 1) * a.n_layers);
+    for (int p = 0; p < nq; p++) {
+      KArgs ah = a;
+      ah.off.x = a.off.vx + (size_t)p * (SH::H / 2) * 8;
+      ah.off.amax = a.off.vamax + (size_t)p * 3 * cx.nwg * 8;
+      Step st;
+      st.Ly = layers + a.layer0 + a.n_layers - 1;
+      st.idx = (t + 1) * a.n_layers;
+      st.k1 = kl;
+      st.first = false;
+      st.in_hidden = nullptr;
+      st.pos = L.rpos[p];
+      st.emb_row = nullptr;
+      st.tr = L.tr;
+      cx.token = t;
+      int tk = 0;
+      if (!stage_head<SH>(cx, ah, st, HL, t * nq + p, &tk)) return;
+      if (tid_opaque() == 0) L.tok[VB + p] = tk;
+    }
+    __syncthreads();
+    if (a.bmode && tid_opaque() < nq) {   // each row's chosen token is its next input
+      L.tok[tid_opaque()] = L.tok[VB + tid_opaque()];
+      L.rpos[tid_opaque()] += 1;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (cx.w == 0 && tid_opaque() == 0 && a.out_accepted) {
+  if (!a.bmode && cx.w == 0 && tid_opaque() == 0 && a.out_accepted) {
     int acc = 0;
     for (int p = 1; p < nq; p++) {
       if (gp(a.drafts)[p - 1] != L.tok[VB + p - 1]) break;

@@ -71,7 +71,8 @@ struct KCfg {
   int nwg;
   int cpw;     // MLA: q_lat / o_lat outputs per workgroup (absorb, merge)
   int rdim;    // width of the RoPE table rows (head_dim for GQA, rope_dim for MLA)
-  int vq;      // batched verify: max positions (0: not set up)
+  int vq;      // batched kernel: max rows (positions of a verify or sequences of a batch; 0: not set up)
+  int vb;      // batch decode: sequences per layer cache (0: one sequence)
 };
 
 struct DLayer {
@@ -124,6 +125,9 @@ struct KArgs {
   uint32_t hook_seed;
   double temperature;      // LM head: 0 = greedy argmax, > 0 = Gumbel-max sample of softmax(logits / T)
   uint64_t sample_seed;
+  // batched kernel: rows per step; batch decode (bmode 1): per-sequence positions and input tokens
+  int bmode, nrows;
+  int32_t bpos[8], btok[8];
 };
 
 // ------------------------------------------------------------------ device context
@@ -1732,8 +1736,8 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
         k->stage_words < 3 * nwg)
       return PLD_E_UNSUPPORTED;
   }
-  if (c->max_query < 0 || c->max_query > VB) return PLD_E_INVALID;
-  if (c->max_query >= 2) {
+  if (c->max_query < 0 || c->max_query > VB || c->max_batch < 0 || c->max_batch > VB) return PLD_E_INVALID;
+  if (c->max_query >= 2 || c->max_batch >= 2) {
     // batched verify: the per-workgroup row counts must fit its LDS result areas
     if (!pick_verify(c) || c->n_shared > 4 || c->top_k > 8 || c->n_experts > 256 || k->cpw != 128)
       return PLD_E_UNSUPPORTED;
@@ -1741,11 +1745,13 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
     const long long hr = 2 * per(c->hidden / 2), xr = per(c->q_lora + c->kv_lora + c->rope_dim);
     const long long qr = 2 * per((long long)c->n_heads * (c->nope_dim + c->rope_dim) / 2);
     const long long ur = per((long long)c->n_heads * c->v_dim), sr = 2 * per(c->inter / 2);
-    const long long gr = 2 * (2 * per((long long)c->max_query * c->top_k * c->inter / 2));
+    const int rows = std::max(c->max_query, c->max_batch);
+    const long long gr = 2 * (2 * per((long long)rows * c->top_k * c->inter / 2));
     if (hr > 32 || xr > 64 || qr > 64 || ur > 64 || 2 * c->n_shared * sr > 64 ||
         98432 + (long long)VB * gr * 4 > VACT_BYTES || ((long long)c->n_heads * c->v_dim) % nwg)
       return PLD_E_UNSUPPORTED;
-    k->vq = c->max_query;
+    k->vq = rows;
+    k->vb = c->max_batch >= 2 ? c->max_batch : 0;
   }
   return PLD_OK;
 }
@@ -2235,9 +2241,9 @@ pld_status decode_layers_persistent(pld_handle* h, const pld_persistent_args* a,
 pld_status decode_verify_batched(pld_handle* h, const pld_persistent_args* a, void* stream) {
   if (!h || !a) return PLD_E_INVALID;
   if (h->bad) return PLD_E_STATE;
-  if (!h->vfn) return PLD_E_UNSUPPORTED;
+  if (!h->vfn || h->cfg.max_query < 2) return PLD_E_UNSUPPORTED;
   const int nq = a->n_query;
-  if (nq < 2 || nq > h->kc.vq || a->n_tokens != 1) return PLD_E_INVALID;
+  if (nq < 2 || nq > h->cfg.max_query || a->n_tokens != 1) return PLD_E_INVALID;
   if (a->in_token < 0 || a->in_token >= h->cfg.vocab || !a->draft_tokens || ((uintptr_t)a->draft_tokens & 3u))
     return PLD_E_INVALID;
   if (!a->out_hidden || !aligned16(a->out_hidden)) return PLD_E_INVALID;
@@ -2249,7 +2255,9 @@ pld_status decode_verify_batched(pld_handle* h, const pld_persistent_args* a, vo
   k.ws = h->ws;
   k.off = h->off;
   k.n_layers = h->n_layers;
-  k.n_tokens = nq;
+  k.n_tokens = 1;
+  k.nrows = nq;
+  k.bmode = 0;
   k.pos0 = a->start_pos;
   k.layer0 = 0;
   k.step0 = h->steps;
@@ -2278,6 +2286,63 @@ pld_status decode_verify_batched(pld_handle* h, const pld_persistent_args* a, vo
   if (e != hipSuccess) return PLD_E_HIP;
   h->hooks &= ~PLD_HOOK_DROP_WG0;
   h->steps += (uint32_t)h->n_layers;
+  h->last_stream = s;
+  return PLD_OK;
+}
+
+pld_status decode_batch(pld_handle* h, const pld_batch_args* a, void* stream) {
+  if (!h || !a) return PLD_E_INVALID;
+  if (h->bad) return PLD_E_STATE;
+  if (!h->vfn || h->kc.vb < 2) return PLD_E_UNSUPPORTED;
+  const int nb = a->n_seq;
+  if (nb < 2 || nb > h->kc.vb || a->n_tokens < 1) return PLD_E_INVALID;
+  if (!a->out_tokens || ((uintptr_t)a->out_tokens & 3u) || !a->out_hidden || !aligned16(a->out_hidden))
+    return PLD_E_INVALID;
+  if (!(a->temperature >= 0.0) || !std::isfinite(a->temperature)) return PLD_E_INVALID;
+  for (int b = 0; b < nb; b++) {
+    if (a->in_token[b] < 0 || a->in_token[b] >= h->cfg.vocab) return PLD_E_INVALID;
+    if (a->start_pos[b] < 0 || (long long)a->start_pos[b] + a->n_tokens > h->cfg.max_seq) return PLD_E_CAPACITY;
+  }
+  if ((long long)a->n_tokens * h->n_layers > (1ll << 24)) return PLD_E_INVALID;
+  KArgs k;
+  memset(&k, 0, sizeof(k));
+  k.c = h->kc;
+  k.ws = h->ws;
+  k.off = h->off;
+  k.n_layers = h->n_layers;
+  k.n_tokens = a->n_tokens;
+  k.nrows = nb;
+  k.bmode = 1;
+  for (int b = 0; b < nb; b++) {
+    k.bpos[b] = a->start_pos[b];
+    k.btok[b] = a->in_token[b];
+  }
+  k.pos0 = a->start_pos[0];
+  k.layer0 = 0;
+  k.step0 = h->steps;
+  k.out_hidden = (uint16_t*)a->out_hidden;
+  k.budget = h->budget;
+  k.trace = h->trace;
+  k.trace_steps = h->trace_steps;
+  k.head_on = 1;
+  k.in_token = a->in_token[0];
+  k.out_logits = a->out_logits;
+  k.out_tokens = a->out_tokens;
+  k.embed = h->embed;
+  k.fnorm = h->fnorm;
+  k.head = h->head;
+  k.hooks = h->hooks;
+  k.hook_seed = h->hook_seed;
+  k.temperature = a->temperature;
+  k.sample_seed = a->sample_seed;
+  void* args[] = {&k};
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = h->coop ? hipLaunchCooperativeKernel((const void*)h->vfn, dim3(h->kc.nwg), dim3(BLOCK), args,
+                                                            (unsigned)h->vlds_bytes, s)
+                               : hipLaunchKernel((const void*)h->vfn, dim3(h->kc.nwg), dim3(BLOCK), args, h->vlds_bytes, s);
+  if (e != hipSuccess) return PLD_E_HIP;
+  h->hooks &= ~PLD_HOOK_DROP_WG0;
+  h->steps += (uint32_t)(h->n_layers * a->n_tokens);
   h->last_stream = s;
   return PLD_OK;
 }

@@ -62,6 +62,9 @@ int main(void) {
   P(pld_persistent_args, temperature) P(pld_persistent_args, sample_seed)
   printf("pld_spec_args %zu\n", sizeof(pld_spec_args));
   P(pld_spec_args, temperature) P(pld_spec_args, out_tokens) P(pld_spec_args, out_stats)
+  printf("pld_batch_args %zu\n", sizeof(pld_batch_args));
+  P(pld_batch_args, in_token) P(pld_batch_args, out_logits) P(pld_batch_args, temperature)
+  P(pld_batch_args, sample_seed) P(pld_config, max_batch)
   return 0;
 }
 '''
@@ -84,11 +87,13 @@ def test_ctypes_struct_layout_matches_c():
     assert lay["pld_device_status"] == ctypes.sizeof(pld.PldDeviceStatus)
     assert lay["pld_persistent_args"] == ctypes.sizeof(pld.PldPersistentArgs)
     assert lay["pld_spec_args"] == ctypes.sizeof(pld.PldSpecArgs)
+    assert lay["pld_batch_args"] == ctypes.sizeof(pld.PldBatchArgs)
     for key, off in lay.items():
         if "." in key:
             T, f = key.split(".")
             cls = {"pld_config": pld.PldConfig, "pld_layer_weights": pld.PldLayerWeights,
-                   "pld_persistent_args": pld.PldPersistentArgs, "pld_spec_args": pld.PldSpecArgs}[T]
+                   "pld_persistent_args": pld.PldPersistentArgs, "pld_spec_args": pld.PldSpecArgs,
+                   "pld_batch_args": pld.PldBatchArgs}[T]
             assert getattr(cls, f).offset == off, key
 
 
@@ -106,6 +111,7 @@ def test_null_arguments_are_rejected_before_any_device_work():
     assert L.decode_step(None, 0, None, 0, None, None) == pld.PLD_E_INVALID
     assert L.decode_layers_persistent(None, None, None) == pld.PLD_E_INVALID
     assert L.decode_verify_batched(None, None, None) == pld.PLD_E_INVALID
+    assert L.decode_batch(None, None, None) == pld.PLD_E_INVALID
     assert L.decode_reset(None) == pld.PLD_E_INVALID
     L.decode_layer_destroy(None)
 

@@ -1,0 +1,202 @@
+"""GPU parity of batched decoding (decode_batch) against the CPU oracle.
+
+B independent sequences share the weights and decode together: every step, their tokens go
+through each layer at once (the dense projections, the shared expert and the union of the
+routed experts on the matrix cores with bf16 activation operands, each weight read once
+per step), each sequence attends to its own cache (sequence b's rows at b * max_seq + r in
+the layer's latent cache) and appends its own row, and the head chooses each sequence's
+next token, which is its input at the next step.
+
+Reference: the oracle run per sequence, step by step, teacher-forced with the GPU's chosen
+tokens (its own cache, its own start position).
+
+Bars: TOL (2e-2) on logits; BAR_VB (1e-2, derived in test_gpu_verify_batched.py from the
+bf16 activation operands) on each sequence's attention branch y = h2 - x and FFN output f
+of its last step (one-layer stack, so the layer input is the exact embedding row); the
+expert choice of every sequence identical; the chosen tokens identical unless the oracle's
+two logits are within TOL.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from gpu_common import TOL, rel_err, say  # noqa: E402
+from oracle import layer as OL  # noqa: E402
+from oracle import model as OM  # noqa: E402
+from oracle import numerics as nx  # noqa: E402
+from synth import configs, gen  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+BAR_VB = 1e-2
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _model(n_layers, cache_len):
+    L = configs.scaled(configs.C5_LAYER, cache_len=cache_len, max_seq=cache_len + 64)
+    return configs.ModelShape(layer=L, n_layers=n_layers, vocab=32768, n_tokens=4)
+
+
+def _head(m):
+    from synth import device as sdev
+    return {"embed": sdev.embedding(m), "final_norm": sdev.final_norm(m), "head": sdev.head(m)}
+
+
+def _batch_decoder(m, nb):
+    """Weights of seed 0; layer caches holding sequences b = 0..nb-1 (cache seed b) back to back."""
+    import persistent_latency_bound_amd as pld
+    from synth import device as sdev
+    Ws = [sdev.layer_weights(m.layer, 0, l) for l in range(m.n_layers)]
+    Cs = [{"latent": torch.cat([sdev.kv_cache(m.layer, b, l)["latent"] for b in range(nb)], dim=0).contiguous()}
+          for l in range(m.n_layers)]
+    return pld.Decoder(m.layer, Ws, Cs, head=_head(m), vocab=m.vocab, max_batch=nb)
+
+
+def _single_decoder(m, seq):
+    import persistent_latency_bound_amd as pld
+    from synth import device as sdev
+    Ws = [sdev.layer_weights(m.layer, 0, l) for l in range(m.n_layers)]
+    Cs = [sdev.kv_cache(m.layer, seq, l) for l in range(m.n_layers)]
+    return pld.Decoder(m.layer, Ws, Cs, head=_head(m), vocab=m.vocab)
+
+
+def _status_ok(dec, tag):
+    st = dec.status()
+    assert st.code == 0, f"{tag}: device status {st.code} wait {st.stage} layer {st.layer} token {st.token} wg {st.wg}"
+
+
+def _run_batch(dec, m, starts, toks, n, temperature=0.0, seed=0):
+    nb = len(starts)
+    lg = torch.zeros((n, nb, m.vocab), dtype=torch.float32, device="cuda")
+    tk = torch.full((n, nb), -1, dtype=torch.int32, device="cuda")
+    out = torch.zeros(m.layer.hidden, dtype=torch.int16, device="cuda")
+    dec.batch(starts, toks, n, tk, out, out_logits=lg, temperature=temperature, sample_seed=seed)
+    torch.cuda.synchronize()
+    _status_ok(dec, "batch decode")
+    return lg.cpu().numpy(), tk.cpu().numpy()
+
+
+@pytest.mark.parametrize("temperature", [0.0, 0.8])
+def test_batch_decode_one_layer_vs_oracle(temperature):
+    """Four sequences with their own histories and start positions (300, 290, 257, 300), three
+    tokens each: per sequence and step, logits and tokens against the oracle; the last step's
+    y, f and expert choice of every sequence."""
+    _need_gpu()
+    m = _model(n_layers=1, cache_len=300)
+    starts, toks0 = [300, 290, 257, 300], [11, 20000, 777, 31337]
+    nb, n = len(starts), 3
+    say(f"case: 1-layer FP8 MLA stack + head, batch of {nb} sequences at {starts}, {n} tokens, T {temperature}")
+    dec = _batch_decoder(m, nb)
+    lg, tk = _run_batch(dec, m, starts, toks0, n, temperature, 5)
+    say(f"GPU tokens per step: {tk.tolist()}")
+    H = m.layer.hidden
+    vh2 = dec.debug("vh2").cpu().numpy().astype(np.float64).reshape(8, H)
+    vf = dec.debug("vf").cpu().numpy().astype(np.float64).reshape(8, H)
+    vsel = dec.debug("vsel").cpu().numpy()
+    W = gen.LayerWeights(m.layer, 0, 0)
+    head_m, fg = gen.head_matrix(m), gen.final_norm(m)
+    fails = []
+    for b in range(nb):
+        cache = gen.padded_cache(m.layer, b, 0)
+        tin = toks0[b]
+        for t in range(n):
+            p = starts[b] + t
+            x = gen.embedding_rows(m, [tin])[0]
+            rec = OL.decode_layer(m.layer, W, cache, x, p)
+            OL.append_to_cache(m.layer, cache, rec, p)
+            lo = OM.head_logits(m.layer, head_m, fg, rec["out_bits"])
+            otok = OM.sample_token(lo, temperature, 5, p)
+            e = rel_err(lg[t, b], lo)
+            msg = f"sequence {b} step {t} (pos {p}): logits rel err {e:.2e}; oracle token {otok}, GPU {tk[t, b]}"
+            if t == n - 1:
+                xin = nx.bf16_to_f64(np.asarray(x).view(np.uint16))
+                e_y, e_f = rel_err(vh2[b] - xin, rec["y"]), rel_err(vf[b], rec["f"])
+                sel = [int(v) for v in vsel[b * 8: b * 8 + m.layer.top_k]]
+                msg += f"; y {e_y:.2e}, f {e_f:.2e}, experts {'same' if sel == list(rec['router_sel']) else 'DIFFER'}"
+                if e_y >= BAR_VB or e_f >= BAR_VB or sel != list(rec["router_sel"]):
+                    fails.append(msg)
+            say(msg)
+            if e >= TOL:
+                fails.append(msg)
+            if otok != tk[t, b] and abs(lo[otok] - lo[tk[t, b]]) > TOL * np.max(np.abs(lo)):
+                fails.append(msg + " (decisive token difference)")
+            tin = int(tk[t, b])
+    assert not fails, fails
+
+
+def test_batch_decode_matches_single_sequence_decodes():
+    """Eight sequences over two layers (ragged 517-row histories, start positions spread
+    400..517), three tokens: each sequence's tokens equal those of decoding it alone with
+    decode_layers_persistent, logits within TOL. Where a sequence's tokens or logits differ
+    beyond that, the oracle must show a router near-tie at that step (see the verify test)."""
+    _need_gpu()
+    m = _model(n_layers=2, cache_len=517)
+    nb, n = 8, 3
+    starts = [517, 500, 480, 450, 517, 401, 512, 460]
+    toks0 = [(b * 4099 + 17) % m.vocab for b in range(nb)]
+    say(f"case: 2-layer stack, batch of {nb} sequences at {starts}, {n} tokens")
+    dec = _batch_decoder(m, nb)
+    lgB, tkB = _run_batch(dec, m, starts, toks0, n)
+    say(f"batch tokens per step: {tkB.tolist()}")
+    bad = []
+    for b in range(nb):
+        d1 = _single_decoder(m, b)
+        lg1 = torch.zeros((n, m.vocab), dtype=torch.float32, device="cuda")
+        tk1 = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+        out = torch.zeros(m.layer.hidden, dtype=torch.int16, device="cuda")
+        d1.persistent(start_pos=starts[b], in_token=toks0[b], n_tokens=n, out_hidden=out, out_logits=lg1,
+                      out_tokens=tk1)
+        torch.cuda.synchronize()
+        _status_ok(d1, f"single sequence {b}")
+        lg1, tk1 = lg1.cpu().numpy(), [int(v) for v in tk1.cpu().numpy()]
+        errs = [rel_err(lgB[t, b], lg1[t]) for t in range(n)]
+        say(f"sequence {b}: alone {tk1}, batched {tkB[:, b].tolist()}, logits rel err {[f'{e:.1e}' for e in errs]}")
+        if tk1 != tkB[:, b].tolist() or max(errs) >= TOL:
+            bad.append(b)
+        del d1
+    for b in bad:
+        # explained only by a router near-tie of the oracle at the first differing step
+        W = [gen.LayerWeights(m.layer, 0, l) for l in range(m.n_layers)]
+        caches = [gen.padded_cache(m.layer, b, l) for l in range(m.n_layers)]
+        tin = toks0[b]
+        gaps = []
+        for t in range(n):
+            x = gen.embedding_rows(m, [tin])[0]
+            for l in range(m.n_layers):
+                rec = OL.decode_layer(m.layer, W[l], caches[l], x, starts[b] + t)
+                OL.append_to_cache(m.layer, caches[l], rec, starts[b] + t)
+                r = np.asarray(rec["router_logits"], np.float64)
+                key = np.sort(1.0 / (1.0 + np.exp(-r)) + np.asarray(W[l].router_bias(), np.float64))[::-1]
+                gaps.append(float(key[m.layer.top_k - 1] - key[m.layer.top_k]))
+                x = rec["out_bits"]
+            tin = int(tkB[t, b])
+        say(f"sequence {b}: oracle router key gaps {['%.1e' % g for g in gaps]}")
+        assert min(gaps) < 1e-3, f"sequence {b}: batched and single decodes differ without a router near-tie"
+
+
+def test_batch_decode_argument_errors():
+    _need_gpu()
+    import persistent_latency_bound_amd as pld
+    m = _model(n_layers=1, cache_len=64)
+    say("case: batch decode argument errors")
+    out = torch.zeros(m.layer.hidden, dtype=torch.int16, device="cuda")
+    tk = torch.zeros((2, 4), dtype=torch.int32, device="cuda")
+    d0 = _single_decoder(m, 0)
+    with pytest.raises(pld.PldError) as e:
+        d0.batch([10, 10], [1, 2], 2, tk, out)
+    assert e.value.code == pld.PLD_E_UNSUPPORTED
+    dec = _batch_decoder(m, 4)
+    with pytest.raises(pld.PldError) as e:
+        dec.batch([10] * 5, [1] * 5, 2, tk, out)   # 5 sequences > max_batch
+    assert e.value.code == pld.PLD_E_INVALID
+    with pytest.raises(pld.PldError) as e:
+        dec.batch([10, 127], [1, 2], 2, tk, out)   # 127 + 2 > max_seq
+    assert e.value.code == pld.PLD_E_CAPACITY
+    with pytest.raises(pld.PldError) as e:
+        dec.batch([10, 10], [1, m.vocab], 2, tk, out)   # token out of range
+    assert e.value.code == pld.PLD_E_INVALID
