@@ -57,6 +57,9 @@ WORKLOADS = {   # name -> (synth.configs attribute, traffic file stem, dtype of 
     # the same stack, one 6-position speculative verify per launch (seeded drafts)
     "mla_stack24_fp8_verify6": ("C5", "traffic_mla_stack24_fp8_verify6",
                                 "fp8-e4m3 weights, fp32 accumulate, fp64 head"),
+    "mla_stack24_fp8_batch8": ("C5", "traffic_mla_stack24_fp8_batch8",
+                               "fp8-e4m3 weights widened to bf16, bf16 activations, fp32 accumulate "
+                               "(matrix cores); fp64 router and head"),
     "mla_stack24_fp8_verify6_batched": ("C5", "traffic_mla_stack24_fp8_verify6_batched",
                                         "fp8-e4m3 weights widened to bf16, bf16 activations, fp32 accumulate "
                                         "(matrix cores); fp64 router and head"),
@@ -380,6 +383,85 @@ def run_verify(args):
     print(json.dumps(line), flush=True)
 
 
+def run_batch(args):
+    """Batched decoding: B sequences of the 24-layer stack, each with its own 8192-row history,
+    decode args.tokens tokens together per launch. One line for B = 8 with the curve over
+    B = 1 (the single-sequence stack launch), 2, 4, 8 beside it."""
+    import torch
+    import persistent_latency_bound_amd as pld
+    from oracle import accounting
+    from synth import configs, device as sdev, gen
+    m = configs.C5
+    L = m.layer
+    pos0 = L.cache_len
+    n_tok = args.tokens
+    Ws = [sdev.layer_weights(L, 0, l) for l in range(m.n_layers)]
+    head = {"embed": sdev.embedding(m), "final_norm": sdev.final_norm(m), "head": sdev.head(m)}
+    curve = {}
+    for nb in (1, 2, 4, 8):
+        if nb == 1:
+            Cs = [sdev.kv_cache(L, 0, l) for l in range(m.n_layers)]
+            dec = pld.Decoder(L, Ws, Cs, head=head, vocab=m.vocab)
+        else:
+            Cs = [{"latent": torch.cat([sdev.kv_cache(L, b, l)["latent"] for b in range(nb)], dim=0).contiguous()}
+                  for l in range(m.n_layers)]
+            dec = pld.Decoder(L, Ws, Cs, head=head, vocab=m.vocab, max_batch=nb)
+        out = torch.zeros(L.hidden, dtype=torch.int16, device="cuda")
+        tk = torch.zeros((n_tok, nb), dtype=torch.int32, device="cuda")
+        toks0 = [(gen.first_token(m) + 977 * b) % m.vocab for b in range(nb)]
+
+        def one():
+            if nb == 1:
+                dec.persistent(start_pos=pos0, in_token=toks0[0], n_tokens=n_tok, out_hidden=out, out_tokens=tk)
+            else:
+                dec.batch([pos0] * nb, toks0, n_tok, tk, out)
+
+        for _ in range(args.warmup):
+            one()
+        torch.cuda.synchronize()
+        if dec.status().code != 0:
+            raise SystemExit(f"device status after warm-up (batch {nb})")
+        stream = torch.cuda.current_stream()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            one()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if dec.status().code != 0:
+            raise SystemExit(f"device status after the timed launches (batch {nb})")
+        ms = e0.elapsed_time(e1) / args.steps
+        us_step = ms * 1e3 / n_tok
+        union = accounting.expected_union_experts(L.n_experts, L.top_k, nb)
+        curve[nb] = {"us_per_step": round(us_step, 1), "us_per_layer_step": round(us_step / m.n_layers, 2),
+                     "tokens_per_s_user": round(1e6 / us_step, 1), "tokens_per_s_total": round(nb * 1e6 / us_step, 1),
+                     "expected_union_routed_experts": round(union, 2)}
+        del dec, Cs
+        torch.cuda.empty_cache()
+    c8 = curve[8]
+    # algorithmic bytes of one 8-sequence step per layer: shared weights once, the expected union
+    # of the routed experts, each sequence's own history and appended row
+    layer_b = accounting.verify_layer_bytes(L, pos0, 8) + 7 * accounting.layer_kv_bytes(L, pos0)["kv_read"]
+    step_b = layer_b * m.n_layers + accounting.head_bytes(L.hidden, m.vocab)
+    achieved = step_b / (c8["us_per_step"] * 1e-6) / 1e9
+    line = {
+        "metric": "batch-1 decode us/layer (achieved HBM TB/s vs peak, implied tokens/s/user)",
+        "value": c8["us_per_layer_step"], "unit": "us/layer (one step of 8 sequences)", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(c8["us_per_step"] * n_tok / 1e3, 3),
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": WORKLOADS[args.workload][2],
+        "data": "synthetic",
+        "config": {"workload": args.workload, "layers": m.n_layers, "sequences": 8, "tokens_per_launch": n_tok,
+                   "start_pos": pos0, "vocab": m.vocab, "hidden": L.hidden},
+        "tokens_per_s_total": c8["tokens_per_s_total"], "tokens_per_s_user": c8["tokens_per_s_user"],
+        "curve_by_batch": curve,
+        "achieved_TBps": round(achieved / 1e3, 3), "frac_of_peak": round(achieved / PEAK_HBM_GBPS, 4),
+        "algorithmic_bytes_per_step": int(step_b),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": None},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -391,7 +473,8 @@ def main():
                     help="also time decode_step (one layer per launch, launch cost included)")
     ap.add_argument("--trace", default=None, help="write a per-stage device-trace summary (JSON) to this path")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=sorted(WORKLOADS))
-    ap.add_argument("--tokens", type=int, default=256, help="tokens per launch (multi-layer workload)")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="tokens per launch (multi-layer workloads; default 256 for the stack, 32 for the batch)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="first run one plain 1 GiB device-to-device copy (reference for HBM byte counters)")
     ap.add_argument("--no-single-launch", action="store_true",
@@ -400,9 +483,12 @@ def main():
     args = ap.parse_args()
     stack = args.workload.startswith("mla_stack24")
     if args.steps is None:
-        args.steps = 20 if args.workload == "mla_stack24_fp8_greedy256" else 10 if stack else 100
+        args.steps = (20 if args.workload == "mla_stack24_fp8_greedy256" else 3 if args.workload.endswith("batch8")
+                      else 10 if stack else 100)
     if args.warmup is None:
         args.warmup = 3 if stack else 10
+    if args.tokens is None:
+        args.tokens = 32 if args.workload.endswith("batch8") else 256
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU path is not built.",
               file=sys.stderr)
@@ -419,6 +505,8 @@ def main():
         return run_stack(args)
     if args.workload.startswith("mla_stack24_fp8_verify6"):
         return run_verify(args)
+    if args.workload == "mla_stack24_fp8_batch8":
+        return run_batch(args)
 
     import torch
     import persistent_latency_bound_amd as pld

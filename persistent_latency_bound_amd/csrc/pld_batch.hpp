@@ -358,76 +358,95 @@ __device__ __forceinline__ void block_sum_rows(double (&v)[VB], double* redv) {
   __syncthreads();
 }
 
-// RMSNorm of the nq rows of an N-vector, in fp64 like the single-position path (fp64 sum of
-// squares and product, one rounding to bf16), into the bf16 A rows A + p * astr. The input
-// element (p, i) is ld(p, i) (LDS; it may be the A row itself: each element is read and then
-// written by the same thread); gamma in registers; the fp32 result also to f32 + p * fstr
-// when f32 is set. A thread's elements of one row are read together before any write.
-template <int N, typename Ld>
-__device__ __forceinline__ void rms_rows(uint16_t* A, int astr, Ld&& ld, const RegVec<N>& gam, double eps,
-                                         double* redv, int nq, float* f32 = nullptr, int fstr = 0) {
-  constexpr int KK = RegVec<N>::K;
-  double ss[VB];
+// Element pairs (2j, 2j + 1), j = tid + k * BLOCK, of a length-N fp32 vector in registers
+// (norm gains, loaded before a stage's weight stream is issued).
+template <int N>
+struct RegPairs {
+  static constexpr int K = (N / 2 + BLOCK - 1) / BLOCK;
+  float2 v[K];
+  __device__ __forceinline__ void load(const float* p) {
+    const PLD_GLOBAL float2* g = gp(reinterpret_cast<const float2*>(p));
 #pragma unroll
-  for (int p = 0; p < VB; p++) {
-    ss[p] = 0.0;
-    if (p < nq) {
-      float xv[KK];
-#pragma unroll
-      for (int k = 0; k < KK; k++) {
-        const int i = tid_opaque() + k * BLOCK;
-        xv[k] = (N % BLOCK == 0 || i < N) ? ld(p, i) : 0.f;
+    for (int k = 0; k < K; k++) {
+      const int j = tid_opaque() + k * BLOCK;
+      v[k] = make_float2(0.f, 0.f);
+      if ((N / 2) % BLOCK == 0 || j < N / 2) {
+        const float2 t = g[j];
+        v[k] = t;
       }
-#pragma unroll
-      for (int k = 0; k < KK; k++) ss[p] += (double)xv[k] * (double)xv[k];
     }
   }
-  block_sum_rows(ss, redv);
+};
+
+// Sums over the workgroup of VB per-thread fp32 values at once (one pair of barriers).
+__device__ __forceinline__ void block_sum_rows_f32(float (&v)[VB], double* redv) {
+  float* red = reinterpret_cast<float*>(redv);   // [NWAVES][VB]
+  const int lane = tid_opaque() & 63, wave = tid_opaque() >> 6;
+#pragma unroll
+  for (int p = 0; p < VB; p++) v[p] = wave_sum_dpp(v[p]);
+  __syncthreads();
+  if (lane == 0) {
+#pragma unroll
+    for (int p = 0; p < VB; p++) red[wave * VB + p] = v[p];
+  }
+  __syncthreads();
 #pragma unroll
   for (int p = 0; p < VB; p++) {
-    if (p < nq) {
-      const double r = 1.0 / sqrt(ss[p] / (double)N + eps);
-      float xv[KK];
+    float t = 0.f;
 #pragma unroll
-      for (int k = 0; k < KK; k++) {
-        const int i = tid_opaque() + k * BLOCK;
-        xv[k] = (N % BLOCK == 0 || i < N) ? ld(p, i) : 0.f;
-      }
-#pragma unroll
-      for (int k = 0; k < KK; k++) {
-        const int i = tid_opaque() + k * BLOCK;
-        if (N % BLOCK == 0 || i < N) {
-          const double y = ((double)xv[k] * r) * (double)gam.v[k];
-          A[p * astr + i] = (uint16_t)f64_to_bf16(y);
-          if (f32) f32[p * fstr + i] = (float)y;
-        }
-      }
-    }
+    for (int w = 0; w < NWAVES; w++) t += red[w * VB + p];
+    v[p] = t;
   }
   __syncthreads();
 }
 
-// RMSNorm of a vector held in LDS as fp32 (src) into a bf16 A row (dst), in fp64 like the
-// single-position path (fp64 sum of squares, fp64 product, one rounding to bf16). All
-// threads call; ends with a barrier.
-template <int N>
-__device__ __forceinline__ void rms_to_bf16(uint16_t* dst, const float* src, const PLD_GLOBAL float* gam, double eps,
-                                            double* red) {
-  constexpr int KK = (N + BLOCK - 1) / BLOCK;
-  float xv[KK];
-  double ss = 0.0;
+// RMSNorm of the nq rows of an N-vector into the bf16 A rows A + p * astr (the matrix cores
+// take bf16 operands, whose rounding, 2^-9, is far above that of fp32 statistics, so the
+// statistics and the product are fp32 here): y = (x * r) * gamma, r = 1/sqrt(sum(x^2)/N + eps).
+// The input pair (p, j) is ld(p, j) (elements 2j, 2j + 1; LDS; it may be the A row itself:
+// each pair is read and then written by the same thread); the fp32 y also to f32 + p * fstr
+// when f32 is set. A thread's pairs of one row are read together before any write.
+template <int N, typename Ld>
+__device__ __forceinline__ void rms_rows(uint16_t* A, int astr, Ld&& ld, const RegPairs<N>& gam, double eps,
+                                         double* redv, int nq, float* f32 = nullptr, int fstr = 0) {
+  constexpr int KK = RegPairs<N>::K;
+  static_assert(N % 2 == 0, "pairs");
+  float ss[VB];
 #pragma unroll
-  for (int k = 0; k < KK; k++) {
-    const int i = tid_opaque() + k * BLOCK;
-    xv[k] = (N % BLOCK == 0 || i < N) ? src[i] : 0.f;
-    ss += (double)xv[k] * (double)xv[k];
+  for (int p = 0; p < VB; p++) {
+    ss[p] = 0.f;
+    if (p < nq) {
+      float2 xv[KK];
+#pragma unroll
+      for (int k = 0; k < KK; k++) {
+        const int j = tid_opaque() + k * BLOCK;
+        xv[k] = ((N / 2) % BLOCK == 0 || j < N / 2) ? ld(p, j) : make_float2(0.f, 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < KK; k++) ss[p] = fmaf(xv[k].x, xv[k].x, fmaf(xv[k].y, xv[k].y, ss[p]));
+    }
   }
-  ss = block_sum(ss, red);
-  const double r = 1.0 / sqrt(ss / (double)N + eps);
+  block_sum_rows_f32(ss, redv);
 #pragma unroll
-  for (int k = 0; k < KK; k++) {
-    const int i = tid_opaque() + k * BLOCK;
-    if (N % BLOCK == 0 || i < N) dst[i] = (uint16_t)f64_to_bf16(((double)xv[k] * r) * (double)gam[i]);
+  for (int p = 0; p < VB; p++) {
+    if (p < nq) {
+      const float r = 1.0f / sqrtf(ss[p] / (float)N + (float)eps);
+      float2 xv[KK];
+#pragma unroll
+      for (int k = 0; k < KK; k++) {
+        const int j = tid_opaque() + k * BLOCK;
+        xv[k] = ((N / 2) % BLOCK == 0 || j < N / 2) ? ld(p, j) : make_float2(0.f, 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < KK; k++) {
+        const int j = tid_opaque() + k * BLOCK;
+        if ((N / 2) % BLOCK == 0 || j < N / 2) {
+          const float y0 = (xv[k].x * r) * gam.v[k].x, y1 = (xv[k].y * r) * gam.v[k].y;
+          reinterpret_cast<uint32_t*>(A + p * astr)[j] = f32_to_bf16(y0) | (f32_to_bf16(y1) << 16);
+          if (f32) reinterpret_cast<float2*>(f32 + p * fstr)[j] = make_float2(y0, y1);
+        }
+      }
+    }
   }
   __syncthreads();
 }
@@ -441,7 +460,7 @@ __device__ __forceinline__ bool bstage_x(Ctx& cx, const KArgs& a, const Step& st
   const int r0 = split_at(R, nwg, w), r1 = split_at(R, nwg, w + 1);
   int h0, h1;
   hrows(H, nwg, w, &h0, &h1);
-  RegVec<H> gam;
+  RegPairs<H> gam;
   gam.load(Ly.attn_norm);
   {
     __syncthreads();
@@ -477,7 +496,10 @@ __device__ __forceinline__ bool bstage_x(Ctx& cx, const KArgs& a, const Step& st
         L.xres[p * 32 + (r - h0)] = bf16_to_f32(L.A[p * AST + r]);
       }
       __syncthreads();
-      rms_rows<H>(L.A, AST, [&](int p, int i) { return bf16_to_f32(L.A[p * AST + i]); }, gam, a.c.eps, L.redv, nq);
+      rms_rows<H>(L.A, AST, [&](int p, int j) {
+        const uint32_t v = reinterpret_cast<const uint32_t*>(L.A + p * AST)[j];
+        return make_float2(bf_lo(v), bf_hi(v));
+      }, gam, a.c.eps, L.redv, nq);
       stamp(a, cx, st, TR_X_NORMED);
       return true;
     };
@@ -502,7 +524,7 @@ __device__ __forceinline__ bool bstage_q(Ctx& cx, const KArgs& a, const Step& st
   constexpr int QL = SH::QL, RQ = SH::NH * SH::QH, AST = vb_astr(QL);
   const int r0 = 2 * split_at(RQ / 2, nwg, w), r1 = 2 * split_at(RQ / 2, nwg, w + 1);
   float* tmp = reinterpret_cast<float*>(L.A + VB * AST);   // [VB][QL] fp32
-  RegVec<QL> gq;
+  RegPairs<QL> gq;
   gq.load(Ly.q_norm);
   __syncthreads();
   mseg_set(L.segs, 0, Ly.w_uq.w + (size_t)r0 * QL, Ly.w_uq.s, r1 - r0, r0, 0, 0, nq);
@@ -510,7 +532,8 @@ __device__ __forceinline__ bool bstage_q(Ctx& cx, const KArgs& a, const Step& st
   auto pre = [&]() -> bool {
     if (!ll_fetch_rows<QL>(cx, reinterpret_cast<uint32_t*>(tmp), QL, vbuf(a, a.off.vcqr, QL, 0), QL, nq, st.k1, W_CQ))
       return false;
-    rms_rows<QL>(L.A, AST, [&](int p, int i) { return tmp[p * QL + i]; }, gq, a.c.eps, L.redv, nq);
+    rms_rows<QL>(L.A, AST, [&](int p, int j) { return reinterpret_cast<const float2*>(tmp + p * QL)[j]; }, gq, a.c.eps,
+                 L.redv, nq);
     stamp(a, cx, st, TR_CQ_READY);
     return true;
   };
@@ -863,6 +886,8 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
       }
     }
     __syncthreads();   // (the last block's LDS reads are done before Cs buffer 1 holds the next queries)
+    if (p0 == 0) stamp(a, cx, st, 17);
+    if (p0 == (shared ? VPP : 1)) stamp(a, cx, st, 31);
     // the new rows (last chunk): position p0 + j sees new rows 0 .. p0 + j
     if (last) {
       // scores: thread (half-wave hr = head, lane j32) over the LAT dims of new row r
@@ -927,6 +952,7 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
     }
     // publish the partials of the pass's positions
     if (p0 == 0) stamp(a, cx, st, TR_ATT_SOFTMAX);
+    if (p0 == (shared ? VPP : 1)) stamp(a, cx, st, 29);
 #pragma unroll
     for (int j = 0; j < VPP; j++) {
       if (j < np) {
@@ -1105,7 +1131,7 @@ __device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& 
   constexpr int H = SH::H, AST = vb_astr(H), INTER = SH::INTER;
   static_assert(SH::MOE && SH::FP8, "the batched FFN is the FP8 MoE one");
   float* tmp = reinterpret_cast<float*>(L.A + VB * AST);   // [2][H] fp32 normalised activations (router)
-  RegVec<H> gmf;
+  RegPairs<H> gmf;
   gmf.load(Ly.ffn_norm);
   // router row of expert w (bf16), loaded ahead of the expert weights
   constexpr int RCH = H / 8, RPT = (RCH + BLOCK - 1) / BLOCK;
@@ -1140,7 +1166,8 @@ __device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& 
       const int np = min(2, nq - p0);
       if (!ll_fetch_rows<H>(cx, reinterpret_cast<uint32_t*>(tmp), H, vbuf(a, a.off.vh2, H, p0), H, np, k1, W_H2))
         return false;
-      rms_rows<H>(L.A + p0 * AST, AST, [&](int p, int i) { return tmp[p * H + i]; }, gmf, c.eps, L.redv, np, tmp, H);
+      rms_rows<H>(L.A + p0 * AST, AST, [&](int p, int j) { return reinterpret_cast<const float2*>(tmp + p * H)[j]; },
+                  gmf, c.eps, L.redv, np, tmp, H);
       if (w < c.E) {
         double sv[VB];
 #pragma unroll
