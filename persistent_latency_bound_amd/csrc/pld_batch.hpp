@@ -64,36 +64,64 @@ __device__ __forceinline__ void mseg_set(MSeg* segs, int i, const uint8_t* w, co
 // Rows of a segment list times up to 16 activation rows on the matrix cores.
 //  * Each segment is cut into tiles of 16 rows (the last one partial: its spare columns
 //    reload the segment's last row, which costs no extra HBM bytes); tile t is the B
-//    operand of v_mfma_f32_16x16x32_bf16, lane (n, g) = (lane & 15, lane >> 4) holding
-//    row n of the tile. One 16-byte load per lane covers k in [k0 + 16 g, k0 + 16 g + 16)
-//    of its row, and the 64 lanes cover a 64-wide k-step of 16 rows; its two halves are
-//    two products (the k order inside a product is the same permutation on both operands).
+//    operand of v_mfma_f32_16x16x32_bf16, lane (n, g) = (lane & 15, lane >> 4) holding row n.
+//  * An item is a 128-wide k-step of a tile: two 16-byte loads per lane, each covering 8
+//    rows x 128 contiguous bytes (whole cache lines): the first, rows 0..7, lane (n, g)
+//    reading row n & 7 at byte 64 (n >> 3) + 16 g; the second the same for rows 8..15. A
+//    rotate by 8 lanes inside each 16-lane row (DPP) then leaves lane (n, g) with row n's
+//    bytes [16 g, 16 g + 16) and [64 + 16 g, 64 + 16 g + 16): four products of 32 k (the k
+//    order inside a product is the same permutation on both operands). Loading 16 rows x
+//    64 bytes per instruction instead (the plain layout) ran the stream ~12% slower.
 //  * Work units are (tile, k-slice): with fewer than 8 tiles, K is split into KS slices
 //    so that every wave of the workgroup streams; the slices' partial sums are added in
 //    slice order afterwards (fixed order, so results do not depend on timing).
-//  * Each wave streams its units as one pipeline with D loads in flight per lane; the
-//    first D are issued before pre() (the dependency wait), like the vector GEMV.
-//  * The fp32 block scale of the lane's row multiplies each k-step's partial product
-//    (the output column of a lane is its own B row, so the lane holds its own scale).
+//  * Each wave streams its units as one pipeline with D items (2 D loads) in flight per
+//    lane; the first D are issued before pre() (the dependency wait), like the vector GEMV.
+//  * The fp32 block scale of the lane's row multiplies each item's partial product (the
+//    output column of a lane is its own B row, so the lane holds its own scale; an item
+//    lies in one 128-wide scale block).
 // `segs` lives in LDS; `part` is LDS scratch of 8 * 16 * VB floats; ostr 0 means each
-// segment's own row count. Returns false if
-// pre() reported an abort. Ends with a workgroup barrier.
+// segment's own row count. Returns false if pre() reported an abort. Ends with a
+// workgroup barrier.
+__device__ __forceinline__ uint4 ror8_rows(uint4 v) {
+  uint4 r;
+  r.x = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.x, 0x128, 0xf, 0xf, false);   // row_ror:8
+  r.y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.y, 0x128, 0xf, 0xf, false);
+  r.z = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.z, 0x128, 0xf, 0xf, false);
+  r.w = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v.w, 0x128, 0xf, 0xf, false);
+  return r;
+}
+__device__ __forceinline__ void fp8x16_to_bf16(const uint4& v, bf16x8_t& b0, bf16x8_t& b1) {
+  const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+  uint32_t bw[8];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const bf16x2_v lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[i], 1.0f, false);
+    const bf16x2_v hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[i], 1.0f, true);
+    bw[2 * i] = __builtin_bit_cast(uint32_t, lo);
+    bw[2 * i + 1] = __builtin_bit_cast(uint32_t, hi);
+  }
+  b0 = __builtin_bit_cast(bf16x8_t, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+  b1 = __builtin_bit_cast(bf16x8_t, make_uint4(bw[4], bw[5], bw[6], bw[7]));
+}
+
 template <int K, int D, typename Pre>
 __device__ __forceinline__ bool mfma_list(const MSeg* segs, int nseg, const uint16_t* A, float* out, int ostr,
                                           float* part, int nq, Pre&& pre) {
-  static_assert(K % 64 == 0, "whole 64-wide k-steps");
+  static_assert(K % 128 == 0, "whole 128-wide items");
   constexpr int AST = vb_astr(K);
   constexpr int SBK = (K + 127) / 128;
   const int tid = tid_opaque(), lane = tid & 63, wave = tid >> 6;
   const int n = lane & 15, g = lane >> 4;
+  const bool lo8 = n < 8;
   int ntiles = 0;
   for (int s = 0; s < nseg; s++) ntiles += (segs[s].n + 15) >> 4;
   int KS = 1;
   if (ntiles > 0 && ntiles < NWAVES) {
     KS = NWAVES / ntiles;
-    while ((K / 64) % KS) KS--;
+    while ((K / 128) % KS) KS--;
   }
-  const int NS = K / 64 / KS;                   // k-steps per unit
+  const int NS = K / 128 / KS;                  // items per unit
   const int nunits = ntiles * KS;
   const int myunits = wave < nunits ? (nunits - wave + NWAVES - 1) / NWAVES : 0;
   const int nit = myunits * NS;
@@ -116,26 +144,29 @@ __device__ __forceinline__ bool mfma_list(const MSeg* segs, int nseg, const uint
     *sg = s;
     *tt = t;
   };
-  // issue cursor: unit iu, step is; per-unit row pointers
+  // issue cursor: unit iu, item is; per-unit row pointers of the lane's two loads
   int iu = 0, is = 0;
-  const uint8_t* wrow = nullptr;
+  const uint8_t* wa = nullptr;   // row (n & 7) of the tile, at this lane's byte offset
+  const uint8_t* wb = nullptr;   // row 8 + (n & 7)
   const PLD_GLOBAL float* srow = nullptr;
   int kbeg = 0;
   auto open_unit = [&](int ui) {
     int sg, tt, q;
     unit_of(ui, &sg, &tt, &q);
     const MSeg& S = segs[sg];
-    const int r = min(16 * tt + n, S.n - 1);
-    wrow = S.w + (size_t)r * K;
-    srow = gp(S.s) + (size_t)((S.srow + r) >> 7) * SBK;
+    const int ra = min(16 * tt + (n & 7), S.n - 1), rb = min(16 * tt + 8 + (n & 7), S.n - 1);
+    const int rn = min(16 * tt + n, S.n - 1);
     kbeg = q * (K / KS);
+    wa = S.w + (size_t)ra * K + kbeg + 64 * (n >> 3) + 16 * g;
+    wb = S.w + (size_t)rb * K + kbeg + 64 * (n >> 3) + 16 * g;
+    srow = gp(S.s) + (size_t)((S.srow + rn) >> 7) * SBK + (kbeg >> 7);
   };
-  uint4 buf[D];
+  uint4 bufa[D], bufb[D];
   float scb[D];
   auto issue = [&](int d) {
-    const int k0 = kbeg + 64 * is;
-    buf[d] = ld_stream16(wrow + k0 + 16 * g);
-    scb[d] = srow[k0 >> 7];
+    bufa[d] = ld_stream16(wa + 128 * is);
+    bufb[d] = ld_stream16(wb + 128 * is);
+    scb[d] = srow[is];
     if (is + 1 < NS) {
       is++;
     } else if (iu + 1 < myunits) {
@@ -158,58 +189,54 @@ __device__ __forceinline__ bool mfma_list(const MSeg* segs, int nseg, const uint
     unit_of(ui, &csg, &ctt, &cq);
     const MSeg& S = segs[csg];
     const int vr = (n < VB) ? (int)S.vrow[n] : -1;
-    arow = vr >= 0 ? A + S.a_off + vr * AST : nullptr;
+    arow = vr >= 0 ? A + S.a_off + vr * AST + cq * (K / KS) + 16 * g : nullptr;
   };
   if (myunits > 0) open_compute(0);
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   for (int it0 = 0; it0 < nitD; it0 += D) {
 #pragma unroll
     for (int d = 0; d < D; d++) {
-      {
-        const bool live = it0 + d < nit;
-        const int k0 = (cq * (K / KS)) + 64 * cs;
-        uint4 a0 = make_uint4(0u, 0u, 0u, 0u), a1 = a0;
-        if (arow) {
-          a0 = *reinterpret_cast<const uint4*>(arow + k0 + 16 * g);
-          a1 = *reinterpret_cast<const uint4*>(arow + k0 + 16 * g + 8);
-        }
-        const uint4 wv = buf[d];
-        const float sc = scb[d];
-        issue(d);
-        const uint32_t wd[4] = {wv.x, wv.y, wv.z, wv.w};
-        uint32_t bw[8];
+      const bool live = it0 + d < nit;
+      uint4 a0 = make_uint4(0u, 0u, 0u, 0u), a1 = a0, a2 = a0, a3 = a0;
+      if (arow) {
+        const uint16_t* ap = arow + 128 * cs;
+        a0 = *reinterpret_cast<const uint4*>(ap);
+        a1 = *reinterpret_cast<const uint4*>(ap + 8);
+        a2 = *reinterpret_cast<const uint4*>(ap + 64);
+        a3 = *reinterpret_cast<const uint4*>(ap + 72);
+      }
+      const uint4 va = bufa[d], vb = bufb[d];
+      const float sc = scb[d];
+      issue(d);
+      const uint4 ra = ror8_rows(va), rb = ror8_rows(vb);
+      const uint4 p0 = lo8 ? va : rb, p1 = lo8 ? ra : vb;   // row n: bytes [16 g, +16) and [64 + 16 g, +16)
+      bf16x8_t b0, b1, b2, b3;
+      fp8x16_to_bf16(p0, b0, b1);
+      fp8x16_to_bf16(p1, b2, b3);
+      f32x4_t pk = {0.f, 0.f, 0.f, 0.f};
+      pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), b0, pk, 0, 0, 0);
+      pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), b1, pk, 0, 0, 0);
+      pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a2), b2, pk, 0, 0, 0);
+      pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a3), b3, pk, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const bf16x2_v lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[i], 1.0f, false);
-          const bf16x2_v hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd[i], 1.0f, true);
-          bw[2 * i] = __builtin_bit_cast(uint32_t, lo);
-          bw[2 * i + 1] = __builtin_bit_cast(uint32_t, hi);
-        }
-        const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, make_uint4(bw[0], bw[1], bw[2], bw[3]));
-        const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, make_uint4(bw[4], bw[5], bw[6], bw[7]));
-        f32x4_t pk = {0.f, 0.f, 0.f, 0.f};
-        pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0), b0, pk, 0, 0, 0);
-        pk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a1), b1, pk, 0, 0, 0);
+      for (int i = 0; i < 4; i++) acc[i] = fmaf(sc, pk[i], acc[i]);
+      if (live && ++cs == NS) {
+        // unit done: lane holds rows p = 4 g + i of column n
+        const MSeg& S = segs[csg];
+        const int r = 16 * ctt + n;
+        if (r < S.n) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) acc[i] = fmaf(sc, pk[i], acc[i]);
-        if (live && ++cs == NS) {
-          // unit done: lane holds rows p = 4 g + i of column n
-          const MSeg& S = segs[csg];
-          const int r = 16 * ctt + n;
-          if (r < S.n) {
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-              const int p = 4 * g + i;
-              if (p < nq) {
-                if (KS == 1) out[S.o_off + p * (ostr ? ostr : S.n) + r] = acc[i];
-                else part[((cq * ntiles + (wave + cu * NWAVES) % ntiles) * 16 + n) * VB + p] = acc[i];
-              }
+          for (int i = 0; i < 4; i++) {
+            const int p = 4 * g + i;
+            if (p < nq) {
+              if (KS == 1) out[S.o_off + p * (ostr ? ostr : S.n) + r] = acc[i];
+              else part[((cq * ntiles + (wave + cu * NWAVES) % ntiles) * 16 + n) * VB + p] = acc[i];
             }
           }
-          acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          cs = 0;
-          if (++cu < myunits) open_compute(cu);
         }
+        acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        cs = 0;
+        if (++cu < myunits) open_compute(cu);
       }
     }
   }
@@ -503,7 +530,7 @@ __device__ __forceinline__ bool bstage_x(Ctx& cx, const KArgs& a, const Step& st
       stamp(a, cx, st, TR_X_NORMED);
       return true;
     };
-    if (!mfma_list<H, 8>(L.segs, ns, L.A, L.out, r1 - r0, L.part, nq, pre)) return false;
+    if (!mfma_list<H, 4>(L.segs, ns, L.A, L.out, r1 - r0, L.part, nq, pre)) return false;
   }
   stamp(a, cx, st, TR_QKV_GEMV);
   for (int i = tid_opaque(); i < nq * (r1 - r0); i += BLOCK) {
@@ -537,7 +564,7 @@ __device__ __forceinline__ bool bstage_q(Ctx& cx, const KArgs& a, const Step& st
     stamp(a, cx, st, TR_CQ_READY);
     return true;
   };
-  if (!mfma_list<QL, 8>(L.segs, r1 > r0 ? 1 : 0, L.A, L.out, r1 - r0, L.part, nq, pre)) return false;
+  if (!mfma_list<QL, 4>(L.segs, r1 > r0 ? 1 : 0, L.A, L.out, r1 - r0, L.part, nq, pre)) return false;
   stamp(a, cx, st, TR_Q_GEMV);
   const int npair = (r1 - r0) / 2;
   for (int i = tid_opaque(); i < nq * npair; i += BLOCK) {
@@ -1082,7 +1109,7 @@ __device__ __forceinline__ bool bstage_uv(Ctx& cx, const KArgs& a, const Step& s
     __syncthreads();
     return true;
   };
-  if (!mfma_list<KL, 4>(L.segs, r1 > r0 ? 1 : 0, L.A, L.out, r1 - r0, L.part, nq, pre)) return false;
+  if (!mfma_list<KL, 2>(L.segs, r1 > r0 ? 1 : 0, L.A, L.out, r1 - r0, L.part, nq, pre)) return false;
   const int npair = (r1 - r0) / 2;
   for (int i = tid_opaque(); i < nq * npair; i += BLOCK) {
     const int p = i / npair, r = r0 + 2 * (i % npair);
@@ -1110,7 +1137,7 @@ __device__ __forceinline__ bool bstage_wo(Ctx& cx, const KArgs& a, const Step& s
     stamp(a, cx, st, TR_O_READY);
     return true;
   };
-  if (!mfma_list<OD, 8>(L.segs, r1 > r0 ? 1 : 0, L.A, L.out, r1 - r0, L.part, nq, pre)) return false;
+  if (!mfma_list<OD, 4>(L.segs, r1 > r0 ? 1 : 0, L.A, L.out, r1 - r0, L.part, nq, pre)) return false;
   for (int i = tid_opaque(); i < nq * (r1 - r0); i += BLOCK) {
     const int p = i / (r1 - r0), r = i % (r1 - r0);
     const float v = L.xres[p * 32 + r] + L.out[i];
@@ -1195,7 +1222,7 @@ __device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& 
     stamp(a, cx, st, TR_H2_READY);
     return true;
   };
-  if (!mfma_list<H, 8>(L.segs, nj > 0 ? 2 * ns : 0, L.A, L.out, 2 * ns * nj, L.part, nq, pre)) return false;
+  if (!mfma_list<H, 4>(L.segs, nj > 0 ? 2 * ns : 0, L.A, L.out, 2 * ns * nj, L.part, nq, pre)) return false;
   // shared m: silu(gate) * up as bf16 pairs, union slot s, position p
   for (int i = tid_opaque(); i < ns * nq * (nj / 2); i += BLOCK) {
     const int s = i / (nq * (nj / 2)), rem = i % (nq * (nj / 2)), p = rem / (nj / 2), jp = 2 * (rem % (nj / 2));
@@ -1323,7 +1350,7 @@ __device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& 
   }
   __syncthreads();
   float* rout = tmp;   // [nq][nrows] (the router scratch is free now)
-  if (!mfma_list<H, 8>(L.segs, 2 * npc, L.A, rout, nrows, L.part, nq, NoPre{})) return false;
+  if (!mfma_list<H, 4>(L.segs, 2 * npc, L.A, rout, nrows, L.part, nq, NoPre{})) return false;
   {
     int oo = 0;
     for (int q = 0; q < npc; q++) {
@@ -1407,7 +1434,7 @@ __device__ __forceinline__ bool bstage_down(Ctx& cx, const KArgs& a, const Step&
     return true;
   };
   // (ostr 0: segment g's results form a [VB][rows_g] block at o_off = rows before g * VB)
-  if (!mfma_list<INTER, 8>(L.segs, nseg, L.A, res, 0, L.part, nq, pre)) return false;
+  if (!mfma_list<INTER, 4>(L.segs, nseg, L.A, res, 0, L.part, nq, pre)) return false;
   stamp(a, cx, st, TR_DOWN_GEMV);
   // gated partials out: fpart[slot][p][row]
   {
