@@ -675,6 +675,53 @@ __device__ __forceinline__ bool bstage_absorb(Ctx& cx, const KArgs& a, const Ste
   return true;
 }
 
+// The new latent rows of the step's rows (computed by the last chunk's workgroups): all
+// rows' c_kv' | k_r' fetched together into tmp [VB][LAT] fp32 (LDS), RMSNorm of c_kv (fp64
+// statistics, one reduction for all rows) and RoPE of k_r at each row's position, bf16 into
+// newr [VB][LAT]; head group 0 appends each row to its cache row crow(p).
+template <class SH, typename CRow>
+__device__ __forceinline__ bool new_rows(Ctx& cx, const KArgs& a, const DLayer& Ly, VLds& V, int nq, uint32_t k1,
+                                         bool append, float* tmp, uint16_t* newr, CRow&& crow) {
+  constexpr int LAT = SH::LAT, KL = SH::KL, RD = SH::RD;
+  const int tid = tid_opaque();
+  if (!ll_fetch_rows<LAT>(cx, reinterpret_cast<uint32_t*>(tmp), LAT, vbuf(a, a.off.vckv, LAT, 0), LAT, nq, k1, W_KV))
+    return false;
+  double ss[VB];
+#pragma unroll
+  for (int p = 0; p < VB; p++) {
+    ss[p] = 0.0;
+    if (p < nq)
+      for (int i = tid; i < KL; i += BLOCK) ss[p] += (double)tmp[p * LAT + i] * (double)tmp[p * LAT + i];
+  }
+  block_sum_rows(ss, V.redv);
+  const PLD_GLOBAL float* gk = gp(Ly.kv_norm);
+  for (int e = tid; e < nq * (LAT / 2); e += BLOCK) {
+    const int p = e / (LAT / 2), i = e % (LAT / 2), k = 2 * i;
+    double r = 0.0;
+#pragma unroll
+    for (int q = 0; q < VB; q++) r = q == p ? ss[q] : r;
+    r = 1.0 / sqrt(r / (double)KL + a.c.eps);
+    const float* x = tmp + p * LAT;
+    float v0, v1;
+    if (k < KL) {
+      v0 = (float)(((double)x[k] * r) * (double)gk[k]);
+      v1 = (float)(((double)x[k + 1] * r) * (double)gk[k + 1]);
+    } else {
+      const int d = k - KL;
+      const PLD_GLOBAL float* rope = gp(wsp<float>(a, a.off.rope)) + (size_t)V.rpos[p] * RD;
+      const float x0 = x[k], x1 = x[k + 1], cs = rope[d], sg = rope[d + 1];
+      v0 = x0 * cs - x1 * sg;
+      v1 = x0 * sg + x1 * cs;
+    }
+    const uint32_t pair = f32_to_bf16(v0) | (f32_to_bf16(v1) << 16);
+    reinterpret_cast<uint32_t*>(newr + p * LAT)[i] = pair;
+    if (append) st_u32(reinterpret_cast<uint32_t*>(Ly.lat + crow(p) * LAT) + i, pair);
+  }
+  __syncthreads();
+  vm_wait();   // the appended rows are written before this workgroup's next publication
+  return true;
+}
+
 // ------------------------------------------------------------------ BT: attention, VPP positions per pass
 // Workgroup (head group hg of HPW = 16 heads, chunk ch) as in the single-position stage:
 // the chunk's rows [t0, t1) of the pos history rows (all written before this launch, so
@@ -721,35 +768,10 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
   // the new rows of this step (last chunk): RMSNorm(c_kv') and RoPE(k_r'), bf16; appended
   // to the cache by head group 0
   if (last) {
-    for (int p = 0; p < nq; p++) {
-      if (!ll_fetch<per_for(LAT)>(cx, reinterpret_cast<uint32_t*>(ntmp), vbuf(a, a.off.vckv, LAT, p), LAT, k1, W_KV))
-        return false;
-      double ss = 0.0;
-      for (int i = tid; i < KL; i += BLOCK) ss += (double)ntmp[i] * (double)ntmp[i];
-      ss = block_sum(ss, V.red);
-      const double r = 1.0 / sqrt(ss / (double)KL + c.eps);
-      const PLD_GLOBAL float* gk = gp(Ly.kv_norm);
-      const PLD_GLOBAL float* rope = gp(wsp<float>(a, a.off.rope)) + (size_t)V.rpos[p] * RD;
-      const size_t crow = (shared ? 0 : (size_t)p * seq_rows) + (size_t)V.rpos[p];   // cache row of the new row
-      for (int i = tid; i < LAT / 2; i += BLOCK) {
-        const int k = 2 * i;
-        float v0, v1;
-        if (k < KL) {
-          v0 = (float)(((double)ntmp[k] * r) * (double)gk[k]);
-          v1 = (float)(((double)ntmp[k + 1] * r) * (double)gk[k + 1]);
-        } else {
-          const int d = k - KL;
-          const float x0 = ntmp[k], x1 = ntmp[k + 1], cs = rope[d], sg = rope[d + 1];
-          v0 = x0 * cs - x1 * sg;
-          v1 = x0 * sg + x1 * cs;
-        }
-        const uint32_t pair = f32_to_bf16(v0) | (f32_to_bf16(v1) << 16);
-        reinterpret_cast<uint32_t*>(newr + p * LAT)[i] = pair;
-        if (hg == 0) st_u32(reinterpret_cast<uint32_t*>(Ly.lat + crow * LAT) + i, pair);
-      }
-      __syncthreads();
-    }
-    vm_wait();   // the appended rows are written before this workgroup's next publication
+    // (Cs buffer 0 is free until the first sub-block is staged)
+    if (!new_rows<SH>(cx, a, Ly, V, nq, k1, hg == 0, reinterpret_cast<float*>(Cs), newr,
+                      [&](int p) { return (shared ? 0 : (size_t)p * seq_rows) + (size_t)V.rpos[p]; }))
+      return false;
   }
   const float scale = 1.0f / sqrtf((float)(SH::ND + SH::RD));
   const int ln = lane & 15, lq = lane >> 4;
@@ -1011,6 +1033,256 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
   return true;
 }
 
+// ------------------------------------------------------------------ BV: attention of a verify, all positions in one pass
+// For the verify (the rows are consecutive positions of one sequence sharing its history):
+// workgroup (group of 8 heads, chunk of the history; NG = 8 groups x NCV = nwg / 8 chunks,
+// the groups of one chunk on one XCD). The A operand rows are (position, head) pairs, two
+// positions per 16-row tile (rows 8 (p & 1) + h of tile p >> 1), so every staged 32-row
+// sub-block serves all positions at once: S = Q C^T with wave w on tile (w >> 1, column
+// half w & 1) over all 36 k-steps, online softmax per row (half-wave hw holds row hw of each
+// tile), O += P C with wave w owning output columns [64 w, 64 w + 64) of all tiles. The last
+// chunk adds the new rows of the step (position p sees new rows 0..p) on the vector ALU.
+// Partials per (position, head, chunk) with NCV chunks.
+constexpr int VHG = 8;   // heads per workgroup in the verify attention
+template <class SH>
+__device__ __forceinline__ bool bstage_attn_v(Ctx& cx, const KArgs& a, const Step& st, VLds& V, int nq) {
+  const KCfg& c = a.c;
+  const DLayer Ly = *gp(st.Ly);
+  const uint32_t k1 = st.k1;
+  constexpr int LAT = SH::LAT, KL = SH::KL, RD = SH::RD, TB = SH::TB, CSTR = SH::CSTR;
+  constexpr int KSTEPS = LAT / 16;
+  constexpr int CPRW = LAT / 8;
+  constexpr int NLD = (TB * CPRW + BLOCK - 1) / BLOCK;
+  constexpr int MT = VB / 2;            // 16-row tiles of (position, head) rows
+  constexpr int QW = KL / 2 + RD / 2;   // words of one (position, head) query row
+  static_assert(KL == 512 && TB == 32 && SH::NH % VHG == 0 && NWAVES == 2 * MT, "the verify attention tiling");
+  const int tid = tid_opaque();
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 15, lq = lane >> 4;
+  const int nch = cx.nwg / (SH::NH / VHG);   // chunks per head group
+  const int hg = cx.w / nch, ch = cx.w % nch;
+  const int hbase = hg * VHG;
+  const int pos = V.rpos[0];                 // history rows [0, pos), shared by all positions
+  // the split counts the new-row sub-block of the last chunk as TB more rows, so that chunk
+  // holds one history sub-block fewer
+  const int t0 = split_at(pos + TB, nch, ch), n = max(0, min(split_at(pos + TB, nch, ch + 1), pos) - t0);
+  const uint16_t* lat = Ly.lat;
+  // LDS
+  uint16_t* Qs = V.A;                                        // [MT * 16][CSTR] (position, head) rows
+  uint16_t* Cs = Qs + MT * 16 * CSTR;                        // [TB][CSTR] the staged sub-block
+  uint16_t* Ps = Cs + TB * CSTR;                             // [MT * 16][TB] bf16
+  float* Ssc = reinterpret_cast<float*>(Ps + MT * 16 * TB);  // [MT][2][256] score tiles
+  float* alph = Ssc + MT * 2 * 256;                          // [MT * 16]
+  uint16_t* newr = reinterpret_cast<uint16_t*>(alph + MT * 16);   // [VB][LAT] new rows (bf16)
+  float* ntmp = reinterpret_cast<float*>(newr + VB * LAT);   // [LAT]
+  float* sn = ntmp + LAT;                                    // [MT * 16][VB + 2] new-row scores, p, alpha
+  const bool last = ch == nch - 1;
+  // the new rows of this step (last chunk): RMSNorm(c_kv') and RoPE(k_r'), bf16; appended by group 0
+  if (last) {
+    // (Cs is free until the first sub-block is staged)
+    if (!new_rows<SH>(cx, a, Ly, V, nq, k1, hg == 0, reinterpret_cast<float*>(Cs), newr,
+                      [&](int p) { return (size_t)V.rpos[p]; }))
+      return false;
+  }
+  // sub-block staging: DEPTH register sets, loads issued DEPTH blocks ahead (static rows: L2)
+  const int nsb = (n + TB - 1) / TB;
+  constexpr int DEPTH = 2;
+  uint4 cb[DEPTH][NLD];
+  auto issue = [&](int set, int sb) {
+    const bool live = sb < nsb;
+#pragma unroll
+    for (int i = 0; i < NLD; i++) {
+      const int idx = min(tid + i * BLOCK, TB * CPRW - 1);
+      const int r = idx / CPRW, k = idx % CPRW;
+      const int t = max(min(sb * TB + r, n - 1), 0);
+      const uint16_t* p = live ? lat + (size_t)(t0 + t) * LAT + k * 8 : lat;
+      cb[set][i] = ld_g16(p);
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < DEPTH; d++) issue(d, d);
+  // queries of all positions: q_lat [8 heads][KL] then q_rope [8 heads][RD] (bf16 pairs) -> Qs
+  // rows; one LL fetch (word (p, h, k2) of the query row lands at Qs row (p, h), word k2)
+  {
+    const int qlat_off = (int)((a.off.vqlat - a.off.vqr) / 8);   // vqlat lies after vqr
+    struct IdxQ {
+      int qlat_off, hbase;
+      __device__ __forceinline__ int operator()(int i) const {
+        const int p = i / (VHG * QW), k = i % (VHG * QW);
+        if (k < VHG * (KL / 2)) return qlat_off + p * (SH::NH * KL / 2) + hbase * (KL / 2) + k;
+        const int j = k - VHG * (KL / 2);
+        return p * (SH::NH * RD / 2) + hbase * (RD / 2) + j;
+      }
+    };
+    struct StQ {
+      __device__ __forceinline__ void operator()(uint32_t* dst, int i, uint32_t v) const {
+        const int p = i / (VHG * QW), k = i % (VHG * QW);
+        int h, k2;
+        if (k < VHG * (KL / 2)) {
+          h = k / (KL / 2);
+          k2 = k % (KL / 2);
+        } else {
+          const int j = k - VHG * (KL / 2);
+          h = j / (RD / 2);
+          k2 = KL / 2 + j % (RD / 2);
+        }
+        dst[(((p >> 1) * 16 + (p & 1) * VHG + h) * CSTR) / 2 + k2] = v;
+      }
+    };
+    for (int i = tid; i < (MT * 16 - nq * VHG) * (CSTR / 2); i += BLOCK)   // rows of absent positions: zero
+      reinterpret_cast<uint32_t*>(Qs)[nq * VHG * (CSTR / 2) + i] = 0u;
+    if (!ll_fetch<per_for(VB * VHG * QW)>(cx, reinterpret_cast<uint32_t*>(Qs), wsp<uint64_t>(a, a.off.vqr),
+                                          nq * VHG * QW, k1, W_QLAT, IdxQ{qlat_off, hbase}, StQ{}))
+      return false;
+  }
+  for (int i = tid; i < MT * 16 * TB; i += BLOCK) Ps[i] = 0;
+  __syncthreads();
+  stamp(a, cx, st, TR_ATT_READY);
+  const float scale = 1.0f / sqrtf((float)(SH::ND + SH::RD));
+  // softmax state of half-wave hw = row hw of each tile
+  const int hw = tid >> 5, tl = lane & 31;
+  float m_run[MT], l_run[MT];
+  f32x4 O[MT][4];
+#pragma unroll
+  for (int mi = 0; mi < MT; mi++) {
+    m_run[mi] = -INFINITY;
+    l_run[mi] = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; t++) O[mi][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  auto row_live = [&](int mi, int r16) { return 2 * mi + (r16 >= VHG ? 1 : 0) < nq; };
+  auto block = [&](int tb0, bool causal) {
+    // S tile (mi, nt) of wave w: two accumulator chains over the 36 k-steps
+    {
+      const int mi = wave >> 1, nt = wave & 1;
+      f32x4 s4 = {0.f, 0.f, 0.f, 0.f}, s5 = {0.f, 0.f, 0.f, 0.f};
+      const uint16_t* Q = Qs + mi * 16 * CSTR;
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; kk++) {
+        const int k0 = kk * 16 + 4 * lq;
+        const bf16x4 av = *reinterpret_cast<const bf16x4*>(Q + ln * CSTR + k0);
+        const bf16x4 bv = *reinterpret_cast<const bf16x4*>(Cs + (nt * 16 + ln) * CSTR + k0);
+        if (kk & 1) s5 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, s5, 0, 0, 0);
+        else s4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, s4, 0, 0, 0);
+      }
+      s4 += s5;
+      float* dst = Ssc + (mi * 2 + nt) * 256;
+#pragma unroll
+      for (int q = 0; q < 4; q++) dst[(4 * lq + q) * 16 + ln] = s4[q];
+    }
+    __syncthreads();
+    // online softmax: row hw of tile mi, token tb0 + tl (causal: new row tl, seen by positions >= tl)
+#pragma unroll
+    for (int mi = 0; mi < MT; mi++) {
+      float sc = -INFINITY;
+      const int prow = 2 * mi + (hw >= VHG ? 1 : 0);
+      const bool ok = causal ? (tl < nq && tl <= prow) : (tb0 + tl < n);
+      if (ok && prow < nq) sc = Ssc[(mi * 2 + (tl >> 4)) * 256 + hw * 16 + (tl & 15)] * scale;
+      const float mb = half_max_dpp(sc);
+      const float mnew = fmaxf(m_run[mi], mb);
+      const float al = m_run[mi] == -INFINITY ? 0.f : __expf(m_run[mi] - mnew);
+      const float pv = sc == -INFINITY ? 0.f : __expf(sc - mnew);
+      l_run[mi] = l_run[mi] * al + half_sum_dpp(pv);
+      m_run[mi] = mnew;
+      Ps[(mi * 16 + hw) * TB + tl] = (uint16_t)bf16_bits(pv);
+      if (tl == 0) alph[mi * 16 + hw] = al;
+    }
+    __syncthreads();
+    // O = alpha O + P C: wave owns columns [wave*64, +64) of every tile
+#pragma unroll
+    for (int mi = 0; mi < MT; mi++) {
+      float fa[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++) fa[q] = alph[mi * 16 + 4 * lq + q];
+#pragma unroll
+      for (int t = 0; t < 4; t++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) O[mi][t][q] *= fa[q];
+    }
+#pragma unroll
+    for (int ks = 0; ks < TB / 16; ks++) {
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        const int col = (wave * 4 + t) * 16 + ln;
+        bf16x4 bv;
+#pragma unroll
+        for (int q = 0; q < 4; q++) bv[q] = (short)Cs[(ks * 16 + 4 * lq + q) * CSTR + col];
+#pragma unroll
+        for (int mi = 0; mi < MT; mi++) {
+          const bf16x4 av = *reinterpret_cast<const bf16x4*>(Ps + (mi * 16 + ln) * TB + ks * 16 + 4 * lq);
+          O[mi][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, O[mi][t], 0, 0, 0);
+        }
+      }
+    }
+  };
+  // the history sub-blocks, then (last chunk) the new rows of the step as one more sub-block
+  // with the causal mask: row (p, h) sees new rows 0..p
+  const int nall = nsb + (last ? 1 : 0);
+  for (int sb0 = 0; sb0 < nall; sb0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; d++) {
+      const int sb = sb0 + d;
+      if (sb >= nall) break;
+      __syncthreads();   // (the previous block's reads of Cs are done)
+      if (sb < nsb) {
+#pragma unroll
+        for (int i = 0; i < NLD; i++) {
+          const int idx = tid + i * BLOCK;
+          if (idx < TB * CPRW) {
+            const int r = idx / CPRW, k = idx % CPRW;
+            uint32_t* dd = reinterpret_cast<uint32_t*>(Cs + r * CSTR + k * 8);
+            dd[0] = cb[d][i].x; dd[1] = cb[d][i].y; dd[2] = cb[d][i].z; dd[3] = cb[d][i].w;
+          }
+        }
+      } else {
+        for (int i = tid; i < TB * (CSTR / 2); i += BLOCK) {
+          const int r = i / (CSTR / 2), k2 = i % (CSTR / 2);
+          reinterpret_cast<uint32_t*>(Cs)[i] =
+              (r < nq && k2 < LAT / 2) ? reinterpret_cast<const uint32_t*>(newr + r * LAT)[k2] : 0u;
+        }
+      }
+      __syncthreads();
+      issue(d, sb + DEPTH);
+      block(sb * TB, sb >= nsb);
+    }
+  }
+  __syncthreads();
+  stamp(a, cx, st, 17);
+  stamp(a, cx, st, TR_ATT_SOFTMAX);
+  // partials: LL words [m, l, acc as fp16 pairs] of (position p, head hbase + h, chunk)
+  constexpr int PSTR = KL / 2 + 2;
+  const size_t pwords = (size_t)SH::NH * c.cpg * PSTR;   // per-position stride of the partial buffer
+  uint64_t* pll = wsp<uint64_t>(a, a.off.vpart);
+#pragma unroll
+  for (int mi = 0; mi < MT; mi++) {
+    const int p = 2 * mi + (hw >= VHG ? 1 : 0);
+    if (tl == 0 && p < nq) {
+      uint64_t* q = pll + (size_t)p * pwords + ((size_t)(hbase + (hw & (VHG - 1))) * nch + ch) * PSTR;
+      ll_put_f32(q, m_run[mi], k1);
+      ll_put_f32(q + 1, l_run[mi], k1);
+    }
+  }
+#pragma unroll
+  for (int mi = 0; mi < MT; mi++) {
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      const int col = (wave * 4 + t) * 16 + ln;
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const float nb = dpp_mov<0xB1, 0xf, false>(O[mi][t][q]);
+        const int r16 = 4 * lq + q, p = 2 * mi + (r16 >= VHG ? 1 : 0), h = r16 & (VHG - 1);
+        if ((ln & 1) == 0 && p < nq) {
+          const uint32_t pr = (uint32_t)__half_as_ushort(__float2half_rn(O[mi][t][q])) |
+                              ((uint32_t)__half_as_ushort(__float2half_rn(nb)) << 16);
+          ll_put(pll + (size_t)p * pwords + ((size_t)(hbase + h) * nch + ch) * PSTR + 2 + col / 2, pr, k1);
+        }
+      }
+    }
+  }
+  stamp(a, cx, st, TR_ATT_PARTIAL);
+  return true;
+}
+
 // ------------------------------------------------------------------ BM: merge, per position
 // Workgroup (head h, cpw columns) as in the single-position stage; the partials of MG
 // positions are fetched together (one LL fetch), then wave p (< MG) forms position p's
@@ -1019,14 +1291,15 @@ template <class SH>
 __device__ __forceinline__ bool bstage_merge(Ctx& cx, const KArgs& a, const Step& st, VLds& V, int nq) {
   const KCfg& c = a.c;
   constexpr int KL = SH::KL, MG = 4;
-  const int nch = c.cpg, cpw = c.cpw;
+  // chunks per head: the verify attention (8 heads per workgroup) or the per-row one (HPW)
+  const int nch = a.bmode == 0 ? cx.nwg / (SH::NH / VHG) : c.cpg, cpw = c.cpw;
   const int h = (cx.w * cpw) / KL, c0 = (cx.w * cpw) % KL;
   const int tid = tid_opaque();
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int PSTR = KL / 2 + 2;
   const int cpw2 = cpw / 2, nacc = nch * cpw, naw = nch * cpw2;
   const int per = naw + 2 * nch;                 // words of one position
-  const int pwords = SH::NH * nch * PSTR;        // LL words of one position's partials
+  const int pwords = SH::NH * c.cpg * PSTR;      // LL words of one position's partials (stride)
   const int fstr = nacc + 2 * nch;               // floats of one position in LDS
   // word i of the group: position i / per, then as in the single-position stage
   struct IdxM {
@@ -1060,6 +1333,7 @@ __device__ __forceinline__ bool bstage_merge(Ctx& cx, const KArgs& a, const Step
     if (!ll_fetch<16>(cx, reinterpret_cast<uint32_t*>(base), wsp<uint64_t>(a, a.off.vpart) + (size_t)p0 * pwords,
                       np * per, st.k1, W_PART, IdxM{per, naw, cpw2, nch, h, c0, pwords}, StM{per, naw, fstr}))
       return false;
+    if (p0 == 0) stamp(a, cx, st, TR_MERGE_COPIED);
     if (wave < np) {
       const float* mls = base + wave * fstr + nacc;
       float M = -INFINITY;
@@ -1559,7 +1833,11 @@ __global__ void __launch_bounds__(BLOCK, 1) k_verify_mla(KArgs a) {
       if (!bstage_x<SH>(cs, as, st, L, nq, li)) return;
       if (!bstage_q<SH>(cs, as, st, L, nq)) return;
       if (!bstage_absorb<SH>(cs, as, st, L, nq)) return;
-      if (!bstage_attn<SH>(cs, as, st, L, nq)) return;
+      if (as.bmode == 0) {
+        if (!bstage_attn_v<SH>(cs, as, st, L, nq)) return;
+      } else {
+        if (!bstage_attn<SH>(cs, as, st, L, nq)) return;
+      }
       if (!bstage_merge<SH>(cs, as, st, L, nq)) return;
       if (!bstage_uv<SH>(cs, as, st, L, nq)) return;
       if (!bstage_wo<SH>(cs, as, st, L, nq)) return;
