@@ -66,7 +66,7 @@ WORKLOADS = {   # name -> (synth.configs attribute, traffic file stem, dtype of 
 }
 DEFAULT_WORKLOAD = "mla_stack24_fp8_greedy256"
 KERNEL_SOURCES = [os.path.join(ROOT, "persistent_latency_bound_amd", "csrc", f)
-                  for f in ("pld_kernel.hip", "pld_device.hpp", "pld_mla.hpp", "pld_kda.hpp", "pld_math.hpp")]
+                  for f in ("pld_kernel.hip", "pld_device.hpp", "pld_mla.hpp", "pld_kda.hpp", "pld_math.hpp", "pld_batch.hpp")]
 
 
 def kernel_sha() -> str:

@@ -22,10 +22,13 @@
 //   BM  merge of the chunk partials, per position
 //   BU  o = W_UV o_lat per head                                               (matrix cores)
 //   BO  h2_p = x_p + W_O o_p                                                  (matrix cores)
-//   BF  RMSNorm(h2_p); router logits in fp64 from the fp32 activation (the selection
-//       must match an fp64 evaluation); shared experts (matrix cores); per-position
-//       top-k; the UNION of the selected experts, each read once for the positions
-//       that chose it (matrix cores)
+//       and, over this workgroup's rows, the partial sums that BF needs
+//   BF  RMSNorm(h2_p) and the router logits in fp64 (the selection must match an fp64
+//       evaluation), both from partial sums that the W_O workgroups form over their own
+//       rows (sum of h2^2; sum of W_r * gamma * h2 per expert): the router no longer waits
+//       for the whole h2; shared experts (matrix cores); the top-k of every position at
+//       once; the UNION of the selected experts, each read once for the positions that
+//       chose it (matrix cores)
 //   BD  down projections: this workgroup's output rows for every (expert, position)
 //       pair, the expert's rows read once; f_p = sum of gated results; x'_p = h2_p + f_p
 // then, after the last layer, the LM head and the token choice of each position and the
@@ -1400,10 +1403,24 @@ __device__ __forceinline__ bool bstage_wo(Ctx& cx, const KArgs& a, const Step& s
   constexpr int OD = SH::ODIM, AST = vb_astr(OD);
   int r0, r1;
   hrows(SH::H, cx.nwg, cx.w, &r0, &r1);
-  const DMat wo = gp(st.Ly)->wo;
+  const DLayer Ly = *gp(st.Ly);
+  const KCfg& c = a.c;
+  const int tid = tid_opaque(), nr = r1 - r0;
   __syncthreads();
-  mseg_set(L.segs, 0, wo.w + (size_t)r0 * OD, wo.s, r1 - r0, r0, 0, 0, nq);
+  mseg_set(L.segs, 0, Ly.wo.w + (size_t)r0 * OD, Ly.wo.s, nr, r0, 0, 0, nq);
   __syncthreads();
+  // loaded ahead of the W_O stream: thread (half hh, expert e) takes its half of the row
+  // pairs of W_r[e][r0, r1) (bf16 pairs); thread (p, r) the FFN norm weight gamma[r0 + r]
+  constexpr int RW = 8;   // pairs per half: rows per workgroup <= 32
+  const int np2 = nr / 2, hh = tid >> 8, jb = hh ? np2 / 2 : 0, jn = hh ? np2 - np2 / 2 : np2 / 2;
+  uint32_t rw[RW];
+  {
+    const PLD_GLOBAL uint32_t* rp =
+        gp(reinterpret_cast<const uint32_t*>(Ly.router + (size_t)min(tid & 255, c.E - 1) * SH::H + r0)) + jb;
+#pragma unroll
+    for (int j = 0; j < RW; j++) rw[j] = rp[max(min(j, jn - 1), 0)];
+  }
+  const float gr = gp(Ly.ffn_norm)[r0 + min(tid & 31, nr - 1)];
   auto pre = [&]() -> bool {
     if (!ll_fetch_rows<OD / 2>(cx, reinterpret_cast<uint32_t*>(L.A), AST / 2, vbuf(a, a.off.vo, OD / 2, 0), OD / 2, nq,
                                st.k1, W_O))
@@ -1411,12 +1428,72 @@ __device__ __forceinline__ bool bstage_wo(Ctx& cx, const KArgs& a, const Step& s
     stamp(a, cx, st, TR_O_READY);
     return true;
   };
-  if (!mfma_list<OD, 4>(L.segs, r1 > r0 ? 1 : 0, L.A, L.out, r1 - r0, L.part, nq, pre)) return false;
-  for (int i = tid_opaque(); i < nq * (r1 - r0); i += BLOCK) {
-    const int p = i / (r1 - r0), r = i % (r1 - r0);
-    const float v = L.xres[p * 32 + r] + L.out[i];
-    L.h2res[p * 32 + r] = v;
-    ll_put_f32(vbuf(a, a.off.vh2, SH::H, p) + r0 + r, v, st.k1);
+  if (!mfma_list<OD, 4>(L.segs, nr > 0 ? 1 : 0, L.A, L.out, nr, L.part, nq, pre)) return false;
+  // (the A rows are free again: mfma_list ends with a barrier)
+  for (int i = tid; i < nq * nr; i += BLOCK) {
+    const int p = i / nr, r = i % nr;
+    L.h2res[p * 32 + r] = L.xres[p * 32 + r] + L.out[i];
+  }
+  __syncthreads();
+  // This workgroup's share of the FFN norm statistics, sum of h2[p][r]^2 over its rows, one
+  // 16-word line [position][lo, hi] written by one store instruction; published first, so
+  // that the consumers' norm scale does not wait for the router sums below.
+  if (tid < 2 * VB) {
+    const int p = tid >> 1;
+    double q = 0.0;
+    if (p < nq)
+      for (int r = 0; r < nr; r++) q += (double)L.h2res[p * 32 + r] * (double)L.h2res[p * 32 + r];
+    const uint64_t b = (uint64_t)__double_as_longlong(q);
+    ll_put(wsp<uint64_t>(a, a.off.vss) + (size_t)cx.w * VB * 2 + tid, (uint32_t)(b >> (32 * (tid & 1))), st.k1);
+  }
+  for (int i = tid; i < nq * nr; i += BLOCK) {
+    const int p = i / nr, r = i % nr;
+    ll_put_f32(vbuf(a, a.off.vh2, SH::H, p) + r0 + r, L.h2res[p * 32 + r], st.k1);
+  }
+  // the router's partial dot products of expert e over these rows, gamma included:
+  // sum_r W_r[e][r0 + r] * gamma[r0 + r] * h2[p][r] (fp64), each half of the rows on its own
+  // thread; the router workgroup of e adds the workgroups' sums and applies the norm scale
+  double* gh = reinterpret_cast<double*>(L.A);   // [VB][32] gamma_r * h2[p][r] (exact fp64 products)
+  double* rpl = gh + VB * 32;                    // [2][256][VB] the two halves' sums
+  if (tid < VB * 32) {
+    const int p = tid >> 5, r = tid & 31;
+    gh[tid] = (p < nq && r < nr) ? (double)gr * (double)L.h2res[p * 32 + r] : 0.0;
+  }
+  __syncthreads();
+  if ((tid & 255) < c.E) {
+    double acc[VB];
+#pragma unroll
+    for (int p = 0; p < VB; p++) acc[p] = 0.0;
+#pragma unroll
+    for (int j = 0; j < RW; j++) {
+      if (j < jn) {
+        const int r = 2 * (jb + j);
+        const double w0 = (double)bf_lo(rw[j]), w1 = (double)bf_hi(rw[j]);
+        double g0[VB], g1[VB];
+#pragma unroll
+        for (int p = 0; p < VB; p++) {
+          g0[p] = gh[p * 32 + r];
+          g1[p] = gh[p * 32 + r + 1];
+        }
+#pragma unroll
+        for (int p = 0; p < VB; p++) acc[p] = fma(w1, g1[p], fma(w0, g0[p], acc[p]));
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < VB; p++) rpl[(hh * 256 + (tid & 255)) * VB + p] = acc[p];
+  }
+  __syncthreads();
+  // Published as whole 128-byte lines: the 16 words [position][lo, hi] of (expert e, this
+  // workgroup) come from 16 consecutive lanes (scattered 8-byte stores from every workgroup
+  // would each be a separate partial-line write to memory).
+  {
+    uint64_t* rpb = wsp<uint64_t>(a, a.off.vrp);
+    const int k = tid & 15, p = k >> 1;
+    for (int e = tid >> 4; e < c.E; e += BLOCK / 16) {
+      const double v = p < nq ? rpl[e * VB + p] + rpl[(256 + e) * VB + p] : 0.0;
+      const uint64_t b = (uint64_t)__double_as_longlong(v);
+      ll_put(rpb + ((size_t)e * cx.nwg + cx.w) * VB * 2 + k, (uint32_t)(b >> (32 * (k & 1))), st.k1);
+    }
   }
   stamp(a, cx, st, TR_WO_DONE);
   return true;
@@ -1431,22 +1508,11 @@ __device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& 
   const uint32_t k1 = st.k1;
   constexpr int H = SH::H, AST = vb_astr(H), INTER = SH::INTER;
   static_assert(SH::MOE && SH::FP8, "the batched FFN is the FP8 MoE one");
-  float* tmp = reinterpret_cast<float*>(L.A + VB * AST);   // [2][H] fp32 normalised activations (router)
+  float* tmp = reinterpret_cast<float*>(L.A + VB * AST);   // [H] norm weights, then [nq][E][2] logits, keys
   RegPairs<H> gmf;
   gmf.load(Ly.ffn_norm);
-  // router row of expert w (bf16), loaded ahead of the expert weights
-  constexpr int RCH = H / 8, RPT = (RCH + BLOCK - 1) / BLOCK;
-  uint4 rrow[RPT];
   float rbias = 0.f;
-  if (w < c.E) {
-    if (c.router == PLD_ROUTER_SIGMOID_BIAS) rbias = gp(Ly.router_bias)[w];
-    const uint16_t* rp0 = Ly.router + (size_t)w * H;
-#pragma unroll
-    for (int k = 0; k < RPT; k++) {
-      const int q = tid_opaque() + k * BLOCK;
-      rrow[k] = q < RCH ? ld_g16(rp0 + q * 8) : make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
+  if (w < c.E && c.router == PLD_ROUTER_SIGMOID_BIAS) rbias = gp(Ly.router_bias)[w];
   const int ns = c.nshared;
   uint64_t* mbase = wsp<uint64_t>(a, a.off.vm);
   const size_t mwords = (size_t)VB * INTER / 2;   // words of one union slot
@@ -1460,38 +1526,69 @@ __device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& 
              (2 * s + 1) * nj, nq);
   }
   __syncthreads();
+  double* rnorm = L.redv;   // [VB] the FFN norm's scale 1 / rms(h2_p)
   auto pre = [&]() -> bool {
-    // two positions at a time (fp32 h2 rows in tmp): RMSNorm in fp64, the fp32 result for the
-    // router and its bf16 rounding for the matrix cores; then the router logits (fp64)
-    for (int p0 = 0; p0 < nq; p0 += 2) {
-      const int np = min(2, nq - p0);
-      if (!ll_fetch_rows<H>(cx, reinterpret_cast<uint32_t*>(tmp), H, vbuf(a, a.off.vh2, H, p0), H, np, k1, W_H2))
+    const int tid = tid_opaque(), lane = tid & 63, wave = tid >> 6;
+    // the norm weights into LDS (visible after the fetch's closing barrier)
+#pragma unroll
+    for (int k = 0; k < RegPairs<H>::K; k++) {
+      const int j = tid + k * BLOCK;
+      if ((H / 2) % BLOCK == 0 || j < H / 2) reinterpret_cast<float2*>(tmp)[j] = gmf.v[k];
+    }
+    // the W_O workgroups' partial sums: words k < 2 nq of each producer's 16-word line
+    struct IdxP {
+      int nq2;
+      __device__ __forceinline__ int operator()(int i) const { return (i / nq2) * (VB * 2) + i % nq2; }
+    };
+    const double* pd = reinterpret_cast<const double*>(L.A);   // [nwg][nq] (fetched fp64 pairs)
+    // (1) the norm statistics -> wave p: position p's scale, the producers' sums added in a
+    // fixed order (lane sums in producer order, then the wave's tree)
+    if (!ll_fetch<per_for(256 * VB * 2)>(cx, reinterpret_cast<uint32_t*>(L.A), wsp<uint64_t>(a, a.off.vss),
+                                         nwg * nq * 2, k1, W_H2, IdxP{nq * 2}))
+      return false;
+    if (wave < nq) {
+      double q = 0.0;
+      for (int k = lane; k < nwg; k += 64) q += pd[k * nq + wave];
+      q = wave_sum_any(q);
+      if (lane == 0) rnorm[wave] = 1.0 / sqrt(q / (double)H + c.eps);
+    }
+    __syncthreads();
+    // (2) h2 of every position, normalised as it arrives: bf16(fp32((h2 * r_p) * gamma))
+    struct StNorm {
+      uint16_t* A;
+      const double* r;
+      const float* g;
+      __device__ __forceinline__ void operator()(uint32_t*, int i, uint32_t v) const {
+        const int p = i / H, col = i - p * H;
+        const float y = (float)(((double)__uint_as_float(v) * r[p]) * (double)g[col]);
+        A[p * AST + col] = (uint16_t)f32_to_bf16(y);
+      }
+    };
+    // (24 loads per thread and round: three rounds for six positions; more loads in flight
+    // would spill registers here)
+    if (!ll_fetch<24>(cx, nullptr, vbuf(a, a.off.vh2, H, 0), nq * H, k1, W_H2, IdxLinear{},
+                      StNorm{L.A, rnorm, tmp}))
+      return false;
+    // (3) router workgroups: expert w's logit of every position from the producers' router
+    // sums (fixed order as above) times the norm scale; published as four LL words (logit
+    // lo, hi, key lo, hi) per position
+    if (w < c.E) {
+      double* rd = reinterpret_cast<double*>(tmp + H);   // [nwg][nq] (fetched fp64 pairs; past the norm weights)
+      if (!ll_fetch<per_for(256 * VB * 2)>(cx, reinterpret_cast<uint32_t*>(rd),
+                                           wsp<uint64_t>(a, a.off.vrp) + (size_t)w * nwg * VB * 2, nwg * nq * 2, k1,
+                                           W_H2, IdxP{nq * 2}))
         return false;
-      rms_rows<H>(L.A + p0 * AST, AST, [&](int p, int j) { return reinterpret_cast<const float2*>(tmp + p * H)[j]; },
-                  gmf, c.eps, L.redv, np, tmp, H);
-      if (w < c.E) {
-        double sv[VB];
-#pragma unroll
-        for (int p = 0; p < VB; p++) {
-          sv[p] = 0.0;
-          if (p < np) {
-#pragma unroll
-            for (int k = 0; k < RPT; k++) {
-              const int q = tid_opaque() + k * BLOCK;
-              if (q < RCH) sv[p] += dot8_bf16_f64(rrow[k], tmp + p * H + q * 8);
-            }
-          }
-        }
-        block_sum_rows(sv, L.redv);
-        if (tid_opaque() < 4 * np) {
-          const int p = tid_opaque() >> 2, wd = tid_opaque() & 3;
-          const double sp = p == 0 ? sv[0] : sv[1];
+      if (wave < nq) {
+        double d = 0.0;
+        for (int k = lane; k < nwg; k += 64) d += rd[k * nq + wave];
+        d = wave_sum_any(d);
+        const double sp = rnorm[wave] * d;
+        if (lane < 4) {
           const double key = c.router == PLD_ROUTER_SIGMOID_BIAS ? (1.0 / (1.0 + exp_f64(-sp, L.dk))) + (double)rbias : sp;
-          const uint64_t bits = (uint64_t)__double_as_longlong(wd < 2 ? sp : key);
-          ll_put(vbuf(a, a.off.vlog, 4 * (size_t)c.E, p0 + p) + 4 * w + wd, (uint32_t)(bits >> (32 * (wd & 1))), k1);
+          const uint64_t bits = (uint64_t)__double_as_longlong(lane < 2 ? sp : key);
+          ll_put(vbuf(a, a.off.vlog, 4 * (size_t)c.E, wave) + 4 * w + lane, (uint32_t)(bits >> (32 * (lane & 1))), k1);
         }
       }
-      __syncthreads();
     }
     stamp(a, cx, st, TR_H2_READY);
     return true;
@@ -1507,58 +1604,64 @@ __device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& 
            k1);
   }
   stamp(a, cx, st, TR_SHARED_GEMV);
-  // top-k per position (wave 0; the same selection in every workgroup), then the union
-  double* lk = reinterpret_cast<double*>(tmp);   // [E][2] (logit, key) of one position
-  for (int p = 0; p < nq; p++) {
-    if (!ll_fetch<per_for(4 * 512)>(cx, reinterpret_cast<uint32_t*>(lk), vbuf(a, a.off.vlog, 4 * (size_t)c.E, p), 4 * c.E,
-                                    k1, W_RT))
-      return false;
-    if (tid_opaque() < 64) {
-      const int lane = tid_opaque();
-      constexpr int NS = 4;   // E <= 256
-      uint64_t ks[NS];
+  // every position's router logits and keys in one fetch: lk[p][E][2]; wave p selects
+  // position p's top-k (the same selection in every workgroup)
+  double* lk = reinterpret_cast<double*>(tmp);
+  if (!ll_fetch<per_for(VB * 4 * 256)>(cx, reinterpret_cast<uint32_t*>(lk), vbuf(a, a.off.vlog, 4 * (size_t)c.E, 0),
+                                       nq * 4 * c.E, k1, W_RT))
+    return false;
+  if ((tid_opaque() >> 6) < nq) {
+    const int lane = tid_opaque() & 63, p = tid_opaque() >> 6;
+    const double* lkp = lk + (size_t)p * 2 * c.E;
+    constexpr int NS = 4;   // E <= 256
+    uint64_t ks[NS];
 #pragma unroll
-      for (int i = 0; i < NS; i++) {
-        const int e = lane + 64 * i;
-        const double ke = e < c.E ? lk[2 * e + 1] : 0.0;
-        const uint64_t bb = (uint64_t)__double_as_longlong(ke == 0.0 ? 0.0 : ke);
-        ks[i] = e < c.E ? ((bb >> 63) ? ~bb : (bb | (1ull << 63))) : 0ull;
-      }
-      for (int r = 0; r < c.topk; r++) {
-        uint64_t b = ks[0];
-        uint32_t bi = 0u;
-#pragma unroll
-        for (int i = 1; i < NS; i++) {
-          const bool gt = ks[i] > b;
-          b = gt ? ks[i] : b;
-          bi = gt ? (uint32_t)i : bi;
-        }
-        uint64_t m = b;
-        for (int off = 32; off >= 1; off >>= 1) {
-          const uint64_t o = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(m >> 32), off, 64) << 32) |
-                             (uint32_t)__shfl_xor((int)(uint32_t)m, off, 64);
-          m = o > m ? o : m;
-        }
-        const uint32_t mye = (uint32_t)lane + 64u * bi;
-        const bool hold = b == m;
-        const uint32_t ee = wave_minmax_u32<false>(hold ? mye : 0xffffffffu);
-#pragma unroll
-        for (int i = 0; i < NS; i++) ks[i] = (mye == ee && bi == (uint32_t)i) ? 0ull : ks[i];
-        if (lane == 0) L.isel[p * 8 + r] = (int)ee;
-      }
+    for (int i = 0; i < NS; i++) {
+      const int e = lane + 64 * i;
+      const double ke = e < c.E ? lkp[2 * e + 1] : 0.0;
+      const uint64_t bb = (uint64_t)__double_as_longlong(ke == 0.0 ? 0.0 : ke);
+      ks[i] = e < c.E ? ((bb >> 63) ? ~bb : (bb | (1ull << 63))) : 0ull;
     }
-    __syncthreads();
+    for (int r = 0; r < c.topk; r++) {
+      uint64_t b = ks[0];
+      uint32_t bi = 0u;
+#pragma unroll
+      for (int i = 1; i < NS; i++) {
+        const bool gt = ks[i] > b;
+        b = gt ? ks[i] : b;
+        bi = gt ? (uint32_t)i : bi;
+      }
+      uint64_t m = b;
+      for (int off = 32; off >= 1; off >>= 1) {
+        const uint64_t o = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(m >> 32), off, 64) << 32) |
+                           (uint32_t)__shfl_xor((int)(uint32_t)m, off, 64);
+        m = o > m ? o : m;
+      }
+      const uint32_t mye = (uint32_t)lane + 64u * bi;
+      const bool hold = b == m;
+      const uint32_t ee = wave_minmax_u32<false>(hold ? mye : 0xffffffffu);
+#pragma unroll
+      for (int i = 0; i < NS; i++) ks[i] = (mye == ee && bi == (uint32_t)i) ? 0ull : ks[i];
+      if (lane == 0) L.isel[p * 8 + r] = (int)ee;
+    }
+  }
+  __syncthreads();
+  {
+    // gates of (position p, rank r): softmax over the position's selected logits, or their
+    // sigmoid scores normalised over the selection
     const bool sig = c.router == PLD_ROUTER_SIGMOID_BIAS;
-    double* num = L.red;   // [topk <= 8]
-    if (tid_opaque() < c.topk) {
-      const double r = lk[2 * L.isel[p * 8 + tid_opaque()]];
-      num[tid_opaque()] = sig ? 1.0 / (1.0 + exp_f64(-r, L.dk)) : exp_f64(r - lk[2 * L.isel[p * 8]], L.dk);
+    double* num = lk + (size_t)VB * 2 * 256;   // [VB][8]
+    const int t = tid_opaque(), p = t / 8, r = t % 8;
+    if (p < nq && r < c.topk) {
+      const double* lkp = lk + (size_t)p * 2 * c.E;
+      const double x = lkp[2 * L.isel[p * 8 + r]];
+      num[t] = sig ? 1.0 / (1.0 + exp_f64(-x, L.dk)) : exp_f64(x - lkp[2 * L.isel[p * 8]], L.dk);
     }
     __syncthreads();
-    if (tid_opaque() < c.topk) {
+    if (p < nq && r < c.topk) {
       double gsum = 0.0;
-      for (int j = 0; j < c.topk; j++) gsum += num[j];
-      L.fgate[p * 8 + tid_opaque()] = (float)(num[tid_opaque()] / gsum);
+      for (int j = 0; j < c.topk; j++) gsum += num[p * 8 + j];
+      L.fgate[p * 8 + r] = (float)(num[t] / gsum);
     }
     __syncthreads();
   }

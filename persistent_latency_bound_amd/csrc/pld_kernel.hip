@@ -33,6 +33,7 @@
 #include <algorithm>
 #include <cmath>
 #include <new>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/pld.h"
@@ -97,7 +98,7 @@ struct WsOff {
   size_t status, x, q, kv, part, o, h2, logits, m, cqr, ckvr, qr, qlat, olat, amax, ixr, qi, ilist, isel, ll_end, sel,
       gates, spec, a_dbg, b_dbg, f_dbg, ikh, ikl, ilo, itok, kx, rope, layers, total;
   // batched verify (per-position copies of the LL buffers; vsel is a plain debug area)
-  size_t vx, vcqr, vckv, vqn, vqr, vqlat, vpart, volat, vo, vh2, vlog, vm, vfp, vamax, vsel, vf;
+  size_t vx, vcqr, vckv, vqn, vqr, vqlat, vpart, volat, vo, vh2, vss, vrp, vlog, vm, vfp, vamax, vsel, vf;
 };
 
 struct KArgs {
@@ -205,6 +206,10 @@ struct StPad {
 template <int PER, typename Idx = IdxLinear, typename St = StU32>
 __device__ __forceinline__ bool ll_fetch(Ctx& cx, uint32_t* dst, const uint64_t* src, int n, uint32_t ep, int wid,
                                          Idx idx = Idx{}, St store = St{}) {
+  // one bit per load in the pending masks: a 64-bit mask past 32 loads (a shift by 32 or
+  // more of a 32-bit value is undefined)
+  static_assert(PER >= 1 && PER <= 64, "loads per thread and round");
+  using Mask = typename std::conditional<(PER > 32), uint64_t, uint32_t>::type;
   int failed = 0;
   const int tid = tid_opaque();
   uint64_t t_in = 0;
@@ -216,9 +221,9 @@ __device__ __forceinline__ bool ll_fetch(Ctx& cx, uint32_t* dst, const uint64_t*
       const int i = base + j * BLOCK + tid;
       v[j] = i < n ? ld_u64_off(src, (uint32_t)idx(i) * 8u) : ll_word(0u, ep);
     }
-    uint32_t pend = 0;
+    Mask pend = 0;
 #pragma unroll
-    for (int j = 0; j < PER; j++) pend |= (uint32_t)((uint32_t)(v[j] >> 32) != ep) << j;
+    for (int j = 0; j < PER; j++) pend |= (Mask)((uint32_t)(v[j] >> 32) != ep) << j;
     if (pend && !failed) {
       const long long deadline = wall_clock64() + cx.budget;
       int it = 0;
@@ -229,9 +234,9 @@ __device__ __forceinline__ bool ll_fetch(Ctx& cx, uint32_t* dst, const uint64_t*
           if (pend >> j & 1u) v[j] = ld_u64_off(src, (uint32_t)idx(base + j * BLOCK + tid) * 8u);
         // (a mask of the words that arrived, built with shifts: constant masks ~(1 << j)
         // would be hoisted into registers that stay live across the whole kernel)
-        uint32_t got = 0;
+        Mask got = 0;
 #pragma unroll
-        for (int j = 0; j < PER; j++) got |= (uint32_t)((uint32_t)(v[j] >> 32) == ep) << j;
+        for (int j = 0; j < PER; j++) got |= (Mask)((uint32_t)(v[j] >> 32) == ep) << j;
         pend &= ~got;
         if ((++it & 15) == 0 && pend) {
           if (ld_u32(cx.status + ST_ABORT)) { failed = 1; break; }
@@ -1810,13 +1815,17 @@ WsOff layout(const KCfg& k, int n_layers) {
     o.volat = p; p += al(VBW * k.nh * k.kv_lora * W);
     o.vo = p; p += al(VBW * (k.nh * k.vdim / 2) * W);
     o.vh2 = p; p += al(VBW * k.H * W);
+    // partial sums over each W_O workgroup's rows (fp64 as two words): sum of h2^2 per
+    // position [nwg][VBW], then the router's gamma-weighted dot products [E][nwg][VBW]
+    o.vss = p; p += al((size_t)k.nwg * VBW * 2 * W);
+    o.vrp = p; p += al((size_t)k.E * k.nwg * VBW * 2 * W);
     o.vlog = p; p += al(VBW * 4 * k.E * W);
     o.vm = p; p += al((size_t)(k.vq * k.topk + k.nshared) * VBW * (k.inter / 2) * W);
     o.vfp = p; p += al((size_t)(k.vq * k.topk + k.nshared) * VBW * k.H * W);   // gated down partials
     o.vamax = p; p += al(VBW * 3 * k.nwg * W);
   } else {
-    o.vx = o.vcqr = o.vckv = o.vqn = o.vqr = o.vqlat = o.vpart = o.volat = o.vo = o.vh2 = o.vlog = o.vm = o.vfp =
-        o.vamax = 0;
+    o.vx = o.vcqr = o.vckv = o.vqn = o.vqr = o.vqlat = o.vpart = o.volat = o.vo = o.vh2 = o.vss = o.vrp = o.vlog =
+        o.vm = o.vfp = o.vamax = 0;
   }
   o.ll_end = p;
   if (k.vq >= 2) {
