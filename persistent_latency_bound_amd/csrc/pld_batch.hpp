@@ -38,6 +38,12 @@
 constexpr int VB = 8;                    // positions per batched step (max)
 constexpr int VACT_BYTES = 150528;       // LDS region for matrix-core operands / attention (147 KiB)
 constexpr int VPP = 2;                   // positions per attention pass over a chunk
+// Attention partial of one (position, head, chunk): LL words [m, l, 14 spare | acc as fp16
+// pairs]; the acc words start one 128-byte line after the row start and rows are whole
+// lines, so stores that cover 16 consecutive words write whole lines.
+constexpr int VP_ACC = 16;
+template <int KL>
+__host__ __device__ constexpr int vp_stride() { return KL / 2 + VP_ACC; }
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 
@@ -360,10 +366,13 @@ struct StRows {
   int dstride;
   __device__ __forceinline__ void operator()(uint32_t* dst, int i, uint32_t v) const { dst[(i / N) * dstride + i % N] = v; }
 };
+// (up to 24 loads per thread and round: each round is a full round trip, and the per-position
+// handoffs of up to 8 rows are several times larger than the single-position ones)
+constexpr int per_rows(int n) { return (n + BLOCK - 1) / BLOCK > 24 ? 24 : (n + BLOCK - 1) / BLOCK; }
 template <int N>
 __device__ __forceinline__ bool ll_fetch_rows(Ctx& cx, uint32_t* dst, int dstride, const uint64_t* src, int sstride,
                                               int nq, uint32_t ep, int wid) {
-  return ll_fetch<per_for(VB * N)>(cx, dst, src, nq * N, ep, wid, IdxRows<N>{sstride}, StRows<N>{dstride});
+  return ll_fetch<per_rows(VB * N)>(cx, dst, src, nq * N, ep, wid, IdxRows<N>{sstride}, StRows<N>{dstride});
 }
 
 // Sums over the workgroup of VB per-thread values at once (one pair of barriers); every
@@ -686,7 +695,19 @@ template <class SH, typename CRow>
 __device__ __forceinline__ bool new_rows(Ctx& cx, const KArgs& a, const DLayer& Ly, VLds& V, int nq, uint32_t k1,
                                          bool append, float* tmp, uint16_t* newr, CRow&& crow) {
   constexpr int LAT = SH::LAT, KL = SH::KL, RD = SH::RD;
+  constexpr int NE = (VB * (LAT / 2) + BLOCK - 1) / BLOCK;   // output pairs per thread
   const int tid = tid_opaque();
+  // this thread's RMSNorm weights (c_kv) or RoPE factors (k_r), loaded before the fetch so
+  // that they do not wait behind it
+  float f0[NE], f1[NE];
+#pragma unroll
+  for (int j = 0; j < NE; j++) {
+    const int e = min(tid + j * BLOCK, nq * (LAT / 2) - 1), p = e / (LAT / 2), k = 2 * (e % (LAT / 2));
+    const PLD_GLOBAL float* src = k < KL ? gp(Ly.kv_norm) + k
+                                         : gp(wsp<float>(a, a.off.rope)) + (size_t)V.rpos[p] * RD + (k - KL);
+    f0[j] = src[0];
+    f1[j] = src[1];
+  }
   if (!ll_fetch_rows<LAT>(cx, reinterpret_cast<uint32_t*>(tmp), LAT, vbuf(a, a.off.vckv, LAT, 0), LAT, nq, k1, W_KV))
     return false;
   double ss[VB];
@@ -697,22 +718,23 @@ __device__ __forceinline__ bool new_rows(Ctx& cx, const KArgs& a, const DLayer& 
       for (int i = tid; i < KL; i += BLOCK) ss[p] += (double)tmp[p * LAT + i] * (double)tmp[p * LAT + i];
   }
   block_sum_rows(ss, V.redv);
-  const PLD_GLOBAL float* gk = gp(Ly.kv_norm);
-  for (int e = tid; e < nq * (LAT / 2); e += BLOCK) {
+#pragma unroll
+  for (int p = 0; p < VB; p++) ss[p] = 1.0 / sqrt(ss[p] / (double)KL + a.c.eps);   // each row's norm scale
+#pragma unroll
+  for (int j = 0; j < NE; j++) {
+    const int e = tid + j * BLOCK;
+    if (e >= nq * (LAT / 2)) break;
     const int p = e / (LAT / 2), i = e % (LAT / 2), k = 2 * i;
     double r = 0.0;
 #pragma unroll
-    for (int q = 0; q < VB; q++) r = q == p ? ss[q] : r;
-    r = 1.0 / sqrt(r / (double)KL + a.c.eps);
+    for (int q = 0; q < VB; q++) r = q == p ? ss[q] : r;   // (ss[] holds the scales, below)
     const float* x = tmp + p * LAT;
     float v0, v1;
     if (k < KL) {
-      v0 = (float)(((double)x[k] * r) * (double)gk[k]);
-      v1 = (float)(((double)x[k + 1] * r) * (double)gk[k + 1]);
+      v0 = (float)(((double)x[k] * r) * (double)f0[j]);
+      v1 = (float)(((double)x[k + 1] * r) * (double)f1[j]);
     } else {
-      const int d = k - KL;
-      const PLD_GLOBAL float* rope = gp(wsp<float>(a, a.off.rope)) + (size_t)V.rpos[p] * RD;
-      const float x0 = x[k], x1 = x[k + 1], cs = rope[d], sg = rope[d + 1];
+      const float x0 = x[k], x1 = x[k + 1], cs = f0[j], sg = f1[j];
       v0 = x0 * cs - x1 * sg;
       v1 = x0 * sg + x1 * cs;
     }
@@ -804,7 +826,7 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
       }
     }
   };
-  constexpr int PSTR = KL / 2 + 2;
+  constexpr int PSTR = vp_stride<KL>();
   uint64_t* pll = wsp<uint64_t>(a, a.off.vpart);
   const size_t pwords = (size_t)SH::NH * nch * PSTR;   // words of one position's partials
   for (int p0 = 0; p0 < nq; p0 += shared ? VPP : 1) {
@@ -1024,7 +1046,7 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
             if ((ln & 1) == 0) {
               const uint32_t pr = (uint32_t)__half_as_ushort(__float2half_rn(O[j][t][q])) |
                                   ((uint32_t)__half_as_ushort(__float2half_rn(nb)) << 16);
-              ll_put(pp + ((size_t)(hbase + hh) * nch + ch) * PSTR + 2 + col / 2, pr, k1);
+              ll_put(pp + ((size_t)(hbase + hh) * nch + ch) * PSTR + VP_ACC + col / 2, pr, k1);
             }
           }
         }
@@ -1042,23 +1064,29 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
 // the groups of one chunk on one XCD). The A operand rows are (position, head) pairs, two
 // positions per 16-row tile (rows 8 (p & 1) + h of tile p >> 1), so every staged 32-row
 // sub-block serves all positions at once: S = Q C^T with wave w on tile (w >> 1, column
-// half w & 1) over all 36 k-steps, online softmax per row (half-wave hw holds row hw of each
-// tile), O += P C with wave w owning output columns [64 w, 64 w + 64) of all tiles. The last
-// chunk adds the new rows of the step (position p sees new rows 0..p) on the vector ALU.
-// Partials per (position, head, chunk) with NCV chunks.
+// half w & 1) over all 18 k-steps of 32, online softmax per row (8 lanes per row, four columns
+// each), O += P C with wave w owning output columns [64 w, 64 w + 64) of all tiles. The last
+// chunk adds the new rows of the step as one more sub-block with the causal mask (position p
+// sees new rows 0..p). Partials per (position, head, chunk) with NCV chunks.
 constexpr int VHG = 8;   // heads per workgroup in the verify attention
 template <class SH>
 __device__ __forceinline__ bool bstage_attn_v(Ctx& cx, const KArgs& a, const Step& st, VLds& V, int nq) {
   const KCfg& c = a.c;
   const DLayer Ly = *gp(st.Ly);
   const uint32_t k1 = st.k1;
-  constexpr int LAT = SH::LAT, KL = SH::KL, RD = SH::RD, TB = SH::TB, CSTR = SH::CSTR;
-  constexpr int KSTEPS = LAT / 16;
+  constexpr int LAT = SH::LAT, KL = SH::KL, RD = SH::RD, TB = SH::TB;
+  constexpr int CSTR = LAT + 8;   // LDS row stride (bf16): rows 16-byte aligned for the 16-byte operand reads
+  constexpr int KSTEPS = LAT / 32;
   constexpr int CPRW = LAT / 8;
   constexpr int NLD = (TB * CPRW + BLOCK - 1) / BLOCK;
   constexpr int MT = VB / 2;            // 16-row tiles of (position, head) rows
   constexpr int QW = KL / 2 + RD / 2;   // words of one (position, head) query row
   static_assert(KL == 512 && TB == 32 && SH::NH % VHG == 0 && NWAVES == 2 * MT, "the verify attention tiling");
+  static_assert(LAT % 32 == 0, "whole 32-wide k-steps");
+  // LDS: Qs, Cs, Ps, Ssc, alph, newr, ntmp, sn (below) inside the operand region
+  static_assert((MT * 16 + TB) * CSTR * 2 + MT * 16 * TB * 2 + (MT * 2 * 256 + MT * 16) * 4 + VB * LAT * 2 + LAT * 4 +
+                        MT * 16 * (VB + 2) * 4 <= VACT_BYTES,
+                "verify attention LDS");
   const int tid = tid_opaque();
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 15, lq = lane >> 4;
@@ -1080,13 +1108,6 @@ __device__ __forceinline__ bool bstage_attn_v(Ctx& cx, const KArgs& a, const Ste
   float* ntmp = reinterpret_cast<float*>(newr + VB * LAT);   // [LAT]
   float* sn = ntmp + LAT;                                    // [MT * 16][VB + 2] new-row scores, p, alpha
   const bool last = ch == nch - 1;
-  // the new rows of this step (last chunk): RMSNorm(c_kv') and RoPE(k_r'), bf16; appended by group 0
-  if (last) {
-    // (Cs is free until the first sub-block is staged)
-    if (!new_rows<SH>(cx, a, Ly, V, nq, k1, hg == 0, reinterpret_cast<float*>(Cs), newr,
-                      [&](int p) { return (size_t)V.rpos[p]; }))
-      return false;
-  }
   // sub-block staging: DEPTH register sets, loads issued DEPTH blocks ahead (static rows: L2)
   const int nsb = (n + TB - 1) / TB;
   constexpr int DEPTH = 2;
@@ -1138,35 +1159,45 @@ __device__ __forceinline__ bool bstage_attn_v(Ctx& cx, const KArgs& a, const Ste
                                           nq * VHG * QW, k1, W_QLAT, IdxQ{qlat_off, hbase}, StQ{}))
       return false;
   }
+  // the new rows of this step (last chunk): RMSNorm(c_kv') and RoPE(k_r'), bf16; appended by group 0
+  if (last) {
+    // (after the queries, which every chunk waits for: the new rows' input was published
+    // long before; Cs is free until the first sub-block is staged, and the first sub-blocks'
+    // loads, issued above, are in flight meanwhile)
+    if (!new_rows<SH>(cx, a, Ly, V, nq, k1, hg == 0, reinterpret_cast<float*>(Cs), newr,
+                      [&](int p) { return (size_t)V.rpos[p]; }))
+      return false;
+  }
   for (int i = tid; i < MT * 16 * TB; i += BLOCK) Ps[i] = 0;
   __syncthreads();
   stamp(a, cx, st, TR_ATT_READY);
   const float scale = 1.0f / sqrtf((float)(SH::ND + SH::RD));
-  // softmax state of half-wave hw = row hw of each tile
-  const int hw = tid >> 5, tl = lane & 31;
-  float m_run[MT], l_run[MT];
+  // softmax: thread t owns row R = t / 8 of the MT * 16 (position, head) rows and four of
+  // the sub-block's 32 columns; its row's running max and sum (the same in its 8 lanes)
+  const int srow = tid >> 3, scg = tid & 7, smi = srow >> 4, sr16 = srow & 15;
+  const int sprow = 2 * smi + (sr16 >= VHG ? 1 : 0);   // the row's position
+  float m_run = -INFINITY, l_run = 0.f;
   f32x4 O[MT][4];
 #pragma unroll
   for (int mi = 0; mi < MT; mi++) {
-    m_run[mi] = -INFINITY;
-    l_run[mi] = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; t++) O[mi][t] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   auto row_live = [&](int mi, int r16) { return 2 * mi + (r16 >= VHG ? 1 : 0) < nq; };
   auto block = [&](int tb0, bool causal) {
-    // S tile (mi, nt) of wave w: two accumulator chains over the 36 k-steps
+    // S tile (mi, nt) of wave w: two accumulator chains over the 18 k-steps of 32 (lane
+    // (ln, lq) supplies k = 8 lq .. 8 lq + 7 of its row for both operands)
     {
       const int mi = wave >> 1, nt = wave & 1;
       f32x4 s4 = {0.f, 0.f, 0.f, 0.f}, s5 = {0.f, 0.f, 0.f, 0.f};
       const uint16_t* Q = Qs + mi * 16 * CSTR;
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; kk++) {
-        const int k0 = kk * 16 + 4 * lq;
-        const bf16x4 av = *reinterpret_cast<const bf16x4*>(Q + ln * CSTR + k0);
-        const bf16x4 bv = *reinterpret_cast<const bf16x4*>(Cs + (nt * 16 + ln) * CSTR + k0);
-        if (kk & 1) s5 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, s5, 0, 0, 0);
-        else s4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, s4, 0, 0, 0);
+        const int k0 = kk * 32 + 8 * lq;
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(Q + ln * CSTR + k0);
+        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(Cs + (nt * 16 + ln) * CSTR + k0);
+        if (kk & 1) s5 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, s5, 0, 0, 0);
+        else s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, s4, 0, 0, 0);
       }
       s4 += s5;
       float* dst = Ssc + (mi * 2 + nt) * 256;
@@ -1174,21 +1205,36 @@ __device__ __forceinline__ bool bstage_attn_v(Ctx& cx, const KArgs& a, const Ste
       for (int q = 0; q < 4; q++) dst[(4 * lq + q) * 16 + ln] = s4[q];
     }
     __syncthreads();
-    // online softmax: row hw of tile mi, token tb0 + tl (causal: new row tl, seen by positions >= tl)
+    // online softmax of row srow over tokens tb0 + 4 scg .. + 3 (causal: new rows, row
+    // position p sees new rows 0..p); max and sum over the row's 8 lanes with DPP moves
+    {
+      const float4 sv = *reinterpret_cast<const float4*>(Ssc + (smi * 2 + (scg >> 2)) * 256 + sr16 * 16 + 4 * (scg & 3));
+      float sc[4] = {sv.x, sv.y, sv.z, sv.w};
+      float mb = -INFINITY;
 #pragma unroll
-    for (int mi = 0; mi < MT; mi++) {
-      float sc = -INFINITY;
-      const int prow = 2 * mi + (hw >= VHG ? 1 : 0);
-      const bool ok = causal ? (tl < nq && tl <= prow) : (tb0 + tl < n);
-      if (ok && prow < nq) sc = Ssc[(mi * 2 + (tl >> 4)) * 256 + hw * 16 + (tl & 15)] * scale;
-      const float mb = half_max_dpp(sc);
-      const float mnew = fmaxf(m_run[mi], mb);
-      const float al = m_run[mi] == -INFINITY ? 0.f : __expf(m_run[mi] - mnew);
-      const float pv = sc == -INFINITY ? 0.f : __expf(sc - mnew);
-      l_run[mi] = l_run[mi] * al + half_sum_dpp(pv);
-      m_run[mi] = mnew;
-      Ps[(mi * 16 + hw) * TB + tl] = (uint16_t)bf16_bits(pv);
-      if (tl == 0) alph[mi * 16 + hw] = al;
+      for (int c = 0; c < 4; c++) {
+        const int tl = 4 * scg + c;
+        const bool ok = (causal ? (tl < nq && tl <= sprow) : (tb0 + tl < n)) && sprow < nq;
+        sc[c] = ok ? sc[c] * scale : -INFINITY;
+        mb = fmaxf(mb, sc[c]);
+      }
+      mb = fmaxf(mb, dpp_mov<0xB1, 0xf, false>(mb));    // quad_perm [1,0,3,2]
+      mb = fmaxf(mb, dpp_mov<0x4E, 0xf, false>(mb));    // quad_perm [2,3,0,1]
+      mb = fmaxf(mb, dpp_mov<0x141, 0xf, false>(mb));   // row_half_mirror: max of 8
+      const float mnew = fmaxf(m_run, mb);
+      const float al = m_run == -INFINITY ? 0.f : __expf(m_run - mnew);
+      float ps = 0.f;
+      uint32_t pb[4];
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const float pv = sc[c] == -INFINITY ? 0.f : __expf(sc[c] - mnew);
+        ps += pv;
+        pb[c] = (uint32_t)(uint16_t)bf16_bits(pv);
+      }
+      l_run = l_run * al + dpp_sum<8>(ps);
+      m_run = mnew;
+      *reinterpret_cast<uint2*>(Ps + srow * TB + 4 * scg) = make_uint2(pb[0] | (pb[1] << 16), pb[2] | (pb[3] << 16));
+      if (scg == 0) alph[srow] = al;
     }
     __syncthreads();
     // O = alpha O + P C: wave owns columns [wave*64, +64) of every tile
@@ -1233,8 +1279,7 @@ __device__ __forceinline__ bool bstage_attn_v(Ctx& cx, const KArgs& a, const Ste
           const int idx = tid + i * BLOCK;
           if (idx < TB * CPRW) {
             const int r = idx / CPRW, k = idx % CPRW;
-            uint32_t* dd = reinterpret_cast<uint32_t*>(Cs + r * CSTR + k * 8);
-            dd[0] = cb[d][i].x; dd[1] = cb[d][i].y; dd[2] = cb[d][i].z; dd[3] = cb[d][i].w;
+            *reinterpret_cast<uint4*>(Cs + r * CSTR + k * 8) = cb[d][i];   // (16-byte aligned rows)
           }
         }
       } else {
@@ -1252,32 +1297,34 @@ __device__ __forceinline__ bool bstage_attn_v(Ctx& cx, const KArgs& a, const Ste
   __syncthreads();
   stamp(a, cx, st, 17);
   stamp(a, cx, st, TR_ATT_SOFTMAX);
-  // partials: LL words [m, l, acc as fp16 pairs] of (position p, head hbase + h, chunk)
-  constexpr int PSTR = KL / 2 + 2;
+  // partials of (position p, head hbase + h, chunk), whole 128-byte lines per store
+  // instruction: the (m, l) line from the row's 8 lanes (m, l, then zeros), and the acc words
+  // of a tile pair (2u, 2u + 1) as 16 consecutive words per row: the even lanes of a row
+  // write tile 2u's pairs (columns ln, ln + 1), the odd lanes tile 2u + 1's (ln - 1, ln)
+  constexpr int PSTR = vp_stride<KL>();
   const size_t pwords = (size_t)SH::NH * c.cpg * PSTR;   // per-position stride of the partial buffer
   uint64_t* pll = wsp<uint64_t>(a, a.off.vpart);
-#pragma unroll
-  for (int mi = 0; mi < MT; mi++) {
-    const int p = 2 * mi + (hw >= VHG ? 1 : 0);
-    if (tl == 0 && p < nq) {
-      uint64_t* q = pll + (size_t)p * pwords + ((size_t)(hbase + (hw & (VHG - 1))) * nch + ch) * PSTR;
-      ll_put_f32(q, m_run[mi], k1);
-      ll_put_f32(q + 1, l_run[mi], k1);
-    }
+  if (sprow < nq) {
+    uint64_t* q = pll + (size_t)sprow * pwords + ((size_t)(hbase + (sr16 & (VHG - 1))) * nch + ch) * PSTR + 2 * scg;
+    ll_put_f32(q, scg == 0 ? m_run : 0.f, k1);
+    ll_put_f32(q + 1, scg == 0 ? l_run : 0.f, k1);
   }
+  const bool ev = (ln & 1) == 0;
 #pragma unroll
   for (int mi = 0; mi < MT; mi++) {
 #pragma unroll
-    for (int t = 0; t < 4; t++) {
-      const int col = (wave * 4 + t) * 16 + ln;
+    for (int u = 0; u < 2; u++) {
 #pragma unroll
       for (int q = 0; q < 4; q++) {
-        const float nb = dpp_mov<0xB1, 0xf, false>(O[mi][t][q]);
+        const float a0 = O[mi][2 * u][q], a1 = O[mi][2 * u + 1][q];
+        const float n0 = dpp_mov<0xB1, 0xf, false>(a0), n1 = dpp_mov<0xB1, 0xf, false>(a1);   // lane ln ^ 1
+        const float lo = ev ? a0 : n1, hi = ev ? n0 : a1;
         const int r16 = 4 * lq + q, p = 2 * mi + (r16 >= VHG ? 1 : 0), h = r16 & (VHG - 1);
-        if ((ln & 1) == 0 && p < nq) {
-          const uint32_t pr = (uint32_t)__half_as_ushort(__float2half_rn(O[mi][t][q])) |
-                              ((uint32_t)__half_as_ushort(__float2half_rn(nb)) << 16);
-          ll_put(pll + (size_t)p * pwords + ((size_t)(hbase + h) * nch + ch) * PSTR + 2 + col / 2, pr, k1);
+        if (p < nq) {
+          const uint32_t pr = (uint32_t)__half_as_ushort(__float2half_rn(lo)) |
+                              ((uint32_t)__half_as_ushort(__float2half_rn(hi)) << 16);
+          const int word = (wave * 4 + 2 * u) * 8 + (ev ? 0 : 8) + (ln >> 1);
+          ll_put(pll + (size_t)p * pwords + ((size_t)(hbase + h) * nch + ch) * PSTR + VP_ACC + word, pr, k1);
         }
       }
     }
@@ -1288,18 +1335,20 @@ __device__ __forceinline__ bool bstage_attn_v(Ctx& cx, const KArgs& a, const Ste
 
 // ------------------------------------------------------------------ BM: merge, per position
 // Workgroup (head h, cpw columns) as in the single-position stage; the partials of MG
-// positions are fetched together (one LL fetch), then wave p (< MG) forms position p's
+// positions (all eight when they fit in LDS, else four) are fetched together (one LL
+// fetch), then wave p (< MG) forms position p's
 // chunk weights and thread (p, column) sums the chunks.
 template <class SH>
 __device__ __forceinline__ bool bstage_merge(Ctx& cx, const KArgs& a, const Step& st, VLds& V, int nq) {
   const KCfg& c = a.c;
-  constexpr int KL = SH::KL, MG = 4;
+  constexpr int KL = SH::KL;
   // chunks per head: the verify attention (8 heads per workgroup) or the per-row one (HPW)
   const int nch = a.bmode == 0 ? cx.nwg / (SH::NH / VHG) : c.cpg, cpw = c.cpw;
+  const int MG = (size_t)NWAVES * (nch * (cpw + 3) + 1) * 4 <= (size_t)VACT_BYTES ? NWAVES : NWAVES / 2;
   const int h = (cx.w * cpw) / KL, c0 = (cx.w * cpw) % KL;
   const int tid = tid_opaque();
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr int PSTR = KL / 2 + 2;
+  constexpr int PSTR = vp_stride<KL>();
   const int cpw2 = cpw / 2, nacc = nch * cpw, naw = nch * cpw2;
   const int per = naw + 2 * nch;                 // words of one position
   const int pwords = SH::NH * c.cpg * PSTR;      // LL words of one position's partials (stride)
@@ -1309,7 +1358,7 @@ __device__ __forceinline__ bool bstage_merge(Ctx& cx, const KArgs& a, const Step
     int per, naw, cpw2, nch, h, c0, pwords;
     __device__ __forceinline__ int operator()(int i) const {
       const int q = i / per, k = i % per;
-      if (k < naw) return q * pwords + (h * nch + k / cpw2) * PSTR + 2 + c0 / 2 + k % cpw2;
+      if (k < naw) return q * pwords + (h * nch + k / cpw2) * PSTR + VP_ACC + c0 / 2 + k % cpw2;
       const int j = k - naw;
       return q * pwords + (h * nch + (j >> 1)) * PSTR + (j & 1);
     }
@@ -1333,7 +1382,7 @@ __device__ __forceinline__ bool bstage_merge(Ctx& cx, const KArgs& a, const Step
   stamp(a, cx, st, TR_MERGE_START);
   for (int p0 = 0; p0 < nq; p0 += MG) {
     const int np = min(MG, nq - p0);
-    if (!ll_fetch<16>(cx, reinterpret_cast<uint32_t*>(base), wsp<uint64_t>(a, a.off.vpart) + (size_t)p0 * pwords,
+    if (!ll_fetch<24>(cx, reinterpret_cast<uint32_t*>(base), wsp<uint64_t>(a, a.off.vpart) + (size_t)p0 * pwords,
                       np * per, st.k1, W_PART, IdxM{per, naw, cpw2, nch, h, c0, pwords}, StM{per, naw, fstr}))
       return false;
     if (p0 == 0) stamp(a, cx, st, TR_MERGE_COPIED);
@@ -1610,6 +1659,7 @@ __device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& 
   if (!ll_fetch<per_for(VB * 4 * 256)>(cx, reinterpret_cast<uint32_t*>(lk), vbuf(a, a.off.vlog, 4 * (size_t)c.E, 0),
                                        nq * 4 * c.E, k1, W_RT))
     return false;
+  stamp(a, cx, st, TR_RT_READY);
   if ((tid_opaque() >> 6) < nq) {
     const int lane = tid_opaque() & 63, p = tid_opaque() >> 6;
     const double* lkp = lk + (size_t)p * 2 * c.E;
@@ -1665,26 +1715,38 @@ __device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& 
     }
     __syncthreads();
   }
-  // union of the selected experts, ascending (thread e tests expert e), slots after the shared ones
+  stamp(a, cx, st, TR_TOPK);
+  // union of the selected experts, ascending, slots after the shared ones: thread (p, r) sets
+  // bit p of its expert's mask (LDS atomic OR: the result does not depend on the order),
+  // then thread e places expert e by a ballot count over the lower experts
   {
-    int* flag = reinterpret_cast<int*>(tmp);   // [E] position masks, then the prefix scan
-    for (int e = tid_opaque(); e < c.E; e += BLOCK) flag[e] = 0;
+    static_assert(BLOCK >= 256, "one thread per expert");
+    int* flag = reinterpret_cast<int*>(tmp);   // [E] position masks
+    int* wcnt = flag + 256;                     // [NWAVES] experts in use per wave
+    const int tid = tid_opaque(), lane = tid & 63, wave = tid >> 6;
+    for (int e = tid; e < c.E; e += BLOCK) flag[e] = 0;
     __syncthreads();
-    if (tid_opaque() == 0) {
-      for (int p = 0; p < nq; p++)
-        for (int r = 0; r < c.topk; r++) flag[L.isel[p * 8 + r]] |= 1 << p;
-      int u = 0;
-      for (int e = 0; e < c.E; e++)
-        if (flag[e]) {
-          L.uexp[ns + u] = e;
-          L.umask[ns + u] = flag[e];
-          u++;
-        }
-      for (int s = 0; s < ns; s++) {
-        L.uexp[s] = c.E + s;
-        L.umask[s] = (1 << nq) - 1;
-      }
-      L.misc[0] = ns + u;
+    if (tid < nq * 8 && (tid & 7) < c.topk) atomicOr(&flag[L.isel[tid]], 1 << (tid >> 3));
+    __syncthreads();
+    const int fe = tid < c.E ? flag[tid] : 0;
+    const uint64_t on = __ballot(fe != 0);
+    if (lane == 0) wcnt[wave] = __popcll(on);
+    __syncthreads();
+    int off = 0;
+    for (int v = 0; v < wave; v++) off += wcnt[v];
+    if (fe != 0) {
+      const int u = off + __popcll(on & ((1ull << lane) - 1ull));
+      L.uexp[ns + u] = tid;
+      L.umask[ns + u] = fe;
+    }
+    if (tid < ns) {
+      L.uexp[tid] = c.E + tid;
+      L.umask[tid] = (1 << nq) - 1;
+    }
+    if (tid == 0) {
+      int tot = 0;
+      for (int v = 0; v < NWAVES; v++) tot += wcnt[v];
+      L.misc[0] = ns + tot;
     }
     __syncthreads();
   }

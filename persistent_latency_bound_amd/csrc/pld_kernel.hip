@@ -1811,7 +1811,7 @@ WsOff layout(const KCfg& k, int n_layers) {
     o.vqn = p; p += al(VBW * k.nh * k.nope * W);
     o.vqr = p; p += al(VBW * (k.nh * k.rope / 2) * W);
     o.vqlat = p; p += al(VBW * (k.nh * k.kv_lora / 2) * W);
-    o.vpart = p; p += al(VBW * k.nh * k.cpg * (k.kv_lora / 2 + 2) * W);
+    o.vpart = p; p += al(VBW * k.nh * k.cpg * (k.kv_lora / 2 + VP_ACC) * W);   // [m, l, spare | acc] rows of whole lines
     o.volat = p; p += al(VBW * k.nh * k.kv_lora * W);
     o.vo = p; p += al(VBW * (k.nh * k.vdim / 2) * W);
     o.vh2 = p; p += al(VBW * k.H * W);
