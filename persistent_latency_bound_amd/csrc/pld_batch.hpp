@@ -1191,13 +1191,15 @@ __device__ __forceinline__ bool bstage_attn_v(Ctx& cx, const KArgs& a, const Ste
       const int mi = wave >> 1, nt = wave & 1;
       f32x4 s4 = {0.f, 0.f, 0.f, 0.f}, s5 = {0.f, 0.f, 0.f, 0.f};
       const uint16_t* Q = Qs + mi * 16 * CSTR;
+      if (2 * mi < nq) {   // (a tile with no live row is masked by the softmax: not computed)
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; kk++) {
-        const int k0 = kk * 32 + 8 * lq;
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(Q + ln * CSTR + k0);
-        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(Cs + (nt * 16 + ln) * CSTR + k0);
-        if (kk & 1) s5 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, s5, 0, 0, 0);
-        else s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, s4, 0, 0, 0);
+        for (int kk = 0; kk < KSTEPS; kk++) {
+          const int k0 = kk * 32 + 8 * lq;
+          const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(Q + ln * CSTR + k0);
+          const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(Cs + (nt * 16 + ln) * CSTR + k0);
+          if (kk & 1) s5 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, s5, 0, 0, 0);
+          else s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, s4, 0, 0, 0);
+        }
       }
       s4 += s5;
       float* dst = Ssc + (mi * 2 + nt) * 256;
@@ -1237,31 +1239,36 @@ __device__ __forceinline__ bool bstage_attn_v(Ctx& cx, const KArgs& a, const Ste
       if (scg == 0) alph[srow] = al;
     }
     __syncthreads();
-    // O = alpha O + P C: wave owns columns [wave*64, +64) of every tile
+    // O = alpha O + P C: wave owns columns [wave*64, +64) of every tile, one 16x16x32 product
+    // per (tile, column tile) over the sub-block's 32 rows (lane (ln, lq) supplies rows
+    // 8 lq .. 8 lq + 7 of both operands); tiles with no live row (positions >= nq) are skipped
 #pragma unroll
     for (int mi = 0; mi < MT; mi++) {
-      float fa[4];
+      if (2 * mi < nq) {
+        float fa[4];
 #pragma unroll
-      for (int q = 0; q < 4; q++) fa[q] = alph[mi * 16 + 4 * lq + q];
+        for (int q = 0; q < 4; q++) fa[q] = alph[mi * 16 + 4 * lq + q];
 #pragma unroll
-      for (int t = 0; t < 4; t++)
+        for (int t = 0; t < 4; t++)
 #pragma unroll
-        for (int q = 0; q < 4; q++) O[mi][t][q] *= fa[q];
-    }
-#pragma unroll
-    for (int ks = 0; ks < TB / 16; ks++) {
-#pragma unroll
-      for (int t = 0; t < 4; t++) {
-        const int col = (wave * 4 + t) * 16 + ln;
-        bf16x4 bv;
-#pragma unroll
-        for (int q = 0; q < 4; q++) bv[q] = (short)Cs[(ks * 16 + 4 * lq + q) * CSTR + col];
-#pragma unroll
-        for (int mi = 0; mi < MT; mi++) {
-          const bf16x4 av = *reinterpret_cast<const bf16x4*>(Ps + (mi * 16 + ln) * TB + ks * 16 + 4 * lq);
-          O[mi][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, O[mi][t], 0, 0, 0);
-        }
+          for (int q = 0; q < 4; q++) O[mi][t][q] *= fa[q];
       }
+    }
+    static_assert(TB == 32, "one 32-deep product per sub-block");
+    bf16x8_t av[MT];
+#pragma unroll
+    for (int mi = 0; mi < MT; mi++) av[mi] = *reinterpret_cast<const bf16x8_t*>(Ps + (mi * 16 + ln) * TB + 8 * lq);
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      const int col = (wave * 4 + t) * 16 + ln;
+      uint32_t bw[4];
+#pragma unroll
+      for (int q = 0; q < 4; q++)
+        bw[q] = (uint32_t)Cs[(8 * lq + 2 * q) * CSTR + col] | ((uint32_t)Cs[(8 * lq + 2 * q + 1) * CSTR + col] << 16);
+      const bf16x8_t bv = __builtin_bit_cast(bf16x8_t, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+#pragma unroll
+      for (int mi = 0; mi < MT; mi++)
+        if (2 * mi < nq) O[mi][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[mi], bv, O[mi][t], 0, 0, 0);
     }
   };
   // the history sub-blocks, then (last chunk) the new rows of the step as one more sub-block
