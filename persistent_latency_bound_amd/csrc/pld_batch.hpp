@@ -38,12 +38,6 @@
 constexpr int VB = 8;                    // positions per batched step (max)
 constexpr int VACT_BYTES = 150528;       // LDS region for matrix-core operands / attention (147 KiB)
 constexpr int VPP = 2;                   // positions per attention pass over a chunk
-// Attention partial of one (position, head, chunk): LL words [m, l, 14 spare | acc as fp16
-// pairs]; the acc words start one 128-byte line after the row start and rows are whole
-// lines, so stores that cover 16 consecutive words write whole lines.
-constexpr int VP_ACC = 16;
-template <int KL>
-__host__ __device__ constexpr int vp_stride() { return KL / 2 + VP_ACC; }
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 

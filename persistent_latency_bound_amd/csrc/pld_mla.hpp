@@ -47,6 +47,15 @@ __device__ __forceinline__ uint4 ld_coh16(const void* p) {
 // The sparse layer accumulates these rows in fp64: c_q' feeds the indexer's selection,
 // an integer result, so it travels as fp64 (two LL words per value) and the indexer head
 // weights w and key k_I are rounded to fp32 once, from fp64 sums.
+// Attention partial of one (head, chunk) (and position, in the batched path): LL words
+// [m, l, 14 spare | acc as fp16 pairs]; the acc words start one 128-byte line after the row
+// start and rows are whole lines, so stores that cover 16 consecutive words write whole lines
+// (8-byte stores of half a line each from every workgroup at once were twice as many partial
+// line writes).
+constexpr int VP_ACC = 16;
+template <int KL>
+__host__ __device__ constexpr int vp_stride() { return KL / 2 + VP_ACC; }
+
 template <class SH>
 __device__ __forceinline__ bool stage_x_mla(Ctx& cx, const KArgs& a, const Step& st, Lds& L) {
   const DLayer Ly = *gp(st.Ly);
@@ -1446,29 +1455,36 @@ __device__ __forceinline__ bool stage_attn_mla(Ctx& cx, const KArgs& a, const St
     }
   }
   stamp(a, cx, st, TR_ATT_SOFTMAX);
-  // publish the partial of each head: LL words [m, l, acc as fp16 pairs] at
+  // publish the partial of each head: LL words [m, l, spare | acc as fp16 pairs] at
   // ((h * nch) + ch) * PSTR (fp16 keeps the merged result at fp32 accuracy here: the
   // partial sums stay far inside its range, and the error is set by the bf16 P operand)
-  constexpr int PSTR = KL / 2 + 2;
+  constexpr int PSTR = vp_stride<KL>();
   vm_wait();   // the cache row appended above is visible before this workgroup's next publication
   __syncthreads();
   uint64_t* pll = wsp<uint64_t>(a, a.off.part);
-  if ((lane & 31) == 0 && (HS == 2 || lane == 0)) {
-    uint64_t* p = pll + ((size_t)(hbase + hown) * nch + ch) * PSTR;
-    ll_put_f32(p, m_run, k1);
-    ll_put_f32(p + 1, l_run, k1);
+  // (m, l) line of head hown: 8 lanes write words 2 j, 2 j + 1 (m, l, then zeros)
+  if ((lane & 31) < 8 && (HS == 2 || lane < 8)) {
+    const int j = lane & 7;
+    uint64_t* p = pll + ((size_t)(hbase + hown) * nch + ch) * PSTR + 2 * j;
+    ll_put_f32(p, j == 0 ? m_run : 0.f, k1);
+    ll_put_f32(p + 1, j == 0 ? l_run : 0.f, k1);
   }
+  // acc of a tile pair (2u, 2u + 1) as 16 consecutive words per head: the even lanes write
+  // tile 2u's pairs (columns ln, ln + 1), the odd lanes tile 2u + 1's (ln - 1, ln)
+  const bool ev = (ln & 1) == 0;
 #pragma unroll
-  for (int t = 0; t < 4; t++) {
-    const int col = (wave * 4 + t) * 16 + ln;   // even lanes publish columns (col, col + 1)
+  for (int u = 0; u < 2; u++) {
 #pragma unroll
     for (int q = 0; q < 4; q++) {
-      const float nb = dpp_mov<0xB1, 0xf, false>(O[t][q]);   // the odd neighbour's value
+      const float a0 = O[2 * u][q], a1 = O[2 * u + 1][q];
+      const float n0 = dpp_mov<0xB1, 0xf, false>(a0), n1 = dpp_mov<0xB1, 0xf, false>(a1);   // lane ln ^ 1
+      const float lo = ev ? a0 : n1, hi = ev ? n0 : a1;
       const int h = 4 * lq + q;
-      if (h < HPW && (ln & 1) == 0) {
-        const uint32_t pr = (uint32_t)__half_as_ushort(__float2half_rn(O[t][q])) |
-                            ((uint32_t)__half_as_ushort(__float2half_rn(nb)) << 16);
-        ll_put(pll + ((size_t)(hbase + h) * nch + ch) * PSTR + 2 + col / 2, pr, k1);
+      if (h < HPW) {
+        const uint32_t pr = (uint32_t)__half_as_ushort(__float2half_rn(lo)) |
+                            ((uint32_t)__half_as_ushort(__float2half_rn(hi)) << 16);
+        const int word = (wave * 4 + 2 * u) * 8 + (ev ? 0 : 8) + (ln >> 1);
+        ll_put(pll + ((size_t)(hbase + h) * nch + ch) * PSTR + VP_ACC + word, pr, k1);
       }
     }
   }
@@ -1485,12 +1501,12 @@ __device__ __forceinline__ bool stage_merge_mla(Ctx& cx, const KArgs& a, const S
   const int h = (cx.w * cpw) / KL, c0 = (cx.w * cpw) % KL;
   const int tid = tid_opaque();
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  constexpr int PSTR = KL / 2 + 2;
+  constexpr int PSTR = vp_stride<KL>();
   const int cpw2 = cpw / 2;             // fp16-pair words per chunk
   const int nacc = nch * cpw;           // floats
   const int naw = nch * cpw2;           // their words
   auto pidx = [=](int i) -> int {
-    if (i < naw) return (h * nch + i / cpw2) * PSTR + 2 + c0 / 2 + i % cpw2;
+    if (i < naw) return (h * nch + i / cpw2) * PSTR + VP_ACC + c0 / 2 + i % cpw2;
     const int j = i - naw;
     return (h * nch + (j >> 1)) * PSTR + (j & 1);
   };
