@@ -288,13 +288,14 @@ struct VLds {
   MSeg* segs;      // [MAX_MSEGS]
   uint64_t* tr;    // [TR_SLOTS]
   double* dk;      // [16]
+  double* vnorm;   // [VB]          FFN norm scale of each position (W_O stage -> FFN stage)
   uint32_t* stage; // [3 * 1024]    LL staging for the head's inputs (aliases nothing live)
 };
 constexpr int VOUT_FLOATS = VB * 64;
 __host__ __device__ inline size_t vlds_bytes() {
   return (size_t)VACT_BYTES + 4 * (VOUT_FLOATS + 8 * 16 * VB + 3 * VB * 32) + 8 * 16 + 8 * NWAVES * VB + 4 * (VB * 8) * 2 +
          4 * 2 * (VB * 8 + 4) + 4 * 16 + 4 * 2 * VB + 4 * VB + 4 * 3 * (MAX_MSEGS / 2) + 4 * 32 + sizeof(MSeg) * MAX_MSEGS +
-         8 * TR_SLOTS + 8 * 16;
+         8 * TR_SLOTS + 8 * 16 + 8 * VB;
 }
 __device__ __forceinline__ VLds vcarve(float* base) {
   VLds L;
@@ -318,7 +319,8 @@ __device__ __forceinline__ VLds vcarve(float* base) {
   L.vsrc = reinterpret_cast<int*>(p); p += 4 * 32;
   L.segs = reinterpret_cast<MSeg*>(p); p += sizeof(MSeg) * MAX_MSEGS;
   L.tr = reinterpret_cast<uint64_t*>(p); p += 8 * TR_SLOTS;
-  L.dk = reinterpret_cast<double*>(p);
+  L.dk = reinterpret_cast<double*>(p); p += 8 * 16;
+  L.vnorm = reinterpret_cast<double*>(p);
   L.stage = reinterpret_cast<uint32_t*>(reinterpret_cast<char*>(base) + 98432);   // inside A, past 8 rows of K = 6144
   return L;
 }
@@ -1546,6 +1548,39 @@ __device__ __forceinline__ bool bstage_wo(Ctx& cx, const KArgs& a, const Step& s
     }
   }
   stamp(a, cx, st, TR_WO_DONE);
+  // The FFN norm scale of every position, r_p = 1 / sqrt(sum(h2_p^2) / H + eps), from all
+  // workgroups' sums (fetched while the router sums above were formed; added in a fixed
+  // order: lane sums in producer order, then the wave's tree). It stays in LDS (vnorm) for
+  // the FFN stage. Then this workgroup's rows of the FFN operand, bf16(fp32((h2 * r_p) *
+  // gamma)), go out as LL words of bf16 pairs: the consumers fetch half the words of fp32 h2
+  // and no longer normalise.
+  {
+    struct IdxS {
+      int nq2;
+      __device__ __forceinline__ int operator()(int i) const { return (i / nq2) * (VB * 2) + i % nq2; }
+    };
+    const double* pd = rpl + 2 * 256 * VB;   // [nwg][nq] (fetched fp64 pairs)
+    if (!ll_fetch<per_for(256 * VB * 2)>(cx, reinterpret_cast<uint32_t*>(const_cast<double*>(pd)),
+                                         wsp<uint64_t>(a, a.off.vss), cx.nwg * nq * 2, st.k1, W_H2, IdxS{nq * 2}))
+      return false;
+    const int lane = tid & 63, wave = tid >> 6;
+    if (wave < nq) {
+      double q = 0.0;
+      for (int k = lane; k < cx.nwg; k += 64) q += pd[k * nq + wave];
+      q = wave_sum_any(q);
+      if (lane == 0) L.vnorm[wave] = 1.0 / sqrt(q / (double)SH::H + c.eps);
+    }
+    if (tid < 32) reinterpret_cast<float*>(gh)[tid] = gr;   // gamma of this workgroup's rows (gh is free)
+    __syncthreads();
+    const float* gw = reinterpret_cast<const float*>(gh);
+    for (int i = tid; i < nq * (nr / 2); i += BLOCK) {
+      const int p = i / (nr / 2), j = 2 * (i % (nr / 2));
+      const double r = L.vnorm[p];
+      const float y0 = (float)(((double)L.h2res[p * 32 + j] * r) * (double)gw[j]);
+      const float y1 = (float)(((double)L.h2res[p * 32 + j + 1] * r) * (double)gw[j + 1]);
+      ll_put(vbuf(a, a.off.vhn, SH::H / 2, p) + (r0 + j) / 2, f32_to_bf16(y0) | (f32_to_bf16(y1) << 16), st.k1);
+    }
+  }
   return true;
 }
 
@@ -1558,9 +1593,7 @@ __device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& 
   const uint32_t k1 = st.k1;
   constexpr int H = SH::H, AST = vb_astr(H), INTER = SH::INTER;
   static_assert(SH::MOE && SH::FP8, "the batched FFN is the FP8 MoE one");
-  float* tmp = reinterpret_cast<float*>(L.A + VB * AST);   // [H] norm weights, then [nq][E][2] logits, keys
-  RegPairs<H> gmf;
-  gmf.load(Ly.ffn_norm);
+  float* tmp = reinterpret_cast<float*>(L.A + VB * AST);   // router sums, then [nq][E][2] logits, keys
   float rbias = 0.f;
   if (w < c.E && c.router == PLD_ROUTER_SIGMOID_BIAS) rbias = gp(Ly.router_bias)[w];
   const int ns = c.nshared;
@@ -1576,55 +1609,19 @@ __device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& 
              (2 * s + 1) * nj, nq);
   }
   __syncthreads();
-  double* rnorm = L.redv;   // [VB] the FFN norm's scale 1 / rms(h2_p)
   auto pre = [&]() -> bool {
     const int tid = tid_opaque(), lane = tid & 63, wave = tid >> 6;
-    // the norm weights into LDS (visible after the fetch's closing barrier)
-#pragma unroll
-    for (int k = 0; k < RegPairs<H>::K; k++) {
-      const int j = tid + k * BLOCK;
-      if ((H / 2) % BLOCK == 0 || j < H / 2) reinterpret_cast<float2*>(tmp)[j] = gmf.v[k];
-    }
-    // the W_O workgroups' partial sums: words k < 2 nq of each producer's 16-word line
-    struct IdxP {
-      int nq2;
-      __device__ __forceinline__ int operator()(int i) const { return (i / nq2) * (VB * 2) + i % nq2; }
-    };
-    const double* pd = reinterpret_cast<const double*>(L.A);   // [nwg][nq] (fetched fp64 pairs)
-    // (1) the norm statistics -> wave p: position p's scale, the producers' sums added in a
-    // fixed order (lane sums in producer order, then the wave's tree)
-    if (!ll_fetch<per_for(256 * VB * 2)>(cx, reinterpret_cast<uint32_t*>(L.A), wsp<uint64_t>(a, a.off.vss),
-                                         nwg * nq * 2, k1, W_H2, IdxP{nq * 2}))
-      return false;
-    if (wave < nq) {
-      double q = 0.0;
-      for (int k = lane; k < nwg; k += 64) q += pd[k * nq + wave];
-      q = wave_sum_any(q);
-      if (lane == 0) rnorm[wave] = 1.0 / sqrt(q / (double)H + c.eps);
-    }
-    __syncthreads();
-    // (2) h2 of every position, normalised as it arrives: bf16(fp32((h2 * r_p) * gamma))
-    struct StNorm {
-      uint16_t* A;
-      const double* r;
-      const float* g;
-      __device__ __forceinline__ void operator()(uint32_t*, int i, uint32_t v) const {
-        const int p = i / H, col = i - p * H;
-        const float y = (float)(((double)__uint_as_float(v) * r[p]) * (double)g[col]);
-        A[p * AST + col] = (uint16_t)f32_to_bf16(y);
-      }
-    };
-    // (24 loads per thread and round: three rounds for six positions; more loads in flight
-    // would spill registers here)
-    if (!ll_fetch<24>(cx, nullptr, vbuf(a, a.off.vh2, H, 0), nq * H, k1, W_H2, IdxLinear{},
-                      StNorm{L.A, rnorm, tmp}))
-      return false;
-    // (3) router workgroups: expert w's logit of every position from the producers' router
-    // sums (fixed order as above) times the norm scale; published as four LL words (logit
-    // lo, hi, key lo, hi) per position
+    // (1) router workgroups: expert w's logit of every position from the W_O workgroups'
+    // router sums (words k < 2 nq of each producer's 16-word line, added in a fixed order:
+    // lane sums in producer order, then the wave's tree) times the norm scale; published as
+    // four LL words (logit lo, hi, key lo, hi) per position
     if (w < c.E) {
-      double* rd = reinterpret_cast<double*>(tmp + H);   // [nwg][nq] (fetched fp64 pairs; past the norm weights)
-      if (!ll_fetch<per_for(256 * VB * 2)>(cx, reinterpret_cast<uint32_t*>(rd),
+      struct IdxP {
+        int nq2;
+        __device__ __forceinline__ int operator()(int i) const { return (i / nq2) * (VB * 2) + i % nq2; }
+      };
+      const double* rd = reinterpret_cast<const double*>(tmp);   // [nwg][nq] (fetched fp64 pairs)
+      if (!ll_fetch<per_for(256 * VB * 2)>(cx, reinterpret_cast<uint32_t*>(tmp),
                                            wsp<uint64_t>(a, a.off.vrp) + (size_t)w * nwg * VB * 2, nwg * nq * 2, k1,
                                            W_H2, IdxP{nq * 2}))
         return false;
@@ -1632,7 +1629,7 @@ __device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& 
         double d = 0.0;
         for (int k = lane; k < nwg; k += 64) d += rd[k * nq + wave];
         d = wave_sum_any(d);
-        const double sp = rnorm[wave] * d;
+        const double sp = L.vnorm[wave] * d;
         if (lane < 4) {
           const double key = c.router == PLD_ROUTER_SIGMOID_BIAS ? (1.0 / (1.0 + exp_f64(-sp, L.dk))) + (double)rbias : sp;
           const uint64_t bits = (uint64_t)__double_as_longlong(lane < 2 ? sp : key);
@@ -1640,6 +1637,10 @@ __device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& 
         }
       }
     }
+    // (2) the FFN operand rows, normalised by their W_O workgroups (bf16 pairs)
+    if (!ll_fetch_rows<H / 2>(cx, reinterpret_cast<uint32_t*>(L.A), AST / 2, vbuf(a, a.off.vhn, H / 2, 0), H / 2, nq, k1,
+                              W_H2))
+      return false;
     stamp(a, cx, st, TR_H2_READY);
     return true;
   };

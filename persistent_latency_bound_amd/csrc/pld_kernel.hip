@@ -98,7 +98,7 @@ struct WsOff {
   size_t status, x, q, kv, part, o, h2, logits, m, cqr, ckvr, qr, qlat, olat, amax, ixr, qi, ilist, isel, ll_end, sel,
       gates, spec, a_dbg, b_dbg, f_dbg, ikh, ikl, ilo, itok, kx, rope, layers, total;
   // batched verify (per-position copies of the LL buffers; vsel is a plain debug area)
-  size_t vx, vcqr, vckv, vqn, vqr, vqlat, vpart, volat, vo, vh2, vss, vrp, vlog, vm, vfp, vamax, vsel, vf;
+  size_t vx, vcqr, vckv, vqn, vqr, vqlat, vpart, volat, vo, vh2, vss, vrp, vhn, vlog, vm, vfp, vamax, vsel, vf;
 };
 
 struct KArgs {
@@ -1819,13 +1819,14 @@ WsOff layout(const KCfg& k, int n_layers) {
     // position [nwg][VBW], then the router's gamma-weighted dot products [E][nwg][VBW]
     o.vss = p; p += al((size_t)k.nwg * VBW * 2 * W);
     o.vrp = p; p += al((size_t)k.E * k.nwg * VBW * 2 * W);
+    o.vhn = p; p += al(VBW * (k.H / 2) * W);   // the normalised FFN operand rows (bf16 pairs)
     o.vlog = p; p += al(VBW * 4 * k.E * W);
     o.vm = p; p += al((size_t)(k.vq * k.topk + k.nshared) * VBW * (k.inter / 2) * W);
     o.vfp = p; p += al((size_t)(k.vq * k.topk + k.nshared) * VBW * k.H * W);   // gated down partials
     o.vamax = p; p += al(VBW * 3 * k.nwg * W);
   } else {
-    o.vx = o.vcqr = o.vckv = o.vqn = o.vqr = o.vqlat = o.vpart = o.volat = o.vo = o.vh2 = o.vss = o.vrp = o.vlog =
-        o.vm = o.vfp = o.vamax = 0;
+    o.vx = o.vcqr = o.vckv = o.vqn = o.vqr = o.vqlat = o.vpart = o.volat = o.vo = o.vh2 = o.vss = o.vrp = o.vhn =
+        o.vlog = o.vm = o.vfp = o.vamax = 0;
   }
   o.ll_end = p;
   if (k.vq >= 2) {
