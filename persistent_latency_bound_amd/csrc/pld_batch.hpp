@@ -1683,15 +1683,28 @@ __device__ __forceinline__ bool bstage_ffn(Ctx& cx, const KArgs& a, const Step& 
         b = gt ? ks[i] : b;
         bi = gt ? (uint32_t)i : bi;
       }
+      // wave-wide largest key with DPP moves (a lane keeps its own value where a move does
+      // not write it); the result from lane 63
       uint64_t m = b;
-      for (int off = 32; off >= 1; off >>= 1) {
-        const uint64_t o = ((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)(m >> 32), off, 64) << 32) |
-                           (uint32_t)__shfl_xor((int)(uint32_t)m, off, 64);
+      auto step = [&](auto ctrl_tag) {
+        constexpr int CTRL = decltype(ctrl_tag)::value >> 4, RM = decltype(ctrl_tag)::value & 0xf;
+        const uint64_t o = ((uint64_t)dpp_keep_u32<CTRL, RM>((uint32_t)(m >> 32)) << 32) | dpp_keep_u32<CTRL, RM>((uint32_t)m);
         m = o > m ? o : m;
-      }
+      };
+      step(std::integral_constant<int, (0xB1 << 4) | 0xf>{});    // quad_perm [1,0,3,2]
+      step(std::integral_constant<int, (0x4E << 4) | 0xf>{});    // quad_perm [2,3,0,1]
+      step(std::integral_constant<int, (0x141 << 4) | 0xf>{});   // row_half_mirror
+      step(std::integral_constant<int, (0x140 << 4) | 0xf>{});   // row_mirror
+      step(std::integral_constant<int, (0x142 << 4) | 0xa>{});   // row_bcast:15
+      step(std::integral_constant<int, (0x143 << 4) | 0xc>{});   // row_bcast:31
+      m = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(m >> 32), 63) << 32) |
+          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)m, 63);
       const uint32_t mye = (uint32_t)lane + 64u * bi;
       const bool hold = b == m;
-      const uint32_t ee = wave_minmax_u32<false>(hold ? mye : 0xffffffffu);
+      const uint64_t hm = __ballot(hold);
+      const uint32_t ee = __popcll(hm) == 1
+                              ? (uint32_t)__builtin_amdgcn_readlane((int)mye, __ffsll((unsigned long long)hm) - 1)
+                              : wave_minmax_u32<false>(hold ? mye : 0xffffffffu);
 #pragma unroll
       for (int i = 0; i < NS; i++) ks[i] = (mye == ee && bi == (uint32_t)i) ? 0ull : ks[i];
       if (lane == 0) L.isel[p * 8 + r] = (int)ee;
