@@ -492,7 +492,12 @@ __device__ __forceinline__ bool bstage_x(Ctx& cx, const KArgs& a, const Step& st
   const DLayer Ly = *gp(st.Ly);
   const int w = cx.w, nwg = cx.nwg;
   constexpr int H = SH::H, R = SH::QL + SH::LAT, AST = vb_astr(H);
-  const int r0 = split_at(R, nwg, w), r1 = split_at(R, nwg, w + 1);
+  // W_DQ rows over the first nwq workgroups, W_DKV rows over the rest (in proportion), so
+  // that no workgroup holds rows of both (two segments: two 16-row tiles and twice the items
+  // per wave for the one workgroup that did)
+  const int nwq = max(1, min(nwg - 1, (int)(((long long)nwg * SH::QL + R / 2) / R)));
+  const int r0 = w < nwq ? split_at(SH::QL, nwq, w) : SH::QL + split_at(SH::LAT, nwg - nwq, w - nwq);
+  const int r1 = w < nwq ? split_at(SH::QL, nwq, w + 1) : SH::QL + split_at(SH::LAT, nwg - nwq, w - nwq + 1);
   int h0, h1;
   hrows(H, nwg, w, &h0, &h1);
   RegPairs<H> gam;

@@ -1747,7 +1747,11 @@ pld_status derive(const pld_config* c, int nwg, KCfg* k) {
     if (!pick_verify(c) || c->n_shared > 4 || c->top_k > 8 || c->n_experts > 256 || k->cpw != 128)
       return PLD_E_UNSUPPORTED;
     auto per = [nwg](long long n) { return (n + nwg - 1) / nwg; };
-    const long long hr = 2 * per(c->hidden / 2), xr = per(c->q_lora + c->kv_lora + c->rope_dim);
+    // X rows: W_DQ over the first nwq workgroups, W_DKV over the rest (as the batched X stage splits them)
+    const long long R = c->q_lora + c->kv_lora + c->rope_dim;
+    const long long nwq = std::max(1LL, std::min((long long)nwg - 1, ((long long)nwg * c->q_lora + R / 2) / R));
+    const long long hr = 2 * per(c->hidden / 2),
+                    xr = nwg < 2 ? R : std::max((c->q_lora + nwq - 1) / nwq, (R - c->q_lora + (nwg - nwq) - 1) / (nwg - nwq));
     const long long qr = 2 * per((long long)c->n_heads * (c->nope_dim + c->rope_dim) / 2);
     const long long ur = per((long long)c->n_heads * c->v_dim), sr = 2 * per(c->inter / 2);
     const int rows = std::max(c->max_query, c->max_batch);
