@@ -16,9 +16,11 @@
 //   BX  a_p = RMSNorm(x_p); [c_q' ; c_kv' | k_r']_p = [W_DQ ; W_DKV] a_p      (matrix cores)
 //   BQ  RMSNorm(c_q'_p); q_p = W_UQ c_q_p, RoPE at position pos + p          (matrix cores)
 //   BA  q_lat = W_UK^T q_nope per head and position (weights in registers, reused)
-//   BT  attention per (16-head group, chunk of the shared history), two positions per
-//       pass over the chunk; the nq new latent rows join the last chunk with the causal
-//       mask (position p sees new rows 0..p)
+//   BT  attention. Verify: per (8-head group, chunk of the shared history), all positions
+//       in one pass over the chunk; the nq new latent rows join the last chunk with the
+//       causal mask (position p sees new rows 0..p). Batch decode: per (16-head group,
+//       sequence, chunk of that sequence's history), one pass; the sequence's new row
+//       joins its last chunk
 //   BM  merge of the chunk partials, per position
 //   BU  o = W_UV o_lat per head                                               (matrix cores)
 //   BO  h2_p = x_p + W_O o_p                                                  (matrix cores)
@@ -37,7 +39,6 @@
 
 constexpr int VB = 8;                    // positions per batched step (max)
 constexpr int VACT_BYTES = 150528;       // LDS region for matrix-core operands / attention (147 KiB)
-constexpr int VPP = 2;                   // positions per attention pass over a chunk
 
 typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
 
@@ -688,34 +689,36 @@ __device__ __forceinline__ bool bstage_absorb(Ctx& cx, const KArgs& a, const Ste
   return true;
 }
 
-// The new latent rows of the step's rows (computed by the last chunk's workgroups): all
-// rows' c_kv' | k_r' fetched together into tmp [VB][LAT] fp32 (LDS), RMSNorm of c_kv (fp64
-// statistics, one reduction for all rows) and RoPE of k_r at each row's position, bf16 into
-// newr [VB][LAT]; head group 0 appends each row to its cache row crow(p).
+// The new latent rows of the step's rows plo .. phi - 1 (computed by the last chunk's
+// workgroups): their c_kv' | k_r' fetched together into tmp [VB][LAT] fp32 (LDS), RMSNorm of
+// c_kv (fp64 statistics, one reduction for all rows) and RoPE of k_r at each row's position,
+// bf16 into newr [VB][LAT]; with append, each row is also written to its cache row crow(p).
 template <class SH, typename CRow>
-__device__ __forceinline__ bool new_rows(Ctx& cx, const KArgs& a, const DLayer& Ly, VLds& V, int nq, uint32_t k1,
-                                         bool append, float* tmp, uint16_t* newr, CRow&& crow) {
+__device__ __forceinline__ bool new_rows(Ctx& cx, const KArgs& a, const DLayer& Ly, VLds& V, int plo, int phi,
+                                         uint32_t k1, bool append, float* tmp, uint16_t* newr, CRow&& crow) {
   constexpr int LAT = SH::LAT, KL = SH::KL, RD = SH::RD;
   constexpr int NE = (VB * (LAT / 2) + BLOCK - 1) / BLOCK;   // output pairs per thread
   const int tid = tid_opaque();
   // this thread's RMSNorm weights (c_kv) or RoPE factors (k_r), loaded before the fetch so
   // that they do not wait behind it
+  const int nr = phi - plo;
   float f0[NE], f1[NE];
 #pragma unroll
   for (int j = 0; j < NE; j++) {
-    const int e = min(tid + j * BLOCK, nq * (LAT / 2) - 1), p = e / (LAT / 2), k = 2 * (e % (LAT / 2));
+    const int e = min(tid + j * BLOCK, nr * (LAT / 2) - 1), p = plo + e / (LAT / 2), k = 2 * (e % (LAT / 2));
     const PLD_GLOBAL float* src = k < KL ? gp(Ly.kv_norm) + k
                                          : gp(wsp<float>(a, a.off.rope)) + (size_t)V.rpos[p] * RD + (k - KL);
     f0[j] = src[0];
     f1[j] = src[1];
   }
-  if (!ll_fetch_rows<LAT>(cx, reinterpret_cast<uint32_t*>(tmp), LAT, vbuf(a, a.off.vckv, LAT, 0), LAT, nq, k1, W_KV))
+  if (!ll_fetch_rows<LAT>(cx, reinterpret_cast<uint32_t*>(tmp + plo * LAT), LAT, vbuf(a, a.off.vckv, LAT, plo), LAT, nr, k1,
+                         W_KV))
     return false;
   double ss[VB];
 #pragma unroll
   for (int p = 0; p < VB; p++) {
     ss[p] = 0.0;
-    if (p < nq)
+    if (p >= plo && p < phi)
       for (int i = tid; i < KL; i += BLOCK) ss[p] += (double)tmp[p * LAT + i] * (double)tmp[p * LAT + i];
   }
   block_sum_rows(ss, V.redv);
@@ -724,8 +727,8 @@ __device__ __forceinline__ bool new_rows(Ctx& cx, const KArgs& a, const DLayer& 
 #pragma unroll
   for (int j = 0; j < NE; j++) {
     const int e = tid + j * BLOCK;
-    if (e >= nq * (LAT / 2)) break;
-    const int p = e / (LAT / 2), i = e % (LAT / 2), k = 2 * i;
+    if (e >= nr * (LAT / 2)) break;
+    const int p = plo + e / (LAT / 2), i = e % (LAT / 2), k = 2 * i;
     double r = 0.0;
 #pragma unroll
     for (int q = 0; q < VB; q++) r = q == p ? ss[q] : r;   // (ss[] holds the scales, below)
@@ -748,20 +751,26 @@ __device__ __forceinline__ bool new_rows(Ctx& cx, const KArgs& a, const DLayer& 
   return true;
 }
 
-// ------------------------------------------------------------------ BT: attention, VPP positions per pass
-// Workgroup (head group hg of HPW = 16 heads, chunk ch) as in the single-position stage:
-// the chunk's rows [t0, t1) of the pos history rows (all written before this launch, so
-// read through L2, which the head groups of a chunk share). For each pass, the queries of
-// VPP positions are staged, the chunk's 32-row sub-blocks are staged once and used by
-// both positions (S = Q C^T and O += P C on the matrix cores, online softmax per head and
-// position), then the last chunk adds the nq new rows of this step on the vector ALU,
-// each position seeing the new rows up to its own. Partials go to the position's buffer.
+// ------------------------------------------------------------------ BT: attention of a batch decode
+// Every row is a sequence of its own: its cache rows start at p * max_seq and its history is
+// [0, rpos[p]). The workgroups of each head group (HPW = 16 heads, nwg / NG of them) are
+// dealt to the sequences, CB = (nwg / NG) / nq consecutive workgroups per sequence; workgroup
+// (head group hg, sequence b, chunk c) runs one pipeline over the 32-row sub-blocks of chunk
+// c of b's history (staged in LDS, double buffer, DEPTH register sets of loads in flight):
+// S = Q C^T and O += P C on the matrix cores, online softmax per head; the last chunk adds
+// b's new row on the vector ALU. The head groups of one (sequence, chunk) are workgroups
+// hg * (nwg / NG) + i for one i, so they lie on one XCD and share the rows through its L2;
+// rows written inside this launch are read coherently. Partials per (sequence, head, chunk).
+template <class SH>
+__device__ __forceinline__ int batch_chunks(int nwg, int nq) {
+  return (nwg / (SH::NH / SH::HPW)) / nq;
+}
+
 template <class SH>
 __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step& st, VLds& V, int nq) {
-  const KCfg& c = a.c;
   const DLayer Ly = *gp(st.Ly);
   const uint32_t k1 = st.k1;
-  constexpr int LAT = SH::LAT, KL = SH::KL, RD = SH::RD, HPW = SH::HPW, TB = SH::TB, CSTR = SH::CSTR;
+  constexpr int LAT = SH::LAT, KL = SH::KL, HPW = SH::HPW, TB = SH::TB, CSTR = SH::CSTR;
   constexpr int KSTEPS = LAT / 16, KQ = KSTEPS / 4;
   constexpr int CPRW = LAT / 8;
   constexpr int NLD = (TB * CPRW + BLOCK - 1) / BLOCK;
@@ -770,291 +779,229 @@ __device__ __forceinline__ bool bstage_attn(Ctx& cx, const KArgs& a, const Step&
   const int tid = tid_opaque();
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hown = wave * HS + ((lane & 63) >> 5);
-  const int nch = c.cpg;
-  const int hg = cx.w / nch, ch = cx.w % nch;
+  const int ngw = cx.nwg / (SH::NH / HPW);   // workgroups per head group
+  const int CB = batch_chunks<SH>(cx.nwg, nq);
+  const int hg = cx.w / ngw, i = cx.w % ngw;
+  const int b = i / CB, ch = i % CB;
+  if (b >= nq) {   // (nwg / NG not a multiple of nq: the spare workgroups have no chunk)
+    stamp(a, cx, st, TR_ATT_PARTIAL);
+    return true;
+  }
   const int hbase = hg * HPW;
-  // verify (a.bmode == 0): the rows are consecutive positions of one sequence and share its
-  // history [0, rpos[0]); batch decode: row p is sequence p, with its own cache (rows
-  // p * max_seq ..) and history [0, rpos[p]); set per pass below
-  const bool shared = a.bmode == 0;
-  const size_t seq_rows = (size_t)c.max_seq;
-  int t0 = 0, n = 0;
-  const uint16_t* lat = Ly.lat;
+  const int hist = V.rpos[b];
+  const int t0 = split_at(hist, CB, ch), n = split_at(hist, CB, ch + 1) - t0;
+  const int nsb = (n + TB - 1) / TB;
+  const int fresh = hist - cx.token;   // b's rows >= fresh were appended inside this launch (one per step)
+  const uint16_t* lat = Ly.lat + (size_t)b * a.c.max_seq * LAT;
+  const bool last = ch == CB - 1;
   // LDS
-  uint16_t* Qs = V.A;                                        // [VPP][16][CSTR]
-  uint16_t* Cs = Qs + VPP * 16 * CSTR;                       // [2][TB][CSTR]
-  uint16_t* Ps = Cs + 2 * TB * CSTR;                         // [VPP][16][TB]
-  float* Ssc = reinterpret_cast<float*>(Ps + VPP * 16 * TB); // [VPP][4][2][256]
-  float* alph = Ssc + VPP * 4 * 2 * 256;                     // [VPP][16]
-  uint16_t* newr = reinterpret_cast<uint16_t*>(alph + VPP * 16);   // [VB][LAT] new rows (bf16)
-  float* ntmp = reinterpret_cast<float*>(newr + VB * LAT);   // [LAT]
-  float* sn = ntmp + LAT;                                    // [VPP][16][VB + 2] new-row scores, alpha, p
-  float* qtmp = reinterpret_cast<float*>(Cs + TB * CSTR);    // q staging (Cs buffer 1, free between passes)
-  const bool last = ch == nch - 1;
-  // the new rows of this step (last chunk): RMSNorm(c_kv') and RoPE(k_r'), bf16; appended
-  // to the cache by head group 0
+  uint16_t* Qs = V.A;                                        // [16][CSTR]
+  uint16_t* Cs = Qs + 16 * CSTR;                             // [2][TB][CSTR]
+  uint16_t* Ps = Cs + 2 * TB * CSTR;                         // [16][TB]
+  float* Ssc = reinterpret_cast<float*>(Ps + 16 * TB);       // [4][2][256]
+  float* alph = Ssc + 4 * 2 * 256;                           // [16]
+  uint16_t* newr = reinterpret_cast<uint16_t*>(alph + 16);   // [VB][LAT] new rows (bf16; row b used)
+  float* sn = reinterpret_cast<float*>(newr + VB * LAT);     // [16] new-row scores, then [16][2] (p, alpha)
+  float* qtmp = reinterpret_cast<float*>(Cs + TB * CSTR);    // q staging (Cs buffer 1, free until the second sub-block)
+  // b's new row (last chunk): RMSNorm(c_kv') and RoPE(k_r'), bf16; appended to b's cache
+  // row rpos[b] by head group 0
   if (last) {
     // (Cs buffer 0 is free until the first sub-block is staged)
-    if (!new_rows<SH>(cx, a, Ly, V, nq, k1, hg == 0, reinterpret_cast<float*>(Cs), newr,
-                      [&](int p) { return (shared ? 0 : (size_t)p * seq_rows) + (size_t)V.rpos[p]; }))
+    if (!new_rows<SH>(cx, a, Ly, V, b, b + 1, k1, hg == 0, reinterpret_cast<float*>(Cs), newr,
+                      [&](int p) { return (size_t)p * a.c.max_seq + (size_t)V.rpos[p]; }))
       return false;
   }
   const float scale = 1.0f / sqrtf((float)(SH::ND + SH::RD));
   const int ln = lane & 15, lq = lane >> 4;
-  int nsb = 0;
   constexpr int DEPTH = 3;
+  auto fresh_block = [&](int sb) -> bool {   // does sub-block sb hold a row written in this launch?
+    const int lr = min(sb * TB + TB, n) - 1;
+    return lr >= 0 && t0 + lr >= fresh;
+  };
   uint4 cb[DEPTH][NLD];
-  auto issue = [&](int set, int sb) {
+  auto issue_k = [&](int set, int sb, auto coh_tag) {
+    constexpr bool COH = decltype(coh_tag)::value;
     const bool live = sb < nsb;
 #pragma unroll
-    for (int i = 0; i < NLD; i++) {
-      const int idx = min(tid + i * BLOCK, TB * CPRW - 1);
+    for (int k8 = 0; k8 < NLD; k8++) {
+      const int idx = min(tid + k8 * BLOCK, TB * CPRW - 1);
       const int r = idx / CPRW, k = idx % CPRW;
       const int t = max(min(sb * TB + r, n - 1), 0);
       const uint16_t* p = live ? lat + (size_t)(t0 + t) * LAT + k * 8 : lat;
-      cb[set][i] = ld_g16(p);
+      cb[set][k8] = COH ? ld_coh16(p) : ld_g16(p);
     }
+  };
+  auto issue = [&](int set, int sb) {
+    if (sb < nsb && fresh_block(sb)) issue_k(set, sb, std::true_type{});
+    else issue_k(set, sb, std::false_type{});
   };
   auto store = [&](int set, int buf) {
     uint16_t* C = Cs + buf * TB * CSTR;
 #pragma unroll
-    for (int i = 0; i < NLD; i++) {
-      const int idx = tid + i * BLOCK;
+    for (int k8 = 0; k8 < NLD; k8++) {
+      const int idx = tid + k8 * BLOCK;
       if (idx < TB * CPRW) {
         const int r = idx / CPRW, k = idx % CPRW;
         uint32_t* d = reinterpret_cast<uint32_t*>(C + r * CSTR + k * 8);
-        d[0] = cb[set][i].x; d[1] = cb[set][i].y; d[2] = cb[set][i].z; d[3] = cb[set][i].w;
+        d[0] = cb[set][k8].x; d[1] = cb[set][k8].y; d[2] = cb[set][k8].z; d[3] = cb[set][k8].w;
       }
     }
   };
-  constexpr int PSTR = vp_stride<KL>();
-  uint64_t* pll = wsp<uint64_t>(a, a.off.vpart);
-  const size_t pwords = (size_t)SH::NH * nch * PSTR;   // words of one position's partials
-  for (int p0 = 0; p0 < nq; p0 += shared ? VPP : 1) {
-    const int np = shared ? min(VPP, nq - p0) : 1;
-    {
-      const int hist = V.rpos[shared ? 0 : p0];   // history rows of the pass's rows
-      t0 = split_at(hist, nch, ch);
-      n = split_at(hist, nch, ch + 1) - t0;
-      nsb = (n + TB - 1) / TB;
-      lat = Ly.lat + (shared ? 0 : (size_t)p0 * seq_rows * LAT);
-    }
 #pragma unroll
-    for (int d = 0; d < DEPTH; d++) issue(d, d);
-    // queries of the pass: q_lat [HPW][KL] and q_rope [HPW][RD] (bf16 pairs) -> rows of Qs
-    for (int j = 0; j < VPP; j++) {
-      uint16_t* Q = Qs + j * 16 * CSTR;
-      if (j < np) {
-        uint32_t* qw = reinterpret_cast<uint32_t*>(qtmp);
-        const int p = p0 + j;
-        if (!ll_fetch<per_for(HPW * KL / 2)>(cx, qw, vbuf(a, a.off.vqlat, SH::NH * KL / 2, p) + (size_t)hbase * KL / 2,
-                                             HPW * KL / 2, k1, W_QLAT))
-          return false;
-        if (!ll_fetch<per_for(HPW * RD / 2)>(cx, qw + HPW * KL / 2,
-                                             vbuf(a, a.off.vqr, SH::NH * RD / 2, p) + (size_t)hbase * RD / 2,
-                                             HPW * RD / 2, k1, W_QLAT))
-          return false;
-        for (int i = tid; i < 16 * LAT / 2; i += BLOCK) {
-          const int hh = i / (LAT / 2), k2 = i % (LAT / 2);
-          const uint32_t v = k2 < KL / 2 ? qw[hh * (KL / 2) + k2] : qw[HPW * KL / 2 + hh * (RD / 2) + (k2 - KL / 2)];
-          reinterpret_cast<uint32_t*>(Q + hh * CSTR)[k2] = v;
-        }
-        __syncthreads();
-      } else {
-        for (int i = tid; i < 16 * LAT / 2; i += BLOCK) reinterpret_cast<uint32_t*>(Q + (i / (LAT / 2)) * CSTR)[i % (LAT / 2)] = 0u;
-      }
-    }
-    for (int i = tid; i < VPP * 16 * TB; i += BLOCK) Ps[i] = 0;
-    __syncthreads();
-    if (p0 == 0) stamp(a, cx, st, TR_ATT_READY);
-    float m_run[VPP], l_run[VPP];
-    f32x4 O[VPP][4];
-#pragma unroll
-    for (int j = 0; j < VPP; j++) {
-      m_run[j] = -INFINITY;
-      l_run[j] = 0.f;
-#pragma unroll
-      for (int t = 0; t < 4; t++) O[j][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-    auto block = [&](const uint16_t* C, int tb0) {
-      // S partials: wave pair (wave >> 1) covers k-steps [kq*KQ, +KQ), tile nt = wave & 1
-      {
-        const int nt = wave & 1, kq = wave >> 1;
-#pragma unroll
-        for (int j = 0; j < VPP; j++) {
-          const uint16_t* Q = Qs + j * 16 * CSTR;
-          f32x4 s4 = {0.f, 0.f, 0.f, 0.f}, s5 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kk = 0; kk < KQ; kk++) {
-            const int k0 = (kq * KQ + kk) * 16 + 4 * lq;
-            const bf16x4 av = *reinterpret_cast<const bf16x4*>(Q + ln * CSTR + k0);
-            const bf16x4 bv = *reinterpret_cast<const bf16x4*>(C + (nt * 16 + ln) * CSTR + k0);
-            if (kk & 1) s5 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, s5, 0, 0, 0);
-            else s4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, s4, 0, 0, 0);
-          }
-          s4 += s5;
-          float* dst = Ssc + ((j * 4 + kq) * 2 + nt) * 256;
-#pragma unroll
-          for (int q = 0; q < 4; q++) dst[(4 * lq + q) * 16 + ln] = s4[q];
-        }
-      }
-      __syncthreads();
-      // online softmax: head hown, token tb0 + (lane & 31), per position
-      {
-        const int h = hown, tl = lane & 31;
-#pragma unroll
-        for (int j = 0; j < VPP; j++) {
-          float s = -INFINITY;
-          if (tb0 + tl < n) {
-            const int nt = tl >> 4, col = tl & 15;
-            s = 0.f;
-#pragma unroll
-            for (int kq = 0; kq < 4; kq++) s += Ssc[((j * 4 + kq) * 2 + nt) * 256 + h * 16 + col];
-            s *= scale;
-          }
-          const float mb = half_max_dpp(s);
-          const float mnew = fmaxf(m_run[j], mb);
-          const float al = m_run[j] == -INFINITY ? 0.f : __expf(m_run[j] - mnew);
-          const float pv = s == -INFINITY ? 0.f : __expf(s - mnew);
-          l_run[j] = l_run[j] * al + half_sum_dpp(pv);
-          m_run[j] = mnew;
-          Ps[(j * 16 + h) * TB + tl] = (uint16_t)bf16_bits(pv);
-          if (tl == 0) alph[j * 16 + h] = al;
-        }
-      }
-      __syncthreads();
-      // O = alpha O + P C: wave owns columns [wave*64, +64)
-#pragma unroll
-      for (int j = 0; j < VPP; j++) {
-        float fa[4];
-#pragma unroll
-        for (int q = 0; q < 4; q++) fa[q] = alph[j * 16 + 4 * lq + q];
-#pragma unroll
-        for (int t = 0; t < 4; t++)
-#pragma unroll
-          for (int q = 0; q < 4; q++) O[j][t][q] *= fa[q];
-#pragma unroll
-        for (int ks = 0; ks < TB / 16; ks++) {
-          const bf16x4 av = *reinterpret_cast<const bf16x4*>(Ps + (j * 16 + ln) * TB + ks * 16 + 4 * lq);
-#pragma unroll
-          for (int t = 0; t < 4; t++) {
-            const int col = (wave * 4 + t) * 16 + ln;
-            bf16x4 bv;
-#pragma unroll
-            for (int q = 0; q < 4; q++) bv[q] = (short)C[(ks * 16 + 4 * lq + q) * CSTR + col];
-            O[j][t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, O[j][t], 0, 0, 0);
-          }
-        }
-      }
-    };
-    for (int sb0 = 0; sb0 < nsb; sb0 += DEPTH) {
-#pragma unroll
-      for (int d = 0; d < DEPTH; d++) {
-        const int sb = sb0 + d;
-        if (sb >= nsb) break;
-        const int buf = sb & 1;
-        const uint16_t* C = Cs + buf * TB * CSTR;
-        store(d, buf);
-        __syncthreads();
-        issue(d, sb + DEPTH);
-        block(C, sb * TB);
-      }
-    }
-    __syncthreads();   // (the last block's LDS reads are done before Cs buffer 1 holds the next queries)
-    if (p0 == 0) stamp(a, cx, st, 17);
-    if (p0 == (shared ? VPP : 1)) stamp(a, cx, st, 31);
-    // the new rows (last chunk): position p0 + j sees new rows 0 .. p0 + j
-    if (last) {
-      // scores: thread (half-wave hr = head, lane j32) over the LAT dims of new row r
-      for (int j = 0; j < np; j++) {
-        const int p = p0 + j;
-        const uint16_t* Q = Qs + j * 16 * CSTR;
-        for (int r = shared ? 0 : p; r <= p; r++) {
-          constexpr int DPJ = LAT / 32;
-          const int hr = tid >> 5, jj = tid & 31;
-          float sv = 0.f;
-#pragma unroll
-          for (int d = 0; d < DPJ; d++)
-            sv = fmaf(bf16_to_f32(Q[hr * CSTR + jj * DPJ + d]), bf16_to_f32(newr[r * LAT + jj * DPJ + d]), sv);
-          sv = dpp_sum<32>(sv);
-          if (jj == 31) sn[(j * 16 + hr) * (VB + 2) + r] = sv * scale;
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < VPP; j++) {
-        if (j < np) {
-          const int p = p0 + j;
-          float* snh = sn + (j * 16 + hown) * (VB + 2);
-          const int rlo = shared ? 0 : p;   // the new rows this row sees: rlo .. p
-          float mb = -INFINITY;
-          for (int r = rlo; r <= p; r++) mb = fmaxf(mb, snh[r]);
-          const float mnew = fmaxf(m_run[j], mb);
-          const float al = m_run[j] == -INFINITY ? 0.f : __expf(m_run[j] - mnew);
-          float ls = 0.f;
-          __syncthreads();
-          // p_r = exp(s_r - mnew), kept in snh[r] (written by one lane per head)
-          float pr[VB];
-#pragma unroll
-          for (int r = 0; r < VB; r++) {
-            pr[r] = (r >= rlo && r <= p) ? __expf(snh[r] - mnew) : 0.f;
-            ls += pr[r];
-          }
-          __syncthreads();
-          if ((lane & 31) == 0) {
-#pragma unroll
-            for (int r = 0; r < VB; r++) snh[r] = pr[r];
-            snh[VB] = al;
-          }
-          l_run[j] = l_run[j] * al + ls;
-          m_run[j] = mnew;
-          __syncthreads();
-#pragma unroll
-          for (int t = 0; t < 4; t++) {
-            const int col = (wave * 4 + t) * 16 + ln;
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-              const int hh = 4 * lq + q;
-              const float* sh = sn + (j * 16 + hh) * (VB + 2);
-              float o = O[j][t][q] * sh[VB];
-              for (int r = rlo; r <= p; r++) o = fmaf(sh[r], bf16_to_f32(newr[r * LAT + col]), o);
-              O[j][t][q] = o;
-            }
-          }
-          __syncthreads();
-        }
-      }
-    }
-    // publish the partials of the pass's positions
-    if (p0 == 0) stamp(a, cx, st, TR_ATT_SOFTMAX);
-    if (p0 == (shared ? VPP : 1)) stamp(a, cx, st, 29);
-#pragma unroll
-    for (int j = 0; j < VPP; j++) {
-      if (j < np) {
-        uint64_t* pp = pll + (size_t)(p0 + j) * pwords;
-        if ((lane & 31) == 0) {
-          uint64_t* q = pp + ((size_t)(hbase + hown) * nch + ch) * PSTR;
-          ll_put_f32(q, m_run[j], k1);
-          ll_put_f32(q + 1, l_run[j], k1);
-        }
-#pragma unroll
-        for (int t = 0; t < 4; t++) {
-          const int col = (wave * 4 + t) * 16 + ln;
-#pragma unroll
-          for (int q = 0; q < 4; q++) {
-            const float nb = dpp_mov<0xB1, 0xf, false>(O[j][t][q]);
-            const int hh = 4 * lq + q;
-            if ((ln & 1) == 0) {
-              const uint32_t pr = (uint32_t)__half_as_ushort(__float2half_rn(O[j][t][q])) |
-                                  ((uint32_t)__half_as_ushort(__float2half_rn(nb)) << 16);
-              ll_put(pp + ((size_t)(hbase + hh) * nch + ch) * PSTR + VP_ACC + col / 2, pr, k1);
-            }
-          }
-        }
-      }
+  for (int d = 0; d < DEPTH; d++) issue(d, d);
+  // b's queries: q_lat [HPW][KL] and q_rope [HPW][RD] (bf16 pairs) -> rows of Qs
+  {
+    constexpr int RD = SH::RD;
+    uint32_t* qw = reinterpret_cast<uint32_t*>(qtmp);
+    if (!ll_fetch<per_for(HPW * KL / 2)>(cx, qw, vbuf(a, a.off.vqlat, SH::NH * KL / 2, b) + (size_t)hbase * KL / 2,
+                                         HPW * KL / 2, k1, W_QLAT))
+      return false;
+    if (!ll_fetch<per_for(HPW * RD / 2)>(cx, qw + HPW * KL / 2, vbuf(a, a.off.vqr, SH::NH * RD / 2, b) + (size_t)hbase * RD / 2,
+                                         HPW * RD / 2, k1, W_QLAT))
+      return false;
+    for (int e = tid; e < 16 * LAT / 2; e += BLOCK) {
+      const int hh = e / (LAT / 2), k2 = e % (LAT / 2);
+      const uint32_t v = k2 < KL / 2 ? qw[hh * (KL / 2) + k2] : qw[HPW * KL / 2 + hh * (RD / 2) + (k2 - KL / 2)];
+      reinterpret_cast<uint32_t*>(Qs + hh * CSTR)[k2] = v;
     }
     __syncthreads();
   }
+  stamp(a, cx, st, TR_ATT_READY);
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 O[4];
+#pragma unroll
+  for (int t = 0; t < 4; t++) O[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto block = [&](const uint16_t* C, int tb0) {
+    // S partials: wave pair (wave >> 1) covers k-steps [kq*KQ, +KQ), tile nt = wave & 1
+    {
+      const int nt = wave & 1, kq = wave >> 1;
+      f32x4 s4 = {0.f, 0.f, 0.f, 0.f}, s5 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KQ; kk++) {
+        const int k0 = (kq * KQ + kk) * 16 + 4 * lq;
+        const bf16x4 av = *reinterpret_cast<const bf16x4*>(Qs + ln * CSTR + k0);
+        const bf16x4 bv = *reinterpret_cast<const bf16x4*>(C + (nt * 16 + ln) * CSTR + k0);
+        if (kk & 1) s5 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, s5, 0, 0, 0);
+        else s4 = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, s4, 0, 0, 0);
+      }
+      s4 += s5;
+      float* dst = Ssc + (kq * 2 + nt) * 256;
+#pragma unroll
+      for (int q = 0; q < 4; q++) dst[(4 * lq + q) * 16 + ln] = s4[q];
+    }
+    __syncthreads();
+    // online softmax: head hown, token tb0 + (lane & 31)
+    {
+      const int tl = lane & 31;
+      float s = -INFINITY;
+      if (tb0 + tl < n) {
+        const int nt = tl >> 4, col = tl & 15;
+        s = 0.f;
+#pragma unroll
+        for (int kq = 0; kq < 4; kq++) s += Ssc[(kq * 2 + nt) * 256 + hown * 16 + col];
+        s *= scale;
+      }
+      const float mb = half_max_dpp(s);
+      const float mnew = fmaxf(m_run, mb);
+      const float al = m_run == -INFINITY ? 0.f : __expf(m_run - mnew);
+      const float pv = s == -INFINITY ? 0.f : __expf(s - mnew);
+      l_run = l_run * al + half_sum_dpp(pv);
+      m_run = mnew;
+      Ps[hown * TB + tl] = (uint16_t)bf16_bits(pv);
+      if (tl == 0) alph[hown] = al;
+    }
+    __syncthreads();
+    // O = alpha O + P C: wave owns columns [wave*64, +64)
+    float fa[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) fa[q] = alph[4 * lq + q];
+#pragma unroll
+    for (int t = 0; t < 4; t++)
+#pragma unroll
+      for (int q = 0; q < 4; q++) O[t][q] *= fa[q];
+#pragma unroll
+    for (int ks = 0; ks < TB / 16; ks++) {
+      const bf16x4 av = *reinterpret_cast<const bf16x4*>(Ps + ln * TB + ks * 16 + 4 * lq);
+#pragma unroll
+      for (int t = 0; t < 4; t++) {
+        const int col = (wave * 4 + t) * 16 + ln;
+        bf16x4 bv;
+#pragma unroll
+        for (int q = 0; q < 4; q++) bv[q] = (short)C[(ks * 16 + 4 * lq + q) * CSTR + col];
+        O[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, bv, O[t], 0, 0, 0);
+      }
+    }
+  };
+  for (int sb0 = 0; sb0 < nsb; sb0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; d++) {
+      const int sb = sb0 + d;
+      if (sb >= nsb) break;
+      const int buf = sb & 1;
+      store(d, buf);
+      __syncthreads();
+      issue(d, sb + DEPTH);
+      block(Cs + buf * TB * CSTR, sb * TB);
+    }
+  }
+  __syncthreads();
+  // b's new row (last chunk): thread (half-wave hr = head, lane jj) over LAT / 32 dims
+  if (last) {
+    constexpr int DPJ = LAT / 32;
+    const int hr = tid >> 5, jj = tid & 31;
+    const uint16_t* nr = newr + b * LAT;
+    float sv = 0.f;
+#pragma unroll
+    for (int d = 0; d < DPJ; d++) sv = fmaf(bf16_to_f32(Qs[hr * CSTR + jj * DPJ + d]), bf16_to_f32(nr[jj * DPJ + d]), sv);
+    sv = dpp_sum<32>(sv);
+    if (jj == 31) sn[hr] = sv * scale;
+    __syncthreads();
+    const float s = sn[hown];
+    const float mnew = fmaxf(m_run, s);
+    const float al = m_run == -INFINITY ? 0.f : __expf(m_run - mnew);
+    const float pr = __expf(s - mnew);
+    l_run = l_run * al + pr;
+    m_run = mnew;
+    if ((lane & 31) == 0) {
+      sn[16 + 2 * hown] = pr;
+      sn[16 + 2 * hown + 1] = al;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 4; t++) {
+      const int col = (wave * 4 + t) * 16 + ln;
+      const float c = bf16_to_f32(nr[col]);
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        const int hh = 4 * lq + q;
+        O[t][q] = fmaf(sn[16 + 2 * hh], c, O[t][q] * sn[16 + 2 * hh + 1]);
+      }
+    }
+  }
+  stamp(a, cx, st, TR_ATT_SOFTMAX);
+  // publish: m, l (fp32) and the accumulators as fp16 pairs, at (b, head, chunk)
+  constexpr int PSTR = vp_stride<KL>();
+  uint64_t* pp = wsp<uint64_t>(a, a.off.vpart) + (size_t)b * SH::NH * CB * PSTR;
+  if ((lane & 31) == 0) {
+    uint64_t* q = pp + ((size_t)(hbase + hown) * CB + ch) * PSTR;
+    ll_put_f32(q, m_run, k1);
+    ll_put_f32(q + 1, l_run, k1);
+  }
+#pragma unroll
+  for (int t = 0; t < 4; t++) {
+    const int col = (wave * 4 + t) * 16 + ln;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      const float nb = dpp_mov<0xB1, 0xf, false>(O[t][q]);
+      const int hh = 4 * lq + q;
+      if ((ln & 1) == 0) {
+        const uint32_t pr = (uint32_t)__half_as_ushort(__float2half_rn(O[t][q])) |
+                            ((uint32_t)__half_as_ushort(__float2half_rn(nb)) << 16);
+        ll_put(pp + ((size_t)(hbase + hh) * CB + ch) * PSTR + VP_ACC + col / 2, pr, k1);
+      }
+    }
+  }
+  __syncthreads();
   stamp(a, cx, st, TR_ATT_PARTIAL);
   return true;
 }
@@ -1165,7 +1112,7 @@ __device__ __forceinline__ bool bstage_attn_v(Ctx& cx, const KArgs& a, const Ste
     // (after the queries, which every chunk waits for: the new rows' input was published
     // long before; Cs is free until the first sub-block is staged, and the first sub-blocks'
     // loads, issued above, are in flight meanwhile)
-    if (!new_rows<SH>(cx, a, Ly, V, nq, k1, hg == 0, reinterpret_cast<float*>(Cs), newr,
+    if (!new_rows<SH>(cx, a, Ly, V, 0, nq, k1, hg == 0, reinterpret_cast<float*>(Cs), newr,
                       [&](int p) { return (size_t)V.rpos[p]; }))
       return false;
   }
@@ -1350,8 +1297,8 @@ template <class SH>
 __device__ __forceinline__ bool bstage_merge(Ctx& cx, const KArgs& a, const Step& st, VLds& V, int nq) {
   const KCfg& c = a.c;
   constexpr int KL = SH::KL;
-  // chunks per head: the verify attention (8 heads per workgroup) or the per-row one (HPW)
-  const int nch = a.bmode == 0 ? cx.nwg / (SH::NH / VHG) : c.cpg, cpw = c.cpw;
+  // chunks per head: the verify attention's (8 heads per workgroup) or a batch sequence's
+  const int nch = a.bmode == 0 ? cx.nwg / (SH::NH / VHG) : batch_chunks<SH>(cx.nwg, nq), cpw = c.cpw;
   const int MG = (size_t)NWAVES * (nch * (cpw + 3) + 1) * 4 <= (size_t)VACT_BYTES ? NWAVES : NWAVES / 2;
   const int h = (cx.w * cpw) / KL, c0 = (cx.w * cpw) % KL;
   const int tid = tid_opaque();
@@ -1359,7 +1306,7 @@ __device__ __forceinline__ bool bstage_merge(Ctx& cx, const KArgs& a, const Step
   constexpr int PSTR = vp_stride<KL>();
   const int cpw2 = cpw / 2, nacc = nch * cpw, naw = nch * cpw2;
   const int per = naw + 2 * nch;                 // words of one position
-  const int pwords = SH::NH * c.cpg * PSTR;      // LL words of one position's partials (stride)
+  const int pwords = SH::NH * (a.bmode == 0 ? c.cpg : nch) * PSTR;   // LL words of one position's partials (stride)
   const int fstr = nacc + 2 * nch;               // floats of one position in LDS
   // word i of the group: position i / per, then as in the single-position stage
   struct IdxM {
