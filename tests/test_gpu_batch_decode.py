@@ -81,14 +81,25 @@ def _run_batch(dec, m, starts, toks, n, temperature=0.0, seed=0):
     return lg.cpu().numpy(), tk.cpu().numpy()
 
 
-@pytest.mark.parametrize("temperature", [0.0, 0.8])
-def test_batch_decode_one_layer_vs_oracle(temperature):
-    """Four sequences with their own histories and start positions (300, 290, 257, 300), three
-    tokens each: per sequence and step, logits and tokens against the oracle; the last step's
-    y, f and expert choice of every sequence."""
+# (start positions, first tokens, temperature). Each head group's 64 attention workgroups are
+# dealt to the sequences, 64 // nb chunks each: with 3 or 5 sequences some workgroups have no
+# chunk, and a 5-row history leaves most of its sequence's chunks empty.
+BATCH_CASES = [
+    ([300, 290, 257, 300], [11, 20000, 777, 31337], 0.0),
+    ([300, 290, 257, 300], [11, 20000, 777, 31337], 0.8),
+    ([5, 300, 41], [9, 123, 4567], 0.0),
+    ([299, 17, 256, 300, 130], [1, 2, 3, 4, 5], 0.8),
+]
+
+
+@pytest.mark.parametrize("starts,toks0,temperature", BATCH_CASES,
+                         ids=["4seq-greedy", "4seq-T0.8", "3seq-short-history", "5seq-T0.8"])
+def test_batch_decode_one_layer_vs_oracle(starts, toks0, temperature):
+    """Sequences with their own histories and start positions, three tokens each: per sequence
+    and step, logits and tokens against the oracle; the last step's y, f and expert choice of
+    every sequence."""
     _need_gpu()
     m = _model(n_layers=1, cache_len=300)
-    starts, toks0 = [300, 290, 257, 300], [11, 20000, 777, 31337]
     nb, n = len(starts), 3
     say(f"case: 1-layer FP8 MLA stack + head, batch of {nb} sequences at {starts}, {n} tokens, T {temperature}")
     dec = _batch_decoder(m, nb)
