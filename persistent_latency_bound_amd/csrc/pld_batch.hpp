@@ -1906,15 +1906,17 @@ __device__ __forceinline__ bool bstage_down(Ctx& cx, const KArgs& a, const Step&
 }
 
 // ------------------------------------------------------------------ the batched kernel
-// Verify (a.bmode == 0): a.nrows positions from a.pos0 of one sequence; position 0 takes
+// Verify (BM == 0): a.nrows positions from a.pos0 of one sequence; position 0 takes
 // a.in_token, position p > 0 the caller's draft p - 1 (clamped into the vocabulary).
 // Per-position logits and tokens, and the count of leading drafts equal to the token
 // chosen at the position before.
-// Batch decode (a.bmode == 1): a.nrows sequences, row p at cache position a.bpos[p] of its
+// Batch decode (BM == 1): a.nrows sequences, row p at cache position a.bpos[p] of its
 // own cache, fed a.btok[p]; a.n_tokens steps, each choosing every row's next token, which
 // is the row's input at the next step.
 static_assert(VB == 8, "KArgs holds 8 rows of batch positions and tokens");
-template <class SH>
+// The two modes are separate instantiations (a.bmode == BM), so each compiles only its own
+// attention stage and neither's register allocation depends on the other's.
+template <class SH, int BM>
 __global__ void __launch_bounds__(BLOCK, 1) k_verify_mla(KArgs a) {
   extern __shared__ float lds_raw[];
   Ctx cx;
@@ -1926,14 +1928,14 @@ __global__ void __launch_bounds__(BLOCK, 1) k_verify_mla(KArgs a) {
   const DLayer* layers = wsp<DLayer>(a, a.off.layers);
   if ((a.hooks & PLD_HOOK_DROP_WG0) && cx.w == 0) return;
   const int nq = a.nrows;
-  const int nsteps = a.bmode ? a.n_tokens : 1;
+  const int nsteps = BM ? a.n_tokens : 1;
   VLds L = vcarve(lds_raw);
   if (tid_opaque() < TR_SLOTS) L.tr[tid_opaque()] = 0;
   exp_f64_init(L.dk);
   __syncthreads();
   if (tid_opaque() < nq) {
     const int p = tid_opaque();
-    if (a.bmode) {
+    if (BM) {
       L.tok[p] = a.btok[p];
       L.rpos[p] = a.bpos[p];
     } else {
@@ -1957,6 +1959,7 @@ __global__ void __launch_bounds__(BLOCK, 1) k_verify_mla(KArgs a) {
       st.emb_row = nullptr;
       st.tr = L.tr;
       KArgs as = a;
+      as.bmode = BM;   // (a constant for the stages)
       asm volatile("" : "+s"(as.ws));
       Ctx cs = cx;
       asm volatile("" : "+s"(cs.w), "+s"(cs.nwg), "+s"(as.c.cpw), "+s"(as.c.cpg));
@@ -1965,7 +1968,7 @@ __global__ void __launch_bounds__(BLOCK, 1) k_verify_mla(KArgs a) {
       if (!bstage_x<SH>(cs, as, st, L, nq, li)) return;
       if (!bstage_q<SH>(cs, as, st, L, nq)) return;
       if (!bstage_absorb<SH>(cs, as, st, L, nq)) return;
-      if (as.bmode == 0) {
+      if (BM == 0) {
         if (!bstage_attn_v<SH>(cs, as, st, L, nq)) return;
       } else {
         if (!bstage_attn<SH>(cs, as, st, L, nq)) return;
@@ -1999,13 +2002,13 @@ __global__ void __launch_bounds__(BLOCK, 1) k_verify_mla(KArgs a) {
       if (tid_opaque() == 0) L.tok[VB + p] = tk;
     }
     __syncthreads();
-    if (a.bmode && tid_opaque() < nq) {   // each row's chosen token is its next input
+    if (BM && tid_opaque() < nq) {   // each row's chosen token is its next input
       L.tok[tid_opaque()] = L.tok[VB + tid_opaque()];
       L.rpos[tid_opaque()] += 1;
     }
     __syncthreads();
   }
-  if (!a.bmode && cx.w == 0 && tid_opaque() == 0 && a.out_accepted) {
+  if (!BM && cx.w == 0 && tid_opaque() == 0 && a.out_accepted) {
     int acc = 0;
     for (int p = 1; p < nq; p++) {
       if (gp(a.drafts)[p - 1] != L.tok[VB + p - 1]) break;

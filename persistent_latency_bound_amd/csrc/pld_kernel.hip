@@ -1523,9 +1523,10 @@ static KernelFn pick_kernel(const pld_config* c) {
   return nullptr;
 }
 
-// the batched verify kernel of a configuration (the FP8 MLA MoE shape with a head), or null
-static KernelFn pick_verify(const pld_config* c) {
-  if (matches_mla<ShapeMlaFp8>(c) && c->vocab > 0) return k_verify_mla<ShapeMlaFp8>;
+// the batched kernel of a configuration (the FP8 MLA MoE shape with a head) for a verify
+// (batch = false) or a batch decode, or null
+static KernelFn pick_verify(const pld_config* c, bool batch = false) {
+  if (matches_mla<ShapeMlaFp8>(c) && c->vocab > 0) return batch ? k_verify_mla<ShapeMlaFp8, 1> : k_verify_mla<ShapeMlaFp8, 0>;
   return nullptr;
 }
 
@@ -1550,6 +1551,7 @@ struct pld_handle {
   hipStream_t last_stream;
   KernelFn fn;
   KernelFn vfn;            // batched verify kernel (cfg.max_query >= 2), else null
+  KernelFn bfn;            // batch decode kernel (with vfn), else null
   size_t vlds_bytes;
   int device;
   uint64_t* trace;
@@ -2072,6 +2074,7 @@ pld_status init_into(pld_handle* h, const pld_config* cfg, int32_t n_layers, con
   h->coop = coop && atoi(coop) != 0;
   h->fn = pick_kernel(cfg);
   h->vfn = k.vq >= 2 ? pick_verify(cfg) : nullptr;
+  h->bfn = h->vfn ? pick_verify(cfg, true) : nullptr;
   h->vlds_bytes = vlds_bytes();
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0) khz = 100000;
@@ -2087,11 +2090,12 @@ pld_status init_into(pld_handle* h, const pld_config* cfg, int32_t n_layers, con
   ok = ok && hipFuncSetAttribute((const void*)h->fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->lds_bytes) == hipSuccess;
   int per_cu = 0;
   ok = ok && hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)h->fn, BLOCK, h->lds_bytes) == hipSuccess;
-  if (ok && h->vfn) {
+  for (KernelFn f : {h->vfn, h->bfn}) {
+    if (!ok || !f) continue;
     int per_v = 0;
-    ok = hipFuncSetAttribute((const void*)h->vfn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->vlds_bytes) ==
+    ok = hipFuncSetAttribute((const void*)f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)h->vlds_bytes) ==
              hipSuccess &&
-         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_v, (const void*)h->vfn, BLOCK, h->vlds_bytes) == hipSuccess;
+         hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_v, (const void*)f, BLOCK, h->vlds_bytes) == hipSuccess;
     per_cu = std::min(per_cu, per_v);
   }
   ok = ok && hipDeviceSynchronize() == hipSuccess;
@@ -2307,7 +2311,7 @@ pld_status decode_verify_batched(pld_handle* h, const pld_persistent_args* a, vo
 pld_status decode_batch(pld_handle* h, const pld_batch_args* a, void* stream) {
   if (!h || !a) return PLD_E_INVALID;
   if (h->bad) return PLD_E_STATE;
-  if (!h->vfn || h->kc.vb < 2) return PLD_E_UNSUPPORTED;
+  if (!h->bfn || h->kc.vb < 2) return PLD_E_UNSUPPORTED;
   const int nb = a->n_seq;
   if (nb < 2 || nb > h->kc.vb || a->n_tokens < 1) return PLD_E_INVALID;
   if (!a->out_tokens || ((uintptr_t)a->out_tokens & 3u) || !a->out_hidden || !aligned16(a->out_hidden))
@@ -2351,9 +2355,9 @@ pld_status decode_batch(pld_handle* h, const pld_batch_args* a, void* stream) {
   k.sample_seed = a->sample_seed;
   void* args[] = {&k};
   hipStream_t s = (hipStream_t)stream;
-  const hipError_t e = h->coop ? hipLaunchCooperativeKernel((const void*)h->vfn, dim3(h->kc.nwg), dim3(BLOCK), args,
+  const hipError_t e = h->coop ? hipLaunchCooperativeKernel((const void*)h->bfn, dim3(h->kc.nwg), dim3(BLOCK), args,
                                                             (unsigned)h->vlds_bytes, s)
-                               : hipLaunchKernel((const void*)h->vfn, dim3(h->kc.nwg), dim3(BLOCK), args, h->vlds_bytes, s);
+                               : hipLaunchKernel((const void*)h->bfn, dim3(h->kc.nwg), dim3(BLOCK), args, h->vlds_bytes, s);
   if (e != hipSuccess) return PLD_E_HIP;
   h->hooks &= ~PLD_HOOK_DROP_WG0;
   h->steps += (uint32_t)(h->n_layers * a->n_tokens);
