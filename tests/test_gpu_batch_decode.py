@@ -81,6 +81,45 @@ def _run_batch(dec, m, starts, toks, n, temperature=0.0, seed=0):
     return lg.cpu().numpy(), tk.cpu().numpy()
 
 
+def _oracle_check(m, dec, starts, toks0, lg, tk, n, temperature, seed, seqs):
+    """The oracle run per sequence in seqs, step by step, teacher-forced with the GPU's tokens:
+    logits and tokens of every step, and the last step's y, f and expert choice (one-layer
+    stack). Returns the failures."""
+    H = m.layer.hidden
+    vh2 = dec.debug("vh2").cpu().numpy().astype(np.float64).reshape(8, H)
+    vf = dec.debug("vf").cpu().numpy().astype(np.float64).reshape(8, H)
+    vsel = dec.debug("vsel").cpu().numpy()
+    W = gen.LayerWeights(m.layer, 0, 0)
+    head_m, fg = gen.head_matrix(m), gen.final_norm(m)
+    fails = []
+    for b in seqs:
+        cache = gen.padded_cache(m.layer, b, 0)
+        tin = toks0[b]
+        for t in range(n):
+            p = starts[b] + t
+            x = gen.embedding_rows(m, [tin])[0]
+            rec = OL.decode_layer(m.layer, W, cache, x, p)
+            OL.append_to_cache(m.layer, cache, rec, p)
+            lo = OM.head_logits(m.layer, head_m, fg, rec["out_bits"])
+            otok = OM.sample_token(lo, temperature, seed, p)
+            e = rel_err(lg[t, b], lo)
+            msg = f"sequence {b} step {t} (pos {p}): logits rel err {e:.2e}; oracle token {otok}, GPU {tk[t, b]}"
+            if t == n - 1:
+                xin = nx.bf16_to_f64(np.asarray(x).view(np.uint16))
+                e_y, e_f = rel_err(vh2[b] - xin, rec["y"]), rel_err(vf[b], rec["f"])
+                sel = [int(v) for v in vsel[b * 8: b * 8 + m.layer.top_k]]
+                msg += f"; y {e_y:.2e}, f {e_f:.2e}, experts {'same' if sel == list(rec['router_sel']) else 'DIFFER'}"
+                if e_y >= BAR_VB or e_f >= BAR_VB or sel != list(rec["router_sel"]):
+                    fails.append(msg)
+            say(msg)
+            if e >= TOL:
+                fails.append(msg)
+            if otok != tk[t, b] and abs(lo[otok] - lo[tk[t, b]]) > TOL * np.max(np.abs(lo)):
+                fails.append(msg + " (decisive token difference)")
+            tin = int(tk[t, b])
+    return fails
+
+
 # (start positions, first tokens, temperature). Each head group's 64 attention workgroups are
 # dealt to the sequences, 64 // nb chunks each: with 3 or 5 sequences some workgroups have no
 # chunk, and a 5-row history leaves most of its sequence's chunks empty.
@@ -105,38 +144,44 @@ def test_batch_decode_one_layer_vs_oracle(starts, toks0, temperature):
     dec = _batch_decoder(m, nb)
     lg, tk = _run_batch(dec, m, starts, toks0, n, temperature, 5)
     say(f"GPU tokens per step: {tk.tolist()}")
-    H = m.layer.hidden
-    vh2 = dec.debug("vh2").cpu().numpy().astype(np.float64).reshape(8, H)
-    vf = dec.debug("vf").cpu().numpy().astype(np.float64).reshape(8, H)
-    vsel = dec.debug("vsel").cpu().numpy()
-    W = gen.LayerWeights(m.layer, 0, 0)
-    head_m, fg = gen.head_matrix(m), gen.final_norm(m)
+    fails = _oracle_check(m, dec, starts, toks0, lg, tk, n, temperature, 5, range(nb))
+    assert not fails, fails
+
+
+def test_batch_decode_full_histories_sampled_vs_oracle():
+    """The batch at the size the benchmark runs: eight sequences with 8000..8192-row histories
+    (each sequence's chunks 1000..1024 rows, one per workgroup and head group), one layer, two
+    tokens in one launch (the second step also reads the rows the first appended). Sampled:
+    sequences 0, 3 and 6 against the oracle (its layer takes seconds per token at this history
+    length), teacher-forced; every sequence's first-step logits against its own
+    single-sequence decode (and the second step's where both chose the same first token)."""
+    _need_gpu()
+    m = _model(n_layers=1, cache_len=8192)
+    nb, n = 8, 2
+    starts = [8192, 8150, 8192, 8000, 8192, 8100, 8191, 8192]
+    toks0 = [(b * 7919 + 3) % m.vocab for b in range(nb)]
+    say(f"case: 1-layer FP8 MLA stack + head, batch of {nb} sequences at {starts}, {n} tokens")
+    dec = _batch_decoder(m, nb)
+    lg, tk = _run_batch(dec, m, starts, toks0, n)
+    say(f"GPU tokens per step: {tk.tolist()}")
     fails = []
     for b in range(nb):
-        cache = gen.padded_cache(m.layer, b, 0)
-        tin = toks0[b]
-        for t in range(n):
-            p = starts[b] + t
-            x = gen.embedding_rows(m, [tin])[0]
-            rec = OL.decode_layer(m.layer, W, cache, x, p)
-            OL.append_to_cache(m.layer, cache, rec, p)
-            lo = OM.head_logits(m.layer, head_m, fg, rec["out_bits"])
-            otok = OM.sample_token(lo, temperature, 5, p)
-            e = rel_err(lg[t, b], lo)
-            msg = f"sequence {b} step {t} (pos {p}): logits rel err {e:.2e}; oracle token {otok}, GPU {tk[t, b]}"
-            if t == n - 1:
-                xin = nx.bf16_to_f64(np.asarray(x).view(np.uint16))
-                e_y, e_f = rel_err(vh2[b] - xin, rec["y"]), rel_err(vf[b], rec["f"])
-                sel = [int(v) for v in vsel[b * 8: b * 8 + m.layer.top_k]]
-                msg += f"; y {e_y:.2e}, f {e_f:.2e}, experts {'same' if sel == list(rec['router_sel']) else 'DIFFER'}"
-                if e_y >= BAR_VB or e_f >= BAR_VB or sel != list(rec["router_sel"]):
-                    fails.append(msg)
-            say(msg)
-            if e >= TOL:
-                fails.append(msg)
-            if otok != tk[t, b] and abs(lo[otok] - lo[tk[t, b]]) > TOL * np.max(np.abs(lo)):
-                fails.append(msg + " (decisive token difference)")
-            tin = int(tk[t, b])
+        d1 = _single_decoder(m, b)
+        lg1 = torch.zeros((n, m.vocab), dtype=torch.float32, device="cuda")
+        tk1 = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+        out = torch.zeros(m.layer.hidden, dtype=torch.int16, device="cuda")
+        d1.persistent(start_pos=starts[b], in_token=toks0[b], n_tokens=n, out_hidden=out, out_logits=lg1,
+                      out_tokens=tk1)
+        torch.cuda.synchronize()
+        _status_ok(d1, f"single sequence {b}")
+        lg1, tk1 = lg1.cpu().numpy(), [int(v) for v in tk1.cpu().numpy()]
+        steps = n if tk1[0] == tk[0, b] else 1
+        errs = [rel_err(lg[t, b], lg1[t]) for t in range(steps)]
+        say(f"sequence {b}: alone {tk1}, batched {tk[:, b].tolist()}, logits rel err {[f'{e:.1e}' for e in errs]}")
+        if max(errs) >= TOL:
+            fails.append(f"sequence {b}: batched vs single logits {errs}")
+        del d1
+    fails += _oracle_check(m, dec, starts, toks0, lg, tk, n, 0.0, 0, (0, 3, 6))
     assert not fails, fails
 
 
