@@ -753,14 +753,15 @@ __device__ __forceinline__ bool new_rows(Ctx& cx, const KArgs& a, const DLayer& 
 
 // ------------------------------------------------------------------ BT: attention of a batch decode
 // Every row is a sequence of its own: its cache rows start at p * max_seq and its history is
-// [0, rpos[p]). The workgroups of each head group (HPW = 16 heads, nwg / NG of them) are
-// dealt to the sequences, CB = (nwg / NG) / nq consecutive workgroups per sequence; workgroup
-// (head group hg, sequence b, chunk c) runs one pipeline over the 32-row sub-blocks of chunk
-// c of b's history (staged in LDS, double buffer, DEPTH register sets of loads in flight):
-// S = Q C^T and O += P C on the matrix cores, online softmax per head; the last chunk adds
-// b's new row on the vector ALU. The head groups of one (sequence, chunk) are workgroups
-// hg * (nwg / NG) + i for one i, so they lie on one XCD and share the rows through its L2;
-// rows written inside this launch are read coherently. Partials per (sequence, head, chunk).
+// [0, rpos[p]). The workgroups of each of the NG = NH / HPW head groups (HPW = 16 heads,
+// nwg / NG workgroups each) are dealt to the sequences, CB = (nwg / NG) / nq consecutive
+// workgroups per sequence; workgroup (head group hg, sequence b, chunk c) runs one pipeline
+// over the 32-row sub-blocks of chunk c of b's history (staged in LDS, double buffer, DEPTH
+// register sets of loads in flight): S = Q C^T and O += P C on the matrix cores, online
+// softmax per head; the last chunk adds b's new row on the vector ALU. The head groups of
+// one (sequence, chunk) are workgroups hg * (nwg / NG) + i for one i, so they lie on one XCD
+// and share the rows through its L2; rows written inside this launch are read coherently.
+// Partials per (sequence, head, chunk).
 template <class SH>
 __device__ __forceinline__ int batch_chunks(int nwg, int nq) {
   return (nwg / (SH::NH / SH::HPW)) / nq;
