@@ -1043,9 +1043,11 @@ __device__ __forceinline__ bool bstage_attn_v(Ctx& cx, const KArgs& a, const Ste
   const int hg = cx.w / nch, ch = cx.w % nch;
   const int hbase = hg * VHG;
   const int pos = V.rpos[0];                 // history rows [0, pos), shared by all positions
-  // the split counts the new-row sub-block of the last chunk as TB more rows, so that chunk
-  // holds one history sub-block fewer
-  const int t0 = split_at(pos + TB, nch, ch), n = max(0, min(split_at(pos + TB, nch, ch + 1), pos) - t0);
+  // the split counts the last chunk's extra work as 3 TB more rows (its new-row sub-block,
+  // and the new rows' norm and RoPE, which take about two sub-blocks' time), so that chunk
+  // holds about three history sub-blocks fewer and finishes with the others
+  constexpr int XTRA = 3 * TB;
+  const int t0 = split_at(pos + XTRA, nch, ch), n = max(0, min(split_at(pos + XTRA, nch, ch + 1), pos) - t0);
   const uint16_t* lat = Ly.lat;
   // LDS
   uint16_t* Qs = V.A;                                        // [MT * 16][CSTR] (position, head) rows
